@@ -1,0 +1,80 @@
+"""Frozen-base linear with a LoRA branch, forward and backward, in fp64.
+
+TEST INFRASTRUCTURE ONLY: see ``oracle/__init__.py`` for who may import this.
+
+Sources:
+* "QLoRA: Quantized Low-Rank Adaptation" (completesystemdesign.dev): the
+  three-piece summary (the frozen 4-bit base is expanded to bf16 for the
+  multiply; only the low-rank branch learns, the base gets no gradient) and
+  the storage / compute / learning diagram (bf16 matmuls; gradients flow back
+  into the adapter only).
+* "What is QLoRA?" (qubittool.com), "Key Characteristics": gradients are
+  propagated through the quantized weights; adapters are trained in full
+  precision.
+* "QLoRA Explained ..." (gamut.so), "Step 3: Configure and Apply LoRA
+  Adapters" and "QLoRA Hyperparameter Quick Reference": rank r, alpha, no
+  bias.
+
+Notation: W' [N, K] is the dequantized bf16 weight (``oracle.nf4.dequant``),
+X [M, K], A [r, K], B [N, r], dY [M, N]; s = alpha / r (reading: the usual
+LoRA scale; the pages give r and alpha but no formula). Every operand is the
+exact fp64 value of the bf16 (or fp32) number the GPU consumed, and each
+product is one fp64 matrix multiply. The result is the exact real product up
+to fp64 rounding; it is unique, unlike a GPU's fp32 accumulation order.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def linear_fwd(X, Wd, A, B, s):
+    """Y = X W'^T + s (X A^T) B^T and the saved T = X A^T.  Returns (Y, T)."""
+    X, Wd, A, B = _f64(X), _f64(Wd), _f64(A), _f64(B)
+    s = float(s)
+    T = X @ A.T
+    Y = X @ Wd.T + s * (T @ B.T)
+    return Y, T
+
+
+def linear_bwd(X, Wd, A, B, s, dY, T=None):
+    """Gradients of <dY, Y> with W' frozen.
+
+    U  = dY B
+    dX = dY W' + s U A
+    dA = s U^T X
+    dB = s dY^T T,   T = X A^T (recomputed in fp64 unless given)
+    There is no gradient for W'.  Returns (dX, dA, dB, U).
+    """
+    X, Wd, A, B, dY = _f64(X), _f64(Wd), _f64(A), _f64(B), _f64(dY)
+    s = float(s)
+    if T is None:
+        T = X @ A.T
+    T = _f64(T)
+    U = dY @ B
+    dX = dY @ Wd + s * (U @ A)
+    dA = s * (U.T @ X)
+    dB = s * (dY.T @ T)
+    return dX, dA, dB, U
+
+
+def relerr(Z, Zref) -> float:
+    """Relative Frobenius error ||Z - Zref||_F / ||Zref||_F, in fp64."""
+    Z, Zref = _f64(Z), _f64(Zref)
+    den = np.linalg.norm(Zref)
+    num = np.linalg.norm(Z - Zref)
+    return float(num / den) if den > 0 else float(num)
+
+
+def bf16_floor(Zref) -> float:
+    """relerr of Zref rounded once to bf16 (RNE): the least error a bf16 output
+    can have. Reported beside every bf16 result."""
+    z = np.asarray(Zref, dtype=np.float64)
+    z32 = z.astype(np.float32)
+    u = z32.view(np.uint32).astype(np.uint64)
+    r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
+    return relerr(r, z)
