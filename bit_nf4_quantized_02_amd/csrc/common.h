@@ -1,0 +1,97 @@
+// Shared device helpers for the gfx950 kernels of libqlora.
+//
+// Storage format (per 64-weight block b of the row-major weight, see
+// include/qlora.h): packed nibble codes, an 8-bit E4M3 code for the block's
+// centred absmax, one fp32 second-level scale per 256 blocks, one fp32 mean.
+// Sources: "QLoRA: Quantized Low-Rank Adaptation" (completesystemdesign.dev),
+// three-piece summary and "NF4: a 4-bit format matched to weight
+// statistics"; "QLoRA Explained ..." (gamut.so), "Double Quantization".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+constexpr int kBlock = 64;     // weights per first-level block
+constexpr int kDqBlock = 256;  // blocks per second-level scale
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 values -> packed bf16 pair (lo in bits 0..15), round to nearest
+// even. gfx950 does this in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// OCP FP8 E4M3 bit pattern -> fp32, from the format's definition: sign bit,
+// 4-bit exponent with bias 7, 3-bit mantissa, subnormals at exponent 0.
+// Exact for every finite pattern (the encoder never writes the NaN pattern).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t sign = (b & 0x80u) << 24;
+  const uint32_t e = (b >> 3) & 0xFu;
+  const uint32_t m = b & 0x7u;
+  float mag;
+  if (e == 0) {
+    mag = (float)m * 0.001953125f;  // m/8 * 2^-6 = m * 2^-9, exact
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  }
+  return __uint_as_float(__float_as_uint(mag) | sign);
+}
+
+// c'_b = RN32(RN32(fp8 * s2) + mean): two separately rounded fp32 operations.
+// The pragma keeps the compiler from fusing them into one FMA.
+__device__ __forceinline__ float decode_block_scale(uint32_t code8, float s2, float mean) {
+#pragma clang fp contract(off)
+  const float v = e4m3_to_f32(code8);
+  const float p = v * s2;
+  return p + mean;
+}
+
+// Scale of block `blk` (global block index) read from the encoded weight.
+__device__ __forceinline__ float block_scale(const uint8_t* __restrict__ code8,
+                                             const float* __restrict__ s2, float mean,
+                                             int64_t blk) {
+  return decode_block_scale(code8[blk], s2[blk / kDqBlock], mean);
+}
+
+// One weight: w' = RN_bf16(RN32(L[code] * c')); the product is a single
+// fp32 multiply (nothing to fuse it with), the bf16 rounding is RNE.
+__device__ __forceinline__ float nf4_scaled(float level, float cprime) {
+#pragma clang fp contract(off)
+  return level * cprime;
+}
+
+// Eight codes of one 32-bit word (code 2t in the low nibble of byte t) ->
+// eight bf16 values as four packed pairs, levels looked up in `lut`
+// (16 fp32 entries, normally in LDS).
+__device__ __forceinline__ u32x4 dequant8(uint32_t word, const float* lut, float cprime) {
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = nf4_scaled(lut[(word >> (8 * p)) & 0xF], cprime);
+    const float b = nf4_scaled(lut[(word >> (8 * p + 4)) & 0xF], cprime);
+    out[p] = pack_bf16x2(a, b);
+  }
+  return out;
+}
+
+__host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace qlora

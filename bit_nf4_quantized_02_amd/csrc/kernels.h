@@ -1,0 +1,75 @@
+// Internal launch functions of libqlora (host side). Each enqueues kernels on
+// `stream` and returns hipGetLastError(); argument checking happens before,
+// in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qlora {
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// ---- encoder workspace: absmax fp32 [nb], run sums fp64 [ceil(nb/256)]
+inline size_t quantize_ws_absmax_bytes(int64_t nb) { return align256((size_t)nb * 4); }
+inline size_t quantize_ws_bytes(int64_t nb) {
+  return quantize_ws_absmax_bytes(nb) + align256((size_t)((nb + 255) / 256) * 8);
+}
+
+hipError_t launch_quantize(const void* W, bool w_bf16, int64_t n, int64_t k, const float* codebook,
+                           uint8_t* codes, uint8_t* code8, float* s2, float* mean, void* ws,
+                           hipStream_t stream);
+
+// Encoded weight as the kernels see it.
+struct Nf4View {
+  int64_t n, k;
+  const uint8_t* codes;
+  const uint8_t* code8;
+  const float* s2;
+  const float* mean;
+  const float* codebook;
+};
+
+hipError_t launch_dequant(const Nf4View& w, uint16_t* out, hipStream_t stream);
+
+// Columns of the LoRA "extra" contraction region: [hi | lo] halves of the
+// scaled low-rank activation, padded with zeros to a multiple of 64.
+inline int lora_extra_cols(int r) { return r > 0 ? ((2 * r + 63) / 64) * 64 : 0; }
+
+// out[m, j] = sum_c P[m, c] * Q[j, c]   (P bf16 [M, C], Q bf16 [r, C]), fp32.
+// If split != NULL it also receives [bf16(scale*out) | bf16(scale*out - hi) | 0 ...]
+// rows of lora_extra_cols(r) elements; out may then be NULL. part is workspace.
+size_t rowdot_ws_bytes(int64_t M, int64_t C, int r);
+hipError_t launch_rowdot_impl(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
+                              uint16_t* split, float scale, float* part, hipStream_t stream);
+// B [n, r] -> B^T [r, n]
+hipError_t launch_transpose(const uint16_t* B, int64_t n, int r, uint16_t* BT, hipStream_t stream);
+
+// Column reduction over M in fixed order, for the adapter gradients:
+//   G[c, j] (+)= scale * sum_m P[m, c] * Q[m, j]    P bf16 [M, C], Q fp32 [M, r]
+// written at G[c * g_sc + j * g_sj]. partial (fp32, [splits, C, r]) is workspace.
+int coldot_splits(int64_t M);
+size_t coldot_ws_bytes(int64_t M, int64_t C, int r);
+hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale,
+                         float* G, int64_t g_sc, int64_t g_sj, int accumulate, float* partial,
+                         hipStream_t stream);
+
+// Y = RN_bf16(X W'^T + [sT_hi | sT_lo] [B | B]^T): fused dequant + MFMA GEMM.
+hipError_t launch_gemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* TS,
+                           const uint16_t* B, int r, uint16_t* Y, hipStream_t stream);
+
+// dX = RN_bf16(dY W' + [sU_hi | sU_lo] [A ; A]): fused transposed dequant + MFMA GEMM.
+hipError_t launch_gemm_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const uint16_t* US,
+                          const uint16_t* A, int r, uint16_t* dX, hipStream_t stream);
+
+// Small-M dequant-GEMV: Y = RN_bf16(X W'^T + scale * T B^T), M <= 16.
+hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T,
+                       const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t stream);
+
+hipError_t launch_silu_fwd(const uint16_t* G, const uint16_t* U, uint16_t* H, int64_t count,
+                           hipStream_t stream);
+hipError_t launch_silu_bwd(const uint16_t* G, const uint16_t* U, const uint16_t* dH, uint16_t* dG,
+                           uint16_t* dU, int64_t count, hipStream_t stream);
+
+}  // namespace qlora

@@ -1,0 +1,274 @@
+"""Thin Python binding over libqlora.so (ctypes).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every computation happens in the library's kernels.
+Importing this module loads the library and raises ImportError if it has not
+been built (``python -m bit_nf4_quantized_02_amd.build``) -- there is no
+fallback of any kind.
+
+Names follow the C ABI in include/qlora.h.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bit_nf4_quantized_02_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+BLOCK = 64
+DQ_BLOCK = 256
+MAX_RANK = 128
+DT_BF16, DT_FP32 = 0, 1
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+_f = ctypes.c_float
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("n", _i64), ("k", _i64), ("codes", _vp), ("code8", _vp), ("s2", _vp), ("mean", _vp),
+                ("codebook", _vp)]
+
+
+_W = ctypes.POINTER(_Weight)
+
+_SIGS = {
+    "qlora_status_string": (ctypes.c_char_p, [_int]),
+    "qlora_build_nf4_codebook": (_int, [ctypes.POINTER(_f)]),
+    "qlora_nf4_packed_bytes": (_sz, [_i64, _i64]),
+    "qlora_quantize_workspace_bytes": (_sz, [_i64, _i64]),
+    "qlora_quantize_nf4": (_int, [_vp, _int, _W, _vp, _sz, _vp]),
+    "qlora_dequant": (_int, [_W, _vp, _vp]),
+    "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
+    "qlora_linear_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_bwd": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "qlora_silu_mul_fwd": (_int, [_vp, _vp, _vp, _i64, _vp]),
+    "qlora_silu_mul_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class QLoraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return _lib.qlora_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise QLoraError(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on the GPU, "
+                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+
+
+def _bytes(nbytes: int, device) -> torch.Tensor | None:
+    return torch.empty(max(int(nbytes), 0), dtype=torch.uint8, device=device) if nbytes > 0 else None
+
+
+# --------------------------------------------------------------------------- codebook
+
+def build_nf4_codebook() -> list[float]:
+    """The 16 NF4 levels (host, fp32), ascending."""
+    buf = (_f * 16)()
+    _check(_lib.qlora_build_nf4_codebook(buf), "qlora_build_nf4_codebook")
+    return [buf[i] for i in range(16)]
+
+
+def nf4_packed_bytes(n: int, k: int) -> int:
+    return int(_lib.qlora_nf4_packed_bytes(n, k))
+
+
+def quantize_workspace_bytes(n: int, k: int) -> int:
+    return int(_lib.qlora_quantize_workspace_bytes(n, k))
+
+
+def linear_workspace_bytes(M: int, n: int, k: int, r: int, is_bwd: bool) -> int:
+    return int(_lib.qlora_linear_workspace_bytes(M, n, k, r, int(bool(is_bwd))))
+
+
+# --------------------------------------------------------------------------- weight
+
+@dataclass
+class NF4Weight:
+    """Device buffers of one encoded [n, k] weight (owned by these tensors)."""
+    n: int
+    k: int
+    codes: torch.Tensor      # uint8 [n, k/2]
+    code8: torch.Tensor      # uint8 [n*k/64]
+    s2: torch.Tensor         # fp32  [ceil(nb/256)]
+    mean: torch.Tensor       # fp32  [1]
+    codebook: torch.Tensor   # fp32  [16]
+
+    @staticmethod
+    def empty(n: int, k: int, device="cuda", codebook: torch.Tensor | None = None) -> "NF4Weight":
+        nb = n * k // BLOCK
+        nc = -(-nb // DQ_BLOCK)
+        if codebook is None:
+            codebook = torch.tensor(build_nf4_codebook(), dtype=torch.float32, device=device)
+        return NF4Weight(n, k,
+                         torch.empty((n, k // 2), dtype=torch.uint8, device=device),
+                         torch.empty((nb,), dtype=torch.uint8, device=device),
+                         torch.empty((nc,), dtype=torch.float32, device=device),
+                         torch.empty((1,), dtype=torch.float32, device=device),
+                         codebook)
+
+    def struct(self) -> _Weight:
+        return _Weight(self.n, self.k, self.codes.data_ptr(), self.code8.data_ptr(), self.s2.data_ptr(),
+                       self.mean.data_ptr(), self.codebook.data_ptr())
+
+    def nbytes(self) -> int:
+        return nf4_packed_bytes(self.n, self.k)
+
+
+def quantize_nf4(W: torch.Tensor, out: NF4Weight | None = None, ws: torch.Tensor | None = None,
+                 stream=None) -> NF4Weight:
+    """Encode W ([n, k] bf16 or fp32, on the GPU) as NF4 codes + double-quantized scales."""
+    if W.dim() != 2:
+        raise ValueError("W must be [n, k]")
+    n, k = W.shape
+    dt = {torch.bfloat16: DT_BF16, torch.float32: DT_FP32}.get(W.dtype)
+    if dt is None:
+        raise ValueError("W must be bf16 or fp32")
+    _need(W, W.dtype, (n, k), "W")
+    if out is None:
+        out = NF4Weight.empty(n, k, device=W.device)
+    need = quantize_workspace_bytes(n, k)
+    if ws is None:
+        ws = _bytes(need, W.device)
+    st = out.struct()
+    _check(_lib.qlora_quantize_nf4(_ptr(W), dt, ctypes.byref(st), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(stream)), "qlora_quantize_nf4")
+    return out
+
+
+def dequant(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """bf16 [n, k] expansion, bit-identical to what the GEMM kernels multiply."""
+    if out is None:
+        out = torch.empty((w.n, w.k), dtype=torch.bfloat16, device=w.codes.device)
+    _need(out, torch.bfloat16, (w.n, w.k), "out")
+    st = w.struct()
+    _check(_lib.qlora_dequant(ctypes.byref(st), _ptr(out), _stream(stream)), "qlora_dequant")
+    return out
+
+
+# --------------------------------------------------------------------------- linear
+
+def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, scale: float,
+               Y: torch.Tensor | None = None, T: torch.Tensor | None = None, save_T: bool = True,
+               ws: torch.Tensor | None = None, stream=None):
+    """Y = X W'^T + scale (X A^T) B^T.  Returns (Y, T) with T None unless saved."""
+    M = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(X, torch.bfloat16, (M, w.k), "X")
+    if r:
+        _need(A, torch.bfloat16, (r, w.k), "A")
+        _need(B, torch.bfloat16, (w.n, r), "B")
+    if Y is None:
+        Y = torch.empty((M, w.n), dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, (M, w.n), "Y")
+    if T is None and save_T and r:
+        T = torch.empty((M, r), dtype=torch.float32, device=X.device)
+    if T is not None:
+        _need(T, torch.float32, (M, r), "T")
+    if ws is None:
+        ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, False), X.device)
+    st = w.struct()
+    _check(_lib.qlora_linear_fwd(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), _ptr(Y), _ptr(T),
+                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_fwd")
+    return Y, T
+
+
+def linear_bwd(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY: torch.Tensor,
+               A: torch.Tensor | None, B: torch.Tensor | None, scale: float, need_dX: bool = True,
+               need_dA: bool = True, need_dB: bool = True, dX: torch.Tensor | None = None,
+               dA: torch.Tensor | None = None, dB: torch.Tensor | None = None, accumulate: bool = False,
+               ws: torch.Tensor | None = None, stream=None):
+    """dX = dY W' + s (dY B) A;  dA = s (dY B)^T X;  dB = s dY^T T.  Returns (dX, dA, dB)."""
+    M = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dev = dY.device
+    _need(dY, torch.bfloat16, (M, w.n), "dY")
+    if X is not None:
+        _need(X, torch.bfloat16, (M, w.k), "X")
+    if r:
+        _need(A, torch.bfloat16, (r, w.k), "A")
+        _need(B, torch.bfloat16, (w.n, r), "B")
+    if T is not None:
+        _need(T, torch.float32, (M, r), "T")
+    if need_dX and dX is None:
+        dX = torch.empty((M, w.k), dtype=torch.bfloat16, device=dev)
+    if r and need_dA and dA is None:
+        dA = (torch.zeros if accumulate else torch.empty)((r, w.k), dtype=torch.float32, device=dev)
+    if r and need_dB and dB is None:
+        dB = (torch.zeros if accumulate else torch.empty)((w.n, r), dtype=torch.float32, device=dev)
+    if dX is not None:
+        _need(dX, torch.bfloat16, (M, w.k), "dX")
+    if dA is not None:
+        _need(dA, torch.float32, (r, w.k), "dA")
+    if dB is not None:
+        _need(dB, torch.float32, (w.n, r), "dB")
+    if ws is None:
+        ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, True), dev)
+    st = w.struct()
+    _check(_lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(T), _ptr(dY), M, _ptr(A), _ptr(B), r, float(scale),
+                                 _ptr(dX), _ptr(dA), _ptr(dB), int(bool(accumulate)), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+# --------------------------------------------------------------------------- MLP join
+
+def silu_mul_fwd(G: torch.Tensor, U: torch.Tensor, H: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _need(U, torch.bfloat16, G.shape, "Up")
+    _need(G, torch.bfloat16, G.shape, "G")
+    if H is None:
+        H = torch.empty_like(G)
+    _check(_lib.qlora_silu_mul_fwd(_ptr(G), _ptr(U), _ptr(H), G.numel(), _stream(stream)), "qlora_silu_mul_fwd")
+    return H
+
+
+def silu_mul_bwd(G: torch.Tensor, U: torch.Tensor, dH: torch.Tensor, stream=None):
+    for t, nme in ((G, "G"), (U, "Up"), (dH, "dH")):
+        _need(t, torch.bfloat16, G.shape, nme)
+    dG = torch.empty_like(G)
+    dU = torch.empty_like(G)
+    _check(_lib.qlora_silu_mul_bwd(_ptr(G), _ptr(U), _ptr(dH), _ptr(dG), _ptr(dU), G.numel(), _stream(stream)),
+           "qlora_silu_mul_bwd")
+    return dG, dU
+
+
+def raw():
+    """The ctypes handle, for tests that call the C ABI directly."""
+    return _lib

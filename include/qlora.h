@@ -1,0 +1,208 @@
+/*
+ * qlora.h — C ABI of libqlora.so: the frozen-base NF4 linear layer with a
+ * LoRA branch, for AMD Instinct MI355X (gfx950).
+ *
+ *   Y  = X W'^T + s (X A^T) B^T          forward
+ *   dX = dY W' + s (dY B) A              backward through the frozen base
+ *   dA = s (dY B)^T X,  dB = s dY^T (X A^T)   adapter gradients (no dW)
+ *
+ * W' is the bf16 expansion of a weight stored as 4-bit NF4 codes in blocks of
+ * 64 consecutive weights, each block with an absmax scale that is itself
+ * quantized to 8 bits ("double quantization").
+ *
+ * Sources (web pages on QLoRA, cited by title and section):
+ *   [QQ] "QLoRA: Quantized Low-Rank Adaptation" (completesystemdesign.dev):
+ *        three-piece summary (4-bit storage, 16-bit compute on 64-weight
+ *        blocks expanded on the fly, learning only in the adapter), the worked
+ *        8-weight block, "NF4: a 4-bit format matched to weight statistics",
+ *        the double-quantization paragraph, "Batched 4-bit matmuls".
+ *   [QX] "QLoRA Explained: Fine-Tune 70B+ LLMs on a Single GPU" (gamut.so):
+ *        "4-Bit NormalFloat (NF4) Quantization", "Double Quantization",
+ *        "Step 3: Configure and Apply LoRA Adapters".
+ *   [WQ] "What is QLoRA?" (qubittool.com), "Key Characteristics".
+ *
+ * Conventions shared by every call
+ *   - Memory: every pointer marked (device) is device memory owned by the
+ *     caller; (host) is host memory. The library never allocates or frees,
+ *     keeps no state between calls, and writes only the outputs and the
+ *     workspace it is given.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream). Every device call only enqueues work on that stream and
+ *     returns; none synchronizes the host.
+ *   - Layouts: all matrices are dense row-major with the last index
+ *     contiguous and no padding: X [M,K], Y [M,N], dY [M,N], dX [M,K],
+ *     A [r,K], B [N,r], T [M,r], dA [r,K], dB [N,r]. W is [N,K] (out x in),
+ *     as a linear layer stores it.
+ *   - Types: X, Y, dY, dX, A, B are bf16 (IEEE binary32 truncated to 16 bits,
+ *     stored as uint16). T, dA, dB are fp32. bf16 outputs are rounded once,
+ *     to nearest-even, from an fp32 accumulator that already includes the
+ *     LoRA term.
+ *   - Alignment: every device pointer must be 16-byte aligned.
+ *   - Errors: arguments are checked on the host before anything is enqueued;
+ *     on any error nothing is launched and a negative qlora_status returns.
+ *     A failed launch returns QLORA_ERR_HIP. No C++ exception crosses the
+ *     ABI. qlora_status_string() names each status.
+ *   - Sizes: M = 0 is a no-op that returns QLORA_OK. r = 0 means no LoRA
+ *     branch (A, B, T, dA, dB may then be NULL).
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_BLOCK 64      /* weights per first-level block [QQ] */
+#define QLORA_DQ_BLOCK 256  /* first-level scales per second-level block */
+#define QLORA_MAX_RANK 128  /* largest supported LoRA rank */
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = -1, /* NULL where a buffer is needed, bad enum, misaligned */
+  QLORA_ERR_SHAPE = -2,       /* K % 64 != 0, negative sizes, rank out of range */
+  QLORA_ERR_UNSUPPORTED = -3, /* valid request this build does not implement */
+  QLORA_ERR_WORKSPACE = -4,   /* workspace smaller than the matching *_workspace_bytes() */
+  QLORA_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} qlora_status;
+
+typedef enum { QLORA_DT_BF16 = 0, QLORA_DT_FP32 = 1 } qlora_dtype;
+
+/*
+ * One encoded weight W [n, k]. All pointers are (device), owned by the caller.
+ * Block b covers the 64 weights W[b / (k/64)][64 (b % (k/64)) ...], i.e. the
+ * row-major flattening cut into runs of 64; blocks never straddle rows.
+ *   codes    [n*k/2]  bytes; weight 2t in the low nibble of byte t, weight
+ *                     2t+1 in the high nibble; a code indexes `codebook`.
+ *   code8    [n*k/64] bytes; OCP FP8 E4M3 bit pattern of block b's centred,
+ *                     scaled absmax [QX "Double Quantization"].
+ *   s2       [ceil(n*k/64/256)] fp32 second-level scales, one per 256 blocks.
+ *   mean     [1]      fp32 mean of all block absmax values.
+ *   codebook [16]     fp32 NF4 levels, ascending (from
+ *                     qlora_build_nf4_codebook, copied to the device).
+ * Block b's scale is c'_b = RN32(RN32(fp8(code8[b]) * s2[b/256]) + mean[0])
+ * (two separately rounded fp32 operations) and its weight i expands to
+ * w' = RN_bf16(RN32(codebook[code] * c'_b)).
+ */
+typedef struct {
+  int64_t n;
+  int64_t k;
+  uint8_t *codes;
+  uint8_t *code8;
+  float *s2;
+  float *mean;
+  const float *codebook;
+} qlora_nf4_weight;
+
+/* Name of a status code (static string, never NULL). */
+const char *qlora_status_string(int status);
+
+/*
+ * The 16 NF4 levels into levels_out (host, 16 floats), ascending: index 0 is
+ * -1, index 7 is exactly 0, index 15 is +1 [QQ "NF4: a 4-bit format matched
+ * to weight statistics"; QX "4-Bit NormalFloat (NF4) Quantization"]. Eight
+ * positive levels are standard-normal quantiles at the probabilities
+ * 1/2 + (j/8)(delta - 1/2), j = 1..8, seven negative levels mirror the
+ * quantiles at 1/2 + (j/7)(delta - 1/2), j = 1..7, with
+ * delta = ((1 - 1/30) + (1 - 1/32)) / 2; all are divided by the quantile of
+ * delta, evaluated in fp64 and rounded once to fp32. Pure host code; no HIP
+ * call. Errors: INVALID_ARG if levels_out is NULL.
+ */
+qlora_status qlora_build_nf4_codebook(float *levels_out);
+
+/* Bytes of the encoded weight (codes + code8 + s2 + mean, codebook excluded).
+ * Returns 0 if k % 64 != 0 or a size is not positive. */
+size_t qlora_nf4_packed_bytes(int64_t n, int64_t k);
+
+/* Workspace bytes qlora_quantize_nf4 needs for an [n, k] weight (0 on bad shape). */
+size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
+
+/*
+ * Encode W (device, [n, k] row-major, bf16 or fp32 per w_dtype, finite) into
+ * the buffers of *out (out->n, out->k must equal the shape; out->codebook must
+ * hold the 16 levels) [QQ worked 8-weight block and "NF4: ..."; QX "Double
+ * Quantization"]:
+ *   c_b   = max |w| over block b (fp32, exact);
+ *   code  = nearest level to w / c_b, ties to the lower level, evaluated as
+ *           #{j : w > (L_j + L_{j+1})/2 * c_b} in exact fp64; c_b = 0 gives 7;
+ *   mean  = (sum of c_b, added in fp64 left to right within each run of 256
+ *           blocks, then run totals left to right) / nb, rounded to fp32;
+ *   d_b   = RN32(c_b - mean); s2_j = RN32(max |d_b| over run j / 448);
+ *   code8 = E4M3 pattern of the finite E4M3 value nearest to d_b / s2_j, ties
+ *           to the lower value, -0 never produced; s2_j = 0 gives 0x00.
+ * ws (device) must hold qlora_quantize_workspace_bytes(n, k) bytes. The result
+ * is deterministic and independent of the launch configuration.
+ * Errors: INVALID_ARG (NULL/misaligned pointers, bad dtype), SHAPE (k % 64,
+ * n or k < 1, shape mismatch), WORKSPACE, HIP.
+ */
+qlora_status qlora_quantize_nf4(const void *W, int w_dtype, const qlora_nf4_weight *out,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Expand the whole weight to bf16: out (device, [n, k] bf16) receives exactly
+ * the values the forward and backward kernels feed to the matrix cores
+ * [QQ three-piece summary, piece 2 (compute in 16 bits)].
+ * Errors: INVALID_ARG, SHAPE, HIP.
+ */
+qlora_status qlora_dequant(const qlora_nf4_weight *w, void *out, void *stream);
+
+/* Workspace bytes for qlora_linear_fwd (is_bwd = 0) or qlora_linear_bwd
+ * (is_bwd = 1) at this M, weight shape and rank (0 on bad arguments). */
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd);
+
+/*
+ * Forward [QQ three-piece summary and the storage/compute/learning diagram]:
+ *   T = X A^T (fp32, written to T_save if not NULL),
+ *   Y = RN_bf16( X W'^T + scale * T B^T ), accumulated in fp32.
+ * X (device) [M, k] bf16; A (device) [r, k] bf16; B (device) [n, r] bf16;
+ * Y (device) [M, n] bf16; T_save (device, nullable) [M, r] fp32;
+ * scale = alpha / r, the LoRA scale [QX "Step 3"]. Small M (<= 16) uses a
+ * bandwidth-oriented dequant-GEMV; larger M a matrix-core GEMM that expands
+ * each 64-block to bf16 in on-chip memory.
+ * ws (device) must hold qlora_linear_workspace_bytes(M, n, k, r, 0) bytes.
+ * Errors: INVALID_ARG, SHAPE, WORKSPACE, HIP.
+ */
+qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const void *X, int64_t M,
+                              const void *A, const void *B, int r, float scale,
+                              void *Y, float *T_save, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward [WQ "Key Characteristics": backpropagation through quantized
+ * weights, adapters trained in full precision; QQ: the base gets no gradient]:
+ *   U  = dY B                          (fp32, internal)
+ *   dX = RN_bf16( dY W' + scale * U A ) (fp32 accumulate)   if dX != NULL
+ *   dA = scale * U^T X                  (fp32, [r, k])       if dA != NULL
+ *   dB = scale * dY^T T                 (fp32, [n, r])       if dB != NULL
+ * T_saved (device, nullable) is the forward's T; if NULL it is recomputed from
+ * X and A. X is needed when dA != NULL or T_saved == NULL. accumulate = 0
+ * overwrites dA and dB, 1 adds to them (gradient accumulation). There is no
+ * weight gradient. dA and dB are reduced in a fixed order: reruns are
+ * bit-identical.
+ * ws (device) must hold qlora_linear_workspace_bytes(M, n, k, r, 1) bytes.
+ * Errors: INVALID_ARG, SHAPE, WORKSPACE, HIP.
+ */
+qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const void *X, const float *T_saved,
+                              const void *dY, int64_t M, const void *A, const void *B, int r,
+                              float scale, void *dX, float *dA, float *dB, int accumulate,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The gated-MLP join used between the gate/up and down linears of the MLP
+ * workloads (not a QLoRA operation; provided so a whole MLP block runs on
+ * this library):
+ *   forward:  H = RN_bf16( silu(G) * Up ),  silu(g) = g / (1 + exp(-g))
+ *   backward: dG = RN_bf16( dH * Up * silu'(g) ), dUp = RN_bf16( dH * silu(g) )
+ * All tensors (device) bf16 with `count` elements; math in fp32.
+ * Errors: INVALID_ARG, SHAPE, HIP.
+ */
+qlora_status qlora_silu_mul_fwd(const void *G, const void *Up, void *H, int64_t count, void *stream);
+qlora_status qlora_silu_mul_bwd(const void *G, const void *Up, const void *dH, void *dG, void *dUp,
+                                int64_t count, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */
