@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Throughput of the QLoRA NF4 linear (forward + backward) on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  forward   T = X A^T (+ bf16 hi/lo split)            qlora_lowrank_project
+            Y = X W'^T + s T B^T (fused dequant GEMM)   qlora_nf4_gemm_fwd / _gemv_fwd
+  backward  U = dY B (+ split)                          qlora_lowrank_project
+            dX = dY W' + s U A (fused dequant GEMM)     qlora_nf4_gemm_dx
+            dA = s U^T X, dB = s dY^T T                 qlora_lowrank_grad
+These are exactly the calls qlora_linear_fwd / qlora_linear_bwd make, issued
+one by one so each can be bracketed by HIP events on the launch stream.
+Inputs are resident in HBM when the timed region starts; the weight is
+encoded once before it (the encoder is reported separately).
+
+Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
+tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
+(1: 1024^2 at M = 16; 3: 7B MLP block chained through SiLU; 4: 70B-class
+decode GEMVs). Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from bit_nf4_quantized_02_amd import synth  # noqa: E402
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s and packed-weight GB/s vs roofline, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
+    p.add_argument("--json", default=None, help="also write the JSON line to this file")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- one linear
+
+class LinearPlan:
+    """Device tensors and prebuilt C-ABI calls of one QLoRA linear."""
+
+    def __init__(self, q, li: synth.LinearInputs, backward: bool = True, X=None, dY=None):
+        dev = "cuda"
+        m = li.meta
+        self.m, self.n, self.k, self.r, self.s = m["m"], m["n"], m["k"], m["r"], li.scale
+        self.li = li
+        M, N, K, r = self.m, self.n, self.k, self.r
+        self.W = q.quantize_nf4(li.W.to(dev))
+        self.X = li.X.to(dev) if X is None else X
+        self.dY = li.dY.to(dev) if dY is None else dY
+        self.A = li.A.to(dev).contiguous()
+        self.B = li.B.to(dev).contiguous()
+        xc = q.lowrank_split_cols(r)
+        self.T = torch.empty((M, r), dtype=torch.float32, device=dev)
+        self.TS = torch.empty((M, xc), dtype=torch.bfloat16, device=dev)
+        self.Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.U = torch.empty((M, r), dtype=torch.float32, device=dev)
+        self.US = torch.empty((M, xc), dtype=torch.bfloat16, device=dev)
+        self.dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+        self.dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+        lib = q.raw()
+        pw = max(lib.qlora_lowrank_project_workspace_bytes(M, K, r), lib.qlora_lowrank_project_workspace_bytes(M, N, r))
+        gw = max(lib.qlora_lowrank_grad_workspace_bytes(M, K, r), lib.qlora_lowrank_grad_workspace_bytes(M, N, r))
+        self.ws = torch.empty(max(pw, gw, 256), dtype=torch.uint8, device=dev)
+        st = q._stream()
+        P = q._ptr
+        self.wst = self.W.struct()
+        wref = q.ctypes.byref(self.wst)
+        ws, wsn = P(self.ws), self.ws.numel()
+        self.fwd, self.bwd = [], []
+        if M <= 16:
+            self.fwd.append(("lowrank_project_T", 2 * M * K * r,
+                             q.Call("qlora_lowrank_project", P(self.X), M, K, P(self.A), 0, r, self.s, P(self.T), None,
+                                    ws, wsn, st)))
+            self.fwd.append(("nf4_gemv_fwd", 2 * M * N * K + 2 * M * N * r,
+                             q.Call("qlora_nf4_gemv_fwd", wref, P(self.X), M, P(self.T), P(self.B), r, self.s,
+                                    P(self.Y), st, keep=(self.wst,))))
+        else:
+            self.fwd.append(("lowrank_project_T", 2 * M * K * r,
+                             q.Call("qlora_lowrank_project", P(self.X), M, K, P(self.A), 0, r, self.s, P(self.T),
+                                    P(self.TS), ws, wsn, st)))
+            self.fwd.append(("nf4_gemm_fwd", 2 * M * N * K + 2 * M * N * r,
+                             q.Call("qlora_nf4_gemm_fwd", wref, P(self.X), M, P(self.TS), P(self.B), r, P(self.Y), st,
+                                    keep=(self.wst,))))
+        if backward:
+            self.bwd.append(("lowrank_project_U", 2 * M * N * r,
+                             q.Call("qlora_lowrank_project", P(self.dY), M, N, P(self.B), 1, r, self.s, P(self.U),
+                                    P(self.US), ws, wsn, st)))
+            self.bwd.append(("nf4_gemm_dx", 2 * M * N * K + 2 * M * K * r,
+                             q.Call("qlora_nf4_gemm_dx", wref, P(self.dY), M, P(self.US), P(self.A), r, P(self.dX), st,
+                                    keep=(self.wst,))))
+            self.bwd.append(("lowrank_grad_dA", 2 * M * K * r,
+                             q.Call("qlora_lowrank_grad", P(self.X), M, K, P(self.U), r, self.s, P(self.dA), 0, 0, ws,
+                                    wsn, st)))
+            self.bwd.append(("lowrank_grad_dB", 2 * M * N * r,
+                             q.Call("qlora_lowrank_grad", P(self.dY), M, N, P(self.T), r, self.s, P(self.dB), 1, 0, ws,
+                                    wsn, st)))
+
+    @property
+    def packed_bytes(self):
+        return self.W.nbytes()
+
+
+# ----------------------------------------------------------------------------- workloads
+
+class Workload:
+    def __init__(self, cid: int, q):
+        self.cid = cid
+        self.c = synth.CONFIGS[cid]
+        c = self.c
+        self.pieces = []      # (name, flops, call)
+        self.plans = []
+        self.passes_bytes = 0  # packed-weight bytes streamed per step
+        if cid in (1, 2):
+            lin = c.linears[0]
+            li = synth.linear_inputs(cid, 0, 0, lin.n, lin.k, c.m[0], c.r, c.scale, sigma=c.sigma)
+            p = LinearPlan(q, li)
+            self.plans.append(p)
+            self.pieces = p.fwd + p.bwd
+            self.passes_bytes = 2 * p.packed_bytes
+            self.desc = dict(workload=c.title, M=c.m[0], N=lin.n, K=lin.k, r=c.r, alpha=c.alpha, passes="fwd+bwd")
+        elif cid == 3:
+            M = c.m[0]
+            gate, up, down = c.linears
+            X = synth.normal_bf16((M, gate.k), 1.0, cid, 0, synth.T_X).cuda()
+            lg = synth.linear_inputs(cid, 0, 0, gate.n, gate.k, M, c.r, c.scale, sigma=c.sigma,
+                                     outlier_frac=c.outlier_frac)
+            lu = synth.linear_inputs(cid, 0, 1, up.n, up.k, M, c.r, c.scale, sigma=c.sigma, outlier_frac=c.outlier_frac)
+            ld = synth.linear_inputs(cid, 0, 2, down.n, down.k, M, c.r, c.scale, sigma=c.sigma,
+                                     outlier_frac=c.outlier_frac)
+            H = torch.empty((M, gate.n), dtype=torch.bfloat16, device="cuda")
+            dG = torch.empty_like(H)
+            dU = torch.empty_like(H)
+            pd = LinearPlan(q, ld, X=H)
+            pg = LinearPlan(q, lg, X=X, dY=dG)
+            pu = LinearPlan(q, lu, X=X, dY=dU)
+            cnt = M * gate.n
+            st = q._stream()
+            P = q._ptr
+            silu_f = q.Call("qlora_silu_mul_fwd", P(pg.Y), P(pu.Y), P(H), cnt, st)
+            silu_b = q.Call("qlora_silu_mul_bwd", P(pg.Y), P(pu.Y), P(pd.dX), P(dG), P(dU), cnt, st)
+            ren = lambda pl, tag: [(f"{tag}.{nme}", f, cl) for nme, f, cl in pl]  # noqa: E731
+            self.pieces = (ren(pg.fwd, "gate") + ren(pu.fwd, "up") + [("silu_mul_fwd", 0, silu_f)] + ren(pd.fwd, "down")
+                           + ren(pd.bwd, "down") + [("silu_mul_bwd", 0, silu_b)] + ren(pu.bwd, "up")
+                           + ren(pg.bwd, "gate"))
+            self.plans = [pg, pu, pd]
+            self.passes_bytes = 2 * sum(p.packed_bytes for p in self.plans)
+            self.desc = dict(workload=c.title, M=M, r=c.r, alpha=c.alpha, passes="fwd+bwd, chained through SiLU")
+        elif cid == 4:
+            for li_i, lin in enumerate(c.linears):
+                for M in c.m:
+                    li = synth.linear_inputs(cid, 0, li_i, lin.n, lin.k, M, c.r, c.scale, sigma=c.sigma)
+                    p = LinearPlan(q, li, backward=False)
+                    self.plans.append(p)
+                    self.pieces += [(f"{lin.name}.M{M}.{nme}", f, cl) for nme, f, cl in p.fwd]
+                    self.passes_bytes += p.packed_bytes
+            self.desc = dict(workload=c.title, M=list(c.m), r=c.r, alpha=c.alpha, passes="fwd")
+        self.flops = sum(f for _, f, _ in self.pieces)
+
+    def dominant_kernels(self):
+        return [nme for nme, _, _ in self.pieces if "gemm" in nme or "gemv" in nme]
+
+
+def time_steps(wl: Workload, steps: int, warmup: int):
+    calls = [cl for _, _, cl in wl.pieces]
+    npc = len(calls)
+    for _ in range(warmup):
+        for cl in calls:
+            cl()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(npc + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev = evs[s]
+        ev[0].record()
+        for i, cl in enumerate(calls):
+            cl()
+            ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    per = np.zeros(npc)
+    for s in range(steps):
+        for i in range(npc):
+            per[i] += evs[s][i].elapsed_time(evs[s][i + 1])
+    per_ms = per / steps
+    ev_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]))
+    return wall * 1e3, ev_step, per_ms
+
+
+def gemm_traffic(kernel_name: str):
+    """Measured HBM bytes per launch from the committed counter summary, used
+    only while the kernel source still matches the one the counters came from."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        src = os.path.join(ROOT, "bit_nf4_quantized_02_amd", "csrc", data["source"])
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        ent = data["kernels"].get(kernel_name)
+        if ent is None or ent.get("source_sha256") != h:
+            return None
+        return float(ent["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+# ----------------------------------------------------------------------------- CPU oracle leg
+
+def cpu_baseline(wl: Workload, target_s: float):
+    """The oracle as it stands, timed on this host's cores on a bounded sample
+    of the same workload: whole steps of the first linear (all M tokens),
+    repeated until about target_s seconds; the weight's oracle encoding is
+    made once beforehand and not timed."""
+    from oracle import linear as olin
+    from oracle import nf4 as onf4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"]
+                      or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    p = wl.plans[0]
+    li = p.li
+    ow = onf4.NF4Weight(li.W.float().numpy())
+    # the inputs this linear actually consumed on the GPU (for chained
+    # workloads X or dY come from the previous GPU step)
+    X, A, B, dY = (t.float().cpu().numpy().astype(np.float64) for t in (p.X, li.A, li.B, p.dY))
+    backward = len(p.bwd) > 0
+    flops = sum(f for _, f, _ in p.fwd + p.bwd)
+    n, spent = 0, 0.0
+    out = None
+    while (spent < target_s and n < 20) or n == 0:
+        t0 = time.perf_counter()
+        cp = onf4.decode_scales(ow.code8, ow.s2, ow.mean)
+        Wd = onf4.dequant(ow.codes, cp, ow.levels)
+        Y, T = olin.linear_fwd(X, Wd, A, B, li.scale)
+        if backward:
+            dX, dA, dB, _ = olin.linear_bwd(X, Wd, A, B, li.scale, dY, T)
+            out = (Y, dX, dA, dB)
+        else:
+            out = (Y,)
+        spent += time.perf_counter() - t0
+        n += 1
+    # parity of the timed GPU outputs against this sample
+    got = [p.Y] + ([p.dX, p.dA, p.dB] if backward else [])
+    errs = {nme: olin.relerr(g.float().cpu().numpy(), o) for nme, g, o in zip(["Y", "dX", "dA", "dB"], got, out)}
+    return dict(value=flops * n / spent / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{n} whole fwd{'+bwd' if backward else ''} step(s) of linear '{wl.c.linears[0].name}' "
+                       f"(M={p.m}, N={p.n}, K={p.k}, r={p.r}): numpy fp64 products, bf16 expansion of the "
+                       f"encoded weight each step; {spent:.1f} s total",
+                seconds=spent, parity_relerr=errs)
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the path shards by data parallelism "
+                                   "(see DESIGN.md); --gpus must be 1"}), flush=True)
+        sys.exit(2)
+    from bit_nf4_quantized_02_amd import qlora as q
+    torch.cuda.set_device(0)
+    log(f"bench: building workload config {args.config}")
+    wl = Workload(args.config, q)
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
+    ms_wall, ms_ev, per_ms = time_steps(wl, args.steps, args.warmup)
+    names = [nme for nme, _, _ in wl.pieces]
+    flops = [f for _, f, _ in wl.pieces]
+    value = wl.flops / (ms_wall * 1e-3) / 1e12
+    gbps = wl.passes_bytes / (ms_wall * 1e-3) / 1e9
+    breakdown = {nme: round(t * 1e3, 2) for nme, t in zip(names, per_ms)}
+
+    # dominant kernel: the slowest fused NF4 kernel
+    dom = max(wl.dominant_kernels(), key=lambda nme: per_ms[names.index(nme)])
+    i = names.index(dom)
+    dom_ms = per_ms[i]
+    gemv = "gemv" in dom
+    base = dom.split(".")[-1]
+    if gemv:
+        pl = [p for p in wl.plans if any(c is wl.pieces[i][2] for _, _, c in p.fwd)][0]
+        achieved = pl.packed_bytes / (dom_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBPS, 4))
+    else:
+        achieved = flops[i] / (dom_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
+    roof["traffic"] = gemm_traffic(f"config{args.config}.{base}")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,sigma) weights, N(0,1) activations; no dataset)",
+        "config": wl.desc,
+        "packed_weight_GBps": round(gbps, 1),
+        "ms_per_step_events": round(ms_ev, 4),
+        "flops_per_step": wl.flops,
+        "breakdown_us": breakdown,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.json:
+        with open(args.json, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

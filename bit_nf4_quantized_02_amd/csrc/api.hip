@@ -45,47 +45,70 @@ struct Carver {
 
 bool small_m(int64_t M) { return M <= 16; }
 
-size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver* c,
-              float** T, uint16_t** TS, float** part) {
-  Carver local(nullptr);
-  Carver& cv = c ? *c : local;
-  float* t = nullptr;
-  uint16_t* ts = nullptr;
-  float* pt = nullptr;
+// ---- building-block workspaces
+size_t project_ws(int64_t M, int64_t C, int r) {
+  return align256((size_t)C * r * 2) + rowdot_ws_bytes(M, C, r);
+}
+size_t grad_ws(int64_t M, int64_t C, int r) { return coldot_ws_bytes(M, C, r); }
+
+// T = P Q^T (q_layout 0, Q [r, C]) or P Q (q_layout 1, Q [C, r]); optional split.
+hipError_t do_project(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r, float scale,
+                      float* out, uint16_t* split, void* ws, hipStream_t st) {
+  Carver cv(ws);
+  uint16_t* QT = cv.take<uint16_t>((size_t)C * r * 2);
+  float* part = cv.take<float>(rowdot_ws_bytes(M, C, r));
+  const uint16_t* q = Q;
+  if (q_layout == 1) {
+    const hipError_t e = launch_transpose(Q, C, r, QT, st);
+    if (e != hipSuccess) return e;
+    q = QT;
+  }
+  return launch_rowdot_impl(P, M, C, q, r, out, split, scale, part, st);
+}
+
+hipError_t do_grad(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,
+                   int g_layout, int accumulate, void* ws, hipStream_t st) {
+  const int64_t g_sc = g_layout == 0 ? 1 : r;
+  const int64_t g_sj = g_layout == 0 ? C : 1;
+  return launch_coldot(P, M, C, Q, r, scale, G, g_sc, g_sj, accumulate, static_cast<float*>(ws), st);
+}
+
+// ---- whole-layer workspaces (layouts shared by the size query and the call)
+struct FwdWs {
+  float* T = nullptr;
+  uint16_t* TS = nullptr;
+  void* proj = nullptr;
+};
+
+size_t fwd_ws(int64_t M, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o) {
   if (r > 0) {
     if (small_m(M)) {
-      if (!have_tsave) t = cv.take<float>((size_t)M * r * 4);
+      if (!have_tsave) o.T = cv.take<float>((size_t)M * r * 4);
     } else {
-      ts = cv.take<uint16_t>((size_t)M * lora_extra_cols(r) * 2);
+      o.TS = cv.take<uint16_t>((size_t)M * lora_extra_cols(r) * 2);
     }
-    pt = cv.take<float>(rowdot_ws_bytes(M, k, r));
+    o.proj = cv.take<char>(project_ws(M, k, r));
   }
-  (void)n;
-  if (T) *T = t;
-  if (TS) *TS = ts;
-  if (part) *part = pt;
   return cv.used;
 }
 
 struct BwdWs {
   float* T = nullptr;
-  uint16_t* BT = nullptr;
   float* U = nullptr;
   uint16_t* US = nullptr;
-  float* part = nullptr;
-  float* colpart = nullptr;
+  void* proj = nullptr;
+  void* grad = nullptr;
 };
 
 size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o) {
   if (r > 0) {
     if (!have_tsaved) o.T = cv.take<float>((size_t)M * r * 4);
-    o.BT = cv.take<uint16_t>((size_t)n * r * 2);
     o.U = cv.take<float>((size_t)M * r * 4);
     o.US = cv.take<uint16_t>((size_t)M * lora_extra_cols(r) * 2);
-    const size_t p1 = rowdot_ws_bytes(M, n, r), p2 = rowdot_ws_bytes(M, k, r);
-    o.part = cv.take<float>(p1 > p2 ? p1 : p2);
-    const size_t c1 = coldot_ws_bytes(M, k, r), c2 = coldot_ws_bytes(M, n, r);
-    o.colpart = cv.take<float>(c1 > c2 ? c1 : c2);
+    const size_t p1 = project_ws(M, n, r), p2 = project_ws(M, k, r);
+    o.proj = cv.take<char>(p1 > p2 ? p1 : p2);
+    const size_t g1 = grad_ws(M, k, r), g2 = grad_ws(M, n, r);
+    o.grad = cv.take<char>(g1 > g2 ? g1 : g2);
   }
   return cv.used;
 }
@@ -140,10 +163,86 @@ qlora_status qlora_dequant(const qlora_nf4_weight* w, void* out, void* stream) {
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
   if (M < 0 || n < 1 || k < 1 || k % QLORA_BLOCK || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (M == 0) return 0;
-  if (!is_bwd) return fwd_ws(M, n, k, r, /*have_tsave=*/false, nullptr, nullptr, nullptr, nullptr);
   Carver cv(nullptr);
+  if (!is_bwd) {
+    FwdWs o;
+    return fwd_ws(M, k, r, /*have_tsave=*/false, cv, o);
+  }
   BwdWs o;
   return bwd_ws(M, n, k, r, /*have_tsaved=*/false, cv, o);
+}
+
+int qlora_lowrank_split_cols(int r) { return (r < 0 || r > QLORA_MAX_RANK) ? 0 : lora_extra_cols(r); }
+
+size_t qlora_lowrank_project_workspace_bytes(int64_t M, int64_t C, int r) {
+  if (M < 1 || C < 1 || r < 1 || r > QLORA_MAX_RANK) return 0;
+  return project_ws(M, C, r);
+}
+
+qlora_status qlora_lowrank_project(const void* P, int64_t M, int64_t C, const void* Q, int q_layout, int r,
+                                   float scale, float* out, void* split, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || C < 1 || r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (q_layout != 0 && q_layout != 1) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  if (!P || !Q || !aligned16(P) || !aligned16(Q)) return QLORA_ERR_INVALID_ARG;
+  if ((out && !aligned16(out)) || (split && !aligned16(split)) || (!out && !split)) return QLORA_ERR_INVALID_ARG;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < project_ws(M, C, r)) return QLORA_ERR_WORKSPACE;
+  return hip_status(do_project(static_cast<const uint16_t*>(P), M, C, static_cast<const uint16_t*>(Q), q_layout, r,
+                               scale, out, static_cast<uint16_t*>(split), ws, static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_nf4_gemm_fwd(const qlora_nf4_weight* w, const void* X, int64_t M, const void* split,
+                                const void* B, int r, void* Y, void* stream) {
+  const qlora_status s = check_weight(w);
+  if (s != QLORA_OK) return s;
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if (!X || !Y || !aligned16(X) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!split || !B || !aligned16(split) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
+  return hip_status(launch_gemm_fwd(view_of(w), static_cast<const uint16_t*>(X), M,
+                                    static_cast<const uint16_t*>(split), static_cast<const uint16_t*>(B), r,
+                                    static_cast<uint16_t*>(Y), static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_nf4_gemm_dx(const qlora_nf4_weight* w, const void* dY, int64_t M, const void* split,
+                               const void* A, int r, void* dX, void* stream) {
+  const qlora_status s = check_weight(w);
+  if (s != QLORA_OK) return s;
+  if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if (!dY || !dX || !aligned16(dY) || !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!split || !A || !aligned16(split) || !aligned16(A))) return QLORA_ERR_INVALID_ARG;
+  return hip_status(launch_gemm_dx(view_of(w), static_cast<const uint16_t*>(dY), M,
+                                   static_cast<const uint16_t*>(split), static_cast<const uint16_t*>(A), r,
+                                   static_cast<uint16_t*>(dX), static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight* w, const void* X, int64_t M, const float* T, const void* B,
+                                int r, float scale, void* Y, void* stream) {
+  const qlora_status s = check_weight(w);
+  if (s != QLORA_OK) return s;
+  if (M < 0 || M > 16 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if (!X || !Y || !aligned16(X) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!T || !B || !aligned16(T) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
+  return hip_status(launch_gemv(view_of(w), static_cast<const uint16_t*>(X), M, T, static_cast<const uint16_t*>(B),
+                                r, scale, static_cast<uint16_t*>(Y), static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r) {
+  if (M < 1 || C < 1 || r < 1 || r > QLORA_MAX_RANK) return 0;
+  return grad_ws(M, C, r);
+}
+
+qlora_status qlora_lowrank_grad(const void* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,
+                                int g_layout, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || C < 1 || r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if ((g_layout != 0 && g_layout != 1) || (accumulate != 0 && accumulate != 1)) return QLORA_ERR_INVALID_ARG;
+  if (M == 0) return QLORA_OK;
+  if (!G || !aligned16(G) || !P || !Q || !aligned16(P) || !aligned16(Q)) return QLORA_ERR_INVALID_ARG;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < grad_ws(M, C, r)) return QLORA_ERR_WORKSPACE;
+  return hip_status(do_grad(static_cast<const uint16_t*>(P), M, C, Q, r, scale, G, g_layout, accumulate, ws,
+                            static_cast<hipStream_t>(stream)));
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A, const void* B,
@@ -155,15 +254,16 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t 
   if (!X || !Y || !aligned16(X) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
   if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
   if (T_save && !aligned16(T_save)) return QLORA_ERR_INVALID_ARG;
-  const size_t need = fwd_ws(M, w->n, w->k, r, T_save != nullptr, nullptr, nullptr, nullptr, nullptr);
-  if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
-
+  {
+    Carver probe(nullptr);
+    FwdWs tmp;
+    const size_t need = fwd_ws(M, w->k, r, T_save != nullptr, probe, tmp);
+    if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
-  float* Tws = nullptr;
-  uint16_t* TS = nullptr;
-  float* part = nullptr;
-  fwd_ws(M, w->n, w->k, r, T_save != nullptr, &cv, &Tws, &TS, &part);
+  FwdWs o;
+  fwd_ws(M, w->k, r, T_save != nullptr, cv, o);
   const Nf4View v = view_of(w);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* a = static_cast<const uint16_t*>(A);
@@ -171,12 +271,12 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t 
   uint16_t* y = static_cast<uint16_t*>(Y);
   hipError_t e = hipSuccess;
   if (small_m(M)) {
-    float* T = T_save ? T_save : Tws;
-    if (r > 0) e = launch_rowdot_impl(x, M, w->k, a, r, T, nullptr, scale, part, st);
+    float* T = T_save ? T_save : o.T;
+    if (r > 0) e = do_project(x, M, w->k, a, 0, r, scale, T, nullptr, o.proj, st);
     if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, scale, y, st);
   } else {
-    if (r > 0) e = launch_rowdot_impl(x, M, w->k, a, r, T_save, TS, scale, part, st);
-    if (e == hipSuccess) e = launch_gemm_fwd(v, x, M, TS, b, r, y, st);
+    if (r > 0) e = do_project(x, M, w->k, a, 0, r, scale, T_save, o.TS, o.proj, st);
+    if (e == hipSuccess) e = launch_gemm_fwd(v, x, M, o.TS, b, r, y, st);
   }
   return hip_status(e);
 }
@@ -197,11 +297,12 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const fl
   if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
   if ((dA && !aligned16(dA)) || (dB && !aligned16(dB)) || (T_saved && !aligned16(T_saved)))
     return QLORA_ERR_INVALID_ARG;
-  Carver probe(nullptr);
-  BwdWs tmp;
-  const size_t need = bwd_ws(M, w->n, w->k, r, T_saved != nullptr, probe, tmp);
-  if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
-
+  {
+    Carver probe(nullptr);
+    BwdWs tmp;
+    const size_t need = bwd_ws(M, w->n, w->k, r, T_saved != nullptr, probe, tmp);
+    if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
   BwdWs o;
@@ -212,22 +313,17 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const fl
   const uint16_t* a = static_cast<const uint16_t*>(A);
   const uint16_t* b = static_cast<const uint16_t*>(B);
   hipError_t e = hipSuccess;
-  if (r > 0 && (dX || dA)) {
-    e = launch_transpose(b, w->n, r, o.BT, st);
-    if (e == hipSuccess) e = launch_rowdot_impl(dy, M, w->n, o.BT, r, o.U, o.US, scale, o.part, st);
-  }
+  if (r > 0 && (dX || dA)) e = do_project(dy, M, w->n, b, 1, r, scale, o.U, dX ? o.US : nullptr, o.proj, st);
   if (e == hipSuccess && dX)
     e = launch_gemm_dx(v, dy, M, r > 0 ? o.US : nullptr, a, r, static_cast<uint16_t*>(dX), st);
-  if (e == hipSuccess && dA)
-    e = launch_coldot(x, M, w->k, o.U, r, scale, dA, /*g_sc=*/1, /*g_sj=*/w->k, accumulate, o.colpart, st);
+  if (e == hipSuccess && dA) e = do_grad(x, M, w->k, o.U, r, scale, dA, 0, accumulate, o.grad, st);
   if (e == hipSuccess && dB) {
     const float* T = T_saved;
     if (T == nullptr) {
-      e = launch_rowdot_impl(x, M, w->k, a, r, o.T, nullptr, scale, o.part, st);
+      e = do_project(x, M, w->k, a, 0, r, scale, o.T, nullptr, o.proj, st);
       T = o.T;
     }
-    if (e == hipSuccess)
-      e = launch_coldot(dy, M, w->n, T, r, scale, dB, /*g_sc=*/r, /*g_sj=*/1, accumulate, o.colpart, st);
+    if (e == hipSuccess) e = do_grad(dy, M, w->n, T, r, scale, dB, 1, accumulate, o.grad, st);
   }
   return hip_status(e);
 }

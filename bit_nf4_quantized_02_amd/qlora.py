@@ -53,6 +53,14 @@ _SIGS = {
     "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
     "qlora_linear_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "qlora_lowrank_split_cols": (_int, [_int]),
+    "qlora_lowrank_project_workspace_bytes": (_sz, [_i64, _i64, _int]),
+    "qlora_lowrank_project": (_int, [_vp, _i64, _i64, _vp, _int, _int, _f, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_nf4_gemm_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
+    "qlora_nf4_gemm_dx": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
+    "qlora_nf4_gemv_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp]),
+    "qlora_lowrank_grad_workspace_bytes": (_sz, [_i64, _i64, _int]),
+    "qlora_lowrank_grad": (_int, [_vp, _i64, _i64, _vp, _int, _f, _vp, _int, _int, _vp, _sz, _vp]),
     "qlora_silu_mul_fwd": (_int, [_vp, _vp, _vp, _i64, _vp]),
     "qlora_silu_mul_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp]),
 }
@@ -246,6 +254,100 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY:
                                  _ptr(dX), _ptr(dA), _ptr(dB), int(bool(accumulate)), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_bwd")
     return dX, dA, dB
+
+
+# --------------------------------------------------------------------------- building blocks
+
+def lowrank_split_cols(r: int) -> int:
+    return int(_lib.qlora_lowrank_split_cols(r))
+
+
+def lowrank_project(P: torch.Tensor, Q: torch.Tensor, q_layout: int, scale: float, want_out: bool = True,
+                    want_split: bool = False, out: torch.Tensor | None = None, split: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None, stream=None):
+    """out = P Q^T (q_layout 0, Q [r, C]) or P Q (q_layout 1, Q [C, r]), fp32; split = bf16 hi/lo of scale*out."""
+    M, C = P.shape
+    r = Q.shape[0] if q_layout == 0 else Q.shape[1]
+    _need(P, torch.bfloat16, (M, C), "P")
+    _need(Q, torch.bfloat16, (r, C) if q_layout == 0 else (C, r), "Q")
+    if want_out and out is None:
+        out = torch.empty((M, r), dtype=torch.float32, device=P.device)
+    if want_split and split is None:
+        split = torch.empty((M, lowrank_split_cols(r)), dtype=torch.bfloat16, device=P.device)
+    if ws is None:
+        ws = _bytes(int(_lib.qlora_lowrank_project_workspace_bytes(M, C, r)), P.device)
+    _check(_lib.qlora_lowrank_project(_ptr(P), M, C, _ptr(Q), int(q_layout), r, float(scale), _ptr(out), _ptr(split),
+                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "qlora_lowrank_project")
+    return out, split
+
+
+def nf4_gemm_fwd(w: NF4Weight, X: torch.Tensor, split: torch.Tensor | None, B: torch.Tensor | None,
+                 Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    M = X.shape[0]
+    r = 0 if B is None else B.shape[1]
+    if Y is None:
+        Y = torch.empty((M, w.n), dtype=torch.bfloat16, device=X.device)
+    st = w.struct()
+    _check(_lib.qlora_nf4_gemm_fwd(ctypes.byref(st), _ptr(X), M, _ptr(split), _ptr(B), r, _ptr(Y), _stream(stream)),
+           "qlora_nf4_gemm_fwd")
+    return Y
+
+
+def nf4_gemm_dx(w: NF4Weight, dY: torch.Tensor, split: torch.Tensor | None, A: torch.Tensor | None,
+                dX: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    M = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if dX is None:
+        dX = torch.empty((M, w.k), dtype=torch.bfloat16, device=dY.device)
+    st = w.struct()
+    _check(_lib.qlora_nf4_gemm_dx(ctypes.byref(st), _ptr(dY), M, _ptr(split), _ptr(A), r, _ptr(dX), _stream(stream)),
+           "qlora_nf4_gemm_dx")
+    return dX
+
+
+def nf4_gemv_fwd(w: NF4Weight, X: torch.Tensor, T: torch.Tensor | None, B: torch.Tensor | None, scale: float,
+                 Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    M = X.shape[0]
+    r = 0 if B is None else B.shape[1]
+    if Y is None:
+        Y = torch.empty((M, w.n), dtype=torch.bfloat16, device=X.device)
+    st = w.struct()
+    _check(_lib.qlora_nf4_gemv_fwd(ctypes.byref(st), _ptr(X), M, _ptr(T), _ptr(B), r, float(scale), _ptr(Y),
+                                   _stream(stream)), "qlora_nf4_gemv_fwd")
+    return Y
+
+
+def lowrank_grad(P: torch.Tensor, Q: torch.Tensor, scale: float, g_layout: int, G: torch.Tensor | None = None,
+                 accumulate: bool = False, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """G = scale P^T Q as [r, C] (g_layout 0) or [C, r] (g_layout 1), fp32."""
+    M, C = P.shape
+    r = Q.shape[1]
+    if G is None:
+        G = (torch.zeros if accumulate else torch.empty)((r, C) if g_layout == 0 else (C, r), dtype=torch.float32,
+                                                         device=P.device)
+    if ws is None:
+        ws = _bytes(int(_lib.qlora_lowrank_grad_workspace_bytes(M, C, r)), P.device)
+    _check(_lib.qlora_lowrank_grad(_ptr(P), M, C, _ptr(Q), r, float(scale), _ptr(G), int(g_layout),
+                                   int(bool(accumulate)), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "qlora_lowrank_grad")
+    return G
+
+
+class Call:
+    """One C-ABI call with its ctypes arguments prebuilt (for tight timing
+    loops); calling it only forwards the stored arguments."""
+
+    def __init__(self, name: str, *args, keep=()):
+        self.name = name
+        self.fn = getattr(_lib, name)
+        self.args = args
+        self._keep = keep  # keeps ctypes structs referenced by pointer alive
+
+    def __call__(self):
+        s = self.fn(*self.args)
+        if s != 0:
+            raise QLoraError(s, self.name)
 
 
 # --------------------------------------------------------------------------- MLP join

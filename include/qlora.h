@@ -188,6 +188,80 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const void *X, const fl
                               float scale, void *dX, float *dA, float *dB, int accumulate,
                               void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Building blocks. qlora_linear_fwd and qlora_linear_bwd are compositions of
+ * the calls below (same kernels, same order); they are exported so a caller
+ * can reuse a low-rank activation it already has, or time each step.
+ * ------------------------------------------------------------------------ */
+
+/* Columns of the bf16 "split" rows the fused GEMMs take: 2r rounded up to a
+ * multiple of 64 (0 for r = 0). */
+int qlora_lowrank_split_cols(int r);
+
+/* Workspace bytes of qlora_lowrank_project (0 on bad arguments). */
+size_t qlora_lowrank_project_workspace_bytes(int64_t M, int64_t C, int r);
+
+/*
+ * Low-rank projection of an activation [QQ three-piece summary, piece 3]:
+ *   out[m, j] = sum_c P[m, c] Q(c, j)        (fp32; T = X A^T or U = dY B)
+ * P (device) [M, C] bf16; Q (device) bf16, q_layout 0: Q is [r, C] (j-major,
+ * as A), 1: Q is [C, r] (as B). out (device, nullable) [M, r] fp32. If split
+ * (device, nullable, [M, qlora_lowrank_split_cols(r)] bf16) is given, row m
+ * receives [hi | lo | zeros] with hi_j = RN_bf16(scale * out[m, j]) and
+ * lo_j = RN_bf16(scale * out[m, j] - hi_j): the 2r extra contraction columns
+ * the fused GEMMs use to add the low-rank term in fp32. bf16 products, fp32
+ * sums; the contraction is split over workgroups and added in a fixed order.
+ * Errors: INVALID_ARG, SHAPE (r < 1 or > QLORA_MAX_RANK), WORKSPACE, HIP.
+ */
+qlora_status qlora_lowrank_project(const void *P, int64_t M, int64_t C, const void *Q, int q_layout, int r,
+                                   float scale, float *out, void *split, void *ws, size_t ws_bytes,
+                                   void *stream);
+
+/*
+ * Fused forward GEMM [QQ three-piece summary, piece 2; "Batched 4-bit matmuls"]:
+ *   Y = RN_bf16( X W'^T + split [B | B]^T )
+ * i.e. the base product with every 64-block expanded to bf16 on chip, plus the
+ * low-rank term when split = qlora_lowrank_project(X, A, scale) and B
+ * (device, [n, r] bf16). r = 0: split and B are ignored. M >= 1, any size.
+ * Errors: INVALID_ARG, SHAPE, HIP.
+ */
+qlora_status qlora_nf4_gemm_fwd(const qlora_nf4_weight *w, const void *X, int64_t M, const void *split,
+                                const void *B, int r, void *Y, void *stream);
+
+/*
+ * Fused backward-data GEMM through the frozen base [WQ "Key Characteristics"]:
+ *   dX = RN_bf16( dY W' + split [A ; A] )
+ * dY (device) [M, n] bf16; split = qlora_lowrank_project(dY, B, scale) rows;
+ * A (device) [r, k] bf16. The contraction runs over n, so each 64-block is
+ * expanded transposed into on-chip memory. Errors: INVALID_ARG, SHAPE, HIP.
+ */
+qlora_status qlora_nf4_gemm_dx(const qlora_nf4_weight *w, const void *dY, int64_t M, const void *split,
+                               const void *A, int r, void *dX, void *stream);
+
+/*
+ * Bandwidth-oriented forward for M <= 16 tokens:
+ *   Y = RN_bf16( X W'^T + scale T B^T ),   T (device, [M, r] fp32) = X A^T.
+ * One pass over the packed codes. Errors: INVALID_ARG, SHAPE (M > 16), HIP.
+ */
+qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight *w, const void *X, int64_t M, const float *T,
+                                const void *B, int r, float scale, void *Y, void *stream);
+
+/* Workspace bytes of qlora_lowrank_grad (0 on bad arguments). */
+size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r);
+
+/*
+ * Adapter gradient, a reduction over the M tokens [QQ: all updates land on the
+ * low-rank branch]:
+ *   G(c, j) (+)= scale * sum_m P[m, c] Q[m, j]
+ * P (device) [M, C] bf16; Q (device) [M, r] fp32; G (device) fp32 with
+ * g_layout 0: G is [r, C] (dA = s U^T X), 1: G is [C, r] (dB = s dY^T T).
+ * accumulate 0 overwrites, 1 adds. fp32 products and sums, reduced over M in
+ * a fixed order (bit-identical reruns).
+ * Errors: INVALID_ARG, SHAPE, WORKSPACE, HIP.
+ */
+qlora_status qlora_lowrank_grad(const void *P, int64_t M, int64_t C, const float *Q, int r, float scale, float *G,
+                                int g_layout, int accumulate, void *ws, size_t ws_bytes, void *stream);
+
 /*
  * The gated-MLP join used between the gate/up and down linears of the MLP
  * workloads (not a QLoRA operation; provided so a whole MLP block runs on
