@@ -46,12 +46,10 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   const uint32_t sign = (b & 0x80u) << 24;
   const uint32_t e = (b >> 3) & 0xFu;
   const uint32_t m = b & 0x7u;
-  float mag;
-  if (e == 0) {
-    mag = (float)m * 0.001953125f;  // m/8 * 2^-6 = m * 2^-9, exact
-  } else {
-    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  }
+  // both cases computed, one selected: no divergent branch
+  const float sub = (float)m * 0.001953125f;  // m/8 * 2^-6 = m * 2^-9, exact
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float mag = e == 0 ? sub : nrm;
   return __uint_as_float(__float_as_uint(mag) | sign);
 }
 

@@ -54,38 +54,50 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t c = w0; c < w1; c += 32) {
-    const int64_t cc = c + ko;
-    u32x4 a = {0u, 0u, 0u, 0u};
-    if (m < M) {
-      if constexpr (kVec) {
-        if (cc < w1) a = *reinterpret_cast<const u32x4*>(P + m * C + cc);
-      } else {
-        uint16_t e[8];
+  // 4 chunks of 32 columns per iteration: all loads first, then the MFMAs,
+  // so each lane keeps several 16-byte loads in flight
+  constexpr int kU = 4;
+  for (int64_t c = w0; c < w1; c += 32 * kU) {
+    u32x4 a[kU];
+    u32x4 b[kU][kTiles];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = (cc + i < w1) ? P[m * C + cc + i] : (uint16_t)0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      const int j = t * 16 + row;
-      u32x4 b = {0u, 0u, 0u, 0u};
-      if (j < r) {
+    for (int u = 0; u < kU; ++u) {
+      const int64_t cc = c + 32 * u + ko;
+      a[u] = u32x4{0u, 0u, 0u, 0u};
+      if (m < M) {
         if constexpr (kVec) {
-          if (cc < w1) b = *reinterpret_cast<const u32x4*>(Q + (int64_t)j * C + cc);
+          if (cc < w1) a[u] = *reinterpret_cast<const u32x4*>(P + m * C + cc);
         } else {
           uint16_t e[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) e[i] = (cc + i < w1) ? Q[(int64_t)j * C + cc + i] : (uint16_t)0;
+          for (int i = 0; i < 8; ++i) e[i] = (cc + i < w1) ? P[m * C + cc + i] : (uint16_t)0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) b[i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
+          for (int i = 0; i < 4; ++i) a[u][i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
         }
       }
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), acc[t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        const int j = t * 16 + row;
+        b[u][t] = u32x4{0u, 0u, 0u, 0u};
+        if (j < r) {
+          if constexpr (kVec) {
+            if (cc < w1) b[u][t] = *reinterpret_cast<const u32x4*>(Q + (int64_t)j * C + cc);
+          } else {
+            uint16_t e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] = (cc + i < w1) ? Q[(int64_t)j * C + cc + i] : (uint16_t)0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[u][t][i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
+          }
+        }
+      }
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                         __builtin_bit_cast(bf16x8, b[u][t]), acc[t], 0, 0, 0);
   }
   // D layout: lane -> column (lane & 15), rows 4 * (lane >> 4) + v
 #pragma unroll
@@ -135,30 +147,89 @@ __global__ __launch_bounds__(256) void rowdot_finalize_kernel(const float* __res
   split[i] = v;
 }
 
-// G partial: thread = one column c, r fp32 accumulators, rows [m0, m1).
-template <int kR>
-__global__ __launch_bounds__(256) void coldot_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
-                                                     const float* __restrict__ Q, int r, int64_t mchunk,
-                                                     float* __restrict__ partial) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// G partial on the matrix cores: Gp[s][j][c] = sum_{m in split s} Q[m, j] P[m, c].
+// v_mfma_f32_16x16x32_bf16 with rows = j (rank), columns = c, contraction =
+// 32 tokens: every lane gathers 8 consecutive tokens of one column of P (2-byte
+// loads; across the wave they cover 16 columns x 32 tokens) and of one column
+// of Q, so neither operand is transposed through LDS. Q is fp32: each value is
+// split into bf16 hi + lo and both halves are multiplied, so the products
+// carry ~16 significant bits of Q. Each wave owns 64 columns; a workgroup
+// 256 columns and one token split.
+template <int kRP>
+__global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
+                                                          const float* __restrict__ Q, int r, int64_t mchunk,
+                                                          float* __restrict__ partial) {
+#pragma clang fp contract(off)
+  constexpr int kJT = kRP / 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t c0 = (int64_t)blockIdx.x * 256 + wave * 64;
   const int64_t s = blockIdx.y;
   const int64_t m0 = s * mchunk;
   const int64_t m1 = (m0 + mchunk < M) ? m0 + mchunk : M;
-  float acc[kR];
+  const int col = lane & 15;
+  const int mo = (lane >> 4) * 8;
+  f32x4 acc[kJT][4];
 #pragma unroll
-  for (int j = 0; j < kR; ++j) acc[j] = 0.0f;
-  if (c < C) {
-    for (int64_t m = m0; m < m1; ++m) {
-      const float p = bf16_bits_to_f32(P[m * C + c]);
-      const float* q = Q + m * r;
+  for (int a = 0; a < kJT; ++a)
 #pragma unroll
-      for (int j = 0; j < kR; ++j)
-        if (j < r) acc[j] = fmaf(p, q[j], acc[j]);
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t mb = m0; mb < m1; mb += 32) {
+    // B operands: 4 column tiles x 8 tokens of P
+    bf16x8 pb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t c = c0 + t * 16 + col;
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t m = mb + mo + e;
+        h[e] = (c < C && m < m1) ? (uint32_t)P[m * C + c] : 0u;
+      }
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = h[2 * e] | (h[2 * e + 1] << 16);
+      pb[t] = __builtin_bit_cast(bf16x8, v);
     }
+    // A operands: rank tiles x 8 tokens of Q, split into hi and lo
 #pragma unroll
-    for (int j = 0; j < kR; ++j)
-      if (j < r) partial[(s * r + j) * C + c] = acc[j];
+    for (int a = 0; a < kJT; ++a) {
+      const int j = a * 16 + col;
+      u32x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t hh[2], ll[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int64_t m = mb + mo + 2 * e + f;
+          const float q = (j < r && m < m1) ? Q[m * r + j] : 0.0f;
+          const uint16_t qh = to_bf16_bits(q);
+          hh[f] = qh;
+          ll[f] = to_bf16_bits(q - bf16_bits_to_f32(qh));
+        }
+        hi[e] = hh[0] | (hh[1] << 16);
+        lo[e] = ll[0] | (ll[1] << 16);
+      }
+      const bf16x8 ah = __builtin_bit_cast(bf16x8, hi), al = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, pb[t], acc[a][t], 0, 0, 0);
+        acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, pb[t], acc[a][t], 0, 0, 0);
+      }
+    }
   }
+  // D[j][c]: lane -> c = col, j = 4 (lane >> 4) + v
+#pragma unroll
+  for (int a = 0; a < kJT; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t c = c0 + t * 16 + col;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = a * 16 + 4 * (lane >> 4) + v;
+        if (c < C && j < r) partial[(s * r + j) * C + c] = acc[a][t][v];
+      }
+    }
 }
 
 __global__ __launch_bounds__(256) void coldot_reduce_kernel(const float* __restrict__ partial, int64_t C, int r,
@@ -210,7 +281,7 @@ hipError_t launch_rowdot_impl(const uint16_t* P, int64_t M, int64_t C, const uin
 }
 
 int coldot_splits(int64_t M) {
-  int64_t s = M / 128;
+  int64_t s = M / 256;
   if (s > 32) s = 32;
   if (s < 1) s = 1;
   return (int)s;
@@ -223,13 +294,12 @@ size_t coldot_ws_bytes(int64_t M, int64_t C, int r) {
 hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,
                          int64_t g_sc, int64_t g_sj, int accumulate, float* partial, hipStream_t stream) {
   const int ns = coldot_splits(M);
-  const int64_t mchunk = cdiv(M, ns);
+  const int64_t mchunk = cdiv(cdiv(M, ns), 32) * 32;
   const dim3 grid((unsigned)cdiv(C, 256), (unsigned)ns);
-  if (r <= 8) coldot_kernel<8><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
-  else if (r <= 16) coldot_kernel<16><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
-  else if (r <= 32) coldot_kernel<32><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
-  else if (r <= 64) coldot_kernel<64><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
-  else coldot_kernel<128><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
+  if (r <= 16) coldot_mfma_kernel<16><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
+  else if (r <= 32) coldot_mfma_kernel<32><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
+  else if (r <= 64) coldot_mfma_kernel<64><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
+  else coldot_mfma_kernel<128><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
   coldot_reduce_kernel<<<(unsigned)cdiv(C * r, 256), 256, 0, stream>>>(partial, C, r, ns, scale, G, g_sc, g_sj,
                                                                       accumulate);
   return hipGetLastError();
