@@ -135,13 +135,16 @@ __device__ __forceinline__ void load_act(const GemmArgs& a, int64_t m0, int step
 // required: the forward always, dX when n % 8 == 0). Each wavefront
 // instruction fills one contiguous 1 KB of LDS = 8 tile rows; lane l lands at
 // row 8 b + l / 8, physical chunk l % 8, so it fetches logical chunk
-// (l % 8) ^ (row & 7). Rows past M read a clamped in-range row: their outputs
-// are never stored, so the values do not matter.
+// (l % 8) ^ (row & 7). Every address stays inside the operand: rows past M
+// read a clamped in-range row (their outputs are never stored), and chunks
+// past the last contraction column read the last in-range chunk (the weight
+// rows they meet are exactly zero, and the data are finite).
 __device__ __forceinline__ void issue_act_lds(const GemmArgs& a, int64_t m0, int step, int nk_main, char* As) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool extra = step >= nk_main;
   const uint16_t* src = extra ? a.act_x : a.act;
   const int64_t ld = extra ? (int64_t)a.kx : a.lda;
+  const int64_t cols = extra ? (int64_t)a.kx : a.kc;
   const int64_t c0 = (int64_t)(extra ? step - nk_main : step) * kBK;
 #pragma unroll
   for (int i = 0; i < 32 / kWaves; ++i) {
@@ -150,7 +153,9 @@ __device__ __forceinline__ void issue_act_lds(const GemmArgs& a, int64_t m0, int
     const int lc = (lane & 7) ^ (row & 7);
     const int64_t m = m0 + row;
     const int64_t mc = m < a.M ? m : a.M - 1;
-    const uint16_t* g = src + mc * ld + c0 + 8 * lc;
+    const int64_t c = c0 + 8 * lc;
+    const int64_t cc = c < cols ? c : cols - 8;
+    const uint16_t* g = src + mc * ld + cc;
     __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(As + blk * 1024), 16,
                                      0, 0);
   }

@@ -25,25 +25,29 @@ namespace qlora {
 
 namespace {
 
-constexpr int kRowTile = 16;   // rows of P per workgroup (one 16x16x32 MFMA row block)
 constexpr int kMaxRank = 128;
 
-// Each workgroup: 16 rows, columns [c0, c1) of the contraction, all r outputs.
-// 4 waves split [c0, c1) into quarters; lanes read P and Q straight from
-// global memory in the MFMA operand layout (8 consecutive bf16 per lane).
-template <bool kVec, int kRP>
+// Each workgroup: RT x 16 rows, columns [c0, c1) of the contraction, all r
+// outputs. Wave w takes row tile w % RT and part w / RT of the column range
+// (4 / RT parts); lanes read P and Q straight from global memory in the MFMA
+// operand layout (8 consecutive bf16 per lane), 8 column chunks per
+// iteration so each lane keeps eight 16-byte loads in flight. With RT = 4 the
+// four waves share one slice of Q (read once per 64 rows instead of per 16).
+template <bool kVec, int kRP, int RT>
 __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
                                                      const uint16_t* __restrict__ Q, int r,
                                                      int64_t cchunk, float* __restrict__ part) {
-  __shared__ float red[4][kRowTile][kRP];
+  constexpr int kParts = 4 / RT;
+  __shared__ float red[4][16][kRP];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t m0 = (int64_t)blockIdx.x * kRowTile;
+  const int rt = wave % RT, cpart = wave / RT;
+  const int64_t m0 = (int64_t)blockIdx.x * (16 * RT) + 16 * rt;
   const int64_t cs = blockIdx.y;
   const int64_t cbeg = cs * cchunk;
   const int64_t cend = (cbeg + cchunk < C) ? cbeg + cchunk : C;
-  const int64_t qlen = cdiv(cend - cbeg, 4 * 32) * 32;  // per-wave length, multiple of 32
-  const int64_t w0 = cbeg + wave * qlen;
+  const int64_t qlen = cdiv(cend - cbeg, kParts * 32) * 32;  // per-wave length, multiple of 32
+  const int64_t w0 = cbeg + cpart * qlen;
   const int64_t w1 = (w0 + qlen < cend) ? w0 + qlen : cend;
 
   const int row = lane & 15;
@@ -54,9 +58,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // 4 chunks of 32 columns per iteration: all loads first, then the MFMAs,
-  // so each lane keeps several 16-byte loads in flight
-  constexpr int kU = 4;
+  constexpr int kU = kTiles >= 4 ? 2 : 8 / kTiles;
   for (int64_t c = w0; c < w1; c += 32 * kU) {
     u32x4 a[kU];
     u32x4 b[kU][kTiles];
@@ -105,12 +107,16 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][t * 16 + (lane & 15)] = acc[t][v];
   __syncthreads();
-  for (int i = threadIdx.x; i < kRowTile * kRP; i += 256) {
+  const int64_t mw = (int64_t)blockIdx.x * (16 * RT);
+  for (int i = threadIdx.x; i < 16 * RT * kRP; i += 256) {
     const int rr = i / kRP, j = i % kRP;
-    const int64_t mm = m0 + rr;
+    const int64_t mm = mw + rr;
     if (mm < M && j < r) {
-      const float s = ((red[0][rr][j] + red[1][rr][j]) + red[2][rr][j]) + red[3][rr][j];
-      part[(cs * M + mm) * r + j] = s;
+      const int rtile = rr / 16, rin = rr % 16;
+      float sum = red[rtile][rin][j];
+#pragma unroll
+      for (int pp = 1; pp < kParts; ++pp) sum += red[rtile + pp * RT][rin][j];  // parts in order
+      part[(cs * M + mm) * r + j] = sum;
     }
   }
 }
@@ -148,86 +154,127 @@ __global__ __launch_bounds__(256) void rowdot_finalize_kernel(const float* __res
 }
 
 // G partial on the matrix cores: Gp[s][j][c] = sum_{m in split s} Q[m, j] P[m, c].
-// v_mfma_f32_16x16x32_bf16 with rows = j (rank), columns = c, contraction =
-// 32 tokens: every lane gathers 8 consecutive tokens of one column of P (2-byte
-// loads; across the wave they cover 16 columns x 32 tokens) and of one column
-// of Q, so neither operand is transposed through LDS. Q is fp32: each value is
-// split into bf16 hi + lo and both halves are multiplied, so the products
-// carry ~16 significant bits of Q. Each wave owns 64 columns; a workgroup
-// 256 columns and one token split.
+// The contraction runs over the tokens m, which are the slow index of both
+// operands, so each 32-token step is staged in LDS in its stored orientation
+// -- P as [32][256 columns] bf16 (coalesced 16-byte loads), Q as [32][r] bf16
+// hi and lo halves of the fp32 value -- and both MFMA operands are gathered
+// with the transposing read ds_read_b64_tr_b16 (8 consecutive tokens of one
+// column per lane). v_mfma_f32_16x16x32_bf16: rows = j, columns = c; the hi
+// and lo halves of Q are multiplied separately, so the products carry ~16
+// significant bits of Q. Each wave owns 64 columns; a workgroup 256 columns
+// and one token split. The next step's P is loaded into registers while the
+// current step's MFMAs run.
+constexpr int kPPitch = 512 + 32;  // bytes per staged P row (256 bf16 + pad)
+
 template <int kRP>
+struct ColdotSmem {
+  static constexpr int kQPitch = kRP * 2 + (kRP >= 32 ? 32 : 0);
+  char p[32 * kPPitch];
+  char qh[32 * kQPitch];
+  char ql[32 * kQPitch];
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Operand of v_mfma_f32_16x16x32_bf16 from a [token][col] bf16 tile: lane
+// gets column c0 + lane % 16, tokens 8 (lane / 16) .. +7. Inside each 16-lane
+// group lane i addresses token base + i / 4, columns 4 (i % 4) .. +3 and
+// receives its own column of the 4 tokens.
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, int pitch, int c0, int lane) {
+  const int i = lane & 15;
+  const char* p = tile + (8 * (lane >> 4) + (i >> 2)) * pitch + (c0 + 4 * (i & 3)) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 4 * pitch));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int kRP, bool kVec>
 __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
                                                           const float* __restrict__ Q, int r, int64_t mchunk,
                                                           float* __restrict__ partial) {
 #pragma clang fp contract(off)
   constexpr int kJT = kRP / 16;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t c0 = (int64_t)blockIdx.x * 256 + wave * 64;
+  using Smem = ColdotSmem<kRP>;
+  constexpr int kQP = Smem::kQPitch;
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int64_t cw = (int64_t)blockIdx.x * 256;
   const int64_t s = blockIdx.y;
   const int64_t m0 = s * mchunk;
   const int64_t m1 = (m0 + mchunk < M) ? m0 + mchunk : M;
-  const int col = lane & 15;
-  const int mo = (lane >> 4) * 8;
   f32x4 acc[kJT][4];
 #pragma unroll
   for (int a = 0; a < kJT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // P tile: 32 rows x 32 chunks of 16 B; thread t owns chunk t % 32 of rows
+  // t / 32 + 8 i (i = 0..3). Out-of-range rows / columns load zeros.
+  auto load_p = [&](int64_t mb, u32x4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = mb + (t >> 5) + 8 * i;
+      const int64_t c = cw + (t & 31) * 8;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (m < m1) {
+        if constexpr (kVec) {
+          if (c < C) v[i] = *reinterpret_cast<const u32x4*>(P + m * C + c);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) e[q] = (c + q < C) ? (uint32_t)P[m * C + c + q] : 0u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[i][q] = e[2 * q] | (e[2 * q + 1] << 16);
+        }
+      }
+    }
+  };
+  u32x4 pv[4];
+  load_p(m0, pv);
   for (int64_t mb = m0; mb < m1; mb += 32) {
-    // B operands: 4 column tiles x 8 tokens of P
+    // stage this step: P from registers, Q converted to bf16 hi / lo
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(sm.p + ((t >> 5) + 8 * i) * kPPitch + (t & 31) * 16) = pv[i];
+    for (int e = t; e < 32 * kRP; e += 256) {
+      const int mm = e / kRP, j = e % kRP;
+      const int64_t m = mb + mm;
+      const float q = (j < r && m < m1) ? Q[m * r + j] : 0.0f;
+      const uint16_t qh = to_bf16_bits(q);
+      const uint16_t ql = to_bf16_bits(q - bf16_bits_to_f32(qh));
+      *reinterpret_cast<uint16_t*>(sm.qh + mm * kQP + j * 2) = qh;
+      *reinterpret_cast<uint16_t*>(sm.ql + mm * kQP + j * 2) = ql;
+    }
+    __syncthreads();
+    if (mb + 32 < m1) load_p(mb + 32, pv);  // in flight during the MFMAs
     bf16x8 pb[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t c = c0 + t * 16 + col;
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t m = mb + mo + e;
-        h[e] = (c < C && m < m1) ? (uint32_t)P[m * C + c] : 0u;
-      }
-      u32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = h[2 * e] | (h[2 * e + 1] << 16);
-      pb[t] = __builtin_bit_cast(bf16x8, v);
-    }
-    // A operands: rank tiles x 8 tokens of Q, split into hi and lo
+    for (int ct = 0; ct < 4; ++ct) pb[ct] = tr_operand(sm.p, kPPitch, wave * 64 + ct * 16, lane);
 #pragma unroll
     for (int a = 0; a < kJT; ++a) {
-      const int j = a * 16 + col;
-      u32x4 hi, lo;
+      const bf16x8 ah = tr_operand(sm.qh, kQP, a * 16, lane);
+      const bf16x8 al = tr_operand(sm.ql, kQP, a * 16, lane);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t hh[2], ll[2];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int64_t m = mb + mo + 2 * e + f;
-          const float q = (j < r && m < m1) ? Q[m * r + j] : 0.0f;
-          const uint16_t qh = to_bf16_bits(q);
-          hh[f] = qh;
-          ll[f] = to_bf16_bits(q - bf16_bits_to_f32(qh));
-        }
-        hi[e] = hh[0] | (hh[1] << 16);
-        lo[e] = ll[0] | (ll[1] << 16);
-      }
-      const bf16x8 ah = __builtin_bit_cast(bf16x8, hi), al = __builtin_bit_cast(bf16x8, lo);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, pb[t], acc[a][t], 0, 0, 0);
-        acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, pb[t], acc[a][t], 0, 0, 0);
+      for (int ct = 0; ct < 4; ++ct) {
+        acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, pb[ct], acc[a][ct], 0, 0, 0);
+        acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, pb[ct], acc[a][ct], 0, 0, 0);
       }
     }
+    __syncthreads();
   }
-  // D[j][c]: lane -> c = col, j = 4 (lane >> 4) + v
+  // D[j][c]: lane -> c = lane % 16, j = 4 (lane / 16) + v
 #pragma unroll
   for (int a = 0; a < kJT; ++a)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t c = c0 + t * 16 + col;
+    for (int ct = 0; ct < 4; ++ct) {
+      const int64_t c = cw + wave * 64 + ct * 16 + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = a * 16 + 4 * (lane >> 4) + v;
-        if (c < C && j < r) partial[(s * r + j) * C + c] = acc[a][t][v];
+        if (c < C && j < r) partial[(s * r + j) * C + c] = acc[a][ct][v];
       }
     }
 }
@@ -247,10 +294,12 @@ __global__ __launch_bounds__(256) void coldot_reduce_kernel(const float* __restr
 
 }  // namespace
 
+static int rowdot_rt(int64_t M) { return M >= 256 ? 4 : 1; }
+
 static int rowdot_splits(int64_t M, int64_t C) {
-  const int64_t tiles = cdiv(M, kRowTile);
+  const int64_t tiles = cdiv(M, 16 * rowdot_rt(M));
   int64_t s = cdiv(512, tiles);
-  const int64_t maxs = cdiv(C, 4 * 128);  // keep >= 128 columns per wave
+  const int64_t maxs = cdiv(C, 256);  // keep >= 256 columns per split
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;
   return (int)s;
@@ -263,17 +312,21 @@ size_t rowdot_ws_bytes(int64_t M, int64_t C, int r) {
 hipError_t launch_rowdot_impl(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
                               uint16_t* split, float scale, float* part, hipStream_t stream) {
   const int ns = rowdot_splits(M, C);
+  const int rt = rowdot_rt(M);
   const int64_t cchunk = cdiv(cdiv(C, ns), 32) * 32;
-  const dim3 grid((unsigned)cdiv(M, kRowTile), (unsigned)ns);
+  const dim3 grid((unsigned)cdiv(M, 16 * rt), (unsigned)ns);
   const bool vec = (C % 8) == 0;
-#define QLORA_ROWDOT(RP)                                                                          \
-  if (vec) rowdot_kernel<true, RP><<<grid, 256, 0, stream>>>(P, M, C, Q, r, cchunk, part);       \
-  else rowdot_kernel<false, RP><<<grid, 256, 0, stream>>>(P, M, C, Q, r, cchunk, part);
+#define QLORA_ROWDOT2(RP, RT)                                                                          \
+  if (vec) rowdot_kernel<true, RP, RT><<<grid, 256, 0, stream>>>(P, M, C, Q, r, cchunk, part);        \
+  else rowdot_kernel<false, RP, RT><<<grid, 256, 0, stream>>>(P, M, C, Q, r, cchunk, part);
+#define QLORA_ROWDOT(RP) \
+  if (rt == 4) { QLORA_ROWDOT2(RP, 4) } else { QLORA_ROWDOT2(RP, 1) }
   if (r <= 16) { QLORA_ROWDOT(16) }
   else if (r <= 32) { QLORA_ROWDOT(32) }
   else if (r <= 64) { QLORA_ROWDOT(64) }
   else { QLORA_ROWDOT(128) }
 #undef QLORA_ROWDOT
+#undef QLORA_ROWDOT2
   const int xcols = lora_extra_cols(r);
   const int64_t total = split ? M * xcols : M * r;
   rowdot_finalize_kernel<<<(unsigned)cdiv(total, 256), 256, 0, stream>>>(part, M, r, ns, out, split, xcols, scale);
@@ -296,10 +349,15 @@ hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q
   const int ns = coldot_splits(M);
   const int64_t mchunk = cdiv(cdiv(M, ns), 32) * 32;
   const dim3 grid((unsigned)cdiv(C, 256), (unsigned)ns);
-  if (r <= 16) coldot_mfma_kernel<16><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
-  else if (r <= 32) coldot_mfma_kernel<32><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
-  else if (r <= 64) coldot_mfma_kernel<64><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
-  else coldot_mfma_kernel<128><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
+  const bool vec = C % 8 == 0;
+#define QLORA_COLDOT(RP)                                                                             \
+  if (vec) coldot_mfma_kernel<RP, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);  \
+  else coldot_mfma_kernel<RP, false><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
+  if (r <= 16) { QLORA_COLDOT(16) }
+  else if (r <= 32) { QLORA_COLDOT(32) }
+  else if (r <= 64) { QLORA_COLDOT(64) }
+  else { QLORA_COLDOT(128) }
+#undef QLORA_COLDOT
   coldot_reduce_kernel<<<(unsigned)cdiv(C * r, 256), 256, 0, stream>>>(partial, C, r, ns, scale, G, g_sc, g_sj,
                                                                       accumulate);
   return hipGetLastError();
