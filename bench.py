@@ -50,7 +50,24 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     p.add_argument("--json", default=None, help="also write the JSON line to this file")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB 3 times (the known-size kernel that "
+                        "scales FETCH_SIZE / WRITE_SIZE counter readings) and exit")
     return p.parse_args()
+
+
+def copy_calibration(mib: int):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings per
+    dispatch, divided by the bytes it must move, give the factor that turns
+    those counters into bytes for the other kernels of the same run."""
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "dispatches": 3}), flush=True)
 
 
 def log(*a):
@@ -131,6 +148,7 @@ class Workload:
     def __init__(self, cid: int, q):
         self.cid = cid
         self.c = synth.CONFIGS[cid]
+        self.tag = {1: "proj_1024_m16", 2: "attn_proj_4096_m4096", 3: "mlp_7b_m2048", 4: "decode_70b"}[cid]
         c = self.c
         self.pieces = []      # (name, flops, call)
         self.plans = []
@@ -285,8 +303,11 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only: the path shards by data parallelism "
                                    "(see DESIGN.md); --gpus must be 1"}), flush=True)
         sys.exit(2)
-    from bit_nf4_quantized_02_amd import qlora as q
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+        return
+    from bit_nf4_quantized_02_amd import qlora as q
     log(f"bench: building workload config {args.config}")
     wl = Workload(args.config, q)
     torch.cuda.synchronize()
@@ -315,7 +336,7 @@ def main():
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4))
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
-    roof["traffic"] = gemm_traffic(f"config{args.config}.{base}")
+    roof["traffic"] = gemm_traffic(f"{wl.tag}.{base}")
 
     res = {
         "metric": METRIC,
