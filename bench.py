@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    p.add_argument("--path", choices=["auto", "fused", "expanded"], default="auto",
+                   help="large-M kernels: the library's choice (auto) or one forced, for comparison")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     p.add_argument("--json", default=None, help="also write the JSON line to this file")
@@ -79,7 +81,7 @@ def log(*a):
 class LinearPlan:
     """Device tensors and prebuilt C-ABI calls of one QLoRA linear."""
 
-    def __init__(self, q, li: synth.LinearInputs, backward: bool = True, X=None, dY=None):
+    def __init__(self, q, li: synth.LinearInputs, backward: bool = True, X=None, dY=None, force_path=None):
         dev = "cuda"
         m = li.meta
         self.m, self.n, self.k, self.r, self.s = m["m"], m["n"], m["k"], m["r"], li.scale
@@ -109,7 +111,18 @@ class LinearPlan:
         wref = q.ctypes.byref(self.wst)
         ws, wsn = P(self.ws), self.ws.numel()
         self.fwd, self.bwd = [], []
-        if M <= 16:
+        # the kernels qlora_linear_fwd / _bwd choose at this size (or a forced
+        # large-M variant, for comparing the two)
+        self.path_fwd = q.linear_path(M, N, K, False)
+        self.path_bwd = q.linear_path(M, N, K, True)
+        if force_path is not None and self.path_fwd != q.PATH_GEMV:
+            self.path_fwd = force_path
+            self.path_bwd = force_path if (force_path != q.PATH_EXPANDED or N % 8 == 0) else q.PATH_FUSED
+        if self.path_fwd == q.PATH_EXPANDED:
+            self.Fw = torch.empty(q.nf4_expand_bytes(N, K, r, False) // 2, dtype=torch.bfloat16, device=dev)
+        if backward and self.path_bwd == q.PATH_EXPANDED:
+            self.Fx = torch.empty(q.nf4_expand_bytes(N, K, r, True) // 2, dtype=torch.bfloat16, device=dev)
+        if self.path_fwd == q.PATH_GEMV:
             self.fwd.append(("lowrank_project_T", 2 * M * K * r,
                              q.Call("qlora_lowrank_project", P(self.X), M, K, P(self.A), 0, r, self.s, P(self.T), None,
                                     ws, wsn, st)))
@@ -120,16 +133,32 @@ class LinearPlan:
             self.fwd.append(("lowrank_project_T", 2 * M * K * r,
                              q.Call("qlora_lowrank_project", P(self.X), M, K, P(self.A), 0, r, self.s, P(self.T),
                                     P(self.TS), ws, wsn, st)))
-            self.fwd.append(("nf4_gemm_fwd", 2 * M * N * K + 2 * M * N * r,
-                             q.Call("qlora_nf4_gemm_fwd", wref, P(self.X), M, P(self.TS), P(self.B), r, P(self.Y), st,
-                                    keep=(self.wst,))))
+            if self.path_fwd == q.PATH_FUSED:
+                self.fwd.append(("nf4_gemm_fwd", 2 * M * N * K + 2 * M * N * r,
+                                 q.Call("qlora_nf4_gemm_fwd", wref, P(self.X), M, P(self.TS), P(self.B), r, P(self.Y),
+                                        st, keep=(self.wst,))))
+            else:
+                self.fwd.append(("nf4_expand_fwd", 0,
+                                 q.Call("qlora_nf4_expand", wref, P(self.B), r, 0, P(self.Fw), self.Fw.numel() * 2, st,
+                                        keep=(self.wst,))))
+                self.fwd.append(("bf16_gemm_fwd", 2 * M * N * K + 2 * M * N * r,
+                                 q.Call("qlora_bf16_gemm", P(self.X), M, K, P(self.TS), r, P(self.Fw), N, P(self.Y),
+                                        st)))
         if backward:
             self.bwd.append(("lowrank_project_U", 2 * M * N * r,
                              q.Call("qlora_lowrank_project", P(self.dY), M, N, P(self.B), 1, r, self.s, P(self.U),
                                     P(self.US), ws, wsn, st)))
-            self.bwd.append(("nf4_gemm_dx", 2 * M * N * K + 2 * M * K * r,
-                             q.Call("qlora_nf4_gemm_dx", wref, P(self.dY), M, P(self.US), P(self.A), r, P(self.dX), st,
-                                    keep=(self.wst,))))
+            if self.path_bwd == q.PATH_FUSED:
+                self.bwd.append(("nf4_gemm_dx", 2 * M * N * K + 2 * M * K * r,
+                                 q.Call("qlora_nf4_gemm_dx", wref, P(self.dY), M, P(self.US), P(self.A), r,
+                                        P(self.dX), st, keep=(self.wst,))))
+            else:
+                self.bwd.append(("nf4_expand_dx", 0,
+                                 q.Call("qlora_nf4_expand", wref, P(self.A), r, 1, P(self.Fx), self.Fx.numel() * 2, st,
+                                        keep=(self.wst,))))
+                self.bwd.append(("bf16_gemm_dx", 2 * M * N * K + 2 * M * K * r,
+                                 q.Call("qlora_bf16_gemm", P(self.dY), M, N, P(self.US), r, P(self.Fx), K, P(self.dX),
+                                        st)))
             self.bwd.append(("lowrank_grad_dA", 2 * M * K * r,
                              q.Call("qlora_lowrank_grad", P(self.X), M, K, P(self.U), r, self.s, P(self.dA), 0, 0, ws,
                                     wsn, st)))
@@ -145,7 +174,7 @@ class LinearPlan:
 # ----------------------------------------------------------------------------- workloads
 
 class Workload:
-    def __init__(self, cid: int, q):
+    def __init__(self, cid: int, q, force_path=None):
         self.cid = cid
         self.c = synth.CONFIGS[cid]
         self.tag = {1: "proj_1024_m16", 2: "attn_proj_4096_m4096", 3: "mlp_7b_m2048", 4: "decode_70b"}[cid]
@@ -156,7 +185,7 @@ class Workload:
         if cid in (1, 2):
             lin = c.linears[0]
             li = synth.linear_inputs(cid, 0, 0, lin.n, lin.k, c.m[0], c.r, c.scale, sigma=c.sigma)
-            p = LinearPlan(q, li)
+            p = LinearPlan(q, li, force_path=force_path)
             self.plans.append(p)
             self.pieces = p.fwd + p.bwd
             self.passes_bytes = 2 * p.packed_bytes
@@ -173,9 +202,9 @@ class Workload:
             H = torch.empty((M, gate.n), dtype=torch.bfloat16, device="cuda")
             dG = torch.empty_like(H)
             dU = torch.empty_like(H)
-            pd = LinearPlan(q, ld, X=H)
-            pg = LinearPlan(q, lg, X=X, dY=dG)
-            pu = LinearPlan(q, lu, X=X, dY=dU)
+            pd = LinearPlan(q, ld, X=H, force_path=force_path)
+            pg = LinearPlan(q, lg, X=X, dY=dG, force_path=force_path)
+            pu = LinearPlan(q, lu, X=X, dY=dU, force_path=force_path)
             cnt = M * gate.n
             st = q._stream()
             P = q._ptr
@@ -309,7 +338,11 @@ def main():
         return
     from bit_nf4_quantized_02_amd import qlora as q
     log(f"bench: building workload config {args.config}")
-    wl = Workload(args.config, q)
+    force = {"auto": None, "fused": q.PATH_FUSED, "expanded": q.PATH_EXPANDED}[args.path]
+    wl = Workload(args.config, q, force_path=force)
+    names_of = {q.PATH_GEMV: "gemv", q.PATH_FUSED: "fused", q.PATH_EXPANDED: "expanded"}
+    wl.desc["kernels"] = sorted({f"fwd:{names_of[p.path_fwd]}" for p in wl.plans}
+                                | {f"bwd:{names_of[p.path_bwd]}" for p in wl.plans if p.bwd})
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
     ms_wall, ms_ev, per_ms = time_steps(wl, args.steps, args.warmup)

@@ -45,6 +45,13 @@ struct Carver {
 
 bool small_m(int64_t M) { return M <= 16; }
 
+// Kernel choice per pass (the rule qlora_linear_path documents).
+int path_of(int64_t M, int64_t n, bool bwd) {
+  if (!bwd && small_m(M)) return QLORA_PATH_GEMV;
+  if (M >= QLORA_EXPAND_MIN_M && (!bwd || n % 8 == 0)) return QLORA_PATH_EXPANDED;
+  return QLORA_PATH_FUSED;
+}
+
 // ---- building-block workspaces
 size_t project_ws(int64_t M, int64_t C, int r) {
   return align256((size_t)C * r * 2) + rowdot_ws_bytes(M, C, r);
@@ -78,17 +85,20 @@ struct FwdWs {
   float* T = nullptr;
   uint16_t* TS = nullptr;
   void* proj = nullptr;
+  uint16_t* F = nullptr;  // expanded operand (large M)
 };
 
-size_t fwd_ws(int64_t M, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o) {
+size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o) {
+  const int path = path_of(M, n, false);
   if (r > 0) {
-    if (small_m(M)) {
+    if (path == QLORA_PATH_GEMV) {
       if (!have_tsave) o.T = cv.take<float>((size_t)M * r * 4);
     } else {
       o.TS = cv.take<uint16_t>((size_t)M * lora_extra_cols(r) * 2);
     }
     o.proj = cv.take<char>(project_ws(M, k, r));
   }
+  if (path == QLORA_PATH_EXPANDED) o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, false));
   return cv.used;
 }
 
@@ -98,6 +108,7 @@ struct BwdWs {
   uint16_t* US = nullptr;
   void* proj = nullptr;
   void* grad = nullptr;
+  uint16_t* F = nullptr;  // expanded transposed operand (large M)
 };
 
 size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o) {
@@ -110,6 +121,7 @@ size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& 
     const size_t g1 = grad_ws(M, k, r), g2 = grad_ws(M, n, r);
     o.grad = cv.take<char>(g1 > g2 ? g1 : g2);
   }
+  if (path_of(M, n, true) == QLORA_PATH_EXPANDED) o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, true));
   return cv.used;
 }
 
@@ -166,7 +178,7 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int 
   Carver cv(nullptr);
   if (!is_bwd) {
     FwdWs o;
-    return fwd_ws(M, k, r, /*have_tsave=*/false, cv, o);
+    return fwd_ws(M, n, k, r, /*have_tsave=*/false, cv, o);
   }
   BwdWs o;
   return bwd_ws(M, n, k, r, /*have_tsaved=*/false, cv, o);
@@ -229,6 +241,41 @@ qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight* w, const void* X, int64_
                                 r, scale, static_cast<uint16_t*>(Y), static_cast<hipStream_t>(stream)));
 }
 
+int qlora_linear_path(int64_t M, int64_t n, int64_t k, int is_bwd) {
+  if (M < 0 || n < 1 || k < 1 || (k % QLORA_BLOCK) != 0 || (is_bwd != 0 && is_bwd != 1)) return -1;
+  return path_of(M, n, is_bwd == 1);
+}
+
+size_t qlora_nf4_expand_bytes(int64_t n, int64_t k, int r, int transposed) {
+  if (n < 1 || k < 1 || (k % QLORA_BLOCK) != 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (transposed != 0 && transposed != 1) return 0;
+  return expand_ws_bytes(n, k, r, transposed == 1);
+}
+
+qlora_status qlora_nf4_expand(const qlora_nf4_weight* w, const void* lr, int r, int transposed, void* out,
+                              size_t out_bytes, void* stream) {
+  const qlora_status s = check_weight(w);
+  if (s != QLORA_OK) return s;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (transposed != 0 && transposed != 1) return QLORA_ERR_INVALID_ARG;
+  if (!out || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!lr || !aligned16(lr))) return QLORA_ERR_INVALID_ARG;
+  if (out_bytes < expand_ws_bytes(w->n, w->k, r, transposed == 1)) return QLORA_ERR_WORKSPACE;
+  return hip_status(launch_expand(view_of(w), static_cast<const uint16_t*>(lr), r, transposed == 1,
+                                  static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_bf16_gemm(const void* act, int64_t M, int64_t kc, const void* split, int r, const void* F,
+                             int64_t nout, void* out, void* stream) {
+  if (M < 0 || kc < 8 || (kc % 8) != 0 || nout < 1 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if (!act || !F || !out || !aligned16(act) || !aligned16(F) || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!split || !aligned16(split))) return QLORA_ERR_INVALID_ARG;
+  return hip_status(launch_gemm_bf16(static_cast<const uint16_t*>(act), M, kc, static_cast<const uint16_t*>(split),
+                                     lora_extra_cols(r), static_cast<const uint16_t*>(F), nout,
+                                     static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r) {
   if (M < 1 || C < 1 || r < 1 || r > QLORA_MAX_RANK) return 0;
   return grad_ws(M, C, r);
@@ -257,26 +304,32 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t 
   {
     Carver probe(nullptr);
     FwdWs tmp;
-    const size_t need = fwd_ws(M, w->k, r, T_save != nullptr, probe, tmp);
+    const size_t need = fwd_ws(M, w->n, w->k, r, T_save != nullptr, probe, tmp);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
   FwdWs o;
-  fwd_ws(M, w->k, r, T_save != nullptr, cv, o);
+  fwd_ws(M, w->n, w->k, r, T_save != nullptr, cv, o);
   const Nf4View v = view_of(w);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* a = static_cast<const uint16_t*>(A);
   const uint16_t* b = static_cast<const uint16_t*>(B);
   uint16_t* y = static_cast<uint16_t*>(Y);
   hipError_t e = hipSuccess;
-  if (small_m(M)) {
+  const int path = path_of(M, w->n, false);
+  if (path == QLORA_PATH_GEMV) {
     float* T = T_save ? T_save : o.T;
     if (r > 0) e = do_project(x, M, w->k, a, 0, r, scale, T, nullptr, o.proj, st);
     if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, scale, y, st);
   } else {
     if (r > 0) e = do_project(x, M, w->k, a, 0, r, scale, T_save, o.TS, o.proj, st);
-    if (e == hipSuccess) e = launch_gemm_fwd(v, x, M, o.TS, b, r, y, st);
+    if (path == QLORA_PATH_FUSED) {
+      if (e == hipSuccess) e = launch_gemm_fwd(v, x, M, o.TS, b, r, y, st);
+    } else {
+      if (e == hipSuccess) e = launch_expand(v, b, r, false, o.F, st);
+      if (e == hipSuccess) e = launch_gemm_bf16(x, M, w->k, o.TS, lora_extra_cols(r), o.F, w->n, y, st);
+    }
   }
   return hip_status(e);
 }
@@ -314,8 +367,16 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const fl
   const uint16_t* b = static_cast<const uint16_t*>(B);
   hipError_t e = hipSuccess;
   if (r > 0 && (dX || dA)) e = do_project(dy, M, w->n, b, 1, r, scale, o.U, dX ? o.US : nullptr, o.proj, st);
-  if (e == hipSuccess && dX)
-    e = launch_gemm_dx(v, dy, M, r > 0 ? o.US : nullptr, a, r, static_cast<uint16_t*>(dX), st);
+  if (e == hipSuccess && dX) {
+    if (path_of(M, w->n, true) == QLORA_PATH_EXPANDED) {
+      e = launch_expand(v, a, r, true, o.F, st);
+      if (e == hipSuccess)
+        e = launch_gemm_bf16(dy, M, w->n, r > 0 ? o.US : nullptr, lora_extra_cols(r), o.F, w->k,
+                             static_cast<uint16_t*>(dX), st);
+    } else {
+      e = launch_gemm_dx(v, dy, M, r > 0 ? o.US : nullptr, a, r, static_cast<uint16_t*>(dX), st);
+    }
+  }
   if (e == hipSuccess && dA) e = do_grad(x, M, w->k, o.U, r, scale, dA, 0, accumulate, o.grad, st);
   if (e == hipSuccess && dB) {
     const float* T = T_saved;

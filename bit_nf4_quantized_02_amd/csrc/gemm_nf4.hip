@@ -40,16 +40,14 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_tile.h"
 #include "kernels.h"
 
 namespace qlora {
 
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kTileBytes = 256 * 128;  // one 256-row x 64-col bf16 tile
+using namespace gt;
 // dX weight tile: 64 contraction rows (n) x 256 output columns (k), bf16,
 // rows padded from 512 to 544 bytes so the 4 rows one transposing read
 // touches start 8 banks apart.
@@ -80,8 +78,6 @@ struct GemmArgs {
   uint16_t* out;
   int64_t nout;
 };
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 // ------------------------------------------------------------ activation tile
 // 256 rows x 8 chunks of 16 B: thread t owns chunks t + 512 i, i = 0..3
@@ -132,33 +128,18 @@ __device__ __forceinline__ void load_act(const GemmArgs& a, int64_t m0, int step
 }
 
 // Direct global -> LDS copy of the activation tile for `step` (16-B rows
-// required: the forward always, dX when n % 8 == 0). Each wavefront
-// instruction fills one contiguous 1 KB of LDS = 8 tile rows; lane l lands at
-// row 8 b + l / 8, physical chunk l % 8, so it fetches logical chunk
-// (l % 8) ^ (row & 7). Every address stays inside the operand: rows past M
-// read a clamped in-range row (their outputs are never stored), and chunks
-// past the last contraction column read the last in-range chunk (the weight
-// rows they meet are exactly zero, and the data are finite).
+// required: the forward always, dX when n % 8 == 0): the base operand for the
+// first nk_main steps, then the low-rank split columns. Chunks past the last
+// contraction column re-read the last in-range chunk; the weight rows they
+// meet are exactly zero and the data are finite.
 __device__ __forceinline__ void issue_act_lds(const GemmArgs& a, int64_t m0, int step, int nk_main, char* As) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // selects, not a branch: the pipelined loop body stays one basic block
   const bool extra = step >= nk_main;
   const uint16_t* src = extra ? a.act_x : a.act;
   const int64_t ld = extra ? (int64_t)a.kx : a.lda;
   const int64_t cols = extra ? (int64_t)a.kx : a.kc;
   const int64_t c0 = (int64_t)(extra ? step - nk_main : step) * kBK;
-#pragma unroll
-  for (int i = 0; i < 32 / kWaves; ++i) {
-    const int blk = wave * (32 / kWaves) + i;
-    const int row = blk * 8 + (lane >> 3);
-    const int lc = (lane & 7) ^ (row & 7);
-    const int64_t m = m0 + row;
-    const int64_t mc = m < a.M ? m : a.M - 1;
-    const int64_t c = c0 + 8 * lc;
-    const int64_t cc = c < cols ? c : cols - 8;
-    const uint16_t* g = src + mc * ld + cc;
-    __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(As + blk * 1024), 16,
-                                     0, 0);
-  }
+  issue_tile_lds(src, ld, a.M, m0, cols, c0, As);
 }
 
 __device__ __forceinline__ void store_act(char* As, const ActStage& st) {
@@ -303,53 +284,12 @@ __device__ __forceinline__ bf16x8 dx_b_frag(const char* Bc, int cb, int r0, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// ------------------------------------------------------------ tile order
-// Logical tile index of this workgroup: hardware dispatches workgroup i to XCD
-// i % 8, so give each XCD a contiguous range of logical tiles; within the
-// range, walk groups of 8 activation row-tiles column by column.
-__device__ __forceinline__ void tile_of(int64_t& tm, int64_t& tn, int64_t mt, int64_t nt) {
-  const int64_t total = mt * nt;
-  const int64_t bid = blockIdx.x;
-  int64_t lin = bid;
-  if (total % 8 == 0) lin = (bid % 8) * (total / 8) + bid / 8;
-  constexpr int64_t G = 8;
-  const int64_t group = lin / (G * nt);
-  const int64_t first_m = group * G;
-  const int64_t gm = (mt - first_m < G) ? mt - first_m : G;
-  const int64_t in = lin % (G * nt);
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
-
-// ------------------------------------------------------------ step barrier
-// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8. Waits until at most `vm` vector-memory operations are
-// outstanding and all LDS operations are done; expcnt is left free.
-template <int vm>
-constexpr int waitcnt_vm_lgkm0() {
-  return (vm & 0xF) | (0x7 << 4) | (0x0 << 8) | (((vm >> 4) & 0x3) << 14);
-}
-
-// End of a pipelined step: this wave's LDS writes are done and its direct
-// copies into the next activation buffer have landed (they were issued before
-// the `vm_after` weight loads, which may stay in flight); then all waves meet.
-// The empty asm statements keep the compiler from moving memory operations
-// across the barrier.
-template <int vm_after>
-__device__ __forceinline__ void step_barrier() {
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<vm_after>());
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // ------------------------------------------------------------ one step
 // MFMAs of the current step on (Ac, Bc) while the next step's weight tile is
 // expanded into Bn and its activation tile is copied into An. The four LDS
 // buffers are passed as restrict pointers: the compiler then knows the
 // direct copies into An cannot alias the fragment reads of Ac, and does not
 // wait for those copies before reading.
-constexpr int kTM = 4, kTN = 2;  // 32x32 MFMA tiles per wave (128 x 64 outputs)
 
 template <bool kDX, bool kVec>
 __device__ __forceinline__ void pipelined_step(const GemmArgs& a, int step, int nk_main, int64_t m0, int64_t n0,

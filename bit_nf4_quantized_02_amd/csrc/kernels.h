@@ -63,6 +63,17 @@ hipError_t launch_gemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const
 hipError_t launch_gemm_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const uint16_t* US,
                           const uint16_t* A, int r, uint16_t* dX, hipStream_t stream);
 
+// Expanded bf16 operand of the plain GEMM (forward [n, k + xc], or dX
+// [k, np + xc] with np = n rounded up to 64), LoRA factor appended.
+int64_t expand_pad_rows(int64_t n);
+size_t expand_ws_bytes(int64_t n, int64_t k, int r, bool transposed);
+hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool transposed, uint16_t* out,
+                         hipStream_t stream);
+
+// out = RN_bf16([act | split] F^T) over an expanded operand F [nout, kcp + kx].
+hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
+                            const uint16_t* f, int64_t nout, uint16_t* out, hipStream_t stream);
+
 // Small-M dequant-GEMV: Y = RN_bf16(X W'^T + scale * T B^T), M <= 16.
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T,
                        const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t stream);

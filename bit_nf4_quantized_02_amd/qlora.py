@@ -59,6 +59,10 @@ _SIGS = {
     "qlora_nf4_gemm_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
     "qlora_nf4_gemm_dx": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
     "qlora_nf4_gemv_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp]),
+    "qlora_linear_path": (_int, [_i64, _i64, _i64, _int]),
+    "qlora_nf4_expand_bytes": (_sz, [_i64, _i64, _int, _int]),
+    "qlora_nf4_expand": (_int, [_W, _vp, _int, _int, _vp, _sz, _vp]),
+    "qlora_bf16_gemm": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _i64, _vp, _vp]),
     "qlora_lowrank_grad_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "qlora_lowrank_grad": (_int, [_vp, _i64, _i64, _vp, _int, _f, _vp, _int, _int, _vp, _sz, _vp]),
     "qlora_silu_mul_fwd": (_int, [_vp, _vp, _vp, _i64, _vp]),
@@ -304,6 +308,48 @@ def nf4_gemm_dx(w: NF4Weight, dY: torch.Tensor, split: torch.Tensor | None, A: t
     _check(_lib.qlora_nf4_gemm_dx(ctypes.byref(st), _ptr(dY), M, _ptr(split), _ptr(A), r, _ptr(dX), _stream(stream)),
            "qlora_nf4_gemm_dx")
     return dX
+
+
+PATH_GEMV, PATH_FUSED, PATH_EXPANDED = 0, 1, 2
+
+
+def linear_path(M: int, n: int, k: int, is_bwd: bool) -> int:
+    p = _lib.qlora_linear_path(M, n, k, int(is_bwd))
+    if p < 0:
+        raise QLoraError(-1, "qlora_linear_path")
+    return p
+
+
+def nf4_expand_bytes(n: int, k: int, r: int, transposed: bool) -> int:
+    return int(_lib.qlora_nf4_expand_bytes(n, k, r, int(transposed)))
+
+
+def nf4_expand(w: NF4Weight, lr: torch.Tensor | None, r: int, transposed: bool, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """Expanded bf16 operand: [n, k + xc] (forward, lr = B) or [k, np + xc]
+    (transposed, for dX, lr = A); returned as a 2-D bf16 tensor."""
+    xc = lowrank_split_cols(r)
+    if transposed:
+        rows, cols = w.k, ((w.n + 63) // 64) * 64 + xc
+    else:
+        rows, cols = w.n, w.k + xc
+    nbytes = nf4_expand_bytes(w.n, w.k, r, transposed)
+    if out is None:
+        out = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=w.codes.device)
+    st = w.struct()
+    _check(_lib.qlora_nf4_expand(ctypes.byref(st), _ptr(lr), r, int(transposed), _ptr(out), out.numel() * 2,
+                                 _stream(stream)), "qlora_nf4_expand")
+    return out.view(-1)[: rows * cols].view(rows, cols)
+
+
+def bf16_gemm(act: torch.Tensor, split: torch.Tensor | None, r: int, F: torch.Tensor, nout: int,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    M, kc = act.shape
+    if out is None:
+        out = torch.empty((M, nout), dtype=torch.bfloat16, device=act.device)
+    _check(_lib.qlora_bf16_gemm(_ptr(act), M, kc, _ptr(split), r, _ptr(F), nout, _ptr(out), _stream(stream)),
+           "qlora_bf16_gemm")
+    return out
 
 
 def nf4_gemv_fwd(w: NF4Weight, X: torch.Tensor, T: torch.Tensor | None, B: torch.Tensor | None, scale: float,

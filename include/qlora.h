@@ -158,9 +158,10 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int 
  *   Y = RN_bf16( X W'^T + scale * T B^T ), accumulated in fp32.
  * X (device) [M, k] bf16; A (device) [r, k] bf16; B (device) [n, r] bf16;
  * Y (device) [M, n] bf16; T_save (device, nullable) [M, r] fp32;
- * scale = alpha / r, the LoRA scale [QX "Step 3"]. Small M (<= 16) uses a
- * bandwidth-oriented dequant-GEMV; larger M a matrix-core GEMM that expands
- * each 64-block to bf16 in on-chip memory.
+ * scale = alpha / r, the LoRA scale [QX "Step 3"]. The kernels depend on M
+ * (qlora_linear_path): a bandwidth-oriented dequant-GEMV for M <= 16, a
+ * matrix-core GEMM expanding each 64-block in on-chip memory for medium M,
+ * and for large M one expansion into workspace followed by a bf16 GEMM.
  * ws (device) must hold qlora_linear_workspace_bytes(M, n, k, r, 0) bytes.
  * Errors: INVALID_ARG, SHAPE, WORKSPACE, HIP.
  */
@@ -245,6 +246,57 @@ qlora_status qlora_nf4_gemm_dx(const qlora_nf4_weight *w, const void *dY, int64_
  */
 qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight *w, const void *X, int64_t M, const float *T,
                                 const void *B, int r, float scale, void *Y, void *stream);
+
+/*
+ * Which kernels a pass uses at this size; qlora_linear_fwd (is_bwd = 0) and
+ * qlora_linear_bwd (is_bwd = 1, the dX product) make exactly this choice:
+ *   QLORA_PATH_GEMV      M <= 16, forward: qlora_nf4_gemv_fwd (one pass over
+ *                        the packed codes, bandwidth-bound);
+ *   QLORA_PATH_FUSED     qlora_nf4_gemm_fwd / qlora_nf4_gemm_dx (each 64-block
+ *                        expanded in on-chip memory, once per 256-row tile);
+ *   QLORA_PATH_EXPANDED  M >= QLORA_EXPAND_MIN_M (and n % 8 == 0 for dX):
+ *                        qlora_nf4_expand once into workspace, then
+ *                        qlora_bf16_gemm (each weight expanded once per pass
+ *                        instead of M / 256 times).
+ * Returns -1 on bad arguments.
+ */
+#define QLORA_PATH_GEMV 0
+#define QLORA_PATH_FUSED 1
+#define QLORA_PATH_EXPANDED 2
+#define QLORA_EXPAND_MIN_M 1024
+int qlora_linear_path(int64_t M, int64_t n, int64_t k, int is_bwd);
+
+/* Bytes of the expanded operand of qlora_nf4_expand (0 on bad arguments). */
+size_t qlora_nf4_expand_bytes(int64_t n, int64_t k, int r, int transposed);
+
+/*
+ * Expand the encoded weight once to the bf16 operand of qlora_bf16_gemm
+ * [QQ three-piece summary, piece 2: expand to 16 bits right before the
+ * multiply], with the LoRA factor appended as xc = qlora_lowrank_split_cols(r)
+ * extra contraction columns:
+ *   transposed = 0 (forward): out [n, k + xc],  out[i, c] = W'[i, c],
+ *       out[i, k + j] = B[i, j mod r] for j < 2r, else 0;  lr = B [n, r].
+ *   transposed = 1 (dX): np = n rounded up to 64, out [k, np + xc],
+ *       out[c, i] = W'[i, c] (0 for n <= i < np),
+ *       out[c, np + j] = A[j mod r, c] for j < 2r, else 0;  lr = A [r, k].
+ * W' values are bit-identical to qlora_dequant's. out (device) must hold
+ * qlora_nf4_expand_bytes(n, k, r, transposed) bytes (out_bytes).
+ * Errors: INVALID_ARG, SHAPE, WORKSPACE (out_bytes too small), HIP.
+ */
+qlora_status qlora_nf4_expand(const qlora_nf4_weight *w, const void *lr, int r, int transposed, void *out,
+                              size_t out_bytes, void *stream);
+
+/*
+ * bf16 MFMA GEMM over an expanded operand F from qlora_nf4_expand:
+ *   out[m, j] = RN_bf16( sum_{c < kc} act[m, c] F[j, c] + sum_x split[m, x] F[j, kcp + x] )
+ * act (device) [M, kc] bf16 (X with kc = k for the forward, dY with kc = n
+ * for dX; kc % 8 == 0); kcp = kc rounded up to 64; split (device) [M, xc]
+ * bf16 rows from qlora_lowrank_project (ignored for r = 0); F (device)
+ * [nout, kcp + xc]; out (device) [M, nout] bf16 (nout = n forward, k for dX).
+ * Errors: INVALID_ARG, SHAPE, HIP.
+ */
+qlora_status qlora_bf16_gemm(const void *act, int64_t M, int64_t kc, const void *split, int r, const void *F,
+                             int64_t nout, void *out, void *stream);
 
 /* Workspace bytes of qlora_lowrank_grad (0 on bad arguments). */
 size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r);

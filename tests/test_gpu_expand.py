@@ -1,0 +1,131 @@
+"""GPU parity of the large-M path: expansion once per pass + bf16 GEMM.
+
+* The expanded operands are compared bit for bit with the oracle's bf16
+  expansion of its own encoding (forward [n, k + xc]; dX transposed
+  [k, np + xc]), including the appended LoRA columns, the zero padding and
+  weights whose row count is not a multiple of 64 or 256.
+* qlora_bf16_gemm over those operands, and qlora_linear_fwd / _bwd at token
+  counts that select the expanded path, are compared with the fp64 oracle
+  (relative Frobenius error <= 2e-3), on shapes with ragged M, N and K tiles.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from bit_nf4_quantized_02_amd import synth
+from oracle import linear as olin
+
+from gpu_util import TOL, bits16, f32, oracle_encode, report, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_nf4_quantized_02_amd import qlora
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return qlora
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("n,k,r", [(200, 192, 8), (1000, 512, 16), (64, 64, 0), (77, 320, 3), (600, 256, 64),
+                                   (130, 128, 128)])
+def test_expanded_operands_bitwise(q, n, k, r):
+    say(f"case: expand n={n} k={k} r={r}")
+    W = synth.weight_bf16(n, k, 0.02, 55, n, k)
+    A = synth.lora_A(max(r, 1), k, 55, n, 1)[:r].contiguous()
+    B = synth.lora_B(n, max(r, 1), 55, n, 2)[:, :r].contiguous()
+    gw = q.quantize_nf4(W.cuda())
+    Fw = q.nf4_expand(gw, B.cuda() if r else None, r, transposed=False)
+    Fx = q.nf4_expand(gw, A.cuda() if r else None, r, transposed=True)
+    torch.cuda.synchronize()
+    wb = oracle_encode(W).dequant_bits()          # [n, k] uint16, the oracle's W'
+    xc = q.lowrank_split_cols(r)
+    np_ = ((n + 63) // 64) * 64
+    fw, fx = _bits(Fw), _bits(Fx)
+    assert fw.shape == (n, k + xc) and fx.shape == (k, np_ + xc)
+    assert np.array_equal(fw[:, :k], wb)
+    assert np.array_equal(fx[:, :n], wb.T)
+    assert not fx[:, n:np_].any()
+    bb, ab = _bits(B), _bits(A)
+    for j in range(xc):
+        want_f = bb[:, j % r] if j < 2 * r else np.zeros(n, np.uint16)
+        want_x = ab[j % r, :] if j < 2 * r else np.zeros(k, np.uint16)
+        assert np.array_equal(fw[:, k + j], want_f), j
+        assert np.array_equal(fx[:, np_ + j], want_x), j
+
+
+@pytest.mark.parametrize("m,n,k,r", [(300, 200, 192, 8), (520, 264, 640, 16), (17, 72, 64, 1), (256, 512, 256, 0),
+                                     (700, 96, 512, 64)])
+def test_bf16_gemm_building_blocks(q, m, n, k, r):
+    """T/U split + expansion + bf16 GEMM, forward and dX, against the oracle."""
+    say(f"case: bf16 gemm M={m} N={n} K={k} r={r}")
+    s = 2.0 if r else 0.0
+    li = synth.linear_inputs(78, m + n, 0, n, k, m, r, s, sigma=0.02)
+    gw = q.quantize_nf4(li.W.cuda())
+    X, dY = li.X.cuda(), li.dY.cuda()
+    A = li.A.cuda() if r else None
+    B = li.B.cuda() if r else None
+    TS = US = None
+    if r:
+        _, TS = q.lowrank_project(X, A, 0, s, want_out=False, want_split=True)
+        _, US = q.lowrank_project(dY, B, 1, s, want_out=False, want_split=True)
+    Fw = q.nf4_expand(gw, B, r, transposed=False)
+    Fx = q.nf4_expand(gw, A, r, transposed=True)
+    Y = q.bf16_gemm(X, TS, r, Fw, n)
+    dX = q.bf16_gemm(dY, US, r, Fx, k)
+    torch.cuda.synchronize()
+    Wd = oracle_encode(li.W).dequant()
+    Xo, Ao, Bo, dYo = (t.float().numpy() for t in (li.X, li.A, li.B, li.dY))
+    Yr, _ = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
+    dXr, _, _, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
+    assert report("Y", f32(Y), Yr) <= TOL
+    assert report("dX", f32(dX), dXr) <= TOL
+
+
+@pytest.mark.parametrize("m,n,k,r", [(1030, 520, 384, 16), (1024, 100, 256, 8), (1300, 264, 192, 64)])
+def test_linear_at_expanded_sizes(q, m, n, k, r):
+    """qlora_linear_fwd/bwd where the path is the expanded one (n % 8 != 0
+    keeps dX on the fused kernel)."""
+    fwd_path = q.linear_path(m, n, k, False)
+    bwd_path = q.linear_path(m, n, k, True)
+    say(f"case: linear M={m} N={n} K={k} r={r} paths fwd={fwd_path} bwd={bwd_path}")
+    assert fwd_path == q.PATH_EXPANDED
+    assert bwd_path == (q.PATH_EXPANDED if n % 8 == 0 else q.PATH_FUSED)
+    s = 0.5
+    li = synth.linear_inputs(79, m, 0, n, k, m, r, s, sigma=0.02)
+    gw = q.quantize_nf4(li.W.cuda())
+    X, dY, A, B = li.X.cuda(), li.dY.cuda(), li.A.cuda(), li.B.cuda()
+    Y, T = q.linear_fwd(gw, X, A, B, s)
+    dX, dA, dB = q.linear_bwd(gw, X, T, dY, A, B, s)
+    torch.cuda.synchronize()
+    Wd = oracle_encode(li.W).dequant()
+    Xo, Ao, Bo, dYo = (t.float().numpy() for t in (li.X, li.A, li.B, li.dY))
+    Yr, _ = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
+    dXr, dAr, dBr, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
+    assert report("Y", f32(Y), Yr) <= TOL
+    assert report("dX", f32(dX), dXr) <= TOL
+    assert report("dA", f32(dA), dAr, floor=False) <= TOL
+    assert report("dB", f32(dB), dBr, floor=False) <= TOL
+
+
+def test_expanded_and_fused_agree_closely(q):
+    """Both large-M paths on the same inputs: each within the bar of the
+    oracle, and within a few bf16 ulps of each other (different fp32
+    summation orders only)."""
+    m, n, k, r, s = 512, 256, 512, 16, 2.0
+    li = synth.linear_inputs(80, 0, 0, n, k, m, r, s, sigma=0.02)
+    gw = q.quantize_nf4(li.W.cuda())
+    X, A, B = li.X.cuda(), li.A.cuda(), li.B.cuda()
+    _, TS = q.lowrank_project(X, A, 0, s, want_out=False, want_split=True)
+    Y1 = q.nf4_gemm_fwd(gw, X, TS, B)
+    Y2 = q.bf16_gemm(X, TS, r, q.nf4_expand(gw, B, r, transposed=False), n)
+    torch.cuda.synchronize()
+    d = (f32(Y1) - f32(Y2))
+    ref = np.abs(f32(Y1)).max()
+    say(f"  fused vs expanded: max |diff| {np.abs(d).max():.3e} (max |Y| {ref:.3e})")
+    assert np.abs(d).max() <= 2 ** -6 * ref
