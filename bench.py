@@ -113,8 +113,8 @@ class LinearPlan:
         self.fwd, self.bwd = [], []
         # the kernels qlora_linear_fwd / _bwd choose at this size (or a forced
         # large-M variant, for comparing the two)
-        self.path_fwd = q.linear_path(M, N, K, False)
-        self.path_bwd = q.linear_path(M, N, K, True)
+        self.path_fwd = q.linear_path(M, N, K, r, False)
+        self.path_bwd = q.linear_path(M, N, K, r, True)
         if force_path is not None and self.path_fwd != q.PATH_GEMV:
             self.path_fwd = force_path
             self.path_bwd = force_path if (force_path != q.PATH_EXPANDED or N % 8 == 0) else q.PATH_FUSED

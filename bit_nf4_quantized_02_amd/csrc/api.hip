@@ -46,9 +46,11 @@ struct Carver {
 bool small_m(int64_t M) { return M <= 16; }
 
 // Kernel choice per pass (the rule qlora_linear_path documents).
-int path_of(int64_t M, int64_t n, bool bwd) {
+int path_of(int64_t M, int64_t n, int64_t k, int r, bool bwd) {
   if (!bwd && small_m(M)) return QLORA_PATH_GEMV;
-  if (M >= QLORA_EXPAND_MIN_M && (!bwd || n % 8 == 0)) return QLORA_PATH_EXPANDED;
+  const int xc = lora_extra_cols(r);
+  const bool fits = bwd ? gemm_bf16_offsets_fit(M, n, xc, k) : gemm_bf16_offsets_fit(M, k, xc, n);
+  if (M >= QLORA_EXPAND_MIN_M && fits && (!bwd || n % 8 == 0)) return QLORA_PATH_EXPANDED;
   return QLORA_PATH_FUSED;
 }
 
@@ -89,7 +91,7 @@ struct FwdWs {
 };
 
 size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o) {
-  const int path = path_of(M, n, false);
+  const int path = path_of(M, n, k, r, false);
   if (r > 0) {
     if (path == QLORA_PATH_GEMV) {
       if (!have_tsave) o.T = cv.take<float>((size_t)M * r * 4);
@@ -121,7 +123,7 @@ size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& 
     const size_t g1 = grad_ws(M, k, r), g2 = grad_ws(M, n, r);
     o.grad = cv.take<char>(g1 > g2 ? g1 : g2);
   }
-  if (path_of(M, n, true) == QLORA_PATH_EXPANDED) o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, true));
+  if (path_of(M, n, k, r, true) == QLORA_PATH_EXPANDED) o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, true));
   return cv.used;
 }
 
@@ -241,9 +243,10 @@ qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight* w, const void* X, int64_
                                 r, scale, static_cast<uint16_t*>(Y), static_cast<hipStream_t>(stream)));
 }
 
-int qlora_linear_path(int64_t M, int64_t n, int64_t k, int is_bwd) {
-  if (M < 0 || n < 1 || k < 1 || (k % QLORA_BLOCK) != 0 || (is_bwd != 0 && is_bwd != 1)) return -1;
-  return path_of(M, n, is_bwd == 1);
+int qlora_linear_path(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
+  if (M < 0 || n < 1 || k < 1 || (k % QLORA_BLOCK) != 0 || r < 0 || r > QLORA_MAX_RANK) return -1;
+  if (is_bwd != 0 && is_bwd != 1) return -1;
+  return path_of(M, n, k, r, is_bwd == 1);
 }
 
 size_t qlora_nf4_expand_bytes(int64_t n, int64_t k, int r, int transposed) {
@@ -271,6 +274,7 @@ qlora_status qlora_bf16_gemm(const void* act, int64_t M, int64_t kc, const void*
   if (M == 0) return QLORA_OK;
   if (!act || !F || !out || !aligned16(act) || !aligned16(F) || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
   if (r > 0 && (!split || !aligned16(split))) return QLORA_ERR_INVALID_ARG;
+  if (!gemm_bf16_offsets_fit(M, kc, lora_extra_cols(r), nout)) return QLORA_ERR_SHAPE;
   return hip_status(launch_gemm_bf16(static_cast<const uint16_t*>(act), M, kc, static_cast<const uint16_t*>(split),
                                      lora_extra_cols(r), static_cast<const uint16_t*>(F), nout,
                                      static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
@@ -317,7 +321,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t 
   const uint16_t* b = static_cast<const uint16_t*>(B);
   uint16_t* y = static_cast<uint16_t*>(Y);
   hipError_t e = hipSuccess;
-  const int path = path_of(M, w->n, false);
+  const int path = path_of(M, w->n, w->k, r, false);
   if (path == QLORA_PATH_GEMV) {
     float* T = T_save ? T_save : o.T;
     if (r > 0) e = do_project(x, M, w->k, a, 0, r, scale, T, nullptr, o.proj, st);
@@ -368,7 +372,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const fl
   hipError_t e = hipSuccess;
   if (r > 0 && (dX || dA)) e = do_project(dy, M, w->n, b, 1, r, scale, o.U, dX ? o.US : nullptr, o.proj, st);
   if (e == hipSuccess && dX) {
-    if (path_of(M, w->n, true) == QLORA_PATH_EXPANDED) {
+    if (path_of(M, w->n, w->k, r, true) == QLORA_PATH_EXPANDED) {
       e = launch_expand(v, a, r, true, o.F, st);
       if (e == hipSuccess)
         e = launch_gemm_bf16(dy, M, w->n, r > 0 ? o.US : nullptr, lora_extra_cols(r), o.F, w->k,

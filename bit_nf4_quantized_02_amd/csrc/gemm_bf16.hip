@@ -15,6 +15,15 @@
 // global_load_lds_dwordx4 (no registers, no VALU), double-buffered: the copies
 // for step s + 1 are issued at the start of step s and waited for at its end,
 // so one barrier per step separates filling a buffer from reading it.
+//
+// Per-step cost is kept off the vector ALU: every lane's byte offset inside
+// each operand (row, swizzled chunk) is computed once, and a step only moves
+// the wave-uniform base pointer by 128 bytes, so each copy is one
+// scalar-base + 32-bit-offset instruction. Inside a step the next substep's
+// fragment reads are interleaved one-to-one with the current substep's MFMAs
+// (scheduling groups), so LDS latency hides behind the matrix core. The
+// epilogue stages each wave's bf16 outputs through LDS and writes full 16-byte
+// row segments.
 #include "common.h"
 #include "gemm_tile.h"
 #include "kernels.h"
@@ -26,8 +35,8 @@ namespace {
 using namespace gt;
 
 struct BfArgs {
-  const uint16_t* act;   // [M, lda] bf16, kc columns used
-  int64_t lda, M, kc;
+  const uint16_t* act;   // [M, kc] bf16
+  int64_t M, kc;
   const uint16_t* act_x; // [M, kx] low-rank split columns
   int kx;
   const uint16_t* f;     // [nout, ldf] expanded operand, ldf = 64 * nk_main + kx
@@ -35,21 +44,69 @@ struct BfArgs {
   uint16_t* out;         // [M, nout]
 };
 
-__device__ __forceinline__ void issue_step(const BfArgs& a, int64_t m0, int64_t n0, int step, int nk_main,
-                                           char* As, char* Bs) {
-  const bool extra = step >= nk_main;
-  const uint16_t* src = extra ? a.act_x : a.act;
-  const int64_t ld = extra ? (int64_t)a.kx : a.lda;
-  const int64_t cols = extra ? (int64_t)a.kx : a.kc;
-  const int64_t c0 = (int64_t)(extra ? step - nk_main : step) * kBK;
-  issue_tile_lds(src, ld, a.M, m0, cols, c0, As);
-  issue_tile_lds(a.f, a.ldf, a.nout, n0, a.ldf, (int64_t)step * kBK, Bs);
+constexpr int kCopies = 32 / kWaves;  // 1 KB copies per wave per operand tile
+
+// Byte offsets of this lane's copies, relative to the operands' base pointer
+// advanced to the step's first column. For the last base step of a ragged
+// contraction (kc % 64 != 0) the column is clamped to the last in-range chunk
+// (the F rows it meets there are exactly zero).
+// (Vectors, not arrays: an array in a struct may be placed in LDS by the
+// compiler, which would turn every copy into an LDS read first.)
+static_assert(kCopies == 4, "one u32x4 of offsets per operand");
+struct CopyPlan {
+  u32x4 a;      // activation, base steps
+  u32x4 alast;  // activation, last base step (clamped columns)
+  u32x4 x;      // low-rank split columns
+  u32x4 f;      // expanded operand
+};
+
+__device__ __forceinline__ void make_plan(const BfArgs& a, int64_t m0, int64_t n0, int nk_main, CopyPlan& p) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int row = (wave * kCopies + i) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ swz_key(row);
+    const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
+    const int64_t n = n0 + row < a.nout ? n0 + row : a.nout - 1;
+    p.a[i] = (uint32_t)((m * a.kc + 8 * lc) * 2);
+    const int64_t cl = (int64_t)(nk_main - 1) * kBK + 8 * lc;
+    const int64_t cc = cl < a.kc ? cl : a.kc - 8;
+    p.alast[i] = (uint32_t)((m * a.kc + cc - (int64_t)(nk_main - 1) * kBK) * 2);
+    p.x[i] = (uint32_t)((m * a.kx + 8 * lc) * 2);
+    p.f[i] = (uint32_t)((n * a.ldf + 8 * lc) * 2);
+  }
+}
+
+__device__ __forceinline__ void copy16(const char* base, uint32_t off, char* dst) {
+  __builtin_amdgcn_global_load_lds((const void*)(base + off), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// Copies of step `step` into (As, Bs). The branch is uniform (it depends on
+// the step only), so both bases stay scalar.
+__device__ __forceinline__ void issue_step(const BfArgs& a, const CopyPlan& p, int step, int nk_main, char* As,
+                                           char* Bs) {
+  const int wave = threadIdx.x >> 6;
+  char* const as = As + wave * kCopies * 1024;
+  char* const bs = Bs + wave * kCopies * 1024;
+  if (step < nk_main) {
+    const char* base = reinterpret_cast<const char*>(a.act) + (int64_t)step * (kBK * 2);
+    const u32x4 off = step == nk_main - 1 ? p.alast : p.a;
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy16(base, off[i], as + i * 1024);
+  } else {
+    const char* base = reinterpret_cast<const char*>(a.act_x) + (int64_t)(step - nk_main) * (kBK * 2);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy16(base, p.x[i], as + i * 1024);
+  }
+  const char* fbase = reinterpret_cast<const char*>(a.f) + (int64_t)step * (kBK * 2);
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) copy16(fbase, p.f[i], bs + i * 1024);
 }
 
 // One step: MFMAs on (Ac, Bc) while the copies of step + 1 fill (An, Bn).
 // Restrict pointers tell the compiler the copies cannot alias the fragment
 // reads, so it does not wait for them before reading.
-__device__ __forceinline__ void bf16_step(const BfArgs& a, int step, int nk, int nk_main, int64_t m0, int64_t n0,
+__device__ __forceinline__ void bf16_step(const BfArgs& a, const CopyPlan& p, int step, int nk, int nk_main,
                                           const char* __restrict__ Ac, const char* __restrict__ Bc,
                                           char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -66,7 +123,7 @@ __device__ __forceinline__ void bf16_step(const BfArgs& a, int step, int nk, int
   };
   read_frags(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  issue_step(a, m0, n0, s1, nk_main, An, Bn);
+  issue_step(a, p, s1, nk_main, An, Bn);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -78,6 +135,17 @@ __device__ __forceinline__ void bf16_step(const BfArgs& a, int step, int nk, int
       for (int j = 0; j < kTN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
   }
+  // schedule: for substeps 0..2 one fragment read (of the next substep) per
+  // MFMA, then the last substep's MFMAs
+  constexpr int kReads = kTM + kTN, kMfma = kTM * kTN;
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+    for (int g = 0; g < kMfma; ++g) {
+      if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    }
+  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
   step_barrier<0>();
 }
 
@@ -97,6 +165,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   const int nk_main = (int)cdiv(a.kc, (int64_t)kBK);
   const int nk = nk_main + a.kx / kBK;
 
+  CopyPlan plan;
+  make_plan(a, m0, n0, nk_main, plan);
+
   f32x16 acc[kTM][kTN];
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
@@ -105,21 +176,63 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  issue_step(a, m0, n0, 0, nk_main, As0, Bs0);
+  issue_step(a, plan, 0, nk_main, As0, Bs0);
   step_barrier<0>();
   for (int step = 0; step < nk; step += 2) {
-    bf16_step(a, step, nk, nk_main, m0, n0, As0, Bs0, As1, Bs1, acc);
-    if (step + 1 < nk) bf16_step(a, step + 1, nk, nk_main, m0, n0, As1, Bs1, As0, Bs0, acc);
+    bf16_step(a, plan, step, nk, nk_main, As0, Bs0, As1, Bs1, acc);
+    if (step + 1 < nk) bf16_step(a, plan, step + 1, nk, nk_main, As1, Bs1, As0, Bs0, acc);
   }
-  store_acc_bf16(acc, a.out, a.nout, a.M, a.nout, m0, n0, wm0, wn0, lane);
+
+  // Epilogue: each wave writes its 128 x 64 bf16 block (16 KB) into its own
+  // LDS region (all copies have landed and all fragment reads are done: the
+  // last step ended with a barrier after waiting for both), then stores
+  // 16-byte row segments.
+  {
+    char* const bufs0 = wave < 4 ? (wave < 2 ? As0 : As1) : (wave < 6 ? Bs0 : Bs1);
+    uint16_t* reg = reinterpret_cast<uint16_t*>(bufs0 + (wave & 1) * 16384);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          reg[rr * 64 + j * 32 + (lane & 31)] = to_bf16_bits(acc[i][j][v]);
+        }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // this wave's LDS writes are done
+    // 128 rows x 8 chunks of 16 B
+#pragma unroll 4
+    for (int q = lane; q < 128 * 8; q += 64) {
+      const int rr = q >> 3, cc = q & 7;
+      const int64_t m = m0 + wm0 + rr, n = n0 + wn0 + cc * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + rr * 64 + cc * 8);
+      if (m < a.M) {
+        if (n + 8 <= a.nout && (a.nout & 7) == 0) {
+          *reinterpret_cast<u32x4*>(a.out + m * a.nout + n) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            if (n + e < a.nout) a.out[m * a.nout + n + e] = (uint16_t)h;
+          }
+        }
+      }
+    }
+  }
 }
 
 }  // namespace
 
+bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
+  const int64_t ldf = cdiv(kc, (int64_t)kBK) * kBK + kx;
+  const int64_t lim = (int64_t)1 << 32;
+  return M * kc * 2 < lim && M * (int64_t)kx * 2 < lim && nout * ldf * 2 < lim;
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                             const uint16_t* f, int64_t nout, uint16_t* out, hipStream_t stream) {
   BfArgs a{};
-  a.act = act; a.lda = kc; a.M = M; a.kc = kc;
+  a.act = act; a.M = M; a.kc = kc;
   a.act_x = split; a.kx = kx;
   a.f = f; a.ldf = cdiv(kc, (int64_t)kBK) * kBK + kx; a.nout = nout;
   a.out = out;

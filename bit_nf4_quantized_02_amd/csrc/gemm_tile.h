@@ -5,8 +5,13 @@
 // Workgroup tile 256 x 256 outputs, 64-deep contraction steps, 512 threads =
 // 8 waves (two per SIMD) in a 2 x 4 grid, each wave a 128 x 64 sub-tile of
 // v_mfma_f32_32x32x16_bf16. An operand tile is 256 rows x 64 bf16 (128 B per
-// row = 8 chunks of 16 B); chunk c of row r is stored at chunk c ^ (r & 7), so
-// the 32 rows one fragment read touches fall in distinct LDS banks.
+// row = 8 chunks of 16 B); chunk c of row r is stored at chunk c ^ key(r),
+// key(r) = (r & 7) ^ ((r >> 3) & 1). A fragment read sends 16 consecutive
+// rows of one logical chunk to the LDS per cycle (256 B across its 64 banks):
+// consecutive rows alternate 128-B halves, and the key gives rows r and r + 8
+// (same half) different chunks, so the 16 reads hit 16 distinct 16-B bank
+// groups. (The plain r & 7 key maps r and r + 8 to the same banks: measured
+// as one conflict cycle per LDS cycle.)
 #pragma once
 
 #include "common.h"
@@ -20,14 +25,15 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kTileBytes = 256 * 128;  // one 256-row x 64-col bf16 tile
 constexpr int kTM = 4, kTN = 2;        // 32x32 MFMA tiles per wave (128 x 64 outputs)
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
 
 // Direct global -> LDS copy of one 256 x 64 tile: rows r0 .. r0+255 and
 // columns c0 .. c0+63 of a row-major bf16 matrix with leading dimension ld
 // (rows and ld*2 bytes must keep every 16-byte chunk 16-byte aligned). Each
 // wavefront instruction fills one contiguous 1 KB of LDS = 8 tile rows; lane l
 // lands at row 8 b + l / 8, physical chunk l % 8, so it fetches logical chunk
-// (l % 8) ^ (row & 7). Every address stays inside the matrix: rows past
+// (l % 8) ^ key(row). Every address stays inside the matrix: rows past
 // `rows` read the last row and chunks past `cols` read the last chunk; the
 // caller makes those positions harmless (outputs never stored, or the other
 // operand is zero there).
@@ -38,7 +44,7 @@ __device__ __forceinline__ void issue_tile_lds(const uint16_t* src, int64_t ld, 
   for (int i = 0; i < 32 / kWaves; ++i) {
     const int blk = wave * (32 / kWaves) + i;
     const int row = blk * 8 + (lane >> 3);
-    const int lc = (lane & 7) ^ (row & 7);
+    const int lc = (lane & 7) ^ swz_key(row);
     const int64_t m = r0 + row;
     const int64_t mc = m < rows ? m : rows - 1;
     const int64_t c = c0 + 8 * lc;

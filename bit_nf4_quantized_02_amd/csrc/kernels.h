@@ -71,6 +71,9 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
                          hipStream_t stream);
 
 // out = RN_bf16([act | split] F^T) over an expanded operand F [nout, kcp + kx].
+// The kernel addresses each operand with 32-bit byte offsets: every operand
+// must be smaller than 4 GiB (gemm_bf16_offsets_fit).
+bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout);
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                             const uint16_t* f, int64_t nout, uint16_t* out, hipStream_t stream);
 

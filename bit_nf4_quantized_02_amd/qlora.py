@@ -59,7 +59,7 @@ _SIGS = {
     "qlora_nf4_gemm_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
     "qlora_nf4_gemm_dx": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
     "qlora_nf4_gemv_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp]),
-    "qlora_linear_path": (_int, [_i64, _i64, _i64, _int]),
+    "qlora_linear_path": (_int, [_i64, _i64, _i64, _int, _int]),
     "qlora_nf4_expand_bytes": (_sz, [_i64, _i64, _int, _int]),
     "qlora_nf4_expand": (_int, [_W, _vp, _int, _int, _vp, _sz, _vp]),
     "qlora_bf16_gemm": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _i64, _vp, _vp]),
@@ -313,8 +313,8 @@ def nf4_gemm_dx(w: NF4Weight, dY: torch.Tensor, split: torch.Tensor | None, A: t
 PATH_GEMV, PATH_FUSED, PATH_EXPANDED = 0, 1, 2
 
 
-def linear_path(M: int, n: int, k: int, is_bwd: bool) -> int:
-    p = _lib.qlora_linear_path(M, n, k, int(is_bwd))
+def linear_path(M: int, n: int, k: int, r: int, is_bwd: bool) -> int:
+    p = _lib.qlora_linear_path(M, n, k, r, int(is_bwd))
     if p < 0:
         raise QLoraError(-1, "qlora_linear_path")
     return p

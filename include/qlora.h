@@ -254,17 +254,18 @@ qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight *w, const void *X, int64_
  *                        the packed codes, bandwidth-bound);
  *   QLORA_PATH_FUSED     qlora_nf4_gemm_fwd / qlora_nf4_gemm_dx (each 64-block
  *                        expanded in on-chip memory, once per 256-row tile);
- *   QLORA_PATH_EXPANDED  M >= QLORA_EXPAND_MIN_M (and n % 8 == 0 for dX):
+ *   QLORA_PATH_EXPANDED  M >= QLORA_EXPAND_MIN_M (and n % 8 == 0 for dX, and
+ *                        every operand of the bf16 GEMM under 4 GiB):
  *                        qlora_nf4_expand once into workspace, then
  *                        qlora_bf16_gemm (each weight expanded once per pass
  *                        instead of M / 256 times).
- * Returns -1 on bad arguments.
+ * r is the LoRA rank. Returns -1 on bad arguments.
  */
 #define QLORA_PATH_GEMV 0
 #define QLORA_PATH_FUSED 1
 #define QLORA_PATH_EXPANDED 2
 #define QLORA_EXPAND_MIN_M 1024
-int qlora_linear_path(int64_t M, int64_t n, int64_t k, int is_bwd);
+int qlora_linear_path(int64_t M, int64_t n, int64_t k, int r, int is_bwd);
 
 /* Bytes of the expanded operand of qlora_nf4_expand (0 on bad arguments). */
 size_t qlora_nf4_expand_bytes(int64_t n, int64_t k, int r, int transposed);
@@ -293,6 +294,7 @@ qlora_status qlora_nf4_expand(const qlora_nf4_weight *w, const void *lr, int r, 
  * for dX; kc % 8 == 0); kcp = kc rounded up to 64; split (device) [M, xc]
  * bf16 rows from qlora_lowrank_project (ignored for r = 0); F (device)
  * [nout, kcp + xc]; out (device) [M, nout] bf16 (nout = n forward, k for dX).
+ * Each operand (act, split, F) must be smaller than 4 GiB.
  * Errors: INVALID_ARG, SHAPE, HIP.
  */
 qlora_status qlora_bf16_gemm(const void *act, int64_t M, int64_t kc, const void *split, int r, const void *F,

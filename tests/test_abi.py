@@ -126,18 +126,18 @@ def test_oracle_and_library_are_independent():
 
 def test_path_choice_and_expanded_sizes(q):
     # forward: GEMV up to 16 tokens, fused below the expansion threshold, expanded above
-    assert q.linear_path(1, 4096, 4096, False) == q.PATH_GEMV
-    assert q.linear_path(16, 4096, 4096, False) == q.PATH_GEMV
-    assert q.linear_path(17, 4096, 4096, False) == q.PATH_FUSED
-    assert q.linear_path(16, 4096, 4096, True) == q.PATH_FUSED
+    assert q.linear_path(1, 4096, 4096, 16, False) == q.PATH_GEMV
+    assert q.linear_path(16, 4096, 4096, 16, False) == q.PATH_GEMV
+    assert q.linear_path(17, 4096, 4096, 16, False) == q.PATH_FUSED
+    assert q.linear_path(16, 4096, 4096, 16, True) == q.PATH_FUSED
     big = 4096
-    assert q.linear_path(big, 4096, 4096, False) == q.PATH_EXPANDED
-    assert q.linear_path(big, 4096, 4096, True) == q.PATH_EXPANDED
+    assert q.linear_path(big, 4096, 4096, 16, False) == q.PATH_EXPANDED
+    assert q.linear_path(big, 4096, 4096, 16, True) == q.PATH_EXPANDED
     # dX over unaligned dY rows (n % 8 != 0) stays on the fused kernel
-    assert q.linear_path(big, 100, 4096, True) == q.PATH_FUSED
-    assert q.linear_path(big, 100, 4096, False) == q.PATH_EXPANDED
+    assert q.linear_path(big, 100, 4096, 16, True) == q.PATH_FUSED
+    assert q.linear_path(big, 100, 4096, 16, False) == q.PATH_EXPANDED
     with pytest.raises(q.QLoraError):
-        q.linear_path(big, 64, 100, False)
+        q.linear_path(big, 64, 100, 16, False)
     # expanded operand sizes: [n, k + xc] and [k, roundup(n, 64) + xc] bf16 (256-B rounded)
     def r256(b):
         return (b + 255) // 256 * 256
@@ -163,3 +163,12 @@ def test_expand_and_bf16_gemm_errors(q):
     assert lib.qlora_bf16_gemm(p, 64, 100, p, 8, p, 64, p, None) == -2      # kc % 8 != 0
     assert lib.qlora_bf16_gemm(p, 64, 128, None, 8, p, 64, p, None) == -1   # r > 0 needs split
     assert lib.qlora_bf16_gemm(p, 0, 128, None, 8, p, 64, p, None) == 0     # M = 0: no-op
+
+
+def test_expanded_path_needs_operands_under_4gib(q):
+    lib = q.raw()
+    p = ctypes.c_void_p(1 << 24)
+    huge_m = 1 << 20  # [2^20, 4096] bf16 activation = 8 GiB
+    assert q.linear_path(huge_m, 4096, 4096, 16, False) == q.PATH_FUSED
+    assert q.linear_path(huge_m, 4096, 4096, 16, True) == q.PATH_FUSED
+    assert lib.qlora_bf16_gemm(p, huge_m, 4096, p, 16, p, 4096, p, None) == -2

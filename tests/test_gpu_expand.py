@@ -91,8 +91,8 @@ def test_bf16_gemm_building_blocks(q, m, n, k, r):
 def test_linear_at_expanded_sizes(q, m, n, k, r):
     """qlora_linear_fwd/bwd where the path is the expanded one (n % 8 != 0
     keeps dX on the fused kernel)."""
-    fwd_path = q.linear_path(m, n, k, False)
-    bwd_path = q.linear_path(m, n, k, True)
+    fwd_path = q.linear_path(m, n, k, r, False)
+    bwd_path = q.linear_path(m, n, k, r, True)
     say(f"case: linear M={m} N={n} K={k} r={r} paths fwd={fwd_path} bwd={bwd_path}")
     assert fwd_path == q.PATH_EXPANDED
     assert bwd_path == (q.PATH_EXPANDED if n % 8 == 0 else q.PATH_FUSED)
