@@ -56,23 +56,15 @@ int path_of(int64_t M, int64_t n, int64_t k, int r, bool bwd) {
 
 // ---- building-block workspaces
 size_t project_ws(int64_t M, int64_t C, int r) {
-  return align256((size_t)C * r * 2) + rowdot_ws_bytes(M, C, r);
+  const size_t b = rowdot_ws_bytes(M, C, r);
+  return b > 0 ? b : 256;  // a non-empty region keeps the workspace pointer checks uniform
 }
 size_t grad_ws(int64_t M, int64_t C, int r) { return coldot_ws_bytes(M, C, r); }
 
 // T = P Q^T (q_layout 0, Q [r, C]) or P Q (q_layout 1, Q [C, r]); optional split.
 hipError_t do_project(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r, float scale,
                       float* out, uint16_t* split, void* ws, hipStream_t st) {
-  Carver cv(ws);
-  uint16_t* QT = cv.take<uint16_t>((size_t)C * r * 2);
-  float* part = cv.take<float>(rowdot_ws_bytes(M, C, r));
-  const uint16_t* q = Q;
-  if (q_layout == 1) {
-    const hipError_t e = launch_transpose(Q, C, r, QT, st);
-    if (e != hipSuccess) return e;
-    q = QT;
-  }
-  return launch_rowdot_impl(P, M, C, q, r, out, split, scale, part, st);
+  return launch_rowdot(P, M, C, Q, q_layout, r, out, split, scale, static_cast<float*>(ws), st);
 }
 
 hipError_t do_grad(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,

@@ -24,8 +24,13 @@ namespace qlora {
 
 namespace {
 
-// One thread per 16-byte output chunk (8 bf16): consecutive threads write
-// consecutive chunks of a row, and read consecutive 32-bit code words.
+// Row expansion: one thread per 16-byte output chunk (8 bf16 = one 32-bit
+// code word). Workgroup (x, row) covers chunks 256 x .. 256 x + 255 of one
+// output row, so every store instruction of a wavefront writes 1 KB of
+// contiguous output and no index needs a division (grid: x = rows, y = chunk
+// blocks). Workgroups with y equal to the number of code-chunk blocks write
+// the LoRA columns of 256 / (xc / 8) rows each (the others in that column
+// exit at once).
 __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ code8,
                                                           const float* __restrict__ s2,
@@ -33,43 +38,47 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
                                                           const float* __restrict__ codebook, int64_t n, int64_t k,
                                                           const uint16_t* __restrict__ B, int r, int xc,
                                                           u32x4* __restrict__ out) {
-  __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = codebook[threadIdx.x];
-  __syncthreads();
-  const float mean = mean_p[0];
-  const int64_t row_chunks = (k + xc) / 8;
-  const int64_t total = n * row_chunks;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int64_t row = i / row_chunks;
-    const int64_t c = (i - row * row_chunks) * 8;
+  const int t = threadIdx.x;
+  const int64_t kw = k / 8;
+  const int64_t ldc = (k + xc) / 8;  // output row pitch in chunks
+  const int64_t row = blockIdx.x;
+  if ((int64_t)blockIdx.y * 256 >= kw) {
+    // LoRA columns: rows row .. row + rpb - 1 when row % rpb == 0
+    const int cpr = xc / 8, rpb = 256 / cpr;
+    if (row % rpb != 0 || t >= rpb * cpr) return;
+    const int64_t rr = row + t / cpr;
+    const int j0 = (t % cpr) * 8;
+    if (rr >= n) return;
     u32x4 v;
-    if (c < k) {
-      const float cp = block_scale(code8, s2, mean, row * (k / kBlock) + c / kBlock);
-      v = dequant8(codes[(row * k + c) / 8], lut, cp);
-    } else {
-      const int j0 = (int)(c - k);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        uint32_t h[2];
+    for (int p = 0; p < 4; ++p) {
+      uint32_t h[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = j0 + 2 * p + e;
-          h[e] = j < 2 * r ? (uint32_t)B[row * r + (j % r)] : 0u;
-        }
-        v[p] = h[0] | (h[1] << 16);
+      for (int e = 0; e < 2; ++e) {
+        const int j = j0 + 2 * p + e;
+        h[e] = j < 2 * r ? (uint32_t)B[rr * r + (j % r)] : 0u;
       }
+      v[p] = h[0] | (h[1] << 16);
     }
-    out[i] = v;
+    out[rr * ldc + kw + t % cpr] = v;
+    return;
   }
+  __shared__ float lut[16];
+  if (t < 16) lut[t] = codebook[t];
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.y * 256 + t;
+  if (c >= kw) return;
+  const int64_t wi = row * kw + c;  // code word index
+  out[row * ldc + c] = dequant8(codes[wi], lut, block_scale(code8, s2, mean_p[0], wi >> 3));
 }
 
-// Transposing expansion. Workgroup (tn, kb) expands k-block kb (64 weights)
-// of 256 weight rows n0 .. n0+255 into LDS as [64 k][256 n] and writes the 64
-// output rows' 512-byte segments. Thread t takes weight rows 2 (t % 128) and
-// +1 and half (t / 128) of the block, so its LDS writes are (row pair) dwords
-// and a wavefront writes 64 consecutive dwords of one k row. Workgroups with
-// tn == number of n tiles write the low-rank columns of their 64 k rows.
+// Transposing expansion, straight from registers. Workgroup (tn, kb) covers
+// weight rows n0 .. n0+255 and k-block kb: thread t takes rows 2 (t % 128)
+// and +1, half (t / 128) of the block (32 weights each), and for every one of
+// its 32 k writes the (row pair) as one 4-byte word of output row k. A
+// wavefront's 64 lanes thus write 256 contiguous bytes per store. Rows in
+// [n, np) are written as zeros; workgroups with tn == number of n tiles write
+// the low-rank columns of their 64 k rows.
 constexpr int kXT = 256;  // weight rows per tile
 
 __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restrict__ codes,
@@ -80,7 +89,6 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
                                                           int64_t np, const uint16_t* __restrict__ A, int r, int xc,
                                                           uint16_t* __restrict__ out) {
   __shared__ float lut[16];
-  __shared__ __attribute__((aligned(16))) uint32_t tile[64][kXT / 2];
   const int t = threadIdx.x;
   const int64_t ldo = np + xc;
   const int64_t kb = blockIdx.y;
@@ -100,43 +108,30 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
   const int64_t n0 = (int64_t)blockIdx.x * kXT;
   const int pr = t & 127, half = t >> 7;
   const int64_t na = n0 + 2 * pr, nb = na + 1;
-  uint32_t qa[4] = {0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-  uint32_t qb[4] = {0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+  if (na >= np) return;  // np is a multiple of 64: the pair is in or out together
+  u32x4 qa = {0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+  u32x4 qb = qa;
   float ca = 0.0f, cb = 0.0f;
   const int64_t kblocks = k / kBlock;
   if (na < n) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(codes + na * (k / 2) + kb * 32 + half * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qa[j] = v[j];
+    qa = *reinterpret_cast<const u32x4*>(codes + na * (k / 2) + kb * 32 + half * 16);
     ca = block_scale(code8, s2, mean, na * kblocks + kb);
   }
   if (nb < n) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(codes + nb * (k / 2) + kb * 32 + half * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qb[j] = v[j];
+    qb = *reinterpret_cast<const u32x4*>(codes + nb * (k / 2) + kb * 32 + half * 16);
     cb = block_scale(code8, s2, mean, nb * kblocks + kb);
   }
   // rows past n decode code 7 (level 0) times scale 0: exact zeros
+  uint32_t* dst = reinterpret_cast<uint32_t*>(out + (kb * kBlock + half * 32) * ldo + na);
+  const int64_t ldw = ldo / 2;  // output row pitch in 4-byte words
 #pragma unroll
   for (int w = 0; w < 4; ++w)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float va = nf4_scaled(lut[(qa[w] >> (4 * e)) & 0xF], ca);
       const float vb = nf4_scaled(lut[(qb[w] >> (4 * e)) & 0xF], cb);
-      tile[half * 32 + w * 8 + e][pr] = pack_bf16x2(va, vb);
+      dst[(w * 8 + e) * ldw] = pack_bf16x2(va, vb);
     }
-  __syncthreads();
-  // 64 rows x 512 bytes = 2048 chunks of 16 B; chunk q: row q / 32, col chunk q % 32
-  const int64_t ncols = np - n0 < kXT ? np - n0 : kXT;  // multiple of 64
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q = t + 256 * i;
-    const int row = q >> 5, ch = q & 31;
-    if (ch * 8 < ncols) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&tile[row][ch * 4]);
-      *reinterpret_cast<u32x4*>(out + (kb * kBlock + row) * ldo + n0 + ch * 8) = v;
-    }
-  }
 }
 
 }  // namespace
@@ -153,12 +148,10 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
                          hipStream_t stream) {
   const int xc = lora_extra_cols(r);
   if (!transposed) {
-    const int64_t total = w.n * (w.k + xc) / 8;
-    int64_t blocks = cdiv(total, (int64_t)256);
-    if (blocks > 256 * 64) blocks = 256 * 64;
-    expand_rows_kernel<<<(unsigned)blocks, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(w.codes), w.code8,
-                                                             w.s2, w.mean, w.codebook, w.n, w.k, lr, r, xc,
-                                                             reinterpret_cast<u32x4*>(out));
+    const int64_t kw = w.k / 8;
+    const dim3 grid((unsigned)w.n, (unsigned)(cdiv(kw, (int64_t)256) + (xc > 0 ? 1 : 0)));
+    expand_rows_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(w.codes), w.code8, w.s2, w.mean,
+                                                 w.codebook, w.n, w.k, lr, r, xc, reinterpret_cast<u32x4*>(out));
   } else {
     const int64_t np = expand_pad_rows(w.n);
     const int64_t ntiles = cdiv(np, (int64_t)kXT);

@@ -37,14 +37,13 @@ hipError_t launch_dequant(const Nf4View& w, uint16_t* out, hipStream_t stream);
 // scaled low-rank activation, padded with zeros to a multiple of 64.
 inline int lora_extra_cols(int r) { return r > 0 ? ((2 * r + 63) / 64) * 64 : 0; }
 
-// out[m, j] = sum_c P[m, c] * Q[j, c]   (P bf16 [M, C], Q bf16 [r, C]), fp32.
-// If split != NULL it also receives [bf16(scale*out) | bf16(scale*out - hi) | 0 ...]
-// rows of lora_extra_cols(r) elements; out may then be NULL. part is workspace.
+// out[m, j] = sum_c P[m, c] Q(c, j), P bf16 [M, C]; Q bf16 [r, C] (q_layout
+// 0) or [C, r] (q_layout 1); fp32 out [M, r] (nullable). If split != NULL it
+// also receives rows [bf16(scale*out) | bf16(scale*out - hi) | 0 ...] of
+// lora_extra_cols(r) elements. part: workspace of rowdot_ws_bytes (may be 0).
 size_t rowdot_ws_bytes(int64_t M, int64_t C, int r);
-hipError_t launch_rowdot_impl(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
-                              uint16_t* split, float scale, float* part, hipStream_t stream);
-// B [n, r] -> B^T [r, n]
-hipError_t launch_transpose(const uint16_t* B, int64_t n, int r, uint16_t* BT, hipStream_t stream);
+hipError_t launch_rowdot(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r,
+                         float* out, uint16_t* split, float scale, float* part, hipStream_t stream);
 
 // Column reduction over M in fixed order, for the adapter gradients:
 //   G[c, j] (+)= scale * sum_m P[m, c] * Q[m, j]    P bf16 [M, C], Q fp32 [M, r]

@@ -27,132 +27,6 @@ namespace {
 
 constexpr int kMaxRank = 128;
 
-// Each workgroup: RT x 16 rows, columns [c0, c1) of the contraction, all r
-// outputs. Wave w takes row tile w % RT and part w / RT of the column range
-// (4 / RT parts); lanes read P and Q straight from global memory in the MFMA
-// operand layout (8 consecutive bf16 per lane), 8 column chunks per
-// iteration so each lane keeps eight 16-byte loads in flight. With RT = 4 the
-// four waves share one slice of Q (read once per 64 rows instead of per 16).
-template <bool kVec, int kRP, int RT>
-__global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
-                                                     const uint16_t* __restrict__ Q, int r,
-                                                     int64_t cchunk, float* __restrict__ part) {
-  constexpr int kParts = 4 / RT;
-  __shared__ float red[4][16][kRP];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int rt = wave % RT, cpart = wave / RT;
-  const int64_t m0 = (int64_t)blockIdx.x * (16 * RT) + 16 * rt;
-  const int64_t cs = blockIdx.y;
-  const int64_t cbeg = cs * cchunk;
-  const int64_t cend = (cbeg + cchunk < C) ? cbeg + cchunk : C;
-  const int64_t qlen = cdiv(cend - cbeg, kParts * 32) * 32;  // per-wave length, multiple of 32
-  const int64_t w0 = cbeg + cpart * qlen;
-  const int64_t w1 = (w0 + qlen < cend) ? w0 + qlen : cend;
-
-  const int row = lane & 15;
-  const int ko = (lane >> 4) * 8;
-  const int64_t m = m0 + row;
-  constexpr int kTiles = kRP / 16;
-  f32x4 acc[kTiles];
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  constexpr int kU = kTiles >= 4 ? 2 : 8 / kTiles;
-  for (int64_t c = w0; c < w1; c += 32 * kU) {
-    u32x4 a[kU];
-    u32x4 b[kU][kTiles];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t cc = c + 32 * u + ko;
-      a[u] = u32x4{0u, 0u, 0u, 0u};
-      if (m < M) {
-        if constexpr (kVec) {
-          if (cc < w1) a[u] = *reinterpret_cast<const u32x4*>(P + m * C + cc);
-        } else {
-          uint16_t e[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) e[i] = (cc + i < w1) ? P[m * C + cc + i] : (uint16_t)0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[u][i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        const int j = t * 16 + row;
-        b[u][t] = u32x4{0u, 0u, 0u, 0u};
-        if (j < r) {
-          if constexpr (kVec) {
-            if (cc < w1) b[u][t] = *reinterpret_cast<const u32x4*>(Q + (int64_t)j * C + cc);
-          } else {
-            uint16_t e[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] = (cc + i < w1) ? Q[(int64_t)j * C + cc + i] : (uint16_t)0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) b[u][t][i] = (uint32_t)e[2 * i] | ((uint32_t)e[2 * i + 1] << 16);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
-                                                         __builtin_bit_cast(bf16x8, b[u][t]), acc[t], 0, 0, 0);
-  }
-  // D layout: lane -> column (lane & 15), rows 4 * (lane >> 4) + v
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][t * 16 + (lane & 15)] = acc[t][v];
-  __syncthreads();
-  const int64_t mw = (int64_t)blockIdx.x * (16 * RT);
-  for (int i = threadIdx.x; i < 16 * RT * kRP; i += 256) {
-    const int rr = i / kRP, j = i % kRP;
-    const int64_t mm = mw + rr;
-    if (mm < M && j < r) {
-      const int rtile = rr / 16, rin = rr % 16;
-      float sum = red[rtile][rin][j];
-#pragma unroll
-      for (int pp = 1; pp < kParts; ++pp) sum += red[rtile + pp * RT][rin][j];  // parts in order
-      part[(cs * M + mm) * r + j] = sum;
-    }
-  }
-}
-
-// Sum the contraction pieces in order; write out (fp32) and the bf16 hi/lo pair.
-__global__ __launch_bounds__(256) void rowdot_finalize_kernel(const float* __restrict__ part, int64_t M, int r,
-                                                              int64_t nsplit, float* __restrict__ out,
-                                                              uint16_t* __restrict__ split, int xcols,
-                                                              float scale) {
-#pragma clang fp contract(off)
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (split == nullptr) {
-    if (i >= M * (int64_t)r) return;
-    const int64_t m = i / r;
-    const int j = (int)(i % r);
-    float s = 0.0f;
-    for (int64_t p = 0; p < nsplit; ++p) s += part[(p * M + m) * r + j];
-    out[i] = s;
-    return;
-  }
-  if (i >= M * (int64_t)xcols) return;
-  const int64_t m = i / xcols;
-  const int col = (int)(i % xcols);
-  uint16_t v = 0;
-  if (col < 2 * r) {
-    const int j = col < r ? col : col - r;
-    float s = 0.0f;
-    for (int64_t p = 0; p < nsplit; ++p) s += part[(p * M + m) * r + j];
-    if (col < r && out != nullptr) out[m * r + j] = s;
-    const float ss = scale * s;
-    const uint16_t hi = to_bf16_bits(ss);
-    v = (col < r) ? hi : to_bf16_bits(ss - bf16_bits_to_f32(hi));  // exact difference, then RNE
-  }
-  split[i] = v;
-}
-
 // G partial on the matrix cores: Gp[s][j][c] = sum_{m in split s} Q[m, j] P[m, c].
 // The contraction runs over the tokens m, which are the slow index of both
 // operands, so each 32-token step is staged in LDS in its stored orientation
@@ -294,45 +168,6 @@ __global__ __launch_bounds__(256) void coldot_reduce_kernel(const float* __restr
 
 }  // namespace
 
-static int rowdot_rt(int64_t M) { return M >= 256 ? 4 : 1; }
-
-static int rowdot_splits(int64_t M, int64_t C) {
-  const int64_t tiles = cdiv(M, 16 * rowdot_rt(M));
-  int64_t s = cdiv(512, tiles);
-  const int64_t maxs = cdiv(C, 256);  // keep >= 256 columns per split
-  if (s > maxs) s = maxs;
-  if (s < 1) s = 1;
-  return (int)s;
-}
-
-size_t rowdot_ws_bytes(int64_t M, int64_t C, int r) {
-  return align256((size_t)rowdot_splits(M, C) * (size_t)M * (size_t)r * 4);
-}
-
-hipError_t launch_rowdot_impl(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
-                              uint16_t* split, float scale, float* part, hipStream_t stream) {
-  const int ns = rowdot_splits(M, C);
-  const int rt = rowdot_rt(M);
-  const int64_t cchunk = cdiv(cdiv(C, ns), 32) * 32;
-  const dim3 grid((unsigned)cdiv(M, 16 * rt), (unsigned)ns);
-  const bool vec = (C % 8) == 0;
-#define QLORA_ROWDOT2(RP, RT)                                                                          \
-  if (vec) rowdot_kernel<true, RP, RT><<<grid, 256, 0, stream>>>(P, M, C, Q, r, cchunk, part);        \
-  else rowdot_kernel<false, RP, RT><<<grid, 256, 0, stream>>>(P, M, C, Q, r, cchunk, part);
-#define QLORA_ROWDOT(RP) \
-  if (rt == 4) { QLORA_ROWDOT2(RP, 4) } else { QLORA_ROWDOT2(RP, 1) }
-  if (r <= 16) { QLORA_ROWDOT(16) }
-  else if (r <= 32) { QLORA_ROWDOT(32) }
-  else if (r <= 64) { QLORA_ROWDOT(64) }
-  else { QLORA_ROWDOT(128) }
-#undef QLORA_ROWDOT
-#undef QLORA_ROWDOT2
-  const int xcols = lora_extra_cols(r);
-  const int64_t total = split ? M * xcols : M * r;
-  rowdot_finalize_kernel<<<(unsigned)cdiv(total, 256), 256, 0, stream>>>(part, M, r, ns, out, split, xcols, scale);
-  return hipGetLastError();
-}
-
 int coldot_splits(int64_t M) {
   int64_t s = M / 256;
   if (s > 32) s = 32;
@@ -360,23 +195,6 @@ hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q
 #undef QLORA_COLDOT
   coldot_reduce_kernel<<<(unsigned)cdiv(C * r, 256), 256, 0, stream>>>(partial, C, r, ns, scale, G, g_sc, g_sj,
                                                                       accumulate);
-  return hipGetLastError();
-}
-
-// B [n, r] -> B^T [r, n], so dY B is a rowdot with a contiguous second operand.
-namespace {
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ B, int64_t n, int r,
-                                                        uint16_t* __restrict__ BT) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n * r) return;
-  const int64_t j = i / n, c = i % n;
-  BT[i] = B[c * r + j];
-  (void)j;
-}
-}  // namespace
-
-hipError_t launch_transpose(const uint16_t* B, int64_t n, int r, uint16_t* BT, hipStream_t stream) {
-  transpose_kernel<<<(unsigned)cdiv(n * r, 256), 256, 0, stream>>>(B, n, r, BT);
   return hipGetLastError();
 }
 

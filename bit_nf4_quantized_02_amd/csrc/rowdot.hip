@@ -1,0 +1,317 @@
+// Low-rank projection of an activation: the skinny product on the way into
+// the adapter ("QLoRA: Quantized Low-Rank Adaptation" (completesystemdesign.dev),
+// three-piece summary, piece 3: only the low-rank pair learns; "What is
+// QLoRA?" (qubittool.com), "Key Characteristics": adapters in full precision).
+//
+//   out[m, j] = sum_c P[m, c] Q(c, j)       T = X A^T (Q = A, [r, C]),  U = dY B (Q = B, [C, r])
+//
+// bf16 products on the matrix cores (v_mfma_f32_16x16x32_bf16), fp32 sums.
+// Optionally the scaled value s*out is also written as a bf16 hi/lo pair per
+// row, [hi | lo | zero pad] with hi = RN_bf16(s*out), lo = RN_bf16(s*out - hi):
+// the 2r extra contraction columns through which the main GEMMs add the
+// low-rank term to their fp32 accumulator, so Y and dX are rounded once.
+//
+// Workgroup: one 16-row tile of P and a range of columns, NW waves splitting
+// the range into contiguous parts. Lanes read P in the MFMA operand layout
+// (8 consecutive bf16 per lane, 16-byte loads, kU column steps in flight).
+// Q as [r, C] is read the same way. Q as [C, r] (j contiguous) is staged per
+// wave in LDS as a [32 c][r] tile and read back with the transposing read
+// ds_read_b64_tr_b16, which hands each lane 4 consecutive c of its column j.
+// The waves' partial sums are added in a fixed order in LDS. With the whole
+// contraction in one workgroup (large M) the result and its split are written
+// directly; for small M the contraction is also split over workgroups, each
+// writes its partial, and a finalize kernel adds the partials in a fixed
+// (split-major, then group) order. Reruns are bit-identical either way.
+#include "common.h"
+#include "kernels.h"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kMaxRankPad = 128;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Operand of v_mfma_f32_16x16x32_bf16 from a [row][col] bf16 tile: lane gets
+// column c0 + lane % 16, rows 8 (lane / 16) .. +7. Inside each 16-lane group
+// lane i addresses row base + i / 4, columns 4 (i % 4) .. +3 and receives its
+// own column of the 4 rows.
+__device__ __forceinline__ bf16x8 tr_rows8(const char* tile, int pitch, int c0, int lane) {
+  const int i = lane & 15;
+  const char* p = tile + (8 * (lane >> 4) + (i >> 2)) * pitch + (c0 + 4 * (i & 3)) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 4 * pitch));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// 8 bf16 starting at p (element index e0 of a row with `lim` valid elements):
+// one 16-byte load when the row is 16-byte aligned (kVec), else 8 guarded loads.
+template <bool kVec>
+__device__ __forceinline__ u32x4 load8(const uint16_t* __restrict__ row, int64_t e0, int64_t lim) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if constexpr (kVec) {
+    if (e0 < lim) v = *reinterpret_cast<const u32x4*>(row + e0);
+  } else {
+    uint32_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = (e0 + i < lim) ? (uint32_t)row[e0 + i] : 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = e[2 * i] | (e[2 * i + 1] << 16);
+  }
+  return v;
+}
+
+template <int kRP>
+constexpr int rowdot_threads() { return (kRP <= 64 ? 8 : 4) * 64; }
+
+template <int kRP, int kQL>
+struct RowdotCfg {
+  static constexpr int kTiles = kRP / 16;
+  static constexpr int kU = kTiles >= 8 ? 1 : 8 / kTiles;           // column steps per load batch
+  static constexpr int kNW = rowdot_threads<kRP>() / 64;              // waves per workgroup
+  static constexpr int kQPitch = kRP * 2 + (kRP >= 32 ? 32 : 0);     // bytes per staged Q row
+  static constexpr int kStage = kU * 32 * kQPitch;                   // staged Q bytes per wave
+  static constexpr int kRed = kNW * 16 * kRP * 4;                    // partial sums of the waves
+  static constexpr int kSmem = (kQL == 1 && kNW * kStage > kRed) ? kNW * kStage : kRed;
+};
+
+// kQL: 0 = Q is [r, C], 1 = Q is [C, r]. kVecP / kVecQ: 16-byte rows.
+// kDirect: write out / split (single column split), else write partials.
+template <int kRP, int kQL, bool kVecP, bool kVecQ, bool kDirect>
+__global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
+    const uint16_t* __restrict__ P, int64_t M, int64_t C, const uint16_t* __restrict__ Q, int r, int64_t cchunk,
+    float* __restrict__ out, uint16_t* __restrict__ split, int xc, float scale, float* __restrict__ part) {
+#pragma clang fp contract(off)
+  using Cfg = RowdotCfg<kRP, kQL>;
+  constexpr int kTiles = Cfg::kTiles, kU = Cfg::kU, kNW = Cfg::kNW;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::kSmem];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int64_t cs = blockIdx.y;
+  const int64_t cbeg = cs * cchunk;
+  const int64_t cend = (cbeg + cchunk < C) ? cbeg + cchunk : C;
+  const int64_t qlen = cdiv(cend - cbeg, (int64_t)kNW * 32) * 32;  // per-wave length, multiple of 32
+  const int64_t w0 = cbeg + wave * qlen;
+  const int64_t w1 = (w0 + qlen < cend) ? w0 + qlen : cend;
+
+  const int row = lane & 15;
+  const int ko = (lane >> 4) * 8;
+  const int64_t m = m0 + row;
+  const uint16_t* prow = P + (m < M ? m : M - 1) * C;
+  char* const stage = smem + wave * Cfg::kStage;
+
+  f32x4 acc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t c = w0; c < w1; c += 32 * kU) {
+    u32x4 a[kU];
+    bf16x8 b[kU][kTiles];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      a[u] = load8<kVecP>(prow, c + 32 * u + ko, w1);
+      if (m >= M) a[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (kQL == 0) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          const int j = t * 16 + row;
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (j < r) v = load8<kVecQ>(Q + (int64_t)j * C, c + 32 * u + ko, w1);
+          b[u][t] = __builtin_bit_cast(bf16x8, v);
+        }
+    } else {
+      // The staged region is rewritten every iteration: the empty asm keeps
+      // the compiler from moving these stores above the previous iteration's
+      // transposing reads (or the reads above the stores), which it might
+      // otherwise treat as unrelated accesses.
+      asm volatile("" ::: "memory");
+      // stage Q[c + 32 u + cc][0 .. kRP) as [32][kRP] bf16 tiles (zeros past w1 / r)
+      constexpr int kChunks = 32 * kRP / 8;  // 16-byte chunks per tile
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int i = 0; i < kChunks / 64; ++i) {
+          const int q = lane + 64 * i;
+          const int cc = q / (kRP / 8), jc = (q % (kRP / 8)) * 8;
+          const int64_t cq = c + 32 * u + cc;
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (cq < w1) {
+            if constexpr (kVecQ) {
+              if (jc < r) v = *reinterpret_cast<const u32x4*>(Q + cq * r + jc);
+            } else {
+              uint32_t e[8];
+#pragma unroll
+              for (int x = 0; x < 8; ++x) e[x] = (jc + x < r) ? (uint32_t)Q[cq * r + jc + x] : 0u;
+#pragma unroll
+              for (int x = 0; x < 4; ++x) v[x] = e[2 * x] | (e[2 * x + 1] << 16);
+            }
+          }
+          *reinterpret_cast<u32x4*>(stage + u * 32 * Cfg::kQPitch + cc * Cfg::kQPitch + jc * 2) = v;
+        }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) b[u][t] = tr_rows8(stage + u * 32 * Cfg::kQPitch, Cfg::kQPitch, t * 16, lane);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]), b[u][t], acc[t], 0, 0, 0);
+  }
+  __syncthreads();  // all staged-Q reads done before the region is reused
+  // D layout: lane -> column (lane & 15), rows 4 (lane >> 4) + v
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * (lane >> 4) + v) * kRP + t * 16 + (lane & 15)] = acc[t][v];
+  __syncthreads();
+  if constexpr (kDirect) {
+    // one thread per (row, split column): columns [0, r) hi, [r, 2r) lo, rest 0
+    if (split != nullptr) for (int i = threadIdx.x; i < 16 * xc; i += kNW * 64) {
+      const int rr = i / xc, col = i - rr * xc;
+      const int64_t mm = m0 + rr;
+      if (mm >= M) continue;
+      if (col < 2 * r) {
+        const int j = col < r ? col : col - r;
+        float s = red[rr * kRP + j];
+#pragma unroll
+        for (int w = 1; w < kNW; ++w) s += red[(w * 16 + rr) * kRP + j];  // parts in order
+        if (col < r && out != nullptr) out[mm * r + j] = s;
+        const float ss = scale * s;
+        const uint16_t hi = to_bf16_bits(ss);
+        split[mm * xc + col] = col < r ? hi : to_bf16_bits(ss - bf16_bits_to_f32(hi));
+      } else {
+        split[mm * xc + col] = 0;
+      }
+    }
+    else {
+      for (int i = threadIdx.x; i < 16 * r; i += kNW * 64) {
+        const int rr = i / r, j = i - rr * r;
+        const int64_t mm = m0 + rr;
+        if (mm >= M) continue;
+        float s = red[rr * kRP + j];
+#pragma unroll
+        for (int w = 1; w < kNW; ++w) s += red[(w * 16 + rr) * kRP + j];
+        out[mm * r + j] = s;
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < 16 * r; i += kNW * 64) {
+      const int rr = i / r, j = i - rr * r;
+      const int64_t mm = m0 + rr;
+      if (mm >= M) continue;
+      float s = red[rr * kRP + j];
+#pragma unroll
+      for (int w = 1; w < kNW; ++w) s += red[(w * 16 + rr) * kRP + j];
+      part[(cs * M + mm) * r + j] = s;
+    }
+  }
+}
+
+// Partials of the small-M case -> out / split. Block = one row m; G = 256 / r
+// thread groups each add splits g, g + G, ... in order; then thread j adds the
+// G group sums in order.
+__global__ __launch_bounds__(256) void rowdot_finalize_kernel(const float* __restrict__ part, int64_t M, int r,
+                                                              int64_t nsplit, float* __restrict__ out,
+                                                              uint16_t* __restrict__ split, int xc, float scale) {
+#pragma clang fp contract(off)
+  __shared__ float gsum[256];
+  __shared__ float tot[kMaxRankPad];
+  const int t = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const int G = 256 / r;
+  if (t < G * r) {
+    const int j = t % r, g = t / r;
+    float s = 0.0f;
+    for (int64_t p = g; p < nsplit; p += G) s += part[(p * M + m) * r + j];
+    gsum[g * r + j] = s;
+  }
+  __syncthreads();
+  if (t < r) {
+    float s = gsum[t];
+    for (int g = 1; g < G; ++g) s += gsum[g * r + t];
+    tot[t] = s;
+    if (out != nullptr) out[m * r + t] = s;
+  }
+  __syncthreads();
+  if (split != nullptr) {
+    for (int col = t; col < xc; col += 256) {
+      uint16_t v = 0;
+      if (col < 2 * r) {
+        const float ss = scale * tot[col < r ? col : col - r];
+        const uint16_t hi = to_bf16_bits(ss);
+        v = col < r ? hi : to_bf16_bits(ss - bf16_bits_to_f32(hi));
+      }
+      split[m * xc + col] = v;
+    }
+  }
+}
+
+int rowdot_splits(int64_t M, int64_t C) {
+  const int64_t tiles = cdiv(M, (int64_t)16);
+  if (tiles >= 128) return 1;                // enough row tiles: whole contraction per workgroup
+  int64_t s = cdiv((int64_t)256, tiles);
+  const int64_t maxs = cdiv(C, (int64_t)256);  // keep >= 256 columns per split
+  if (s > maxs) s = maxs;
+  return (int)(s < 1 ? 1 : s);
+}
+
+template <int kRP, int kQL>
+hipError_t launch_rp(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
+                     uint16_t* split, float scale, float* part, hipStream_t stream) {
+  constexpr int kNW = RowdotCfg<kRP, kQL>::kNW;
+  const int ns = rowdot_splits(M, C);
+  const int64_t cchunk = cdiv(cdiv(C, (int64_t)ns), (int64_t)32) * 32;
+  const dim3 grid((unsigned)cdiv(M, (int64_t)16), (unsigned)ns);
+  const int xc = lora_extra_cols(r);
+  const bool vp = C % 8 == 0;
+  const bool vq = kQL == 0 ? (C % 8 == 0) : (r % 8 == 0);
+#define QLORA_RD(VP, VQ, D) \
+  rowdot_kernel<kRP, kQL, VP, VQ, D><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, split, xc, scale, part)
+#define QLORA_RD2(D)                    \
+  if (vp && vq) QLORA_RD(true, true, D); \
+  else if (vp) QLORA_RD(true, false, D); \
+  else if (vq) QLORA_RD(false, true, D); \
+  else QLORA_RD(false, false, D);
+  if (ns == 1) {
+    QLORA_RD2(true)
+    return hipGetLastError();
+  }
+  QLORA_RD2(false)
+#undef QLORA_RD2
+#undef QLORA_RD
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  rowdot_finalize_kernel<<<(unsigned)M, 256, 0, stream>>>(part, M, r, ns, out, split, xc, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t rowdot_ws_bytes(int64_t M, int64_t C, int r) {
+  const int ns = rowdot_splits(M, C);
+  return ns > 1 ? align256((size_t)ns * (size_t)M * (size_t)r * 4) : 0;
+}
+
+hipError_t launch_rowdot(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r,
+                         float* out, uint16_t* split, float scale, float* part, hipStream_t stream) {
+#define QLORA_RP(RP)                                                                      \
+  return q_layout == 0 ? launch_rp<RP, 0>(P, M, C, Q, r, out, split, scale, part, stream) \
+                       : launch_rp<RP, 1>(P, M, C, Q, r, out, split, scale, part, stream);
+  if (r <= 16) { QLORA_RP(16) }
+  if (r <= 32) { QLORA_RP(32) }
+  if (r <= 64) { QLORA_RP(64) }
+  QLORA_RP(128)
+#undef QLORA_RP
+}
+
+}  // namespace qlora
