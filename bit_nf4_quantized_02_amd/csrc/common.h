@@ -90,6 +90,19 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t word, const float* lut, float
   return out;
 }
 
+// The same expansion through a byte-indexed table: lut2[b] holds the level
+// pair (L[b & 15], L[b >> 4]) of the two codes packed in byte b, so one LDS
+// read serves two weights. Products and rounding are those of dequant8.
+__device__ __forceinline__ u32x4 dequant8_pairs(uint32_t word, const float2* lut2, float cprime) {
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float2 l = lut2[(word >> (8 * p)) & 0xFF];
+    out[p] = pack_bf16x2(nf4_scaled(l.x, cprime), nf4_scaled(l.y, cprime));
+  }
+  return out;
+}
+
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace qlora

@@ -10,9 +10,12 @@
 //
 // Each workgroup owns NT output rows (n) and the whole contraction; its 4
 // waves split the contraction into quarters. A wave walks its quarter in
-// 128-wide chunks: every lane loads 16 contiguous bytes of codes (32 weights
-// of one row, one 64-block, one scale), expands them to bf16 in registers
-// through the LDS codebook and feeds them straight to
+// 128-wide chunks, keeping the loads of the next chunk in flight while it
+// works on one: every lane loads 16 contiguous bytes of codes (32 weights of
+// one row, one 64-block, one scale), expands them to bf16 in registers
+// through an LDS table indexed by whole code bytes (one read yields the
+// levels of two weights; the products are those of the 16-entry codebook)
+// and feeds them straight to
 // v_mfma_f32_16x16x32_bf16 as the B operand; X (padded to 16 rows with zeros)
 // is the A operand. The contraction order inside a chunk is permuted the same
 // way on both operands (lane group g takes columns 32 g .. 32 g + 31), which
@@ -37,11 +40,11 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
                                                        const uint16_t* __restrict__ B, int r, float scale,
                                                        uint16_t* __restrict__ Y) {
   constexpr int kTiles = NT / 16;
-  __shared__ float lut[16];
+  __shared__ float2 lut2[256];
   __shared__ float red[4][kTiles][16][16];
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
-  if (t < 16) lut[t] = codebook[t];
+  lut2[t] = float2{codebook[t & 15], codebook[t >> 4]};  // levels of the two codes in byte t
   __syncthreads();
   const float mean = mean_p[0];
   const int64_t n0 = (int64_t)blockIdx.x * NT;
@@ -56,29 +59,80 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
 #pragma unroll
   for (int i = 0; i < kTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k0 = kb; k0 < ke; k0 += 128) {
+  // Per-lane row bases, computed once. Every load below reads a clamped,
+  // in-range address; out-of-range rows / columns / tokens are then replaced
+  // by code 7 (level 0) or zero activations with selects, so the loop body is
+  // one basic block and the loads of later chunks stay in flight while a
+  // chunk is expanded and multiplied.
+  const uint8_t* crow[kTiles];
+  int64_t bbase[kTiles];
+  bool rowok[kTiles];
+#pragma unroll
+  for (int i = 0; i < kTiles; ++i) {
+    const int64_t n = n0 + i * 16 + col;
+    const int64_t nc = n < N ? n : N - 1;
+    rowok[i] = n < N;
+    crow[i] = codes + nc * (K / 2);
+    bbase[i] = nc * kblocks;
+  }
+  const uint16_t* xrow = X + (int64_t)(col < M ? col : M - 1) * K;
+  const bool xok = col < M;
+
+  struct Stage {
+    u32x4 cw[kTiles];
+    uint32_t c8[kTiles];
+    float s2v[kTiles];
+    u32x4 xa[4];
+    bool kin;
+  };
+  auto load = [&](int64_t k0, Stage& st) {
     const int64_t k = k0 + 32 * grp;
-    const bool kin = k < ke;  // ke is a multiple of 32 (K % 64 == 0)
-    bf16x8 af[4];
+    st.kin = k < ke;                        // ke is a multiple of 32 (K % 64 == 0)
+    const int64_t kc = st.kin ? k : ke - 32;  // a valid column of this wave's range
+#pragma unroll
+    for (int s = 0; s < 4; ++s) st.xa[s] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * s);
+#pragma unroll
+    for (int i = 0; i < kTiles; ++i) {
+      st.cw[i] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2);
+      const int64_t blk = bbase[i] + kc / kBlock;
+      st.c8[i] = code8[blk];
+      st.s2v[i] = s2[blk / kDqBlock];
+    }
+  };
+  auto compute = [&](const Stage& st) {
+    const bool xuse = st.kin && xok;
+    bf16x8 xa[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (kin && col < M) v = *reinterpret_cast<const u32x4*>(X + col * K + k + 8 * s);
-      af[s] = __builtin_bit_cast(bf16x8, v);
+      u32x4 v = st.xa[s];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = xuse ? v[e] : 0u;
+      xa[s] = __builtin_bit_cast(bf16x8, v);
     }
 #pragma unroll
     for (int i = 0; i < kTiles; ++i) {
-      const int64_t n = n0 + i * 16 + col;
-      u32x4 cw = {0u, 0u, 0u, 0u};
-      float cp = 0.0f;
-      if (kin && n < N) {
-        cw = *reinterpret_cast<const u32x4*>(codes + n * (K / 2) + k / 2);
-        cp = block_scale(code8, s2, mean, n * kblocks + k / kBlock);
-      }
+      const bool use = st.kin && rowok[i];
+      const float cp = decode_block_scale(st.c8[i], st.s2v[i], mean);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 bw = dequant8(cw[s], lut, cp);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], __builtin_bit_cast(bf16x8, bw), acc[i], 0, 0, 0);
+        const uint32_t word = use ? st.cw[i][s] : 0x77777777u;  // code 7: level 0
+        const u32x4 bw = dequant8_pairs(word, lut2, cp);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[s], __builtin_bit_cast(bf16x8, bw), acc[i], 0, 0, 0);
+      }
+    }
+  };
+  if (kb < ke) {  // (a wave may have no columns when K is tiny)
+    {
+      Stage st0, st1;
+      load(kb, st0);
+      for (int64_t k0 = kb; k0 < ke; k0 += 2 * 128) {
+        load(k0 + 128, st1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st0);
+        if (k0 + 128 >= ke) break;
+        load(k0 + 256, st0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st1);
       }
     }
   }
@@ -107,19 +161,23 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
 
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T, const uint16_t* B, int r,
                        float scale, uint16_t* Y, hipStream_t stream) {
+  // Rows per workgroup: as many as keep >= ~256-448 workgroups in flight
+  // (measured on the 70B-class shapes: 64 for 28672 rows, 32 for 8192).
   const bool lora = r > 0;
 #define QLORA_GEMV(NT)                                                                                        \
   {                                                                                                           \
     const dim3 grid((unsigned)cdiv(w.n, NT));                                                                 \
     if (lora)                                                                                                 \
-      gemv_nf4_kernel<NT, true><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.n,   \
-                                                           w.k, X, M, T, B, r, scale, Y);                     \
+      gemv_nf4_kernel<NT, true><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean,            \
+                                                                    w.codebook, w.n, w.k, X, M, T, B, r,      \
+                                                                    scale, Y);                                \
     else                                                                                                      \
-      gemv_nf4_kernel<NT, false><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.n,  \
-                                                            w.k, X, M, T, B, r, scale, Y);                    \
+      gemv_nf4_kernel<NT, false><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean,           \
+                                                                     w.codebook, w.n, w.k, X, M, T, B, r,     \
+                                                                     scale, Y);                               \
   }
-  if (w.n / 64 >= 512) QLORA_GEMV(64)
-  else if (w.n / 32 >= 512) QLORA_GEMV(32)
+  if (w.n / 64 >= 448) QLORA_GEMV(64)
+  else if (w.n / 32 >= 256) QLORA_GEMV(32)
   else QLORA_GEMV(16)
 #undef QLORA_GEMV
   return hipGetLastError();
