@@ -62,6 +62,22 @@ def linear_bwd(X, Wd, A, B, s, dY, T=None):
     return dX, dA, dB, U
 
 
+def adapter_grads(X, A, B, s, dY, T=None):
+    """The adapter gradients of ``linear_bwd`` alone (no dX product):
+    U = dY B, dA = s U^T X, dB = s dY^T T with T = X A^T.  Returns (dA, dB, U).
+    Used where the full dX would be too large a product for the oracle and dX
+    is checked on sampled rows instead."""
+    X, A, B, dY = _f64(X), _f64(A), _f64(B), _f64(dY)
+    s = float(s)
+    if T is None:
+        T = X @ A.T
+    T = _f64(T)
+    U = dY @ B
+    dA = s * (U.T @ X)
+    dB = s * (dY.T @ T)
+    return dA, dB, U
+
+
 def relerr(Z, Zref) -> float:
     """Relative Frobenius error ||Z - Zref||_F / ||Zref||_F, in fp64."""
     Z, Zref = _f64(Z), _f64(Zref)

@@ -112,3 +112,13 @@ def test_end_to_end_small_layer_tolerance_is_feasible():
     B = nf4.bf16_bits_to_f32(nf4.bf16_bits((g.standard_normal((96, 8)) * 0.01).astype(np.float32)))
     Y, _ = linear.linear_fwd(X, q.dequant(), A, B, 2.0)
     assert linear.bf16_floor(Y) < 2e-3
+
+
+def test_adapter_grads_equal_the_full_backward():
+    rng = np.random.default_rng(21)
+    M, N, K, r, s = 37, 29, 64, 5, 0.75
+    X, Wd = rng.standard_normal((M, K)), rng.standard_normal((N, K))
+    A, B, dY = rng.standard_normal((r, K)), rng.standard_normal((N, r)), rng.standard_normal((M, N))
+    _, dA, dB, U = linear.linear_bwd(X, Wd, A, B, s, dY)
+    dA2, dB2, U2 = linear.adapter_grads(X, A, B, s, dY)
+    assert np.array_equal(dA, dA2) and np.array_equal(dB, dB2) and np.array_equal(U, U2)
