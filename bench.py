@@ -261,16 +261,18 @@ def time_steps(wl: Workload, steps: int, warmup: int):
 
 def gemm_traffic(kernel_name: str):
     """Measured HBM bytes per launch from the committed counter summary, used
-    only while the kernel source still matches the one the counters came from."""
+    only while the kernel's source file still matches the one the counters
+    came from (sha256 recorded beside each entry)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         data = json.load(open(path))
-        src = os.path.join(ROOT, "bit_nf4_quantized_02_amd", "csrc", data["source"])
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
         ent = data["kernels"].get(kernel_name)
-        if ent is None or ent.get("source_sha256") != h:
+        if ent is None:
+            return None
+        src = os.path.join(ROOT, "bit_nf4_quantized_02_amd", "csrc", ent["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != ent["source_sha256"]:
             return None
         return float(ent["bytes_per_launch"])
     except Exception:

@@ -79,7 +79,22 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
 // wavefront's 64 lanes thus write 256 contiguous bytes per store. Rows in
 // [n, np) are written as zeros; workgroups with tn == number of n tiles write
 // the low-rank columns of their 64 k rows.
+// Order: the four k-blocks of one 128-byte code line (kb = 4 g .. 4 g + 3)
+// get workgroup ids 8 apart, i.e. the same XCD (ids go to XCDs round-robin)
+// at nearly the same time, so each line is fetched into one L2 once.
 constexpr int kXT = 256;  // weight rows per tile
+
+__device__ __forceinline__ bool cols_unit(int64_t ntiles1, int64_t kblocks, int64_t& tn, int64_t& kb) {
+  const int64_t b = blockIdx.x;
+  const int64_t x = b % 8, q = b / 8;
+  const int64_t j = q % 4, p = q / 4;
+  const int64_t kg = cdiv(kblocks, (int64_t)4);
+  const int64_t u = p * 8 + x;  // (tile, line group) unit
+  if (u >= ntiles1 * kg) return false;
+  tn = u / kg;
+  kb = 4 * (u % kg) + j;
+  return kb < kblocks;
+}
 
 __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ code8,
@@ -91,9 +106,10 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
   __shared__ float lut[16];
   const int t = threadIdx.x;
   const int64_t ldo = np + xc;
-  const int64_t kb = blockIdx.y;
   const int64_t ntiles = (np + kXT - 1) / kXT;
-  if ((int64_t)blockIdx.x == ntiles) {
+  int64_t tn, kb;
+  if (!cols_unit(ntiles + (xc > 0 ? 1 : 0), k / kBlock, tn, kb)) return;
+  if (tn == ntiles) {
     // low-rank columns: out[kb*64 + row, np + j]
     for (int idx = t; idx < 64 * xc; idx += 256) {
       const int row = idx / xc, j = idx - row * xc;
@@ -105,7 +121,7 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
   if (t < 16) lut[t] = codebook[t];
   __syncthreads();
   const float mean = mean_p[0];
-  const int64_t n0 = (int64_t)blockIdx.x * kXT;
+  const int64_t n0 = tn * kXT;
   const int pr = t & 127, half = t >> 7;
   const int64_t na = n0 + 2 * pr, nb = na + 1;
   if (na >= np) return;  // np is a multiple of 64: the pair is in or out together
@@ -155,7 +171,8 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
   } else {
     const int64_t np = expand_pad_rows(w.n);
     const int64_t ntiles = cdiv(np, (int64_t)kXT);
-    const dim3 grid((unsigned)(ntiles + (xc > 0 ? 1 : 0)), (unsigned)(w.k / kBlock));
+    const int64_t units = (ntiles + (xc > 0 ? 1 : 0)) * cdiv(w.k / kBlock, (int64_t)4);
+    const dim3 grid((unsigned)(cdiv(units, (int64_t)8) * 8 * 4));
     expand_cols_kernel<<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, np, lr, r,
                                                  xc, out);
   }

@@ -10,15 +10,15 @@
 //
 // Each workgroup owns NT output rows (n) and the whole contraction; its 4
 // waves split the contraction into quarters. A wave walks its quarter in
-// 128-wide chunks, keeping the loads of the next chunk in flight while it
-// works on one: every lane loads 16 contiguous bytes of codes (32 weights of
-// one row, one 64-block, one scale), expands them to bf16 in registers
+// 256-wide chunks, keeping the loads of the next chunk in flight while it
+// works on one: every lane loads 32 contiguous bytes of codes (one whole
+// 64-block of one row, one scale), expands them to bf16 in registers
 // through an LDS table indexed by whole code bytes (one read yields the
 // levels of two weights; the products are those of the 16-entry codebook)
 // and feeds them straight to
 // v_mfma_f32_16x16x32_bf16 as the B operand; X (padded to 16 rows with zeros)
 // is the A operand. The contraction order inside a chunk is permuted the same
-// way on both operands (lane group g takes columns 32 g .. 32 g + 31), which
+// way on both operands (lane group g takes columns 64 g .. 64 g + 63), which
 // leaves the sum unchanged and makes each lane's code load contiguous.
 // Partial sums of the 4 waves are added in a fixed order through LDS, the
 // low-rank term is added in fp32, and Y is rounded to bf16 once.
@@ -48,10 +48,11 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
   __syncthreads();
   const float mean = mean_p[0];
   const int64_t n0 = (int64_t)blockIdx.x * NT;
-  const int64_t kq = cdiv(cdiv(K, 4), 128) * 128;  // per-wave share, multiple of 128
+  constexpr int kChunk = 256;                            // columns per wave iteration
+  const int64_t kq = cdiv(cdiv(K, 4), kChunk) * kChunk;  // per-wave share
   const int64_t kb = wave * kq;
-  const int64_t ke = (kb + kq < K) ? kb + kq : K;
-  const int grp = lane >> 4;   // 0..3: which 32 columns of a 128-chunk
+  const int64_t ke = (kb + kq < K) ? kb + kq : K;        // multiple of 64
+  const int grp = lane >> 4;   // 0..3: which 64-block of a 256-column chunk
   const int col = lane & 15;   // A: token row m; B: weight row within a tile
   const int64_t kblocks = K / kBlock;
 
@@ -60,10 +61,14 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
   for (int i = 0; i < kTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Per-lane row bases, computed once. Every load below reads a clamped,
-  // in-range address; out-of-range rows / columns / tokens are then replaced
+  // in-range address; out-of-range rows / blocks / tokens are then replaced
   // by code 7 (level 0) or zero activations with selects, so the loop body is
-  // one basic block and the loads of later chunks stay in flight while a
-  // chunk is expanded and multiplied.
+  // one basic block and the next chunk's loads stay in flight while a chunk
+  // is expanded and multiplied. Lane group g takes the whole 64-block g of
+  // the chunk (32 code bytes, one scale): a row's 128-byte code line is read
+  // by one wave in one iteration. The 64 columns are fed to 8 MFMAs, 8 per
+  // MFMA; the activations follow the same column permutation, which leaves
+  // the sum unchanged.
   const uint8_t* crow[kTiles];
   int64_t bbase[kTiles];
   bool rowok[kTiles];
@@ -79,21 +84,22 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
   const bool xok = col < M;
 
   struct Stage {
-    u32x4 cw[kTiles];
+    u32x4 cw[kTiles][2];
     uint32_t c8[kTiles];
     float s2v[kTiles];
-    u32x4 xa[4];
+    u32x4 xa[8];
     bool kin;
   };
   auto load = [&](int64_t k0, Stage& st) {
-    const int64_t k = k0 + 32 * grp;
-    st.kin = k < ke;                        // ke is a multiple of 32 (K % 64 == 0)
-    const int64_t kc = st.kin ? k : ke - 32;  // a valid column of this wave's range
+    const int64_t k = k0 + 64 * grp;
+    st.kin = k < ke;
+    const int64_t kc = st.kin ? k : ke - 64;  // a valid block of this wave's range
 #pragma unroll
-    for (int s = 0; s < 4; ++s) st.xa[s] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * s);
+    for (int s = 0; s < 8; ++s) st.xa[s] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * s);
 #pragma unroll
     for (int i = 0; i < kTiles; ++i) {
-      st.cw[i] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2);
+      st.cw[i][0] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2);
+      st.cw[i][1] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2 + 16);
       const int64_t blk = bbase[i] + kc / kBlock;
       st.c8[i] = code8[blk];
       st.s2v[i] = s2[blk / kDqBlock];
@@ -101,9 +107,9 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
   };
   auto compute = [&](const Stage& st) {
     const bool xuse = st.kin && xok;
-    bf16x8 xa[4];
+    bf16x8 xa[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 8; ++s) {
       u32x4 v = st.xa[s];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = xuse ? v[e] : 0u;
@@ -114,26 +120,27 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
       const bool use = st.kin && rowok[i];
       const float cp = decode_block_scale(st.c8[i], st.s2v[i], mean);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t word = use ? st.cw[i][s] : 0x77777777u;  // code 7: level 0
+      for (int s = 0; s < 8; ++s) {
+        const uint32_t word = use ? st.cw[i][s >> 2][s & 3] : 0x77777777u;  // code 7: level 0
         const u32x4 bw = dequant8_pairs(word, lut2, cp);
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[s], __builtin_bit_cast(bf16x8, bw), acc[i], 0, 0, 0);
       }
     }
   };
   if (kb < ke) {  // (a wave may have no columns when K is tiny)
-    {
-      Stage st0, st1;
-      load(kb, st0);
-      for (int64_t k0 = kb; k0 < ke; k0 += 2 * 128) {
-        load(k0 + 128, st1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(st0);
-        if (k0 + 128 >= ke) break;
-        load(k0 + 256, st0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(st1);
-      }
+    Stage st0, st1;
+    load(kb, st0);
+    for (int64_t k0 = kb; k0 < ke; k0 += 2 * kChunk) {
+      // the scheduling barriers keep each chunk's loads issued ahead of the
+      // work on the previous chunk (the compiler would otherwise sink them to
+      // their first use)
+      load(k0 + kChunk, st1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st0);
+      if (k0 + kChunk >= ke) break;
+      load(k0 + 2 * kChunk, st0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st1);
     }
   }
   // D[m][n]: lane -> n = lane & 15, m = 4 (lane >> 4) + v
