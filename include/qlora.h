@@ -264,7 +264,7 @@ qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight *w, const void *X, int64_
 #define QLORA_PATH_GEMV 0
 #define QLORA_PATH_FUSED 1
 #define QLORA_PATH_EXPANDED 2
-#define QLORA_EXPAND_MIN_M 1024
+#define QLORA_EXPAND_MIN_M 128
 int qlora_linear_path(int64_t M, int64_t n, int64_t k, int r, int is_bwd);
 
 /* Bytes of the expanded operand of qlora_nf4_expand (0 on bad arguments). */

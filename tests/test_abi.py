@@ -129,6 +129,8 @@ def test_path_choice_and_expanded_sizes(q):
     assert q.linear_path(1, 4096, 4096, 16, False) == q.PATH_GEMV
     assert q.linear_path(16, 4096, 4096, 16, False) == q.PATH_GEMV
     assert q.linear_path(17, 4096, 4096, 16, False) == q.PATH_FUSED
+    assert q.linear_path(127, 4096, 4096, 16, False) == q.PATH_FUSED
+    assert q.linear_path(128, 4096, 4096, 16, False) == q.PATH_EXPANDED
     assert q.linear_path(16, 4096, 4096, 16, True) == q.PATH_FUSED
     big = 4096
     assert q.linear_path(big, 4096, 4096, 16, False) == q.PATH_EXPANDED
@@ -146,7 +148,7 @@ def test_path_choice_and_expanded_sizes(q):
     assert q.nf4_expand_bytes(100, 256, 0, True) == r256(256 * 128 * 2)
     assert q.nf4_expand_bytes(100, 255, 0, True) == 0
     # the layer workspace grows by the expanded operand exactly when that path is taken
-    fw_small = q.linear_workspace_bytes(512, 4096, 4096, 16, False)
+    fw_small = q.linear_workspace_bytes(64, 4096, 4096, 16, False)
     fw_big = q.linear_workspace_bytes(big, 4096, 4096, 16, False)
     assert fw_big - fw_small >= q.nf4_expand_bytes(4096, 4096, 16, False)
 

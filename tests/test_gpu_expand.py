@@ -87,7 +87,7 @@ def test_bf16_gemm_building_blocks(q, m, n, k, r):
     assert report("dX", f32(dX), dXr) <= TOL
 
 
-@pytest.mark.parametrize("m,n,k,r", [(1030, 520, 384, 16), (1024, 100, 256, 8), (1300, 264, 192, 64)])
+@pytest.mark.parametrize("m,n,k,r", [(1030, 520, 384, 16), (1024, 100, 256, 8), (1300, 264, 192, 64), (128, 72, 64, 1)])
 def test_linear_at_expanded_sizes(q, m, n, k, r):
     """qlora_linear_fwd/bwd where the path is the expanded one (n % 8 != 0
     keeps dX on the fused kernel)."""

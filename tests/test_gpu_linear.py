@@ -131,3 +131,30 @@ def test_identity_input_lists_the_effective_weight(q):
     wd = q.dequant(gw)
     torch.cuda.synchronize()
     assert torch.equal(Y.cpu(), wd.cpu().t().contiguous())
+
+
+@pytest.mark.parametrize("m,n,k,r", [(300, 200, 192, 8), (512, 384, 1024, 16), (257, 100, 640, 5), (700, 264, 512, 64),
+                                     (256, 128, 256, 128), (300, 130, 320, 0)])
+def test_fused_kernels_direct(q, m, n, k, r):
+    """The fused dequant GEMMs called directly (qlora_linear_* prefers the
+    expanded path at these token counts): several tiles, ragged edges."""
+    say(f"case: fused kernels M={m} N={n} K={k} r={r}")
+    s = 2.0 if r else 0.0
+    li = _inputs(m, n, k, r, seed=7 * m + n + k + r)
+    gw = q.quantize_nf4(li.W.cuda())
+    X, dY = li.X.cuda(), li.dY.cuda()
+    A = li.A.cuda() if r else None
+    B = li.B.cuda() if r else None
+    TS = US = None
+    if r:
+        _, TS = q.lowrank_project(X, A, 0, s, want_out=False, want_split=True)
+        _, US = q.lowrank_project(dY, B, 1, s, want_out=False, want_split=True)
+    Y = q.nf4_gemm_fwd(gw, X, TS, B)
+    dX = q.nf4_gemm_dx(gw, dY, US, A)
+    torch.cuda.synchronize()
+    Wd = oracle_encode(li.W).dequant()
+    Xo, Ao, Bo, dYo = (t.float().numpy() for t in (li.X, li.A, li.B, li.dY))
+    Yr, _ = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
+    dXr, _, _, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
+    assert report("Y", f32(Y), Yr) <= TOL
+    assert report("dX", f32(dX), dXr) <= TOL
