@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
 """Throughput of the QLoRA NF4 linear (forward + backward) on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input:
-  forward   T = X A^T (+ bf16 hi/lo split)            qlora_lowrank_project
-            Y = X W'^T + s T B^T (fused dequant GEMM)   qlora_nf4_gemm_fwd / _gemv_fwd
-  backward  U = dY B (+ split)                          qlora_lowrank_project
-            dX = dY W' + s U A (fused dequant GEMM)     qlora_nf4_gemm_dx
-            dA = s U^T X, dB = s dY^T T                 qlora_lowrank_grad
-These are exactly the calls qlora_linear_fwd / qlora_linear_bwd make, issued
-one by one so each can be bracketed by HIP events on the launch stream.
-Inputs are resident in HBM when the timed region starts; the weight is
-encoded once before it (the encoder is reported separately).
+One step = one pass of the whole hot path over one batch of synthetic input,
+issued as the layer calls a caller makes: qlora_linear_fwd then
+qlora_linear_bwd (the step time and `value`). At large token counts they run
+  forward   T = X A^T (+ bf16 hi/lo split)            rowdot
+            F = expanded W' with [B | B] appended      row expansion
+            Y = [X | sT] F^T, one bf16 rounding         bf16 MFMA GEMM
+  backward  U = dY B (+ split)                          rowdot
+            G = expanded W'^T with [A ; A] appended    transposing expansion
+            dX = [dY | sU] G^T                          bf16 MFMA GEMM
+            dA = s U^T X, dB = s dY^T T                 split-M MFMA + ordered reduce
+(medium M: fused dequant GEMMs; M <= 16: dequant GEMV). A second timed
+region issues the same kernels as the exported building-block calls, each
+bracketed by HIP events on the launch stream, for the per-piece breakdown and
+the dominant kernel's roofline. Inputs are resident in HBM when the timed
+regions start; the weight is encoded once before them.
 
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
@@ -166,6 +171,20 @@ class LinearPlan:
                              q.Call("qlora_lowrank_grad", P(self.dY), M, N, P(self.T), r, self.s, P(self.dB), 1, 0, ws,
                                     wsn, st)))
 
+        # the layer calls themselves (what a caller runs: same kernels, launched
+        # back to back inside one C call per pass)
+        fw = lib.qlora_linear_workspace_bytes(M, N, K, r, 0)
+        bw = lib.qlora_linear_workspace_bytes(M, N, K, r, 1) if backward else 0
+        self.lws = torch.empty(max(fw, bw, 256), dtype=torch.uint8, device=dev)
+        lw, lwn = P(self.lws), self.lws.numel()
+        self.api_fwd = q.Call("qlora_linear_fwd", wref, P(self.X), M, P(self.A), P(self.B), r, self.s, P(self.Y),
+                              P(self.T), lw, lwn, st, keep=(self.wst,))
+        self.api_bwd = None
+        if backward:
+            self.api_bwd = q.Call("qlora_linear_bwd", wref, P(self.X), P(self.T), P(self.dY), M, P(self.A),
+                                  P(self.B), r, self.s, P(self.dX), P(self.dA), P(self.dB), 0, lw, lwn, st,
+                                  keep=(self.wst,))
+
     @property
     def packed_bytes(self):
         return self.W.nbytes()
@@ -179,7 +198,8 @@ class Workload:
         self.c = synth.CONFIGS[cid]
         self.tag = {1: "proj_1024_m16", 2: "attn_proj_4096_m4096", 3: "mlp_7b_m2048", 4: "decode_70b"}[cid]
         c = self.c
-        self.pieces = []      # (name, flops, call)
+        self.pieces = []      # (name, flops, call): the building blocks, for the per-piece breakdown
+        self.api = []         # the layer calls of one step, in order
         self.plans = []
         self.passes_bytes = 0  # packed-weight bytes streamed per step
         if cid in (1, 2):
@@ -188,6 +208,7 @@ class Workload:
             p = LinearPlan(q, li, force_path=force_path)
             self.plans.append(p)
             self.pieces = p.fwd + p.bwd
+            self.api = [p.api_fwd, p.api_bwd]
             self.passes_bytes = 2 * p.packed_bytes
             self.desc = dict(workload=c.title, M=c.m[0], N=lin.n, K=lin.k, r=c.r, alpha=c.alpha, passes="fwd+bwd")
         elif cid == 3:
@@ -215,6 +236,7 @@ class Workload:
                            + ren(pd.bwd, "down") + [("silu_mul_bwd", 0, silu_b)] + ren(pu.bwd, "up")
                            + ren(pg.bwd, "gate"))
             self.plans = [pg, pu, pd]
+            self.api = [pg.api_fwd, pu.api_fwd, silu_f, pd.api_fwd, pd.api_bwd, silu_b, pu.api_bwd, pg.api_bwd]
             self.passes_bytes = 2 * sum(p.packed_bytes for p in self.plans)
             self.desc = dict(workload=c.title, M=M, r=c.r, alpha=c.alpha, passes="fwd+bwd, chained through SiLU")
         elif cid == 4:
@@ -223,6 +245,7 @@ class Workload:
                     li = synth.linear_inputs(cid, 0, li_i, lin.n, lin.k, M, c.r, c.scale, sigma=c.sigma)
                     p = LinearPlan(q, li, backward=False)
                     self.plans.append(p)
+                    self.api.append(p.api_fwd)
                     self.pieces += [(f"{lin.name}.M{M}.{nme}", f, cl) for nme, f, cl in p.fwd]
                     self.passes_bytes += p.packed_bytes
             self.desc = dict(workload=c.title, M=list(c.m), r=c.r, alpha=c.alpha, passes="fwd")
@@ -233,15 +256,40 @@ class Workload:
 
 
 def time_steps(wl: Workload, steps: int, warmup: int):
-    calls = [cl for _, _, cl in wl.pieces]
-    npc = len(calls)
+    """Two timed regions over the same workload.
+
+    A (the step time and `value`): K steps of the layer calls exactly as a
+      caller issues them; nothing else on the stream, synchronize before and
+      after; one event pair brackets the whole region.
+    B (breakdown and roofline): K steps of the same kernels issued as the
+      building-block calls, each bracketed by HIP events on the launch stream.
+      Every event adds a few microseconds of idle time at its boundary, so the
+      pieces of B sum to more than A's step; each piece's own duration is
+      what the breakdown and the dominant-kernel roofline use.
+    """
     for _ in range(warmup):
-        for cl in calls:
+        for cl in wl.api:
+            cl()
+        for _, _, cl in wl.pieces:
             cl()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(npc + 1)] for _ in range(steps)]
+    # region A
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        for cl in wl.api:
+            cl()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ev_step = e0.elapsed_time(e1) / steps
+    # region B
+    calls = [cl for _, _, cl in wl.pieces]
+    npc = len(calls)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(npc + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
     for s in range(steps):
         ev = evs[s]
         ev[0].record()
@@ -249,14 +297,13 @@ def time_steps(wl: Workload, steps: int, warmup: int):
             cl()
             ev[i + 1].record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
     per = np.zeros(npc)
     for s in range(steps):
         for i in range(npc):
             per[i] += evs[s][i].elapsed_time(evs[s][i + 1])
     per_ms = per / steps
-    ev_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]))
-    return wall * 1e3, ev_step, per_ms
+    pieces_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]))
+    return wall * 1e3, ev_step, per_ms, pieces_step
 
 
 def gemm_traffic(kernel_name: str):
@@ -347,7 +394,7 @@ def main():
                                 | {f"bwd:{names_of[p.path_bwd]}" for p in wl.plans if p.bwd})
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
-    ms_wall, ms_ev, per_ms = time_steps(wl, args.steps, args.warmup)
+    ms_wall, ms_ev, per_ms, ms_pieces = time_steps(wl, args.steps, args.warmup)
     names = [nme for nme, _, _ in wl.pieces]
     flops = [f for _, f, _ in wl.pieces]
     value = wl.flops / (ms_wall * 1e-3) / 1e12
@@ -389,6 +436,7 @@ def main():
         "config": wl.desc,
         "packed_weight_GBps": round(gbps, 1),
         "ms_per_step_events": round(ms_ev, 4),
+        "ms_per_step_evented_pieces": round(ms_pieces, 4),
         "flops_per_step": wl.flops,
         "breakdown_us": breakdown,
         "roofline": roof,
