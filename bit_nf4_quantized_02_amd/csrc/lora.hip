@@ -106,24 +106,45 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
       }
     }
   };
-  u32x4 pv[4];
-  load_p(m0, pv);
-  for (int64_t mb = m0; mb < m1; mb += 32) {
+  // Q of one step (32 tokens x kRP, fp32): thread t owns elements t + 256 e
+  constexpr int kQE = 32 * kRP / 256;
+  auto load_q = [&](int64_t mb, float (&qv)[kQE]) {
+#pragma unroll
+    for (int e = 0; e < kQE; ++e) {
+      const int idx = t + 256 * e;
+      const int mm = idx / kRP, j = idx % kRP;
+      const int64_t m = mb + mm;
+      qv[e] = (j < r && m < m1) ? Q[m * r + j] : 0.0f;
+    }
+  };
+  // Several steps of P and Q in flight: a ring of register stages with
+  // compile-time indices (the loop is unrolled by the ring length), each
+  // refilled for the step kDepth ahead right after it has been staged into
+  // LDS. Four stages up to r = 32; one for larger ranks (register budget).
+  constexpr int kDepth = kRP <= 32 ? 4 : 1;
+  struct Stage {
+    u32x4 p[4];
+    float q[kQE];
+  };
+  auto step = [&](int64_t mb, Stage& stg) {
     // stage this step: P from registers, Q converted to bf16 hi / lo
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(sm.p + ((t >> 5) + 8 * i) * kPPitch + (t & 31) * 16) = pv[i];
-    for (int e = t; e < 32 * kRP; e += 256) {
-      const int mm = e / kRP, j = e % kRP;
-      const int64_t m = mb + mm;
-      const float q = (j < r && m < m1) ? Q[m * r + j] : 0.0f;
-      const uint16_t qh = to_bf16_bits(q);
-      const uint16_t ql = to_bf16_bits(q - bf16_bits_to_f32(qh));
+      *reinterpret_cast<u32x4*>(sm.p + ((t >> 5) + 8 * i) * kPPitch + (t & 31) * 16) = stg.p[i];
+#pragma unroll
+    for (int e = 0; e < kQE; ++e) {
+      const int idx = t + 256 * e;
+      const int mm = idx / kRP, j = idx % kRP;
+      const uint16_t qh = to_bf16_bits(stg.q[e]);
+      const uint16_t ql = to_bf16_bits(stg.q[e] - bf16_bits_to_f32(qh));
       *reinterpret_cast<uint16_t*>(sm.qh + mm * kQP + j * 2) = qh;
       *reinterpret_cast<uint16_t*>(sm.ql + mm * kQP + j * 2) = ql;
     }
     __syncthreads();
-    if (mb + 32 < m1) load_p(mb + 32, pv);  // in flight during the MFMAs
+    if (mb + kDepth * 32 < m1) {
+      load_p(mb + kDepth * 32, stg.p);
+      load_q(mb + kDepth * 32, stg.q);
+    }
     bf16x8 pb[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) pb[ct] = tr_operand(sm.p, kPPitch, wave * 64 + ct * 16, lane);
@@ -138,6 +159,26 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
       }
     }
     __syncthreads();
+  };
+  if constexpr (kDepth == 4) {
+    Stage s0, s1, s2, s3;
+    load_p(m0, s0.p); load_q(m0, s0.q);
+    load_p(m0 + 32, s1.p); load_q(m0 + 32, s1.q);
+    load_p(m0 + 64, s2.p); load_q(m0 + 64, s2.q);
+    load_p(m0 + 96, s3.p); load_q(m0 + 96, s3.q);
+    for (int64_t mb = m0; mb < m1; mb += 4 * 32) {
+      step(mb, s0);
+      if (mb + 32 >= m1) break;
+      step(mb + 32, s1);
+      if (mb + 64 >= m1) break;
+      step(mb + 64, s2);
+      if (mb + 96 >= m1) break;
+      step(mb + 96, s3);
+    }
+  } else {
+    Stage s0;
+    load_p(m0, s0.p); load_q(m0, s0.q);
+    for (int64_t mb = m0; mb < m1; mb += 32) step(mb, s0);
   }
   // D[j][c]: lane -> c = lane % 16, j = 4 (lane / 16) + v
 #pragma unroll
