@@ -200,8 +200,18 @@ __global__ __launch_bounds__(256) void coldot_reduce_kernel(const float* __restr
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= C * r) return;
   const int64_t j = i / C, c = i % C;
+  // partials added in split order; loaded eight at a time so the loads of a
+  // batch are in flight together
   float s = 0.0f;
-  for (int64_t p = 0; p < nsplit; ++p) s += partial[(p * r + j) * C + c];
+  int64_t p = 0;
+  for (; p + 8 <= nsplit; p += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[((p + u) * r + j) * C + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; p < nsplit; ++p) s += partial[(p * r + j) * C + c];
   float* g = G + c * g_sc + j * g_sj;
   const float v = scale * s;
   *g = accumulate ? (*g + v) : v;

@@ -107,13 +107,21 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t c = w0; c < w1; c += 32 * kU) {
+  // One batch = kU column steps of 32: the P operand and the raw Q values.
+  // Two batches rotate (the loop is unrolled by two), so the next batch's
+  // loads are in flight while the current one is multiplied.
+  constexpr int kChunks = 32 * kRP / 8;  // 16-byte chunks of one staged [32][kRP] Q tile
+  constexpr int kQL1 = kQL == 1 ? kU * (kChunks / 64) : 1;
+  struct Batch {
     u32x4 a[kU];
-    bf16x8 b[kU][kTiles];
+    u32x4 q0[kQL == 0 ? kU * kTiles : 1];  // Q = [r, C]: operand layout
+    u32x4 q1[kQL1];                        // Q = [C, r]: raw chunks for the LDS tile
+  };
+  auto load = [&](int64_t c, Batch& bt) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      a[u] = load8<kVecP>(prow, c + 32 * u + ko, w1);
-      if (m >= M) a[u] = u32x4{0u, 0u, 0u, 0u};
+      bt.a[u] = load8<kVecP>(prow, c + 32 * u + ko, w1);
+      if (m >= M) bt.a[u] = u32x4{0u, 0u, 0u, 0u};
     }
     if constexpr (kQL == 0) {
 #pragma unroll
@@ -123,16 +131,10 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
           const int j = t * 16 + row;
           u32x4 v = {0u, 0u, 0u, 0u};
           if (j < r) v = load8<kVecQ>(Q + (int64_t)j * C, c + 32 * u + ko, w1);
-          b[u][t] = __builtin_bit_cast(bf16x8, v);
+          bt.q0[u * kTiles + t] = v;
         }
     } else {
-      // The staged region is rewritten every iteration: the empty asm keeps
-      // the compiler from moving these stores above the previous iteration's
-      // transposing reads (or the reads above the stores), which it might
-      // otherwise treat as unrelated accesses.
-      asm volatile("" ::: "memory");
-      // stage Q[c + 32 u + cc][0 .. kRP) as [32][kRP] bf16 tiles (zeros past w1 / r)
-      constexpr int kChunks = 32 * kRP / 8;  // 16-byte chunks per tile
+      // Q[c + 32 u + cc][jc .. jc + 7] for chunk q = lane + 64 i (zeros past w1 / r)
 #pragma unroll
       for (int u = 0; u < kU; ++u)
 #pragma unroll
@@ -152,7 +154,31 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
               for (int x = 0; x < 4; ++x) v[x] = e[2 * x] | (e[2 * x + 1] << 16);
             }
           }
-          *reinterpret_cast<u32x4*>(stage + u * 32 * Cfg::kQPitch + cc * Cfg::kQPitch + jc * 2) = v;
+          bt.q1[u * (kChunks / 64) + i] = v;
+        }
+    }
+  };
+  auto compute = [&](const Batch& bt) {
+    bf16x8 b[kU][kTiles];
+    if constexpr (kQL == 0) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) b[u][t] = __builtin_bit_cast(bf16x8, bt.q0[u * kTiles + t]);
+    } else {
+      // The staged region is rewritten every batch: the empty asm keeps the
+      // compiler from moving these stores above the previous batch's
+      // transposing reads (or the reads above the stores), which it might
+      // otherwise treat as unrelated accesses.
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int i = 0; i < kChunks / 64; ++i) {
+          const int q = lane + 64 * i;
+          const int cc = q / (kRP / 8), jc = (q % (kRP / 8)) * 8;
+          *reinterpret_cast<u32x4*>(stage + u * 32 * Cfg::kQPitch + cc * Cfg::kQPitch + jc * 2) =
+              bt.q1[u * (kChunks / 64) + i];
         }
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -164,7 +190,28 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int t = 0; t < kTiles; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]), b[u][t], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bt.a[u]), b[u][t], acc[t], 0, 0, 0);
+  };
+  constexpr int64_t kStep = 32 * kU;
+  if constexpr (!kVecP || !kVecQ) {
+    // element-wise loads hold several registers per value: no second batch
+    for (int64_t c = w0; c < w1; c += kStep) {
+      Batch b0;
+      load(c, b0);
+      compute(b0);
+    }
+  } else if (w0 < w1) {
+    Batch b0, b1;
+    load(w0, b0);
+    for (int64_t c = w0; c < w1; c += 2 * kStep) {
+      load(c + kStep, b1);  // past w1 the loads read nothing (zeros)
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b0);
+      if (c + kStep >= w1) break;
+      load(c + 2 * kStep, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(b1);
+    }
   }
   __syncthreads();  // all staged-Q reads done before the region is reused
   // D layout: lane -> column (lane & 15), rows 4 (lane >> 4) + v
@@ -231,8 +278,17 @@ __global__ __launch_bounds__(256) void rowdot_finalize_kernel(const float* __res
   const int G = 256 / r;
   if (t < G * r) {
     const int j = t % r, g = t / r;
+    // splits g, g + G, ... in order, loaded four at a time
     float s = 0.0f;
-    for (int64_t p = g; p < nsplit; p += G) s += part[(p * M + m) * r + j];
+    int64_t p = g;
+    for (; p + 3 * G < nsplit; p += 4 * G) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = part[((p + u * G) * M + m) * r + j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; p < nsplit; p += G) s += part[(p * M + m) * r + j];
     gsum[g * r + j] = s;
   }
   __syncthreads();
