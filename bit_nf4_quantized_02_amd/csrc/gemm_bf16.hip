@@ -18,8 +18,10 @@
 //
 // Per-step cost is kept off the vector ALU: every lane's byte offset inside
 // each operand (row, swizzled chunk) is computed once, and a step only moves
-// the wave-uniform base pointer by 128 bytes, so each copy is one
-// scalar-base + 32-bit-offset instruction. Inside a step the next substep's
+// a scalar offset by 128 bytes. The copies are buffer loads into LDS (one
+// descriptor per operand, 32-bit lane offset + scalar step offset): measured
+// 4-8% faster for the whole GEMM than the same copies issued as global loads
+// into LDS, which need a 64-bit address per lane. Inside a step the next substep's
 // fragment reads are interleaved one-to-one with the current substep's MFMAs
 // (scheduling groups), so LDS latency hides behind the matrix core. The
 // epilogue stages each wave's bf16 outputs through LDS and writes full 16-byte
@@ -46,6 +48,8 @@ struct BfArgs {
 
 constexpr int kCopies = 32 / kWaves;  // 1 KB copies per wave per operand tile
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 // Byte offsets of this lane's copies, relative to the operands' base pointer
 // advanced to the step's first column. For the last base step of a ragged
 // contraction (kc % 64 != 0) the column is clamped to the last in-range chunk
@@ -60,8 +64,8 @@ struct CopyPlan {
   u32x4 f;      // expanded operand
 };
 
-__device__ __forceinline__ void make_plan(const BfArgs& a, int64_t m0, int64_t n0, int nk_main, CopyPlan& p) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void make_plan(const BfArgs& a, int64_t m0, int64_t n0, int nk_main, int wave, CopyPlan& p) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) {
     const int row = (wave * kCopies + i) * 8 + (lane >> 3);
@@ -77,39 +81,58 @@ __device__ __forceinline__ void make_plan(const BfArgs& a, int64_t m0, int64_t n
   }
 }
 
-__device__ __forceinline__ void copy16(const char* base, uint32_t off, char* dst) {
-  __builtin_amdgcn_global_load_lds((const void*)(base + off), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+// Direct buffer load into LDS (16 bytes per lane, LDS address from the wave-
+// uniform destination), declared through its LLVM intrinsic so the compiler
+// keeps track of the LDS region written and does not wait for these copies
+// before reading the other buffer.
+__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds, int size, int voffset,
+                                    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer descriptor for a whole operand: base address, size in bytes (the
+// offsets of every copy stay below it), raw 32-bit dword format.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r[2] = (int)(uint32_t)(bytes < (int64_t)0xFFFFFFFF ? bytes : (int64_t)0xFFFFFFFF);
+  r[3] = 0x00020000;
+  return r;
 }
 
-// Copies of step `step` into (As, Bs). The branch is uniform (it depends on
-// the step only), so both bases stay scalar.
-__device__ __forceinline__ void issue_step(const BfArgs& a, const CopyPlan& p, int step, int nk_main, char* As,
-                                           char* Bs) {
-  const int wave = threadIdx.x >> 6;
+struct Rsrc {
+  i32x4 act, x, f;
+};
+
+__device__ __forceinline__ void copy16(const i32x4& r, uint32_t voff, int soff, char* dst) {
+  raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t*)dst, 16, (int)voff, soff, 0, 0);
+}
+
+// Copies of step `step` into (As, Bs). The operand choice is wave-uniform
+// (it depends on the step only), so descriptors and step offsets stay scalar.
+__device__ __forceinline__ void issue_step(const Rsrc& rs, const CopyPlan& p, int step, int nk_main, int wave,
+                                           char* As, char* Bs) {
   char* const as = As + wave * kCopies * 1024;
   char* const bs = Bs + wave * kCopies * 1024;
   if (step < nk_main) {
-    const char* base = reinterpret_cast<const char*>(a.act) + (int64_t)step * (kBK * 2);
     const u32x4 off = step == nk_main - 1 ? p.alast : p.a;
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) copy16(base, off[i], as + i * 1024);
+    for (int i = 0; i < kCopies; ++i) copy16(rs.act, off[i], step * (kBK * 2), as + i * 1024);
   } else {
-    const char* base = reinterpret_cast<const char*>(a.act_x) + (int64_t)(step - nk_main) * (kBK * 2);
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) copy16(base, p.x[i], as + i * 1024);
+    for (int i = 0; i < kCopies; ++i) copy16(rs.x, p.x[i], (step - nk_main) * (kBK * 2), as + i * 1024);
   }
-  const char* fbase = reinterpret_cast<const char*>(a.f) + (int64_t)step * (kBK * 2);
 #pragma unroll
-  for (int i = 0; i < kCopies; ++i) copy16(fbase, p.f[i], bs + i * 1024);
+  for (int i = 0; i < kCopies; ++i) copy16(rs.f, p.f[i], step * (kBK * 2), bs + i * 1024);
 }
 
 // One step: MFMAs on (Ac, Bc) while the copies of step + 1 fill (An, Bn).
 // Restrict pointers tell the compiler the copies cannot alias the fragment
 // reads, so it does not wait for them before reading.
-__device__ __forceinline__ void bf16_step(const BfArgs& a, const CopyPlan& p, int step, int nk, int nk_main,
+__device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int step, int nk, int nk_main, int wave,
                                           const char* __restrict__ Ac, const char* __restrict__ Bc,
                                           char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
   // past the last step the copy repeats the last step into a buffer no later
   // step reads: keeps the body free of branches
@@ -123,7 +146,7 @@ __device__ __forceinline__ void bf16_step(const BfArgs& a, const CopyPlan& p, in
   };
   read_frags(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  issue_step(a, p, s1, nk_main, An, Bn);
+  issue_step(rs, p, s1, nk_main, wave, An, Bn);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -157,7 +180,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   __shared__ __attribute__((aligned(16))) char Bs0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs1[kTileBytes];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
   int64_t tm, tn;
   tile_of(tm, tn, cdiv(a.M, (int64_t)kBM), cdiv(a.nout, (int64_t)kBN));
@@ -166,7 +190,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   const int nk = nk_main + a.kx / kBK;
 
   CopyPlan plan;
-  make_plan(a, m0, n0, nk_main, plan);
+  make_plan(a, m0, n0, nk_main, wave, plan);
+  Rsrc rs;
+  rs.act = make_rsrc(a.act, a.M * a.kc * 2);
+  rs.x = make_rsrc(a.act_x, a.M * (int64_t)a.kx * 2);
+  rs.f = make_rsrc(a.f, a.nout * a.ldf * 2);
 
   f32x16 acc[kTM][kTN];
 #pragma unroll
@@ -176,11 +204,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  issue_step(a, plan, 0, nk_main, As0, Bs0);
+  issue_step(rs, plan, 0, nk_main, wave, As0, Bs0);
   step_barrier<0>();
   for (int step = 0; step < nk; step += 2) {
-    bf16_step(a, plan, step, nk, nk_main, As0, Bs0, As1, Bs1, acc);
-    if (step + 1 < nk) bf16_step(a, plan, step + 1, nk, nk_main, As1, Bs1, As0, Bs0, acc);
+    bf16_step(rs, plan, step, nk, nk_main, wave, As0, Bs0, As1, Bs1, acc);
+    if (step + 1 < nk) bf16_step(rs, plan, step + 1, nk, nk_main, wave, As1, Bs1, As0, Bs0, acc);
   }
 
   // Epilogue: each wave writes its 128 x 64 bf16 block (16 KB) into its own
