@@ -24,13 +24,16 @@ namespace qlora {
 
 namespace {
 
-// Row expansion: one thread per 16-byte output chunk (8 bf16 = one 32-bit
-// code word). Workgroup (x, row) covers chunks 256 x .. 256 x + 255 of one
-// output row, so every store instruction of a wavefront writes 1 KB of
-// contiguous output and no index needs a division (grid: x = rows, y = chunk
-// blocks). Workgroups with y equal to the number of code-chunk blocks write
-// the LoRA columns of 256 / (xc / 8) rows each (the others in that column
-// exit at once).
+// Row expansion: one thread per 16-byte output chunk column (8 bf16 = one
+// 32-bit code word) of kRows consecutive weight rows. Workgroup (x, y) covers
+// chunks 256 y .. 256 y + 255 of rows kRows x .. kRows x + kRows - 1: every
+// store instruction of a wavefront writes 1 KB of contiguous output, and a
+// thread issues all kRows code-word and scale loads before its first store,
+// so each workgroup keeps kRows round trips to memory in flight instead of
+// one. Workgroups with y equal to the number of code-chunk blocks write the
+// LoRA columns of their rows.
+constexpr int kRows = 8;
+
 __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ code8,
                                                           const float* __restrict__ s2,
@@ -41,12 +44,12 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
   const int t = threadIdx.x;
   const int64_t kw = k / 8;
   const int64_t ldc = (k + xc) / 8;  // output row pitch in chunks
-  const int64_t row = blockIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * kRows;
   if ((int64_t)blockIdx.y * 256 >= kw) {
-    // LoRA columns: rows row .. row + rpb - 1 when row % rpb == 0
-    const int cpr = xc / 8, rpb = 256 / cpr;
-    if (row % rpb != 0 || t >= rpb * cpr) return;
-    const int64_t rr = row + t / cpr;
+    // LoRA columns of rows r0 .. r0 + kRows - 1 (kRows * xc / 8 <= 128 threads)
+    const int cpr = xc / 8;
+    if (t >= kRows * cpr) return;
+    const int64_t rr = r0 + t / cpr;
     const int j0 = (t % cpr) * 8;
     if (rr >= n) return;
     u32x4 v;
@@ -68,8 +71,20 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
   __syncthreads();
   const int64_t c = (int64_t)blockIdx.y * 256 + t;
   if (c >= kw) return;
-  const int64_t wi = row * kw + c;  // code word index
-  out[row * ldc + c] = dequant8(codes[wi], lut, block_scale(code8, s2, mean_p[0], wi >> 3));
+  const float mean = mean_p[0];
+  uint32_t word[kRows], c8[kRows];
+  float s2v[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int64_t row = r0 + i < n ? r0 + i : n - 1;  // rows past n repeat the last one (not stored)
+    const int64_t wi = row * kw + c;                  // code word index
+    word[i] = codes[wi];
+    c8[i] = code8[wi >> 3];
+    s2v[i] = s2[(wi >> 3) / kDqBlock];
+  }
+#pragma unroll
+  for (int i = 0; i < kRows; ++i)
+    if (r0 + i < n) out[(r0 + i) * ldc + c] = dequant8(word[i], lut, decode_block_scale(c8[i], s2v[i], mean));
 }
 
 // Transposing expansion, straight from registers. Workgroup (tn, kb) covers
@@ -165,7 +180,7 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
   const int xc = lora_extra_cols(r);
   if (!transposed) {
     const int64_t kw = w.k / 8;
-    const dim3 grid((unsigned)w.n, (unsigned)(cdiv(kw, (int64_t)256) + (xc > 0 ? 1 : 0)));
+    const dim3 grid((unsigned)cdiv(w.n, (int64_t)kRows), (unsigned)(cdiv(kw, (int64_t)256) + (xc > 0 ? 1 : 0)));
     expand_rows_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(w.codes), w.code8, w.s2, w.mean,
                                                  w.codebook, w.n, w.k, lr, r, xc, reinterpret_cast<u32x4*>(out));
   } else {
