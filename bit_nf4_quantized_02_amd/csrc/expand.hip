@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
   const int64_t ldc = (k + xc) / 8;  // output row pitch in chunks
   const int64_t r0 = (int64_t)blockIdx.x * kRows;
   if ((int64_t)blockIdx.y * 256 >= kw) {
-    // LoRA columns of rows r0 .. r0 + kRows - 1 (kRows * xc / 8 <= 128 threads)
+    // LoRA columns of rows r0 .. r0 + kRows - 1 (kRows * xc / 8 <= 256 threads for r <= 128)
     const int cpr = xc / 8;
     if (t >= kRows * cpr) return;
     const int64_t rr = r0 + t / cpr;
