@@ -351,7 +351,7 @@ def cpu_baseline(wl: Workload, target_s: float):
     flops = sum(f for _, f, _ in p.fwd + p.bwd)
     n, spent = 0, 0.0
     out = None
-    while (spent < target_s and n < 20) or n == 0:
+    while (spent < target_s and n < 200) or n == 0:
         t0 = time.perf_counter()
         cp = onf4.decode_scales(ow.code8, ow.s2, ow.mean)
         Wd = onf4.dequant(ow.codes, cp, ow.levels)
