@@ -15,7 +15,11 @@ qlora_linear_bwd (the step time and `value`). At large token counts they run
 region issues the same kernels as the exported building-block calls, each
 bracketed by HIP events on the launch stream, for the per-piece breakdown and
 the dominant kernel's roofline. Inputs are resident in HBM when the timed
-regions start; the weight is encoded once before them.
+regions start; the weight is encoded once before them. Also reported: the
+10th/50th/90th percentile step (one event per step boundary), the forward and
+backward passes each timed as a region of their own, and what this box
+sustains (a matrix-core loop without memory traffic, a 1 GiB streaming read)
+beside the published peaks.
 
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
@@ -200,6 +204,7 @@ class Workload:
         c = self.c
         self.pieces = []      # (name, flops, call): the building blocks, for the per-piece breakdown
         self.api = []         # the layer calls of one step, in order
+        self.n_fwd = 0        # how many of them (from the start) form the forward pass
         self.plans = []
         self.passes_bytes = 0  # packed-weight bytes streamed per step
         if cid in (1, 2):
@@ -209,6 +214,7 @@ class Workload:
             self.plans.append(p)
             self.pieces = p.fwd + p.bwd
             self.api = [p.api_fwd, p.api_bwd]
+            self.n_fwd = 1
             self.passes_bytes = 2 * p.packed_bytes
             self.desc = dict(workload=c.title, M=c.m[0], N=lin.n, K=lin.k, r=c.r, alpha=c.alpha, passes="fwd+bwd")
         elif cid == 3:
@@ -237,6 +243,7 @@ class Workload:
                            + ren(pg.bwd, "gate"))
             self.plans = [pg, pu, pd]
             self.api = [pg.api_fwd, pu.api_fwd, silu_f, pd.api_fwd, pd.api_bwd, silu_b, pu.api_bwd, pg.api_bwd]
+            self.n_fwd = 4
             self.passes_bytes = 2 * sum(p.packed_bytes for p in self.plans)
             self.desc = dict(workload=c.title, M=M, r=c.r, alpha=c.alpha, passes="fwd+bwd, chained through SiLU")
         elif cid == 4:
@@ -248,6 +255,7 @@ class Workload:
                     self.api.append(p.api_fwd)
                     self.pieces += [(f"{lin.name}.M{M}.{nme}", f, cl) for nme, f, cl in p.fwd]
                     self.passes_bytes += p.packed_bytes
+            self.n_fwd = len(self.api)
             self.desc = dict(workload=c.title, M=list(c.m), r=c.r, alpha=c.alpha, passes="fwd")
         self.flops = sum(f for _, f, _ in self.pieces)
 
@@ -304,6 +312,63 @@ def time_steps(wl: Workload, steps: int, warmup: int):
     per_ms = per / steps
     pieces_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]))
     return wall * 1e3, ev_step, per_ms, pieces_step
+
+
+def region_ms(calls, steps: int) -> float:
+    """Mean time of `calls` issued back to back `steps` times, one event pair
+    around the whole region."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        for cl in calls:
+            cl()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def step_distribution(wl: Workload, steps: int):
+    """Per-step times of the layer calls with one event at each step boundary
+    (the only addition to region A), and the forward and backward passes each
+    timed as a region of their own (a backward reuses the forward's saved T,
+    which stays valid). Returns (p10, p50, p90 in us, fwd us, bwd us or None)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for s_ in range(steps):
+        for cl in wl.api:
+            cl()
+        evs[s_ + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]) * 1e3
+    p10, p50, p90 = (float(np.percentile(per, q_)) for q_ in (10, 50, 90))
+    fwd = region_ms(wl.api[:wl.n_fwd], steps) * 1e3
+    bwd = region_ms(wl.api[wl.n_fwd:], steps) * 1e3 if wl.n_fwd < len(wl.api) else None
+    return p10, p50, p90, fwd, bwd
+
+
+def attainable(q):
+    """What this machine sustains: a matrix-core loop with no memory traffic
+    (bf16 MFMA TFLOP/s) and one streaming read of a 1 GiB buffer (GB/s)."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    out = {}
+    for nme, fn in (("mfma_bf16_tflops", lambda: q.calib_mfma(cus, 2048, sink)),
+                    ("hbm_read_gbps", lambda: q.calib_stream_read(buf, sink))):
+        work = fn()  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 5 * 1e-3
+        out[nme] = round(work / t / (1e12 if nme.startswith("mfma") else 1e9), 1)
+    del buf
+    return out
 
 
 def gemm_traffic(kernel_name: str):
@@ -395,6 +460,8 @@ def main():
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
     ms_wall, ms_ev, per_ms, ms_pieces = time_steps(wl, args.steps, args.warmup)
+    p10, p50, p90, fwd_us, bwd_us = step_distribution(wl, args.steps)
+    att = attainable(q)
     names = [nme for nme, _, _ in wl.pieces]
     flops = [f for _, f, _ in wl.pieces]
     value = wl.flops / (ms_wall * 1e-3) / 1e12
@@ -411,11 +478,13 @@ def main():
         pl = [p for p in wl.plans if any(c is wl.pieces[i][2] for _, _, c in p.fwd)][0]
         achieved = pl.packed_bytes / (dom_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBPS, 4))
+                    frac=round(achieved / PEAK_HBM_GBPS, 4), attainable=att["hbm_read_gbps"],
+                    frac_of_attainable=round(achieved / att["hbm_read_gbps"], 4))
     else:
         achieved = flops[i] / (dom_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), attainable=att["mfma_bf16_tflops"],
+                    frac_of_attainable=round(achieved / att["mfma_bf16_tflops"], 4))
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
     roof["traffic"] = gemm_traffic(f"{wl.tag}.{base}")
@@ -437,6 +506,10 @@ def main():
         "packed_weight_GBps": round(gbps, 1),
         "ms_per_step_events": round(ms_ev, 4),
         "ms_per_step_evented_pieces": round(ms_pieces, 4),
+        "step_us_p10_p50_p90": [round(p10, 1), round(p50, 1), round(p90, 1)],
+        "fwd_us": round(fwd_us, 1),
+        "bwd_us": None if bwd_us is None else round(bwd_us, 1),
+        "attainable": att,
         "flops_per_step": wl.flops,
         "breakdown_us": breakdown,
         "roofline": roof,

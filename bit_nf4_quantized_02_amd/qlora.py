@@ -67,6 +67,8 @@ _SIGS = {
     "qlora_lowrank_grad": (_int, [_vp, _i64, _i64, _vp, _int, _f, _vp, _int, _int, _vp, _sz, _vp]),
     "qlora_silu_mul_fwd": (_int, [_vp, _vp, _vp, _i64, _vp]),
     "qlora_silu_mul_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "qlora_calib_mfma": (_int, [_int, _int, _vp, _vp]),
+    "qlora_calib_stream_read": (_int, [_vp, _i64, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -415,6 +417,20 @@ def silu_mul_bwd(G: torch.Tensor, U: torch.Tensor, dH: torch.Tensor, stream=None
     _check(_lib.qlora_silu_mul_bwd(_ptr(G), _ptr(U), _ptr(dH), _ptr(dG), _ptr(dU), G.numel(), _stream(stream)),
            "qlora_silu_mul_bwd")
     return dG, dU
+
+
+def calib_mfma(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> int:
+    """Enqueue the matrix-core probe; returns its flop count."""
+    _need(sink, torch.float32, sink.shape, "sink")
+    _check(_lib.qlora_calib_mfma(blocks, iters, _ptr(sink), _stream(stream)), "qlora_calib_mfma")
+    return blocks * 8 * iters * 8 * 32768
+
+
+def calib_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> int:
+    """Enqueue one streaming read of `buf`; returns the bytes read."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.qlora_calib_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "qlora_calib_stream_read")
+    return nbytes
 
 
 def raw():

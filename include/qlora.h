@@ -329,6 +329,24 @@ qlora_status qlora_silu_mul_fwd(const void *G, const void *Up, void *H, int64_t 
 qlora_status qlora_silu_mul_bwd(const void *G, const void *Up, const void *dH, void *dG, void *dUp,
                                 int64_t count, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (not part of the layer): attainable peaks on the box at
+ * hand, reported beside the published ones.
+ *
+ * qlora_calib_mfma: `blocks` workgroups of 8 waves; each wave runs `iters`
+ * rounds of 8 independent v_mfma_f32_32x32x16_bf16 with no memory traffic.
+ * Work = blocks * 8 * iters * 8 * 32768 flops. `sink` (device, 1 fp32) is
+ * written only in a case that never occurs (it keeps the work alive).
+ * Errors: INVALID_ARG (blocks or iters < 1, sink NULL), HIP.
+ *
+ * qlora_calib_stream_read: reads `bytes` (multiple of 16) of `buf` (device,
+ * 16-byte aligned) once with 16-byte loads, grid-stride, four loads in flight
+ * per thread; `sink` as above. Errors: INVALID_ARG, SHAPE (alignment or size),
+ * HIP.
+ * ------------------------------------------------------------------------- */
+qlora_status qlora_calib_mfma(int blocks, int iters, float *sink, void *stream);
+qlora_status qlora_calib_stream_read(const void *buf, int64_t bytes, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -174,3 +174,14 @@ def test_expanded_path_needs_operands_under_4gib(q):
     assert q.linear_path(huge_m, 4096, 4096, 16, False) == q.PATH_FUSED
     assert q.linear_path(huge_m, 4096, 4096, 16, True) == q.PATH_FUSED
     assert lib.qlora_bf16_gemm(p, huge_m, 4096, p, 16, p, 4096, p, None) == -2
+
+
+def test_calibration_probe_errors(q):
+    lib = q.raw()
+    p = ctypes.c_void_p(1 << 24)
+    assert lib.qlora_calib_mfma(0, 10, p, None) == -1
+    assert lib.qlora_calib_mfma(4, 0, p, None) == -1
+    assert lib.qlora_calib_mfma(4, 10, None, None) == -1
+    assert lib.qlora_calib_stream_read(p, 1000, p, None) == -2                     # not a multiple of 16
+    assert lib.qlora_calib_stream_read(ctypes.c_void_p((1 << 24) + 4), 1024, p, None) == -2  # misaligned
+    assert lib.qlora_calib_stream_read(None, 1024, p, None) == -1
