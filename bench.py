@@ -113,7 +113,8 @@ class LinearPlan:
         lib = q.raw()
         pw = max(lib.qlora_lowrank_project_workspace_bytes(M, K, r), lib.qlora_lowrank_project_workspace_bytes(M, N, r))
         gw = max(lib.qlora_lowrank_grad_workspace_bytes(M, K, r), lib.qlora_lowrank_grad_workspace_bytes(M, N, r))
-        self.ws = torch.empty(max(pw, gw, 256), dtype=torch.uint8, device=dev)
+        bw = max(lib.qlora_bf16_gemm_workspace_bytes(M, K, r, N), lib.qlora_bf16_gemm_workspace_bytes(M, N, r, K))
+        self.ws = torch.empty(max(pw, gw, bw, 256), dtype=torch.uint8, device=dev)
         st = q._stream()
         P = q._ptr
         self.wst = self.W.struct()
@@ -152,7 +153,7 @@ class LinearPlan:
                                         keep=(self.wst,))))
                 self.fwd.append(("bf16_gemm_fwd", 2 * M * N * K + 2 * M * N * r,
                                  q.Call("qlora_bf16_gemm", P(self.X), M, K, P(self.TS), r, P(self.Fw), N, P(self.Y),
-                                        st)))
+                                        ws, wsn, st)))
         if backward:
             self.bwd.append(("lowrank_project_U", 2 * M * N * r,
                              q.Call("qlora_lowrank_project", P(self.dY), M, N, P(self.B), 1, r, self.s, P(self.U),
@@ -167,7 +168,7 @@ class LinearPlan:
                                         keep=(self.wst,))))
                 self.bwd.append(("bf16_gemm_dx", 2 * M * N * K + 2 * M * K * r,
                                  q.Call("qlora_bf16_gemm", P(self.dY), M, N, P(self.US), r, P(self.Fx), K, P(self.dX),
-                                        st)))
+                                        ws, wsn, st)))
             self.bwd.append(("lowrank_grad_dA", 2 * M * K * r,
                              q.Call("qlora_lowrank_grad", P(self.X), M, K, P(self.U), r, self.s, P(self.dA), 0, 0, ws,
                                     wsn, st)))

@@ -80,6 +80,7 @@ struct FwdWs {
   uint16_t* TS = nullptr;
   void* proj = nullptr;
   uint16_t* F = nullptr;  // expanded operand (large M)
+  float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
 };
 
 size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o) {
@@ -92,7 +93,11 @@ size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& c
     }
     o.proj = cv.take<char>(project_ws(M, k, r));
   }
-  if (path == QLORA_PATH_EXPANDED) o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, false));
+  if (path == QLORA_PATH_EXPANDED) {
+    o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, false));
+    const size_t pb = gemm_bf16_ws_bytes(M, k, lora_extra_cols(r), n);
+    if (pb > 0) o.part = cv.take<float>(pb);
+  }
   return cv.used;
 }
 
@@ -103,6 +108,7 @@ struct BwdWs {
   void* proj = nullptr;
   void* grad = nullptr;
   uint16_t* F = nullptr;  // expanded transposed operand (large M)
+  float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
 };
 
 size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o) {
@@ -115,7 +121,11 @@ size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& 
     const size_t g1 = grad_ws(M, k, r), g2 = grad_ws(M, n, r);
     o.grad = cv.take<char>(g1 > g2 ? g1 : g2);
   }
-  if (path_of(M, n, k, r, true) == QLORA_PATH_EXPANDED) o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, true));
+  if (path_of(M, n, k, r, true) == QLORA_PATH_EXPANDED) {
+    o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, true));
+    const size_t pb = gemm_bf16_ws_bytes(M, n, lora_extra_cols(r), k);
+    if (pb > 0) o.part = cv.take<float>(pb);
+  }
   return cv.used;
 }
 
@@ -260,16 +270,24 @@ qlora_status qlora_nf4_expand(const qlora_nf4_weight* w, const void* lr, int r, 
                                   static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
 
+size_t qlora_bf16_gemm_workspace_bytes(int64_t M, int64_t kc, int r, int64_t nout) {
+  if (M < 1 || kc < 8 || (kc % 8) != 0 || nout < 1 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  return gemm_bf16_ws_bytes(M, kc, lora_extra_cols(r), nout);
+}
+
 qlora_status qlora_bf16_gemm(const void* act, int64_t M, int64_t kc, const void* split, int r, const void* F,
-                             int64_t nout, void* out, void* stream) {
+                             int64_t nout, void* out, void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || kc < 8 || (kc % 8) != 0 || nout < 1 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
   if (M == 0) return QLORA_OK;
   if (!act || !F || !out || !aligned16(act) || !aligned16(F) || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
   if (r > 0 && (!split || !aligned16(split))) return QLORA_ERR_INVALID_ARG;
   if (!gemm_bf16_offsets_fit(M, kc, lora_extra_cols(r), nout)) return QLORA_ERR_SHAPE;
+  const size_t need = gemm_bf16_ws_bytes(M, kc, lora_extra_cols(r), nout);
+  if (need > 0 && (!ws || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   return hip_status(launch_gemm_bf16(static_cast<const uint16_t*>(act), M, kc, static_cast<const uint16_t*>(split),
                                      lora_extra_cols(r), static_cast<const uint16_t*>(F), nout,
-                                     static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+                                     static_cast<uint16_t*>(out), need > 0 ? static_cast<float*>(ws) : nullptr,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r) {
@@ -324,7 +342,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t 
       if (e == hipSuccess) e = launch_gemm_fwd(v, x, M, o.TS, b, r, y, st);
     } else {
       if (e == hipSuccess) e = launch_expand(v, b, r, false, o.F, st);
-      if (e == hipSuccess) e = launch_gemm_bf16(x, M, w->k, o.TS, lora_extra_cols(r), o.F, w->n, y, st);
+      if (e == hipSuccess) e = launch_gemm_bf16(x, M, w->k, o.TS, lora_extra_cols(r), o.F, w->n, y, o.part, st);
     }
   }
   return hip_status(e);
@@ -368,7 +386,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const fl
       e = launch_expand(v, a, r, true, o.F, st);
       if (e == hipSuccess)
         e = launch_gemm_bf16(dy, M, w->n, r > 0 ? o.US : nullptr, lora_extra_cols(r), o.F, w->k,
-                             static_cast<uint16_t*>(dX), st);
+                             static_cast<uint16_t*>(dX), o.part, st);
     } else {
       e = launch_gemm_dx(v, dy, M, r > 0 ? o.US : nullptr, a, r, static_cast<uint16_t*>(dX), st);
     }

@@ -44,6 +44,8 @@ struct BfArgs {
   const uint16_t* f;     // [nout, ldf] expanded operand, ldf = 64 * nk_main + kx
   int64_t ldf, nout;
   uint16_t* out;         // [M, nout]
+  float* part;           // split-K: [splits, M, nout] fp32 partial sums (else unused)
+  int splits;            // contraction split over workgroups (1: whole contraction)
 };
 
 constexpr int kCopies = 32 / kWaves;  // 1 KB copies per wave per operand tile
@@ -134,8 +136,9 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
                                           char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN]) {
   const int lane = threadIdx.x & 63;
   const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
-  // past the last step the copy repeats the last step into a buffer no later
-  // step reads: keeps the body free of branches
+  // past the last step (nk: end of this workgroup's range) the copy repeats
+  // the last step into a buffer no later step reads: keeps the body free of
+  // branches
   const int s1 = step + 1 < nk ? step + 1 : nk - 1;
   bf16x8 af[2][kTM], bfr[2][kTN];
   auto read_frags = [&](int kk, int buf) {
@@ -183,11 +186,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
+  const int64_t mt = cdiv(a.M, (int64_t)kBM), nt = cdiv(a.nout, (int64_t)kBN);
+  // workgroup = (split, tile); with the tile count a multiple of 8 every
+  // split keeps the XCD-aware tile order
+  const int64_t split = blockIdx.x / (mt * nt);
   int64_t tm, tn;
-  tile_of(tm, tn, cdiv(a.M, (int64_t)kBM), cdiv(a.nout, (int64_t)kBN));
+  tile_of(tm, tn, mt, nt, (int64_t)blockIdx.x % (mt * nt));
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
   const int nk_main = (int)cdiv(a.kc, (int64_t)kBK);
-  const int nk = nk_main + a.kx / kBK;
+  const int nk_all = nk_main + a.kx / kBK;
+  // this workgroup's contiguous range of 64-deep steps
+  const int chunk = (int)cdiv((int64_t)nk_all, (int64_t)a.splits);
+  const int sbeg = (int)split * chunk;
+  const int nk = sbeg + chunk < nk_all ? sbeg + chunk : nk_all;  // exclusive end
 
   CopyPlan plan;
   make_plan(a, m0, n0, nk_main, wave, plan);
@@ -204,11 +215,32 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  issue_step(rs, plan, 0, nk_main, wave, As0, Bs0);
-  step_barrier<0>();
-  for (int step = 0; step < nk; step += 2) {
-    bf16_step(rs, plan, step, nk, nk_main, wave, As0, Bs0, As1, Bs1, acc);
-    if (step + 1 < nk) bf16_step(rs, plan, step + 1, nk, nk_main, wave, As1, Bs1, As0, Bs0, acc);
+  if (sbeg < nk) {  // (every split range is non-empty for the split counts gemm_bf16_splits picks)
+    issue_step(rs, plan, sbeg, nk_main, wave, As0, Bs0);
+    step_barrier<0>();
+    for (int step = sbeg; step < nk; step += 2) {
+      bf16_step(rs, plan, step, nk, nk_main, wave, As0, Bs0, As1, Bs1, acc);
+      if (step + 1 < nk) bf16_step(rs, plan, step + 1, nk, nk_main, wave, As1, Bs1, As0, Bs0, acc);
+    }
+  }
+
+  if (a.splits > 1) {
+    // split-K: this range's fp32 sums go to the partial buffer, added in
+    // split order by gemm_bf16_reduce_kernel
+    float* const pp = a.part + split * a.M * a.nout;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        const int64_t n = n0 + wn0 + j * 32 + (lane & 31);
+        if (n >= a.nout) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t m = m0 + wm0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (m < a.M) pp[m * a.nout + n] = acc[i][j][v];
+        }
+      }
+    return;
   }
 
   // Epilogue: each wave writes its 128 x 64 bf16 block (16 KB) into its own
@@ -249,7 +281,48 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   }
 }
 
+// out = RN_bf16(part[0] + part[1] + ... + part[S-1]), added in split order
+// (deterministic; one rounding). Four elements per thread when nout % 4 == 0.
+__global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(const float* __restrict__ part, int64_t count,
+                                                               int splits, uint16_t* __restrict__ out, bool vec4) {
+#pragma clang fp contract(off)
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (vec4 ? 4 : 1);
+  if (vec4) {
+    if (i0 >= count) return;
+    float4 s = *reinterpret_cast<const float4*>(part + i0);
+    for (int p = 1; p < splits; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)p * count + i0);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    uint2 o;
+    o.x = pack_bf16x2(s.x, s.y);
+    o.y = pack_bf16x2(s.z, s.w);
+    *reinterpret_cast<uint2*>(out + i0) = o;
+  } else {
+    if (i0 >= count) return;
+    float s = part[i0];
+    for (int p = 1; p < splits; ++p) s += part[(int64_t)p * count + i0];
+    out[i0] = to_bf16_bits(s);
+  }
+}
+
 }  // namespace
+
+// Split-K when the output has at most half a wave of tiles: the largest power
+// of two S <= 8 with tiles * S <= 256 and at least 8 steps per split.
+int gemm_bf16_splits(int64_t M, int64_t kc, int kx, int64_t nout) {
+  const int64_t tiles = cdiv(M, (int64_t)kBM) * cdiv(nout, (int64_t)kBN);
+  const int64_t nk = cdiv(kc, (int64_t)kBK) + kx / kBK;
+  if (tiles > 128) return 1;
+  int s = 1;
+  while (s < 8 && tiles * s * 2 <= 256 && nk >= (int64_t)16 * s) s *= 2;
+  return s;
+}
+
+size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout) {
+  const int s = gemm_bf16_splits(M, kc, kx, nout);
+  return s > 1 ? align256((size_t)s * (size_t)M * (size_t)nout * 4) : 0;
+}
 
 bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
   const int64_t ldf = cdiv(kc, (int64_t)kBK) * kBK + kx;
@@ -258,14 +331,24 @@ bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
-                            const uint16_t* f, int64_t nout, uint16_t* out, hipStream_t stream) {
+                            const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream) {
   BfArgs a{};
   a.act = act; a.M = M; a.kc = kc;
   a.act_x = split; a.kx = kx;
   a.f = f; a.ldf = cdiv(kc, (int64_t)kBK) * kBK + kx; a.nout = nout;
   a.out = out;
-  const dim3 grid((unsigned)(cdiv(nout, (int64_t)kBN) * cdiv(M, (int64_t)kBM)));
-  gemm_bf16_kernel<<<grid, kThreads, 0, stream>>>(a);
+  a.splits = gemm_bf16_splits(M, kc, kx, nout);
+  a.part = part;
+  if (a.splits > 1 && part == nullptr) return hipErrorInvalidValue;
+  const int64_t tiles = cdiv(nout, (int64_t)kBN) * cdiv(M, (int64_t)kBM);
+  gemm_bf16_kernel<<<dim3((unsigned)(tiles * a.splits)), kThreads, 0, stream>>>(a);
+  if (a.splits > 1) {
+    const int64_t count = M * nout;
+    const bool vec4 = nout % 4 == 0;
+    const int64_t threads = vec4 ? cdiv(count, (int64_t)4) : count;
+    gemm_bf16_reduce_kernel<<<dim3((unsigned)cdiv(threads, (int64_t)256)), 256, 0, stream>>>(part, count, a.splits,
+                                                                                          out, vec4);
+  }
   return hipGetLastError();
 }
 

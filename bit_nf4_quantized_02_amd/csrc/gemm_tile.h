@@ -55,12 +55,11 @@ __device__ __forceinline__ void issue_tile_lds(const uint16_t* src, int64_t ld, 
   }
 }
 
-// Logical tile index of this workgroup: hardware dispatches workgroup i to XCD
-// i % 8, so give each XCD a contiguous range of logical tiles; within the
+// Logical tile index of workgroup `bid`: hardware dispatches workgroup i to
+// XCD i % 8, so give each XCD a contiguous range of logical tiles; within the
 // range, walk groups of 8 activation row-tiles column by column.
-__device__ __forceinline__ void tile_of(int64_t& tm, int64_t& tn, int64_t mt, int64_t nt) {
+__device__ __forceinline__ void tile_of(int64_t& tm, int64_t& tn, int64_t mt, int64_t nt, int64_t bid) {
   const int64_t total = mt * nt;
-  const int64_t bid = blockIdx.x;
   int64_t lin = bid;
   if (total % 8 == 0) lin = (bid % 8) * (total / 8) + bid / 8;
   constexpr int64_t G = 8;
@@ -70,6 +69,9 @@ __device__ __forceinline__ void tile_of(int64_t& tm, int64_t& tn, int64_t mt, in
   const int64_t in = lin % (G * nt);
   tm = first_m + in % gm;
   tn = in / gm;
+}
+__device__ __forceinline__ void tile_of(int64_t& tm, int64_t& tn, int64_t mt, int64_t nt) {
+  tile_of(tm, tn, mt, nt, (int64_t)blockIdx.x);
 }
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt

@@ -71,10 +71,15 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
 
 // out = RN_bf16([act | split] F^T) over an expanded operand F [nout, kcp + kx].
 // The kernel addresses each operand with 32-bit byte offsets: every operand
-// must be smaller than 4 GiB (gemm_bf16_offsets_fit).
+// must be smaller than 4 GiB (gemm_bf16_offsets_fit). With few output tiles
+// the contraction is split over gemm_bf16_splits() workgroups per tile whose
+// fp32 partials (gemm_bf16_ws_bytes() of workspace, `part`) are added in
+// split order and rounded once; part may be NULL when that size is 0.
 bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout);
+int gemm_bf16_splits(int64_t M, int64_t kc, int kx, int64_t nout);
+size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout);
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
-                            const uint16_t* f, int64_t nout, uint16_t* out, hipStream_t stream);
+                            const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream);
 
 // Small-M dequant-GEMV: Y = RN_bf16(X W'^T + scale * T B^T), M <= 16.
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T,

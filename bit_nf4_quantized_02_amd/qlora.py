@@ -62,7 +62,8 @@ _SIGS = {
     "qlora_linear_path": (_int, [_i64, _i64, _i64, _int, _int]),
     "qlora_nf4_expand_bytes": (_sz, [_i64, _i64, _int, _int]),
     "qlora_nf4_expand": (_int, [_W, _vp, _int, _int, _vp, _sz, _vp]),
-    "qlora_bf16_gemm": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _i64, _vp, _vp]),
+    "qlora_bf16_gemm_workspace_bytes": (_sz, [_i64, _i64, _int, _i64]),
+    "qlora_bf16_gemm": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _i64, _vp, _vp, _sz, _vp]),
     "qlora_lowrank_grad_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "qlora_lowrank_grad": (_int, [_vp, _i64, _i64, _vp, _int, _f, _vp, _int, _int, _vp, _sz, _vp]),
     "qlora_silu_mul_fwd": (_int, [_vp, _vp, _vp, _i64, _vp]),
@@ -344,13 +345,20 @@ def nf4_expand(w: NF4Weight, lr: torch.Tensor | None, r: int, transposed: bool, 
     return out.view(-1)[: rows * cols].view(rows, cols)
 
 
+def bf16_gemm_workspace_bytes(M: int, kc: int, r: int, nout: int) -> int:
+    return int(_lib.qlora_bf16_gemm_workspace_bytes(M, kc, r, nout))
+
+
 def bf16_gemm(act: torch.Tensor, split: torch.Tensor | None, r: int, F: torch.Tensor, nout: int,
-              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+              out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     M, kc = act.shape
     if out is None:
         out = torch.empty((M, nout), dtype=torch.bfloat16, device=act.device)
-    _check(_lib.qlora_bf16_gemm(_ptr(act), M, kc, _ptr(split), r, _ptr(F), nout, _ptr(out), _stream(stream)),
-           "qlora_bf16_gemm")
+    if ws is None:
+        ws = _bytes(bf16_gemm_workspace_bytes(M, kc, r, nout), act.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.qlora_bf16_gemm(_ptr(act), M, kc, _ptr(split), r, _ptr(F), nout, _ptr(out), _ptr(ws), nbytes,
+                                _stream(stream)), "qlora_bf16_gemm")
     return out
 
 

@@ -287,6 +287,9 @@ size_t qlora_nf4_expand_bytes(int64_t n, int64_t k, int r, int transposed);
 qlora_status qlora_nf4_expand(const qlora_nf4_weight *w, const void *lr, int r, int transposed, void *out,
                               size_t out_bytes, void *stream);
 
+/* Workspace bytes of qlora_bf16_gemm (0: none needed, or bad arguments). */
+size_t qlora_bf16_gemm_workspace_bytes(int64_t M, int64_t kc, int r, int64_t nout);
+
 /*
  * bf16 MFMA GEMM over an expanded operand F from qlora_nf4_expand:
  *   out[m, j] = RN_bf16( sum_{c < kc} act[m, c] F[j, c] + sum_x split[m, x] F[j, kcp + x] )
@@ -295,10 +298,15 @@ qlora_status qlora_nf4_expand(const qlora_nf4_weight *w, const void *lr, int r, 
  * bf16 rows from qlora_lowrank_project (ignored for r = 0); F (device)
  * [nout, kcp + xc]; out (device) [M, nout] bf16 (nout = n forward, k for dX).
  * Each operand (act, split, F) must be smaller than 4 GiB.
- * Errors: INVALID_ARG, SHAPE, HIP.
+ * When the output has few 256 x 256 tiles (at most 128) the contraction is
+ * split over 2-8 workgroups per tile: their fp32 partial sums go to ws
+ * (device, qlora_bf16_gemm_workspace_bytes; may be NULL when that is 0) and
+ * are added in split order, then rounded once. Results are deterministic;
+ * they can differ in the last bits from an unsplit sum.
+ * Errors: INVALID_ARG, SHAPE, WORKSPACE, HIP.
  */
 qlora_status qlora_bf16_gemm(const void *act, int64_t M, int64_t kc, const void *split, int r, const void *F,
-                             int64_t nout, void *out, void *stream);
+                             int64_t nout, void *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes of qlora_lowrank_grad (0 on bad arguments). */
 size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r);

@@ -162,9 +162,15 @@ def test_expand_and_bf16_gemm_errors(q):
     assert lib.qlora_nf4_expand(ctypes.byref(W), p, 8, 2, p, need, None) == -1
     assert lib.qlora_nf4_expand(ctypes.byref(W), None, 8, 0, p, need, None) == -1
     assert lib.qlora_nf4_expand(ctypes.byref(W), p, q.MAX_RANK + 1, 0, p, 1 << 30, None) == -2
-    assert lib.qlora_bf16_gemm(p, 64, 100, p, 8, p, 64, p, None) == -2      # kc % 8 != 0
-    assert lib.qlora_bf16_gemm(p, 64, 128, None, 8, p, 64, p, None) == -1   # r > 0 needs split
-    assert lib.qlora_bf16_gemm(p, 0, 128, None, 8, p, 64, p, None) == 0     # M = 0: no-op
+    assert lib.qlora_bf16_gemm(p, 64, 100, p, 8, p, 64, p, None, 0, None) == -2      # kc % 8 != 0
+    assert lib.qlora_bf16_gemm(p, 64, 128, None, 8, p, 64, p, None, 0, None) == -1   # r > 0 needs split
+    assert lib.qlora_bf16_gemm(p, 0, 128, None, 8, p, 64, p, None, 0, None) == 0     # M = 0: no-op
+    # few output tiles: split contraction, partial sums need workspace
+    need = q.bf16_gemm_workspace_bytes(256, 4096, 8, 256)
+    assert need >= 2 * 256 * 256 * 4
+    assert lib.qlora_bf16_gemm(p, 256, 4096, p, 8, p, 256, p, None, 0, None) == -4
+    assert lib.qlora_bf16_gemm(p, 256, 4096, p, 8, p, 256, p, p, need - 1, None) == -4
+    assert q.bf16_gemm_workspace_bytes(4096, 4096, 16, 4096) == 0   # 256 tiles: whole contraction per tile
 
 
 def test_expanded_path_needs_operands_under_4gib(q):
@@ -173,7 +179,7 @@ def test_expanded_path_needs_operands_under_4gib(q):
     huge_m = 1 << 20  # [2^20, 4096] bf16 activation = 8 GiB
     assert q.linear_path(huge_m, 4096, 4096, 16, False) == q.PATH_FUSED
     assert q.linear_path(huge_m, 4096, 4096, 16, True) == q.PATH_FUSED
-    assert lib.qlora_bf16_gemm(p, huge_m, 4096, p, 16, p, 4096, p, None) == -2
+    assert lib.qlora_bf16_gemm(p, huge_m, 4096, p, 16, p, 4096, p, None, 0, None) == -2
 
 
 def test_calibration_probe_errors(q):

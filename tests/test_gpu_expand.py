@@ -60,7 +60,10 @@ def test_expanded_operands_bitwise(q, n, k, r):
 
 
 @pytest.mark.parametrize("m,n,k,r", [(300, 200, 192, 8), (520, 264, 640, 16), (17, 72, 64, 1), (256, 512, 256, 0),
-                                     (700, 96, 512, 64)])
+                                     (700, 96, 512, 64),
+                                     # few output tiles, long contraction: split-K forward (S = 4) / dX (S = 4,
+                                     # ragged kc = 2056 with n % 64 = 8)
+                                     (300, 520, 2048, 16), (300, 2056, 576, 16)])
 def test_bf16_gemm_building_blocks(q, m, n, k, r):
     """T/U split + expansion + bf16 GEMM, forward and dX, against the oracle."""
     say(f"case: bf16 gemm M={m} N={n} K={k} r={r}")
@@ -76,6 +79,7 @@ def test_bf16_gemm_building_blocks(q, m, n, k, r):
         _, US = q.lowrank_project(dY, B, 1, s, want_out=False, want_split=True)
     Fw = q.nf4_expand(gw, B, r, transposed=False)
     Fx = q.nf4_expand(gw, A, r, transposed=True)
+    say(f"  splits: fwd ws {q.bf16_gemm_workspace_bytes(m, k, r, n)} B, dX ws {q.bf16_gemm_workspace_bytes(m, n, r, k)} B")
     Y = q.bf16_gemm(X, TS, r, Fw, n)
     dX = q.bf16_gemm(dY, US, r, Fx, k)
     torch.cuda.synchronize()
