@@ -176,6 +176,30 @@ qlora_status qlora_dequant(const qlora_nf4_weight* w, void* out, void* stream) {
   return hip_status(launch_dequant(view_of(w), static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
 
+qlora_status qlora_adapter_merge(const qlora_nf4_weight* w, const void* A, const void* B, int r, float scale,
+                                 void* out, int out_dtype, void* stream) {
+  const qlora_status s = check_weight(w);
+  if (s != QLORA_OK) return s;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (out_dtype != QLORA_DT_BF16 && out_dtype != QLORA_DT_FP32) return QLORA_ERR_INVALID_ARG;
+  if (out == nullptr || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
+  const Nf4View v = view_of(w);
+  return hip_status(launch_merge(&v, nullptr, w->n, w->k, static_cast<const uint16_t*>(A),
+                                 static_cast<const uint16_t*>(B), r, scale, out_dtype == QLORA_DT_FP32, out,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_adapter_unmerge(const void* merged, int64_t n, int64_t k, const void* A, const void* B, int r,
+                                   float scale, void* out, void* stream) {
+  if (n < 1 || k < QLORA_BLOCK || k % QLORA_BLOCK || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (!merged || !out || !aligned16(merged) || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
+  return hip_status(launch_merge(nullptr, static_cast<const uint16_t*>(merged), n, k, static_cast<const uint16_t*>(A),
+                                 static_cast<const uint16_t*>(B), r, scale, false, out,
+                                 static_cast<hipStream_t>(stream)));
+}
+
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
   if (M < 0 || n < 1 || k < 1 || k % QLORA_BLOCK || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (M == 0) return 0;

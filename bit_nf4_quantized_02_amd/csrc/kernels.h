@@ -81,6 +81,12 @@ size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout);
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                             const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream);
 
+// Adapter merge: out = round(W' + scale * B A) (w != NULL; bf16, or fp32 if
+// out_f32) or unmerge: out = RN_bf16(Wm - scale * B A) (w == NULL, Wm bf16).
+size_t merge_smem_bytes(int r);
+hipError_t launch_merge(const Nf4View* w, const uint16_t* Wm, int64_t n, int64_t k, const uint16_t* A,
+                        const uint16_t* B, int r, float scale, bool out_f32, void* out, hipStream_t stream);
+
 // Small-M dequant-GEMV: Y = RN_bf16(X W'^T + scale * T B^T), M <= 16.
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T,
                        const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t stream);

@@ -31,22 +31,6 @@ namespace {
 
 constexpr int kMaxRankPad = 128;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-// Operand of v_mfma_f32_16x16x32_bf16 from a [row][col] bf16 tile: lane gets
-// column c0 + lane % 16, rows 8 (lane / 16) .. +7. Inside each 16-lane group
-// lane i addresses row base + i / 4, columns 4 (i % 4) .. +3 and receives its
-// own column of the 4 rows.
-__device__ __forceinline__ bf16x8 tr_rows8(const char* tile, int pitch, int c0, int lane) {
-  const int i = lane & 15;
-  const char* p = tile + (8 * (lane >> 4) + (i >> 2)) * pitch + (c0 + 4 * (i & 3)) * 2;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 4 * pitch));
-  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // 8 bf16 starting at p (element index e0 of a row with `lim` valid elements):
 // one 16-byte load when the row is 16-byte aligned (kVec), else 8 guarded loads.
 template <bool kVec>

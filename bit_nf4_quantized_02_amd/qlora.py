@@ -68,6 +68,8 @@ _SIGS = {
     "qlora_lowrank_grad": (_int, [_vp, _i64, _i64, _vp, _int, _f, _vp, _int, _int, _vp, _sz, _vp]),
     "qlora_silu_mul_fwd": (_int, [_vp, _vp, _vp, _i64, _vp]),
     "qlora_silu_mul_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "qlora_adapter_merge": (_int, [_W, _vp, _vp, _int, _f, _vp, _int, _vp]),
+    "qlora_adapter_unmerge": (_int, [_vp, _i64, _i64, _vp, _vp, _int, _f, _vp, _vp]),
     "qlora_calib_mfma": (_int, [_int, _int, _vp, _vp]),
     "qlora_calib_stream_read": (_int, [_vp, _i64, _vp, _vp]),
 }
@@ -425,6 +427,39 @@ def silu_mul_bwd(G: torch.Tensor, U: torch.Tensor, dH: torch.Tensor, stream=None
     _check(_lib.qlora_silu_mul_bwd(_ptr(G), _ptr(U), _ptr(dH), _ptr(dG), _ptr(dU), G.numel(), _stream(stream)),
            "qlora_silu_mul_bwd")
     return dG, dU
+
+
+def adapter_merge(w: NF4Weight, A: torch.Tensor | None, B: torch.Tensor | None, scale: float,
+                  out_dtype=torch.bfloat16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """round(W' + scale * B A) as a [n, k] bf16 or fp32 tensor."""
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _need(A, torch.bfloat16, (r, w.k), "A")
+        _need(B, torch.bfloat16, (w.n, r), "B")
+    dt = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
+    if out is None:
+        out = torch.empty((w.n, w.k), dtype=out_dtype, device=w.codes.device)
+    _need(out, out_dtype, (w.n, w.k), "out")
+    st = w.struct()
+    _check(_lib.qlora_adapter_merge(ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(out), dt,
+                                    _stream(stream)), "qlora_adapter_merge")
+    return out
+
+
+def adapter_unmerge(merged: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, scale: float,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """RN_bf16(merged - scale * B A); out may be `merged` itself."""
+    n, k = merged.shape
+    r = 0 if A is None else A.shape[0]
+    _need(merged, torch.bfloat16, (n, k), "merged")
+    if r:
+        _need(A, torch.bfloat16, (r, k), "A")
+        _need(B, torch.bfloat16, (n, r), "B")
+    if out is None:
+        out = torch.empty_like(merged)
+    _check(_lib.qlora_adapter_unmerge(_ptr(merged), n, k, _ptr(A), _ptr(B), r, float(scale), _ptr(out),
+                                      _stream(stream)), "qlora_adapter_unmerge")
+    return out
 
 
 def calib_mfma(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> int:

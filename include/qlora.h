@@ -337,6 +337,34 @@ qlora_status qlora_silu_mul_fwd(const void *G, const void *Up, void *H, int64_t 
 qlora_status qlora_silu_mul_bwd(const void *G, const void *Up, const void *dH, void *dG, void *dUp,
                                 int64_t count, void *stream);
 
+/*
+ * Adapter merge for deployment ["QLoRA: Quantized Low-Rank Adaptation"
+ * (completesystemdesign.dev), the two prices, price 2: a 4-bit base cannot
+ * absorb the trained delta, so the adapter is added onto a dequantized copy;
+ * "QLoRA vs LoRA ..." (instagit.com), converting back to full precision]:
+ *   out[i, c] = round( W'[i, c] + scale * sum_j B[i, j] A[j, c] )
+ * W' = the bf16 expansion of w (bit-identical to qlora_dequant); A (device)
+ * [r, k] bf16, B (device) [n, r] bf16 (the trained adapter), scale = alpha / r
+ * as in the forward pass; out (device) [n, k] of out_dtype: QLORA_DT_BF16
+ * (rounded once, nearest-even) or QLORA_DT_FP32. The sum over j is an fp32
+ * matrix-core sum of exact bf16 products; scale * sum and the addition are
+ * single fp32 operations. r = 0 writes W' (A, B may be NULL).
+ * Errors: INVALID_ARG, SHAPE, HIP.
+ */
+qlora_status qlora_adapter_merge(const qlora_nf4_weight *w, const void *A, const void *B, int r, float scale,
+                                 void *out, int out_dtype, void *stream);
+
+/*
+ * Inverse of the bf16 merge (swap adapters on a merged copy):
+ *   out[i, c] = RN_bf16( merged[i, c] - scale * sum_j B[i, j] A[j, c] )
+ * merged, out (device) [n, k] bf16, k % 64 == 0; out may equal merged (each
+ * tile is read whole before it is written). The result equals W' only where
+ * that rounding lands back on it: the merged copy was itself rounded.
+ * Errors: INVALID_ARG, SHAPE, HIP.
+ */
+qlora_status qlora_adapter_unmerge(const void *merged, int64_t n, int64_t k, const void *A, const void *B, int r,
+                                   float scale, void *out, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Measurement helpers (not part of the layer): attainable peaks on the box at
  * hand, reported beside the published ones.

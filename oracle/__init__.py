@@ -14,10 +14,12 @@ Modules
                    the block constants, dequantization to bf16.
 ``oracle.linear``  fp64 forward and backward of the frozen-base linear with the
                    LoRA branch.
+``oracle.merge``   the adapter folded into a dequantized copy of the base (and
+                   taken out again), exact in fp64, rounded once.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against facts that do
 not come from this code (values the pages print, closed forms, brute force,
 library routines for special cases). No function here is "parity unpinned".
 """
 
-from . import nf4, linear  # noqa: F401
+from . import nf4, linear, merge  # noqa: F401
