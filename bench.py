@@ -19,7 +19,8 @@ regions start; the weight is encoded once before them. Also reported: the
 10th/50th/90th percentile step (one event per step boundary), the forward and
 backward passes each timed as a region of their own, and what this box
 sustains (a matrix-core loop without memory traffic, a 1 GiB streaming read)
-beside the published peaks.
+beside the published peaks, and the adapter merge (round(W' + s B A) into a
+bf16 copy) of each weight, timed alone against the HBM roofline.
 
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
@@ -349,6 +350,32 @@ def step_distribution(wl: Workload, steps: int):
     return p10, p50, p90, fwd, bwd
 
 
+def merge_rows(wl: Workload, q, reps: int = 20):
+    """The adapter merge (fold s B A into a dequantized bf16 copy) of every
+    weight of the workload, timed alone: one event pair around `reps`
+    launches per weight. Bytes per launch: the packed weight (0.5159 B per
+    weight) read once, the bf16 copy (2 B per weight) written once."""
+    rows = {}
+    for p in wl.plans:
+        if p.r == 0:
+            continue
+        out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device="cuda")
+        fn = lambda p=p, out=out: q.adapter_merge(p.W, p.A, p.B, p.s, out=out)  # noqa: E731
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        nbytes = p.packed_bytes + 2 * p.n * p.k
+        rows[f"{p.n}x{p.k}"] = dict(us=round(t * 1e6, 2), bytes=nbytes, GBps=round(nbytes / t / 1e9, 1))
+        del out
+    return rows
+
+
 def attainable(q):
     """What this machine sustains: a matrix-core loop with no memory traffic
     (bf16 MFMA TFLOP/s) and one streaming read of a 1 GiB buffer (GB/s)."""
@@ -463,6 +490,10 @@ def main():
     ms_wall, ms_ev, per_ms, ms_pieces = time_steps(wl, args.steps, args.warmup)
     p10, p50, p90, fwd_us, bwd_us = step_distribution(wl, args.steps)
     att = attainable(q)
+    merges = merge_rows(wl, q) if args.config in (1, 2, 3) else {}
+    for row in merges.values():
+        row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
+        row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
     names = [nme for nme, _, _ in wl.pieces]
     flops = [f for _, f, _ in wl.pieces]
     value = wl.flops / (ms_wall * 1e-3) / 1e12
@@ -511,6 +542,7 @@ def main():
         "fwd_us": round(fwd_us, 1),
         "bwd_us": None if bwd_us is None else round(bwd_us, 1),
         "attainable": att,
+        "adapter_merge_bf16": merges,
         "flops_per_step": wl.flops,
         "breakdown_us": breakdown,
         "roofline": roof,
