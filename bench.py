@@ -360,7 +360,8 @@ def merge_rows(wl: Workload, q, reps: int = 20):
         if p.r == 0:
             continue
         out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device="cuda")
-        fn = lambda p=p, out=out: q.adapter_merge(p.W, p.A, p.B, p.s, out=out)  # noqa: E731
+        fn = q.Call("qlora_adapter_merge", q.ctypes.byref(p.wst), q._ptr(p.A), q._ptr(p.B), p.r, p.s, q._ptr(out), 0,
+                    q._stream(), keep=(p.wst,))
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
