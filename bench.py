@@ -19,8 +19,10 @@ regions start; the weight is encoded once before them. Also reported: the
 10th/50th/90th percentile step (one event per step boundary), the forward and
 backward passes each timed as a region of their own, and what this box
 sustains (a matrix-core loop without memory traffic, a 1 GiB streaming read)
-beside the published peaks, and the adapter merge (round(W' + s B A) into a
-bf16 copy) of each weight, timed alone against the HBM roofline.
+beside the published peaks, the adapter merge (round(W' + s B A) into a bf16
+copy) of each weight, timed alone against the HBM roofline, and the same step
+with a bf16 base (the step's calls minus the two weight expansions, over the
+operands they leave in place) with QLoRA's slowdown over it.
 
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
@@ -350,6 +352,24 @@ def step_distribution(wl: Workload, steps: int):
     return p10, p50, p90, fwd, bwd
 
 
+def lora_bf16_base(wl: Workload, q, steps: int):
+    """The same step with a bf16 base: every call of the step except the two
+    weight expansions, over the operands they leave in place (the forward
+    [W | B B] and the transposed [W^T ; A A] a bf16-base layer would hold),
+    timed as one region like the step itself, and the same calls with the
+    expansions (QLoRA issued the same way) for the slowdown. Only for the
+    expanded path, where expansion and multiply are separate kernels. Returns
+    (ms per bf16-base step, ms per QLoRA step) or None."""
+    if any(p.path_fwd != q.PATH_EXPANDED or (p.bwd and p.path_bwd != q.PATH_EXPANDED) for p in wl.plans):
+        return None
+    lora = [cl for nme, _, cl in wl.pieces if "expand" not in nme]
+    full = [cl for _, _, cl in wl.pieces]
+    for cl in full:
+        cl()
+    # the same building-block calls with the expansions, as a region of its own
+    return region_ms(lora, steps), region_ms(full, steps)
+
+
 def merge_rows(wl: Workload, q, reps: int = 20):
     """The adapter merge (fold s B A into a dequantized bf16 copy) of every
     weight of the workload, timed alone: one event pair around `reps`
@@ -492,6 +512,7 @@ def main():
     p10, p50, p90, fwd_us, bwd_us = step_distribution(wl, args.steps)
     att = attainable(q)
     merges = merge_rows(wl, q) if args.config in (1, 2, 3) else {}
+    lora_ms = lora_bf16_base(wl, q, args.steps)
     for row in merges.values():
         row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
         row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
@@ -544,6 +565,11 @@ def main():
         "bwd_us": None if bwd_us is None else round(bwd_us, 1),
         "attainable": att,
         "adapter_merge_bf16": merges,
+        "lora_bf16_base": None if lora_ms is None else {
+            "ms_per_step": round(lora_ms[0], 4),
+            "tflops": round(wl.flops / (lora_ms[0] * 1e-3) / 1e12, 2),
+            "qlora_same_calls_ms_per_step": round(lora_ms[1], 4),
+            "qlora_slowdown": round(lora_ms[1] / lora_ms[0], 3)},
         "flops_per_step": wl.flops,
         "breakdown_us": breakdown,
         "roofline": roof,
