@@ -70,6 +70,7 @@ _SIGS = {
     "qlora_silu_mul_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp]),
     "qlora_adapter_merge": (_int, [_W, _vp, _vp, _int, _f, _vp, _int, _vp]),
     "qlora_adapter_unmerge": (_int, [_vp, _i64, _i64, _vp, _vp, _int, _f, _vp, _vp]),
+    "qlora_adamw_step": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _f, _f, _f, _f, _f, _vp]),
     "qlora_calib_mfma": (_int, [_int, _int, _vp, _vp]),
     "qlora_calib_stream_read": (_int, [_vp, _i64, _vp, _vp]),
 }
@@ -460,6 +461,24 @@ def adapter_unmerge(merged: torch.Tensor, A: torch.Tensor | None, B: torch.Tenso
     _check(_lib.qlora_adapter_unmerge(_ptr(merged), n, k, _ptr(A), _ptr(B), r, float(scale), _ptr(out),
                                       _stream(stream)), "qlora_adapter_unmerge")
     return out
+
+
+def adamw_step(theta: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, step: int, lr: float,
+               betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.0,
+               theta16: torch.Tensor | None = None, stream=None) -> None:
+    """In-place AdamW step; m and v may be CPU tensors in pinned memory."""
+    n = theta.numel()
+    for t, nme in ((theta, "theta"), (grad, "grad")):
+        _need(t, torch.float32, theta.shape, nme)
+    for t, nme in ((m, "m"), (v, "v")):
+        if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{nme}: expected contiguous fp32 with {n} elements on the GPU or in pinned host memory")
+    if theta16 is not None:
+        _need(theta16, torch.bfloat16, theta.shape, "theta16")
+    _check(_lib.qlora_adamw_step(_ptr(theta), _ptr(theta16), _ptr(grad), ctypes.c_void_p(m.data_ptr()),
+                                 ctypes.c_void_p(v.data_ptr()), n, int(step), float(lr), float(betas[0]),
+                                 float(betas[1]), float(eps), float(weight_decay), _stream(stream)),
+           "qlora_adamw_step")
 
 
 def calib_mfma(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> int:

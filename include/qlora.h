@@ -365,6 +365,29 @@ qlora_status qlora_adapter_merge(const qlora_nf4_weight *w, const void *A, const
 qlora_status qlora_adapter_unmerge(const void *merged, int64_t n, int64_t k, const void *A, const void *B, int r,
                                    float scale, void *out, void *stream);
 
+/*
+ * One AdamW step over the adapter's parameters ["QLoRA Explained ..."
+ * (gamut.so), "Paged Optimizers" and the quick reference: the 32-bit paged
+ * AdamW; "QLoRA: Quantized Low-Rank Adaptation" (completesystemdesign.dev),
+ * paged optimizers: states in pinned CPU RAM]. Per element, fp32, each
+ * operation rounded separately:
+ *   m <- b1 m + (1 - b1) g,   v <- b2 v + (1 - b2) g g,
+ *   theta <- theta - lr ( (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps) + wd theta )
+ * (1 - b1, 1 - b2 and the bias corrections are formed in fp64 on the host and
+ * rounded once). theta (device, fp32 master copy), grad (device, fp32, e.g.
+ * dA or dB), m and v (fp32 states: device memory, or host memory pinned with
+ * hipHostMalloc, updated in place through its device mapping) hold `count`
+ * elements; theta16 (device, nullable) receives RN_bf16(theta), the adapter
+ * copy the layer calls read. step t >= 1 (bias correction); lr is the
+ * learning rate of this step (the schedule is the caller's).
+ * All pointers 16-byte aligned. Errors: INVALID_ARG (NULL, misaligned,
+ * hyperparameters out of range, states in pageable host memory), SHAPE
+ * (count < 0, step < 1), HIP.
+ */
+qlora_status qlora_adamw_step(float *theta, uint16_t *theta16, const float *grad, float *m, float *v, int64_t count,
+                              int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                              void *stream);
+
 /* ---------------------------------------------------------------------------
  * Measurement helpers (not part of the layer): attainable peaks on the box at
  * hand, reported beside the published ones.

@@ -16,10 +16,11 @@ Modules
                    LoRA branch.
 ``oracle.merge``   the adapter folded into a dequantized copy of the base (and
                    taken out again), exact in fp64, rounded once.
+``oracle.adamw``   the AdamW step on the adapter and its learning-rate schedule.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against facts that do
 not come from this code (values the pages print, closed forms, brute force,
 library routines for special cases). No function here is "parity unpinned".
 """
 
-from . import nf4, linear, merge  # noqa: F401
+from . import nf4, linear, merge, adamw  # noqa: F401

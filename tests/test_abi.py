@@ -191,3 +191,16 @@ def test_calibration_probe_errors(q):
     assert lib.qlora_calib_stream_read(p, 1000, p, None) == -2                     # not a multiple of 16
     assert lib.qlora_calib_stream_read(ctypes.c_void_p((1 << 24) + 4), 1024, p, None) == -2  # misaligned
     assert lib.qlora_calib_stream_read(None, 1024, p, None) == -1
+
+
+def test_adamw_host_errors(q):
+    lib = q.raw()
+    p = ctypes.c_void_p(1 << 24)
+    f = ctypes.c_float
+    assert lib.qlora_adamw_step(p, None, p, p, p, 0, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 0      # empty
+    assert lib.qlora_adamw_step(p, None, p, p, p, 16, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == -2    # step < 1
+    assert lib.qlora_adamw_step(p, None, None, p, p, 16, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == -1
+    assert lib.qlora_adamw_step(p, None, p, p, p, 16, 1, 1e-3, 1.0, 0.999, 1e-8, 0.0, None) == -1    # beta1 = 1
+    assert lib.qlora_adamw_step(ctypes.c_void_p((1 << 24) + 4), None, p, p, p, 16, 1, 1e-3, 0.9, 0.999, 1e-8,
+                                0.0, None) == -1                                                      # misaligned
+    del f
