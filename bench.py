@@ -22,7 +22,9 @@ sustains (a matrix-core loop without memory traffic, a 1 GiB streaming read)
 beside the published peaks, the adapter merge (round(W' + s B A) into a bf16
 copy) of each weight, timed alone against the HBM roofline, and the same step
 with a bf16 base (the step's calls minus the two weight expansions, over the
-operands they leave in place) with QLoRA's slowdown over it.
+operands they leave in place) with QLoRA's slowdown over it, and the AdamW
+step over all adapter parameters with the moments in device memory and in
+pinned host memory ("paged").
 
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
@@ -397,6 +399,44 @@ def merge_rows(wl: Workload, q, reps: int = 20):
     return rows
 
 
+def adamw_rows(wl: Workload, q, reps: int = 20):
+    """The AdamW step over every adapter parameter of the workload (A and B
+    of each linear, fp32 masters, the step's dA / dB as gradients, bf16 copy
+    written), with the moments in device memory and in pinned host memory,
+    each timed alone. Bytes per parameter: gradient 4, master 4 + 4, moments
+    2 x (4 + 4), bf16 copy 2 = 30."""
+    plans = [p for p in wl.plans if p.r and p.bwd]
+    if not plans:
+        return {}
+    n = sum(p.dA.numel() + p.dB.numel() for p in plans)
+    grad = torch.cat([torch.cat([p.dA.reshape(-1), p.dB.reshape(-1)]) for p in plans])
+    theta = torch.cat([torch.cat([p.A.float().reshape(-1), p.B.float().reshape(-1)]) for p in plans])
+    t16 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    rows = {}
+    for where in ("device", "pinned_host"):
+        if where == "device":
+            m = torch.zeros(n, dtype=torch.float32, device="cuda")
+            v = torch.zeros(n, dtype=torch.float32, device="cuda")
+        else:
+            m = torch.zeros(n, dtype=torch.float32).pin_memory()
+            v = torch.zeros(n, dtype=torch.float32).pin_memory()
+        th = theta.clone()
+        fn = q.Call("qlora_adamw_step", q._ptr(th), q._ptr(t16), q._ptr(grad), q.ctypes.c_void_p(m.data_ptr()),
+                    q.ctypes.c_void_p(v.data_ptr()), n, 1, 2e-4, 0.9, 0.999, 1e-8, 0.0, q._stream())
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        rows[where] = dict(params=n, us=round(t * 1e6, 2), GBps=round(30 * n / t / 1e9, 1))
+    rows["device"]["frac"] = round(rows["device"]["GBps"] / PEAK_HBM_GBPS, 4)
+    return rows
+
+
 def attainable(q):
     """What this machine sustains: a matrix-core loop with no memory traffic
     (bf16 MFMA TFLOP/s) and one streaming read of a 1 GiB buffer (GB/s)."""
@@ -513,6 +553,7 @@ def main():
     att = attainable(q)
     merges = merge_rows(wl, q) if args.config in (1, 2, 3) else {}
     lora_ms = lora_bf16_base(wl, q, args.steps)
+    adamw = adamw_rows(wl, q)
     for row in merges.values():
         row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
         row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
@@ -565,6 +606,7 @@ def main():
         "bwd_us": None if bwd_us is None else round(bwd_us, 1),
         "attainable": att,
         "adapter_merge_bf16": merges,
+        "adamw_step": adamw,
         "lora_bf16_base": None if lora_ms is None else {
             "ms_per_step": round(lora_ms[0], 4),
             "tflops": round(wl.flops / (lora_ms[0] * 1e-3) / 1e12, 2),
