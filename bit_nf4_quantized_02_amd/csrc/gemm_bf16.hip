@@ -44,8 +44,13 @@ struct BfArgs {
   const uint16_t* f;     // [nout, ldf] expanded operand, ldf = 64 * nk_main + kx
   int64_t ldf, nout;
   uint16_t* out;         // [M, nout]
-  float* part;           // split-K: [splits, M, nout] fp32 partial sums (else unused)
-  int splits;            // contraction split over workgroups (1: whole contraction)
+  // Workgroups [0, full) compute whole tiles (tiles 0 .. full-1 in tile_of
+  // order); the `tail` tiles after them are each split over `splits`
+  // workgroups along the contraction, whose fp32 sums go to `part`
+  // ([splits][tail][256 x 256], tile-local row-major).
+  float* part;
+  int64_t full, tail;
+  int splits;
 };
 
 constexpr int kCopies = 32 / kWaves;  // 1 KB copies per wave per operand tile
@@ -187,17 +192,24 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
   const int64_t mt = cdiv(a.M, (int64_t)kBM), nt = cdiv(a.nout, (int64_t)kBN);
-  // workgroup = (split, tile); with the tile count a multiple of 8 every
-  // split keeps the XCD-aware tile order
-  const int64_t split = blockIdx.x / (mt * nt);
+  // workgroup -> whole tile, or (split, tail tile): split units come after
+  // every whole tile, split 0 of all tail tiles first
+  // (integer division leaves its result in vector registers: the values the
+  // step loop and the copy offsets depend on are made wave-uniform again, so
+  // descriptors and step offsets stay scalar)
+  const int b = (int)blockIdx.x;
+  const bool whole = b < a.full;
+  const int unit = whole ? 0 : b - (int)a.full;
+  const int tail_i = whole ? 0 : __builtin_amdgcn_readfirstlane(unit % (int)a.tail);
+  const int split = whole ? 0 : __builtin_amdgcn_readfirstlane(unit / (int)a.tail);
   int64_t tm, tn;
-  tile_of(tm, tn, mt, nt, (int64_t)blockIdx.x % (mt * nt));
+  tile_of(tm, tn, mt, nt, whole ? (int64_t)b : a.full + tail_i);
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
   const int nk_main = (int)cdiv(a.kc, (int64_t)kBK);
   const int nk_all = nk_main + a.kx / kBK;
   // this workgroup's contiguous range of 64-deep steps
-  const int chunk = (int)cdiv((int64_t)nk_all, (int64_t)a.splits);
-  const int sbeg = (int)split * chunk;
+  const int chunk = whole ? nk_all : __builtin_amdgcn_readfirstlane((nk_all + a.splits - 1) / a.splits);
+  const int sbeg = split * chunk;
   const int nk = sbeg + chunk < nk_all ? sbeg + chunk : nk_all;  // exclusive end
 
   CopyPlan plan;
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  if (sbeg < nk) {  // (every split range is non-empty for the split counts gemm_bf16_splits picks)
+  if (sbeg < nk) {  // (every split range is non-empty for the split counts split_plan picks)
     issue_step(rs, plan, sbeg, nk_main, wave, As0, Bs0);
     step_barrier<0>();
     for (int step = sbeg; step < nk; step += 2) {
@@ -224,20 +236,20 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
     }
   }
 
-  if (a.splits > 1) {
-    // split-K: this range's fp32 sums go to the partial buffer, added in
-    // split order by gemm_bf16_reduce_kernel
-    float* const pp = a.part + split * a.M * a.nout;
+  if (!whole) {
+    // split unit: this range's fp32 sums go to the partial buffer (tile-local
+    // layout), added in split order by gemm_bf16_reduce_kernel
+    float* const pp = a.part + ((int64_t)split * a.tail + tail_i) * (kBM * kBN);
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
-        const int64_t n = n0 + wn0 + j * 32 + (lane & 31);
-        if (n >= a.nout) continue;
+        const int c = wn0 + j * 32 + (lane & 31);
+        if (n0 + c >= a.nout) continue;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int64_t m = m0 + wm0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (m < a.M) pp[m * a.nout + n] = acc[i][j][v];
+          const int rr = wm0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (m0 + rr < a.M) pp[rr * kBN + c] = acc[i][j][v];
         }
       }
     return;
@@ -281,47 +293,79 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   }
 }
 
-// out = RN_bf16(part[0] + part[1] + ... + part[S-1]), added in split order
-// (deterministic; one rounding). Four elements per thread when nout % 4 == 0.
-__global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(const float* __restrict__ part, int64_t count,
-                                                               int splits, uint16_t* __restrict__ out, bool vec4) {
+// Tail tiles: out = RN_bf16(part[0] + part[1] + ... + part[S-1]), added in
+// split order (deterministic; one rounding). Four adjacent outputs of one
+// tile row per thread.
+__global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(const float* __restrict__ part, int64_t full,
+                                                               int64_t tail, int splits, int64_t M, int64_t nout,
+                                                               uint16_t* __restrict__ out) {
 #pragma clang fp contract(off)
-  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (vec4 ? 4 : 1);
-  if (vec4) {
-    if (i0 >= count) return;
-    float4 s = *reinterpret_cast<const float4*>(part + i0);
-    for (int p = 1; p < splits; ++p) {
-      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)p * count + i0);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
-    uint2 o;
-    o.x = pack_bf16x2(s.x, s.y);
-    o.y = pack_bf16x2(s.z, s.w);
-    *reinterpret_cast<uint2*>(out + i0) = o;
-  } else {
-    if (i0 >= count) return;
-    float s = part[i0];
-    for (int p = 1; p < splits; ++p) s += part[(int64_t)p * count + i0];
-    out[i0] = to_bf16_bits(s);
+  constexpr int kTile = kBM * kBN;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 4
+  const int64_t ti = g / (kTile / 4);
+  if (ti >= tail) return;
+  const int loc = (int)(g % (kTile / 4)) * 4;
+  const int64_t mt = cdiv(M, (int64_t)kBM), nt = cdiv(nout, (int64_t)kBN);
+  int64_t tm, tn;
+  tile_of(tm, tn, mt, nt, full + ti);
+  const int64_t m = tm * kBM + loc / kBN, n = tn * kBN + loc % kBN;
+  if (m >= M || n >= nout) return;
+  const float* p0 = part + ti * kTile + loc;
+  float4 s = *reinterpret_cast<const float4*>(p0);
+  for (int p = 1; p < splits; ++p) {
+    const float4 v = *reinterpret_cast<const float4*>(p0 + (int64_t)p * tail * kTile);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
+  uint16_t* const o = out + m * nout + n;
+  if (n + 4 <= nout && (nout & 3) == 0) {
+    uint2 w;
+    w.x = pack_bf16x2(s.x, s.y);
+    w.y = pack_bf16x2(s.z, s.w);
+    *reinterpret_cast<uint2*>(o) = w;
+  } else {
+    const float e[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (n + i < nout) o[i] = to_bf16_bits(e[i]);
+  }
+}
+
+struct SplitPlan {
+  int64_t full, tail;
+  int splits;
+};
+
+// One 256 x 256 workgroup fits a CU at a time (128 KB of LDS), so the 256
+// CUs of an MI355X take the tiles in waves of 256. When the last wave holds
+// at most 128 tiles, those tiles are split along the contraction: the
+// largest power of two S <= 8 with tail * S <= 256 and at least 8 steps per
+// split, so the last wave takes about 1/S of a whole tile's time (with fewer
+// than 129 tiles in all, every tile is a tail tile).
+constexpr int64_t kWaveTiles = 256;
+
+SplitPlan split_plan(int64_t M, int64_t kc, int kx, int64_t nout) {
+  const int64_t tiles = cdiv(M, (int64_t)kBM) * cdiv(nout, (int64_t)kBN);
+  const int64_t nk = cdiv(kc, (int64_t)kBK) + kx / kBK;
+  const int64_t rem = tiles % kWaveTiles;
+  SplitPlan p{tiles, 0, 1};
+  if (rem == 0 || rem > kWaveTiles / 2) return p;
+  int s = 1;
+  while (s < 8 && rem * s * 2 <= kWaveTiles && nk >= (int64_t)16 * s) s *= 2;
+  if (s > 1) {
+    p.full = tiles - rem;
+    p.tail = rem;
+    p.splits = s;
+  }
+  return p;
 }
 
 }  // namespace
 
-// Split-K when the output has at most half a wave of tiles: the largest power
-// of two S <= 8 with tiles * S <= 256 and at least 8 steps per split.
-int gemm_bf16_splits(int64_t M, int64_t kc, int kx, int64_t nout) {
-  const int64_t tiles = cdiv(M, (int64_t)kBM) * cdiv(nout, (int64_t)kBN);
-  const int64_t nk = cdiv(kc, (int64_t)kBK) + kx / kBK;
-  if (tiles > 128) return 1;
-  int s = 1;
-  while (s < 8 && tiles * s * 2 <= 256 && nk >= (int64_t)16 * s) s *= 2;
-  return s;
-}
+int gemm_bf16_splits(int64_t M, int64_t kc, int kx, int64_t nout) { return split_plan(M, kc, kx, nout).splits; }
 
 size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout) {
-  const int s = gemm_bf16_splits(M, kc, kx, nout);
-  return s > 1 ? align256((size_t)s * (size_t)M * (size_t)nout * 4) : 0;
+  const SplitPlan p = split_plan(M, kc, kx, nout);
+  return p.splits > 1 ? align256((size_t)p.splits * (size_t)p.tail * kBM * kBN * 4) : 0;
 }
 
 bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
@@ -337,17 +381,15 @@ hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const ui
   a.act_x = split; a.kx = kx;
   a.f = f; a.ldf = cdiv(kc, (int64_t)kBK) * kBK + kx; a.nout = nout;
   a.out = out;
-  a.splits = gemm_bf16_splits(M, kc, kx, nout);
+  const SplitPlan sp = split_plan(M, kc, kx, nout);
+  a.full = sp.full; a.tail = sp.tail; a.splits = sp.splits;
   a.part = part;
   if (a.splits > 1 && part == nullptr) return hipErrorInvalidValue;
-  const int64_t tiles = cdiv(nout, (int64_t)kBN) * cdiv(M, (int64_t)kBM);
-  gemm_bf16_kernel<<<dim3((unsigned)(tiles * a.splits)), kThreads, 0, stream>>>(a);
+  gemm_bf16_kernel<<<dim3((unsigned)(a.full + a.tail * a.splits)), kThreads, 0, stream>>>(a);
   if (a.splits > 1) {
-    const int64_t count = M * nout;
-    const bool vec4 = nout % 4 == 0;
-    const int64_t threads = vec4 ? cdiv(count, (int64_t)4) : count;
-    gemm_bf16_reduce_kernel<<<dim3((unsigned)cdiv(threads, (int64_t)256)), 256, 0, stream>>>(part, count, a.splits,
-                                                                                          out, vec4);
+    const int64_t groups = a.tail * (kBM * kBN / 4);
+    gemm_bf16_reduce_kernel<<<dim3((unsigned)cdiv(groups, (int64_t)256)), 256, 0, stream>>>(
+        part, a.full, a.tail, a.splits, M, nout, out);
   }
   return hipGetLastError();
 }

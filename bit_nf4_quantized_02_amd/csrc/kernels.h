@@ -71,10 +71,11 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
 
 // out = RN_bf16([act | split] F^T) over an expanded operand F [nout, kcp + kx].
 // The kernel addresses each operand with 32-bit byte offsets: every operand
-// must be smaller than 4 GiB (gemm_bf16_offsets_fit). With few output tiles
-// the contraction is split over gemm_bf16_splits() workgroups per tile whose
-// fp32 partials (gemm_bf16_ws_bytes() of workspace, `part`) are added in
-// split order and rounded once; part may be NULL when that size is 0.
+// must be smaller than 4 GiB (gemm_bf16_offsets_fit). When the last wave of
+// 256 tiles holds at most 128 (all of them, for small outputs), those tiles
+// are split along the contraction over gemm_bf16_splits() workgroups each,
+// whose fp32 partials (gemm_bf16_ws_bytes() of workspace, `part`) are added
+// in split order and rounded once; part may be NULL when that size is 0.
 bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout);
 int gemm_bf16_splits(int64_t M, int64_t kc, int kx, int64_t nout);
 size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout);

@@ -298,8 +298,10 @@ size_t qlora_bf16_gemm_workspace_bytes(int64_t M, int64_t kc, int r, int64_t nou
  * bf16 rows from qlora_lowrank_project (ignored for r = 0); F (device)
  * [nout, kcp + xc]; out (device) [M, nout] bf16 (nout = n forward, k for dX).
  * Each operand (act, split, F) must be smaller than 4 GiB.
- * When the output has few 256 x 256 tiles (at most 128) the contraction is
- * split over 2-8 workgroups per tile: their fp32 partial sums go to ws
+ * The 256 x 256 output tiles run in waves of 256 (one per compute unit).
+ * When the last wave holds at most 128 tiles (all of them, for outputs of at
+ * most 128 tiles), each of those tiles has its contraction split over 2-8
+ * workgroups: their fp32 partial sums go to ws
  * (device, qlora_bf16_gemm_workspace_bytes; may be NULL when that is 0) and
  * are added in split order, then rounded once. Results are deterministic;
  * they can differ in the last bits from an unsplit sum.

@@ -63,7 +63,10 @@ def test_expanded_operands_bitwise(q, n, k, r):
                                      (700, 96, 512, 64),
                                      # few output tiles, long contraction: split-K forward (S = 4) / dX (S = 4,
                                      # ragged kc = 2056 with n % 64 = 8)
-                                     (300, 520, 2048, 16), (300, 2056, 576, 16)])
+                                     (300, 520, 2048, 16), (300, 2056, 576, 16),
+                                     # a last wave of few tiles split along the contraction: forward 272 tiles
+                                     # (16 split in 2), ragged 264 tiles (8 split in 4, n % 256 = 8, M % 256 = 208)
+                                     (4352, 4096, 2048, 16), (2000, 8200, 4160, 8)])
 def test_bf16_gemm_building_blocks(q, m, n, k, r):
     """T/U split + expansion + bf16 GEMM, forward and dX, against the oracle."""
     say(f"case: bf16 gemm M={m} N={n} K={k} r={r}")
