@@ -29,7 +29,8 @@ pinned host memory ("paged").
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
 (1: 1024^2 at M = 16; 3: 7B MLP block chained through SiLU; 4: 70B-class
-decode GEMVs). Prints one JSON line.
+decode GEMVs; 5: the 65B-class stack, 80 layers of seven linears, forward
+then backward through all of them). Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -58,9 +59,9 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 5 for config 5)")
+    p.add_argument("--warmup", type=int, default=None, help="warm-up steps (default 10; 1 for config 5)")
+    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     p.add_argument("--path", choices=["auto", "fused", "expanded"], default="auto",
                    help="large-M kernels: the library's choice (auto) or one forced, for comparison")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -69,7 +70,12 @@ def parse():
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB 3 times (the known-size kernel that "
                         "scales FETCH_SIZE / WRITE_SIZE counter readings) and exit")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.steps is None:
+        a.steps = 5 if a.config == 5 else 50
+    if a.warmup is None:
+        a.warmup = 1 if a.config == 5 else 10
+    return a
 
 
 def copy_calibration(mib: int):
@@ -92,15 +98,39 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- one linear
 
-class LinearPlan:
-    """Device tensors and prebuilt C-ABI calls of one QLoRA linear."""
+class Pool:
+    """Device buffers shared by linears that run one after another on one
+    stream: workspaces, expansions, and outputs nothing reads after the next
+    call. One buffer per (role, shape, dtype)."""
 
-    def __init__(self, q, li: synth.LinearInputs, backward: bool = True, X=None, dY=None, force_path=None):
+    def __init__(self):
+        self.bufs = {}
+
+    def __call__(self, role, shape, dtype):
+        key = (role, tuple(shape), dtype)
+        if key not in self.bufs:
+            self.bufs[key] = torch.empty(shape, dtype=dtype, device="cuda")
+        return self.bufs[key]
+
+
+def _own(role, shape, dtype):
+    return torch.empty(shape, dtype=dtype, device="cuda")
+
+
+class LinearPlan:
+    """Device tensors and prebuilt C-ABI calls of one QLoRA linear. With a
+    pool, the buffers no later call reads (workspaces, expansions, TS / U /
+    US, Y unless given, dX) come from it; T, dA, dB stay the linear's own."""
+
+    def __init__(self, q, li: synth.LinearInputs, backward: bool = True, X=None, dY=None, force_path=None,
+                 pool=None, Y=None):
         dev = "cuda"
         m = li.meta
-        self.m, self.n, self.k, self.r, self.s = m["m"], m["n"], m["k"], m["r"], li.scale
+        self.n, self.k, self.r, self.s = m["n"], m["k"], m["r"], li.scale
+        self.m = m["m"] if m["m"] is not None else X.shape[0]
         self.li = li
         M, N, K, r = self.m, self.n, self.k, self.r
+        buf = _own if pool is None else pool
         self.W = q.quantize_nf4(li.W.to(dev))
         self.X = li.X.to(dev) if X is None else X
         self.dY = li.dY.to(dev) if dY is None else dY
@@ -108,18 +138,18 @@ class LinearPlan:
         self.B = li.B.to(dev).contiguous()
         xc = q.lowrank_split_cols(r)
         self.T = torch.empty((M, r), dtype=torch.float32, device=dev)
-        self.TS = torch.empty((M, xc), dtype=torch.bfloat16, device=dev)
-        self.Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        self.U = torch.empty((M, r), dtype=torch.float32, device=dev)
-        self.US = torch.empty((M, xc), dtype=torch.bfloat16, device=dev)
-        self.dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.TS = buf("TS", (M, xc), torch.bfloat16)
+        self.Y = buf("Y", (M, N), torch.bfloat16) if Y is None else Y
+        self.U = buf("U", (M, r), torch.float32)
+        self.US = buf("US", (M, xc), torch.bfloat16)
+        self.dX = buf("dX", (M, K), torch.bfloat16)
         self.dA = torch.empty((r, K), dtype=torch.float32, device=dev)
         self.dB = torch.empty((N, r), dtype=torch.float32, device=dev)
         lib = q.raw()
         pw = max(lib.qlora_lowrank_project_workspace_bytes(M, K, r), lib.qlora_lowrank_project_workspace_bytes(M, N, r))
         gw = max(lib.qlora_lowrank_grad_workspace_bytes(M, K, r), lib.qlora_lowrank_grad_workspace_bytes(M, N, r))
         bw = max(lib.qlora_bf16_gemm_workspace_bytes(M, K, r, N), lib.qlora_bf16_gemm_workspace_bytes(M, N, r, K))
-        self.ws = torch.empty(max(pw, gw, bw, 256), dtype=torch.uint8, device=dev)
+        self.ws = buf("ws", (max(pw, gw, bw, 256),), torch.uint8)
         st = q._stream()
         P = q._ptr
         self.wst = self.W.struct()
@@ -134,9 +164,9 @@ class LinearPlan:
             self.path_fwd = force_path
             self.path_bwd = force_path if (force_path != q.PATH_EXPANDED or N % 8 == 0) else q.PATH_FUSED
         if self.path_fwd == q.PATH_EXPANDED:
-            self.Fw = torch.empty(q.nf4_expand_bytes(N, K, r, False) // 2, dtype=torch.bfloat16, device=dev)
+            self.Fw = buf("Fw", (q.nf4_expand_bytes(N, K, r, False) // 2,), torch.bfloat16)
         if backward and self.path_bwd == q.PATH_EXPANDED:
-            self.Fx = torch.empty(q.nf4_expand_bytes(N, K, r, True) // 2, dtype=torch.bfloat16, device=dev)
+            self.Fx = buf("Fx", (q.nf4_expand_bytes(N, K, r, True) // 2,), torch.bfloat16)
         if self.path_fwd == q.PATH_GEMV:
             self.fwd.append(("lowrank_project_T", 2 * M * K * r,
                              q.Call("qlora_lowrank_project", P(self.X), M, K, P(self.A), 0, r, self.s, P(self.T), None,
@@ -185,7 +215,7 @@ class LinearPlan:
         # back to back inside one C call per pass)
         fw = lib.qlora_linear_workspace_bytes(M, N, K, r, 0)
         bw = lib.qlora_linear_workspace_bytes(M, N, K, r, 1) if backward else 0
-        self.lws = torch.empty(max(fw, bw, 256), dtype=torch.uint8, device=dev)
+        self.lws = buf("lws", (max(fw, bw, 256),), torch.uint8)
         lw, lwn = P(self.lws), self.lws.numel()
         self.api_fwd = q.Call("qlora_linear_fwd", wref, P(self.X), M, P(self.A), P(self.B), r, self.s, P(self.Y),
                               P(self.T), lw, lwn, st, keep=(self.wst,))
@@ -206,7 +236,8 @@ class Workload:
     def __init__(self, cid: int, q, force_path=None):
         self.cid = cid
         self.c = synth.CONFIGS[cid]
-        self.tag = {1: "proj_1024_m16", 2: "attn_proj_4096_m4096", 3: "mlp_7b_m2048", 4: "decode_70b"}[cid]
+        self.tag = {1: "proj_1024_m16", 2: "attn_proj_4096_m4096", 3: "mlp_7b_m2048", 4: "decode_70b",
+                    5: "stack_65b_m4096"}[cid]
         c = self.c
         self.pieces = []      # (name, flops, call): the building blocks, for the per-piece breakdown
         self.api = []         # the layer calls of one step, in order
@@ -263,7 +294,73 @@ class Workload:
                     self.passes_bytes += p.packed_bytes
             self.n_fwd = len(self.api)
             self.desc = dict(workload=c.title, M=list(c.m), r=c.r, alpha=c.alpha, passes="fwd")
+        elif cid == 5:
+            self._stack(q, force_path)
         self.flops = sum(f for _, f, _ in self.pieces)
+
+    def _stack(self, q, force_path):
+        """The 65B-class stack: forward through the seven linears of every
+        layer in order (q, k, v, o; gate, up; SiLU(gate) * up; down), then the
+        backward in reverse. No attention or normalisation math: every
+        attention linear and gate / up read one synthetic X, every
+        8192-wide output gradient is one synthetic dY, and within a layer the
+        MLP is chained through SiLU (gate and up outputs and H are the
+        layer's own, as a training step keeps them for its backward). Layer 0
+        draws its weights on the host (the tensors the full-size parity test
+        uses) and owns all its buffers; the other layers draw W, A, B on the
+        device and share one pool of workspaces and transient outputs."""
+        c = self.c
+        M = c.m[0]
+        names = [lin.name for lin in c.linears]
+        gi, ui, di = names.index("gate"), names.index("up"), names.index("down")
+        width, ff = c.linears[0].k, c.linears[gi].n
+        bf = torch.bfloat16
+        X = synth.normal_bf16((M, width), 1.0, self.cid, 0, synth.T_X).cuda()
+        dY = synth.normal_bf16((M, width), 1.0, self.cid, 0, synth.T_DY).cuda()
+        pool = Pool()
+        st, P = q._stream(), q._ptr
+        ren = lambda pl, tag: [(f"{tag}.{nme}", f, cl) for nme, f, cl in pl]  # noqa: E731
+        fwd_api, fwd_pc, bwd_layers = [], [], []
+        for layer in range(c.layers):
+            G = torch.empty((M, ff), dtype=bf, device="cuda")
+            Uo = torch.empty((M, ff), dtype=bf, device="cuda")
+            H = torch.empty((M, ff), dtype=bf, device="cuda")
+            dG, dU = pool("dG", (M, ff), bf), pool("dU", (M, ff), bf)
+            per = {}
+            for li_i, lin in enumerate(c.linears):
+                if layer == 0:
+                    li = synth.linear_inputs(self.cid, 0, li_i, lin.n, lin.k, M, c.r, c.scale, sigma=c.sigma)
+                else:
+                    li = synth.device_linear_inputs(self.cid, layer, li_i, lin.n, lin.k, c.r, c.scale, sigma=c.sigma)
+                pl = LinearPlan(q, li, X=H if li_i == di else X,
+                                dY=dG if li_i == gi else dU if li_i == ui else dY,
+                                force_path=force_path, pool=None if layer == 0 else pool,
+                                Y=G if li_i == gi else Uo if li_i == ui else None)
+                if layer > 0:
+                    li.W = None  # the step reads only the encoding
+                per[lin.name] = pl
+                self.plans.append(pl)
+            pg, pu, pd = per["gate"], per["up"], per["down"]
+            attn = [per[n_] for n_ in names if n_ not in ("gate", "up", "down")]
+            silu_f = q.Call("qlora_silu_mul_fwd", P(pg.Y), P(pu.Y), P(H), M * ff, st)
+            silu_b = q.Call("qlora_silu_mul_bwd", P(pg.Y), P(pu.Y), P(pd.dX), P(dG), P(dU), M * ff, st)
+            fwd_api += [pl.api_fwd for pl in attn] + [pg.api_fwd, pu.api_fwd, silu_f, pd.api_fwd]
+            for pl in attn:
+                fwd_pc += ren(pl.fwd, names[pl.li.meta["linear"]])
+            fwd_pc += ren(pg.fwd, "gate") + ren(pu.fwd, "up") + [("silu_mul_fwd", 0, silu_f)] + ren(pd.fwd, "down")
+            bapi = [pd.api_bwd, silu_b, pu.api_bwd, pg.api_bwd] + [pl.api_bwd for pl in reversed(attn)]
+            bpc = ren(pd.bwd, "down") + [("silu_mul_bwd", 0, silu_b)] + ren(pu.bwd, "up") + ren(pg.bwd, "gate")
+            for pl in reversed(attn):
+                bpc += ren(pl.bwd, names[pl.li.meta["linear"]])
+            bwd_layers.append((bapi, bpc))
+        self.api = fwd_api + [cl for bapi, _ in reversed(bwd_layers) for cl in bapi]
+        self.pieces = fwd_pc + [pc for _, bpc in reversed(bwd_layers) for pc in bpc]
+        self.n_fwd = len(fwd_api)
+        self.passes_bytes = 2 * sum(p.packed_bytes for p in self.plans)
+        self.desc = dict(workload=c.title, M=M, layers=c.layers, r=c.r, alpha=c.alpha,
+                         packed_GB=round(sum(p.packed_bytes for p in self.plans) / 1e9, 2),
+                         passes="fwd through all 80 layers, then bwd in reverse; MLP chained through SiLU "
+                                "within a layer; one synthetic X and dY shared by the layers")
 
     def dominant_kernels(self):
         return [nme for nme, _, _ in self.pieces if "gemm" in nme or "gemv" in nme]
@@ -379,7 +476,7 @@ def merge_rows(wl: Workload, q, reps: int = 20):
     weight) read once, the bf16 copy (2 B per weight) written once."""
     rows = {}
     for p in wl.plans:
-        if p.r == 0:
+        if p.r == 0 or f"{p.n}x{p.k}" in rows:
             continue
         out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device="cuda")
         fn = q.Call("qlora_adapter_merge", q.ctypes.byref(p.wst), q._ptr(p.A), q._ptr(p.B), p.r, p.s, q._ptr(out), 0,
@@ -413,6 +510,7 @@ def adamw_rows(wl: Workload, q, reps: int = 20):
     theta = torch.cat([torch.cat([p.A.float().reshape(-1), p.B.float().reshape(-1)]) for p in plans])
     t16 = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     rows = {}
+    reps = reps if n < (1 << 27) else 5
     for where in ("device", "pinned_host"):
         if where == "device":
             m = torch.zeros(n, dtype=torch.float32, device="cuda")
@@ -551,7 +649,7 @@ def main():
     ms_wall, ms_ev, per_ms, ms_pieces = time_steps(wl, args.steps, args.warmup)
     p10, p50, p90, fwd_us, bwd_us = step_distribution(wl, args.steps)
     att = attainable(q)
-    merges = merge_rows(wl, q) if args.config in (1, 2, 3) else {}
+    merges = merge_rows(wl, q) if args.config in (1, 2, 3, 5) else {}
     lora_ms = lora_bf16_base(wl, q, args.steps)
     adamw = adamw_rows(wl, q)
     for row in merges.values():
@@ -561,12 +659,20 @@ def main():
     flops = [f for _, f, _ in wl.pieces]
     value = wl.flops / (ms_wall * 1e-3) / 1e12
     gbps = wl.passes_bytes / (ms_wall * 1e-3) / 1e9
-    breakdown = {nme: round(t * 1e3, 2) for nme, t in zip(names, per_ms)}
+    # mean per launch of each named piece (a name repeats only in the 65B
+    # stack, once per layer)
+    agg = {}
+    for nme, t in zip(names, per_ms):
+        a = agg.setdefault(nme, [0.0, 0])
+        a[0] += t
+        a[1] += 1
+    avg_ms = {nme: a[0] / a[1] for nme, a in agg.items()}
+    breakdown = {nme: round(t * 1e3, 2) for nme, t in avg_ms.items()}
 
     # dominant kernel: the slowest fused NF4 kernel
-    dom = max(wl.dominant_kernels(), key=lambda nme: per_ms[names.index(nme)])
+    dom = max(wl.dominant_kernels(), key=lambda nme: avg_ms[nme])
     i = names.index(dom)
-    dom_ms = per_ms[i]
+    dom_ms = avg_ms[dom]
     gemv = "gemv" in dom
     base = dom.split(".")[-1]
     if gemv:

@@ -14,7 +14,9 @@ Recipe (the pages name no dataset; these shapes stand in for the 7B / 65B /
   X, dY ~ N(0, 1) -> bf16;
   A  ~ U(-1/sqrt(K), +1/sqrt(K)) -> bf16 (Kaiming-uniform with a = sqrt 5);
   B  ~ N(0, 0.01) -> bf16.
-Host draws use numpy's PCG64 seeded with the tuple (config, layer, tensor).
+Host draws use numpy's PCG64 seeded with the tuple (config, layer, tensor);
+the 65B stack's layers past the first draw W, A, B on the device instead
+(torch's Philox generator, same distributions and seed tuples).
 """
 
 from __future__ import annotations
@@ -54,6 +56,31 @@ def weight_bf16(n: int, k: int, sigma: float, *seed: int, outlier_frac: float = 
         pos = g.choice(n * k, size=cnt, replace=False)
         w.reshape(-1)[pos] *= np.float32(10.0)
     return to_bf16(w)
+
+
+def device_seed(*seed: int) -> int:
+    """One 63-bit integer from the seed tuple, for torch's device generator."""
+    return int(np.random.SeedSequence(list(seed)).generate_state(1, dtype=np.uint64)[0] >> np.uint64(1))
+
+
+def device_normal_bf16(shape, std: float, *seed: int, device: str = "cuda") -> torch.Tensor:
+    """N(0, std) drawn on the device with torch's Philox generator seeded
+    from the tuple, in fp32, then rounded to bf16 (RNE): for workloads too
+    large to draw on the host (the 65B stack's weights). Not the same numbers
+    as the host draw of the same tuple."""
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(*seed))
+    w = torch.empty(shape, dtype=torch.float32, device=device)
+    w.normal_(0.0, std, generator=g)
+    return w.to(torch.bfloat16)
+
+
+def device_uniform_bf16(shape, bound: float, *seed: int, device: str = "cuda") -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(*seed))
+    w = torch.empty(shape, dtype=torch.float32, device=device)
+    w.uniform_(-bound, bound, generator=g)
+    return w.to(torch.bfloat16)
 
 
 def lora_A(r: int, k: int, *seed: int) -> torch.Tensor:
@@ -131,6 +158,18 @@ def linear_inputs(cid: int, layer: int, li: int, n: int, k: int, m: int, r: int,
     dY = normal_bf16((m, n), 1.0, cid, lid, T_DY)
     return LinearInputs(W, X, A, B, dY, scale,
                         dict(config=cid, layer=layer, linear=li, n=n, k=k, m=m, r=r))
+
+
+def device_linear_inputs(cid: int, layer: int, li: int, n: int, k: int, r: int, scale: float,
+                         sigma: float = 0.02) -> LinearInputs:
+    """W, A, B of one linear drawn on the device (same distributions and seed
+    tuples as linear_inputs, torch's generator); X and dY are left to the
+    caller (None)."""
+    lid = layer * 16 + li
+    W = device_normal_bf16((n, k), sigma, cid, lid, T_W)
+    A = device_uniform_bf16((r, k), 1.0 / math.sqrt(k), cid, lid, T_A)
+    B = device_normal_bf16((n, r), 0.01, cid, lid, T_B)
+    return LinearInputs(W, None, A, B, None, scale, dict(config=cid, layer=layer, linear=li, n=n, k=k, m=None, r=r))
 
 
 def config_linear_inputs(cid: int, li: int = 0, m: int | None = None, layer: int = 0) -> LinearInputs:
