@@ -13,8 +13,9 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // ---- encoder workspace: absmax fp32 [nb], run sums fp64 [ceil(nb/256)]
 inline size_t quantize_ws_absmax_bytes(int64_t nb) { return align256((size_t)nb * 4); }
+inline size_t quantize_ws_runsum_bytes(int64_t nb) { return align256((size_t)((nb + 255) / 256) * 8); }
 inline size_t quantize_ws_bytes(int64_t nb) {
-  return quantize_ws_absmax_bytes(nb) + align256((size_t)((nb + 255) / 256) * 8);
+  return quantize_ws_absmax_bytes(nb) + quantize_ws_runsum_bytes(nb) + align256((size_t)((nb + 255) / 256) * 4);
 }
 
 hipError_t launch_quantize(const void* W, bool w_bf16, int64_t n, int64_t k, const float* codebook,

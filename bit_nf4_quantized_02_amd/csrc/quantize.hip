@@ -8,17 +8,19 @@
 // blocks). "QLoRA Explained ..." (gamut.so), "Double Quantization": the block
 // constants are quantized again to 8 bits.
 //
-// Every decision is taken by exact comparisons in fp64, so the result does not
-// depend on the launch configuration:
+// Every decision is taken by exact comparisons in fp64 (an fp32 estimate only
+// chooses which comparisons to make), so the result does not depend on the
+// launch configuration:
 //   code  = #{ j : w > mu_j * c_b },   mu_j = (L_j + L_{j+1}) / 2
 //   code8 = E4M3 index #{ k : d_b > nu_k * s2 },  nu_k = midpoint of the k-th
 //           and (k+1)-th finite E4M3 values in ascending order.
 // Both products are exact in fp64 (<= 29 and <= 50 significant bits).
 //
 // Kernels, in launch order:
-//   nf4_codes_kernel   8 lanes per 64-block: absmax, 64 codes, packed bytes
-//   dq_runsum_kernel   one thread per run of 256 blocks: fp64 sum in order
-//   dq_mean_kernel     one thread: run sums in order -> fp32 mean
+//   nf4_codes_kernel   workgroups looping over runs of 256 blocks, 8 lanes per
+//                      block: absmax, 64 codes, packed bytes; each run's sum
+//   dq_mean_kernel     fp32 mean of all absmax values, equal to the fp64 sum
+//                      in order (runs summed in order, each run in order)
 //   dq_encode_kernel   one workgroup per run: s2 and the 256 code8 bytes
 #include "common.h"
 #include "kernels.h"
@@ -45,65 +47,229 @@ __device__ __forceinline__ void load8(const void* __restrict__ W, int64_t idx, f
   }
 }
 
-template <bool kBf16>
-__global__ __launch_bounds__(256) void nf4_codes_kernel(const void* __restrict__ W, int64_t nb,
-                                                        const float* __restrict__ codebook,
-                                                        uint32_t* __restrict__ codes,
-                                                        float* __restrict__ absmax) {
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t b = g >> 3;         // block
-  const int part = (int)(g & 7);    // which 8 of its 64 weights
-  // midpoints between adjacent levels, exact in fp64
+// Per-workgroup lookup tables for the code search (built from the codebook
+// at kernel start):
+//   lut[i]   for x in [(i - 64) / 64, (i - 63) / 64): the number of fp32
+//            midpoints below the interval and the one midpoint inside it
+//            (+inf if none; midpoints are >= 0.08 apart, intervals 1/64 wide)
+//   pair[c]  the exact fp64 midpoints around code c: (mu_{c-1}, mu_c), with
+//            -inf / +inf at the ends
+//   mid[j]   the 15 exact fp64 midpoints
+struct CodeTables {
+  uint2 lut[128];
+  double2 pair[16];  // (lo, hi)
   double mid[15];
-#pragma unroll
-  for (int j = 0; j < 15; ++j) mid[j] = ((double)codebook[j] + (double)codebook[j + 1]) * 0.5;
+};
 
-  float w[8];
-  float m = 0.0f;
-  if (b < nb) {
-    load8<kBf16>(W, b * kBlock + part * 8, w);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(w[i]));
+__device__ void build_tables(const float* cb, CodeTables& tb) {
+  const int t = threadIdx.x;
+  if (t < 15) tb.mid[t] = ((double)cb[t] + (double)cb[t + 1]) * 0.5;
+  if (t < 16) {
+    tb.pair[t].x = t == 0 ? -INFINITY : ((double)cb[t - 1] + (double)cb[t]) * 0.5;
+    tb.pair[t].y = t == 15 ? INFINITY : ((double)cb[t] + (double)cb[t + 1]) * 0.5;
   }
-  // max over the 8 lanes of this block (lanes 8-aligned inside the wavefront)
-#pragma unroll
-  for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 8));
-  if (b >= nb) return;
+  if (t < 128) {
+    const float lo = (float)(t - 64) / 64.0f, hi = (float)(t - 63) / 64.0f;
+    uint32_t below = 0;
+    float inside = INFINITY;
+    for (int j = 0; j < 15; ++j) {
+      const float mf = (float)(((double)cb[j] + (double)cb[j + 1]) * 0.5);
+      if (mf < lo) ++below;
+      else if (mf < hi) inside = mf;
+    }
+    tb.lut[t] = make_uint2(below, __float_as_uint(inside));
+  }
+}
 
-  const double c = (double)m;
-  uint32_t word = 0;
+// codes = #{ j : x > mu_j * c } for the 8 weights a lane holds, packed 4
+// bits each. An fp32 estimate of x / c picks each weight's candidate interval
+// from the table; two exact fp64 comparisons confirm it. The estimate's error
+// is far below the midpoint spacing, so they fail only for degenerate scales
+// (an fp32-denormal absmax, whose reciprocal overflows): those weights are
+// flagged in *bad for the full count. Written in stages over the 8 weights so
+// the table reads of all 8 are in flight together.
+__device__ __forceinline__ uint32_t nf4_codes8(const float (&w)[8], float rc, double cd, const CodeTables& tb,
+                                               uint32_t* bad) {
+  float xf[8];
+  uint2 e[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint32_t code = 7;
-    if (m != 0.0f) {
-      const double x = (double)w[i];
-      code = 0;
-#pragma unroll
-      for (int j = 0; j < 15; ++j) code += (x > mid[j] * c) ? 1u : 0u;
-    }
-    word |= code << (4 * i);
+    xf[i] = w[i] * rc;
+    int j = (int)fmaf(xf[i], 64.0f, 64.0f);  // x >= -1: truncation is the floor
+    j = j < 0 ? 0 : (j > 127 ? 127 : j);
+    e[i] = tb.lut[j];
   }
-  codes[b * 8 + part] = word;
-  if (part == 0) absmax[b] = m;
+  double2 pr[8];
+  uint32_t est[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    est[i] = e[i].x + (xf[i] > __uint_as_float(e[i].y) ? 1u : 0u);
+    pr[i] = tb.pair[est[i]];
+  }
+  uint32_t word = 0, fail = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double x = (double)w[i];
+    const bool ok = (x > pr[i].x * cd) & !(x > pr[i].y * cd);
+    word |= est[i] << (4 * i);
+    fail |= ok ? 0u : 1u << i;
+  }
+  *bad = fail;
+  return word;
 }
 
-__global__ __launch_bounds__(256) void dq_runsum_kernel(const float* __restrict__ absmax, int64_t nb,
-                                                        int64_t nruns, double* __restrict__ runsum) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= nruns) return;
-  const int64_t b0 = j * kDqBlock;
-  const int64_t b1 = (b0 + kDqBlock < nb) ? b0 + kDqBlock : nb;
-  double s = 0.0;
-  for (int64_t b = b0; b < b1; ++b) s += (double)absmax[b];  // left to right
-  runsum[j] = s;
+__device__ __forceinline__ uint32_t nf4_code_full(float w, double cd, const CodeTables& tb) {
+  const double x = (double)w;
+  uint32_t code = 0;
+#pragma unroll 1
+  for (int j = 0; j < 15; ++j) code += (x > tb.mid[j] * cd) ? 1u : 0u;
+  return code;
 }
 
-__global__ void dq_mean_kernel(const double* __restrict__ runsum, int64_t nruns, int64_t nb,
-                               float* __restrict__ mean) {
-  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+// Biased exponent of a block absmax for the exactness test of the mean
+// (max(E, 1): denormals share the smallest normal's spacing); 255 = none.
+__device__ __forceinline__ int absmax_exp(float m) {
+  const int e = (int)((__float_as_uint(m) >> 23) & 0xFF);
+  return m == 0.0f ? 255 : (e < 1 ? 1 : e);
+}
+
+// Workgroups loop over runs of 256 blocks: 8 lanes per block, 32 blocks per
+// pass, the loads of 4 passes issued before any of them is encoded. Writes the packed codes, every
+// block's absmax, and for each run the fp64 sum of its absmax values (in any
+// order: it is used only when every partial sum is exact, see
+// dq_mean_kernel) and the smallest exponent among them.
+template <bool kBf16>
+__global__ __launch_bounds__(256, 4) void nf4_codes_kernel(const void* __restrict__ W, int64_t nb, int64_t nruns,
+                                                        const float* __restrict__ codebook,
+                                                        uint32_t* __restrict__ codes,
+                                                        float* __restrict__ absmax, double* __restrict__ runsum,
+                                                        int* __restrict__ runexp) {
+  __shared__ float cb[16];
+  __shared__ CodeTables tb;
+  __shared__ double wsum[4];
+  __shared__ int wexp[4];
+  const int t = threadIdx.x;
+  if (t < 16) cb[t] = codebook[t];
+  __syncthreads();
+  build_tables(cb, tb);
+  __syncthreads();
+
+  const int sub = t >> 3, part = t & 7, wave = t >> 6;
+  constexpr int kPasses = 4;  // passes of 32 blocks whose loads are in flight together
+  for (int64_t run = blockIdx.x; run < nruns; run += gridDim.x) {
+    double rs = 0.0;
+    int re = 255;
+#pragma unroll 1
+    for (int64_t b0 = run * kDqBlock; b0 < (run + 1) * kDqBlock; b0 += kPasses * 32) {
+      float w[kPasses][8];
+#pragma unroll
+      for (int it = 0; it < kPasses; ++it) {
+        const int64_t b = b0 + it * 32 + sub;
+        if (b < nb) {
+          load8<kBf16>(W, b * kBlock + part * 8, w[it]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[it][i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < kPasses; ++it) {
+        const int64_t b = b0 + it * 32 + sub;
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(w[it][i]));
+        // max over the 8 lanes of this block (lanes 8-aligned inside the wavefront)
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 8));
+        uint32_t word = 0x77777777u;  // all-zero block: every code is 7
+        if (m != 0.0f) {
+          const float rc = __builtin_amdgcn_rcpf(m);
+          const double cd = (double)m;
+          uint32_t bad;
+          word = nf4_codes8(w[it], rc, cd, tb, &bad);
+          if (bad) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (bad >> i & 1u) word = (word & ~(0xFu << (4 * i))) | nf4_code_full(w[it][i], cd, tb) << (4 * i);
+          }
+        }
+        if (b < nb) {
+          codes[b * 8 + part] = word;
+          if (part == 0) {
+            absmax[b] = m;
+            rs += (double)m;
+            const int e = absmax_exp(m);
+            re = re < e ? re : e;
+          }
+        }
+      }
+    }
+    // the run's sum and smallest exponent: lanes 0, 8, .., 56 of each wave,
+    // then the 4 waves
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) {
+      rs += __shfl_xor(rs, off);
+      const int o = __shfl_xor(re, off);
+      re = re < o ? re : o;
+    }
+    if ((t & 63) == 0) {
+      wsum[wave] = rs;
+      wexp[wave] = re;
+    }
+    __syncthreads();
+    if (t == 0) {
+      runsum[run] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+      int e = wexp[0] < wexp[1] ? wexp[0] : wexp[1];
+      e = e < wexp[2] ? e : wexp[2];
+      runexp[run] = e < wexp[3] ? e : wexp[3];
+    }
+    __syncthreads();
+  }
+}
+
+// mean = RN_fp32(S / nb), S the fp64 sum of the run sums in order, each run
+// summed in order. Every absmax is a multiple of 2^(emin - 150) (emin: the
+// smallest exponent field among them), so when the total stays below
+// 2^(emin - 98) every partial sum, in any order, is a multiple of that below
+// 2^53 times it: exact, and the ordered sum equals the tree sum of the runs'
+// tree sums. Otherwise one thread takes the ordered sums themselves.
+__global__ __launch_bounds__(1024) void dq_mean_kernel(const double* __restrict__ runsum,
+                                                      const int* __restrict__ runexp, int64_t nruns,
+                                                      const float* __restrict__ absmax, int64_t nb,
+                                                      float* __restrict__ mean) {
+  __shared__ double ssum[1024];
+  __shared__ int sexp[1024];
+  const int t = threadIdx.x;
   double s = 0.0;
-  for (int64_t j = 0; j < nruns; ++j) s += runsum[j];  // left to right
-  mean[0] = (float)(s / (double)nb);
+  int e = 255;
+  for (int64_t j = t; j < nruns; j += 1024) {
+    s += runsum[j];
+    e = e < runexp[j] ? e : runexp[j];
+  }
+  ssum[t] = s;
+  sexp[t] = e;
+  __syncthreads();
+  for (int h = 512; h > 0; h >>= 1) {
+    if (t < h) {
+      ssum[t] += ssum[t + h];
+      sexp[t] = sexp[t] < sexp[t + h] ? sexp[t] : sexp[t + h];
+    }
+    __syncthreads();
+  }
+  if (t != 0) return;
+  double S = ssum[0];
+  const int emin = sexp[0];
+  const bool exact = emin == 255 || S < ldexp(1.0, emin - 98);
+  if (!exact) {
+    S = 0.0;
+    for (int64_t j = 0; j < nruns; ++j) {
+      const int64_t b1 = (j + 1) * kDqBlock < nb ? (j + 1) * kDqBlock : nb;
+      double P = 0.0;
+      for (int64_t b = j * kDqBlock; b < b1; ++b) P += (double)absmax[b];  // left to right
+      S += P;
+    }
+  }
+  mean[0] = (float)(S / (double)nb);
 }
 
 // Ascending index (0..252) of the finite E4M3 values -> bit pattern:
@@ -165,14 +331,16 @@ hipError_t launch_quantize(const void* W, bool w_bf16, int64_t n, int64_t k, con
   const int64_t nruns = cdiv(nb, kDqBlock);
   float* absmax = reinterpret_cast<float*>(ws);
   double* runsum = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + quantize_ws_absmax_bytes(nb));
-  const int64_t threads = nb * 8;
-  const dim3 grid((unsigned)cdiv(threads, 256));
+  int* runexp = reinterpret_cast<int*>(reinterpret_cast<char*>(runsum) + quantize_ws_runsum_bytes(nb));
+  // 4 workgroups per CU of an MI355X, each looping over runs
+  const dim3 grid((unsigned)(nruns < 1024 ? nruns : 1024));
   if (w_bf16)
-    nf4_codes_kernel<true><<<grid, 256, 0, stream>>>(W, nb, codebook, reinterpret_cast<uint32_t*>(codes), absmax);
+    nf4_codes_kernel<true><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, reinterpret_cast<uint32_t*>(codes),
+                                                     absmax, runsum, runexp);
   else
-    nf4_codes_kernel<false><<<grid, 256, 0, stream>>>(W, nb, codebook, reinterpret_cast<uint32_t*>(codes), absmax);
-  dq_runsum_kernel<<<(unsigned)cdiv(nruns, 256), 256, 0, stream>>>(absmax, nb, nruns, runsum);
-  dq_mean_kernel<<<1, 1, 0, stream>>>(runsum, nruns, nb, mean);
+    nf4_codes_kernel<false><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, reinterpret_cast<uint32_t*>(codes),
+                                                      absmax, runsum, runexp);
+  dq_mean_kernel<<<1, 1024, 0, stream>>>(runsum, runexp, nruns, absmax, nb, mean);
   dq_encode_kernel<<<(unsigned)nruns, 256, 0, stream>>>(absmax, nb, mean, s2, code8);
   return hipGetLastError();
 }

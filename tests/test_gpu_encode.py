@@ -76,6 +76,37 @@ def test_zero_blocks_zero_chunk_and_zero_tensor(q):
     assert np.all(gw.s2.cpu().numpy() == 0) and np.all(gw.code8.cpu().numpy() == 0)
 
 
+def _mean_sums_exact(absmax: np.ndarray) -> bool:
+    """Whether every fp64 partial sum of these absmax values is exact (the
+    total stays below 2^52 times the finest spacing among them)."""
+    nz = absmax[absmax != 0].astype(np.float32)
+    if nz.size == 0:
+        return True
+    e = np.maximum((nz.view(np.uint32) >> 23) & 0xFF, 1).min()
+    return float(np.sum(absmax.astype(np.float64))) < 2.0 ** (int(e) - 98)
+
+
+def test_mean_in_and_outside_the_exact_regime(q):
+    """The mean equals the ordered fp64 sum whether or not its partial sums
+    round: block scales spread over 1e-38..1 (with fp32-denormal blocks, whose
+    reciprocal overflows) make them round; ordinary weights keep them exact."""
+    g = np.random.default_rng(17)
+    W = (g.standard_normal((64, 1024)) * 0.02).astype(np.float32)
+    blocks = W.reshape(-1, 64)
+    blocks *= (10.0 ** g.uniform(-38, 0, size=(blocks.shape[0], 1))).astype(np.float32)
+    blocks[5] = g.standard_normal(64).astype(np.float32) * np.float32(1e-40)   # denormal absmax
+    blocks[700, :] = 0.0
+    Wt = torch.from_numpy(blocks.reshape(64, 1024).copy())
+    ow = oracle_encode(Wt.to(torch.float32))
+    assert not _mean_sums_exact(ow.absmax)
+    say("case: mean with rounding partial sums (fp32 input, scales 1e-38..1, denormal block)")
+    _roundtrip(q, Wt, torch.float32)
+    Wn = synth.weight_bf16(256, 1024, 0.02, 99, 18, 0)
+    assert _mean_sums_exact(oracle_encode(Wn).absmax)
+    say("case: mean with exact partial sums")
+    _roundtrip(q, Wn)
+
+
 def test_exact_ties(q):
     """Weights exactly on a midpoint between two levels (only possible where
     the midpoint times the scale is an fp32 number) take the lower level."""
