@@ -24,7 +24,8 @@ copy) of each weight, timed alone against the HBM roofline, and the same step
 with a bf16 base (the step's calls minus the two weight expansions, over the
 operands they leave in place) with QLoRA's slowdown over it, and the AdamW
 step over all adapter parameters with the moments in device memory and in
-pinned host memory ("paged").
+pinned host memory ("paged"), and the offline encode (quantize + double
+quantization) and the bf16 dequant of each weight shape, each timed alone.
 
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
@@ -496,6 +497,47 @@ def merge_rows(wl: Workload, q, reps: int = 20):
     return rows
 
 
+def _region_us(fn, reps: int) -> float:
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def encode_rows(wl: Workload, q, reps: int = 10):
+    """The offline encode (qlora_quantize_nf4: 4-bit codes, block absmax,
+    double quantization of the absmax) and qlora_dequant (the bf16 weight a
+    caller can materialize) of each distinct weight shape, each timed alone
+    on the weight's bf16 values in HBM. Bytes per launch: quantize reads 2 B
+    per weight and writes the packed form, dequant the reverse."""
+    rows = {}
+    for p in wl.plans:
+        key = f"{p.n}x{p.k}"
+        if key in rows or p.li.W is None:
+            continue
+        W = p.li.W.to("cuda")
+        w = q.NF4Weight.empty(p.n, p.k)
+        wsn = max(q.quantize_workspace_bytes(p.n, p.k), 256)
+        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda")
+        out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device="cuda")
+        st = w.struct()
+        fq = q.Call("qlora_quantize_nf4", q._ptr(W), q.DT_BF16, q.ctypes.byref(st), q._ptr(ws), wsn, q._stream(),
+                    keep=(st,))
+        fd = q.Call("qlora_dequant", q.ctypes.byref(st), q._ptr(out), q._stream(), keep=(st,))
+        nbytes = 2 * p.n * p.k + p.packed_bytes
+        tq, td = _region_us(fq, reps), _region_us(fd, reps)
+        rows[key] = dict(quantize_us=round(tq, 2), quantize_GBps=round(nbytes / tq / 1e3, 1),
+                         dequant_us=round(td, 2), dequant_GBps=round(nbytes / td / 1e3, 1), bytes=nbytes,
+                         dequant_frac=round(nbytes / td / 1e3 / PEAK_HBM_GBPS, 4))
+        del W, w, ws, out
+    return rows
+
+
 def adamw_rows(wl: Workload, q, reps: int = 20):
     """The AdamW step over every adapter parameter of the workload (A and B
     of each linear, fp32 masters, the step's dA / dB as gradients, bf16 copy
@@ -652,6 +694,7 @@ def main():
     merges = merge_rows(wl, q) if args.config in (1, 2, 3, 5) else {}
     lora_ms = lora_bf16_base(wl, q, args.steps)
     adamw = adamw_rows(wl, q)
+    encode = encode_rows(wl, q)
     for row in merges.values():
         row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
         row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
@@ -713,6 +756,7 @@ def main():
         "attainable": att,
         "adapter_merge_bf16": merges,
         "adamw_step": adamw,
+        "encode": encode,
         "lora_bf16_base": None if lora_ms is None else {
             "ms_per_step": round(lora_ms[0], 4),
             "tflops": round(wl.flops / (lora_ms[0] * 1e-3) / 1e12, 2),
