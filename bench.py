@@ -626,7 +626,9 @@ def cpu_baseline(wl: Workload, target_s: float):
     """The oracle as it stands, timed on this host's cores on a bounded sample
     of the same workload: whole steps of the first linear (all M tokens),
     repeated until about target_s seconds; the weight's oracle encoding is
-    made once beforehand and not timed."""
+    made once beforehand, timed on its own and not counted in the steps. The
+    parts of a step (scale decode + bf16 expansion, forward, backward) are
+    timed separately as well."""
     from oracle import linear as olin
     from oracle import nf4 as onf4
     try:
@@ -637,25 +639,32 @@ def cpu_baseline(wl: Workload, target_s: float):
         threads = len(os.sched_getaffinity(0))
     p = wl.plans[0]
     li = p.li
+    t0 = time.perf_counter()
     ow = onf4.NF4Weight(li.W.float().numpy())
+    t_encode = time.perf_counter() - t0
     # the inputs this linear actually consumed on the GPU (for chained
     # workloads X or dY come from the previous GPU step)
     X, A, B, dY = (t.float().cpu().numpy().astype(np.float64) for t in (p.X, li.A, li.B, p.dY))
     backward = len(p.bwd) > 0
     flops = sum(f for _, f, _ in p.fwd + p.bwd)
     n, spent = 0, 0.0
+    parts = np.zeros(3)
     out = None
     while (spent < target_s and n < 200) or n == 0:
         t0 = time.perf_counter()
         cp = onf4.decode_scales(ow.code8, ow.s2, ow.mean)
         Wd = onf4.dequant(ow.codes, cp, ow.levels)
+        t1 = time.perf_counter()
         Y, T = olin.linear_fwd(X, Wd, A, B, li.scale)
+        t2 = time.perf_counter()
         if backward:
             dX, dA, dB, _ = olin.linear_bwd(X, Wd, A, B, li.scale, dY, T)
             out = (Y, dX, dA, dB)
         else:
             out = (Y,)
-        spent += time.perf_counter() - t0
+        t3 = time.perf_counter()
+        parts += (t1 - t0, t2 - t1, t3 - t2)
+        spent += t3 - t0
         n += 1
     # parity of the timed GPU outputs against this sample
     got = [p.Y] + ([p.dX, p.dA, p.dB] if backward else [])
@@ -664,7 +673,9 @@ def cpu_baseline(wl: Workload, target_s: float):
                 sample=f"{n} whole fwd{'+bwd' if backward else ''} step(s) of linear '{wl.c.linears[0].name}' "
                        f"(M={p.m}, N={p.n}, K={p.k}, r={p.r}): numpy fp64 products, bf16 expansion of the "
                        f"encoded weight each step; {spent:.1f} s total",
-                seconds=spent, parity_relerr=errs)
+                seconds=spent, parity_relerr=errs,
+                parts_s={"encode_once": round(t_encode, 3), "dequant": round(float(parts[0]) / n, 4),
+                         "fwd": round(float(parts[1]) / n, 4), "bwd": round(float(parts[2]) / n, 4)})
 
 
 # ----------------------------------------------------------------------------- main
