@@ -8,8 +8,8 @@
 //
 //   Y = RN_bf16( X W'^T + s T B^T ),   T = X A^T precomputed (fp32)
 //
-// Each workgroup owns NT output rows (n) and the whole contraction; its 4
-// waves split the contraction into quarters. A wave walks its quarter in
+// Each workgroup owns NT output rows (n) and the whole contraction; its kW
+// waves split the contraction into kW parts. A wave walks its quarter in
 // 256-wide chunks, keeping the loads of the next chunk in flight while it
 // works on one: every lane loads 32 contiguous bytes of codes (one whole
 // 64-block of one row, one scale), expands them to bf16 in registers
@@ -20,8 +20,9 @@
 // is the A operand. The contraction order inside a chunk is permuted the same
 // way on both operands (lane group g takes columns 64 g .. 64 g + 63), which
 // leaves the sum unchanged and makes each lane's code load contiguous.
-// Partial sums of the 4 waves are added in a fixed order through LDS, the
-// low-rank term is added in fp32, and Y is rounded to bf16 once.
+// Partial sums of the waves are added in a fixed order through LDS; the
+// low-rank term T B^T is formed with fp32 MFMAs (one 16-row tile per wave,
+// T and B exact in fp32) and added in fp32, and Y is rounded to bf16 once.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,8 +30,8 @@ namespace qlora {
 
 namespace {
 
-template <int NT, bool kLora>
-__global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict__ codes,
+template <int NT, int kW, bool kLora>
+__global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ code8,
                                                        const float* __restrict__ s2,
                                                        const float* __restrict__ mean_p,
@@ -41,15 +42,17 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
                                                        uint16_t* __restrict__ Y) {
   constexpr int kTiles = NT / 16;
   __shared__ float2 lut2[256];
-  __shared__ float red[4][kTiles][16][16];
+  __shared__ float red[kW][kTiles][16][16];
+  __shared__ float lred[kLora ? kTiles : 1][16][16];
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
-  lut2[t] = float2{codebook[t & 15], codebook[t >> 4]};  // levels of the two codes in byte t
+  for (int i = t; i < 256; i += 64 * kW)
+    lut2[i] = float2{codebook[i & 15], codebook[i >> 4]};  // levels of the two codes in byte i
   __syncthreads();
   const float mean = mean_p[0];
   const int64_t n0 = (int64_t)blockIdx.x * NT;
   constexpr int kChunk = 256;                            // columns per wave iteration
-  const int64_t kq = cdiv(cdiv(K, 4), kChunk) * kChunk;  // per-wave share
+  const int64_t kq = cdiv(cdiv(K, kW), kChunk) * kChunk;  // per-wave share
   const int64_t kb = wave * kq;
   const int64_t ke = (kb + kq < K) ? kb + kq : K;        // multiple of 64
   const int grp = lane >> 4;   // 0..3: which 64-block of a 256-column chunk
@@ -148,18 +151,35 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
   for (int i = 0; i < kTiles; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[wave][i][4 * (lane >> 4) + v][lane & 15] = acc[i][v];
+  if constexpr (kLora) {
+    // L[m][n] = sum_j T[m][j] B[n][j] for tile i on wave i (mod kW), 4 ranks
+    // per v_mfma_f32_16x16x4_f32: A = T (lane: token lane % 16, rank lane / 16),
+    // B = B^T (lane: weight row lane % 16, same rank); rows past M or N and
+    // ranks past r read as zero
+    for (int i = wave; i < kTiles; i += kW) {
+      f32x4 l = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int m = lane & 15;
+      const int64_t n = n0 + i * 16 + (lane & 15);
+      for (int j0 = 0; j0 < r; j0 += 4) {
+        const int j = j0 + (lane >> 4);
+        const float a = (m < M && j < r) ? T[m * r + j] : 0.0f;
+        const float b = (n < N && j < r) ? bf16_bits_to_f32(B[n * r + j]) : 0.0f;
+        l = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, l, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) lred[i][4 * (lane >> 4) + v][lane & 15] = l[v];
+    }
+  }
   __syncthreads();
-  for (int o = t; o < 16 * NT; o += 256) {
+  for (int o = t; o < 16 * NT; o += 64 * kW) {
     const int m = o / NT, nl = o % NT;
     const int64_t n = n0 + nl;
     if (m >= M || n >= N) continue;
     const int i = nl >> 4, nc = nl & 15;
-    float y = ((red[0][i][m][nc] + red[1][i][m][nc]) + red[2][i][m][nc]) + red[3][i][m][nc];
-    if constexpr (kLora) {
-      float l = 0.0f;
-      for (int j = 0; j < r; ++j) l = fmaf(T[m * r + j], bf16_bits_to_f32(B[n * r + j]), l);
-      y = fmaf(scale, l, y);
-    }
+    float y = red[0][i][m][nc];
+#pragma unroll
+    for (int w2 = 1; w2 < kW; ++w2) y += red[w2][i][m][nc];  // in wave order
+    if constexpr (kLora) y = fmaf(scale, lred[i][m][nc], y);
     Y[m * N + n] = to_bf16_bits(y);
   }
 }
@@ -168,24 +188,24 @@ __global__ __launch_bounds__(256) void gemv_nf4_kernel(const uint8_t* __restrict
 
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T, const uint16_t* B, int r,
                        float scale, uint16_t* Y, hipStream_t stream) {
-  // Rows per workgroup: as many as keep >= ~256-448 workgroups in flight
-  // (measured on the 70B-class shapes: 64 for 28672 rows, 32 for 8192).
+  // Rows and waves per workgroup, measured on the 70B-class shapes: 64 rows
+  // and 4 waves for 28672 rows (448 workgroups), 32 rows and 8 waves for
+  // 8192 rows (256 workgroups, each wave an eighth of the 28672-long
+  // contraction), 16 rows and 4 waves below.
   const bool lora = r > 0;
-#define QLORA_GEMV(NT)                                                                                        \
+#define QLORA_GEMV(NT, W)                                                                                     \
   {                                                                                                           \
     const dim3 grid((unsigned)cdiv(w.n, NT));                                                                 \
     if (lora)                                                                                                 \
-      gemv_nf4_kernel<NT, true><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean,            \
-                                                                    w.codebook, w.n, w.k, X, M, T, B, r,      \
-                                                                    scale, Y);                                \
+      gemv_nf4_kernel<NT, W, true><<<grid, 64 * W, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook,   \
+                                                               w.n, w.k, X, M, T, B, r, scale, Y);            \
     else                                                                                                      \
-      gemv_nf4_kernel<NT, false><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean,           \
-                                                                     w.codebook, w.n, w.k, X, M, T, B, r,     \
-                                                                     scale, Y);                               \
+      gemv_nf4_kernel<NT, W, false><<<grid, 64 * W, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook,  \
+                                                                w.n, w.k, X, M, T, B, r, scale, Y);           \
   }
-  if (w.n / 64 >= 448) QLORA_GEMV(64)
-  else if (w.n / 32 >= 256) QLORA_GEMV(32)
-  else QLORA_GEMV(16)
+  if (w.n / 64 >= 448) QLORA_GEMV(64, 4)
+  else if (w.n / 32 >= 256) QLORA_GEMV(32, 8)
+  else QLORA_GEMV(16, 4)
 #undef QLORA_GEMV
   return hipGetLastError();
 }

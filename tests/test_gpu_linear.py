@@ -76,7 +76,11 @@ def test_gemm_path(q, m, n, k, r):
 
 
 @pytest.mark.parametrize("m,n,k,r", [(1, 1024, 1024, 8), (4, 300, 512, 16), (5, 77, 192, 3), (16, 1000, 2048, 16),
-                                     (16, 64, 64, 0), (2, 4096, 320, 64)])
+                                     (16, 64, 64, 0), (2, 4096, 320, 64),
+                                     # 32 rows x 8 waves per workgroup (n >= 8192), ragged rows, odd rank
+                                     (7, 8200, 1024, 5),
+                                     # 64 rows x 4 waves (n >= 28672), ragged rows, largest rank
+                                     (16, 28700, 256, 128)])
 def test_gemv_path(q, m, n, k, r):
     _run(q, _inputs(m, n, k, r, seed=m * 7 + n + k + r, sigma=0.015))
 
