@@ -11,7 +11,9 @@ pages' description of the method.
 Modules
 -------
 ``oracle.nf4``     codebook, blockwise NF4 quantization, double quantization of
-                   the block constants, dequantization to bf16.
+                   the block constants, dequantization to bf16; the uniform
+                   INT4 grid and the encoding without double quantization
+                   (ablations).
 ``oracle.linear``  fp64 forward and backward of the frozen-base linear with the
                    LoRA branch.
 ``oracle.merge``   the adapter folded into a dequantized copy of the base (and

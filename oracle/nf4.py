@@ -40,6 +40,17 @@ Readings where the pages leave a step open (each is listed in the design doc):
      rounded fp32 operations; w' = RN_bf16(RN32(L[code] * c')), bf16 with
      round-to-nearest-even.
   R8 nibble order: element 2t goes in the low nibble of byte t.
+
+Ablation variants the pages contrast NF4 and double quantization with
+(QQ "NF4: a 4-bit format matched to weight statistics": a uniform INT4 grid
+spends code points evenly; QX "Double Quantization": the saving over keeping
+the block constants in full precision):
+  R9  uniform INT4 grid: L_i = RN32((i - 7) / 7), i = 0..15 -- evenly spaced,
+      -1 at index 0, the exact zero at index 7 (where R6 puts all-zero blocks),
+      +1 at index 14; index 15 (8/7) lies beyond any block's largest
+      magnitude and is never chosen (the symmetric absmax INT4 grid).
+  R10 no double quantization: c' = c_b, the fp32 block absmax, stored as is
+      (one fp32 per block instead of one byte plus shares of s2 and mean).
 """
 
 from __future__ import annotations
@@ -87,6 +98,21 @@ def nf4_levels_fp64() -> list[float]:
 def nf4_levels() -> np.ndarray:
     """The 16 NF4 levels rounded once to fp32 (index 0 = -1, 7 = 0, 15 = +1)."""
     return np.array(nf4_levels_fp64(), dtype=np.float64).astype(np.float32)
+
+
+def uniform4_levels() -> np.ndarray:
+    """The uniform INT4 grid of reading R9, each level rounded once to fp32
+    (the rational (i - 7)/7 is rounded directly, not through fp64)."""
+    from fractions import Fraction
+    out = []
+    for i in range(16):
+        q = Fraction(i - 7, 7)
+        lo = np.float32(float(q))                      # within one fp32 ulp of q
+        cands = [np.nextafter(lo, np.float32(-2)), lo, np.nextafter(lo, np.float32(2))]
+        best = min(cands, key=lambda v: (abs(Fraction(float(v)) - q),
+                                         int(np.asarray(v, np.float32).view(np.uint32)) & 1))
+        out.append(best)
+    return np.array(out, dtype=np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -270,17 +296,25 @@ def dequant(codes, cprime, levels) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 class NF4Weight:
-    """Everything the encoder produces for one [N, K] weight."""
+    """Everything the encoder produces for one [N, K] weight. ``levels``
+    selects the 16-level grid (NF4 by default, R9 for the uniform ablation);
+    ``double_quant=False`` keeps the fp32 block scales as they are (R10):
+    code8 and mean are then None and s2 holds one scale per block."""
 
-    def __init__(self, W: np.ndarray, levels: np.ndarray | None = None):
+    def __init__(self, W: np.ndarray, levels: np.ndarray | None = None, double_quant: bool = True):
         W = np.asarray(W, dtype=np.float32)
         self.shape = W.shape
         self.levels = nf4_levels() if levels is None else levels
         self.absmax = block_absmax(W)
         self.codes = nf4_codes(W, self.levels)
         self.packed = pack_nibbles(self.codes)
-        self.code8, self.s2, self.mean = double_quantize(self.absmax)
-        self.cprime = decode_scales(self.code8, self.s2, self.mean)
+        if double_quant:
+            self.code8, self.s2, self.mean = double_quantize(self.absmax)
+            self.cprime = decode_scales(self.code8, self.s2, self.mean)
+        else:
+            self.code8, self.mean = None, None
+            self.s2 = self.absmax.astype(np.float32).copy()
+            self.cprime = self.s2
 
     def dequant_bits(self) -> np.ndarray:
         return dequant_bits(self.codes, self.cprime, self.levels)
@@ -289,9 +323,12 @@ class NF4Weight:
         return dequant(self.codes, self.cprime, self.levels)
 
 
-def packed_bytes(n: int, k: int) -> int:
-    """Bytes of one encoded weight: codes + code8 + s2 + mean (codebook excluded)."""
+def packed_bytes(n: int, k: int, double_quant: bool = True) -> int:
+    """Bytes of one encoded weight: codes + code8 + s2 + mean, or codes + one
+    fp32 scale per block without double quantization (codebook excluded)."""
     nb = n * k // BLOCK
+    if not double_quant:
+        return n * k // 2 + 4 * nb
     nc = -(-nb // DQ_BLOCK)
     return n * k // 2 + nb + 4 * nc + 4
 

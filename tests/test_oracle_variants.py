@@ -1,0 +1,92 @@
+"""Pins for the oracle's ablation variants (no GPU): the uniform INT4 grid
+and the encoding without double quantization.
+
+Pages: a uniform INT4 grid spaces its 16 values evenly while NF4 puts them
+where a bell curve is dense, so NF4 reconstructs Gaussian blocks with less
+error ("QLoRA: Quantized Low-Rank Adaptation" (completesystemdesign.dev),
+"NF4: a 4-bit format matched to weight statistics"); double quantization
+saves about 0.37 bit per parameter over fp32 block constants ("QLoRA
+Explained ..." (gamut.so), "Double Quantization").
+"""
+
+import json
+import os
+
+import numpy as np
+
+from oracle import nf4
+
+from test_oracle_quantize import _brute_codes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_uniform_grid_shape():
+    L = nf4.uniform4_levels().astype(np.float64)
+    assert L.shape == (16,) and np.all(np.diff(L) > 0)
+    assert L[0] == -1.0 and L[7] == 0.0 and L[14] == 1.0
+    # symmetric about the zero level, evenly spaced to within fp32 rounding
+    assert np.array_equal(L[:7], -L[14:7:-1])
+    step = np.diff(L)
+    assert np.max(np.abs(step - step.mean())) <= 2.0 ** -23
+    assert abs(7.0 * L[8] - 1.0) <= 2.0 ** -23
+
+
+def test_uniform_codes_match_brute_force_and_never_use_the_top_level():
+    rng = np.random.default_rng(4)
+    L = nf4.uniform4_levels()
+    for scale in (1.0, 0.02, 3e-5):
+        W = (rng.standard_normal((3, 128)) * scale).astype(np.float32)
+        W[1, 64] = np.abs(W[1, 64:128]).max() * np.float32(1.0)   # a positive block maximum
+        codes = nf4.nf4_codes(W, L)
+        assert np.array_equal(codes, _brute_codes(W, L))
+        assert codes.max() <= 14
+
+
+def test_nf4_has_less_error_than_uniform_on_gaussian_blocks():
+    rng = np.random.default_rng(3)
+    W = (rng.standard_normal((256, 1024)) * 0.02).astype(np.float32)
+    errs = {}
+    for name, L in (("nf4", nf4.nf4_levels()), ("int4", nf4.uniform4_levels())):
+        o = nf4.NF4Weight(W, L, double_quant=False)
+        c = o.absmax.astype(np.float64).reshape(-1, 1)
+        rec = (L.astype(np.float64)[o.codes].reshape(-1, 64) * c).reshape(W.shape)
+        errs[name] = np.mean((rec - W) ** 2)
+        if name == "int4":
+            # an even grid of step c/7 leaves errors spread evenly over
+            # +-step/2 (variance step^2 / 12), except the block maximum, which
+            # is exact: 63/64 of mean(c^2) / 588
+            pred = 63.0 / 64.0 * np.mean(c ** 2) / 588.0
+            assert abs(errs[name] / pred - 1.0) < 0.02
+    assert errs["nf4"] < 0.8 * errs["int4"]
+
+
+def test_without_double_quant_the_scale_is_the_block_absmax():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    W = np.zeros((1, 64), dtype=np.float32)
+    W[0, :8] = np.array(g["weights"], dtype=np.float32)
+    for L in (nf4.nf4_levels(), nf4.uniform4_levels()):
+        o = nf4.NF4Weight(W, L, double_quant=False)
+        assert o.code8 is None and o.mean is None
+        assert o.cprime[0] == np.float32(g["absmax"])
+        # with scale 1.0 every weight comes back as its level, rounded to bf16
+        want = nf4.bf16_bits(L[o.codes[0]].astype(np.float32))
+        assert np.array_equal(o.dequant_bits()[0], want)
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((8, 512)) * 0.02).astype(np.float32)
+    o = nf4.NF4Weight(W, double_quant=False)
+    assert np.array_equal(o.cprime, np.abs(W.reshape(-1, 64)).max(axis=1))
+    # same codes as with double quantization: the codes use the exact absmax
+    assert np.array_equal(o.codes, nf4.NF4Weight(W).codes)
+
+
+def test_storage_without_double_quant():
+    g = json.load(open(os.path.join(GOLDEN, "storage_closed_forms.json")))
+    n, k = 4096, 4096
+    nb = n * k // 64
+    assert nf4.packed_bytes(n, k, double_quant=False) == n * k // 2 + 4 * nb
+    bits_nodq = 8.0 * nf4.packed_bytes(n, k, double_quant=False) / (n * k)
+    bits_dq = 8.0 * nf4.packed_bytes(n, k) / (n * k)
+    assert bits_nodq == 4.5
+    # the difference is the page's saving of about 0.37 bit per parameter
+    assert abs((bits_nodq - bits_dq) - g["dq_saving_bits_per_param_about"]) < 0.01
