@@ -18,10 +18,11 @@ qlora_status hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLOR
 qlora_status check_weight(const qlora_nf4_weight* w) {
   if (w == nullptr) return QLORA_ERR_INVALID_ARG;
   if (w->n < 1 || w->k < 1 || (w->k % QLORA_BLOCK) != 0) return QLORA_ERR_SHAPE;
-  if (!w->codes || !w->code8 || !w->s2 || !w->mean || !w->codebook) return QLORA_ERR_INVALID_ARG;
-  if (!aligned16(w->codes) || !aligned16(w->code8) || !aligned16(w->s2) || !aligned16(w->mean) ||
-      !aligned16(w->codebook))
-    return QLORA_ERR_INVALID_ARG;
+  // code8 NULL: no double quantization (s2 holds one fp32 scale per block,
+  // mean is not read)
+  if (!w->codes || !w->s2 || !w->codebook || (w->code8 && !w->mean)) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(w->codes) || !aligned16(w->s2) || !aligned16(w->codebook)) return QLORA_ERR_INVALID_ARG;
+  if (w->code8 && (!aligned16(w->code8) || !aligned16(w->mean))) return QLORA_ERR_INVALID_ARG;
   return QLORA_OK;
 }
 
@@ -150,6 +151,13 @@ size_t qlora_nf4_packed_bytes(int64_t n, int64_t k) {
   const int64_t nb = n * k / QLORA_BLOCK;
   const int64_t nc = (nb + QLORA_DQ_BLOCK - 1) / QLORA_DQ_BLOCK;
   return (size_t)(n * k / 2 + nb + 4 * nc + 4);
+}
+
+size_t qlora_nf4_storage_bytes(int64_t n, int64_t k, int double_quant) {
+  if (double_quant != 0 && double_quant != 1) return 0;
+  if (double_quant) return qlora_nf4_packed_bytes(n, k);
+  if (n < 1 || k < 1 || k % QLORA_BLOCK) return 0;
+  return (size_t)(n * k / 2 + 4 * (n * k / QLORA_BLOCK));
 }
 
 size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k) {

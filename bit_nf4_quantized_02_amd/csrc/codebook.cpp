@@ -39,6 +39,13 @@ double normal_quantile(double p) {
 
 }  // namespace
 
+extern "C" qlora_status qlora_build_uniform4_codebook(float* levels_out) {
+  if (levels_out == nullptr) return QLORA_ERR_INVALID_ARG;
+  // (i - 7) / 7: both operands exact in fp32, the division rounded once
+  for (int i = 0; i < 16; ++i) levels_out[i] = (float)(i - 7) / 7.0f;
+  return QLORA_OK;
+}
+
 extern "C" qlora_status qlora_build_nf4_codebook(float* levels_out) {
   if (levels_out == nullptr) return QLORA_ERR_INVALID_ARG;
   const double delta = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));

@@ -62,11 +62,37 @@ __device__ __forceinline__ float decode_block_scale(uint32_t code8, float s2, fl
   return p + mean;
 }
 
+// An encoded weight keeps its block scales double-quantized (code8 set) or
+// as one fp32 value per block in s2 (code8 NULL: no double quantization). In
+// the second form the loads below return the E4M3 code of 1.0 and a zero
+// mean, for which decode_block_scale returns the stored scale exactly
+// (1.0 * s and s + 0 are exact for s >= 0), so every kernel decodes both
+// forms with the same arithmetic.
+constexpr uint32_t kE4m3One = 0x38;
+
+__device__ __forceinline__ float weight_mean(const uint8_t* code8, const float* __restrict__ mean_p) {
+  return code8 ? mean_p[0] : 0.0f;
+}
+
+__device__ __forceinline__ void scale_fields(const uint8_t* __restrict__ code8, const float* __restrict__ s2,
+                                             int64_t blk, uint32_t& c8, float& s2v) {
+  if (code8) {
+    c8 = code8[blk];
+    s2v = s2[blk / kDqBlock];
+  } else {
+    c8 = kE4m3One;
+    s2v = s2[blk];
+  }
+}
+
 // Scale of block `blk` (global block index) read from the encoded weight.
 __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ code8,
                                              const float* __restrict__ s2, float mean,
                                              int64_t blk) {
-  return decode_block_scale(code8[blk], s2[blk / kDqBlock], mean);
+  uint32_t c8;
+  float s2v;
+  scale_fields(code8, s2, blk, c8, s2v);
+  return decode_block_scale(c8, s2v, mean);
 }
 
 // One weight: w' = RN_bf16(RN32(L[code] * c')); the product is a single

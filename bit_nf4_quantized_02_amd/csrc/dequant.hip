@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = codebook[threadIdx.x];
   __syncthreads();
-  const float mean = mean_p[0];
+  const float mean = weight_mean(code8, mean_p);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) {
     const int64_t blk = i >> 3;  // 8 words per 64-weight block

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
   __syncthreads();
   const int64_t c = (int64_t)blockIdx.y * 256 + t;
   if (c >= kw) return;
-  const float mean = mean_p[0];
+  const float mean = weight_mean(code8, mean_p);
   uint32_t word[kRows], c8[kRows];
   float s2v[kRows];
 #pragma unroll
@@ -79,8 +79,7 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
     const int64_t row = r0 + i < n ? r0 + i : n - 1;  // rows past n repeat the last one (not stored)
     const int64_t wi = row * kw + c;                  // code word index
     word[i] = codes[wi];
-    c8[i] = code8[wi >> 3];
-    s2v[i] = s2[(wi >> 3) / kDqBlock];
+    scale_fields(code8, s2, wi >> 3, c8[i], s2v[i]);
   }
 #pragma unroll
   for (int i = 0; i < kRows; ++i)
@@ -135,7 +134,7 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
   }
   if (t < 16) lut[t] = codebook[t];
   __syncthreads();
-  const float mean = mean_p[0];
+  const float mean = weight_mean(code8, mean_p);
   const int64_t n0 = tn * kXT;
   const int pr = t & 127, half = t >> 7;
   const int64_t na = n0 + 2 * pr, nb = na + 1;

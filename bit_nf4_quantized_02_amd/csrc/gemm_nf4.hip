@@ -184,8 +184,7 @@ __device__ __forceinline__ void load_w(const GemmArgs& a, int64_t n0, int step, 
   const int64_t kc = k < a.wk ? k : a.wk - 32;
   const u32x4 q = *reinterpret_cast<const u32x4*>(a.codes + nc * (a.wk / 2) + kc / 2);
   const int64_t blk = nc * kblocks + kc / kBlock;
-  st.c8 = a.code8[blk];
-  st.s2v = a.s2[blk / kDqBlock];
+  scale_fields(a.code8, a.s2, blk, st.c8, st.s2v);
 #pragma unroll
   for (int j = 0; j < 4; ++j) st.q[j] = ok ? q[j] : 0x77777777u;
 }
@@ -387,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nf4_kernel(GemmArgs a) {
 
   ActStage ast;
   WStage wst[2];
-  const float mean = a.mean[0];
+  const float mean = weight_mean(a.code8, a.mean);
   // prologue: step 0 into buffer 0; step 1 activations and weights staged
   if constexpr (kVec) {
     issue_act_lds(a, m0, 0, nk_main, As[0]);

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
   for (int i = t; i < 256; i += 64 * kW)
     lut2[i] = float2{codebook[i & 15], codebook[i >> 4]};  // levels of the two codes in byte i
   __syncthreads();
-  const float mean = mean_p[0];
+  const float mean = weight_mean(code8, mean_p);
   const int64_t n0 = (int64_t)blockIdx.x * NT;
   constexpr int kChunk = 256;                            // columns per wave iteration
   const int64_t kq = cdiv(cdiv(K, kW), kChunk) * kChunk;  // per-wave share
@@ -104,8 +104,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
       st.cw[i][0] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2);
       st.cw[i][1] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2 + 16);
       const int64_t blk = bbase[i] + kc / kBlock;
-      st.c8[i] = code8[blk];
-      st.s2v[i] = s2[blk / kDqBlock];
+      scale_fields(code8, s2, blk, st.c8[i], st.s2v[i]);
     }
   };
   auto compute = [&](const Stage& st) {

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ 
   const int64_t c0 = (int64_t)blockIdx.x * kGK;
   const int64_t ibase = (int64_t)blockIdx.y * kGT * kTiles;
   const int kcols = (int)(k - c0 < kGK ? k - c0 : kGK);  // 64 or 128 (k % 64 == 0)
-  const float mean = kFromNf4 ? mean_p[0] : 0.0f;
+  const float mean = kFromNf4 ? weight_mean(code8, mean_p) : 0.0f;
   const int cc = t & 15;
 
   if (kFromNf4 && t < 16) lut[t] = codebook[t];

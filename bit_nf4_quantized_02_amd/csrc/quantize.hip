@@ -329,7 +329,10 @@ hipError_t launch_quantize(const void* W, bool w_bf16, int64_t n, int64_t k, con
                            hipStream_t stream) {
   const int64_t nb = n * k / kBlock;
   const int64_t nruns = cdiv(nb, kDqBlock);
-  float* absmax = reinterpret_cast<float*>(ws);
+  // without double quantization (code8 NULL) the block absmax values are the
+  // stored scales: written straight to s2, and the second level is skipped
+  const bool dq = code8 != nullptr;
+  float* absmax = dq ? reinterpret_cast<float*>(ws) : s2;
   double* runsum = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + quantize_ws_absmax_bytes(nb));
   int* runexp = reinterpret_cast<int*>(reinterpret_cast<char*>(runsum) + quantize_ws_runsum_bytes(nb));
   // 4 workgroups per CU of an MI355X, each looping over runs
@@ -340,8 +343,10 @@ hipError_t launch_quantize(const void* W, bool w_bf16, int64_t n, int64_t k, con
   else
     nf4_codes_kernel<false><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, reinterpret_cast<uint32_t*>(codes),
                                                       absmax, runsum, runexp);
-  dq_mean_kernel<<<1, 1024, 0, stream>>>(runsum, runexp, nruns, absmax, nb, mean);
-  dq_encode_kernel<<<(unsigned)nruns, 256, 0, stream>>>(absmax, nb, mean, s2, code8);
+  if (dq) {
+    dq_mean_kernel<<<1, 1024, 0, stream>>>(runsum, runexp, nruns, absmax, nb, mean);
+    dq_encode_kernel<<<(unsigned)nruns, 256, 0, stream>>>(absmax, nb, mean, s2, code8);
+  }
   return hipGetLastError();
 }
 

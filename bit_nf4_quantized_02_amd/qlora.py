@@ -47,6 +47,8 @@ _SIGS = {
     "qlora_status_string": (ctypes.c_char_p, [_int]),
     "qlora_build_nf4_codebook": (_int, [ctypes.POINTER(_f)]),
     "qlora_nf4_packed_bytes": (_sz, [_i64, _i64]),
+    "qlora_nf4_storage_bytes": (_sz, [_i64, _i64, _int]),
+    "qlora_build_uniform4_codebook": (_int, [ctypes.POINTER(_f)]),
     "qlora_quantize_workspace_bytes": (_sz, [_i64, _i64]),
     "qlora_quantize_nf4": (_int, [_vp, _int, _W, _vp, _sz, _vp]),
     "qlora_dequant": (_int, [_W, _vp, _vp]),
@@ -124,8 +126,15 @@ def build_nf4_codebook() -> list[float]:
     return [buf[i] for i in range(16)]
 
 
-def nf4_packed_bytes(n: int, k: int) -> int:
-    return int(_lib.qlora_nf4_packed_bytes(n, k))
+def build_uniform4_codebook() -> list[float]:
+    """The 16 levels of the uniform INT4 grid (host, fp32), ascending."""
+    buf = (_f * 16)()
+    _check(_lib.qlora_build_uniform4_codebook(buf), "qlora_build_uniform4_codebook")
+    return [buf[i] for i in range(16)]
+
+
+def nf4_packed_bytes(n: int, k: int, double_quant: bool = True) -> int:
+    return int(_lib.qlora_nf4_storage_bytes(n, k, int(bool(double_quant))))
 
 
 def quantize_workspace_bytes(n: int, k: int) -> int:
@@ -144,35 +153,48 @@ class NF4Weight:
     n: int
     k: int
     codes: torch.Tensor      # uint8 [n, k/2]
-    code8: torch.Tensor      # uint8 [n*k/64]
-    s2: torch.Tensor         # fp32  [ceil(nb/256)]
-    mean: torch.Tensor       # fp32  [1]
+    code8: torch.Tensor | None   # uint8 [n*k/64] (None: no double quantization)
+    s2: torch.Tensor             # fp32  [ceil(nb/256)], or [nb] block scales without it
+    mean: torch.Tensor | None    # fp32  [1]
     codebook: torch.Tensor   # fp32  [16]
 
     @staticmethod
-    def empty(n: int, k: int, device="cuda", codebook: torch.Tensor | None = None) -> "NF4Weight":
+    def empty(n: int, k: int, device="cuda", codebook: torch.Tensor | None = None,
+              double_quant: bool = True) -> "NF4Weight":
+        """Buffers for one encoded weight; without double quantization code8
+        and mean are None and s2 holds one fp32 scale per block."""
         nb = n * k // BLOCK
         nc = -(-nb // DQ_BLOCK)
         if codebook is None:
             codebook = torch.tensor(build_nf4_codebook(), dtype=torch.float32, device=device)
-        return NF4Weight(n, k,
-                         torch.empty((n, k // 2), dtype=torch.uint8, device=device),
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=device)
+        if not double_quant:
+            return NF4Weight(n, k, codes, None, torch.empty((nb,), dtype=torch.float32, device=device), None,
+                             codebook)
+        return NF4Weight(n, k, codes,
                          torch.empty((nb,), dtype=torch.uint8, device=device),
                          torch.empty((nc,), dtype=torch.float32, device=device),
                          torch.empty((1,), dtype=torch.float32, device=device),
                          codebook)
 
+    @property
+    def double_quant(self) -> bool:
+        return self.code8 is not None
+
     def struct(self) -> _Weight:
-        return _Weight(self.n, self.k, self.codes.data_ptr(), self.code8.data_ptr(), self.s2.data_ptr(),
-                       self.mean.data_ptr(), self.codebook.data_ptr())
+        p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        return _Weight(self.n, self.k, self.codes.data_ptr(), p(self.code8), self.s2.data_ptr(),
+                       p(self.mean), self.codebook.data_ptr())
 
     def nbytes(self) -> int:
-        return nf4_packed_bytes(self.n, self.k)
+        return nf4_packed_bytes(self.n, self.k, self.double_quant)
 
 
 def quantize_nf4(W: torch.Tensor, out: NF4Weight | None = None, ws: torch.Tensor | None = None,
-                 stream=None) -> NF4Weight:
-    """Encode W ([n, k] bf16 or fp32, on the GPU) as NF4 codes + double-quantized scales."""
+                 stream=None, codebook: torch.Tensor | None = None, double_quant: bool = True) -> NF4Weight:
+    """Encode W ([n, k] bf16 or fp32, on the GPU) as 4-bit codes + block
+    scales, double-quantized unless double_quant is False; the levels are
+    NF4 unless another 16-level device codebook is given (or out's)."""
     if W.dim() != 2:
         raise ValueError("W must be [n, k]")
     n, k = W.shape
@@ -181,7 +203,7 @@ def quantize_nf4(W: torch.Tensor, out: NF4Weight | None = None, ws: torch.Tensor
         raise ValueError("W must be bf16 or fp32")
     _need(W, W.dtype, (n, k), "W")
     if out is None:
-        out = NF4Weight.empty(n, k, device=W.device)
+        out = NF4Weight.empty(n, k, device=W.device, codebook=codebook, double_quant=double_quant)
     need = quantize_workspace_bytes(n, k)
     if ws is None:
         ws = _bytes(need, W.device)

@@ -80,6 +80,9 @@ typedef enum { QLORA_DT_BF16 = 0, QLORA_DT_FP32 = 1 } qlora_dtype;
  *                     scaled absmax [QX "Double Quantization"].
  *   s2       [ceil(n*k/64/256)] fp32 second-level scales, one per 256 blocks.
  *   mean     [1]      fp32 mean of all block absmax values.
+ * Without double quantization (the ablation the pages weigh it against, QX
+ * "Double Quantization"): code8 = NULL, s2 [n*k/64] holds every block's fp32
+ * absmax and mean is not read (may be NULL); then c'_b = s2[b].
  *   codebook [16]     fp32 NF4 levels, ascending (from
  *                     qlora_build_nf4_codebook, copied to the device).
  * Block b's scale is c'_b = RN32(RN32(fp8(code8[b]) * s2[b/256]) + mean[0])
@@ -116,6 +119,22 @@ qlora_status qlora_build_nf4_codebook(float *levels_out);
  * Returns 0 if k % 64 != 0 or a size is not positive. */
 size_t qlora_nf4_packed_bytes(int64_t n, int64_t k);
 
+/* The same with double_quant = 1; with double_quant = 0 the form without
+ * double quantization (codes + one fp32 scale per block). 0 on bad arguments. */
+size_t qlora_nf4_storage_bytes(int64_t n, int64_t k, int double_quant);
+
+/*
+ * The 16 levels of the uniform INT4 grid, the ablation the pages contrast
+ * NF4 with (QQ "NF4: a 4-bit format matched to weight statistics": evenly
+ * spaced code points), into levels_out (host, 16 floats): (i - 7) / 7 rounded
+ * once to fp32, i = 0..15 -- -1 at index 0, exactly 0 at index 7 (the level
+ * all-zero blocks and padding use), +1 at index 14; 8/7 at index 15 is never
+ * chosen for absmax-scaled weights. Any 16 ascending levels with an exact 0
+ * at index 7 can serve as a codebook. Pure host code.
+ * Errors: INVALID_ARG if levels_out is NULL.
+ */
+qlora_status qlora_build_uniform4_codebook(float *levels_out);
+
 /* Workspace bytes qlora_quantize_nf4 needs for an [n, k] weight (0 on bad shape). */
 size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
 
@@ -132,6 +151,7 @@ size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
  *   d_b   = RN32(c_b - mean); s2_j = RN32(max |d_b| over run j / 448);
  *   code8 = E4M3 pattern of the finite E4M3 value nearest to d_b / s2_j, ties
  *           to the lower value, -0 never produced; s2_j = 0 gives 0x00.
+ * With out->code8 = NULL the second level is skipped: s2[b] = c_b.
  * ws (device) must hold qlora_quantize_workspace_bytes(n, k) bytes. The result
  * is deterministic and independent of the launch configuration.
  * Errors: INVALID_ARG (NULL/misaligned pointers, bad dtype), SHAPE (k % 64,

@@ -47,11 +47,34 @@ def test_host_codebook_matches_oracle_bitwise(q):
     assert q.raw().qlora_build_nf4_codebook(None) == -1
 
 
+def test_uniform_codebook_matches_oracle_bitwise(q):
+    lv = np.array(q.build_uniform4_codebook(), dtype=np.float32)
+    assert np.array_equal(lv.view(np.uint32), nf4.uniform4_levels().view(np.uint32))
+    assert q.raw().qlora_build_uniform4_codebook(None) == -1
+
+
 @pytest.mark.parametrize("n,k", [(1024, 1024), (4096, 4096), (11008, 4096), (4096, 11008), (8192, 28672),
                                  (3, 64), (5, 192), (22016, 8192)])
 def test_packed_bytes_agree_with_oracle(q, n, k):
     assert q.nf4_packed_bytes(n, k) == nf4.packed_bytes(n, k)
+    assert q.nf4_packed_bytes(n, k, double_quant=False) == nf4.packed_bytes(n, k, double_quant=False)
     assert q.quantize_workspace_bytes(n, k) > 0
+
+
+def test_weight_without_double_quant_needs_no_code8_or_mean(q):
+    """code8 = NULL selects the form without double quantization (mean is not
+    read, may be NULL); with code8 set, mean is required. Checked on the host
+    with M = 0, which returns before any launch."""
+    lib = q.raw()
+    p = ctypes.c_void_p(1 << 24)
+    base = 1 << 20
+    nodq = q._Weight(64, 128, base, None, base + 8192, None, base + 16384)
+    assert lib.qlora_linear_fwd(ctypes.byref(nodq), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == 0
+    half = q._Weight(64, 128, base, base + 4096, base + 8192, None, base + 16384)
+    assert lib.qlora_linear_fwd(ctypes.byref(half), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == -1
+    nos2 = q._Weight(64, 128, base, None, None, None, base + 16384)
+    assert lib.qlora_linear_fwd(ctypes.byref(nos2), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == -1
+    assert lib.qlora_nf4_storage_bytes(64, 128, 2) == 0
 
 
 def test_size_queries_reject_bad_shapes(q):

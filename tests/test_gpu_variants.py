@@ -1,0 +1,122 @@
+"""GPU parity of the ablation variants: the uniform INT4 grid and the
+encoding without double quantization ("QLoRA: Quantized Low-Rank Adaptation"
+(completesystemdesign.dev), "NF4: a 4-bit format matched to weight
+statistics"; "QLoRA Explained ..." (gamut.so), "Double Quantization").
+
+The kernels take the 16 levels from the weight's codebook and decode either
+scale form, so each variant runs the same kernels as NF4 with double
+quantization. For NF4 without double quantization and for the uniform grid
+with and without it:
+* the encoding is compared bit for bit with the oracle's (codes; code8, s2,
+  mean, or the fp32 block scales) and so is every dequantized bf16 weight;
+* the layer (qlora_linear_fwd / _bwd) on the GEMV, fused and expanded paths
+  against the fp64 oracle over the variant's own dequantized weight (relative
+  Frobenius error <= 2e-3);
+* the adapter merge within the merge's bracket bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from bit_nf4_quantized_02_amd import synth
+from oracle import linear as olin
+from oracle import nf4 as onf4
+
+from gpu_util import TOL, bits16, f32, report, say
+from test_gpu_merge import _bracket
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [("nf4", False), ("uniform", True), ("uniform", False)]
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_nf4_quantized_02_amd import qlora
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return qlora
+
+
+def _levels(grid):
+    return onf4.nf4_levels() if grid == "nf4" else onf4.uniform4_levels()
+
+
+def _encode(q, W, grid, dq):
+    cb = q.build_nf4_codebook() if grid == "nf4" else q.build_uniform4_codebook()
+    gw = q.quantize_nf4(W.cuda(), codebook=torch.tensor(cb, dtype=torch.float32, device="cuda"), double_quant=dq)
+    ow = onf4.NF4Weight(W.float().numpy(), _levels(grid), double_quant=dq)
+    return gw, ow
+
+
+@pytest.mark.parametrize("grid,dq", VARIANTS)
+@pytest.mark.parametrize("n,k", [(37, 192), (300, 4096), (257, 320)])
+def test_encode_and_dequant_bitwise(q, grid, dq, n, k):
+    say(f"case: encode {grid} double_quant={dq} n={n} k={k}")
+    W = synth.weight_bf16(n, k, 0.02, 71, n, k).float()
+    W[n // 2, 64:128] = 0.0                       # an all-zero block
+    W = W.to(torch.bfloat16)
+    gw, ow = _encode(q, W, grid, dq)
+    wd = q.dequant(gw)
+    torch.cuda.synchronize()
+    assert np.array_equal(gw.codes.cpu().numpy(), ow.packed), "packed codes differ"
+    if dq:
+        assert np.array_equal(gw.code8.cpu().numpy(), ow.code8), "code8 differs"
+        assert np.array_equal(gw.s2.cpu().numpy().view(np.uint32), ow.s2.view(np.uint32)), "s2 differs"
+        assert gw.mean.cpu().numpy().view(np.uint32)[0] == np.float32(ow.mean).view(np.uint32)
+    else:
+        assert gw.code8 is None and gw.mean is None
+        assert np.array_equal(gw.s2.cpu().numpy().view(np.uint32), ow.s2.view(np.uint32)), "block scales differ"
+    assert np.array_equal(bits16(wd), ow.dequant_bits()), "dequantized bf16 differs"
+    assert gw.nbytes() == onf4.packed_bytes(n, k, double_quant=dq)
+
+
+@pytest.mark.parametrize("grid,dq", VARIANTS)
+@pytest.mark.parametrize("m", [4, 64, 512])
+def test_layer_on_every_path(q, grid, dq, m):
+    n, k, r, s = 520, 640, 16, 2.0
+    paths = (q.linear_path(m, n, k, r, False), q.linear_path(m, n, k, r, True))
+    say(f"case: layer {grid} double_quant={dq} M={m} N={n} K={k} r={r} paths fwd/bwd={paths}")
+    li = synth.linear_inputs(81, m, 0, n, k, m, r, s, sigma=0.02)
+    gw, ow = _encode(q, li.W, grid, dq)
+    X, dY, A, B = li.X.cuda(), li.dY.cuda(), li.A.cuda(), li.B.cuda()
+    Y, T = q.linear_fwd(gw, X, A, B, s)
+    dX, dA, dB = q.linear_bwd(gw, X, T, dY, A, B, s)
+    torch.cuda.synchronize()
+    Wd = ow.dequant().astype(np.float64)
+    Xo, Ao, Bo, dYo = (t.float().numpy().astype(np.float64) for t in (li.X, li.A, li.B, li.dY))
+    Yr, _ = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
+    dXr, dAr, dBr, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
+    assert report("Y", f32(Y), Yr) <= TOL
+    assert report("dX", f32(dX), dXr) <= TOL
+    assert report("dA", f32(dA), dAr, floor=False) <= TOL
+    assert report("dB", f32(dB), dBr, floor=False) <= TOL
+
+
+@pytest.mark.parametrize("grid,dq", VARIANTS)
+def test_merge(q, grid, dq):
+    n, k, r, s = 200, 320, 8, 2.0
+    say(f"case: merge {grid} double_quant={dq} n={n} k={k} r={r}")
+    li = synth.linear_inputs(82, 0, 0, n, k, 1, r, s, sigma=0.02)
+    gw, ow = _encode(q, li.W, grid, dq)
+    m16 = q.adapter_merge(gw, li.A.cuda(), li.B.cuda(), s)
+    torch.cuda.synchronize()
+    _bracket(f32(m16).astype(np.float64), ow.dequant().astype(np.float64), li.A.float().numpy(),
+             li.B.float().numpy(), s, r, "bf16")
+
+
+def test_decode_gemv_at_full_size_without_double_quant(q):
+    """The 70B-class down weight (8192 x 28672, 8 waves per workgroup) in the
+    uniform grid without double quantization at M = 16: every output."""
+    n, k, r, M = 8192, 28672, 16, 16
+    say(f"case: decode GEMV uniform, no double quant, {n}x{k} M={M}")
+    W = synth.weight_bf16(n, k, 0.015, 83, 0, 0)
+    gw, ow = _encode(q, W, "uniform", False)
+    li = synth.linear_inputs(83, 0, 1, 1, k, M, r, 1.0)
+    X, A = li.X.cuda(), li.A.cuda()
+    B = synth.lora_B(n, r, 83, 0, synth.T_B).cuda()
+    Y, T = q.linear_fwd(gw, X, A, B, 1.0)
+    torch.cuda.synchronize()
+    Yr, _ = olin.linear_fwd(li.X.float().numpy().astype(np.float64), ow.dequant().astype(np.float64),
+                            li.A.float().numpy().astype(np.float64), B.float().cpu().numpy().astype(np.float64), 1.0)
+    assert report("Y", f32(Y), Yr) <= TOL
