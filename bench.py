@@ -25,7 +25,10 @@ with a bf16 base (the step's calls minus the two weight expansions, over the
 operands they leave in place) with QLoRA's slowdown over it, and the AdamW
 step over all adapter parameters with the moments in device memory and in
 pinned host memory ("paged"), and the offline encode (quantize + double
-quantization) and the bf16 dequant of each weight shape, each timed alone.
+quantization) and the bf16 dequant of each weight shape, each timed alone,
+and the storage-format ablations (NF4 or a uniform INT4 grid, with or
+without double quantization) on the first weight: bits per weight,
+reconstruction error and the layer step with each.
 
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
@@ -538,6 +541,44 @@ def encode_rows(wl: Workload, q, reps: int = 10):
     return rows
 
 
+def variant_rows(wl: Workload, q, reps: int = 10):
+    """The ablations of the storage format on the workload's first weight:
+    NF4 or the uniform INT4 grid, with or without double quantization. For
+    each: bits per weight, the relative Frobenius error of its dequantized
+    bf16 weight against the bf16 weight it encodes, and the layer calls of
+    one step (forward, and backward where the workload has one) timed as a
+    region with that encoding, on the same activations and adapter."""
+    p = wl.plans[0]
+    if p.li.W is None:
+        return {}
+    W = p.li.W.to("cuda")
+    Wf = W.double()
+    lib = q.raw()
+    st = q._stream()
+    P = q._ptr
+    out = {}
+    for grid in ("nf4", "uniform"):
+        cb = torch.tensor(q.build_nf4_codebook() if grid == "nf4" else q.build_uniform4_codebook(),
+                          dtype=torch.float32, device="cuda")
+        for dq in (True, False):
+            w = q.quantize_nf4(W, codebook=cb, double_quant=dq)
+            err = float(torch.linalg.norm(q.dequant(w).double() - Wf) / torch.linalg.norm(Wf))
+            wst = w.struct()
+            wref = q.ctypes.byref(wst)
+            lw, lwn = P(p.lws), p.lws.numel()
+            calls = [q.Call("qlora_linear_fwd", wref, P(p.X), p.m, P(p.A), P(p.B), p.r, p.s, P(p.Y), P(p.T), lw,
+                            lwn, st, keep=(wst,))]
+            if p.api_bwd is not None:
+                calls.append(q.Call("qlora_linear_bwd", wref, P(p.X), P(p.T), P(p.dY), p.m, P(p.A), P(p.B), p.r,
+                                    p.s, P(p.dX), P(p.dA), P(p.dB), 0, lw, lwn, st, keep=(wst,)))
+            us = _region_us(lambda: [cl() for cl in calls], reps)
+            out[f"{grid}_{'dq' if dq else 'no_dq'}"] = dict(
+                bits_per_weight=round(8.0 * w.nbytes() / (w.n * w.k), 4), weight_relerr=round(err, 5),
+                step_us=round(us, 2))
+            del w
+    return out
+
+
 def adamw_rows(wl: Workload, q, reps: int = 20):
     """The AdamW step over every adapter parameter of the workload (A and B
     of each linear, fp32 masters, the step's dA / dB as gradients, bf16 copy
@@ -706,6 +747,7 @@ def main():
     lora_ms = lora_bf16_base(wl, q, args.steps)
     adamw = adamw_rows(wl, q)
     encode = encode_rows(wl, q)
+    variants = variant_rows(wl, q)
     for row in merges.values():
         row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
         row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
@@ -768,6 +810,7 @@ def main():
         "adapter_merge_bf16": merges,
         "adamw_step": adamw,
         "encode": encode,
+        "format_variants": variants,
         "lora_bf16_base": None if lora_ms is None else {
             "ms_per_step": round(lora_ms[0], 4),
             "tflops": round(wl.flops / (lora_ms[0] * 1e-3) / 1e12, 2),
