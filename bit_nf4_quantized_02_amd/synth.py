@@ -27,7 +27,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-T_W, T_X, T_A, T_B, T_DY = 0, 1, 2, 3, 4
+T_W, T_X, T_A, T_B, T_DY, T_MASK = 0, 1, 2, 3, 4, 5
 
 
 def rng(*seed: int) -> np.random.Generator:
@@ -81,6 +81,13 @@ def device_uniform_bf16(shape, bound: float, *seed: int, device: str = "cuda") -
     w = torch.empty(shape, dtype=torch.float32, device=device)
     w.uniform_(-bound, bound, generator=g)
     return w.to(torch.bfloat16)
+
+
+def dropout_mask(m: int, k: int, p: float, *seed: int) -> torch.Tensor:
+    """uint8 [m, k] keep mask of the adapter-input dropout: 1 with probability
+    1 - p, else 0 (the caller draws it; kernels only read it)."""
+    g = rng(*seed)
+    return torch.from_numpy((g.random((m, k)) >= p).astype(np.uint8))
 
 
 def lora_A(r: int, k: int, *seed: int) -> torch.Tensor:

@@ -15,7 +15,7 @@ Modules
                    INT4 grid and the encoding without double quantization
                    (ablations).
 ``oracle.linear``  fp64 forward and backward of the frozen-base linear with the
-                   LoRA branch.
+                   LoRA branch, plain and with dropout on the branch's input.
 ``oracle.merge``   the adapter folded into a dequantized copy of the base (and
                    taken out again), exact in fp64, rounded once.
 ``oracle.adamw``   the AdamW step on the adapter and its learning-rate schedule.

@@ -13,7 +13,7 @@ Sources:
   precision.
 * "QLoRA Explained ..." (gamut.so), "Step 3: Configure and Apply LoRA
   Adapters" and "QLoRA Hyperparameter Quick Reference": rank r, alpha, no
-  bias.
+  bias, LoRA dropout 0.05.
 
 Notation: W' [N, K] is the dequantized bf16 weight (``oracle.nf4.dequant``),
 X [M, K], A [r, K], B [N, r], dY [M, N]; s = alpha / r (reading: the usual
@@ -94,3 +94,39 @@ def bf16_floor(Zref) -> float:
     u = z32.view(np.uint32).astype(np.uint64)
     r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
     return relerr(r, z)
+
+
+def linear_fwd_dropout(X, Wd, A, B, s, mask, keep_scale):
+    """The forward with dropout on the adapter's input (reading: the usual
+    inverted dropout of a LoRA branch; the pages give the rate, 0.05, not the
+    formula). D = mask * keep_scale elementwise on X, mask in {0, 1} drawn by
+    the caller, keep_scale = 1 / (1 - p):
+
+        Y = X W'^T + s ((X . D) A^T) B^T
+
+    The base sees the undropped X. Returns (Y, Td) with Td = (X . D) A^T."""
+    X, Wd, A, B = _f64(X), _f64(Wd), _f64(A), _f64(B)
+    D = _f64(mask) * float(keep_scale)
+    s = float(s)
+    Td = (X * D) @ A.T
+    Y = X @ Wd.T + s * (Td @ B.T)
+    return Y, Td
+
+
+def linear_bwd_dropout(X, Wd, A, B, s, dY, mask, keep_scale):
+    """Gradients of <dY, Y> for ``linear_fwd_dropout`` (W' frozen):
+
+    U  = dY B
+    dX = dY W' + s (U A) . D
+    dA = s U^T (X . D)
+    dB = s dY^T Td,   Td = (X . D) A^T
+    Returns (dX, dA, dB, U)."""
+    X, Wd, A, B, dY = _f64(X), _f64(Wd), _f64(A), _f64(B), _f64(dY)
+    D = _f64(mask) * float(keep_scale)
+    s = float(s)
+    Xd = X * D
+    U = dY @ B
+    dX = dY @ Wd + s * ((U @ A) * D)
+    dA = s * (U.T @ Xd)
+    dB = s * (dY.T @ (Xd @ A.T))
+    return dX, dA, dB, U
