@@ -77,6 +77,7 @@ hipError_t do_grad(const uint16_t* P, int64_t M, int64_t C, const float* Q, int 
 
 // ---- whole-layer workspaces (layouts shared by the size query and the call)
 struct FwdWs {
+  uint16_t* Xd = nullptr;  // dropout: X . mask
   float* T = nullptr;
   uint16_t* TS = nullptr;
   void* proj = nullptr;
@@ -84,8 +85,10 @@ struct FwdWs {
   float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
 };
 
-size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o) {
+size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o,
+              bool dropout = false) {
   const int path = path_of(M, n, k, r, false);
+  if (dropout && r > 0) o.Xd = cv.take<uint16_t>((size_t)M * k * 2);
   if (r > 0) {
     if (path == QLORA_PATH_GEMV) {
       if (!have_tsave) o.T = cv.take<float>((size_t)M * r * 4);
@@ -103,6 +106,7 @@ size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& c
 }
 
 struct BwdWs {
+  uint16_t* Xd = nullptr;  // dropout: X . mask
   float* T = nullptr;
   float* U = nullptr;
   uint16_t* US = nullptr;
@@ -112,7 +116,9 @@ struct BwdWs {
   float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
 };
 
-size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o) {
+size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o,
+              bool dropout = false) {
+  if (dropout && r > 0) o.Xd = cv.take<uint16_t>((size_t)M * k * 2);
   if (r > 0) {
     if (!have_tsaved) o.T = cv.take<float>((size_t)M * r * 4);
     o.U = cv.take<float>((size_t)M * r * 4);
@@ -208,16 +214,25 @@ qlora_status qlora_adapter_unmerge(const void* merged, int64_t n, int64_t k, con
                                  static_cast<hipStream_t>(stream)));
 }
 
-size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
+static size_t linear_ws_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd, bool dropout) {
   if (M < 0 || n < 1 || k < 1 || k % QLORA_BLOCK || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (is_bwd != 0 && is_bwd != 1) return 0;
   if (M == 0) return 0;
   Carver cv(nullptr);
   if (!is_bwd) {
     FwdWs o;
-    return fwd_ws(M, n, k, r, /*have_tsave=*/false, cv, o);
+    return fwd_ws(M, n, k, r, /*have_tsave=*/false, cv, o, dropout);
   }
   BwdWs o;
-  return bwd_ws(M, n, k, r, /*have_tsaved=*/false, cv, o);
+  return bwd_ws(M, n, k, r, /*have_tsaved=*/false, cv, o, dropout);
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
+  return linear_ws_bytes(M, n, k, r, is_bwd, false);
+}
+
+size_t qlora_linear_dropout_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
+  return linear_ws_bytes(M, n, k, r, is_bwd, true);
 }
 
 int qlora_lowrank_split_cols(int r) { return (r < 0 || r > QLORA_MAX_RANK) ? 0 : lora_extra_cols(r); }
@@ -338,8 +353,14 @@ qlora_status qlora_lowrank_grad(const void* P, int64_t M, int64_t C, const float
                             static_cast<hipStream_t>(stream)));
 }
 
-qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A, const void* B,
-                              int r, float scale, void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// The layer calls with and without dropout on the adapter's input (mask NULL:
+// none). With dropout the branch reads Xd = X . mask and keep_scale folds
+// into the branch's scale: T_save receives Xd A^T.
+static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A,
+                                    const void* B, int r, float scale, const uint8_t* mask, float keep_scale,
+                                    void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream) {
   qlora_status s = check_weight(w);
   if (s != QLORA_OK) return s;
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
@@ -347,29 +368,38 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t 
   if (!X || !Y || !aligned16(X) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
   if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
   if (T_save && !aligned16(T_save)) return QLORA_ERR_INVALID_ARG;
+  const bool drop = mask != nullptr && r > 0;
   {
     Carver probe(nullptr);
     FwdWs tmp;
-    const size_t need = fwd_ws(M, w->n, w->k, r, T_save != nullptr, probe, tmp);
+    const size_t need = fwd_ws(M, w->n, w->k, r, T_save != nullptr, probe, tmp, drop);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
   FwdWs o;
-  fwd_ws(M, w->n, w->k, r, T_save != nullptr, cv, o);
+  fwd_ws(M, w->n, w->k, r, T_save != nullptr, cv, o, drop);
   const Nf4View v = view_of(w);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* a = static_cast<const uint16_t*>(A);
   const uint16_t* b = static_cast<const uint16_t*>(B);
   uint16_t* y = static_cast<uint16_t*>(Y);
   hipError_t e = hipSuccess;
+  // the branch's input and scale
+  const uint16_t* xb = x;
+  float sb = scale;
+  if (drop) {
+    e = launch_dropout_apply(x, mask, o.Xd, M * w->k, st);
+    xb = o.Xd;
+    sb = scale * keep_scale;
+  }
   const int path = path_of(M, w->n, w->k, r, false);
   if (path == QLORA_PATH_GEMV) {
     float* T = T_save ? T_save : o.T;
-    if (r > 0) e = do_project(x, M, w->k, a, 0, r, scale, T, nullptr, o.proj, st);
-    if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, scale, y, st);
+    if (r > 0 && e == hipSuccess) e = do_project(xb, M, w->k, a, 0, r, sb, T, nullptr, o.proj, st);
+    if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, sb, y, st);
   } else {
-    if (r > 0) e = do_project(x, M, w->k, a, 0, r, scale, T_save, o.TS, o.proj, st);
+    if (r > 0 && e == hipSuccess) e = do_project(xb, M, w->k, a, 0, r, sb, T_save, o.TS, o.proj, st);
     if (path == QLORA_PATH_FUSED) {
       if (e == hipSuccess) e = launch_gemm_fwd(v, x, M, o.TS, b, r, y, st);
     } else {
@@ -380,9 +410,10 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t 
   return hip_status(e);
 }
 
-qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const float* T_saved, const void* dY,
-                              int64_t M, const void* A, const void* B, int r, float scale, void* dX, float* dA,
-                              float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, const float* T_saved,
+                                    const void* dY, int64_t M, const void* A, const void* B, int r, float scale,
+                                    const uint8_t* mask, float keep_scale, void* dX, float* dA, float* dB,
+                                    int accumulate, void* ws, size_t ws_bytes, void* stream) {
   qlora_status s = check_weight(w);
   if (s != QLORA_OK) return s;
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
@@ -391,6 +422,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const fl
   if (!dY || !aligned16(dY)) return QLORA_ERR_INVALID_ARG;
   if (dX && !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
   if (r == 0) { dA = nullptr; dB = nullptr; }
+  const bool drop = mask != nullptr && r > 0;
   const bool need_x = (dA != nullptr) || (dB != nullptr && T_saved == nullptr);
   if (need_x && (!X || !aligned16(X))) return QLORA_ERR_INVALID_ARG;
   if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
@@ -399,40 +431,82 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const fl
   {
     Carver probe(nullptr);
     BwdWs tmp;
-    const size_t need = bwd_ws(M, w->n, w->k, r, T_saved != nullptr, probe, tmp);
+    const size_t need = bwd_ws(M, w->n, w->k, r, T_saved != nullptr, probe, tmp, drop);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
   BwdWs o;
-  bwd_ws(M, w->n, w->k, r, T_saved != nullptr, cv, o);
+  bwd_ws(M, w->n, w->k, r, T_saved != nullptr, cv, o, drop);
   const Nf4View v = view_of(w);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* dy = static_cast<const uint16_t*>(dY);
   const uint16_t* a = static_cast<const uint16_t*>(A);
   const uint16_t* b = static_cast<const uint16_t*>(B);
   hipError_t e = hipSuccess;
+  const uint8_t* dmask = drop ? mask : nullptr;  // dX: dropout on its low-rank term
   if (r > 0 && (dX || dA)) e = do_project(dy, M, w->n, b, 1, r, scale, o.U, dX ? o.US : nullptr, o.proj, st);
   if (e == hipSuccess && dX) {
     if (path_of(M, w->n, w->k, r, true) == QLORA_PATH_EXPANDED) {
       e = launch_expand(v, a, r, true, o.F, st);
       if (e == hipSuccess)
         e = launch_gemm_bf16(dy, M, w->n, r > 0 ? o.US : nullptr, lora_extra_cols(r), o.F, w->k,
-                             static_cast<uint16_t*>(dX), o.part, st);
+                             static_cast<uint16_t*>(dX), o.part, st, dmask, keep_scale);
     } else {
-      e = launch_gemm_dx(v, dy, M, r > 0 ? o.US : nullptr, a, r, static_cast<uint16_t*>(dX), st);
+      e = launch_gemm_dx(v, dy, M, r > 0 ? o.US : nullptr, a, r, static_cast<uint16_t*>(dX), st, dmask, keep_scale);
     }
   }
-  if (e == hipSuccess && dA) e = do_grad(x, M, w->k, o.U, r, scale, dA, 0, accumulate, o.grad, st);
+  // the branch's input and scale for the adapter gradients
+  const uint16_t* xb = x;
+  float sb = scale;
+  if (drop && need_x && e == hipSuccess) {
+    e = launch_dropout_apply(x, mask, o.Xd, M * w->k, st);
+    xb = o.Xd;
+  }
+  if (drop) sb = scale * keep_scale;
+  if (e == hipSuccess && dA) e = do_grad(xb, M, w->k, o.U, r, sb, dA, 0, accumulate, o.grad, st);
   if (e == hipSuccess && dB) {
     const float* T = T_saved;
     if (T == nullptr) {
-      e = do_project(x, M, w->k, a, 0, r, scale, o.T, nullptr, o.proj, st);
+      e = do_project(xb, M, w->k, a, 0, r, scale, o.T, nullptr, o.proj, st);
       T = o.T;
     }
-    if (e == hipSuccess) e = do_grad(dy, M, w->n, T, r, scale, dB, 1, accumulate, o.grad, st);
+    if (e == hipSuccess) e = do_grad(dy, M, w->n, T, r, sb, dB, 1, accumulate, o.grad, st);
   }
   return hip_status(e);
+}
+
+extern "C" {
+
+qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A, const void* B,
+                              int r, float scale, void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream) {
+  return linear_fwd_impl(w, X, M, A, B, r, scale, nullptr, 1.0f, Y, T_save, ws, ws_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const float* T_saved, const void* dY,
+                              int64_t M, const void* A, const void* B, int r, float scale, void* dX, float* dA,
+                              float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  return linear_bwd_impl(w, X, T_saved, dY, M, A, B, r, scale, nullptr, 1.0f, dX, dA, dB, accumulate, ws,
+                         ws_bytes, stream);
+}
+
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A,
+                                      const void* B, int r, float scale, const void* mask, float keep_scale,
+                                      void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream) {
+  if (M > 0 && r > 0 && (mask == nullptr || !aligned16(mask))) return QLORA_ERR_INVALID_ARG;
+  if (!(keep_scale >= 1.0f) || keep_scale == INFINITY) return QLORA_ERR_INVALID_ARG;
+  return linear_fwd_impl(w, X, M, A, B, r, scale, static_cast<const uint8_t*>(mask), keep_scale, Y, T_save, ws,
+                         ws_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const void* X, const float* T_saved, const void* dY,
+                                      int64_t M, const void* A, const void* B, int r, float scale, const void* mask,
+                                      float keep_scale, void* dX, float* dA, float* dB, int accumulate, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  if (M > 0 && r > 0 && (mask == nullptr || !aligned16(mask))) return QLORA_ERR_INVALID_ARG;
+  if (!(keep_scale >= 1.0f) || keep_scale == INFINITY) return QLORA_ERR_INVALID_ARG;
+  return linear_bwd_impl(w, X, T_saved, dY, M, A, B, r, scale, static_cast<const uint8_t*>(mask), keep_scale, dX,
+                         dA, dB, accumulate, ws, ws_bytes, stream);
 }
 
 qlora_status qlora_silu_mul_fwd(const void* G, const void* Up, void* H, int64_t count, void* stream) {

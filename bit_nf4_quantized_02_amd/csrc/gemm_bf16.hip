@@ -51,6 +51,9 @@ struct BfArgs {
   float* part;
   int64_t full, tail;
   int splits;
+  // dropout on the low-rank term (the masked kernel only): uint8 [M, nout]
+  const uint8_t* mask;
+  float keep_scale;
 };
 
 constexpr int kCopies = 32 / kWaves;  // 1 KB copies per wave per operand tile
@@ -180,6 +183,29 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
   step_barrier<0>();
 }
 
+// One step without copies in flight: fragments of (Ac, Bc) and their MFMAs.
+__device__ __forceinline__ void plain_step(const char* Ac, const char* Bc, int wave, f32x16 (&acc)[kTM][kTN]) {
+  const int lane = threadIdx.x & 63;
+  const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
+#pragma unroll
+  for (int kk = 0; kk < kBK / 16; ++kk) {
+    bf16x8 af[kTM], bfr[kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) af[i] = tile_frag(Ac, wm0 + i * 32, kk, lane);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) bfr[j] = tile_frag(Bc, wn0 + j * 32, kk, lane);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// kMask: dropout on the low-rank term. A workgroup whose step range holds the
+// low-rank steps runs them first (unpipelined, 1-4 steps), masks and scales
+// the accumulators, then runs its main steps as usual.
+template <bool kMask>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
   // direct copies from the one being read
@@ -227,12 +253,25 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  if (sbeg < nk) {  // (every split range is non-empty for the split counts split_plan picks)
+  int nk_end = nk;  // exclusive end of the pipelined range
+  if constexpr (kMask) {
+    if (nk > nk_main) {
+      for (int step = sbeg > nk_main ? sbeg : nk_main; step < nk; ++step) {
+        issue_step(rs, plan, step, nk_main, wave, As0, Bs0);
+        step_barrier<0>();
+        plain_step(As0, Bs0, wave, acc);
+        __syncthreads();  // every wave's reads done before the next copies land
+      }
+      mask_acc(acc, a.mask, a.keep_scale, a.M, a.nout, m0, n0, wm0, wn0, lane);
+      nk_end = nk_main;
+    }
+  }
+  if (sbeg < nk_end) {  // (every split range is non-empty for the split counts split_plan picks)
     issue_step(rs, plan, sbeg, nk_main, wave, As0, Bs0);
     step_barrier<0>();
-    for (int step = sbeg; step < nk; step += 2) {
-      bf16_step(rs, plan, step, nk, nk_main, wave, As0, Bs0, As1, Bs1, acc);
-      if (step + 1 < nk) bf16_step(rs, plan, step + 1, nk, nk_main, wave, As1, Bs1, As0, Bs0, acc);
+    for (int step = sbeg; step < nk_end; step += 2) {
+      bf16_step(rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc);
+      if (step + 1 < nk_end) bf16_step(rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc);
     }
   }
 
@@ -375,8 +414,11 @@ bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
-                            const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream) {
+                            const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
+                            const uint8_t* mask, float keep_scale) {
   BfArgs a{};
+  a.mask = mask;
+  a.keep_scale = keep_scale;
   a.act = act; a.M = M; a.kc = kc;
   a.act_x = split; a.kx = kx;
   a.f = f; a.ldf = cdiv(kc, (int64_t)kBK) * kBK + kx; a.nout = nout;
@@ -385,7 +427,11 @@ hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const ui
   a.full = sp.full; a.tail = sp.tail; a.splits = sp.splits;
   a.part = part;
   if (a.splits > 1 && part == nullptr) return hipErrorInvalidValue;
-  gemm_bf16_kernel<<<dim3((unsigned)(a.full + a.tail * a.splits)), kThreads, 0, stream>>>(a);
+  const dim3 grid((unsigned)(a.full + a.tail * a.splits));
+  if (mask != nullptr && kx > 0)
+    gemm_bf16_kernel<true><<<grid, kThreads, 0, stream>>>(a);
+  else
+    gemm_bf16_kernel<false><<<grid, kThreads, 0, stream>>>(a);
   if (a.splits > 1) {
     const int64_t groups = a.tail * (kBM * kBN / 4);
     gemm_bf16_reduce_kernel<<<dim3((unsigned)cdiv(groups, (int64_t)256)), 256, 0, stream>>>(

@@ -77,6 +77,9 @@ struct GemmArgs {
   // output [M, nout] bf16
   uint16_t* out;
   int64_t nout;
+  // dX only: dropout on the low-rank term, uint8 [M, nout] (NULL: none)
+  const uint8_t* mask;
+  float keep_scale;
 };
 
 // ------------------------------------------------------------ activation tile
@@ -384,26 +387,6 @@ __global__ __launch_bounds__(kThreads) void gemm_nf4_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  ActStage ast;
-  WStage wst[2];
-  const float mean = weight_mean(a.code8, a.mean);
-  // prologue: step 0 into buffer 0; step 1 activations and weights staged
-  if constexpr (kVec) {
-    issue_act_lds(a, m0, 0, nk_main, As[0]);
-  } else {
-    load_act<kVec>(a, m0, 0, nk_main, ast);
-  }
-  load_w<kDX>(a, n0, 0, wst[0]);
-  load_w<kDX>(a, n0, nk_main > 1 ? 1 : 0, wst[1]);
-  __syncthreads();  // lut
-  if constexpr (!kVec) {
-    store_act(As[0], ast);
-    load_act<kVec>(a, m0, nk_main > 1 ? 1 : 0, nk_main, ast);
-  }
-  store_w_all<kDX>(Bs[0], lut, wst[0], mean);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
   auto mfma_step = [&](const char* Ac, const char* Bc, auto&& between) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -428,6 +411,44 @@ __global__ __launch_bounds__(kThreads) void gemm_nf4_kernel(GemmArgs a) {
     }
   };
 
+  ActStage ast;
+  WStage wst[2];
+  const float mean = weight_mean(a.code8, a.mean);
+  // low-rank extra steps (1 or 2 for r <= 64): not pipelined
+  auto lowrank_steps = [&]() {
+    for (int xs = 0; xs < nk - nk_main; ++xs) {
+      load_act<kVec>(a, m0, nk_main + xs, nk_main, ast);
+      store_act(As[0], ast);
+      store_lowrank_w<kDX>(Bs[0], a, n0, xs);
+      __syncthreads();
+      mfma_step(As[0], Bs[0], [](int) {});
+      __syncthreads();
+    }
+  };
+  // dropout (dX): the low-rank term alone first, masked and scaled, then the
+  // main contraction on top of it
+  const bool masked = kDX && a.mask != nullptr && nk > nk_main;
+  if (masked) {
+    lowrank_steps();
+    mask_acc(acc, a.mask, a.keep_scale, a.M, a.nout, m0, n0, wm0, wn0, lane);
+  }
+  // prologue: step 0 into buffer 0; step 1 activations and weights staged
+  if constexpr (kVec) {
+    issue_act_lds(a, m0, 0, nk_main, As[0]);
+  } else {
+    load_act<kVec>(a, m0, 0, nk_main, ast);
+  }
+  load_w<kDX>(a, n0, 0, wst[0]);
+  load_w<kDX>(a, n0, nk_main > 1 ? 1 : 0, wst[1]);
+  __syncthreads();  // lut
+  if constexpr (!kVec) {
+    store_act(As[0], ast);
+    load_act<kVec>(a, m0, nk_main > 1 ? 1 : 0, nk_main, ast);
+  }
+  store_w_all<kDX>(Bs[0], lut, wst[0], mean);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
   // The stage index and buffers are compile-time choices (loop unrolled by 2),
   // so staging registers are never indexed dynamically. Loads for steps past
   // the last one use a clamped step index (re-reading the last step); the LDS
@@ -439,15 +460,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nf4_kernel(GemmArgs a) {
       pipelined_step<kDX, kVec>(a, step + 1, nk_main, m0, n0, As1, Bs1, As0, Bs0, lut, mean, wst[1], wst[0], ast,
                                 acc);
   }
-  // low-rank extra steps (1 or 2 for r <= 64): not pipelined
-  for (int xs = 0; xs < nk - nk_main; ++xs) {
-    load_act<kVec>(a, m0, nk_main + xs, nk_main, ast);
-    store_act(As[0], ast);
-    store_lowrank_w<kDX>(Bs[0], a, n0, xs);
-    __syncthreads();
-    mfma_step(As[0], Bs[0], [](int) {});
-    __syncthreads();
-  }
+  if (!masked) lowrank_steps();
 
   // D layout: lane -> column (lane & 31); register v -> row 8 (v/4) + 4 (lane/32) + v%4
 #pragma unroll
@@ -481,8 +494,10 @@ hipError_t launch_gemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const
 }
 
 hipError_t launch_gemm_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const uint16_t* US, const uint16_t* A,
-                          int r, uint16_t* dX, hipStream_t stream) {
+                          int r, uint16_t* dX, hipStream_t stream, const uint8_t* mask, float keep_scale) {
   GemmArgs a{};
+  a.mask = mask;
+  a.keep_scale = keep_scale;
   a.act = dY; a.lda = w.n; a.M = M; a.kc = w.n;
   a.act_x = US; a.kx = lora_extra_cols(r);
   a.codes = w.codes; a.code8 = w.code8; a.s2 = w.s2; a.mean = w.mean; a.codebook = w.codebook;

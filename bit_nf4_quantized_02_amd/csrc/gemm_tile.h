@@ -119,5 +119,25 @@ __device__ __forceinline__ void store_acc_bf16(const f32x16 (&acc)[kTM][kTN], ui
     }
 }
 
+// Dropout on the low-rank term of a tile: while the accumulators hold only
+// that term (its contraction steps run first), each output (m, n) is
+// multiplied by keep_scale where mask[m, n] is set and cleared where it is
+// not (mask: uint8 [M, N], row-major).
+__device__ __forceinline__ void mask_acc(f32x16 (&acc)[kTM][kTN], const uint8_t* __restrict__ mask, float keep_scale,
+                                         int64_t M, int64_t N, int64_t m0, int64_t n0, int wm0, int wn0, int lane) {
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const int64_t n = n0 + wn0 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const bool keep = m < M && n < N && mask[m * N + n] != 0;
+        acc[i][j][v] = keep ? acc[i][j][v] * keep_scale : 0.0f;
+      }
+    }
+}
+
 }  // namespace gt
 }  // namespace qlora

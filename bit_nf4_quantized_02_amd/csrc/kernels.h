@@ -61,7 +61,8 @@ hipError_t launch_gemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const
 
 // dX = RN_bf16(dY W' + [sU_hi | sU_lo] [A ; A]): fused transposed dequant + MFMA GEMM.
 hipError_t launch_gemm_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const uint16_t* US,
-                          const uint16_t* A, int r, uint16_t* dX, hipStream_t stream);
+                          const uint16_t* A, int r, uint16_t* dX, hipStream_t stream,
+                          const uint8_t* mask = nullptr, float keep_scale = 1.0f);
 
 // Expanded bf16 operand of the plain GEMM (forward [n, k + xc], or dX
 // [k, np + xc] with np = n rounded up to 64), LoRA factor appended.
@@ -80,8 +81,16 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
 bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout);
 int gemm_bf16_splits(int64_t M, int64_t kc, int kx, int64_t nout);
 size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout);
+// mask (uint8 [M, nout], may be NULL): dropout on the low-rank term, which is
+// multiplied by keep_scale where mask is set and dropped where it is not,
+// before the main contraction is added (one rounding of the whole sum).
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
-                            const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream);
+                            const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
+                            const uint8_t* mask = nullptr, float keep_scale = 1.0f);
+
+// Xd = X . mask (count elements, a multiple of 8; 16-byte aligned buffers).
+hipError_t launch_dropout_apply(const uint16_t* X, const uint8_t* mask, uint16_t* Xd, int64_t count,
+                                hipStream_t stream);
 
 // Adapter merge: out = round(W' + scale * B A) (w != NULL; bf16, or fp32 if
 // out_f32) or unmerge: out = RN_bf16(Wm - scale * B A) (w == NULL, Wm bf16).

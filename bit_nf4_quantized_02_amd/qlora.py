@@ -55,6 +55,10 @@ _SIGS = {
     "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
     "qlora_linear_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "qlora_linear_dropout_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
+    "qlora_linear_fwd_dropout": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_bwd_dropout": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _f, _vp, _vp, _vp, _int,
+                                         _vp, _sz, _vp]),
     "qlora_lowrank_split_cols": (_int, [_int]),
     "qlora_lowrank_project_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "qlora_lowrank_project": (_int, [_vp, _i64, _i64, _vp, _int, _int, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -225,9 +229,33 @@ def dequant(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch
 
 # --------------------------------------------------------------------------- linear
 
+def linear_dropout_workspace_bytes(M: int, n: int, k: int, r: int, is_bwd: bool) -> int:
+    return int(_lib.qlora_linear_dropout_workspace_bytes(M, n, k, r, int(bool(is_bwd))))
+
+
+def _mask_of(mask: torch.Tensor, M: int, k: int):
+    if mask.dtype != torch.uint8 or tuple(mask.shape) != (M, k) or not mask.is_contiguous() or not mask.is_cuda:
+        raise ValueError(f"mask: expected contiguous uint8 {(M, k)} on the GPU")
+    return _ptr(mask)
+
+
+def linear_fwd_dropout(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, scale: float,
+                       mask: torch.Tensor, keep_scale: float, **kw):
+    """Y = X W'^T + scale ((X . mask * keep_scale) A^T) B^T (qlora_linear_fwd_dropout);
+    the saved T is (X . mask) A^T.  Returns (Y, T)."""
+    return linear_fwd(w, X, A, B, scale, _dropout=(mask, keep_scale), **kw)
+
+
+def linear_bwd_dropout(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY: torch.Tensor,
+                       A: torch.Tensor | None, B: torch.Tensor | None, scale: float, mask: torch.Tensor,
+                       keep_scale: float, **kw):
+    """The gradients of linear_fwd_dropout (qlora_linear_bwd_dropout).  Returns (dX, dA, dB)."""
+    return linear_bwd(w, X, T, dY, A, B, scale, _dropout=(mask, keep_scale), **kw)
+
+
 def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, scale: float,
                Y: torch.Tensor | None = None, T: torch.Tensor | None = None, save_T: bool = True,
-               ws: torch.Tensor | None = None, stream=None):
+               ws: torch.Tensor | None = None, stream=None, _dropout=None):
     """Y = X W'^T + scale (X A^T) B^T.  Returns (Y, T) with T None unless saved."""
     M = X.shape[0]
     r = 0 if A is None else A.shape[0]
@@ -242,9 +270,18 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
         T = torch.empty((M, r), dtype=torch.float32, device=X.device)
     if T is not None:
         _need(T, torch.float32, (M, r), "T")
+    st = w.struct()
+    if _dropout is not None:
+        mp = _mask_of(_dropout[0], M, w.k)
+        if ws is None:
+            ws = _bytes(linear_dropout_workspace_bytes(M, w.n, w.k, r, False), X.device)
+        _check(_lib.qlora_linear_fwd_dropout(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), mp,
+                                             float(_dropout[1]), _ptr(Y), _ptr(T), _ptr(ws),
+                                             0 if ws is None else ws.numel(), _stream(stream)),
+               "qlora_linear_fwd_dropout")
+        return Y, T
     if ws is None:
         ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, False), X.device)
-    st = w.struct()
     _check(_lib.qlora_linear_fwd(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), _ptr(Y), _ptr(T),
                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_fwd")
     return Y, T
@@ -254,7 +291,7 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY:
                A: torch.Tensor | None, B: torch.Tensor | None, scale: float, need_dX: bool = True,
                need_dA: bool = True, need_dB: bool = True, dX: torch.Tensor | None = None,
                dA: torch.Tensor | None = None, dB: torch.Tensor | None = None, accumulate: bool = False,
-               ws: torch.Tensor | None = None, stream=None):
+               ws: torch.Tensor | None = None, stream=None, _dropout=None):
     """dX = dY W' + s (dY B) A;  dA = s (dY B)^T X;  dB = s dY^T T.  Returns (dX, dA, dB)."""
     M = dY.shape[0]
     r = 0 if A is None else A.shape[0]
@@ -279,9 +316,18 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY:
         _need(dA, torch.float32, (r, w.k), "dA")
     if dB is not None:
         _need(dB, torch.float32, (w.n, r), "dB")
+    st = w.struct()
+    if _dropout is not None:
+        mp = _mask_of(_dropout[0], M, w.k)
+        if ws is None:
+            ws = _bytes(linear_dropout_workspace_bytes(M, w.n, w.k, r, True), dev)
+        _check(_lib.qlora_linear_bwd_dropout(ctypes.byref(st), _ptr(X), _ptr(T), _ptr(dY), M, _ptr(A), _ptr(B), r,
+                                             float(scale), mp, float(_dropout[1]), _ptr(dX), _ptr(dA), _ptr(dB),
+                                             int(bool(accumulate)), _ptr(ws), 0 if ws is None else ws.numel(),
+                                             _stream(stream)), "qlora_linear_bwd_dropout")
+        return dX, dA, dB
     if ws is None:
         ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, True), dev)
-    st = w.struct()
     _check(_lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(T), _ptr(dY), M, _ptr(A), _ptr(B), r, float(scale),
                                  _ptr(dX), _ptr(dA), _ptr(dB), int(bool(accumulate)), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_bwd")

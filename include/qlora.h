@@ -209,6 +209,32 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const void *X, const fl
                               float scale, void *dX, float *dA, float *dB, int accumulate,
                               void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * The layer calls with dropout on the adapter's input, the LoRA dropout of the
+ * pages' training configuration ("QLoRA Explained ..." (gamut.so), "Step 3:
+ * Configure and Apply LoRA Adapters": 0.05):
+ *   Y  = RN_bf16( X W'^T + scale ((X . D) A^T) B^T ),   D = mask * keep_scale
+ *   dX = RN_bf16( dY W' + scale (U A) . D ),  U = dY B
+ *   dA = scale U^T (X . D),   dB = scale dY^T ((X . D) A^T)
+ * mask (device, uint8 [M, k], 16-byte aligned): nonzero keeps an element of X
+ * for the branch; the caller draws it. keep_scale (>= 1, finite) is
+ * 1 / (1 - p). The base product uses X itself. T_save / T_saved hold
+ * (X . mask) A^T (without keep_scale; the backward applies it). Workspace:
+ * qlora_linear_dropout_workspace_bytes (the plain one plus M k bf16).
+ * Everything else, including the kernels chosen, is as for qlora_linear_fwd /
+ * qlora_linear_bwd; r = 0 ignores mask.
+ * Errors: as those calls, and INVALID_ARG for a NULL or misaligned mask or a
+ * keep_scale below 1 or not finite.
+ */
+size_t qlora_linear_dropout_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd);
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const void *X, int64_t M, const void *A,
+                                      const void *B, int r, float scale, const void *mask, float keep_scale,
+                                      void *Y, float *T_save, void *ws, size_t ws_bytes, void *stream);
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const void *X, const float *T_saved,
+                                      const void *dY, int64_t M, const void *A, const void *B, int r, float scale,
+                                      const void *mask, float keep_scale, void *dX, float *dA, float *dB,
+                                      int accumulate, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * Building blocks. qlora_linear_fwd and qlora_linear_bwd are compositions of
  * the calls below (same kernels, same order); they are exported so a caller

@@ -227,3 +227,29 @@ def test_adamw_host_errors(q):
     assert lib.qlora_adamw_step(ctypes.c_void_p((1 << 24) + 4), None, p, p, p, 16, 1, 1e-3, 0.9, 0.999, 1e-8,
                                 0.0, None) == -1                                                      # misaligned
     del f
+
+
+def test_dropout_host_errors(q):
+    """NULL or misaligned masks and keep scales below 1 are rejected before any
+    launch; the dropout workspace is the plain one plus the masked copy of X."""
+    lib = q.raw()
+    W = _fake_weight(q)
+    p = ctypes.c_void_p(1 << 24)
+    big = 1 << 30
+    assert lib.qlora_linear_fwd_dropout(ctypes.byref(W), p, 16, p, p, 8, 1.0, None, 1.05, p, None, p, big, None) == -1
+    assert lib.qlora_linear_fwd_dropout(ctypes.byref(W), p, 16, p, p, 8, 1.0, ctypes.c_void_p((1 << 24) + 8), 1.05,
+                                        p, None, p, big, None) == -1
+    assert lib.qlora_linear_fwd_dropout(ctypes.byref(W), p, 16, p, p, 8, 1.0, p, 0.95, p, None, p, big, None) == -1
+    assert lib.qlora_linear_fwd_dropout(ctypes.byref(W), p, 16, p, p, 8, 1.0, p, float("inf"), p, None, p, big,
+                                        None) == -1
+    assert lib.qlora_linear_bwd_dropout(ctypes.byref(W), p, None, p, 16, p, p, 8, 1.0, None, 1.05, p, p, p, 0, p,
+                                        big, None) == -1
+    # M = 0 succeeds without a mask check on shapes
+    assert lib.qlora_linear_fwd_dropout(ctypes.byref(W), p, 0, p, p, 8, 1.0, p, 1.05, p, None, None, 0, None) == 0
+    for is_bwd in (0, 1):
+        plain = q.linear_workspace_bytes(4096, 4096, 4096, 16, bool(is_bwd))
+        drop = q.linear_dropout_workspace_bytes(4096, 4096, 4096, 16, bool(is_bwd))
+        assert drop == plain + 4096 * 4096 * 2
+    need = q.linear_dropout_workspace_bytes(64, 64, 128, 8, False)
+    assert lib.qlora_linear_fwd_dropout(ctypes.byref(W), p, 64, p, p, 8, 1.0, p, 1.05, p, None, p, need - 1,
+                                        None) == -4
