@@ -26,9 +26,10 @@ operands they leave in place) with QLoRA's slowdown over it, and the AdamW
 step over all adapter parameters with the moments in device memory and in
 pinned host memory ("paged"), and the offline encode (quantize + double
 quantization) and the bf16 dequant of each weight shape, each timed alone,
-and the storage-format ablations (NF4 or a uniform INT4 grid, with or
-without double quantization) on the first weight: bits per weight,
-reconstruction error and the layer step with each.
+the storage-format ablations (NF4 or a uniform INT4 grid, with or without
+double quantization) on the first weight: bits per weight, reconstruction
+error and the layer step with each, and the step with LoRA dropout (0.05)
+on every linear beside the plain step timed the same way.
 
 Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
 tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
@@ -579,6 +580,39 @@ def variant_rows(wl: Workload, q, reps: int = 10):
     return out
 
 
+def dropout_step(wl: Workload, q, steps: int):
+    """The step with LoRA dropout (p = 0.05, a seeded keep mask per linear):
+    every layer call replaced by its dropout form, everything else (SiLU)
+    as is, timed as one region like the step itself. Returns (ms per step,
+    ms per plain step timed the same way) or None where the workload has no
+    backward."""
+    if any(p.api_bwd is None for p in wl.plans) or wl.cid == 5:
+        return None
+    P = q._ptr
+    st = q._stream()
+    keep = 1.0 / (1.0 - 0.05)
+    swap = {}
+    hold = []
+    for i, p in enumerate(wl.plans):
+        mask = synth.dropout_mask(p.m, p.k, 0.05, wl.cid, i, synth.T_MASK).cuda()
+        ws = torch.empty(max(q.linear_dropout_workspace_bytes(p.m, p.n, p.k, p.r, True),
+                             q.linear_dropout_workspace_bytes(p.m, p.n, p.k, p.r, False), 256),
+                         dtype=torch.uint8, device="cuda")
+        hold += [mask, ws]
+        wref = q.ctypes.byref(p.wst)
+        swap[id(p.api_fwd)] = q.Call("qlora_linear_fwd_dropout", wref, P(p.X), p.m, P(p.A), P(p.B), p.r, p.s,
+                                     P(mask), keep, P(p.Y), P(p.T), P(ws), ws.numel(), st, keep=(p.wst,))
+        swap[id(p.api_bwd)] = q.Call("qlora_linear_bwd_dropout", wref, P(p.X), P(p.T), P(p.dY), p.m, P(p.A),
+                                     P(p.B), p.r, p.s, P(mask), keep, P(p.dX), P(p.dA), P(p.dB), 0, P(ws),
+                                     ws.numel(), st, keep=(p.wst,))
+    calls = [swap.get(id(cl), cl) for cl in wl.api]
+    for cl in calls:
+        cl()
+    out = (region_ms(calls, steps), region_ms(wl.api, steps))
+    del hold
+    return out
+
+
 def adamw_rows(wl: Workload, q, reps: int = 20):
     """The AdamW step over every adapter parameter of the workload (A and B
     of each linear, fp32 masters, the step's dA / dB as gradients, bf16 copy
@@ -748,6 +782,7 @@ def main():
     adamw = adamw_rows(wl, q)
     encode = encode_rows(wl, q)
     variants = variant_rows(wl, q)
+    drop = dropout_step(wl, q, args.steps)
     for row in merges.values():
         row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
         row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
@@ -811,6 +846,9 @@ def main():
         "adamw_step": adamw,
         "encode": encode,
         "format_variants": variants,
+        "lora_dropout": None if drop is None else {
+            "p": 0.05, "ms_per_step": round(drop[0], 4), "tflops": round(wl.flops / (drop[0] * 1e-3) / 1e12, 2),
+            "plain_ms_per_step_same_region": round(drop[1], 4), "overhead": round(drop[0] / drop[1], 3)},
         "lora_bf16_base": None if lora_ms is None else {
             "ms_per_step": round(lora_ms[0], 4),
             "tflops": round(wl.flops / (lora_ms[0] * 1e-3) / 1e12, 2),
