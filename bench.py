@@ -595,10 +595,8 @@ def dropout_step(wl: Workload, q, steps: int):
     hold = []
     for i, p in enumerate(wl.plans):
         mask = synth.dropout_mask(p.m, p.k, 0.05, wl.cid, i, synth.T_MASK).cuda()
-        ws = torch.empty(max(q.linear_dropout_workspace_bytes(p.m, p.n, p.k, p.r, True),
-                             q.linear_dropout_workspace_bytes(p.m, p.n, p.k, p.r, False), 256),
-                         dtype=torch.uint8, device="cuda")
-        hold += [mask, ws]
+        hold.append(mask)
+        ws = p.lws
         wref = q.ctypes.byref(p.wst)
         swap[id(p.api_fwd)] = q.Call("qlora_linear_fwd_dropout", wref, P(p.X), p.m, P(p.A), P(p.B), p.r, p.s,
                                      P(mask), keep, P(p.Y), P(p.T), P(ws), ws.numel(), st, keep=(p.wst,))

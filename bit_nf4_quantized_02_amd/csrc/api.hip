@@ -64,20 +64,19 @@ size_t grad_ws(int64_t M, int64_t C, int r) { return coldot_ws_bytes(M, C, r); }
 
 // T = P Q^T (q_layout 0, Q [r, C]) or P Q (q_layout 1, Q [C, r]); optional split.
 hipError_t do_project(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r, float scale,
-                      float* out, uint16_t* split, void* ws, hipStream_t st) {
-  return launch_rowdot(P, M, C, Q, q_layout, r, out, split, scale, static_cast<float*>(ws), st);
+                      float* out, uint16_t* split, void* ws, hipStream_t st, const uint8_t* pmask = nullptr) {
+  return launch_rowdot(P, M, C, Q, q_layout, r, out, split, scale, static_cast<float*>(ws), st, pmask);
 }
 
 hipError_t do_grad(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,
-                   int g_layout, int accumulate, void* ws, hipStream_t st) {
+                   int g_layout, int accumulate, void* ws, hipStream_t st, const uint8_t* pmask = nullptr) {
   const int64_t g_sc = g_layout == 0 ? 1 : r;
   const int64_t g_sj = g_layout == 0 ? C : 1;
-  return launch_coldot(P, M, C, Q, r, scale, G, g_sc, g_sj, accumulate, static_cast<float*>(ws), st);
+  return launch_coldot(P, M, C, Q, r, scale, G, g_sc, g_sj, accumulate, static_cast<float*>(ws), st, pmask);
 }
 
 // ---- whole-layer workspaces (layouts shared by the size query and the call)
 struct FwdWs {
-  uint16_t* Xd = nullptr;  // dropout: X . mask
   float* T = nullptr;
   uint16_t* TS = nullptr;
   void* proj = nullptr;
@@ -85,10 +84,8 @@ struct FwdWs {
   float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
 };
 
-size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o,
-              bool dropout = false) {
+size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o) {
   const int path = path_of(M, n, k, r, false);
-  if (dropout && r > 0) o.Xd = cv.take<uint16_t>((size_t)M * k * 2);
   if (r > 0) {
     if (path == QLORA_PATH_GEMV) {
       if (!have_tsave) o.T = cv.take<float>((size_t)M * r * 4);
@@ -106,7 +103,6 @@ size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& c
 }
 
 struct BwdWs {
-  uint16_t* Xd = nullptr;  // dropout: X . mask
   float* T = nullptr;
   float* U = nullptr;
   uint16_t* US = nullptr;
@@ -116,9 +112,7 @@ struct BwdWs {
   float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
 };
 
-size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o,
-              bool dropout = false) {
-  if (dropout && r > 0) o.Xd = cv.take<uint16_t>((size_t)M * k * 2);
+size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o) {
   if (r > 0) {
     if (!have_tsaved) o.T = cv.take<float>((size_t)M * r * 4);
     o.U = cv.take<float>((size_t)M * r * 4);
@@ -214,25 +208,17 @@ qlora_status qlora_adapter_unmerge(const void* merged, int64_t n, int64_t k, con
                                  static_cast<hipStream_t>(stream)));
 }
 
-static size_t linear_ws_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd, bool dropout) {
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
   if (M < 0 || n < 1 || k < 1 || k % QLORA_BLOCK || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (is_bwd != 0 && is_bwd != 1) return 0;
   if (M == 0) return 0;
   Carver cv(nullptr);
   if (!is_bwd) {
     FwdWs o;
-    return fwd_ws(M, n, k, r, /*have_tsave=*/false, cv, o, dropout);
+    return fwd_ws(M, n, k, r, /*have_tsave=*/false, cv, o);
   }
   BwdWs o;
-  return bwd_ws(M, n, k, r, /*have_tsaved=*/false, cv, o, dropout);
-}
-
-size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
-  return linear_ws_bytes(M, n, k, r, is_bwd, false);
-}
-
-size_t qlora_linear_dropout_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
-  return linear_ws_bytes(M, n, k, r, is_bwd, true);
+  return bwd_ws(M, n, k, r, /*have_tsaved=*/false, cv, o);
 }
 
 int qlora_lowrank_split_cols(int r) { return (r < 0 || r > QLORA_MAX_RANK) ? 0 : lora_extra_cols(r); }
@@ -356,8 +342,9 @@ qlora_status qlora_lowrank_grad(const void* P, int64_t M, int64_t C, const float
 }  // extern "C"
 
 // The layer calls with and without dropout on the adapter's input (mask NULL:
-// none). With dropout the branch reads Xd = X . mask and keep_scale folds
-// into the branch's scale: T_save receives Xd A^T.
+// none). With dropout the branch's kernels read X through the mask (dropped
+// entries as zero) and keep_scale folds into the branch's scale: T_save
+// receives (X . mask) A^T.
 static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A,
                                     const void* B, int r, float scale, const uint8_t* mask, float keep_scale,
                                     void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream) {
@@ -372,34 +359,29 @@ static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, in
   {
     Carver probe(nullptr);
     FwdWs tmp;
-    const size_t need = fwd_ws(M, w->n, w->k, r, T_save != nullptr, probe, tmp, drop);
+    const size_t need = fwd_ws(M, w->n, w->k, r, T_save != nullptr, probe, tmp);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
   FwdWs o;
-  fwd_ws(M, w->n, w->k, r, T_save != nullptr, cv, o, drop);
+  fwd_ws(M, w->n, w->k, r, T_save != nullptr, cv, o);
   const Nf4View v = view_of(w);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* a = static_cast<const uint16_t*>(A);
   const uint16_t* b = static_cast<const uint16_t*>(B);
   uint16_t* y = static_cast<uint16_t*>(Y);
   hipError_t e = hipSuccess;
-  // the branch's input and scale
-  const uint16_t* xb = x;
-  float sb = scale;
-  if (drop) {
-    e = launch_dropout_apply(x, mask, o.Xd, M * w->k, st);
-    xb = o.Xd;
-    sb = scale * keep_scale;
-  }
+  // the branch's input mask and scale
+  const uint8_t* pm = drop ? mask : nullptr;
+  const float sb = drop ? scale * keep_scale : scale;
   const int path = path_of(M, w->n, w->k, r, false);
   if (path == QLORA_PATH_GEMV) {
     float* T = T_save ? T_save : o.T;
-    if (r > 0 && e == hipSuccess) e = do_project(xb, M, w->k, a, 0, r, sb, T, nullptr, o.proj, st);
+    if (r > 0) e = do_project(x, M, w->k, a, 0, r, sb, T, nullptr, o.proj, st, pm);
     if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, sb, y, st);
   } else {
-    if (r > 0 && e == hipSuccess) e = do_project(xb, M, w->k, a, 0, r, sb, T_save, o.TS, o.proj, st);
+    if (r > 0) e = do_project(x, M, w->k, a, 0, r, sb, T_save, o.TS, o.proj, st, pm);
     if (path == QLORA_PATH_FUSED) {
       if (e == hipSuccess) e = launch_gemm_fwd(v, x, M, o.TS, b, r, y, st);
     } else {
@@ -431,13 +413,13 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
   {
     Carver probe(nullptr);
     BwdWs tmp;
-    const size_t need = bwd_ws(M, w->n, w->k, r, T_saved != nullptr, probe, tmp, drop);
+    const size_t need = bwd_ws(M, w->n, w->k, r, T_saved != nullptr, probe, tmp);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
   BwdWs o;
-  bwd_ws(M, w->n, w->k, r, T_saved != nullptr, cv, o, drop);
+  bwd_ws(M, w->n, w->k, r, T_saved != nullptr, cv, o);
   const Nf4View v = view_of(w);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* dy = static_cast<const uint16_t*>(dY);
@@ -456,19 +438,14 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
       e = launch_gemm_dx(v, dy, M, r > 0 ? o.US : nullptr, a, r, static_cast<uint16_t*>(dX), st, dmask, keep_scale);
     }
   }
-  // the branch's input and scale for the adapter gradients
-  const uint16_t* xb = x;
-  float sb = scale;
-  if (drop && need_x && e == hipSuccess) {
-    e = launch_dropout_apply(x, mask, o.Xd, M * w->k, st);
-    xb = o.Xd;
-  }
-  if (drop) sb = scale * keep_scale;
-  if (e == hipSuccess && dA) e = do_grad(xb, M, w->k, o.U, r, sb, dA, 0, accumulate, o.grad, st);
+  // the branch's input mask and scale for the adapter gradients
+  const uint8_t* pm = drop ? mask : nullptr;
+  const float sb = drop ? scale * keep_scale : scale;
+  if (e == hipSuccess && dA) e = do_grad(x, M, w->k, o.U, r, sb, dA, 0, accumulate, o.grad, st, pm);
   if (e == hipSuccess && dB) {
     const float* T = T_saved;
     if (T == nullptr) {
-      e = do_project(xb, M, w->k, a, 0, r, scale, o.T, nullptr, o.proj, st);
+      e = do_project(x, M, w->k, a, 0, r, scale, o.T, nullptr, o.proj, st, pm);
       T = o.T;
     }
     if (e == hipSuccess) e = do_grad(dy, M, w->n, T, r, sb, dB, 1, accumulate, o.grad, st);

@@ -131,6 +131,20 @@ __device__ __forceinline__ u32x4 dequant8_pairs(uint32_t word, const float2* lut
 
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Eight bf16 values with the ones whose mask byte is 0 cleared (mask bytes in
+// element order, little-endian in mk): dropout on the adapter's input.
+__device__ __forceinline__ u32x4 apply_mask8(u32x4 v, uint2 mk) {
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t mb = (w < 2 ? mk.x : mk.y) >> (16 * (w & 1));  // bytes of elements 2w, 2w + 1
+    const uint32_t lo = (mb & 0xFFu) ? 0x0000FFFFu : 0u;
+    const uint32_t hi = (mb & 0xFF00u) ? 0xFFFF0000u : 0u;
+    o[w] = v[w] & (lo | hi);
+  }
+  return o;
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 

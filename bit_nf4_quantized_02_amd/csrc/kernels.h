@@ -43,8 +43,11 @@ inline int lora_extra_cols(int r) { return r > 0 ? ((2 * r + 63) / 64) * 64 : 0;
 // also receives rows [bf16(scale*out) | bf16(scale*out - hi) | 0 ...] of
 // lora_extra_cols(r) elements. part: workspace of rowdot_ws_bytes (may be 0).
 size_t rowdot_ws_bytes(int64_t M, int64_t C, int r);
+// pmask (uint8 [M, C], q_layout 0 and C % 8 == 0 only; NULL: none): P's
+// elements whose byte is 0 read as zero (dropout on the adapter's input).
 hipError_t launch_rowdot(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r,
-                         float* out, uint16_t* split, float scale, float* part, hipStream_t stream);
+                         float* out, uint16_t* split, float scale, float* part, hipStream_t stream,
+                         const uint8_t* pmask = nullptr);
 
 // Column reduction over M in fixed order, for the adapter gradients:
 //   G[c, j] (+)= scale * sum_m P[m, c] * Q[m, j]    P bf16 [M, C], Q fp32 [M, r]
@@ -53,7 +56,7 @@ int coldot_splits(int64_t M);
 size_t coldot_ws_bytes(int64_t M, int64_t C, int r);
 hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale,
                          float* G, int64_t g_sc, int64_t g_sj, int accumulate, float* partial,
-                         hipStream_t stream);
+                         hipStream_t stream, const uint8_t* pmask = nullptr);
 
 // Y = RN_bf16(X W'^T + [sT_hi | sT_lo] [B | B]^T): fused dequant + MFMA GEMM.
 hipError_t launch_gemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* TS,
@@ -87,10 +90,6 @@ size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout);
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                             const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
                             const uint8_t* mask = nullptr, float keep_scale = 1.0f);
-
-// Xd = X . mask (count elements, a multiple of 8; 16-byte aligned buffers).
-hipError_t launch_dropout_apply(const uint16_t* X, const uint8_t* mask, uint16_t* Xd, int64_t count,
-                                hipStream_t stream);
 
 // Adapter merge: out = round(W' + scale * B A) (w != NULL; bf16, or fp32 if
 // out_f32) or unmerge: out = RN_bf16(Wm - scale * B A) (w == NULL, Wm bf16).

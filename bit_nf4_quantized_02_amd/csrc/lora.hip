@@ -64,10 +64,13 @@ __device__ __forceinline__ bf16x8 tr_operand(const char* tile, int pitch, int c0
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int kRP, bool kVec>
+// kMask (16-byte P rows only): P's elements whose byte in pmask [M, C] is 0
+// read as zero (dropout on the adapter's input).
+template <int kRP, bool kVec, bool kMask = false>
 __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
                                                           const float* __restrict__ Q, int r, int64_t mchunk,
-                                                          float* __restrict__ partial) {
+                                                          float* __restrict__ partial,
+                                                          const uint8_t* __restrict__ pmask = nullptr) {
 #pragma clang fp contract(off)
   constexpr int kJT = kRP / 16;
   using Smem = ColdotSmem<kRP>;
@@ -87,15 +90,19 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
 
   // P tile: 32 rows x 32 chunks of 16 B; thread t owns chunk t % 32 of rows
   // t / 32 + 8 i (i = 0..3). Out-of-range rows / columns load zeros.
-  auto load_p = [&](int64_t mb, u32x4 (&v)[4]) {
+  auto load_p = [&](int64_t mb, u32x4 (&v)[4], uint2 (&mk)[kMask ? 4 : 1]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = mb + (t >> 5) + 8 * i;
       const int64_t c = cw + (t & 31) * 8;
       v[i] = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kMask) mk[i] = uint2{0u, 0u};
       if (m < m1) {
         if constexpr (kVec) {
-          if (c < C) v[i] = *reinterpret_cast<const u32x4*>(P + m * C + c);
+          if (c < C) {
+            v[i] = *reinterpret_cast<const u32x4*>(P + m * C + c);
+            if constexpr (kMask) mk[i] = *reinterpret_cast<const uint2*>(pmask + m * C + c);
+          }
         } else {
           uint32_t e[8];
 #pragma unroll
@@ -124,13 +131,15 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
   constexpr int kDepth = kRP <= 32 ? 4 : 1;
   struct Stage {
     u32x4 p[4];
+    uint2 mk[kMask ? 4 : 1];
     float q[kQE];
   };
   auto step = [&](int64_t mb, Stage& stg) {
     // stage this step: P from registers, Q converted to bf16 hi / lo
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(sm.p + ((t >> 5) + 8 * i) * kPPitch + (t & 31) * 16) = stg.p[i];
+      *reinterpret_cast<u32x4*>(sm.p + ((t >> 5) + 8 * i) * kPPitch + (t & 31) * 16) =
+          kMask ? apply_mask8(stg.p[i], stg.mk[i]) : stg.p[i];
 #pragma unroll
     for (int e = 0; e < kQE; ++e) {
       const int idx = t + 256 * e;
@@ -142,7 +151,7 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
     }
     __syncthreads();
     if (mb + kDepth * 32 < m1) {
-      load_p(mb + kDepth * 32, stg.p);
+      load_p(mb + kDepth * 32, stg.p, stg.mk);
       load_q(mb + kDepth * 32, stg.q);
     }
     bf16x8 pb[4];
@@ -162,10 +171,10 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
   };
   if constexpr (kDepth == 4) {
     Stage s0, s1, s2, s3;
-    load_p(m0, s0.p); load_q(m0, s0.q);
-    load_p(m0 + 32, s1.p); load_q(m0 + 32, s1.q);
-    load_p(m0 + 64, s2.p); load_q(m0 + 64, s2.q);
-    load_p(m0 + 96, s3.p); load_q(m0 + 96, s3.q);
+    load_p(m0, s0.p, s0.mk); load_q(m0, s0.q);
+    load_p(m0 + 32, s1.p, s1.mk); load_q(m0 + 32, s1.q);
+    load_p(m0 + 64, s2.p, s2.mk); load_q(m0 + 64, s2.q);
+    load_p(m0 + 96, s3.p, s3.mk); load_q(m0 + 96, s3.q);
     for (int64_t mb = m0; mb < m1; mb += 4 * 32) {
       step(mb, s0);
       if (mb + 32 >= m1) break;
@@ -177,7 +186,7 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
     }
   } else {
     Stage s0;
-    load_p(m0, s0.p); load_q(m0, s0.q);
+    load_p(m0, s0.p, s0.mk); load_q(m0, s0.q);
     for (int64_t mb = m0; mb < m1; mb += 32) step(mb, s0);
   }
   // D[j][c]: lane -> c = lane % 16, j = 4 (lane / 16) + v
@@ -231,13 +240,17 @@ size_t coldot_ws_bytes(int64_t M, int64_t C, int r) {
 }
 
 hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,
-                         int64_t g_sc, int64_t g_sj, int accumulate, float* partial, hipStream_t stream) {
+                         int64_t g_sc, int64_t g_sj, int accumulate, float* partial, hipStream_t stream,
+                         const uint8_t* pmask) {
   const int ns = coldot_splits(M);
   const int64_t mchunk = cdiv(cdiv(M, ns), 32) * 32;
   const dim3 grid((unsigned)cdiv(C, 256), (unsigned)ns);
   const bool vec = C % 8 == 0;
-#define QLORA_COLDOT(RP)                                                                             \
-  if (vec) coldot_mfma_kernel<RP, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);  \
+  if (pmask != nullptr && !vec) return hipErrorInvalidValue;
+#define QLORA_COLDOT(RP)                                                                                    \
+  if (pmask != nullptr)                                                                                    \
+    coldot_mfma_kernel<RP, true, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial, pmask);   \
+  else if (vec) coldot_mfma_kernel<RP, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);    \
   else coldot_mfma_kernel<RP, false><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
   if (r <= 16) { QLORA_COLDOT(16) }
   else if (r <= 32) { QLORA_COLDOT(32) }

@@ -64,10 +64,13 @@ struct RowdotCfg {
 
 // kQL: 0 = Q is [r, C], 1 = Q is [C, r]. kVecP / kVecQ: 16-byte rows.
 // kDirect: write out / split (single column split), else write partials.
-template <int kRP, int kQL, bool kVecP, bool kVecQ, bool kDirect>
+// kMask (Q = A only): P's elements whose byte in pmask [M, C] is 0 read as zero
+// (dropout on the adapter's input).
+template <int kRP, int kQL, bool kVecP, bool kVecQ, bool kDirect, bool kMask = false>
 __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
     const uint16_t* __restrict__ P, int64_t M, int64_t C, const uint16_t* __restrict__ Q, int r, int64_t cchunk,
-    float* __restrict__ out, uint16_t* __restrict__ split, int xc, float scale, float* __restrict__ part) {
+    float* __restrict__ out, uint16_t* __restrict__ split, int xc, float scale, float* __restrict__ part,
+    const uint8_t* __restrict__ pmask = nullptr) {
 #pragma clang fp contract(off)
   using Cfg = RowdotCfg<kRP, kQL>;
   constexpr int kTiles = Cfg::kTiles, kU = Cfg::kU, kNW = Cfg::kNW;
@@ -85,6 +88,7 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
   const int ko = (lane >> 4) * 8;
   const int64_t m = m0 + row;
   const uint16_t* prow = P + (m < M ? m : M - 1) * C;
+  const uint8_t* mrow = kMask ? pmask + (m < M ? m : M - 1) * C : nullptr;
   char* const stage = smem + wave * Cfg::kStage;
 
   f32x4 acc[kTiles];
@@ -98,6 +102,7 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
   constexpr int kQL1 = kQL == 1 ? kU * (kChunks / 64) : 1;
   struct Batch {
     u32x4 a[kU];
+    uint2 mk[kMask ? kU : 1];
     u32x4 q0[kQL == 0 ? kU * kTiles : 1];  // Q = [r, C]: operand layout
     u32x4 q1[kQL1];                        // Q = [C, r]: raw chunks for the LDS tile
   };
@@ -106,6 +111,10 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
     for (int u = 0; u < kU; ++u) {
       bt.a[u] = load8<kVecP>(prow, c + 32 * u + ko, w1);
       if (m >= M) bt.a[u] = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (kMask) {
+        const int64_t e0 = c + 32 * u + ko;
+        bt.mk[u] = e0 < w1 ? *reinterpret_cast<const uint2*>(mrow + e0) : uint2{0u, 0u};
+      }
     }
     if constexpr (kQL == 0) {
 #pragma unroll
@@ -174,7 +183,8 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int t = 0; t < kTiles; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bt.a[u]), b[u][t], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, kMask ? apply_mask8(bt.a[u], bt.mk[u]) : bt.a[u]), b[u][t], acc[t], 0, 0, 0);
   };
   constexpr int64_t kStep = 32 * kU;
   if constexpr (!kVecP || !kVecQ) {
@@ -307,7 +317,7 @@ int rowdot_splits(int64_t M, int64_t C) {
 
 template <int kRP, int kQL>
 hipError_t launch_rp(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
-                     uint16_t* split, float scale, float* part, hipStream_t stream) {
+                     uint16_t* split, float scale, float* part, hipStream_t stream, const uint8_t* pmask) {
   constexpr int kNW = RowdotCfg<kRP, kQL>::kNW;
   const int ns = rowdot_splits(M, C);
   const int64_t cchunk = cdiv(cdiv(C, (int64_t)ns), (int64_t)32) * 32;
@@ -317,17 +327,32 @@ hipError_t launch_rp(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q,
   const bool vq = kQL == 0 ? (C % 8 == 0) : (r % 8 == 0);
 #define QLORA_RD(VP, VQ, D) \
   rowdot_kernel<kRP, kQL, VP, VQ, D><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, split, xc, scale, part)
-#define QLORA_RD2(D)                    \
-  if (vp && vq) QLORA_RD(true, true, D); \
-  else if (vp) QLORA_RD(true, false, D); \
-  else if (vq) QLORA_RD(false, true, D); \
-  else QLORA_RD(false, false, D);
+#define QLORA_RDM(VQ, D)                                                                                   \
+  rowdot_kernel<kRP, 0, true, VQ, D, true><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, split, xc, \
+                                                                          scale, part, pmask)
+#define QLORA_RD2(D)                                           \
+  if constexpr (kQL == 0) {                                    \
+    if (pmask != nullptr) {                                    \
+      if (!vp) return hipErrorInvalidValue;                    \
+      if (vq) QLORA_RDM(true, D); else QLORA_RDM(false, D);    \
+    } else if (vp && vq) QLORA_RD(true, true, D);              \
+    else if (vp) QLORA_RD(true, false, D);                     \
+    else if (vq) QLORA_RD(false, true, D);                     \
+    else QLORA_RD(false, false, D);                            \
+  } else {                                                     \
+    if (pmask != nullptr) return hipErrorInvalidValue;         \
+    if (vp && vq) QLORA_RD(true, true, D);                     \
+    else if (vp) QLORA_RD(true, false, D);                     \
+    else if (vq) QLORA_RD(false, true, D);                     \
+    else QLORA_RD(false, false, D);                            \
+  }
   if (ns == 1) {
     QLORA_RD2(true)
     return hipGetLastError();
   }
   QLORA_RD2(false)
 #undef QLORA_RD2
+#undef QLORA_RDM
 #undef QLORA_RD
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -343,10 +368,11 @@ size_t rowdot_ws_bytes(int64_t M, int64_t C, int r) {
 }
 
 hipError_t launch_rowdot(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r,
-                         float* out, uint16_t* split, float scale, float* part, hipStream_t stream) {
-#define QLORA_RP(RP)                                                                      \
-  return q_layout == 0 ? launch_rp<RP, 0>(P, M, C, Q, r, out, split, scale, part, stream) \
-                       : launch_rp<RP, 1>(P, M, C, Q, r, out, split, scale, part, stream);
+                         float* out, uint16_t* split, float scale, float* part, hipStream_t stream,
+                         const uint8_t* pmask) {
+#define QLORA_RP(RP)                                                                             \
+  return q_layout == 0 ? launch_rp<RP, 0>(P, M, C, Q, r, out, split, scale, part, stream, pmask) \
+                       : launch_rp<RP, 1>(P, M, C, Q, r, out, split, scale, part, stream, pmask);
   if (r <= 16) { QLORA_RP(16) }
   if (r <= 32) { QLORA_RP(32) }
   if (r <= 64) { QLORA_RP(64) }

@@ -55,7 +55,6 @@ _SIGS = {
     "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
     "qlora_linear_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
-    "qlora_linear_dropout_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
     "qlora_linear_fwd_dropout": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd_dropout": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _f, _vp, _vp, _vp, _int,
                                          _vp, _sz, _vp]),
@@ -229,10 +228,6 @@ def dequant(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch
 
 # --------------------------------------------------------------------------- linear
 
-def linear_dropout_workspace_bytes(M: int, n: int, k: int, r: int, is_bwd: bool) -> int:
-    return int(_lib.qlora_linear_dropout_workspace_bytes(M, n, k, r, int(bool(is_bwd))))
-
-
 def _mask_of(mask: torch.Tensor, M: int, k: int):
     if mask.dtype != torch.uint8 or tuple(mask.shape) != (M, k) or not mask.is_contiguous() or not mask.is_cuda:
         raise ValueError(f"mask: expected contiguous uint8 {(M, k)} on the GPU")
@@ -274,7 +269,7 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
     if _dropout is not None:
         mp = _mask_of(_dropout[0], M, w.k)
         if ws is None:
-            ws = _bytes(linear_dropout_workspace_bytes(M, w.n, w.k, r, False), X.device)
+            ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, False), X.device)
         _check(_lib.qlora_linear_fwd_dropout(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), mp,
                                              float(_dropout[1]), _ptr(Y), _ptr(T), _ptr(ws),
                                              0 if ws is None else ws.numel(), _stream(stream)),
@@ -320,7 +315,7 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY:
     if _dropout is not None:
         mp = _mask_of(_dropout[0], M, w.k)
         if ws is None:
-            ws = _bytes(linear_dropout_workspace_bytes(M, w.n, w.k, r, True), dev)
+            ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, True), dev)
         _check(_lib.qlora_linear_bwd_dropout(ctypes.byref(st), _ptr(X), _ptr(T), _ptr(dY), M, _ptr(A), _ptr(B), r,
                                              float(scale), mp, float(_dropout[1]), _ptr(dX), _ptr(dA), _ptr(dB),
                                              int(bool(accumulate)), _ptr(ws), 0 if ws is None else ws.numel(),

@@ -220,13 +220,12 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight *w, const void *X, const fl
  * for the branch; the caller draws it. keep_scale (>= 1, finite) is
  * 1 / (1 - p). The base product uses X itself. T_save / T_saved hold
  * (X . mask) A^T (without keep_scale; the backward applies it). Workspace:
- * qlora_linear_dropout_workspace_bytes (the plain one plus M k bf16).
- * Everything else, including the kernels chosen, is as for qlora_linear_fwd /
- * qlora_linear_bwd; r = 0 ignores mask.
+ * qlora_linear_workspace_bytes, as for the plain calls; the branch's kernels
+ * read X through the mask. Everything else, including the kernels chosen, is
+ * as for qlora_linear_fwd / qlora_linear_bwd; r = 0 ignores mask.
  * Errors: as those calls, and INVALID_ARG for a NULL or misaligned mask or a
  * keep_scale below 1 or not finite.
  */
-size_t qlora_linear_dropout_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd);
 qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight *w, const void *X, int64_t M, const void *A,
                                       const void *B, int r, float scale, const void *mask, float keep_scale,
                                       void *Y, float *T_save, void *ws, size_t ws_bytes, void *stream);
