@@ -154,7 +154,8 @@ class LinearPlan:
         pw = max(lib.qlora_lowrank_project_workspace_bytes(M, K, r), lib.qlora_lowrank_project_workspace_bytes(M, N, r))
         gw = max(lib.qlora_lowrank_grad_workspace_bytes(M, K, r), lib.qlora_lowrank_grad_workspace_bytes(M, N, r))
         bw = max(lib.qlora_bf16_gemm_workspace_bytes(M, K, r, N), lib.qlora_bf16_gemm_workspace_bytes(M, N, r, K))
-        self.ws = buf("ws", (max(pw, gw, bw, 256),), torch.uint8)
+        vw = lib.qlora_nf4_gemv_workspace_bytes(K)
+        self.ws = buf("ws", (max(pw, gw, bw, vw, 256),), torch.uint8)
         st = q._stream()
         P = q._ptr
         self.wst = self.W.struct()
@@ -178,7 +179,7 @@ class LinearPlan:
                                     ws, wsn, st)))
             self.fwd.append(("nf4_gemv_fwd", 2 * M * N * K + 2 * M * N * r,
                              q.Call("qlora_nf4_gemv_fwd", wref, P(self.X), M, P(self.T), P(self.B), r, self.s,
-                                    P(self.Y), st, keep=(self.wst,))))
+                                    P(self.Y), ws, wsn, st, keep=(self.wst,))))
         else:
             self.fwd.append(("lowrank_project_T", 2 * M * K * r,
                              q.Call("qlora_lowrank_project", P(self.X), M, K, P(self.A), 0, r, self.s, P(self.T),

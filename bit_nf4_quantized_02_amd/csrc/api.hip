@@ -77,6 +77,7 @@ hipError_t do_grad(const uint16_t* P, int64_t M, int64_t C, const float* Q, int 
 
 // ---- whole-layer workspaces (layouts shared by the size query and the call)
 struct FwdWs {
+  void* xp = nullptr;     // activations in the GEMV's operand order (M <= 16)
   float* T = nullptr;
   uint16_t* TS = nullptr;
   void* proj = nullptr;
@@ -94,6 +95,7 @@ size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& c
     }
     o.proj = cv.take<char>(project_ws(M, k, r));
   }
+  if (path == QLORA_PATH_GEMV) o.xp = cv.take<char>(gemv_ws_bytes(k));
   if (path == QLORA_PATH_EXPANDED) {
     o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, false));
     const size_t pb = gemm_bf16_ws_bytes(M, k, lora_extra_cols(r), n);
@@ -266,16 +268,22 @@ qlora_status qlora_nf4_gemm_dx(const qlora_nf4_weight* w, const void* dY, int64_
                                    static_cast<uint16_t*>(dX), static_cast<hipStream_t>(stream)));
 }
 
+size_t qlora_nf4_gemv_workspace_bytes(int64_t k) {
+  if (k < 1 || k % QLORA_BLOCK) return 0;
+  return gemv_ws_bytes(k);
+}
+
 qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight* w, const void* X, int64_t M, const float* T, const void* B,
-                                int r, float scale, void* Y, void* stream) {
+                                int r, float scale, void* Y, void* ws, size_t ws_bytes, void* stream) {
   const qlora_status s = check_weight(w);
   if (s != QLORA_OK) return s;
   if (M < 0 || M > 16 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
   if (M == 0) return QLORA_OK;
   if (!X || !Y || !aligned16(X) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
   if (r > 0 && (!T || !B || !aligned16(T) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < gemv_ws_bytes(w->k)) return QLORA_ERR_WORKSPACE;
   return hip_status(launch_gemv(view_of(w), static_cast<const uint16_t*>(X), M, T, static_cast<const uint16_t*>(B),
-                                r, scale, static_cast<uint16_t*>(Y), static_cast<hipStream_t>(stream)));
+                                r, scale, static_cast<uint16_t*>(Y), ws, static_cast<hipStream_t>(stream)));
 }
 
 int qlora_linear_path(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
@@ -379,7 +387,7 @@ static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, in
   if (path == QLORA_PATH_GEMV) {
     float* T = T_save ? T_save : o.T;
     if (r > 0) e = do_project(x, M, w->k, a, 0, r, sb, T, nullptr, o.proj, st, pm);
-    if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, sb, y, st);
+    if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, sb, y, o.xp, st);
   } else {
     if (r > 0) e = do_project(x, M, w->k, a, 0, r, sb, T_save, o.TS, o.proj, st, pm);
     if (path == QLORA_PATH_FUSED) {

@@ -19,24 +19,48 @@
 // v_mfma_f32_16x16x32_bf16 as the B operand; X (padded to 16 rows with zeros)
 // is the A operand. The contraction order inside a chunk is permuted the same
 // way on both operands (lane group g takes columns 64 g .. 64 g + 63), which
-// leaves the sum unchanged and makes each lane's code load contiguous.
+// leaves the sum unchanged and makes each lane's code load contiguous. A
+// first small kernel writes X in exactly that operand order (per 256-column
+// chunk, per MFMA, per lane: 16 bytes), so each activation load instruction
+// reads 1 KB in one run; read in place, the 16 token rows and 4 column groups
+// of one instruction fall in 64 different cache lines.
 // Partial sums of the waves are added in a fixed order through LDS; the
 // low-rank term T B^T is formed with fp32 MFMAs (one 16-row tile per wave,
 // T and B exact in fp32) and added in fp32, and Y is rounded to bf16 once.
 #include "common.h"
 #include "kernels.h"
 
+#ifndef QLORA_GEMV_XP_MIN_M
+#define QLORA_GEMV_XP_MIN_M 5
+#endif
+
 namespace qlora {
 
 namespace {
 
-template <int NT, int kW, bool kLora>
+// Xp[q][s][lane] = X[lane % 16][256 q + 64 (lane / 16) + 8 s .. +7] (16 bytes),
+// zero for token rows >= M or columns >= K.
+__global__ __launch_bounds__(256) void gemv_xperm_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                         u32x4* __restrict__ Xp, int64_t entries) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= entries) return;
+  const int lane = (int)(e & 63), s = (int)((e >> 6) & 7);
+  const int64_t q = e >> 9;
+  const int64_t m = lane & 15, c = 256 * q + 64 * (lane >> 4) + 8 * s;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (m < M && c < K) v = *reinterpret_cast<const u32x4*>(X + m * K + c);
+  Xp[e] = v;
+}
+
+// kXp: activations from the operand-ordered copy Xp (else read in place from X).
+template <int NT, int kW, bool kLora, bool kXp>
 __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ code8,
                                                        const float* __restrict__ s2,
                                                        const float* __restrict__ mean_p,
                                                        const float* __restrict__ codebook, int64_t N,
-                                                       int64_t K, const uint16_t* __restrict__ X, int64_t M,
+                                                       int64_t K, const uint16_t* __restrict__ X,
+                                                       const u32x4* __restrict__ Xp, int64_t M,
                                                        const float* __restrict__ T,
                                                        const uint16_t* __restrict__ B, int r, float scale,
                                                        uint16_t* __restrict__ Y) {
@@ -58,6 +82,9 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
   const int grp = lane >> 4;   // 0..3: which 64-block of a 256-column chunk
   const int col = lane & 15;   // A: token row m; B: weight row within a tile
   const int64_t kblocks = K / kBlock;
+  const int64_t nq = cdiv(K, (int64_t)kChunk);  // chunks of the operand-ordered activations
+  const bool xtok = col < M;                     // lanes of token rows past M load nothing
+  const uint16_t* xrow = X + (int64_t)(col < M ? col : M - 1) * K;
 
   f32x4 acc[kTiles];
 #pragma unroll
@@ -83,8 +110,6 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
     crow[i] = codes + nc * (K / 2);
     bbase[i] = nc * kblocks;
   }
-  const uint16_t* xrow = X + (int64_t)(col < M ? col : M - 1) * K;
-  const bool xok = col < M;
 
   struct Stage {
     u32x4 cw[kTiles][2];
@@ -97,8 +122,17 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
     const int64_t k = k0 + 64 * grp;
     st.kin = k < ke;
     const int64_t kc = st.kin ? k : ke - 64;  // a valid block of this wave's range
+    // this chunk's operands, in order (a prefetch past the last chunk reads
+    // the last one again: every group then has kin false and code 7)
+    if constexpr (kXp) {
+      const int64_t q = k0 / kChunk < nq ? k0 / kChunk : nq - 1;
+      const u32x4* xq = Xp + q * 512 + lane;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) st.xa[s] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * s);
+      for (int s = 0; s < 8; ++s) st.xa[s] = xtok ? xq[64 * s] : u32x4{0u, 0u, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) st.xa[s] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * s);
+    }
 #pragma unroll
     for (int i = 0; i < kTiles; ++i) {
       st.cw[i][0] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2);
@@ -108,7 +142,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
     }
   };
   auto compute = [&](const Stage& st) {
-    const bool xuse = st.kin && xok;
+    const bool xuse = st.kin && xtok;
     bf16x8 xa[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -185,27 +219,39 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
 
 }  // namespace
 
+size_t gemv_ws_bytes(int64_t k) { return align256((size_t)cdiv(k, 256) * 512 * 16); }
+
+// Token counts from which the activations are first rewritten in operand
+// order: below it the few distinct rows an activation load touches cost less
+// than the extra pass (measured on the 70B-class shapes).
+constexpr int64_t kXpMinM = QLORA_GEMV_XP_MIN_M;
+
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T, const uint16_t* B, int r,
-                       float scale, uint16_t* Y, hipStream_t stream) {
+                       float scale, uint16_t* Y, void* ws, hipStream_t stream) {
+  u32x4* Xp = static_cast<u32x4*>(ws);
+  const bool xp = M >= kXpMinM;
+  if (xp) {
+    const int64_t entries = cdiv(w.k, (int64_t)256) * 512;
+    gemv_xperm_kernel<<<(unsigned)cdiv(entries, (int64_t)256), 256, 0, stream>>>(X, M, w.k, Xp, entries);
+  }
   // Rows and waves per workgroup, measured on the 70B-class shapes: 64 rows
   // and 4 waves for 28672 rows (448 workgroups), 32 rows and 8 waves for
   // 8192 rows (256 workgroups, each wave an eighth of the 28672-long
   // contraction), 16 rows and 4 waves below.
   const bool lora = r > 0;
-#define QLORA_GEMV(NT, W)                                                                                     \
-  {                                                                                                           \
-    const dim3 grid((unsigned)cdiv(w.n, NT));                                                                 \
-    if (lora)                                                                                                 \
-      gemv_nf4_kernel<NT, W, true><<<grid, 64 * W, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook,   \
-                                                               w.n, w.k, X, M, T, B, r, scale, Y);            \
-    else                                                                                                      \
-      gemv_nf4_kernel<NT, W, false><<<grid, 64 * W, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook,  \
-                                                                w.n, w.k, X, M, T, B, r, scale, Y);           \
+#define QLORA_GEMV2(NT, W, L, XP)                                                                              \
+  gemv_nf4_kernel<NT, W, L, XP><<<dim3((unsigned)cdiv(w.n, NT)), 64 * W, 0, stream>>>(                         \
+      w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, X, Xp, M, T, B, r, scale, Y)
+#define QLORA_GEMV(NT, W)                                                   \
+  {                                                                         \
+    if (lora) { if (xp) QLORA_GEMV2(NT, W, true, true); else QLORA_GEMV2(NT, W, true, false); } \
+    else { if (xp) QLORA_GEMV2(NT, W, false, true); else QLORA_GEMV2(NT, W, false, false); }    \
   }
   if (w.n / 64 >= 448) QLORA_GEMV(64, 4)
   else if (w.n / 32 >= 256) QLORA_GEMV(32, 8)
   else QLORA_GEMV(16, 4)
 #undef QLORA_GEMV
+#undef QLORA_GEMV2
   return hipGetLastError();
 }
 

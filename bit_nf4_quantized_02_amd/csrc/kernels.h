@@ -97,9 +97,11 @@ size_t merge_smem_bytes(int r);
 hipError_t launch_merge(const Nf4View* w, const uint16_t* Wm, int64_t n, int64_t k, const uint16_t* A,
                         const uint16_t* B, int r, float scale, bool out_f32, void* out, hipStream_t stream);
 
-// Small-M dequant-GEMV: Y = RN_bf16(X W'^T + scale * T B^T), M <= 16.
+// Small-M dequant-GEMV: Y = RN_bf16(X W'^T + scale * T B^T), M <= 16. ws:
+// gemv_ws_bytes(k) bytes for the activations in operand order.
+size_t gemv_ws_bytes(int64_t k);
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T,
-                       const uint16_t* B, int r, float scale, uint16_t* Y, hipStream_t stream);
+                       const uint16_t* B, int r, float scale, uint16_t* Y, void* ws, hipStream_t stream);
 
 hipError_t launch_silu_fwd(const uint16_t* G, const uint16_t* U, uint16_t* H, int64_t count,
                            hipStream_t stream);

@@ -63,7 +63,8 @@ _SIGS = {
     "qlora_lowrank_project": (_int, [_vp, _i64, _i64, _vp, _int, _int, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_nf4_gemm_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
     "qlora_nf4_gemm_dx": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
-    "qlora_nf4_gemv_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp]),
+    "qlora_nf4_gemv_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _sz, _vp]),
+    "qlora_nf4_gemv_workspace_bytes": (_sz, [_i64]),
     "qlora_linear_path": (_int, [_i64, _i64, _i64, _int, _int]),
     "qlora_nf4_expand_bytes": (_sz, [_i64, _i64, _int, _int]),
     "qlora_nf4_expand": (_int, [_W, _vp, _int, _int, _vp, _sz, _vp]),
@@ -428,15 +429,21 @@ def bf16_gemm(act: torch.Tensor, split: torch.Tensor | None, r: int, F: torch.Te
     return out
 
 
+def nf4_gemv_workspace_bytes(k: int) -> int:
+    return int(_lib.qlora_nf4_gemv_workspace_bytes(k))
+
+
 def nf4_gemv_fwd(w: NF4Weight, X: torch.Tensor, T: torch.Tensor | None, B: torch.Tensor | None, scale: float,
-                 Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                 Y: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     M = X.shape[0]
     r = 0 if B is None else B.shape[1]
     if Y is None:
         Y = torch.empty((M, w.n), dtype=torch.bfloat16, device=X.device)
+    if ws is None:
+        ws = _bytes(nf4_gemv_workspace_bytes(w.k), X.device)
     st = w.struct()
     _check(_lib.qlora_nf4_gemv_fwd(ctypes.byref(st), _ptr(X), M, _ptr(T), _ptr(B), r, float(scale), _ptr(Y),
-                                   _stream(stream)), "qlora_nf4_gemv_fwd")
+                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "qlora_nf4_gemv_fwd")
     return Y
 
 

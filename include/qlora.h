@@ -284,13 +284,20 @@ qlora_status qlora_nf4_gemm_fwd(const qlora_nf4_weight *w, const void *X, int64_
 qlora_status qlora_nf4_gemm_dx(const qlora_nf4_weight *w, const void *dY, int64_t M, const void *split,
                                const void *A, int r, void *dX, void *stream);
 
+/* Workspace bytes of qlora_nf4_gemv_fwd for a weight with k columns (0 on a
+ * bad k): the activations rewritten in the kernel's operand order. */
+size_t qlora_nf4_gemv_workspace_bytes(int64_t k);
+
 /*
  * Bandwidth-oriented forward for M <= 16 tokens:
  *   Y = RN_bf16( X W'^T + scale T B^T ),   T (device, [M, r] fp32) = X A^T.
- * One pass over the packed codes. Errors: INVALID_ARG, SHAPE (M > 16), HIP.
+ * One pass over the packed codes. ws (device, 16-byte aligned) holds
+ * qlora_nf4_gemv_workspace_bytes(k) bytes. Errors: INVALID_ARG, SHAPE
+ * (M > 16), WORKSPACE, HIP.
  */
 qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight *w, const void *X, int64_t M, const float *T,
-                                const void *B, int r, float scale, void *Y, void *stream);
+                                const void *B, int r, float scale, void *Y, void *ws, size_t ws_bytes,
+                                void *stream);
 
 /*
  * Which kernels a pass uses at this size; qlora_linear_fwd (is_bwd = 0) and

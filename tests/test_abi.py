@@ -86,7 +86,8 @@ def test_size_queries_reject_bad_shapes(q):
     assert q.linear_workspace_bytes(0, 64, 64, 8, True) == 0
     assert q.linear_workspace_bytes(4096, 4096, 4096, 16, False) > 0
     assert q.linear_workspace_bytes(4096, 4096, 4096, 16, True) > 0
-    assert q.linear_workspace_bytes(16, 4096, 4096, 0, False) == 0
+    # M <= 16 without a rank: only the activations in the GEMV operand order
+    assert q.linear_workspace_bytes(16, 4096, 4096, 0, False) == q.nf4_gemv_workspace_bytes(4096)
 
 
 def _fake_weight(q, n=64, k=128, aligned=True):
@@ -249,3 +250,14 @@ def test_dropout_host_errors(q):
     need = q.linear_workspace_bytes(64, 64, 128, 8, False)
     assert lib.qlora_linear_fwd_dropout(ctypes.byref(W), p, 64, p, p, 8, 1.0, p, 1.05, p, None, p, need - 1,
                                         None) == -4
+
+
+def test_gemv_needs_its_workspace(q):
+    lib = q.raw()
+    W = _fake_weight(q)
+    p = ctypes.c_void_p(1 << 24)
+    need = q.nf4_gemv_workspace_bytes(128)
+    assert need >= 16 * 128 * 2 and q.nf4_gemv_workspace_bytes(100) == 0
+    assert lib.qlora_nf4_gemv_fwd(ctypes.byref(W), p, 4, p, p, 8, 1.0, p, None, 0, None) == -4
+    assert lib.qlora_nf4_gemv_fwd(ctypes.byref(W), p, 4, p, p, 8, 1.0, p, p, need - 1, None) == -4
+    assert lib.qlora_nf4_gemv_fwd(ctypes.byref(W), p, 17, p, p, 8, 1.0, p, p, need, None) == -2
