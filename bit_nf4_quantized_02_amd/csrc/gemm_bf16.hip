@@ -202,9 +202,50 @@ __device__ __forceinline__ void plain_step(const char* Ac, const char* Bc, int w
   }
 }
 
+// The tile's 256 x 256 mask bytes, rows 0-127 into lo and 128-255 into hi
+// (32 KB each, row-major), with direct copies: 8 of 1 KB (4 rows) per wave.
+// Rows past M repeat the last row (never read back); nout is a multiple of
+// 64 for dX, so a 16-byte piece never crosses the end of a row.
+__device__ __forceinline__ void issue_mask_lds(const BfArgs& a, int64_t m0, int64_t n0, int wave, char* lo,
+                                               char* hi) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;                // 1 KB block: rows 4 blk .. +3
+    const int row = blk * 4 + (lane >> 4);
+    const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
+    const int64_t c = n0 + (lane & 15) * 16;
+    const int64_t cc = c + 16 <= a.nout ? c : a.nout - 16;
+    char* dst = (blk < 32 ? lo : hi) + (blk & 31) * 1024;
+    __builtin_amdgcn_global_load_lds((const void*)(a.mask + m * a.nout + cc),
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  }
+}
+
+// Dropout on the accumulators while they hold only the low-rank term: keep
+// scale where the staged mask byte is set, zero where it is not.
+__device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char* lo, const char* hi,
+                                             float keep_scale, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                             int wm0, int wn0, int lane) {
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+      const int c = wn0 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = wm0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const uint8_t mb = *reinterpret_cast<const uint8_t*>((rr < 128 ? lo : hi) + (rr & 127) * 256 + c);
+        const bool keep = m0 + rr < M && n0 + c < N && mb != 0;
+        acc[i][j][v] = keep ? acc[i][j][v] * keep_scale : 0.0f;
+      }
+    }
+}
+
 // kMask: dropout on the low-rank term. A workgroup whose step range holds the
-// low-rank steps runs them first (unpipelined, 1-4 steps), masks and scales
-// the accumulators, then runs its main steps as usual.
+// low-rank steps runs them first (unpipelined, 1-4 steps) on buffers 0 while
+// the tile's mask bytes land in buffers 1, masks and scales the accumulators
+// from there, then runs its main steps as usual.
 template <bool kMask>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
@@ -256,13 +297,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   int nk_end = nk;  // exclusive end of the pipelined range
   if constexpr (kMask) {
     if (nk > nk_main) {
+      issue_mask_lds(a, m0, n0, wave, As1, Bs1);
       for (int step = sbeg > nk_main ? sbeg : nk_main; step < nk; ++step) {
         issue_step(rs, plan, step, nk_main, wave, As0, Bs0);
-        step_barrier<0>();
+        step_barrier<0>();  // (the first one also waits for the mask bytes)
         plain_step(As0, Bs0, wave, acc);
         __syncthreads();  // every wave's reads done before the next copies land
       }
-      mask_acc(acc, a.mask, a.keep_scale, a.M, a.nout, m0, n0, wm0, wn0, lane);
+      mask_acc_lds(acc, As1, Bs1, a.keep_scale, a.M, a.nout, m0, n0, wm0, wn0, lane);
+      __syncthreads();  // mask reads done before the main steps' copies reuse buffers 1
       nk_end = nk_main;
     }
   }
