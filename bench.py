@@ -612,6 +612,43 @@ def dropout_step(wl: Workload, q, steps: int):
     return out
 
 
+def f16_step(wl: Workload, q, steps: int):
+    """The step in fp16 compute: every layer call replaced by its fp16 form
+    over fp16 copies of X, A, B and dY (same shapes, same values rounded to
+    fp16), SiLU calls as they are (same bytes), timed as one region like the
+    step itself. Returns (ms per step, ms per plain step timed the same way)
+    or None for the 65B stack."""
+    if wl.cid == 5:
+        return None
+    P = q._ptr
+    st = q._stream()
+    swap = {}
+    hold = []
+    for p in wl.plans:
+        X, A, B = p.X.half(), p.A.half(), p.B.half()
+        Y = torch.empty(p.Y.shape, dtype=torch.float16, device="cuda")
+        nws = q.linear_workspace_bytes(p.m, p.n, p.k, p.r, False, torch.float16)
+        if p.api_bwd is not None:
+            nws = max(nws, q.linear_workspace_bytes(p.m, p.n, p.k, p.r, True, torch.float16))
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+        wref = q.ctypes.byref(p.wst)
+        swap[id(p.api_fwd)] = q.Call("qlora_linear_fwd_f16", wref, P(X), p.m, P(A), P(B), p.r, p.s, P(Y), P(p.T),
+                                     P(ws), ws.numel(), st, keep=(p.wst,))
+        hold += [X, A, B, Y, ws]
+        if p.api_bwd is not None:
+            dY = p.dY.half()
+            dX = torch.empty(p.dX.shape, dtype=torch.float16, device="cuda")
+            swap[id(p.api_bwd)] = q.Call("qlora_linear_bwd_f16", wref, P(X), P(p.T), P(dY), p.m, P(A), P(B), p.r,
+                                         p.s, P(dX), P(p.dA), P(p.dB), 0, P(ws), ws.numel(), st, keep=(p.wst,))
+            hold += [dY, dX]
+    calls = [swap.get(id(cl), cl) for cl in wl.api]
+    for cl in calls:
+        cl()
+    out = (region_ms(calls, steps), region_ms(wl.api, steps))
+    del hold
+    return out
+
+
 def adamw_rows(wl: Workload, q, reps: int = 20):
     """The AdamW step over every adapter parameter of the workload (A and B
     of each linear, fp32 masters, the step's dA / dB as gradients, bf16 copy
@@ -782,6 +819,7 @@ def main():
     encode = encode_rows(wl, q)
     variants = variant_rows(wl, q)
     drop = dropout_step(wl, q, args.steps)
+    f16 = f16_step(wl, q, args.steps)
     for row in merges.values():
         row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
         row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
@@ -848,6 +886,9 @@ def main():
         "lora_dropout": None if drop is None else {
             "p": 0.05, "ms_per_step": round(drop[0], 4), "tflops": round(wl.flops / (drop[0] * 1e-3) / 1e12, 2),
             "plain_ms_per_step_same_region": round(drop[1], 4), "overhead": round(drop[0] / drop[1], 3)},
+        "fp16_compute": None if f16 is None else {
+            "ms_per_step": round(f16[0], 4), "tflops": round(wl.flops / (f16[0] * 1e-3) / 1e12, 2),
+            "bf16_ms_per_step_same_region": round(f16[1], 4), "ratio": round(f16[0] / f16[1], 3)},
         "lora_bf16_base": None if lora_ms is None else {
             "ms_per_step": round(lora_ms[0], 4),
             "tflops": round(wl.flops / (lora_ms[0] * 1e-3) / 1e12, 2),

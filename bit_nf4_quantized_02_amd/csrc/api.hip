@@ -47,6 +47,15 @@ struct Carver {
 bool small_m(int64_t M) { return M <= 16; }
 
 // Kernel choice per pass (the rule qlora_linear_path documents).
+// fp16 compute (the ablation) runs the GEMV for M <= 16 in the forward and the
+// expanded path otherwise; -1 where that path cannot take the shape.
+int path_of_f16(int64_t M, int64_t n, int64_t k, int r, bool bwd) {
+  if (!bwd && small_m(M)) return QLORA_PATH_GEMV;
+  const int xc = lora_extra_cols(r);
+  const bool fits = bwd ? gemm_bf16_offsets_fit(M, n, xc, k) : gemm_bf16_offsets_fit(M, k, xc, n);
+  return fits && (!bwd || n % 8 == 0) ? QLORA_PATH_EXPANDED : -1;
+}
+
 int path_of(int64_t M, int64_t n, int64_t k, int r, bool bwd) {
   if (!bwd && small_m(M)) return QLORA_PATH_GEMV;
   const int xc = lora_extra_cols(r);
@@ -64,15 +73,17 @@ size_t grad_ws(int64_t M, int64_t C, int r) { return coldot_ws_bytes(M, C, r); }
 
 // T = P Q^T (q_layout 0, Q [r, C]) or P Q (q_layout 1, Q [C, r]); optional split.
 hipError_t do_project(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r, float scale,
-                      float* out, uint16_t* split, void* ws, hipStream_t st, const uint8_t* pmask = nullptr) {
-  return launch_rowdot(P, M, C, Q, q_layout, r, out, split, scale, static_cast<float*>(ws), st, pmask);
+                      float* out, uint16_t* split, void* ws, hipStream_t st, const uint8_t* pmask = nullptr,
+                      bool f16 = false) {
+  return launch_rowdot(P, M, C, Q, q_layout, r, out, split, scale, static_cast<float*>(ws), st, pmask, f16);
 }
 
 hipError_t do_grad(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,
-                   int g_layout, int accumulate, void* ws, hipStream_t st, const uint8_t* pmask = nullptr) {
+                   int g_layout, int accumulate, void* ws, hipStream_t st, const uint8_t* pmask = nullptr,
+                   bool f16 = false) {
   const int64_t g_sc = g_layout == 0 ? 1 : r;
   const int64_t g_sj = g_layout == 0 ? C : 1;
-  return launch_coldot(P, M, C, Q, r, scale, G, g_sc, g_sj, accumulate, static_cast<float*>(ws), st, pmask);
+  return launch_coldot(P, M, C, Q, r, scale, G, g_sc, g_sj, accumulate, static_cast<float*>(ws), st, pmask, f16);
 }
 
 // ---- whole-layer workspaces (layouts shared by the size query and the call)
@@ -85,8 +96,8 @@ struct FwdWs {
   float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
 };
 
-size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o) {
-  const int path = path_of(M, n, k, r, false);
+size_t fwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsave, Carver& cv, FwdWs& o, bool f16 = false) {
+  const int path = f16 ? path_of_f16(M, n, k, r, false) : path_of(M, n, k, r, false);
   if (r > 0) {
     if (path == QLORA_PATH_GEMV) {
       if (!have_tsave) o.T = cv.take<float>((size_t)M * r * 4);
@@ -114,7 +125,7 @@ struct BwdWs {
   float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
 };
 
-size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o) {
+size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o, bool f16 = false) {
   if (r > 0) {
     if (!have_tsaved) o.T = cv.take<float>((size_t)M * r * 4);
     o.U = cv.take<float>((size_t)M * r * 4);
@@ -124,7 +135,7 @@ size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& 
     const size_t g1 = grad_ws(M, k, r), g2 = grad_ws(M, n, r);
     o.grad = cv.take<char>(g1 > g2 ? g1 : g2);
   }
-  if (path_of(M, n, k, r, true) == QLORA_PATH_EXPANDED) {
+  if ((f16 ? path_of_f16(M, n, k, r, true) : path_of(M, n, k, r, true)) == QLORA_PATH_EXPANDED) {
     o.F = cv.take<uint16_t>(expand_ws_bytes(n, k, r, true));
     const size_t pb = gemm_bf16_ws_bytes(M, n, lora_extra_cols(r), k);
     if (pb > 0) o.part = cv.take<float>(pb);
@@ -186,6 +197,14 @@ qlora_status qlora_dequant(const qlora_nf4_weight* w, void* out, void* stream) {
   return hip_status(launch_dequant(view_of(w), static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
 
+qlora_status qlora_dequant_f16(const qlora_nf4_weight* w, void* out, void* stream) {
+  const qlora_status s = check_weight(w);
+  if (s != QLORA_OK) return s;
+  if (out == nullptr || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
+  return hip_status(
+      launch_dequant(view_of(w), static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream), /*f16=*/true));
+}
+
 qlora_status qlora_adapter_merge(const qlora_nf4_weight* w, const void* A, const void* B, int r, float scale,
                                  void* out, int out_dtype, void* stream) {
   const qlora_status s = check_weight(w);
@@ -210,17 +229,25 @@ qlora_status qlora_adapter_unmerge(const void* merged, int64_t n, int64_t k, con
                                  static_cast<hipStream_t>(stream)));
 }
 
-size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
+static size_t linear_ws_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd, bool f16) {
   if (M < 0 || n < 1 || k < 1 || k % QLORA_BLOCK || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (is_bwd != 0 && is_bwd != 1) return 0;
   if (M == 0) return 0;
   Carver cv(nullptr);
   if (!is_bwd) {
     FwdWs o;
-    return fwd_ws(M, n, k, r, /*have_tsave=*/false, cv, o);
+    return fwd_ws(M, n, k, r, /*have_tsave=*/false, cv, o, f16);
   }
   BwdWs o;
-  return bwd_ws(M, n, k, r, /*have_tsaved=*/false, cv, o);
+  return bwd_ws(M, n, k, r, /*have_tsaved=*/false, cv, o, f16);
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
+  return linear_ws_bytes(M, n, k, r, is_bwd, false);
+}
+
+size_t qlora_linear_f16_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
+  return linear_ws_bytes(M, n, k, r, is_bwd, true);
 }
 
 int qlora_lowrank_split_cols(int r) { return (r < 0 || r > QLORA_MAX_RANK) ? 0 : lora_extra_cols(r); }
@@ -355,7 +382,8 @@ qlora_status qlora_lowrank_grad(const void* P, int64_t M, int64_t C, const float
 // receives (X . mask) A^T.
 static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A,
                                     const void* B, int r, float scale, const uint8_t* mask, float keep_scale,
-                                    void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream) {
+                                    void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream,
+                                    bool f16 = false) {
   qlora_status s = check_weight(w);
   if (s != QLORA_OK) return s;
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
@@ -364,16 +392,17 @@ static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, in
   if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
   if (T_save && !aligned16(T_save)) return QLORA_ERR_INVALID_ARG;
   const bool drop = mask != nullptr && r > 0;
+  if (f16 && (drop || path_of_f16(M, w->n, w->k, r, false) < 0)) return QLORA_ERR_UNSUPPORTED;
   {
     Carver probe(nullptr);
     FwdWs tmp;
-    const size_t need = fwd_ws(M, w->n, w->k, r, T_save != nullptr, probe, tmp);
+    const size_t need = fwd_ws(M, w->n, w->k, r, T_save != nullptr, probe, tmp, f16);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
   FwdWs o;
-  fwd_ws(M, w->n, w->k, r, T_save != nullptr, cv, o);
+  fwd_ws(M, w->n, w->k, r, T_save != nullptr, cv, o, f16);
   const Nf4View v = view_of(w);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* a = static_cast<const uint16_t*>(A);
@@ -383,18 +412,19 @@ static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, in
   // the branch's input mask and scale
   const uint8_t* pm = drop ? mask : nullptr;
   const float sb = drop ? scale * keep_scale : scale;
-  const int path = path_of(M, w->n, w->k, r, false);
+  const int path = f16 ? path_of_f16(M, w->n, w->k, r, false) : path_of(M, w->n, w->k, r, false);
   if (path == QLORA_PATH_GEMV) {
     float* T = T_save ? T_save : o.T;
-    if (r > 0) e = do_project(x, M, w->k, a, 0, r, sb, T, nullptr, o.proj, st, pm);
-    if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, sb, y, o.xp, st);
+    if (r > 0) e = do_project(x, M, w->k, a, 0, r, sb, T, nullptr, o.proj, st, pm, f16);
+    if (e == hipSuccess) e = launch_gemv(v, x, M, T, b, r, sb, y, o.xp, st, f16);
   } else {
-    if (r > 0) e = do_project(x, M, w->k, a, 0, r, sb, T_save, o.TS, o.proj, st, pm);
+    if (r > 0) e = do_project(x, M, w->k, a, 0, r, sb, T_save, o.TS, o.proj, st, pm, f16);
     if (path == QLORA_PATH_FUSED) {
       if (e == hipSuccess) e = launch_gemm_fwd(v, x, M, o.TS, b, r, y, st);
     } else {
-      if (e == hipSuccess) e = launch_expand(v, b, r, false, o.F, st);
-      if (e == hipSuccess) e = launch_gemm_bf16(x, M, w->k, o.TS, lora_extra_cols(r), o.F, w->n, y, o.part, st);
+      if (e == hipSuccess) e = launch_expand(v, b, r, false, o.F, st, f16);
+      if (e == hipSuccess)
+        e = launch_gemm_bf16(x, M, w->k, o.TS, lora_extra_cols(r), o.F, w->n, y, o.part, st, nullptr, 1.0f, f16);
     }
   }
   return hip_status(e);
@@ -403,7 +433,7 @@ static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, in
 static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, const float* T_saved,
                                     const void* dY, int64_t M, const void* A, const void* B, int r, float scale,
                                     const uint8_t* mask, float keep_scale, void* dX, float* dA, float* dB,
-                                    int accumulate, void* ws, size_t ws_bytes, void* stream) {
+                                    int accumulate, void* ws, size_t ws_bytes, void* stream, bool f16 = false) {
   qlora_status s = check_weight(w);
   if (s != QLORA_OK) return s;
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
@@ -418,16 +448,18 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
   if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
   if ((dA && !aligned16(dA)) || (dB && !aligned16(dB)) || (T_saved && !aligned16(T_saved)))
     return QLORA_ERR_INVALID_ARG;
+  if (f16 && dX && path_of_f16(M, w->n, w->k, r, true) < 0) return QLORA_ERR_UNSUPPORTED;
+  if (f16 && mask != nullptr && r > 0) return QLORA_ERR_UNSUPPORTED;
   {
     Carver probe(nullptr);
     BwdWs tmp;
-    const size_t need = bwd_ws(M, w->n, w->k, r, T_saved != nullptr, probe, tmp);
+    const size_t need = bwd_ws(M, w->n, w->k, r, T_saved != nullptr, probe, tmp, f16);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   Carver cv(ws);
   BwdWs o;
-  bwd_ws(M, w->n, w->k, r, T_saved != nullptr, cv, o);
+  bwd_ws(M, w->n, w->k, r, T_saved != nullptr, cv, o, f16);
   const Nf4View v = view_of(w);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const uint16_t* dy = static_cast<const uint16_t*>(dY);
@@ -435,13 +467,14 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
   const uint16_t* b = static_cast<const uint16_t*>(B);
   hipError_t e = hipSuccess;
   const uint8_t* dmask = drop ? mask : nullptr;  // dX: dropout on its low-rank term
-  if (r > 0 && (dX || dA)) e = do_project(dy, M, w->n, b, 1, r, scale, o.U, dX ? o.US : nullptr, o.proj, st);
+  if (r > 0 && (dX || dA))
+    e = do_project(dy, M, w->n, b, 1, r, scale, o.U, dX ? o.US : nullptr, o.proj, st, nullptr, f16);
   if (e == hipSuccess && dX) {
-    if (path_of(M, w->n, w->k, r, true) == QLORA_PATH_EXPANDED) {
-      e = launch_expand(v, a, r, true, o.F, st);
+    if (f16 || path_of(M, w->n, w->k, r, true) == QLORA_PATH_EXPANDED) {
+      e = launch_expand(v, a, r, true, o.F, st, f16);
       if (e == hipSuccess)
         e = launch_gemm_bf16(dy, M, w->n, r > 0 ? o.US : nullptr, lora_extra_cols(r), o.F, w->k,
-                             static_cast<uint16_t*>(dX), o.part, st, dmask, keep_scale);
+                             static_cast<uint16_t*>(dX), o.part, st, dmask, keep_scale, f16);
     } else {
       e = launch_gemm_dx(v, dy, M, r > 0 ? o.US : nullptr, a, r, static_cast<uint16_t*>(dX), st, dmask, keep_scale);
     }
@@ -449,14 +482,14 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
   // the branch's input mask and scale for the adapter gradients
   const uint8_t* pm = drop ? mask : nullptr;
   const float sb = drop ? scale * keep_scale : scale;
-  if (e == hipSuccess && dA) e = do_grad(x, M, w->k, o.U, r, sb, dA, 0, accumulate, o.grad, st, pm);
+  if (e == hipSuccess && dA) e = do_grad(x, M, w->k, o.U, r, sb, dA, 0, accumulate, o.grad, st, pm, f16);
   if (e == hipSuccess && dB) {
     const float* T = T_saved;
     if (T == nullptr) {
-      e = do_project(x, M, w->k, a, 0, r, scale, o.T, nullptr, o.proj, st, pm);
+      e = do_project(x, M, w->k, a, 0, r, scale, o.T, nullptr, o.proj, st, pm, f16);
       T = o.T;
     }
-    if (e == hipSuccess) e = do_grad(dy, M, w->n, T, r, sb, dB, 1, accumulate, o.grad, st);
+    if (e == hipSuccess) e = do_grad(dy, M, w->n, T, r, sb, dB, 1, accumulate, o.grad, st, nullptr, f16);
   }
   return hip_status(e);
 }
@@ -473,6 +506,19 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const void* X, const fl
                               float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
   return linear_bwd_impl(w, X, T_saved, dY, M, A, B, r, scale, nullptr, 1.0f, dX, dA, dB, accumulate, ws,
                          ws_bytes, stream);
+}
+
+qlora_status qlora_linear_fwd_f16(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A, const void* B,
+                                  int r, float scale, void* Y, float* T_save, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return linear_fwd_impl(w, X, M, A, B, r, scale, nullptr, 1.0f, Y, T_save, ws, ws_bytes, stream, true);
+}
+
+qlora_status qlora_linear_bwd_f16(const qlora_nf4_weight* w, const void* X, const float* T_saved, const void* dY,
+                                  int64_t M, const void* A, const void* B, int r, float scale, void* dX, float* dA,
+                                  float* dB, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  return linear_bwd_impl(w, X, T_saved, dY, M, A, B, r, scale, nullptr, 1.0f, dX, dA, dB, accumulate, ws,
+                         ws_bytes, stream, true);
 }
 
 qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A,

@@ -35,6 +35,36 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// The 16-bit compute type as a template flag: bf16 (kF16 = false, the
+// default everywhere) or fp16 (the compute-type ablation). Operands travel
+// as 16-byte bit patterns (bf16x8) either way; only the roundings and the
+// MFMA instruction differ. Both roundings are to nearest, ties to even.
+template <bool kF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (kF16) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+template <bool kF16>
+__device__ __forceinline__ uint16_t to16(float x) {
+  if constexpr (kF16) return __builtin_bit_cast(uint16_t, (_Float16)x);
+  else return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+template <bool kF16>
+__device__ __forceinline__ float from16(uint32_t b16) {
+  if constexpr (kF16) return (float)__builtin_bit_cast(_Float16, (uint16_t)b16);
+  else return __uint_as_float(b16 << 16);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
@@ -105,13 +135,14 @@ __device__ __forceinline__ float nf4_scaled(float level, float cprime) {
 // Eight codes of one 32-bit word (code 2t in the low nibble of byte t) ->
 // eight bf16 values as four packed pairs, levels looked up in `lut`
 // (16 fp32 entries, normally in LDS).
+template <bool kF16 = false>
 __device__ __forceinline__ u32x4 dequant8(uint32_t word, const float* lut, float cprime) {
   u32x4 out;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const float a = nf4_scaled(lut[(word >> (8 * p)) & 0xF], cprime);
     const float b = nf4_scaled(lut[(word >> (8 * p + 4)) & 0xF], cprime);
-    out[p] = pack_bf16x2(a, b);
+    out[p] = pack2<kF16>(a, b);
   }
   return out;
 }
@@ -119,17 +150,36 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t word, const float* lut, float
 // The same expansion through a byte-indexed table: lut2[b] holds the level
 // pair (L[b & 15], L[b >> 4]) of the two codes packed in byte b, so one LDS
 // read serves two weights. Products and rounding are those of dequant8.
+template <bool kF16 = false>
 __device__ __forceinline__ u32x4 dequant8_pairs(uint32_t word, const float2* lut2, float cprime) {
   u32x4 out;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const float2 l = lut2[(word >> (8 * p)) & 0xFF];
-    out[p] = pack_bf16x2(nf4_scaled(l.x, cprime), nf4_scaled(l.y, cprime));
+    out[p] = pack2<kF16>(nf4_scaled(l.x, cprime), nf4_scaled(l.y, cprime));
   }
   return out;
 }
 
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <bool kF16>
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (kF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool kF16>
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 // Eight bf16 values with the ones whose mask byte is 0 cleared (mask bytes in
 // element order, little-endian in mk): dropout on the adapter's input.

@@ -16,6 +16,7 @@ namespace qlora {
 
 namespace {
 
+template <bool kF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ code8,
                                                       const float* __restrict__ s2,
@@ -30,19 +31,22 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) {
     const int64_t blk = i >> 3;  // 8 words per 64-weight block
     const float cp = block_scale(code8, s2, mean, blk);
-    out[i] = dequant8(codes[i], lut, cp);
+    out[i] = dequant8<kF16>(codes[i], lut, cp);
   }
 }
 
 }  // namespace
 
-hipError_t launch_dequant(const Nf4View& w, uint16_t* out, hipStream_t stream) {
+hipError_t launch_dequant(const Nf4View& w, uint16_t* out, hipStream_t stream, bool f16) {
   const int64_t nwords = w.n * w.k / 8;
   int64_t blocks = cdiv(nwords, 256);
   if (blocks > 256 * 64) blocks = 256 * 64;
-  dequant_kernel<<<(unsigned)blocks, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(w.codes), w.code8,
-                                                       w.s2, w.mean, w.codebook, nwords,
-                                                       reinterpret_cast<u32x4*>(out));
+  auto* cw = reinterpret_cast<const uint32_t*>(w.codes);
+  auto* o4 = reinterpret_cast<u32x4*>(out);
+  if (f16)
+    dequant_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, nwords, o4);
+  else
+    dequant_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, nwords, o4);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ namespace {
 // LoRA columns of their rows.
 constexpr int kRows = 8;
 
+template <bool kF16>
 __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ code8,
                                                           const float* __restrict__ s2,
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
   }
 #pragma unroll
   for (int i = 0; i < kRows; ++i)
-    if (r0 + i < n) out[(r0 + i) * ldc + c] = dequant8(word[i], lut, decode_block_scale(c8[i], s2v[i], mean));
+    if (r0 + i < n) out[(r0 + i) * ldc + c] = dequant8<kF16>(word[i], lut, decode_block_scale(c8[i], s2v[i], mean));
 }
 
 // Transposing expansion, straight from registers. Workgroup (tn, kb) covers
@@ -110,6 +111,7 @@ __device__ __forceinline__ bool cols_unit(int64_t ntiles1, int64_t kblocks, int6
   return kb < kblocks;
 }
 
+template <bool kF16>
 __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ code8,
                                                           const float* __restrict__ s2,
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
     for (int e = 0; e < 8; ++e) {
       const float va = nf4_scaled(lut[(qa[w] >> (4 * e)) & 0xF], ca);
       const float vb = nf4_scaled(lut[(qb[w] >> (4 * e)) & 0xF], cb);
-      dst[(w * 8 + e) * ldw] = pack_bf16x2(va, vb);
+      dst[(w * 8 + e) * ldw] = pack2<kF16>(va, vb);
     }
 }
 
@@ -175,20 +177,30 @@ size_t expand_ws_bytes(int64_t n, int64_t k, int r, bool transposed) {
 }
 
 hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool transposed, uint16_t* out,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool f16) {
   const int xc = lora_extra_cols(r);
   if (!transposed) {
     const int64_t kw = w.k / 8;
     const dim3 grid((unsigned)cdiv(w.n, (int64_t)kRows), (unsigned)(cdiv(kw, (int64_t)256) + (xc > 0 ? 1 : 0)));
-    expand_rows_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const uint32_t*>(w.codes), w.code8, w.s2, w.mean,
-                                                 w.codebook, w.n, w.k, lr, r, xc, reinterpret_cast<u32x4*>(out));
+    auto* cw = reinterpret_cast<const uint32_t*>(w.codes);
+    auto* o4 = reinterpret_cast<u32x4*>(out);
+    if (f16)
+      expand_rows_kernel<true><<<grid, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, lr, r, xc,
+                                                         o4);
+    else
+      expand_rows_kernel<false><<<grid, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, lr, r,
+                                                          xc, o4);
   } else {
     const int64_t np = expand_pad_rows(w.n);
     const int64_t ntiles = cdiv(np, (int64_t)kXT);
     const int64_t units = (ntiles + (xc > 0 ? 1 : 0)) * cdiv(w.k / kBlock, (int64_t)4);
     const dim3 grid((unsigned)(cdiv(units, (int64_t)8) * 8 * 4));
-    expand_cols_kernel<<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, np, lr, r,
-                                                 xc, out);
+    if (f16)
+      expand_cols_kernel<true><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, np,
+                                                         lr, r, xc, out);
+    else
+      expand_cols_kernel<false><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, np,
+                                                          lr, r, xc, out);
   }
   return hipGetLastError();
 }

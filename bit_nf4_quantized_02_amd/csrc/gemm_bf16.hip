@@ -139,6 +139,7 @@ __device__ __forceinline__ void issue_step(const Rsrc& rs, const CopyPlan& p, in
 // One step: MFMAs on (Ac, Bc) while the copies of step + 1 fill (An, Bn).
 // Restrict pointers tell the compiler the copies cannot alias the fragment
 // reads, so it does not wait for them before reading.
+template <bool kF16>
 __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int step, int nk, int nk_main, int wave,
                                           const char* __restrict__ Ac, const char* __restrict__ Bc,
                                           char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN]) {
@@ -167,7 +168,7 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma32<kF16>(af[cb][i], bfr[cb][j], acc[i][j]);
   }
   // schedule: for substeps 0..2 one fragment read (of the next substep) per
   // MFMA, then the last substep's MFMAs
@@ -184,6 +185,7 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
 }
 
 // One step without copies in flight: fragments of (Ac, Bc) and their MFMAs.
+template <bool kF16>
 __device__ __forceinline__ void plain_step(const char* Ac, const char* Bc, int wave, f32x16 (&acc)[kTM][kTN]) {
   const int lane = threadIdx.x & 63;
   const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
@@ -198,7 +200,7 @@ __device__ __forceinline__ void plain_step(const char* Ac, const char* Bc, int w
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma32<kF16>(af[i], bfr[j], acc[i][j]);
   }
 }
 
@@ -246,7 +248,8 @@ __device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char
 // low-rank steps runs them first (unpipelined, 1-4 steps) on buffers 0 while
 // the tile's mask bytes land in buffers 1, masks and scales the accumulators
 // from there, then runs its main steps as usual.
-template <bool kMask>
+// kF16: fp16 operands and output (the compute-type ablation), else bf16.
+template <bool kMask, bool kF16>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
   // direct copies from the one being read
@@ -301,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
       for (int step = sbeg > nk_main ? sbeg : nk_main; step < nk; ++step) {
         issue_step(rs, plan, step, nk_main, wave, As0, Bs0);
         step_barrier<0>();  // (the first one also waits for the mask bytes)
-        plain_step(As0, Bs0, wave, acc);
+        plain_step<kF16>(As0, Bs0, wave, acc);
         __syncthreads();  // every wave's reads done before the next copies land
       }
       mask_acc_lds(acc, As1, Bs1, a.keep_scale, a.M, a.nout, m0, n0, wm0, wn0, lane);
@@ -313,8 +316,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
     issue_step(rs, plan, sbeg, nk_main, wave, As0, Bs0);
     step_barrier<0>();
     for (int step = sbeg; step < nk_end; step += 2) {
-      bf16_step(rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc);
-      if (step + 1 < nk_end) bf16_step(rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc);
+      bf16_step<kF16>(rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc);
+      if (step + 1 < nk_end) bf16_step<kF16>(rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc);
     }
   }
 
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int rr = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          reg[rr * 64 + j * 32 + (lane & 31)] = to_bf16_bits(acc[i][j][v]);
+          reg[rr * 64 + j * 32 + (lane & 31)] = to16<kF16>(acc[i][j][v]);
         }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // this wave's LDS writes are done
     // 128 rows x 8 chunks of 16 B
@@ -378,6 +381,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
 // Tail tiles: out = RN_bf16(part[0] + part[1] + ... + part[S-1]), added in
 // split order (deterministic; one rounding). Four adjacent outputs of one
 // tile row per thread.
+template <bool kF16>
 __global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(const float* __restrict__ part, int64_t full,
                                                                int64_t tail, int splits, int64_t M, int64_t nout,
                                                                uint16_t* __restrict__ out) {
@@ -401,14 +405,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_reduce_kernel(const float* __re
   uint16_t* const o = out + m * nout + n;
   if (n + 4 <= nout && (nout & 3) == 0) {
     uint2 w;
-    w.x = pack_bf16x2(s.x, s.y);
-    w.y = pack_bf16x2(s.z, s.w);
+    w.x = pack2<kF16>(s.x, s.y);
+    w.y = pack2<kF16>(s.z, s.w);
     *reinterpret_cast<uint2*>(o) = w;
   } else {
     const float e[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (n + i < nout) o[i] = to_bf16_bits(e[i]);
+      if (n + i < nout) o[i] = to16<kF16>(e[i]);
   }
 }
 
@@ -458,7 +462,7 @@ bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
 
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                             const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
-                            const uint8_t* mask, float keep_scale) {
+                            const uint8_t* mask, float keep_scale, bool f16) {
   BfArgs a{};
   a.mask = mask;
   a.keep_scale = keep_scale;
@@ -471,14 +475,25 @@ hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const ui
   a.part = part;
   if (a.splits > 1 && part == nullptr) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.full + a.tail * a.splits));
-  if (mask != nullptr && kx > 0)
-    gemm_bf16_kernel<true><<<grid, kThreads, 0, stream>>>(a);
-  else
-    gemm_bf16_kernel<false><<<grid, kThreads, 0, stream>>>(a);
+  if (f16) {
+    if (mask != nullptr && kx > 0)
+      gemm_bf16_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
+    else
+      gemm_bf16_kernel<false, true><<<grid, kThreads, 0, stream>>>(a);
+  } else {
+    if (mask != nullptr && kx > 0)
+      gemm_bf16_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
+    else
+      gemm_bf16_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
+  }
   if (a.splits > 1) {
     const int64_t groups = a.tail * (kBM * kBN / 4);
-    gemm_bf16_reduce_kernel<<<dim3((unsigned)cdiv(groups, (int64_t)256)), 256, 0, stream>>>(
-        part, a.full, a.tail, a.splits, M, nout, out);
+    if (f16)
+      gemm_bf16_reduce_kernel<true><<<dim3((unsigned)cdiv(groups, (int64_t)256)), 256, 0, stream>>>(
+          part, a.full, a.tail, a.splits, M, nout, out);
+    else
+      gemm_bf16_reduce_kernel<false><<<dim3((unsigned)cdiv(groups, (int64_t)256)), 256, 0, stream>>>(
+          part, a.full, a.tail, a.splits, M, nout, out);
   }
   return hipGetLastError();
 }

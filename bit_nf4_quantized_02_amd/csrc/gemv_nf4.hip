@@ -53,7 +53,8 @@ __global__ __launch_bounds__(256) void gemv_xperm_kernel(const uint16_t* __restr
 }
 
 // kXp: activations from the operand-ordered copy Xp (else read in place from X).
-template <int NT, int kW, bool kLora, bool kXp>
+// kF16: fp16 activations, weights, B and output (the compute-type ablation).
+template <int NT, int kW, bool kLora, bool kXp, bool kF16>
 __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ code8,
                                                        const float* __restrict__ s2,
@@ -158,8 +159,8 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const uint32_t word = use ? st.cw[i][s >> 2][s & 3] : 0x77777777u;  // code 7: level 0
-        const u32x4 bw = dequant8_pairs(word, lut2, cp);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[s], __builtin_bit_cast(bf16x8, bw), acc[i], 0, 0, 0);
+        const u32x4 bw = dequant8_pairs<kF16>(word, lut2, cp);
+        acc[i] = mfma16<kF16>(xa[s], __builtin_bit_cast(bf16x8, bw), acc[i]);
       }
     }
   };
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
       for (int j0 = 0; j0 < r; j0 += 4) {
         const int j = j0 + (lane >> 4);
         const float a = (m < M && j < r) ? T[m * r + j] : 0.0f;
-        const float b = (n < N && j < r) ? bf16_bits_to_f32(B[n * r + j]) : 0.0f;
+        const float b = (n < N && j < r) ? from16<kF16>(B[n * r + j]) : 0.0f;
         l = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, l, 0, 0, 0);
       }
 #pragma unroll
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
 #pragma unroll
     for (int w2 = 1; w2 < kW; ++w2) y += red[w2][i][m][nc];  // in wave order
     if constexpr (kLora) y = fmaf(scale, lred[i][m][nc], y);
-    Y[m * N + n] = to_bf16_bits(y);
+    Y[m * N + n] = to16<kF16>(y);
   }
 }
 
@@ -227,7 +228,7 @@ size_t gemv_ws_bytes(int64_t k) { return align256((size_t)cdiv(k, 256) * 512 * 1
 constexpr int64_t kXpMinM = QLORA_GEMV_XP_MIN_M;
 
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T, const uint16_t* B, int r,
-                       float scale, uint16_t* Y, void* ws, hipStream_t stream) {
+                       float scale, uint16_t* Y, void* ws, hipStream_t stream, bool f16) {
   u32x4* Xp = static_cast<u32x4*>(ws);
   const bool xp = M >= kXpMinM;
   if (xp) {
@@ -239,19 +240,22 @@ hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const flo
   // 8192 rows (256 workgroups, each wave an eighth of the 28672-long
   // contraction), 16 rows and 4 waves below.
   const bool lora = r > 0;
-#define QLORA_GEMV2(NT, W, L, XP)                                                                              \
-  gemv_nf4_kernel<NT, W, L, XP><<<dim3((unsigned)cdiv(w.n, NT)), 64 * W, 0, stream>>>(                         \
+#define QLORA_GEMV3(NT, W, L, XP, H)                                                                           \
+  gemv_nf4_kernel<NT, W, L, XP, H><<<dim3((unsigned)cdiv(w.n, NT)), 64 * W, 0, stream>>>(                      \
       w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, X, Xp, M, T, B, r, scale, Y)
+#define QLORA_GEMV2(NT, W, L, XP) \
+  if (f16) QLORA_GEMV3(NT, W, L, XP, true); else QLORA_GEMV3(NT, W, L, XP, false);
 #define QLORA_GEMV(NT, W)                                                   \
   {                                                                         \
-    if (lora) { if (xp) QLORA_GEMV2(NT, W, true, true); else QLORA_GEMV2(NT, W, true, false); } \
-    else { if (xp) QLORA_GEMV2(NT, W, false, true); else QLORA_GEMV2(NT, W, false, false); }    \
+    if (lora) { if (xp) { QLORA_GEMV2(NT, W, true, true) } else { QLORA_GEMV2(NT, W, true, false) } } \
+    else { if (xp) { QLORA_GEMV2(NT, W, false, true) } else { QLORA_GEMV2(NT, W, false, false) } }    \
   }
   if (w.n / 64 >= 448) QLORA_GEMV(64, 4)
   else if (w.n / 32 >= 256) QLORA_GEMV(32, 8)
   else QLORA_GEMV(16, 4)
 #undef QLORA_GEMV
 #undef QLORA_GEMV2
+#undef QLORA_GEMV3
   return hipGetLastError();
 }
 

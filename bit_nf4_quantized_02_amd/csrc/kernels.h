@@ -32,7 +32,7 @@ struct Nf4View {
   const float* codebook;
 };
 
-hipError_t launch_dequant(const Nf4View& w, uint16_t* out, hipStream_t stream);
+hipError_t launch_dequant(const Nf4View& w, uint16_t* out, hipStream_t stream, bool f16 = false);
 
 // Columns of the LoRA "extra" contraction region: [hi | lo] halves of the
 // scaled low-rank activation, padded with zeros to a multiple of 64.
@@ -47,7 +47,7 @@ size_t rowdot_ws_bytes(int64_t M, int64_t C, int r);
 // elements whose byte is 0 read as zero (dropout on the adapter's input).
 hipError_t launch_rowdot(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r,
                          float* out, uint16_t* split, float scale, float* part, hipStream_t stream,
-                         const uint8_t* pmask = nullptr);
+                         const uint8_t* pmask = nullptr, bool f16 = false);
 
 // Column reduction over M in fixed order, for the adapter gradients:
 //   G[c, j] (+)= scale * sum_m P[m, c] * Q[m, j]    P bf16 [M, C], Q fp32 [M, r]
@@ -56,7 +56,7 @@ int coldot_splits(int64_t M);
 size_t coldot_ws_bytes(int64_t M, int64_t C, int r);
 hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale,
                          float* G, int64_t g_sc, int64_t g_sj, int accumulate, float* partial,
-                         hipStream_t stream, const uint8_t* pmask = nullptr);
+                         hipStream_t stream, const uint8_t* pmask = nullptr, bool f16 = false);
 
 // Y = RN_bf16(X W'^T + [sT_hi | sT_lo] [B | B]^T): fused dequant + MFMA GEMM.
 hipError_t launch_gemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* TS,
@@ -72,7 +72,7 @@ hipError_t launch_gemm_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const
 int64_t expand_pad_rows(int64_t n);
 size_t expand_ws_bytes(int64_t n, int64_t k, int r, bool transposed);
 hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool transposed, uint16_t* out,
-                         hipStream_t stream);
+                         hipStream_t stream, bool f16 = false);
 
 // out = RN_bf16([act | split] F^T) over an expanded operand F [nout, kcp + kx].
 // The kernel addresses each operand with 32-bit byte offsets: every operand
@@ -89,7 +89,7 @@ size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout);
 // before the main contraction is added (one rounding of the whole sum).
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                             const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
-                            const uint8_t* mask = nullptr, float keep_scale = 1.0f);
+                            const uint8_t* mask = nullptr, float keep_scale = 1.0f, bool f16 = false);
 
 // Adapter merge: out = round(W' + scale * B A) (w != NULL; bf16, or fp32 if
 // out_f32) or unmerge: out = RN_bf16(Wm - scale * B A) (w == NULL, Wm bf16).
@@ -101,7 +101,8 @@ hipError_t launch_merge(const Nf4View* w, const uint16_t* Wm, int64_t n, int64_t
 // gemv_ws_bytes(k) bytes for the activations in operand order.
 size_t gemv_ws_bytes(int64_t k);
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T,
-                       const uint16_t* B, int r, float scale, uint16_t* Y, void* ws, hipStream_t stream);
+                       const uint16_t* B, int r, float scale, uint16_t* Y, void* ws, hipStream_t stream,
+                       bool f16 = false);
 
 hipError_t launch_silu_fwd(const uint16_t* G, const uint16_t* U, uint16_t* H, int64_t count,
                            hipStream_t stream);

@@ -66,7 +66,8 @@ __device__ __forceinline__ bf16x8 tr_operand(const char* tile, int pitch, int c0
 
 // kMask (16-byte P rows only): P's elements whose byte in pmask [M, C] is 0
 // read as zero (dropout on the adapter's input).
-template <int kRP, bool kVec, bool kMask = false>
+// kF16: fp16 P and fp16 hi/lo halves of Q (the compute-type ablation).
+template <int kRP, bool kVec, bool kMask = false, bool kF16 = false>
 __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
                                                           const float* __restrict__ Q, int r, int64_t mchunk,
                                                           float* __restrict__ partial,
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
     for (int e = 0; e < kQE; ++e) {
       const int idx = t + 256 * e;
       const int mm = idx / kRP, j = idx % kRP;
-      const uint16_t qh = to_bf16_bits(stg.q[e]);
-      const uint16_t ql = to_bf16_bits(stg.q[e] - bf16_bits_to_f32(qh));
+      const uint16_t qh = to16<kF16>(stg.q[e]);
+      const uint16_t ql = to16<kF16>(stg.q[e] - from16<kF16>(qh));
       *reinterpret_cast<uint16_t*>(sm.qh + mm * kQP + j * 2) = qh;
       *reinterpret_cast<uint16_t*>(sm.ql + mm * kQP + j * 2) = ql;
     }
@@ -163,8 +164,8 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
       const bf16x8 al = tr_operand(sm.ql, kQP, a * 16, lane);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, pb[ct], acc[a][ct], 0, 0, 0);
-        acc[a][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, pb[ct], acc[a][ct], 0, 0, 0);
+        acc[a][ct] = mfma16<kF16>(ah, pb[ct], acc[a][ct]);
+        acc[a][ct] = mfma16<kF16>(al, pb[ct], acc[a][ct]);
       }
     }
     __syncthreads();
@@ -241,14 +242,19 @@ size_t coldot_ws_bytes(int64_t M, int64_t C, int r) {
 
 hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,
                          int64_t g_sc, int64_t g_sj, int accumulate, float* partial, hipStream_t stream,
-                         const uint8_t* pmask) {
+                         const uint8_t* pmask, bool f16) {
   const int ns = coldot_splits(M);
   const int64_t mchunk = cdiv(cdiv(M, ns), 32) * 32;
   const dim3 grid((unsigned)cdiv(C, 256), (unsigned)ns);
   const bool vec = C % 8 == 0;
   if (pmask != nullptr && !vec) return hipErrorInvalidValue;
+  if (pmask != nullptr && f16) return hipErrorInvalidValue;
 #define QLORA_COLDOT(RP)                                                                                    \
-  if (pmask != nullptr)                                                                                    \
+  if (f16 && vec)                                                                                          \
+    coldot_mfma_kernel<RP, true, false, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);   \
+  else if (f16)                                                                                            \
+    coldot_mfma_kernel<RP, false, false, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);  \
+  else if (pmask != nullptr)                                                                               \
     coldot_mfma_kernel<RP, true, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial, pmask);   \
   else if (vec) coldot_mfma_kernel<RP, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);    \
   else coldot_mfma_kernel<RP, false><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);

@@ -66,7 +66,8 @@ struct RowdotCfg {
 // kDirect: write out / split (single column split), else write partials.
 // kMask (Q = A only): P's elements whose byte in pmask [M, C] is 0 read as zero
 // (dropout on the adapter's input).
-template <int kRP, int kQL, bool kVecP, bool kVecQ, bool kDirect, bool kMask = false>
+// kF16: fp16 operands and split (the compute-type ablation), else bf16.
+template <int kRP, int kQL, bool kVecP, bool kVecQ, bool kDirect, bool kMask = false, bool kF16 = false>
 __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
     const uint16_t* __restrict__ P, int64_t M, int64_t C, const uint16_t* __restrict__ Q, int r, int64_t cchunk,
     float* __restrict__ out, uint16_t* __restrict__ split, int xc, float scale, float* __restrict__ part,
@@ -183,8 +184,8 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int t = 0; t < kTiles; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, kMask ? apply_mask8(bt.a[u], bt.mk[u]) : bt.a[u]), b[u][t], acc[t], 0, 0, 0);
+        acc[t] = mfma16<kF16>(__builtin_bit_cast(bf16x8, kMask ? apply_mask8(bt.a[u], bt.mk[u]) : bt.a[u]), b[u][t],
+                              acc[t]);
   };
   constexpr int64_t kStep = 32 * kU;
   if constexpr (!kVecP || !kVecQ) {
@@ -228,8 +229,8 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
         for (int w = 1; w < kNW; ++w) s += red[(w * 16 + rr) * kRP + j];  // parts in order
         if (col < r && out != nullptr) out[mm * r + j] = s;
         const float ss = scale * s;
-        const uint16_t hi = to_bf16_bits(ss);
-        split[mm * xc + col] = col < r ? hi : to_bf16_bits(ss - bf16_bits_to_f32(hi));
+        const uint16_t hi = to16<kF16>(ss);
+        split[mm * xc + col] = col < r ? hi : to16<kF16>(ss - from16<kF16>(hi));
       } else {
         split[mm * xc + col] = 0;
       }
@@ -261,6 +262,7 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
 // Partials of the small-M case -> out / split. Block = one row m; G = 256 / r
 // thread groups each add splits g, g + G, ... in order; then thread j adds the
 // G group sums in order.
+template <bool kF16>
 __global__ __launch_bounds__(256) void rowdot_finalize_kernel(const float* __restrict__ part, int64_t M, int r,
                                                               int64_t nsplit, float* __restrict__ out,
                                                               uint16_t* __restrict__ split, int xc, float scale) {
@@ -298,8 +300,8 @@ __global__ __launch_bounds__(256) void rowdot_finalize_kernel(const float* __res
       uint16_t v = 0;
       if (col < 2 * r) {
         const float ss = scale * tot[col < r ? col : col - r];
-        const uint16_t hi = to_bf16_bits(ss);
-        v = col < r ? hi : to_bf16_bits(ss - bf16_bits_to_f32(hi));
+        const uint16_t hi = to16<kF16>(ss);
+        v = col < r ? hi : to16<kF16>(ss - from16<kF16>(hi));
       }
       split[m * xc + col] = v;
     }
@@ -317,7 +319,7 @@ int rowdot_splits(int64_t M, int64_t C) {
 
 template <int kRP, int kQL>
 hipError_t launch_rp(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
-                     uint16_t* split, float scale, float* part, hipStream_t stream, const uint8_t* pmask) {
+                     uint16_t* split, float scale, float* part, hipStream_t stream, const uint8_t* pmask, bool f16) {
   constexpr int kNW = RowdotCfg<kRP, kQL>::kNW;
   const int ns = rowdot_splits(M, C);
   const int64_t cchunk = cdiv(cdiv(C, (int64_t)ns), (int64_t)32) * 32;
@@ -330,8 +332,17 @@ hipError_t launch_rp(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q,
 #define QLORA_RDM(VQ, D)                                                                                   \
   rowdot_kernel<kRP, 0, true, VQ, D, true><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, split, xc, \
                                                                           scale, part, pmask)
+#define QLORA_RDF(VP, VQ, D)                                                                               \
+  rowdot_kernel<kRP, kQL, VP, VQ, D, false, true><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, \
+                                                                               split, xc, scale, part)
 #define QLORA_RD2(D)                                           \
-  if constexpr (kQL == 0) {                                    \
+  if (f16) {                                                   \
+    if (pmask != nullptr) return hipErrorInvalidValue;         \
+    if (vp && vq) QLORA_RDF(true, true, D);                    \
+    else if (vp) QLORA_RDF(true, false, D);                    \
+    else if (vq) QLORA_RDF(false, true, D);                    \
+    else QLORA_RDF(false, false, D);                           \
+  } else if constexpr (kQL == 0) {                             \
     if (pmask != nullptr) {                                    \
       if (!vp) return hipErrorInvalidValue;                    \
       if (vq) QLORA_RDM(true, D); else QLORA_RDM(false, D);    \
@@ -352,11 +363,15 @@ hipError_t launch_rp(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q,
   }
   QLORA_RD2(false)
 #undef QLORA_RD2
+#undef QLORA_RDF
 #undef QLORA_RDM
 #undef QLORA_RD
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  rowdot_finalize_kernel<<<(unsigned)M, 256, 0, stream>>>(part, M, r, ns, out, split, xc, scale);
+  if (f16)
+    rowdot_finalize_kernel<true><<<(unsigned)M, 256, 0, stream>>>(part, M, r, ns, out, split, xc, scale);
+  else
+    rowdot_finalize_kernel<false><<<(unsigned)M, 256, 0, stream>>>(part, M, r, ns, out, split, xc, scale);
   return hipGetLastError();
 }
 
@@ -369,10 +384,10 @@ size_t rowdot_ws_bytes(int64_t M, int64_t C, int r) {
 
 hipError_t launch_rowdot(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int q_layout, int r,
                          float* out, uint16_t* split, float scale, float* part, hipStream_t stream,
-                         const uint8_t* pmask) {
-#define QLORA_RP(RP)                                                                             \
-  return q_layout == 0 ? launch_rp<RP, 0>(P, M, C, Q, r, out, split, scale, part, stream, pmask) \
-                       : launch_rp<RP, 1>(P, M, C, Q, r, out, split, scale, part, stream, pmask);
+                         const uint8_t* pmask, bool f16) {
+#define QLORA_RP(RP)                                                                                  \
+  return q_layout == 0 ? launch_rp<RP, 0>(P, M, C, Q, r, out, split, scale, part, stream, pmask, f16) \
+                       : launch_rp<RP, 1>(P, M, C, Q, r, out, split, scale, part, stream, pmask, f16);
   if (r <= 16) { QLORA_RP(16) }
   if (r <= 32) { QLORA_RP(32) }
   if (r <= 64) { QLORA_RP(64) }

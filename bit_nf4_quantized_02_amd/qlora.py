@@ -55,6 +55,11 @@ _SIGS = {
     "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
     "qlora_linear_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "qlora_dequant_f16": (_int, [_W, _vp, _vp]),
+    "qlora_linear_f16_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
+    "qlora_linear_fwd_f16": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_linear_bwd_f16": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int, _vp, _sz,
+                                     _vp]),
     "qlora_linear_fwd_dropout": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd_dropout": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _f, _vp, _vp, _vp, _int,
                                          _vp, _sz, _vp]),
@@ -145,8 +150,16 @@ def quantize_workspace_bytes(n: int, k: int) -> int:
     return int(_lib.qlora_quantize_workspace_bytes(n, k))
 
 
-def linear_workspace_bytes(M: int, n: int, k: int, r: int, is_bwd: bool) -> int:
-    return int(_lib.qlora_linear_workspace_bytes(M, n, k, r, int(bool(is_bwd))))
+def linear_workspace_bytes(M: int, n: int, k: int, r: int, is_bwd: bool, dtype=torch.bfloat16) -> int:
+    fn = _lib.qlora_linear_f16_workspace_bytes if _is_f16(dtype) else _lib.qlora_linear_workspace_bytes
+    return int(fn(M, n, k, r, int(bool(is_bwd))))
+
+
+def _is_f16(dtype) -> bool:
+    """The 16-bit compute type of a layer call: bf16 (default) or fp16."""
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"compute dtype must be torch.bfloat16 or torch.float16, got {dtype}")
+    return dtype == torch.float16
 
 
 # --------------------------------------------------------------------------- weight
@@ -217,13 +230,15 @@ def quantize_nf4(W: torch.Tensor, out: NF4Weight | None = None, ws: torch.Tensor
     return out
 
 
-def dequant(w: NF4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """bf16 [n, k] expansion, bit-identical to what the GEMM kernels multiply."""
+def dequant(w: NF4Weight, out: torch.Tensor | None = None, stream=None, dtype=torch.bfloat16) -> torch.Tensor:
+    """[n, k] expansion in bf16 (or fp16), bit-identical to what the GEMM kernels multiply."""
+    f16 = _is_f16(dtype)
     if out is None:
-        out = torch.empty((w.n, w.k), dtype=torch.bfloat16, device=w.codes.device)
-    _need(out, torch.bfloat16, (w.n, w.k), "out")
+        out = torch.empty((w.n, w.k), dtype=dtype, device=w.codes.device)
+    _need(out, dtype, (w.n, w.k), "out")
     st = w.struct()
-    _check(_lib.qlora_dequant(ctypes.byref(st), _ptr(out), _stream(stream)), "qlora_dequant")
+    name = "qlora_dequant_f16" if f16 else "qlora_dequant"
+    _check(getattr(_lib, name)(ctypes.byref(st), _ptr(out), _stream(stream)), name)
     return out
 
 
@@ -251,17 +266,19 @@ def linear_bwd_dropout(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | N
 
 def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, scale: float,
                Y: torch.Tensor | None = None, T: torch.Tensor | None = None, save_T: bool = True,
-               ws: torch.Tensor | None = None, stream=None, _dropout=None):
-    """Y = X W'^T + scale (X A^T) B^T.  Returns (Y, T) with T None unless saved."""
+               ws: torch.Tensor | None = None, stream=None, _dropout=None, dtype=torch.bfloat16):
+    """Y = X W'^T + scale (X A^T) B^T.  Returns (Y, T) with T None unless saved.
+    dtype=torch.float16 runs the fp16 layer (qlora_linear_fwd_f16)."""
     M = X.shape[0]
     r = 0 if A is None else A.shape[0]
-    _need(X, torch.bfloat16, (M, w.k), "X")
+    f16 = _is_f16(dtype)
+    _need(X, dtype, (M, w.k), "X")
     if r:
-        _need(A, torch.bfloat16, (r, w.k), "A")
-        _need(B, torch.bfloat16, (w.n, r), "B")
+        _need(A, dtype, (r, w.k), "A")
+        _need(B, dtype, (w.n, r), "B")
     if Y is None:
-        Y = torch.empty((M, w.n), dtype=torch.bfloat16, device=X.device)
-    _need(Y, torch.bfloat16, (M, w.n), "Y")
+        Y = torch.empty((M, w.n), dtype=dtype, device=X.device)
+    _need(Y, dtype, (M, w.n), "Y")
     if T is None and save_T and r:
         T = torch.empty((M, r), dtype=torch.float32, device=X.device)
     if T is not None:
@@ -276,10 +293,13 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
                                              0 if ws is None else ws.numel(), _stream(stream)),
                "qlora_linear_fwd_dropout")
         return Y, T
+    if f16 and _dropout is not None:
+        raise ValueError("LoRA dropout runs in bf16 only")
     if ws is None:
-        ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, False), X.device)
-    _check(_lib.qlora_linear_fwd(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), _ptr(Y), _ptr(T),
-                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_fwd")
+        ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, False, dtype), X.device)
+    name = "qlora_linear_fwd_f16" if f16 else "qlora_linear_fwd"
+    _check(getattr(_lib, name)(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), _ptr(Y), _ptr(T),
+                               _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), name)
     return Y, T
 
 
@@ -287,27 +307,31 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY:
                A: torch.Tensor | None, B: torch.Tensor | None, scale: float, need_dX: bool = True,
                need_dA: bool = True, need_dB: bool = True, dX: torch.Tensor | None = None,
                dA: torch.Tensor | None = None, dB: torch.Tensor | None = None, accumulate: bool = False,
-               ws: torch.Tensor | None = None, stream=None, _dropout=None):
-    """dX = dY W' + s (dY B) A;  dA = s (dY B)^T X;  dB = s dY^T T.  Returns (dX, dA, dB)."""
+               ws: torch.Tensor | None = None, stream=None, _dropout=None, dtype=torch.bfloat16):
+    """dX = dY W' + s (dY B) A;  dA = s (dY B)^T X;  dB = s dY^T T.  Returns (dX, dA, dB).
+    dtype=torch.float16 runs the fp16 layer (qlora_linear_bwd_f16)."""
     M = dY.shape[0]
     r = 0 if A is None else A.shape[0]
     dev = dY.device
-    _need(dY, torch.bfloat16, (M, w.n), "dY")
+    f16 = _is_f16(dtype)
+    if f16 and _dropout is not None:
+        raise ValueError("LoRA dropout runs in bf16 only")
+    _need(dY, dtype, (M, w.n), "dY")
     if X is not None:
-        _need(X, torch.bfloat16, (M, w.k), "X")
+        _need(X, dtype, (M, w.k), "X")
     if r:
-        _need(A, torch.bfloat16, (r, w.k), "A")
-        _need(B, torch.bfloat16, (w.n, r), "B")
+        _need(A, dtype, (r, w.k), "A")
+        _need(B, dtype, (w.n, r), "B")
     if T is not None:
         _need(T, torch.float32, (M, r), "T")
     if need_dX and dX is None:
-        dX = torch.empty((M, w.k), dtype=torch.bfloat16, device=dev)
+        dX = torch.empty((M, w.k), dtype=dtype, device=dev)
     if r and need_dA and dA is None:
         dA = (torch.zeros if accumulate else torch.empty)((r, w.k), dtype=torch.float32, device=dev)
     if r and need_dB and dB is None:
         dB = (torch.zeros if accumulate else torch.empty)((w.n, r), dtype=torch.float32, device=dev)
     if dX is not None:
-        _need(dX, torch.bfloat16, (M, w.k), "dX")
+        _need(dX, dtype, (M, w.k), "dX")
     if dA is not None:
         _need(dA, torch.float32, (r, w.k), "dA")
     if dB is not None:
@@ -323,10 +347,11 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY:
                                              _stream(stream)), "qlora_linear_bwd_dropout")
         return dX, dA, dB
     if ws is None:
-        ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, True), dev)
-    _check(_lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(T), _ptr(dY), M, _ptr(A), _ptr(B), r, float(scale),
-                                 _ptr(dX), _ptr(dA), _ptr(dB), int(bool(accumulate)), _ptr(ws),
-                                 0 if ws is None else ws.numel(), _stream(stream)), "qlora_linear_bwd")
+        ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, True, dtype), dev)
+    name = "qlora_linear_bwd_f16" if f16 else "qlora_linear_bwd"
+    _check(getattr(_lib, name)(ctypes.byref(st), _ptr(X), _ptr(T), _ptr(dY), M, _ptr(A), _ptr(B), r, float(scale),
+                               _ptr(dX), _ptr(dA), _ptr(dB), int(bool(accumulate)), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(stream)), name)
     return dX, dA, dB
 
 

@@ -234,6 +234,38 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight *w, const void *X, 
                                       const void *mask, float keep_scale, void *dX, float *dA, float *dB,
                                       int accumulate, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * The layer in fp16 instead of bf16, the other 16-bit compute type the pages
+ * use ("QLoRA vs LoRA: How Quantized Low-Rank Adaptation Reduces Memory ..."
+ * (instagit.com), "Implementation Guide", "QLoRA Fine-Tuning with 4-Bit
+ * Quantization": a float16 compute dtype for the 4-bit base; "QLoRA
+ * Explained ..." (gamut.so), the LoRA / QLoRA / full fine-tuning table:
+ * fp16 or bf16 16-bit precision). Same storage, same arithmetic, with every 16-bit
+ * value read or written in IEEE binary16 (round to nearest even):
+ *   w'  = RN_fp16(RN32(L[code] * c'))            (qlora_dequant_f16)
+ *   Y   = RN_fp16( X W'^T + scale * T B^T ),  dX = RN_fp16( dY W' + scale * U A )
+ * X, A, B, Y, dY, dX and out (device) are fp16 in the layouts of the bf16
+ * calls; T_save / T_saved, dA and dB stay fp32. The low-rank term enters the
+ * products as fp16 hi / lo pairs of scale * T (and scale * U). Kernels: the
+ * dequant-GEMV for M <= 16 in the forward, otherwise one expansion into
+ * workspace followed by the 16-bit GEMM (the medium-M fused kernel is bf16
+ * only). Workspace: qlora_linear_f16_workspace_bytes (is_bwd as for
+ * qlora_linear_workspace_bytes). Values beyond the fp16 range (65504)
+ * become infinities, as in any fp16 arithmetic; the caller scales.
+ * Errors: as qlora_linear_fwd / qlora_linear_bwd, and UNSUPPORTED for a
+ * backward with dX whose n is not a multiple of 8 (dA and dB alone are
+ * computed at any n).
+ */
+qlora_status qlora_dequant_f16(const qlora_nf4_weight *w, void *out, void *stream);
+size_t qlora_linear_f16_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd);
+qlora_status qlora_linear_fwd_f16(const qlora_nf4_weight *w, const void *X, int64_t M,
+                                  const void *A, const void *B, int r, float scale,
+                                  void *Y, float *T_save, void *ws, size_t ws_bytes, void *stream);
+qlora_status qlora_linear_bwd_f16(const qlora_nf4_weight *w, const void *X, const float *T_saved,
+                                  const void *dY, int64_t M, const void *A, const void *B, int r,
+                                  float scale, void *dX, float *dA, float *dB, int accumulate,
+                                  void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * Building blocks. qlora_linear_fwd and qlora_linear_bwd are compositions of
  * the calls below (same kernels, same order); they are exported so a caller

@@ -96,6 +96,14 @@ def bf16_floor(Zref) -> float:
     return relerr(r, z)
 
 
+def fp16_floor(Zref) -> float:
+    """relerr of Zref rounded once to fp16 (RNE, via ``oracle.nf4.fp16_round``):
+    the least error an fp16 output can have."""
+    from oracle.nf4 import fp16_round
+    z = np.asarray(Zref, dtype=np.float64)
+    return relerr(fp16_round(z.astype(np.float32)), z)
+
+
 def linear_fwd_dropout(X, Wd, A, B, s, mask, keep_scale):
     """The forward with dropout on the adapter's input (reading: the usual
     inverted dropout of a LoRA branch; the pages give the rate, 0.05, not the

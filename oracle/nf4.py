@@ -51,6 +51,11 @@ the block constants in full precision):
       magnitude and is never chosen (the symmetric absmax INT4 grid).
   R10 no double quantization: c' = c_b, the fp32 block absmax, stored as is
       (one fp32 per block instead of one byte plus shares of s2 and mean).
+  R11 fp16 compute (the other 16-bit compute type the pages use: "QLoRA vs
+      LoRA ..." (instagit.com), "QLoRA Fine-Tuning with 4-Bit Quantization",
+      a float16 compute dtype): w' = RN_fp16(RN32(L[code] * c')), IEEE
+      binary16 with round-to-nearest-even, gradual underflow below 2^-14 and
+      overflow to infinity from 65520 up.
 """
 
 from __future__ import annotations
@@ -292,6 +297,61 @@ def dequant(codes, cprime, levels) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# fp16 (reading R11), written from the IEEE 754 binary16 definition:
+# 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; normal numbers
+# 2^-14 <= |x| <= 65504, subnormal spacing 2^-24.
+# --------------------------------------------------------------------------
+
+FP16_MAX = 65504.0
+
+
+def fp16_round(x) -> np.ndarray:
+    """Round to the nearest binary16 value, ties to even, in fp64 (exact for
+    fp32 input): the spacing at |x| in [2^e, 2^(e+1)) is 2^(e-10), and 2^-24
+    throughout the subnormal range e < -14. Overflow gives +-inf (a rounded
+    magnitude above 65504 is one that reached 65536)."""
+    x = np.asarray(x, dtype=np.float64)
+    _, ex = np.frexp(np.abs(x))                  # |x| = m 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -14)                  # floor(log2 |x|), clamped at the subnormal range
+    q = np.ldexp(1.0, e - 10)                    # spacing of binary16 at |x|
+    r = np.rint(x / q) * q                       # rint: nearest integer, ties to even; x / q exact
+    r = np.where(np.abs(r) > FP16_MAX, np.copysign(np.inf, x), r)
+    return np.where(r == 0, np.copysign(0.0, x), r)
+
+
+def fp16_bits_of(v) -> np.ndarray:
+    """Bit patterns of values that are already binary16 numbers (fp64 in)."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.signbit(v).astype(np.uint16) << np.uint16(15)
+    a = np.abs(v)
+    out = np.zeros(v.shape, dtype=np.uint16)
+    inf = np.isinf(a)
+    sub = (a < 2.0 ** -14) & ~inf
+    nrm = ~sub & ~inf
+    out[sub] = (a[sub] / 2.0 ** -24).astype(np.uint16)
+    m, ex = np.frexp(a[nrm])                     # a = m 2^ex, m in [0.5, 1)
+    biased = (ex - 1 + 15).astype(np.uint16)
+    frac = ((m * 2.0 - 1.0) * 1024.0).astype(np.uint16)
+    out[nrm] = (biased << np.uint16(10)) | frac
+    out[inf] = 0x7C00
+    return out | sign
+
+
+def scaled_levels(codes: np.ndarray, cprime: np.ndarray, levels: np.ndarray) -> np.ndarray:
+    """RN32(L[code_i] * c'_b), the fp32 product both 16-bit roundings start from, [N, K]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    lv = np.asarray(levels, dtype=np.float32)
+    c = np.asarray(cprime, dtype=np.float32).reshape(N, K // BLOCK)
+    return (lv[codes].reshape(N, K // BLOCK, BLOCK) * c[:, :, None]).astype(np.float32).reshape(N, K)
+
+
+def dequant_f16_bits(codes: np.ndarray, cprime: np.ndarray, levels: np.ndarray) -> np.ndarray:
+    """w'_i = RN_fp16(RN32(L[code_i] * c'_b)) as binary16 bit patterns, [N, K] uint16."""
+    return fp16_bits_of(fp16_round(scaled_levels(codes, cprime, levels)))
+
+
+# --------------------------------------------------------------------------
 # Whole encode, and storage arithmetic
 # --------------------------------------------------------------------------
 
@@ -321,6 +381,13 @@ class NF4Weight:
 
     def dequant(self) -> np.ndarray:
         return dequant(self.codes, self.cprime, self.levels)
+
+    def dequant_f16_bits(self) -> np.ndarray:
+        return dequant_f16_bits(self.codes, self.cprime, self.levels)
+
+    def dequant_f16(self) -> np.ndarray:
+        """fp64 values of the fp16 dequantized weight (reading R11)."""
+        return fp16_round(scaled_levels(self.codes, self.cprime, self.levels))
 
 
 def packed_bytes(n: int, k: int, double_quant: bool = True) -> int:

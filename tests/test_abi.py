@@ -14,6 +14,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 from oracle import nf4
 
@@ -261,3 +262,24 @@ def test_gemv_needs_its_workspace(q):
     assert lib.qlora_nf4_gemv_fwd(ctypes.byref(W), p, 4, p, p, 8, 1.0, p, None, 0, None) == -4
     assert lib.qlora_nf4_gemv_fwd(ctypes.byref(W), p, 4, p, p, 8, 1.0, p, p, need - 1, None) == -4
     assert lib.qlora_nf4_gemv_fwd(ctypes.byref(W), p, 17, p, p, 8, 1.0, p, p, need, None) == -2
+
+
+def test_f16_host_checks(q):
+    """The fp16 layer calls: their own workspace query, UNSUPPORTED for dX on an
+    n that is not a multiple of 8, WORKSPACE before any launch, and the
+    binding's dtype check."""
+    lib = q.raw()
+    W = _fake_weight(q, n=60)
+    p = ctypes.c_void_p(1 << 24)
+    big = 1 << 30
+    # M <= 16 forward: GEMV workspace; M > 16: expanded path (expanded weight in it)
+    assert q.linear_workspace_bytes(4, 60, 128, 8, False, torch.float16) >= q.nf4_gemv_workspace_bytes(128)
+    assert q.linear_workspace_bytes(64, 64, 128, 8, False, torch.float16) >= 64 * 128 * 2
+    assert q.linear_workspace_bytes(64, 60, 128, 8, True, torch.float16) > 0
+    assert lib.qlora_linear_bwd_f16(ctypes.byref(W), p, None, p, 64, p, p, 8, 1.0, p, p, p, 0, p, big, None) == -3
+    need = q.linear_workspace_bytes(64, 60, 128, 8, False, torch.float16)
+    assert lib.qlora_linear_fwd_f16(ctypes.byref(W), p, 64, p, p, 8, 1.0, p, None, p, need - 1, None) == -4
+    assert lib.qlora_linear_fwd_f16(ctypes.byref(W), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == 0
+    assert lib.qlora_dequant_f16(ctypes.byref(W), ctypes.c_void_p((1 << 24) + 8), None) == -1
+    with pytest.raises(ValueError):
+        q.linear_workspace_bytes(64, 64, 128, 8, False, torch.float32)

@@ -1,0 +1,121 @@
+"""GPU parity of the fp16 compute form (reading R11 of ``oracle/nf4.py``;
+"QLoRA vs LoRA ..." (instagit.com), "QLoRA Fine-Tuning with 4-Bit
+Quantization": a float16 compute dtype for the 4-bit base).
+
+The same encoded weight is expanded to IEEE binary16 instead of bf16 and the
+layer takes fp16 activations and adapters:
+* every dequantized fp16 weight equals the oracle's RN_fp16 of the fp32
+  product, bit for bit (NF4 with double quantization and the uniform grid
+  without it);
+* qlora_linear_fwd_f16 / _bwd_f16 on the GEMV (M <= 16) and expanded paths,
+  ragged shapes included, against the fp64 oracle over the fp16 weight: fp16
+  outputs within 1.25x the error of rounding the exact result once to fp16
+  (plus 1e-5), fp32 adapter gradients within 5e-4 relative Frobenius error;
+* the backward without dX on an n that is not a multiple of 8, and the
+  UNSUPPORTED error with dX there.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from bit_nf4_quantized_02_amd import synth
+from oracle import linear as olin
+from oracle import nf4 as onf4
+
+from gpu_util import bits16, f32, say
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 5e-4
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_nf4_quantized_02_amd import qlora
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return qlora
+
+
+def _check16(name, got, ref):
+    e = olin.relerr(got, ref)
+    fl = olin.fp16_floor(ref)
+    say(f"  {name}: relerr {e:.3e} (fp16 floor {fl:.3e})")
+    assert e <= 1.25 * fl + 1e-5, name
+
+
+def _check32(name, got, ref):
+    e = olin.relerr(got, ref)
+    say(f"  {name}: relerr {e:.3e}")
+    assert e <= GRAD_TOL, name
+
+
+def _encode(q, W, grid="nf4", dq=True):
+    cb = q.build_nf4_codebook() if grid == "nf4" else q.build_uniform4_codebook()
+    gw = q.quantize_nf4(W.cuda(), codebook=torch.tensor(cb, dtype=torch.float32, device="cuda"), double_quant=dq)
+    lv = onf4.nf4_levels() if grid == "nf4" else onf4.uniform4_levels()
+    return gw, onf4.NF4Weight(W.float().numpy(), lv, double_quant=dq)
+
+
+@pytest.mark.parametrize("grid,dq", [("nf4", True), ("uniform", False)])
+@pytest.mark.parametrize("n,k", [(37, 192), (300, 4096)])
+def test_dequant_f16_bitwise(q, grid, dq, n, k):
+    say(f"case: dequant fp16 {grid} double_quant={dq} n={n} k={k}")
+    W = synth.weight_bf16(n, k, 0.02, 91, n, k).float()
+    W[n // 2, 64:128] = 0.0
+    W[1, :64] *= 2000.0                      # products near the top of the fp16 range
+    gw, ow = _encode(q, W.to(torch.bfloat16), grid, dq)
+    wd = q.dequant(gw, dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(wd), ow.dequant_f16_bits()), "dequantized fp16 differs"
+
+
+def _inputs(seed, m, n, k, r, s):
+    li = synth.linear_inputs(seed, m, 0, n, k, m, r, s, sigma=0.02)
+    h = [t.to(torch.float16) for t in (li.X, li.A, li.B, li.dY)]   # the operands the GPU gets
+    return li.W, h
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 520, 640), (4, 517, 640), (16, 1030, 512), (17, 520, 640),
+                                   (128, 520, 640), (300, 517, 1088), (512, 1024, 640)])
+def test_layer_f16(q, m, n, k):
+    r, s = 16, 2.0
+    bwd = n % 8 == 0
+    say(f"case: fp16 layer M={m} N={n} K={k} r={r} backward={bwd}")
+    W, (X, A, B, dY) = _inputs(92, m, n, k, r, s)
+    gw, ow = _encode(q, W)
+    Xc, Ac, Bc, dYc = X.cuda(), A.cuda(), B.cuda(), dY.cuda()
+    Y, T = q.linear_fwd(gw, Xc, Ac, Bc, s, dtype=torch.float16)
+    if bwd:
+        dX, dA, dB = q.linear_bwd(gw, Xc, T, dYc, Ac, Bc, s, dtype=torch.float16)
+    else:
+        dX, dA, dB = q.linear_bwd(gw, Xc, T, dYc, Ac, Bc, s, need_dX=False, dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert Y.dtype == torch.float16
+    Wd = ow.dequant_f16()
+    Xo, Ao, Bo, dYo = (t.double().numpy() for t in (X, A, B, dY))
+    Yr, Tr = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
+    dXr, dAr, dBr, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
+    _check16("Y", f32(Y), Yr)
+    _check32("T", f32(T), Tr)
+    if bwd:
+        _check16("dX", f32(dX), dXr)
+    else:
+        assert dX is None
+    _check32("dA", f32(dA), dAr)
+    _check32("dB", f32(dB), dBr)
+
+
+def test_layer_f16_without_adapter_and_errors(q):
+    m, n, k = 200, 516, 320
+    say(f"case: fp16 layer r=0 M={m} N={n} K={k}; dX on n % 8 != 0")
+    W, (X, A, B, dY) = _inputs(93, m, n, k, 4, 1.0)
+    gw, ow = _encode(q, W)
+    Y, _ = q.linear_fwd(gw, X.cuda(), None, None, 1.0, dtype=torch.float16)
+    torch.cuda.synchronize()
+    Yr, _ = olin.linear_fwd(X.double().numpy(), ow.dequant_f16(), np.zeros((0, k)), np.zeros((n, 0)), 1.0)
+    _check16("Y r=0", f32(Y), Yr)
+    with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+        q.linear_bwd(gw, X.cuda(), None, dY.cuda(), A.cuda(), B.cuda(), 1.0, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        q.linear_fwd(gw, X.cuda(), A.cuda(), B.cuda(), 1.0)          # fp16 tensors to the bf16 call
