@@ -138,8 +138,12 @@ __device__ __forceinline__ void issue_step(const Rsrc& rs, const CopyPlan& p, in
 
 // One step: MFMAs on (Ac, Bc) while the copies of step + 1 fill (An, Bn).
 // Restrict pointers tell the compiler the copies cannot alias the fragment
-// reads, so it does not wait for them before reading.
-template <bool kF16>
+// reads, so it does not wait for them before reading. kPrio raises the
+// wave's issue priority over its MFMA stream. Measured on the plain bf16
+// GEMM: 4-6% faster where the operands (360 MB of expanded weight and more)
+// exceed the 256 MB last-level cache and stream from HBM, 3-10% slower where
+// they fit in it; the launch picks it by operand size.
+template <bool kF16, bool kPrio>
 __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int step, int nk, int nk_main, int wave,
                                           const char* __restrict__ Ac, const char* __restrict__ Bc,
                                           char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN]) {
@@ -160,6 +164,10 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
   __builtin_amdgcn_sched_barrier(0);
   issue_step(rs, p, s1, nk_main, wave, An, Bn);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kPrio) {
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int kk = 0; kk < kBK / 16; ++kk) {
     const int cb = kk & 1;
@@ -181,6 +189,11 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
     }
   __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+  if constexpr (kPrio) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   step_barrier<0>();
 }
 
@@ -249,7 +262,7 @@ __device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char
 // the tile's mask bytes land in buffers 1, masks and scales the accumulators
 // from there, then runs its main steps as usual.
 // kF16: fp16 operands and output (the compute-type ablation), else bf16.
-template <bool kMask, bool kF16>
+template <bool kMask, bool kF16, bool kPrio = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
   // direct copies from the one being read
@@ -316,8 +329,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
     issue_step(rs, plan, sbeg, nk_main, wave, As0, Bs0);
     step_barrier<0>();
     for (int step = sbeg; step < nk_end; step += 2) {
-      bf16_step<kF16>(rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc);
-      if (step + 1 < nk_end) bf16_step<kF16>(rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc);
+      bf16_step<kF16, kPrio>(rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc);
+      if (step + 1 < nk_end)
+        bf16_step<kF16, kPrio>(rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc);
     }
   }
 
@@ -460,6 +474,10 @@ bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
   return M * kc * 2 < lim && M * (int64_t)kx * 2 < lim && nout * ldf * 2 < lim;
 }
 
+// operand bytes (activation + expanded weight) above which the plain bf16
+// GEMM raises its MFMA priority: the last-level cache (256 MB)
+constexpr int64_t kPrioOperandBytes = 256LL << 20;
+
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                             const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
                             const uint8_t* mask, float keep_scale, bool f16) {
@@ -483,6 +501,8 @@ hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const ui
   } else {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
+    else if ((M * kc + nout * a.ldf) * 2 > kPrioOperandBytes)
+      gemm_bf16_kernel<false, false, true><<<grid, kThreads, 0, stream>>>(a);
     else
       gemm_bf16_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
   }

@@ -119,3 +119,40 @@ def test_layer_f16_without_adapter_and_errors(q):
         q.linear_bwd(gw, X.cuda(), None, dY.cuda(), A.cuda(), B.cuda(), 1.0, dtype=torch.float16)
     with pytest.raises(ValueError):
         q.linear_fwd(gw, X.cuda(), A.cuda(), B.cuda(), 1.0)          # fp16 tensors to the bf16 call
+
+
+def test_f16_at_the_attention_projection_size(q):
+    """4096 x 4096, M = 4096, r = 16 (the default bench workload) in fp16: every output."""
+    m = n = k = 4096
+    r, s = 16, 2.0
+    say("case: fp16 layer 4096^3 r=16")
+    W, (X, A, B, dY) = _inputs(94, m, n, k, r, s)
+    gw, ow = _encode(q, W)
+    Xc, Ac, Bc, dYc = X.cuda(), A.cuda(), B.cuda(), dY.cuda()
+    Y, T = q.linear_fwd(gw, Xc, Ac, Bc, s, dtype=torch.float16)
+    dX, dA, dB = q.linear_bwd(gw, Xc, T, dYc, Ac, Bc, s, dtype=torch.float16)
+    torch.cuda.synchronize()
+    Wd = ow.dequant_f16()
+    Xo, Ao, Bo, dYo = (t.double().numpy() for t in (X, A, B, dY))
+    Yr, _ = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
+    dXr, dAr, dBr, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
+    _check16("Y", f32(Y), Yr)
+    _check16("dX", f32(dX), dXr)
+    _check32("dA", f32(dA), dAr)
+    _check32("dB", f32(dB), dBr)
+
+
+def test_f16_decode_gemv_at_full_size(q):
+    """The 70B-class down weight (8192 x 28672, 8 waves per workgroup) in fp16
+    at M = 16 (operand-order activations): every output."""
+    n, k, r, M = 8192, 28672, 16, 16
+    say(f"case: fp16 decode GEMV {n}x{k} M={M}")
+    W = synth.weight_bf16(n, k, 0.015, 95, 0, 0)
+    gw, ow = _encode(q, W)
+    li = synth.linear_inputs(95, 0, 1, 1, k, M, r, 1.0)
+    X, A = li.X.to(torch.float16), li.A.to(torch.float16)
+    B = synth.lora_B(n, r, 95, 0, synth.T_B).to(torch.float16)
+    Y, _ = q.linear_fwd(gw, X.cuda(), A.cuda(), B.cuda(), 1.0, dtype=torch.float16)
+    torch.cuda.synchronize()
+    Yr, _ = olin.linear_fwd(X.double().numpy(), ow.dequant_f16(), A.double().numpy(), B.double().numpy(), 1.0)
+    _check16("Y", f32(Y), Yr)
