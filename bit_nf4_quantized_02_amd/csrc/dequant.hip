@@ -16,6 +16,7 @@ namespace qlora {
 
 namespace {
 
+// kF16: each w' rounded to fp16 instead of bf16 (the compute-type ablation).
 template <bool kF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ code8,

@@ -34,6 +34,8 @@ namespace {
 // LoRA columns of their rows.
 constexpr int kRows = 8;
 
+// kF16 (both expansions): the operand written in fp16 instead of bf16, w'
+// and the low-rank columns alike (the compute-type ablation).
 template <bool kF16>
 __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ code8,
