@@ -143,6 +143,19 @@ size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& 
   return cv.used;
 }
 
+// Zeros for the adapter gradients of an empty batch (a kernel, not a memset,
+// so the call stays capturable in a graph).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+hipError_t zero_f32(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  zero_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -438,7 +451,15 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
   if (s != QLORA_OK) return s;
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
   if (accumulate != 0 && accumulate != 1) return QLORA_ERR_INVALID_ARG;
-  if (M == 0) return QLORA_OK;
+  if (M == 0) {
+    // an empty batch: dA and dB are empty sums (zeros), unless accumulating
+    if (accumulate || r == 0) return QLORA_OK;
+    if ((dA && !aligned16(dA)) || (dB && !aligned16(dB))) return QLORA_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = dA ? zero_f32(dA, (int64_t)r * w->k, st) : hipSuccess;
+    if (e == hipSuccess && dB) e = zero_f32(dB, w->n * (int64_t)r, st);
+    return hip_status(e);
+  }
   if (!dY || !aligned16(dY)) return QLORA_ERR_INVALID_ARG;
   if (dX && !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
   if (r == 0) { dA = nullptr; dB = nullptr; }

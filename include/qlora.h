@@ -42,8 +42,10 @@
  *     on any error nothing is launched and a negative qlora_status returns.
  *     A failed launch returns QLORA_ERR_HIP. No C++ exception crosses the
  *     ABI. qlora_status_string() names each status.
- *   - Sizes: M = 0 is a no-op that returns QLORA_OK. r = 0 means no LoRA
- *     branch (A, B, T, dA, dB may then be NULL).
+ *   - Sizes: M = 0 launches nothing and returns QLORA_OK, except that a
+ *     backward with accumulate = 0 writes zeros to dA and dB (the gradient
+ *     of an empty batch). r = 0 means no LoRA branch (A, B, T, dA, dB may
+ *     then be NULL).
  */
 #ifndef QLORA_H
 #define QLORA_H

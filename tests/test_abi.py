@@ -125,9 +125,13 @@ def test_error_paths_return_before_any_launch(q):
     assert lib.qlora_linear_fwd(ctypes.byref(W), p, -1, p, p, 8, 1.0, p, none, p, 1 << 30, none) == -2
     assert lib.qlora_linear_bwd(ctypes.byref(W), p, none, p, 16, p, p, 8, 1.0, p, p, p, 2, p, 1 << 30, none) == -1
     assert lib.qlora_linear_fwd(ctypes.byref(W), p, 16, none, p, 8, 1.0, p, none, p, 1 << 30, none) == -1
-    # M = 0 is a no-op that succeeds
+    # M = 0 launches nothing and succeeds, except that a backward with
+    # accumulate = 0 zeroes dA and dB (checked, then launched: GPU tests)
     assert lib.qlora_linear_fwd(ctypes.byref(W), p, 0, p, p, 8, 1.0, p, none, none, 0, none) == 0
-    assert lib.qlora_linear_bwd(ctypes.byref(W), p, none, p, 0, p, p, 8, 1.0, p, p, p, 0, none, 0, none) == 0
+    assert lib.qlora_linear_bwd(ctypes.byref(W), p, none, p, 0, p, p, 8, 1.0, p, p, p, 1, none, 0, none) == 0
+    assert lib.qlora_linear_bwd(ctypes.byref(W), p, none, p, 0, p, p, 0, 1.0, p, p, p, 0, none, 0, none) == 0
+    assert lib.qlora_linear_bwd(ctypes.byref(W), p, none, p, 0, p, p, 8, 1.0, p, ctypes.c_void_p((1 << 24) + 4),
+                                p, 0, none, 0, none) == -1
     assert lib.qlora_silu_mul_fwd(p, p, p, 0, none) == 0
     assert lib.qlora_silu_mul_fwd(None, p, p, 8, none) == -1
     assert lib.qlora_silu_mul_bwd(p, p, p, p, p, -1, none) == -2

@@ -162,3 +162,34 @@ def test_fused_kernels_direct(q, m, n, k, r):
     dXr, _, _, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
     assert report("Y", f32(Y), Yr) <= TOL
     assert report("dX", f32(dX), dXr) <= TOL
+
+
+@pytest.mark.parametrize("form", ["bf16", "fp16", "dropout"])
+def test_empty_batch(q, form):
+    """M = 0: the forward writes nothing; the backward's dA and dB are the
+    gradient of an empty batch, zeros, or left as they are when accumulating."""
+    n, k, r, s = 200, 320, 8, 2.0
+    say(f"case: empty batch, {form}")
+    li = synth.linear_inputs(96, 0, 0, n, k, 1, r, s)
+    gw = q.quantize_nf4(li.W.cuda())
+    dt = torch.float16 if form == "fp16" else torch.bfloat16
+    X = torch.empty((0, k), dtype=dt, device="cuda")
+    dY = torch.empty((0, n), dtype=dt, device="cuda")
+    A, B = li.A.to(dt).cuda(), li.B.to(dt).cuda()
+    kw = {"dtype": dt}
+    if form == "dropout":
+        mask = torch.empty((0, k), dtype=torch.uint8, device="cuda")
+        Y, T = q.linear_fwd_dropout(gw, X, A, B, s, mask, 1.25)
+    else:
+        Y, T = q.linear_fwd(gw, X, A, B, s, **kw)
+    assert tuple(Y.shape) == (0, n)
+    for accumulate in (False, True):
+        dA = torch.full((r, k), 7.0, device="cuda")
+        dB = torch.full((n, r), 7.0, device="cuda")
+        if form == "dropout":
+            q.linear_bwd_dropout(gw, X, T, dY, A, B, s, mask, 1.25, dA=dA, dB=dB, accumulate=accumulate)
+        else:
+            q.linear_bwd(gw, X, T, dY, A, B, s, dA=dA, dB=dB, accumulate=accumulate, **kw)
+        torch.cuda.synchronize()
+        want = 7.0 if accumulate else 0.0
+        assert bool((dA == want).all()) and bool((dB == want).all())
