@@ -156,3 +156,25 @@ def test_f16_decode_gemv_at_full_size(q):
     torch.cuda.synchronize()
     Yr, _ = olin.linear_fwd(X.double().numpy(), ow.dequant_f16(), A.double().numpy(), B.double().numpy(), 1.0)
     _check16("Y", f32(Y), Yr)
+
+
+@pytest.mark.parametrize("m", [4, 300])
+def test_f16_layer_uniform_grid_without_double_quant(q, m):
+    """The fp16 layer over the uniform INT4 grid without double quantization
+    (GEMV and expanded paths): the same kernels take the other codebook and
+    scale form."""
+    n, k, r, s = 517, 640, 16, 2.0
+    say(f"case: fp16 layer, uniform grid, no double quant, M={m}")
+    W, (X, A, B, dY) = _inputs(97, m, n, k, r, s)
+    gw, ow = _encode(q, W, "uniform", False)
+    Xc, Ac, Bc, dYc = X.cuda(), A.cuda(), B.cuda(), dY.cuda()
+    Y, T = q.linear_fwd(gw, Xc, Ac, Bc, s, dtype=torch.float16)
+    _, dA, dB = q.linear_bwd(gw, Xc, T, dYc, Ac, Bc, s, need_dX=False, dtype=torch.float16)
+    torch.cuda.synchronize()
+    Wd = ow.dequant_f16()
+    Xo, Ao, Bo, dYo = (t.double().numpy() for t in (X, A, B, dY))
+    Yr, _ = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
+    _, dAr, dBr, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
+    _check16("Y", f32(Y), Yr)
+    _check32("dA", f32(dA), dAr)
+    _check32("dB", f32(dB), dBr)
