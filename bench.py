@@ -794,8 +794,8 @@ def cpu_baseline(wl: Workload, target_s: float):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the path shards by data parallelism "
-                                   "(see DESIGN.md); --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "the benchmark runs on one GPU only (the layer shards by data "
+                                   "parallelism, one replica per GPU); --gpus must be 1"}), flush=True)
         sys.exit(2)
     torch.cuda.set_device(0)
     if args.copy_calibration_mib > 0:

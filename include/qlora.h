@@ -65,7 +65,7 @@ typedef enum {
   QLORA_OK = 0,
   QLORA_ERR_INVALID_ARG = -1, /* NULL where a buffer is needed, bad enum, misaligned */
   QLORA_ERR_SHAPE = -2,       /* K % 64 != 0, negative sizes, rank out of range */
-  QLORA_ERR_UNSUPPORTED = -3, /* valid request this build does not implement */
+  QLORA_ERR_UNSUPPORTED = -3, /* valid request the library does not implement */
   QLORA_ERR_WORKSPACE = -4,   /* workspace smaller than the matching *_workspace_bytes() */
   QLORA_ERR_HIP = -5          /* a HIP launch or runtime call failed */
 } qlora_status;

@@ -11,8 +11,8 @@ Sources (cited by page title and section):
 * "QLoRA: Quantized Low-Rank Adaptation" (completesystemdesign.dev), paged
   optimizers: AdamW states in pinned CPU RAM; piece 3: only the adapter learns.
 
-The pages name the optimizer but give no update formula. Reading (listed in
-the design doc): AdamW with decoupled weight decay and bias correction, states m, v
+The pages name the optimizer but give no update formula. Reading: AdamW
+with decoupled weight decay and bias correction, states m, v
 in fp32 ("32-bit"), step t >= 1:
     m <- b1 m + (1 - b1) g
     v <- b2 v + (1 - b2) g^2

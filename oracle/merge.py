@@ -15,7 +15,7 @@ Sources (cited by page title and section):
   a higher precision (fp16 or fp32).
 * "QLoRA Explained ..." (gamut.so), "Step 5: Save and Merge Adapters".
 
-What is computed (readings, listed in DESIGN.md):
+What is computed (readings of the pages):
 * merged[i, c] = round(W'[i, c] + s * sum_j B[i, j] A[j, c]) with W' the
   dequantized base (``oracle.nf4.dequant``) and s = alpha / r, the LoRA
   scale of the forward pass, so that X merged^T reproduces the trained

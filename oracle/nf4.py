@@ -23,7 +23,7 @@ What the pages fix, in my words:
     blocks ("double quantization"), which saves about 0.37 bit per weight;
   - right before a multiply, the 64-block is expanded back to bf16.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   R1 levels: 7 negative quantiles, an exact zero and 8 positive quantiles of
      N(0,1), taken at evenly spaced probabilities between 1/2 and delta on
      each side, delta = ((1-1/30) + (1-1/32))/2, divided by Phi^-1(delta),
