@@ -15,14 +15,18 @@ Modules
                    INT4 grid and the encoding without double quantization
                    (ablations).
 ``oracle.linear``  fp64 forward and backward of the frozen-base linear with the
-                   LoRA branch, plain and with dropout on the branch's input.
+                   LoRA branch, plain and with dropout on the branch's input,
+                   and the element-wise error bound of an fp32-accumulated
+                   16-bit result.
 ``oracle.merge``   the adapter folded into a dequantized copy of the base (and
                    taken out again), exact in fp64, rounded once.
 ``oracle.adamw``   the AdamW step on the adapter and its learning-rate schedule.
+``oracle.mlp``     the gated-MLP join silu(G) * U and its gradients, which chains
+                   the MLP linears of the 7B block and the 65B-class stack.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against facts that do
 not come from this code (values the pages print, closed forms, brute force,
 library routines for special cases). No function here is "parity unpinned".
 """
 
-from . import nf4, linear, merge, adamw  # noqa: F401
+from . import nf4, linear, merge, adamw, mlp  # noqa: F401

@@ -138,3 +138,80 @@ def linear_bwd_dropout(X, Wd, A, B, s, dY, mask, keep_scale):
     dA = s * (U.T @ Xd)
     dB = s * (dY.T @ (Xd @ A.T))
     return dX, dA, dB, U
+
+
+# --------------------------------------------------------------------------- element-wise error bounds
+#
+# What a bf16 (or fp16) output of an fp32-accumulated product of 16-bit
+# operands may differ from the exact value, element by element. The products
+# of two 16-bit numbers are exact in fp32; a sum of n of them, in any order
+# and any grouping, carries at most gamma_n * sum |terms| of error with
+# gamma_n = n u / (1 - n u), u = 2^-24 (the standard forward bound of
+# floating-point summation; u is taken as 2^-23 below). The low-rank term enters as the hi/lo bf16 pair
+# of s T (T itself an fp32 sum over the contraction): the pair misses s T by
+# at most 2^-18 |s T| (hi is s T to half a bf16 step, 2^-9 relative; lo is the
+# remainder to half a bf16 step of itself), and s T is one fp32 product.
+# The output is the fp32 sum rounded once: at most half a step of the output
+# type more, 2^-8 relative for bf16 (8 significant bits), 2^-11 for fp16
+# (11 bits, plus 2^-25 absolute in its subnormal range). So, with S the sum
+# of absolute terms,
+#
+#     |z - z_exact| <= E + u_out (|z_exact| + E) + a_out,
+#     E = gamma_(n + slack) S + (2^-17 + 2^-23) |s| (|X| |A|^T) |B|^T.
+#
+# `slack` covers the few extra fp32 additions a kernel may make (split
+# contraction partials added in order, the low-rank columns padded to 64).
+# The bound is loose on purpose against the typical error but it holds
+# element by element, so a single wrong output (a misplaced tile, a wrong
+# code, a dropped low-rank term on a row) fails it where a global Frobenius
+# norm would not notice.
+
+# (2^-23, not 2^-24: also holds for an accumulator that truncates instead of
+# rounding to nearest)
+_U32 = 2.0 ** -23
+_OUT = {"bf16": (2.0 ** -8, 0.0), "fp16": (2.0 ** -11, 2.0 ** -25)}
+
+
+def _gamma(n: int) -> float:
+    nu = n * _U32
+    return nu / (1.0 - nu)
+
+
+def _bound(Zref, S_main, S_lora, s, n, out, slack):
+    u_out, a_out = _OUT[out]
+    E = _gamma(n + slack) * (S_main + abs(s) * S_lora) + (2.0 ** -17 + 2.0 ** -23) * abs(s) * S_lora
+    return E + u_out * (np.abs(_f64(Zref)) + E) + a_out
+
+
+def fwd_error_bound(X, Wd, A, B, s, Yref, out: str = "bf16", mask=None, keep_scale: float = 1.0,
+                    slack: int = 256):
+    """Largest |Y - Yref| an fp32-accumulated forward may show, element by
+    element ([M, N]); `mask` / `keep_scale` as in ``linear_fwd_dropout``."""
+    aX, aW = np.abs(_f64(X)), np.abs(_f64(Wd))
+    S_main = aX @ aW.T
+    S_lora = 0.0
+    if A is not None and np.size(A):
+        aXl = aX if mask is None else aX * (_f64(mask) * abs(float(keep_scale)))
+        S_lora = (aXl @ np.abs(_f64(A)).T) @ np.abs(_f64(B)).T
+    return _bound(Yref, S_main, S_lora, float(s), aX.shape[1], out, slack)
+
+
+def dx_error_bound(dY, Wd, A, B, s, dXref, out: str = "bf16", mask=None, keep_scale: float = 1.0,
+                   slack: int = 256):
+    """Largest |dX - dXref| an fp32-accumulated dX may show, element by
+    element ([M, K]); with dropout the low-rank term is multiplied by
+    mask * keep_scale elementwise, as in ``linear_bwd_dropout``."""
+    adY, aW = np.abs(_f64(dY)), np.abs(_f64(Wd))
+    S_main = adY @ aW
+    S_lora = 0.0
+    if A is not None and np.size(A):
+        S_lora = (adY @ np.abs(_f64(B))) @ np.abs(_f64(A))
+        if mask is not None:
+            S_lora = S_lora * (_f64(mask) * abs(float(keep_scale)))
+    return _bound(dXref, S_main, S_lora, float(s), adY.shape[1], out, slack)
+
+
+def outside_bound(Z, Zref, bound) -> int:
+    """How many elements of Z lie outside Zref +- bound (NaN counts)."""
+    d = np.abs(_f64(Z) - _f64(Zref))
+    return int(np.count_nonzero(~(d <= bound)))

@@ -51,6 +51,15 @@ the block constants in full precision):
       magnitude and is never chosen (the symmetric absmax INT4 grid).
   R10 no double quantization: c' = c_b, the fp32 block absmax, stored as is
       (one fp32 per block instead of one byte plus shares of s2 and mean).
+  R12 no double quantization with a bf16 block scale (QQ's worked block and
+      its 65B arithmetic store "one BF16 scalar per 64-weight block"):
+      c_b = RN_bf16(block absmax), stored as its bf16 bit pattern (16 bits per
+      block: 4.25 bit per weight); the codes are the nearest levels to
+      w / c_b for that stored c_b (the scale the dequant will use), so a
+      weight above c_b in magnitude takes an end level; c' = c_b. A block
+      whose c_b is zero stores code 7 (R6). For bf16 weights the absmax is
+      already a bf16 number: c_b equals the fp32 form's scale and the codes
+      are the same, at 0.25 bit per weight less storage.
   R11 fp16 compute (the other 16-bit compute type the pages use: "QLoRA vs
       LoRA ..." (instagit.com), "QLoRA Fine-Tuning with 4-Bit Quantization",
       a float16 compute dtype): w' = RN_fp16(RN32(L[code] * c')), IEEE
@@ -132,22 +141,29 @@ def block_absmax(W: np.ndarray) -> np.ndarray:
     return np.abs(W.reshape(-1, BLOCK)).max(axis=1)
 
 
-def nf4_codes(W: np.ndarray, levels: np.ndarray, rows_per_chunk: int = 256) -> np.ndarray:
+def nf4_codes(W: np.ndarray, levels: np.ndarray, rows_per_chunk: int = 256, scales=None) -> np.ndarray:
     """Unpacked 4-bit codes [N, K] (uint8), nearest level to w / c_b.
 
     Nearest with ties to the lower index (R5) is evaluated without dividing:
     code = #{ j in 0..14 : w > mu_j * c_b }, mu_j the midpoint of levels j and
     j+1. mu_j and mu_j * c_b are exact in fp64 (fp32 inputs), so every
-    comparison is exact. An all-zero block gets code 7 (R6).
+    comparison is exact. A block with c_b = 0 (all-zero) gets code 7 (R6).
+    c_b is the block absmax unless ``scales`` (one fp32 per block, R12)
+    gives the scale the codes are taken against.
     """
     W = np.asarray(W, dtype=np.float32)
     N, K = W.shape
     lv = levels.astype(np.float64)
     mids = (lv[:-1] + lv[1:]) / 2.0                      # 15 midpoints
     codes = np.empty((N, K), dtype=np.uint8)
+    bpr = K // BLOCK
     for r0 in range(0, N, rows_per_chunk):
         blk = W[r0:r0 + rows_per_chunk].astype(np.float64).reshape(-1, BLOCK)
-        c = np.abs(blk).max(axis=1)
+        if scales is None:
+            c = np.abs(blk).max(axis=1)
+        else:
+            r1 = min(r0 + rows_per_chunk, N)
+            c = np.asarray(scales, dtype=np.float32)[r0 * bpr:r1 * bpr].astype(np.float64)
         thr = c[:, None] * mids[None, :]                 # [nb, 15]
         q = (blk[:, :, None] > thr[:, None, :]).sum(axis=2).astype(np.uint8)
         q[c == 0.0] = 7
@@ -358,23 +374,35 @@ def dequant_f16_bits(codes: np.ndarray, cprime: np.ndarray, levels: np.ndarray) 
 class NF4Weight:
     """Everything the encoder produces for one [N, K] weight. ``levels``
     selects the 16-level grid (NF4 by default, R9 for the uniform ablation);
-    ``double_quant=False`` keeps the fp32 block scales as they are (R10):
-    code8 and mean are then None and s2 holds one scale per block."""
+    ``double_quant=False`` keeps one scale per block instead (code8 and mean
+    are then None): the fp32 block absmax in s2 (R10), or with
+    ``scale_dtype="bf16"`` its bf16 rounding, s2 holding the uint16 bit
+    patterns (R12)."""
 
-    def __init__(self, W: np.ndarray, levels: np.ndarray | None = None, double_quant: bool = True):
+    def __init__(self, W: np.ndarray, levels: np.ndarray | None = None, double_quant: bool = True,
+                 scale_dtype: str = "fp32"):
         W = np.asarray(W, dtype=np.float32)
+        assert scale_dtype in ("fp32", "bf16") and (scale_dtype == "fp32" or not double_quant)
         self.shape = W.shape
+        self.scale_dtype = scale_dtype
         self.levels = nf4_levels() if levels is None else levels
         self.absmax = block_absmax(W)
-        self.codes = nf4_codes(W, self.levels)
+        if scale_dtype == "bf16":
+            self.s2 = bf16_bits(self.absmax)
+            self.cprime = bf16_bits_to_f32(self.s2)
+            self.codes = nf4_codes(W, self.levels, scales=self.cprime)
+        else:
+            self.codes = nf4_codes(W, self.levels)
         self.packed = pack_nibbles(self.codes)
         if double_quant:
             self.code8, self.s2, self.mean = double_quantize(self.absmax)
             self.cprime = decode_scales(self.code8, self.s2, self.mean)
-        else:
+        elif scale_dtype == "fp32":
             self.code8, self.mean = None, None
             self.s2 = self.absmax.astype(np.float32).copy()
             self.cprime = self.s2
+        else:
+            self.code8, self.mean = None, None
 
     def dequant_bits(self) -> np.ndarray:
         return dequant_bits(self.codes, self.cprime, self.levels)
@@ -390,12 +418,13 @@ class NF4Weight:
         return fp16_round(scaled_levels(self.codes, self.cprime, self.levels))
 
 
-def packed_bytes(n: int, k: int, double_quant: bool = True) -> int:
+def packed_bytes(n: int, k: int, double_quant: bool = True, scale_bits: int = 32) -> int:
     """Bytes of one encoded weight: codes + code8 + s2 + mean, or codes + one
-    fp32 scale per block without double quantization (codebook excluded)."""
+    fp32 (or bf16: scale_bits 16) scale per block without double
+    quantization (codebook excluded)."""
     nb = n * k // BLOCK
     if not double_quant:
-        return n * k // 2 + 4 * nb
+        return n * k // 2 + scale_bits // 8 * nb
     nc = -(-nb // DQ_BLOCK)
     return n * k // 2 + nb + 4 * nc + 4
 

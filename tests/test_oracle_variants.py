@@ -90,3 +90,94 @@ def test_storage_without_double_quant():
     assert bits_nodq == 4.5
     # the difference is the page's saving of about 0.37 bit per parameter
     assert abs((bits_nodq - bits_dq) - g["dq_saving_bits_per_param_about"]) < 0.01
+
+
+# --------------------------------------------------------------------------- bf16 block scale (no double quant)
+#
+# "QLoRA: Quantized Low-Rank Adaptation" (completesystemdesign.dev): the worked
+# 8-weight block stores its scale (the largest magnitude) in BF16, and the
+# 65B arithmetic after it counts one BF16 scalar per 64-weight block.
+
+from fractions import Fraction  # noqa: E402
+
+
+def _brute_codes_against(W, levels, scales):
+    """Exact rational nearest level to w / c for a given per-block c (ties to
+    the lower index; c = 0 -> code 7)."""
+    lv = [Fraction(float(v)) for v in levels]
+    out = np.zeros(W.shape, dtype=np.uint8)
+    flat = W.reshape(-1, 64)
+    for b, blk in enumerate(flat):
+        c = Fraction(float(scales[b]))
+        for i, w in enumerate(blk):
+            if c == 0:
+                code = 7
+            else:
+                x = Fraction(float(w)) / c
+                code = min(range(16), key=lambda j: (abs(x - lv[j]), j))
+            out.reshape(-1, 64)[b, i] = code
+    return out
+
+
+def _torch_bf16(x):
+    import torch
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def test_bf16_scale_storage_is_4_25_bits_and_the_pages_35_gb():
+    g = json.load(open(os.path.join(GOLDEN, "storage_closed_forms.json")))
+    n, k = 8192, 8192
+    assert nf4.packed_bytes(n, k, double_quant=False, scale_bits=16) == n * k // 2 + 2 * (n * k // 64)
+    assert 8.0 * nf4.packed_bytes(n, k, double_quant=False, scale_bits=16) / (n * k) == 4.25
+    assert nf4.bits_per_weight(double_quant=False, scale_bits=16) == 4.25
+    # 65B parameters at 4.25 bit: the page's "about 35 GB" (4.5 bit would be 36.6)
+    gb = g["params"] * 4.25 / 8 / 1e9
+    assert abs(gb - g["nf4_with_scales_GB_about"]) < 0.6
+    assert abs(g["params"] * 4.5 / 8 / 1e9 - g["nf4_with_scales_GB_about"]) > 1.5
+
+
+def test_bf16_scale_worked_block():
+    """The page's block: scale 1.00 in BF16 (bit pattern 0x3F80), every
+    weight snapped to its nearest level."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    W = np.zeros((1, 64), dtype=np.float32)
+    W[0, :8] = np.array(g["weights"], dtype=np.float32)
+    o = nf4.NF4Weight(W, double_quant=False, scale_dtype="bf16")
+    assert o.code8 is None and o.mean is None
+    assert o.s2.dtype == np.uint16 and int(o.s2[0]) == 0x3F80 and o.cprime[0] == np.float32(g["absmax"])
+    assert np.array_equal(o.codes, _brute_codes_against(W, nf4.nf4_levels(), [1.0]))
+
+
+def test_bf16_scale_codes_brute_force_with_fp32_weights():
+    """fp32 weights whose block absmax is not a bf16 number: the stored scale
+    is torch's bf16 rounding of it (above or below), and the codes are the
+    exact nearest levels against that stored scale, end levels included for
+    weights beyond it."""
+    rng = np.random.default_rng(21)
+    for L in (nf4.nf4_levels(), nf4.uniform4_levels()):
+        W = (rng.standard_normal((4, 192)) * 0.02).astype(np.float32)
+        W[0, 10] = np.float32(0.0501)           # absmax rounds down in bf16
+        W[1, 70] = np.float32(-0.0507)          # absmax rounds up in bf16
+        W[2, 128:192] = 0.0                     # an all-zero block
+        o = nf4.NF4Weight(W, L, double_quant=False, scale_dtype="bf16")
+        absmax = np.abs(W.reshape(-1, 64)).max(axis=1)
+        want_c = _torch_bf16(absmax)
+        assert np.array_equal(o.cprime.view(np.uint32), want_c.view(np.uint32))
+        assert np.array_equal(o.s2, (want_c.view(np.uint32) >> 16).astype(np.uint16))
+        assert np.any(want_c < absmax) and np.any(want_c > absmax)
+        assert np.array_equal(o.codes, _brute_codes_against(W, L, want_c))
+        # dequant = RN_bf16(L[code] * c') with c' the stored bf16 scale
+        prod = (L[o.codes].reshape(-1, 64) * want_c[:, None]).astype(np.float32).reshape(W.shape)
+        assert np.array_equal(o.dequant_bits(), nf4.bf16_bits(prod))
+
+
+def test_bf16_scale_is_lossless_for_bf16_weights():
+    """bf16 weights: the absmax is a bf16 number, so the 4.25-bit form has the
+    fp32 form's scales and codes exactly."""
+    rng = np.random.default_rng(22)
+    W = _torch_bf16(rng.standard_normal((16, 512)) * 0.02)
+    a = nf4.NF4Weight(W, double_quant=False, scale_dtype="bf16")
+    b = nf4.NF4Weight(W, double_quant=False)
+    assert np.array_equal(a.codes, b.codes)
+    assert np.array_equal(a.cprime.view(np.uint32), b.cprime.view(np.uint32))
+    assert np.array_equal(a.dequant_bits(), b.dequant_bits())
