@@ -31,11 +31,22 @@ double quantization) on the first weight: bits per weight, reconstruction
 error and the layer step with each, and the step with LoRA dropout (0.05)
 on every linear beside the plain step timed the same way.
 
-Default workload: the 7B-class attention projection, W 4096x4096, M = 4096
-tokens, LoRA r = 16, alpha = 32. --config selects the other workloads
-(1: 1024^2 at M = 16; 3: 7B MLP block chained through SiLU; 4: 70B-class
-decode GEMVs; 5: the 65B-class stack, 80 layers of seven linears, forward
-then backward through all of them). Prints one JSON line.
+Default workload: the 65B-class stack, 80 layers of seven linears (q, k, v,
+o 8192x8192; gate, up 8192->22016; down 22016->8192), M = 4096 tokens, LoRA
+r = 64, alpha = 16, forward then backward through all of them -- the largest
+workload that fits one GPU (33.4 GB packed). --config selects the others
+(1: 1024^2 at M = 16; 2: the 7B-class attention projection 4096^2 at
+M = 4096; 3: 7B MLP block chained through SiLU; 4: 70B-class decode GEMVs).
+
+The side measurements (evented breakdown, step distribution, bf16-base,
+dropout and fp16 regions) run at most as many steps as fit in about five
+seconds of GPU time, so a long workload stays within a few minutes; the
+step time and `value` always come from exactly --steps timed steps.
+
+Parity: the outputs of the first linear right after the timed steps are
+snapshotted and compared with the CPU oracle on the same inputs; the line
+carries `parity_ok`, and the process exits with status 3 when any relative
+error is above 2e-3. Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -66,7 +77,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 5 for config 5)")
     p.add_argument("--warmup", type=int, default=None, help="warm-up steps (default 10; 1 for config 5)")
-    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                   help="workload (default 5: the 65B-class stack, the largest that fits one GPU)")
     p.add_argument("--path", choices=["auto", "fused", "expanded"], default="auto",
                    help="large-M kernels: the library's choice (auto) or one forced, for comparison")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -235,6 +247,16 @@ class LinearPlan:
     def packed_bytes(self):
         return self.W.nbytes()
 
+    def snapshot(self):
+        """Copies of this linear's outputs (Y, and dX, dA, dB with a backward)
+        as they stand: later regions that reuse the buffers cannot change
+        what the parity check sees."""
+        out = {"Y": self.Y.clone()}
+        if self.api_bwd is not None:
+            out.update(dX=self.dX.clone(), dA=self.dA.clone(), dB=self.dB.clone())
+        torch.cuda.synchronize()
+        return out
+
 
 # ----------------------------------------------------------------------------- workloads
 
@@ -372,6 +394,9 @@ class Workload:
         return [nme for nme, _, _ in self.pieces if "gemm" in nme or "gemv" in nme]
 
 
+AUX_REGION_MS = 5000.0  # GPU time allotted to each side region
+
+
 def time_steps(wl: Workload, steps: int, warmup: int):
     """Two timed regions over the same workload.
 
@@ -384,11 +409,12 @@ def time_steps(wl: Workload, steps: int, warmup: int):
       pieces of B sum to more than A's step; each piece's own duration is
       what the breakdown and the dominant-kernel roofline use.
     """
-    for _ in range(warmup):
+    for w_ in range(warmup):
         for cl in wl.api:
             cl()
-        for _, _, cl in wl.pieces:
-            cl()
+        if w_ == 0:
+            for _, _, cl in wl.pieces:
+                cl()
     torch.cuda.synchronize()
     # region A
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -402,6 +428,10 @@ def time_steps(wl: Workload, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     ev_step = e0.elapsed_time(e1) / steps
+    # the timed step's own outputs of the first linear, for the parity check
+    snap = wl.plans[0].snapshot()
+    aux = max(2, min(steps, int(AUX_REGION_MS / (wall * 1e3))))
+    steps = aux
     # region B
     calls = [cl for _, _, cl in wl.pieces]
     npc = len(calls)
@@ -420,7 +450,7 @@ def time_steps(wl: Workload, steps: int, warmup: int):
             per[i] += evs[s][i].elapsed_time(evs[s][i + 1])
     per_ms = per / steps
     pieces_step = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]))
-    return wall * 1e3, ev_step, per_ms, pieces_step
+    return wall * 1e3, ev_step, per_ms, pieces_step, snap, aux
 
 
 def region_ms(calls, steps: int) -> float:
@@ -549,15 +579,18 @@ def variant_rows(wl: Workload, q, reps: int = 10):
     each: bits per weight, the relative Frobenius error of its dequantized
     bf16 weight against the bf16 weight it encodes, and the layer calls of
     one step (forward, and backward where the workload has one) timed as a
-    region with that encoding, on the same activations and adapter."""
+    region with that encoding, on the same activations and adapter. The
+    ablation calls write outputs of their own (Y, T, dX, dA, dB), so the
+    linear's buffers keep the plain step's results."""
     p = wl.plans[0]
     if p.li.W is None:
         return {}
     W = p.li.W.to("cuda")
     Wf = W.double()
-    lib = q.raw()
     st = q._stream()
     P = q._ptr
+    Y, T, dX = torch.empty_like(p.Y), torch.empty_like(p.T), torch.empty_like(p.dX)
+    dA, dB = torch.empty_like(p.dA), torch.empty_like(p.dB)
     out = {}
     for grid in ("nf4", "uniform"):
         cb = torch.tensor(q.build_nf4_codebook() if grid == "nf4" else q.build_uniform4_codebook(),
@@ -568,11 +601,11 @@ def variant_rows(wl: Workload, q, reps: int = 10):
             wst = w.struct()
             wref = q.ctypes.byref(wst)
             lw, lwn = P(p.lws), p.lws.numel()
-            calls = [q.Call("qlora_linear_fwd", wref, P(p.X), p.m, P(p.A), P(p.B), p.r, p.s, P(p.Y), P(p.T), lw,
+            calls = [q.Call("qlora_linear_fwd", wref, P(p.X), p.m, P(p.A), P(p.B), p.r, p.s, P(Y), P(T), lw,
                             lwn, st, keep=(wst,))]
             if p.api_bwd is not None:
-                calls.append(q.Call("qlora_linear_bwd", wref, P(p.X), P(p.T), P(p.dY), p.m, P(p.A), P(p.B), p.r,
-                                    p.s, P(p.dX), P(p.dA), P(p.dB), 0, lw, lwn, st, keep=(wst,)))
+                calls.append(q.Call("qlora_linear_bwd", wref, P(p.X), P(T), P(p.dY), p.m, P(p.A), P(p.B), p.r,
+                                    p.s, P(dX), P(dA), P(dB), 0, lw, lwn, st, keep=(wst,)))
             us = _region_us(lambda: [cl() for cl in calls], reps)
             out[f"{grid}_{'dq' if dq else 'no_dq'}"] = dict(
                 bits_per_weight=round(8.0 * w.nbytes() / (w.n * w.k), 4), weight_relerr=round(err, 5),
@@ -711,29 +744,37 @@ def attainable(q):
     return out
 
 
-def gemm_traffic(kernel_name: str):
-    """Measured HBM bytes per launch from the committed counter summary, used
-    only while the kernel's source file still matches the one the counters
-    came from (sha256 recorded beside each entry)."""
+def gemm_traffic(tag: str, launches):
+    """Measured HBM bytes per launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled), averaged over the named launches of
+    the workload; used only while every entry exists and its kernel's source
+    file still matches the one the counters came from (sha256 recorded
+    beside each entry)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         data = json.load(open(path))
-        ent = data["kernels"].get(kernel_name)
-        if ent is None:
-            return None
-        src = os.path.join(ROOT, "bit_nf4_quantized_02_amd", "csrc", ent["source"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != ent["source_sha256"]:
-            return None
-        return float(ent["bytes_per_launch"])
+        vals = []
+        for nme in launches:
+            ent = data["kernels"].get(f"{tag}.{nme}")
+            if ent is None:
+                return None
+            src = os.path.join(ROOT, "bit_nf4_quantized_02_amd", "csrc", ent["source"])
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != ent["source_sha256"]:
+                return None
+            vals.append(float(ent["bytes_per_launch"]))
+        return round(sum(vals) / len(vals), 0)
     except Exception:
         return None
 
 
 # ----------------------------------------------------------------------------- CPU oracle leg
 
-def cpu_baseline(wl: Workload, target_s: float):
+PARITY_TOL = 2e-3  # relative Frobenius error against the fp64 oracle (Y, dX, dA, dB)
+
+
+def cpu_baseline(wl: Workload, target_s: float, snap: dict):
     """The oracle as it stands, timed on this host's cores on a bounded sample
     of the same workload: whole steps of the first linear (all M tokens),
     repeated until about target_s seconds; the weight's oracle encoding is
@@ -777,14 +818,15 @@ def cpu_baseline(wl: Workload, target_s: float):
         parts += (t1 - t0, t2 - t1, t3 - t2)
         spent += t3 - t0
         n += 1
-    # parity of the timed GPU outputs against this sample
-    got = [p.Y] + ([p.dX, p.dA, p.dB] if backward else [])
-    errs = {nme: olin.relerr(g.float().cpu().numpy(), o) for nme, g, o in zip(["Y", "dX", "dA", "dB"], got, out)}
+    # parity of the timed step's GPU outputs (snapshotted right after it)
+    # against this sample
+    errs = {nme: olin.relerr(snap[nme].float().cpu().numpy(), o) for nme, o in zip(["Y", "dX", "dA", "dB"], out)}
     return dict(value=flops * n / spent / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 sample=f"{n} whole fwd{'+bwd' if backward else ''} step(s) of linear '{wl.c.linears[0].name}' "
                        f"(M={p.m}, N={p.n}, K={p.k}, r={p.r}): numpy fp64 products, bf16 expansion of the "
                        f"encoded weight each step; {spent:.1f} s total",
-                seconds=spent, parity_relerr=errs,
+                seconds=spent, parity_relerr=errs, parity_tol=PARITY_TOL,
+                parity_ok=bool(all(e <= PARITY_TOL for e in errs.values())),
                 parts_s={"encode_once": round(t_encode, 3), "dequant": round(float(parts[0]) / n, 4),
                          "fwd": round(float(parts[1]) / n, 4), "bwd": round(float(parts[2]) / n, 4)})
 
@@ -810,16 +852,17 @@ def main():
                                 | {f"bwd:{names_of[p.path_bwd]}" for p in wl.plans if p.bwd})
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
-    ms_wall, ms_ev, per_ms, ms_pieces = time_steps(wl, args.steps, args.warmup)
-    p10, p50, p90, fwd_us, bwd_us = step_distribution(wl, args.steps)
+    ms_wall, ms_ev, per_ms, ms_pieces, snap, aux = time_steps(wl, args.steps, args.warmup)
+    log(f"bench: side regions with {aux} steps each")
+    p10, p50, p90, fwd_us, bwd_us = step_distribution(wl, aux)
     att = attainable(q)
     merges = merge_rows(wl, q) if args.config in (1, 2, 3, 5) else {}
-    lora_ms = lora_bf16_base(wl, q, args.steps)
+    lora_ms = lora_bf16_base(wl, q, aux)
     adamw = adamw_rows(wl, q)
     encode = encode_rows(wl, q)
     variants = variant_rows(wl, q)
-    drop = dropout_step(wl, q, args.steps)
-    f16 = f16_step(wl, q, args.steps)
+    drop = dropout_step(wl, q, aux)
+    f16 = f16_step(wl, q, aux)
     for row in merges.values():
         row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
         row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
@@ -837,26 +880,45 @@ def main():
     avg_ms = {nme: a[0] / a[1] for nme, a in agg.items()}
     breakdown = {nme: round(t * 1e3, 2) for nme, t in avg_ms.items()}
 
-    # dominant kernel: the slowest fused NF4 kernel
-    dom = max(wl.dominant_kernels(), key=lambda nme: avg_ms[nme])
+    # dominant kernel: the matrix kernel (GEMM or GEMV) with the largest
+    # time per step, taken together with every launch of the same kernel at
+    # the same algorithmic size (within 1%: the 65B stack's six 22016-wide
+    # GEMMs per layer are one such group, 480 launches), so the average
+    # launch duration is the one a kernel trace reports for it
+    tot = {}
+    for nme, f, t in zip(names, flops, per_ms):
+        if "gemm" in nme or "gemv" in nme:
+            tot[nme] = tot.get(nme, 0.0) + t
+    dom = max(tot, key=tot.get)
     i = names.index(dom)
-    dom_ms = avg_ms[dom]
-    gemv = "gemv" in dom
-    base = dom.split(".")[-1]
-    if gemv:
-        pl = [p for p in wl.plans if any(c is wl.pieces[i][2] for _, _, c in p.fwd)][0]
-        achieved = pl.packed_bytes / (dom_ms * 1e-3) / 1e9
+    dom_base = dom.split(".")[-1]
+    kind = "gemv" if "gemv" in dom_base else "gemm"
+    group = [j for j, nme in enumerate(names)
+             if kind in nme.split(".")[-1] and abs(flops[j] - flops[i]) <= 0.01 * flops[i]]
+    grp_ms = float(sum(per_ms[j] for j in group))
+    dom_ms = grp_ms / len(group)
+    plan_of = {}
+    for pl in wl.plans:
+        for _, _, c in pl.fwd + pl.bwd:
+            plan_of[id(c)] = pl
+    pl = plan_of[id(wl.pieces[i][2])]
+    if pl.m <= 16:
+        # few tokens: the packed weight streamed from HBM bounds the kernel
+        nbytes = sum(plan_of[id(wl.pieces[j][2])].packed_bytes for j in group)
+        achieved = nbytes / (grp_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4), attainable=att["hbm_read_gbps"],
                     frac_of_attainable=round(achieved / att["hbm_read_gbps"], 4))
     else:
-        achieved = flops[i] / (dom_ms * 1e-3) / 1e12
+        achieved = sum(flops[j] for j in group) / (grp_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4), attainable=att["mfma_bf16_tflops"],
                     frac_of_attainable=round(achieved / att["mfma_bf16_tflops"], 4))
-    roof["kernel"] = dom
+    roof["kernel"] = dom_base
+    roof["launches"] = sorted({names[j] for j in group})
+    roof["launches_per_step"] = len(group)
     roof["avg_launch_us"] = round(dom_ms * 1e3, 2)
-    roof["traffic"] = gemm_traffic(f"{wl.tag}.{base}")
+    roof["traffic"] = gemm_traffic(wl.tag, roof["launches"])
 
     res = {
         "metric": METRIC,
@@ -900,12 +962,16 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, snap)
+        res["parity_ok"] = res["cpu_baseline"]["parity_ok"]
     line = json.dumps(res)
     print(line, flush=True)
     if args.json:
         with open(args.json, "w") as f:
             f.write(line + "\n")
+    if res.get("parity_ok") is False:
+        log(f"bench: PARITY FAILED (relative error above {PARITY_TOL}): {res['cpu_baseline']['parity_relerr']}")
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -38,7 +38,10 @@ _f = ctypes.c_float
 
 class _Weight(ctypes.Structure):
     _fields_ = [("n", _i64), ("k", _i64), ("codes", _vp), ("code8", _vp), ("s2", _vp), ("mean", _vp),
-                ("codebook", _vp)]
+                ("codebook", _vp), ("scale_bf16", ctypes.c_int32)]
+
+
+SCALE_FP32, SCALE_DQ, SCALE_BF16 = 0, 1, 2
 
 
 _W = ctypes.POINTER(_Weight)
@@ -142,8 +145,11 @@ def build_uniform4_codebook() -> list[float]:
     return [buf[i] for i in range(16)]
 
 
-def nf4_packed_bytes(n: int, k: int, double_quant: bool = True) -> int:
-    return int(_lib.qlora_nf4_storage_bytes(n, k, int(bool(double_quant))))
+def nf4_packed_bytes(n: int, k: int, double_quant: bool = True, scale_dtype=torch.float32) -> int:
+    """Bytes of an encoded weight; without double quantization the block
+    scales are fp32, or bf16 with scale_dtype=torch.bfloat16."""
+    form = SCALE_DQ if double_quant else (SCALE_BF16 if scale_dtype == torch.bfloat16 else SCALE_FP32)
+    return int(_lib.qlora_nf4_storage_bytes(n, k, form))
 
 
 def quantize_workspace_bytes(n: int, k: int) -> int:
@@ -171,23 +177,28 @@ class NF4Weight:
     k: int
     codes: torch.Tensor      # uint8 [n, k/2]
     code8: torch.Tensor | None   # uint8 [n*k/64] (None: no double quantization)
-    s2: torch.Tensor             # fp32  [ceil(nb/256)], or [nb] block scales without it
+    s2: torch.Tensor             # fp32  [ceil(nb/256)], or [nb] fp32 / bf16 block scales without it
     mean: torch.Tensor | None    # fp32  [1]
     codebook: torch.Tensor   # fp32  [16]
 
     @staticmethod
     def empty(n: int, k: int, device="cuda", codebook: torch.Tensor | None = None,
-              double_quant: bool = True) -> "NF4Weight":
+              double_quant: bool = True, scale_dtype=torch.float32) -> "NF4Weight":
         """Buffers for one encoded weight; without double quantization code8
-        and mean are None and s2 holds one fp32 scale per block."""
+        and mean are None and s2 holds one scale per block, fp32 or (with
+        scale_dtype=torch.bfloat16) bf16."""
         nb = n * k // BLOCK
         nc = -(-nb // DQ_BLOCK)
         if codebook is None:
             codebook = torch.tensor(build_nf4_codebook(), dtype=torch.float32, device=device)
         codes = torch.empty((n, k // 2), dtype=torch.uint8, device=device)
         if not double_quant:
-            return NF4Weight(n, k, codes, None, torch.empty((nb,), dtype=torch.float32, device=device), None,
+            if scale_dtype not in (torch.float32, torch.bfloat16):
+                raise ValueError("block scales are fp32 or bf16")
+            return NF4Weight(n, k, codes, None, torch.empty((nb,), dtype=scale_dtype, device=device), None,
                              codebook)
+        if scale_dtype != torch.float32:
+            raise ValueError("a bf16 block scale is a form without double quantization")
         return NF4Weight(n, k, codes,
                          torch.empty((nb,), dtype=torch.uint8, device=device),
                          torch.empty((nc,), dtype=torch.float32, device=device),
@@ -198,20 +209,27 @@ class NF4Weight:
     def double_quant(self) -> bool:
         return self.code8 is not None
 
+    @property
+    def scale_bf16(self) -> bool:
+        return self.code8 is None and self.s2.dtype == torch.bfloat16
+
     def struct(self) -> _Weight:
         p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
         return _Weight(self.n, self.k, self.codes.data_ptr(), p(self.code8), self.s2.data_ptr(),
-                       p(self.mean), self.codebook.data_ptr())
+                       p(self.mean), self.codebook.data_ptr(), int(self.scale_bf16))
 
     def nbytes(self) -> int:
-        return nf4_packed_bytes(self.n, self.k, self.double_quant)
+        return nf4_packed_bytes(self.n, self.k, self.double_quant,
+                                torch.bfloat16 if self.scale_bf16 else torch.float32)
 
 
 def quantize_nf4(W: torch.Tensor, out: NF4Weight | None = None, ws: torch.Tensor | None = None,
-                 stream=None, codebook: torch.Tensor | None = None, double_quant: bool = True) -> NF4Weight:
+                 stream=None, codebook: torch.Tensor | None = None, double_quant: bool = True,
+                 scale_dtype=torch.float32) -> NF4Weight:
     """Encode W ([n, k] bf16 or fp32, on the GPU) as 4-bit codes + block
-    scales, double-quantized unless double_quant is False; the levels are
-    NF4 unless another 16-level device codebook is given (or out's)."""
+    scales, double-quantized unless double_quant is False (then one fp32, or
+    with scale_dtype=torch.bfloat16 one bf16, scale per block); the levels
+    are NF4 unless another 16-level device codebook is given (or out's)."""
     if W.dim() != 2:
         raise ValueError("W must be [n, k]")
     n, k = W.shape
@@ -220,7 +238,8 @@ def quantize_nf4(W: torch.Tensor, out: NF4Weight | None = None, ws: torch.Tensor
         raise ValueError("W must be bf16 or fp32")
     _need(W, W.dtype, (n, k), "W")
     if out is None:
-        out = NF4Weight.empty(n, k, device=W.device, codebook=codebook, double_quant=double_quant)
+        out = NF4Weight.empty(n, k, device=W.device, codebook=codebook, double_quant=double_quant,
+                              scale_dtype=scale_dtype)
     need = quantize_workspace_bytes(n, k)
     if ws is None:
         ws = _bytes(need, W.device)
@@ -272,6 +291,8 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
     M = X.shape[0]
     r = 0 if A is None else A.shape[0]
     f16 = _is_f16(dtype)
+    if f16 and _dropout is not None:
+        raise ValueError("LoRA dropout runs in bf16 only")
     _need(X, dtype, (M, w.k), "X")
     if r:
         _need(A, dtype, (r, w.k), "A")
@@ -293,8 +314,6 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
                                              0 if ws is None else ws.numel(), _stream(stream)),
                "qlora_linear_fwd_dropout")
         return Y, T
-    if f16 and _dropout is not None:
-        raise ValueError("LoRA dropout runs in bf16 only")
     if ws is None:
         ws = _bytes(linear_workspace_bytes(M, w.n, w.k, r, False, dtype), X.device)
     name = "qlora_linear_fwd_f16" if f16 else "qlora_linear_fwd"

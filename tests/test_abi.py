@@ -75,7 +75,17 @@ def test_weight_without_double_quant_needs_no_code8_or_mean(q):
     assert lib.qlora_linear_fwd(ctypes.byref(half), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == -1
     nos2 = q._Weight(64, 128, base, None, None, None, base + 16384)
     assert lib.qlora_linear_fwd(ctypes.byref(nos2), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == -1
-    assert lib.qlora_nf4_storage_bytes(64, 128, 2) == 0
+    assert lib.qlora_nf4_storage_bytes(64, 128, 3) == 0
+    assert lib.qlora_nf4_storage_bytes(64, 128, q.SCALE_BF16) == 64 * 128 // 2 + 2 * 128
+    assert q.nf4_packed_bytes(64, 128, double_quant=False, scale_dtype=torch.bfloat16) == \
+        nf4.packed_bytes(64, 128, double_quant=False, scale_bits=16)
+    # bf16 block scales: only without double quantization, flag 0 or 1
+    bfs = q._Weight(64, 128, base, None, base + 8192, None, base + 16384, 1)
+    assert lib.qlora_linear_fwd(ctypes.byref(bfs), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == 0
+    both = q._Weight(64, 128, base, base + 4096, base + 8192, base + 12288, base + 16384, 1)
+    assert lib.qlora_linear_fwd(ctypes.byref(both), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == -1
+    bad = q._Weight(64, 128, base, None, base + 8192, None, base + 16384, 2)
+    assert lib.qlora_linear_fwd(ctypes.byref(bad), p, 0, p, p, 8, 1.0, p, None, None, 0, None) == -1
 
 
 def test_size_queries_reject_bad_shapes(q):
@@ -287,3 +297,18 @@ def test_f16_host_checks(q):
     assert lib.qlora_dequant_f16(ctypes.byref(W), ctypes.c_void_p((1 << 24) + 8), None) == -1
     with pytest.raises(ValueError):
         q.linear_workspace_bytes(64, 64, 128, 8, False, torch.float32)
+
+
+def test_dropout_in_fp16_is_rejected_before_any_call(q):
+    """LoRA dropout exists in bf16 only: asking for it with the fp16 compute
+    type raises on the host, in the forward as in the backward, before any
+    tensor is checked or any library call is made."""
+    cpu = torch.empty(0)
+    w = q.NF4Weight(64, 128, cpu, cpu, cpu, cpu, cpu)
+    X = torch.zeros((4, 128), dtype=torch.float16)
+    mask = torch.ones((4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="bf16 only"):
+        q.linear_fwd_dropout(w, X, None, None, 1.0, mask, 1.0, dtype=torch.float16)
+    dY = torch.zeros((4, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="bf16 only"):
+        q.linear_bwd_dropout(w, X, None, dY, None, None, 1.0, mask, 1.0, dtype=torch.float16)

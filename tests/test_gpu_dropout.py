@@ -6,7 +6,9 @@ expanded paths, with ragged shapes and a dX whose last-wave tiles are split
 along the contraction; the saved T against (X . mask) A^T; and the special
 masks (keep everything: the forward equals the plain layer bit for bit; drop
 everything: the adapter gradients are exactly zero and dX is the base term).
-Bar: relative Frobenius error <= 2e-3 (T: 1e-5).
+Bars: relative Frobenius error <= 2e-3 for Y and dX with every element of
+them inside the oracle's element-wise bound (low-rank term through the mask);
+1e-5 for the fp32 T, dA and dB.
 """
 
 import numpy as np
@@ -16,7 +18,7 @@ import torch
 from bit_nf4_quantized_02_amd import synth
 from oracle import linear as olin
 
-from gpu_util import TOL, f32, oracle_encode, report, say
+from gpu_util import TOL, assert_dx, assert_fwd, assert_grad, f32, oracle_encode, report, say
 
 pytestmark = pytest.mark.gpu
 
@@ -64,11 +66,11 @@ def test_dropout_layer_against_oracle(q, m, n, k, r):
     mo = mask.numpy()
     Yr, Tdr = olin.linear_fwd_dropout(Xo, Wd, Ao, Bo, s, mo, KEEP)
     dXr, dAr, dBr, _ = olin.linear_bwd_dropout(Xo, Wd, Ao, Bo, s, dYo, mo, KEEP)
-    assert report("Y", f32(Y), Yr) <= TOL
-    assert report("T (X . mask) A^T", f32(T), Tdr / KEEP, floor=False) <= 1e-5
-    assert report("dX", f32(dX), dXr) <= TOL
-    assert report("dA", f32(dA), dAr, floor=False) <= TOL
-    assert report("dB", f32(dB), dBr, floor=False) <= TOL
+    assert_fwd("Y", Y, Xo, Wd, Ao, Bo, s, Yr, mask=mo, keep_scale=KEEP)
+    assert_grad("T (X . mask) A^T", T, Tdr / KEEP)
+    assert_dx("dX", dX, dYo, Wd, Ao, Bo, s, dXr, mask=mo, keep_scale=KEEP)
+    assert_grad("dA", dA, dAr)
+    assert_grad("dB", dB, dBr)
 
 
 def test_keep_everything_matches_the_plain_forward(q):
@@ -114,7 +116,7 @@ def test_dropout_at_the_attention_projection_size(q):
     mo = mask.numpy()
     Yr, _ = olin.linear_fwd_dropout(Xo, Wd, Ao, Bo, s, mo, KEEP)
     dXr, dAr, dBr, _ = olin.linear_bwd_dropout(Xo, Wd, Ao, Bo, s, dYo, mo, KEEP)
-    assert report("Y", f32(Y), Yr) <= TOL
-    assert report("dX", f32(dX), dXr) <= TOL
-    assert report("dA", f32(dA), dAr, floor=False) <= TOL
-    assert report("dB", f32(dB), dBr, floor=False) <= TOL
+    assert_fwd("Y", Y, Xo, Wd, Ao, Bo, s, Yr, mask=mo, keep_scale=KEEP)
+    assert_dx("dX", dX, dYo, Wd, Ao, Bo, s, dXr, mask=mo, keep_scale=KEEP)
+    assert_grad("dA", dA, dAr)
+    assert_grad("dB", dB, dBr)

@@ -2,8 +2,10 @@
 
 For each case the oracle encodes W itself, expands it to W', and evaluates
 Y, T, dX, dA, dB in fp64 from the same bf16 inputs the GPU consumed. Bars:
-relative Frobenius error <= 2e-3 for Y, dX, dA, dB (the north-star bound);
-<= 1e-5 for the fp32 T (bf16 products, fp32 sums).
+relative Frobenius error <= 2e-3 for Y and dX (the benchmark spec's bound) and every
+element of Y and dX inside the oracle's element-wise bound of an
+fp32-accumulated bf16 result; <= 1e-5 for the fp32 T, dA and dB (bf16
+products, fp32 sums, T and U entering the gradients as bf16 hi/lo pairs).
 Shapes cover several tiles plus ragged tails in every dimension, the GEMV
 path (M <= 16) and the GEMM path (M >= 17), r = 0, odd r and the largest r.
 """
@@ -15,7 +17,7 @@ import torch
 from bit_nf4_quantized_02_amd import synth
 from oracle import linear as olin
 
-from gpu_util import TOL, f32, oracle_encode, report, say
+from gpu_util import TOL, assert_dx, assert_fwd, assert_grad, f32, oracle_encode, report, say
 
 pytestmark = pytest.mark.gpu
 
@@ -50,15 +52,15 @@ def _run(q, li, need=("dX", "dA", "dB"), use_T=True, check=True):
     Xo, Ao, Bo, dYo = (t.float().numpy() for t in (li.X, li.A, li.B, li.dY))
     Yr, Tr = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
     dXr, dAr, dBr, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
-    assert report("Y", f32(Y), Yr) <= TOL
+    assert_fwd("Y", Y, Xo, Wd, Ao, Bo, s, Yr)
     if r:
-        assert report("T", f32(T), Tr, floor=False) <= 1e-5
+        assert_grad("T", T, Tr)
     if "dX" in need:
-        assert report("dX", f32(dX), dXr) <= TOL
+        assert_dx("dX", dX, dYo, Wd, Ao, Bo, s, dXr)
     if r and "dA" in need:
-        assert report("dA", f32(dA), dAr, floor=False) <= TOL
+        assert_grad("dA", dA, dAr)
     if r and "dB" in need:
-        assert report("dB", f32(dB), dBr, floor=False) <= TOL
+        assert_grad("dB", dB, dBr)
     return gw, Y, T, dX, dA, dB
 
 
@@ -160,8 +162,8 @@ def test_fused_kernels_direct(q, m, n, k, r):
     Xo, Ao, Bo, dYo = (t.float().numpy() for t in (li.X, li.A, li.B, li.dY))
     Yr, _ = olin.linear_fwd(Xo, Wd, Ao, Bo, s)
     dXr, _, _, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
-    assert report("Y", f32(Y), Yr) <= TOL
-    assert report("dX", f32(dX), dXr) <= TOL
+    assert_fwd("Y", Y, Xo, Wd, Ao, Bo, s, Yr)
+    assert_dx("dX", dX, dYo, Wd, Ao, Bo, s, dXr)
 
 
 @pytest.mark.parametrize("form", ["bf16", "fp16", "dropout"])
