@@ -575,7 +575,8 @@ def encode_rows(wl: Workload, q, reps: int = 10):
 
 def variant_rows(wl: Workload, q, reps: int = 10):
     """The ablations of the storage format on the workload's first weight:
-    NF4 or the uniform INT4 grid, with or without double quantization. For
+    NF4 or the uniform INT4 grid, with double quantization or without it
+    (one fp32 or one bf16 scale per block). For
     each: bits per weight, the relative Frobenius error of its dequantized
     bf16 weight against the bf16 weight it encodes, and the layer calls of
     one step (forward, and backward where the workload has one) timed as a
@@ -592,11 +593,12 @@ def variant_rows(wl: Workload, q, reps: int = 10):
     Y, T, dX = torch.empty_like(p.Y), torch.empty_like(p.T), torch.empty_like(p.dX)
     dA, dB = torch.empty_like(p.dA), torch.empty_like(p.dB)
     out = {}
+    forms = (("dq", True, torch.float32), ("no_dq", False, torch.float32), ("no_dq_bf16_scale", False, torch.bfloat16))
     for grid in ("nf4", "uniform"):
         cb = torch.tensor(q.build_nf4_codebook() if grid == "nf4" else q.build_uniform4_codebook(),
                           dtype=torch.float32, device="cuda")
-        for dq in (True, False):
-            w = q.quantize_nf4(W, codebook=cb, double_quant=dq)
+        for tag, dq, sd in forms:
+            w = q.quantize_nf4(W, codebook=cb, double_quant=dq, scale_dtype=sd)
             err = float(torch.linalg.norm(q.dequant(w).double() - Wf) / torch.linalg.norm(Wf))
             wst = w.struct()
             wref = q.ctypes.byref(wst)
@@ -607,7 +609,7 @@ def variant_rows(wl: Workload, q, reps: int = 10):
                 calls.append(q.Call("qlora_linear_bwd", wref, P(p.X), P(T), P(p.dY), p.m, P(p.A), P(p.B), p.r,
                                     p.s, P(dX), P(dA), P(dB), 0, lw, lwn, st, keep=(wst,)))
             us = _region_us(lambda: [cl() for cl in calls], reps)
-            out[f"{grid}_{'dq' if dq else 'no_dq'}"] = dict(
+            out[f"{grid}_{tag}"] = dict(
                 bits_per_weight=round(8.0 * w.nbytes() / (w.n * w.k), 4), weight_relerr=round(err, 5),
                 step_us=round(us, 2))
             del w

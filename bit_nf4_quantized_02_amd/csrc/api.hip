@@ -19,15 +19,16 @@ qlora_status check_weight(const qlora_nf4_weight* w) {
   if (w == nullptr) return QLORA_ERR_INVALID_ARG;
   if (w->n < 1 || w->k < 1 || (w->k % QLORA_BLOCK) != 0) return QLORA_ERR_SHAPE;
   // code8 NULL: no double quantization (s2 holds one fp32 scale per block,
-  // mean is not read)
+  // or one bf16 bit pattern per block with scale_bf16 = 1; mean is not read)
   if (!w->codes || !w->s2 || !w->codebook || (w->code8 && !w->mean)) return QLORA_ERR_INVALID_ARG;
+  if (w->scale_bf16 != 0 && (w->scale_bf16 != 1 || w->code8)) return QLORA_ERR_INVALID_ARG;
   if (!aligned16(w->codes) || !aligned16(w->s2) || !aligned16(w->codebook)) return QLORA_ERR_INVALID_ARG;
   if (w->code8 && (!aligned16(w->code8) || !aligned16(w->mean))) return QLORA_ERR_INVALID_ARG;
   return QLORA_OK;
 }
 
 Nf4View view_of(const qlora_nf4_weight* w) {
-  return Nf4View{w->n, w->k, w->codes, w->code8, w->s2, w->mean, w->codebook};
+  return Nf4View{w->n, w->k, w->codes, w->code8, w->s2, w->mean, w->codebook, w->scale_bf16 == 1};
 }
 
 // Bump allocator over the caller's workspace (256-byte aligned regions).
@@ -179,11 +180,12 @@ size_t qlora_nf4_packed_bytes(int64_t n, int64_t k) {
   return (size_t)(n * k / 2 + nb + 4 * nc + 4);
 }
 
-size_t qlora_nf4_storage_bytes(int64_t n, int64_t k, int double_quant) {
-  if (double_quant != 0 && double_quant != 1) return 0;
-  if (double_quant) return qlora_nf4_packed_bytes(n, k);
+size_t qlora_nf4_storage_bytes(int64_t n, int64_t k, int scale_form) {
+  if (scale_form < 0 || scale_form > 2) return 0;
+  if (scale_form == QLORA_SCALE_DQ) return qlora_nf4_packed_bytes(n, k);
   if (n < 1 || k < 1 || k % QLORA_BLOCK) return 0;
-  return (size_t)(n * k / 2 + 4 * (n * k / QLORA_BLOCK));
+  const int64_t per_block = scale_form == QLORA_SCALE_BF16 ? 2 : 4;
+  return (size_t)(n * k / 2 + per_block * (n * k / QLORA_BLOCK));
 }
 
 size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k) {
@@ -200,7 +202,8 @@ qlora_status qlora_quantize_nf4(const void* W, int w_dtype, const qlora_nf4_weig
   const size_t need = qlora_quantize_workspace_bytes(out->n, out->k);
   if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return QLORA_ERR_WORKSPACE;
   return hip_status(launch_quantize(W, w_dtype == QLORA_DT_BF16, out->n, out->k, out->codebook, out->codes,
-                                    out->code8, out->s2, out->mean, ws, static_cast<hipStream_t>(stream)));
+                                    out->code8, out->s2, out->mean, ws, static_cast<hipStream_t>(stream),
+                                    out->scale_bf16 == 1));
 }
 
 qlora_status qlora_dequant(const qlora_nf4_weight* w, void* out, void* stream) {

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
                                                       const uint8_t* __restrict__ code8,
                                                       const float* __restrict__ s2,
                                                       const float* __restrict__ mean_p,
-                                                      const float* __restrict__ codebook,
+                                                      const float* __restrict__ codebook, bool s2_bf16,
                                                       int64_t nwords, u32x4* __restrict__ out) {
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = codebook[threadIdx.x];
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) {
     const int64_t blk = i >> 3;  // 8 words per 64-weight block
-    const float cp = block_scale(code8, s2, mean, blk);
+    const float cp = block_scale(code8, s2, s2_bf16, mean, blk);
     out[i] = dequant8<kF16>(codes[i], lut, cp);
   }
 }
@@ -45,9 +45,11 @@ hipError_t launch_dequant(const Nf4View& w, uint16_t* out, hipStream_t stream, b
   auto* cw = reinterpret_cast<const uint32_t*>(w.codes);
   auto* o4 = reinterpret_cast<u32x4*>(out);
   if (f16)
-    dequant_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, nwords, o4);
+    dequant_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, w.s2_bf16,
+                                                               nwords, o4);
   else
-    dequant_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, nwords, o4);
+    dequant_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, w.s2_bf16,
+                                                                nwords, o4);
   return hipGetLastError();
 }
 

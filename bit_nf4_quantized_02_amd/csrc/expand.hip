@@ -41,9 +41,9 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
                                                           const uint8_t* __restrict__ code8,
                                                           const float* __restrict__ s2,
                                                           const float* __restrict__ mean_p,
-                                                          const float* __restrict__ codebook, int64_t n, int64_t k,
-                                                          const uint16_t* __restrict__ B, int r, int xc,
-                                                          u32x4* __restrict__ out) {
+                                                          const float* __restrict__ codebook, bool s2_bf16,
+                                                          int64_t n, int64_t k, const uint16_t* __restrict__ B, int r,
+                                                          int xc, u32x4* __restrict__ out) {
   const int t = threadIdx.x;
   const int64_t kw = k / 8;
   const int64_t ldc = (k + xc) / 8;  // output row pitch in chunks
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(const uint32_t* __rest
     const int64_t row = r0 + i < n ? r0 + i : n - 1;  // rows past n repeat the last one (not stored)
     const int64_t wi = row * kw + c;                  // code word index
     word[i] = codes[wi];
-    scale_fields(code8, s2, wi >> 3, c8[i], s2v[i]);
+    scale_fields(code8, s2, s2_bf16, wi >> 3, c8[i], s2v[i]);
   }
 #pragma unroll
   for (int i = 0; i < kRows; ++i)
@@ -118,8 +118,9 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
                                                           const uint8_t* __restrict__ code8,
                                                           const float* __restrict__ s2,
                                                           const float* __restrict__ mean_p,
-                                                          const float* __restrict__ codebook, int64_t n, int64_t k,
-                                                          int64_t np, const uint16_t* __restrict__ A, int r, int xc,
+                                                          const float* __restrict__ codebook, bool s2_bf16,
+                                                          int64_t n, int64_t k, int64_t np,
+                                                          const uint16_t* __restrict__ A, int r, int xc,
                                                           uint16_t* __restrict__ out) {
   __shared__ float lut[16];
   const int t = threadIdx.x;
@@ -149,11 +150,11 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
   const int64_t kblocks = k / kBlock;
   if (na < n) {
     qa = *reinterpret_cast<const u32x4*>(codes + na * (k / 2) + kb * 32 + half * 16);
-    ca = block_scale(code8, s2, mean, na * kblocks + kb);
+    ca = block_scale(code8, s2, s2_bf16, mean, na * kblocks + kb);
   }
   if (nb < n) {
     qb = *reinterpret_cast<const u32x4*>(codes + nb * (k / 2) + kb * 32 + half * 16);
-    cb = block_scale(code8, s2, mean, nb * kblocks + kb);
+    cb = block_scale(code8, s2, s2_bf16, mean, nb * kblocks + kb);
   }
   // rows past n decode code 7 (level 0) times scale 0: exact zeros
   uint32_t* dst = reinterpret_cast<uint32_t*>(out + (kb * kBlock + half * 32) * ldo + na);
@@ -187,22 +188,22 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
     auto* cw = reinterpret_cast<const uint32_t*>(w.codes);
     auto* o4 = reinterpret_cast<u32x4*>(out);
     if (f16)
-      expand_rows_kernel<true><<<grid, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, lr, r, xc,
-                                                         o4);
+      expand_rows_kernel<true><<<grid, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, w.s2_bf16, w.n, w.k,
+                                                         lr, r, xc, o4);
     else
-      expand_rows_kernel<false><<<grid, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, lr, r,
-                                                          xc, o4);
+      expand_rows_kernel<false><<<grid, 256, 0, stream>>>(cw, w.code8, w.s2, w.mean, w.codebook, w.s2_bf16, w.n, w.k,
+                                                          lr, r, xc, o4);
   } else {
     const int64_t np = expand_pad_rows(w.n);
     const int64_t ntiles = cdiv(np, (int64_t)kXT);
     const int64_t units = (ntiles + (xc > 0 ? 1 : 0)) * cdiv(w.k / kBlock, (int64_t)4);
     const dim3 grid((unsigned)(cdiv(units, (int64_t)8) * 8 * 4));
     if (f16)
-      expand_cols_kernel<true><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, np,
-                                                         lr, r, xc, out);
+      expand_cols_kernel<true><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.s2_bf16, w.n,
+                                                         w.k, np, lr, r, xc, out);
     else
-      expand_cols_kernel<false><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, np,
-                                                          lr, r, xc, out);
+      expand_cols_kernel<false><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.mean, w.codebook, w.s2_bf16, w.n,
+                                                          w.k, np, lr, r, xc, out);
   }
   return hipGetLastError();
 }

@@ -70,6 +70,7 @@ struct GemmArgs {
   const float* s2;
   const float* mean;
   const float* codebook;
+  bool s2_bf16;           // per-block bf16 scales (no double quantization)
   int64_t wn, wk;
   // low-rank second factor: B [wn, r] (forward) or A [r, wk] (dX)
   const uint16_t* lr;
@@ -187,7 +188,7 @@ __device__ __forceinline__ void load_w(const GemmArgs& a, int64_t n0, int step, 
   const int64_t kc = k < a.wk ? k : a.wk - 32;
   const u32x4 q = *reinterpret_cast<const u32x4*>(a.codes + nc * (a.wk / 2) + kc / 2);
   const int64_t blk = nc * kblocks + kc / kBlock;
-  scale_fields(a.code8, a.s2, blk, st.c8, st.s2v);
+  scale_fields(a.code8, a.s2, a.s2_bf16, blk, st.c8, st.s2v);
 #pragma unroll
   for (int j = 0; j < 4; ++j) st.q[j] = ok ? q[j] : 0x77777777u;
 }
@@ -485,6 +486,7 @@ hipError_t launch_gemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const
   a.act = X; a.lda = w.k; a.M = M; a.kc = w.k;
   a.act_x = TS; a.kx = lora_extra_cols(r);
   a.codes = w.codes; a.code8 = w.code8; a.s2 = w.s2; a.mean = w.mean; a.codebook = w.codebook;
+  a.s2_bf16 = w.s2_bf16;
   a.wn = w.n; a.wk = w.k;
   a.lr = B; a.r = r;
   a.out = Y; a.nout = w.n;
@@ -501,6 +503,7 @@ hipError_t launch_gemm_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const
   a.act = dY; a.lda = w.n; a.M = M; a.kc = w.n;
   a.act_x = US; a.kx = lora_extra_cols(r);
   a.codes = w.codes; a.code8 = w.code8; a.s2 = w.s2; a.mean = w.mean; a.codebook = w.codebook;
+  a.s2_bf16 = w.s2_bf16;
   a.wn = w.n; a.wk = w.k;
   a.lr = A; a.r = r;
   a.out = dX; a.nout = w.k;

@@ -59,8 +59,8 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
                                                        const uint8_t* __restrict__ code8,
                                                        const float* __restrict__ s2,
                                                        const float* __restrict__ mean_p,
-                                                       const float* __restrict__ codebook, int64_t N,
-                                                       int64_t K, const uint16_t* __restrict__ X,
+                                                       const float* __restrict__ codebook, bool s2_bf16,
+                                                       int64_t N, int64_t K, const uint16_t* __restrict__ X,
                                                        const u32x4* __restrict__ Xp, int64_t M,
                                                        const float* __restrict__ T,
                                                        const uint16_t* __restrict__ B, int r, float scale,
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
       st.cw[i][0] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2);
       st.cw[i][1] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2 + 16);
       const int64_t blk = bbase[i] + kc / kBlock;
-      scale_fields(code8, s2, blk, st.c8[i], st.s2v[i]);
+      scale_fields(code8, s2, s2_bf16, blk, st.c8[i], st.s2v[i]);
     }
   };
   auto compute = [&](const Stage& st) {
@@ -242,7 +242,7 @@ hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const flo
   const bool lora = r > 0;
 #define QLORA_GEMV3(NT, W, L, XP, H)                                                                           \
   gemv_nf4_kernel<NT, W, L, XP, H><<<dim3((unsigned)cdiv(w.n, NT)), 64 * W, 0, stream>>>(                      \
-      w.codes, w.code8, w.s2, w.mean, w.codebook, w.n, w.k, X, Xp, M, T, B, r, scale, Y)
+      w.codes, w.code8, w.s2, w.mean, w.codebook, w.s2_bf16, w.n, w.k, X, Xp, M, T, B, r, scale, Y)
 #define QLORA_GEMV2(NT, W, L, XP) \
   if (f16) QLORA_GEMV3(NT, W, L, XP, true); else QLORA_GEMV3(NT, W, L, XP, false);
 #define QLORA_GEMV(NT, W)                                                   \

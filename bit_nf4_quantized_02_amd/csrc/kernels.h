@@ -18,11 +18,15 @@ inline size_t quantize_ws_bytes(int64_t nb) {
   return quantize_ws_absmax_bytes(nb) + quantize_ws_runsum_bytes(nb) + align256((size_t)((nb + 255) / 256) * 4);
 }
 
+// code8 NULL: no double quantization, s2 receives one scale per block, fp32
+// or (s2_bf16) the bf16 rounding of the block absmax, which the codes are
+// then taken against.
 hipError_t launch_quantize(const void* W, bool w_bf16, int64_t n, int64_t k, const float* codebook,
                            uint8_t* codes, uint8_t* code8, float* s2, float* mean, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, bool s2_bf16 = false);
 
-// Encoded weight as the kernels see it.
+// Encoded weight as the kernels see it (s2_bf16: without double
+// quantization, s2 holds bf16 bit patterns, one per block).
 struct Nf4View {
   int64_t n, k;
   const uint8_t* codes;
@@ -30,6 +34,7 @@ struct Nf4View {
   const float* s2;
   const float* mean;
   const float* codebook;
+  bool s2_bf16 = false;
 };
 
 hipError_t launch_dequant(const Nf4View& w, uint16_t* out, hipStream_t stream, bool f16 = false);

@@ -56,8 +56,8 @@ struct TileSrc {
 
 template <bool kFromNf4>
 __device__ __forceinline__ void load_src(TileSrc<kFromNf4>& x, const uint8_t* __restrict__ codes,
-                                         const uint8_t* __restrict__ code8, const float* __restrict__ s2, float mean,
-                                         const uint16_t* __restrict__ Wm, int64_t n, int64_t k, int64_t i0, int64_t c0,
+                                         const uint8_t* __restrict__ code8, const float* __restrict__ s2, bool s2_bf16,
+                                         float mean, const uint16_t* __restrict__ Wm, int64_t n, int64_t k, int64_t i0, int64_t c0,
                                          int kcols, int t, const uint16_t* __restrict__ B, int r, int rp) {
   {
     // B rows i0 + 16 wave + lane % 16, ranks 32 ch + 8 (lane / 16) .. + 7
@@ -92,7 +92,7 @@ __device__ __forceinline__ void load_src(TileSrc<kFromNf4>& x, const uint8_t* __
       x.cp[i] = 0.0f;
       if (ok) {
         x.v[0][i] = *reinterpret_cast<const uint32_t*>(codes + gi * (k / 2) + c / 2);
-        x.cp[i] = block_scale(code8, s2, mean, (gi * k + c) / kBlock);
+        x.cp[i] = block_scale(code8, s2, s2_bf16, mean, (gi * k + c) / kBlock);
       }
     } else {
       x.v[i] = u32x4{0u, 0u, 0u, 0u};
@@ -104,7 +104,7 @@ __device__ __forceinline__ void load_src(TileSrc<kFromNf4>& x, const uint8_t* __
 template <bool kFromNf4, bool kOutF32, int kHold>
 __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ code8,
                                                     const float* __restrict__ s2, const float* __restrict__ mean_p,
-                                                    const float* __restrict__ codebook,
+                                                    const float* __restrict__ codebook, bool s2_bf16,
                                                     const uint16_t* __restrict__ Wm, int64_t n, int64_t k,
                                                     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                     int r, int rp, float scale, void* __restrict__ out) {
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ 
     *reinterpret_cast<u32x4*>(at + j * kAPitch + ch * 16) = v;
   }
   TileSrc<kFromNf4> cur;
-  load_src<kFromNf4>(cur, codes, code8, s2, mean, Wm, n, k, ibase, c0, kcols, t, B, r, rp);
+  load_src<kFromNf4>(cur, codes, code8, s2, s2_bf16, mean, Wm, n, k, ibase, c0, kcols, t, B, r, rp);
 
   __syncthreads();  // lut and the A strip are written
   // Each wave works on its own 16 rows of every tile and its own region of
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint8_t* __restrict__ 
     for (int i = 0; i < 4; ++i) wb[i] = kFromNf4 ? dequant8(cur.v[0][i], lut, cur.cp[i]) : cur.v[i];
     // the next tile's loads are in flight while this one is finished
     if (tile + 1 < kTiles && i0 + kGT < n)
-      load_src<kFromNf4>(cur, codes, code8, s2, mean, Wm, n, k, i0 + kGT, c0, kcols, t, B, r, rp);
+      load_src<kFromNf4>(cur, codes, code8, s2, s2_bf16, mean, Wm, n, k, i0 + kGT, c0, kcols, t, B, r, rp);
     asm volatile("" ::: "memory");
     // 3. add, round once, store: rows 16 wave + lane / 16 + 4 i, columns
     //    8 cc .. + 7; a store instruction covers whole 256-byte row segments
@@ -235,7 +235,7 @@ hipError_t launch_merge(const Nf4View* w, const uint16_t* Wm, int64_t n, int64_t
 #define QLORA_MERGE(NF4, F32, H)                                                                               \
   merge_kernel<NF4, F32, H><<<grid, 256, smem, stream>>>(                                                      \
       NF4 ? w->codes : nullptr, NF4 ? w->code8 : nullptr, NF4 ? w->s2 : nullptr, NF4 ? w->mean : nullptr,      \
-      NF4 ? w->codebook : nullptr, Wm, n, k, A, B, r, rp, NF4 ? scale : -scale, out)
+      NF4 ? w->codebook : nullptr, NF4 && w->s2_bf16, Wm, n, k, A, B, r, rp, NF4 ? scale : -scale, out)
 #define QLORA_MERGE_H(NF4, F32)          \
   if (rp == 32) QLORA_MERGE(NF4, F32, 1); \
   else if (rp == 64) QLORA_MERGE(NF4, F32, 2); \

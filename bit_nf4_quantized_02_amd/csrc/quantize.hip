@@ -138,7 +138,12 @@ __device__ __forceinline__ int absmax_exp(float m) {
 // block's absmax, and for each run the fp64 sum of its absmax values (in any
 // order: it is used only when every partial sum is exact, see
 // dq_mean_kernel) and the smallest exponent among them.
-template <bool kBf16>
+// kBf16Scale (no double quantization, bf16 block scales): each block's scale
+// is c = RN_bf16(absmax), the codes are taken against that c (the value the
+// dequant will multiply by), and absmax receives c's bf16 bit patterns
+// (uint16 per block) instead of fp32 values. A block whose c is zero stores
+// code 7 throughout.
+template <bool kBf16, bool kBf16Scale>
 __global__ __launch_bounds__(256, 4) void nf4_codes_kernel(const void* __restrict__ W, int64_t nb, int64_t nruns,
                                                         const float* __restrict__ codebook,
                                                         uint32_t* __restrict__ codes,
@@ -181,10 +186,12 @@ __global__ __launch_bounds__(256, 4) void nf4_codes_kernel(const void* __restric
         // max over the 8 lanes of this block (lanes 8-aligned inside the wavefront)
 #pragma unroll
         for (int off = 1; off < 8; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 8));
-        uint32_t word = 0x77777777u;  // all-zero block: every code is 7
-        if (m != 0.0f) {
-          const float rc = __builtin_amdgcn_rcpf(m);
-          const double cd = (double)m;
+        // the scale the codes are taken against
+        const float c = kBf16Scale ? bf16_bits_to_f32(to_bf16_bits(m)) : m;
+        uint32_t word = 0x77777777u;  // all-zero block (or zero scale): every code is 7
+        if (c != 0.0f) {
+          const float rc = __builtin_amdgcn_rcpf(c);
+          const double cd = (double)c;
           uint32_t bad;
           word = nf4_codes8(w[it], rc, cd, tb, &bad);
           if (bad) {
@@ -196,7 +203,10 @@ __global__ __launch_bounds__(256, 4) void nf4_codes_kernel(const void* __restric
         if (b < nb) {
           codes[b * 8 + part] = word;
           if (part == 0) {
-            absmax[b] = m;
+            if constexpr (kBf16Scale)
+              reinterpret_cast<uint16_t*>(absmax)[b] = to_bf16_bits(m);
+            else
+              absmax[b] = m;
             rs += (double)m;
             const int e = absmax_exp(m);
             re = re < e ? re : e;
@@ -326,7 +336,7 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
 
 hipError_t launch_quantize(const void* W, bool w_bf16, int64_t n, int64_t k, const float* codebook,
                            uint8_t* codes, uint8_t* code8, float* s2, float* mean, void* ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool s2_bf16) {
   const int64_t nb = n * k / kBlock;
   const int64_t nruns = cdiv(nb, kDqBlock);
   // without double quantization (code8 NULL) the block absmax values are the
@@ -337,12 +347,19 @@ hipError_t launch_quantize(const void* W, bool w_bf16, int64_t n, int64_t k, con
   int* runexp = reinterpret_cast<int*>(reinterpret_cast<char*>(runsum) + quantize_ws_runsum_bytes(nb));
   // 4 workgroups per CU of an MI355X, each looping over runs
   const dim3 grid((unsigned)(nruns < 1024 ? nruns : 1024));
-  if (w_bf16)
-    nf4_codes_kernel<true><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, reinterpret_cast<uint32_t*>(codes),
-                                                     absmax, runsum, runexp);
-  else
-    nf4_codes_kernel<false><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, reinterpret_cast<uint32_t*>(codes),
-                                                      absmax, runsum, runexp);
+  auto* cw = reinterpret_cast<uint32_t*>(codes);
+  const bool bs = !dq && s2_bf16;
+  if (w_bf16) {
+    if (bs)
+      nf4_codes_kernel<true, true><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, cw, absmax, runsum, runexp);
+    else
+      nf4_codes_kernel<true, false><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, cw, absmax, runsum, runexp);
+  } else {
+    if (bs)
+      nf4_codes_kernel<false, true><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, cw, absmax, runsum, runexp);
+    else
+      nf4_codes_kernel<false, false><<<grid, 256, 0, stream>>>(W, nb, nruns, codebook, cw, absmax, runsum, runexp);
+  }
   if (dq) {
     dq_mean_kernel<<<1, 1024, 0, stream>>>(runsum, runexp, nruns, absmax, nb, mean);
     dq_encode_kernel<<<(unsigned)nruns, 256, 0, stream>>>(absmax, nb, mean, s2, code8);

@@ -84,7 +84,13 @@ typedef enum { QLORA_DT_BF16 = 0, QLORA_DT_FP32 = 1 } qlora_dtype;
  *   mean     [1]      fp32 mean of all block absmax values.
  * Without double quantization (the ablation the pages weigh it against, QX
  * "Double Quantization"): code8 = NULL, s2 [n*k/64] holds every block's fp32
- * absmax and mean is not read (may be NULL); then c'_b = s2[b].
+ * absmax and mean is not read (may be NULL); then c'_b = s2[b]. With
+ * scale_bf16 = 1 as well (QQ's worked block and its 65B arithmetic: "one
+ * BF16 scalar per 64-weight block", 4.25 bit per weight), s2 points to
+ * n*k/64 uint16 bf16 bit patterns, c_b = RN_bf16(block absmax), the codes
+ * are the nearest levels to w / c_b for that stored c_b, and c'_b = c_b
+ * widened to fp32 (a block whose c_b is 0 stores code 7). scale_bf16 must be
+ * 0 when code8 is set.
  *   codebook [16]     fp32 NF4 levels, ascending (from
  *                     qlora_build_nf4_codebook, copied to the device).
  * Block b's scale is c'_b = RN32(RN32(fp8(code8[b]) * s2[b/256]) + mean[0])
@@ -99,7 +105,15 @@ typedef struct {
   float *s2;
   float *mean;
   const float *codebook;
+  int32_t scale_bf16; /* 0, or 1: per-block bf16 scales in s2 (code8 NULL only) */
 } qlora_nf4_weight;
+
+/* Storage forms of the block scales, for qlora_nf4_storage_bytes. */
+typedef enum {
+  QLORA_SCALE_FP32 = 0, /* one fp32 absmax per block (no double quantization) */
+  QLORA_SCALE_DQ = 1,   /* double-quantized: code8 + s2 + mean */
+  QLORA_SCALE_BF16 = 2  /* one bf16 absmax per block (no double quantization) */
+} qlora_scale_form;
 
 /* Name of a status code (static string, never NULL). */
 const char *qlora_status_string(int status);
@@ -121,9 +135,11 @@ qlora_status qlora_build_nf4_codebook(float *levels_out);
  * Returns 0 if k % 64 != 0 or a size is not positive. */
 size_t qlora_nf4_packed_bytes(int64_t n, int64_t k);
 
-/* The same with double_quant = 1; with double_quant = 0 the form without
- * double quantization (codes + one fp32 scale per block). 0 on bad arguments. */
-size_t qlora_nf4_storage_bytes(int64_t n, int64_t k, int double_quant);
+/* Bytes of an encoded weight in a qlora_scale_form: QLORA_SCALE_DQ as
+ * qlora_nf4_packed_bytes; QLORA_SCALE_FP32 codes + 4 bytes per block (4.5
+ * bit per weight); QLORA_SCALE_BF16 codes + 2 bytes per block (4.25 bit,
+ * QQ's "one BF16 scalar per 64-weight block"). 0 on bad arguments. */
+size_t qlora_nf4_storage_bytes(int64_t n, int64_t k, int scale_form);
 
 /*
  * The 16 levels of the uniform INT4 grid, the ablation the pages contrast
@@ -153,7 +169,9 @@ size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
  *   d_b   = RN32(c_b - mean); s2_j = RN32(max |d_b| over run j / 448);
  *   code8 = E4M3 pattern of the finite E4M3 value nearest to d_b / s2_j, ties
  *           to the lower value, -0 never produced; s2_j = 0 gives 0x00.
- * With out->code8 = NULL the second level is skipped: s2[b] = c_b.
+ * With out->code8 = NULL the second level is skipped: s2[b] = c_b; with
+ * out->scale_bf16 = 1 as well, s2 (as uint16) receives RN_bf16(c_b) and the
+ * codes are taken against that stored value.
  * ws (device) must hold qlora_quantize_workspace_bytes(n, k) bytes. The result
  * is deterministic and independent of the launch configuration.
  * Errors: INVALID_ARG (NULL/misaligned pointers, bad dtype), SHAPE (k % 64,
