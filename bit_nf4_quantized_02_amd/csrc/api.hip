@@ -169,6 +169,8 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_UNSUPPORTED: return "QLORA_ERR_UNSUPPORTED";
     case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace too small";
     case QLORA_ERR_HIP: return "QLORA_ERR_HIP: a HIP launch or runtime call failed";
+    case QLORA_ERR_SCRATCH:
+      return "QLORA_ERR_SCRATCH: the call needs more than the library's static scratch (QLORA_SCRATCH_BYTES)";
     default: return "QLORA_ERR_UNKNOWN";
   }
 }
@@ -261,6 +263,17 @@ static size_t linear_ws_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
   return linear_ws_bytes(M, n, k, r, is_bwd, false);
 }
+
+}  // extern "C"
+
+size_t qlora::linear_fwd_ws_bytes(int64_t M, int64_t n, int64_t k, int r, bool have_tsave) {
+  if (M < 1 || n < 1 || k < 1 || k % QLORA_BLOCK || r < 0 || r > QLORA_MAX_RANK) return 0;
+  Carver cv(nullptr);
+  FwdWs o;
+  return fwd_ws(M, n, k, r, have_tsave, cv, o, false);
+}
+
+extern "C" {
 
 size_t qlora_linear_f16_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
   return linear_ws_bytes(M, n, k, r, is_bwd, true);
@@ -395,11 +408,11 @@ qlora_status qlora_lowrank_grad(const void* P, int64_t M, int64_t C, const float
 // The layer calls with and without dropout on the adapter's input (mask NULL:
 // none). With dropout the branch's kernels read X through the mask (dropped
 // entries as zero) and keep_scale folds into the branch's scale: T_save
-// receives (X . mask) A^T.
-static qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A,
+// receives (X . mask) A^T. (Also the body of the forward that runs in the
+// library's static scratch, noalloc.hip.)
+qlora_status qlora::linear_fwd_impl(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A,
                                     const void* B, int r, float scale, const uint8_t* mask, float keep_scale,
-                                    void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream,
-                                    bool f16 = false) {
+                                    void* Y, float* T_save, void* ws, size_t ws_bytes, void* stream, bool f16) {
   qlora_status s = check_weight(w);
   if (s != QLORA_OK) return s;
   if (M < 0 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
@@ -585,3 +598,4 @@ qlora_status qlora_silu_mul_bwd(const void* G, const void* Up, const void* dH, v
 }
 
 }  // extern "C"
+

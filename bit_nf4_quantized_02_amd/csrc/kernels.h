@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "qlora.h"
+
 namespace qlora {
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -108,6 +110,14 @@ size_t gemv_ws_bytes(int64_t k);
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T,
                        const uint16_t* B, int r, float scale, uint16_t* Y, void* ws, hipStream_t stream,
                        bool f16 = false);
+
+// The layer forward behind qlora_linear_fwd and its dropout / fp16 forms
+// (api.hip), and the workspace it carves for a bf16 call with or without a
+// caller-provided T_save.
+qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, int64_t M, const void* A, const void* B,
+                             int r, float scale, const uint8_t* mask, float keep_scale, void* Y, float* T_save,
+                             void* ws, size_t ws_bytes, void* stream, bool f16 = false);
+size_t linear_fwd_ws_bytes(int64_t M, int64_t n, int64_t k, int r, bool have_tsave);
 
 hipError_t launch_silu_fwd(const uint16_t* G, const uint16_t* U, uint16_t* H, int64_t count,
                            hipStream_t stream);

@@ -27,6 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 BLOCK = 64
 DQ_BLOCK = 256
 MAX_RANK = 128
+SCRATCH_BYTES = 64 << 20   # QLORA_SCRATCH_BYTES: the library's own device scratch per device
 DT_BF16, DT_FP32 = 0, 1
 
 _vp = ctypes.c_void_p
@@ -58,6 +59,7 @@ _SIGS = {
     "qlora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
     "qlora_linear_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "qlora_linear_fwd_scratch": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp]),
     "qlora_dequant_f16": (_int, [_W, _vp, _vp]),
     "qlora_linear_f16_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
     "qlora_linear_fwd_f16": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -319,6 +321,32 @@ def linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.T
     name = "qlora_linear_fwd_f16" if f16 else "qlora_linear_fwd"
     _check(getattr(_lib, name)(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), _ptr(Y), _ptr(T),
                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), name)
+    return Y, T
+
+
+def linear_fwd_scratch(w: NF4Weight, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None,
+                       scale: float, Y: torch.Tensor | None = None, T: torch.Tensor | None = None,
+                       save_T: bool = True, stream=None):
+    """linear_fwd with no workspace (qlora_linear_fwd_scratch): the library's
+    own device scratch serves instead, so the call allocates nothing when Y
+    (and T, if saved) are given. Calls overlapping on one device race.
+    Returns (Y, T)."""
+    M = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(X, torch.bfloat16, (M, w.k), "X")
+    if r:
+        _need(A, torch.bfloat16, (r, w.k), "A")
+        _need(B, torch.bfloat16, (w.n, r), "B")
+    if Y is None:
+        Y = torch.empty((M, w.n), dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, (M, w.n), "Y")
+    if T is None and save_T and r:
+        T = torch.empty((M, r), dtype=torch.float32, device=X.device)
+    if T is not None:
+        _need(T, torch.float32, (M, r), "T")
+    st = w.struct()
+    _check(_lib.qlora_linear_fwd_scratch(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), _ptr(Y),
+                                         _ptr(T), _stream(stream)), "qlora_linear_fwd_scratch")
     return Y, T
 
 

@@ -67,7 +67,8 @@ typedef enum {
   QLORA_ERR_SHAPE = -2,       /* K % 64 != 0, negative sizes, rank out of range */
   QLORA_ERR_UNSUPPORTED = -3, /* valid request the library does not implement */
   QLORA_ERR_WORKSPACE = -4,   /* workspace smaller than the matching *_workspace_bytes() */
-  QLORA_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+  QLORA_ERR_HIP = -5,         /* a HIP launch or runtime call failed */
+  QLORA_ERR_SCRATCH = -6      /* the call needs more than QLORA_SCRATCH_BYTES of library scratch */
 } qlora_status;
 
 typedef enum { QLORA_DT_BF16 = 0, QLORA_DT_FP32 = 1 } qlora_dtype;
@@ -208,6 +209,27 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int 
 qlora_status qlora_linear_fwd(const qlora_nf4_weight *w, const void *X, int64_t M,
                               const void *A, const void *B, int r, float scale,
                               void *Y, float *T_save, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, kernels and results as qlora_linear_fwd;
+ * the regions qlora_linear_fwd carves from ws come from a device array the
+ * library owns instead: QLORA_SCRATCH_BYTES (64 MiB) per device, held from
+ * the first call on that device until the process ends (the only memory the
+ * library keeps; nothing is allocated or freed). The device is the one
+ * `stream` belongs to. Every call on a device shares that device's array and
+ * leaves its contents behind: calls that overlap on one device (two streams,
+ * two host threads) race and must be serialized by the caller.
+ * Errors: as qlora_linear_fwd; SCRATCH (before anything is enqueued) when
+ * qlora_linear_workspace_bytes(M, n, k, r, 0) would exceed QLORA_SCRATCH_BYTES
+ * (e.g. the expanded path of a large weight: use qlora_linear_fwd with a
+ * workspace there).
+ */
+#define QLORA_SCRATCH_BYTES (64 << 20)
+qlora_status qlora_linear_fwd_scratch(const qlora_nf4_weight *w, const void *X, int64_t M,
+                                      const void *A, const void *B, int r, float scale,
+                                      void *Y, float *T_save, void *stream);
 
 /*
  * Backward [WQ "Key Characteristics": backpropagation through quantized

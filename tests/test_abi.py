@@ -312,3 +312,18 @@ def test_dropout_in_fp16_is_rejected_before_any_call(q):
     dY = torch.zeros((4, 64), dtype=torch.float16)
     with pytest.raises(ValueError, match="bf16 only"):
         q.linear_bwd_dropout(w, X, None, dY, None, None, 1.0, mask, 1.0, dtype=torch.float16)
+
+
+def test_scratch_forward_refuses_oversize_before_any_call(q):
+    """qlora_linear_fwd_scratch checks its need against the fixed scratch on
+    the host and returns QLORA_ERR_SCRATCH before touching the device."""
+    lib = q.raw()
+    p = ctypes.c_void_p(1 << 24)
+    base = 1 << 20
+    w = q._Weight(8192, 8192, base, base + 4096, base + 8192, base + 12288, base + 16384, 0)
+    assert q.linear_workspace_bytes(4096, 8192, 8192, 64, False) > q.SCRATCH_BYTES
+    s = lib.qlora_linear_fwd_scratch(ctypes.byref(w), p, 4096, p, p, 64, 0.25, p, None, None)
+    assert s == -6 and q.status_string(s).startswith("QLORA_ERR_SCRATCH")
+    assert lib.qlora_linear_fwd_scratch(None, p, 4, p, p, 8, 1.0, p, None, None) == -1
+    assert lib.qlora_linear_fwd_scratch(ctypes.byref(w), p, 4, p, p, 200, 1.0, p, None, None) == -2
+
