@@ -21,8 +21,8 @@ backward passes each timed as a region of their own, and what this box
 sustains (a matrix-core loop without memory traffic, a 1 GiB streaming read)
 beside the published peaks, the adapter merge (round(W' + s B A) into a bf16
 copy) of each weight, timed alone against the HBM roofline, and the same step
-with a bf16 base (the step's calls minus the two weight expansions, over the
-operands they leave in place) with QLoRA's slowdown over it, and the AdamW
+over bf16 base weights (the bf16-base LoRA layer calls in place of the QLoRA
+ones) with QLoRA's slowdown over it, and the AdamW
 step over all adapter parameters with the moments in device memory and in
 pinned host memory ("paged"), and the offline encode (quantize + double
 quantization) and the bf16 dequant of each weight shape, each timed alone,
@@ -167,7 +167,8 @@ class LinearPlan:
         gw = max(lib.qlora_lowrank_grad_workspace_bytes(M, K, r), lib.qlora_lowrank_grad_workspace_bytes(M, N, r))
         bw = max(lib.qlora_bf16_gemm_workspace_bytes(M, K, r, N), lib.qlora_bf16_gemm_workspace_bytes(M, N, r, K))
         vw = lib.qlora_nf4_gemv_workspace_bytes(K)
-        self.ws = buf("ws", (max(pw, gw, bw, vw, 256),), torch.uint8)
+        dw = lib.qlora_nf4_gemv_dx_workspace_bytes(N, K)
+        self.ws = buf("ws", (max(pw, gw, bw, vw, dw, 256),), torch.uint8)
         st = q._stream()
         P = q._ptr
         self.wst = self.W.struct()
@@ -208,10 +209,15 @@ class LinearPlan:
                                  q.Call("qlora_bf16_gemm", P(self.X), M, K, P(self.TS), r, P(self.Fw), N, P(self.Y),
                                         ws, wsn, st)))
         if backward:
+            gdx = self.path_bwd == q.PATH_GEMV
             self.bwd.append(("lowrank_project_U", 2 * M * N * r,
                              q.Call("qlora_lowrank_project", P(self.dY), M, N, P(self.B), 1, r, self.s, P(self.U),
-                                    P(self.US), ws, wsn, st)))
-            if self.path_bwd == q.PATH_FUSED:
+                                    None if gdx else P(self.US), ws, wsn, st)))
+            if gdx:
+                self.bwd.append(("nf4_gemv_dx", 2 * M * N * K + 2 * M * K * r,
+                                 q.Call("qlora_nf4_gemv_dx", wref, P(self.dY), M, P(self.U), P(self.A), r, self.s,
+                                        P(self.dX), ws, wsn, st, keep=(self.wst,))))
+            elif self.path_bwd == q.PATH_FUSED:
                 self.bwd.append(("nf4_gemm_dx", 2 * M * N * K + 2 * M * K * r,
                                  q.Call("qlora_nf4_gemm_dx", wref, P(self.dY), M, P(self.US), P(self.A), r,
                                         P(self.dX), st, keep=(self.wst,))))
@@ -488,21 +494,50 @@ def step_distribution(wl: Workload, steps: int):
 
 
 def lora_bf16_base(wl: Workload, q, steps: int):
-    """The same step with a bf16 base: every call of the step except the two
-    weight expansions, over the operands they leave in place (the forward
-    [W | B B] and the transposed [W^T ; A A] a bf16-base layer would hold),
-    timed as one region like the step itself, and the same calls with the
-    expansions (QLoRA issued the same way) for the slowdown. Only for the
-    expanded path, where expansion and multiply are separate kernels. Returns
-    (ms per bf16-base step, ms per QLoRA step) or None."""
-    if any(p.path_fwd != q.PATH_EXPANDED or (p.bwd and p.path_bwd != q.PATH_EXPANDED) for p in wl.plans):
+    """The same step over bf16 base weights, the LoRA layer the pages compare
+    QLoRA with: every QLoRA layer call replaced by the bf16-base layer call
+    (qlora_lora_linear_fwd / _bwd) on the same activations, adapters and
+    output buffers, everything else (SiLU) as is, timed as one region like the
+    step, beside the QLoRA step timed the same way. The base weight is the
+    linear's dequantized weight (2 B per weight); the 65B stack holds a few
+    distinct bf16 copies per shape instead of 130 GB (each linear of a layer
+    its own, alternating between even and odd layers), so no call re-reads a
+    weight the last-level cache kept from the call before. Only for token
+    counts that run matrix-core GEMMs (M >= 17). Returns (ms per bf16-base
+    step, ms per QLoRA step) or None."""
+    if any(p.m <= 16 for p in wl.plans):
         return None
-    lora = [cl for nme, _, cl in wl.pieces if "expand" not in nme]
-    full = [cl for _, _, cl in wl.pieces]
-    for cl in full:
+    P, st = q._ptr, q._stream()
+    hold, swap = [], {}
+    copies = {}
+    nws = max(max(q.lora_linear_workspace_bytes(p.m, p.n, p.k, p.r, False),
+                  q.lora_linear_workspace_bytes(p.m, p.n, p.k, p.r, True) if p.api_bwd is not None else 0)
+              for p in wl.plans)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
+    per_layer = len(wl.c.linears)
+    for i, p in enumerate(wl.plans):
+        if wl.cid == 5:
+            layer, li = divmod(i, per_layer)
+            key = (p.n, p.k, li, layer % 2)
+            if key not in copies:
+                copies[key] = q.dequant(p.W) if i < per_layer else \
+                    (torch.randn((p.n, p.k), device="cuda") * 0.02).to(torch.bfloat16)
+            Wb = copies[key]
+        else:
+            Wb = q.dequant(p.W)
+            hold.append(Wb)
+        swap[id(p.api_fwd)] = q.Call("qlora_lora_linear_fwd", P(Wb), p.n, p.k, P(p.X), p.m, P(p.A), P(p.B), p.r, p.s,
+                                     P(p.Y), P(p.T), P(ws), ws.numel(), st)
+        if p.api_bwd is not None:
+            swap[id(p.api_bwd)] = q.Call("qlora_lora_linear_bwd", P(Wb), p.n, p.k, P(p.X), P(p.T), P(p.dY), p.m,
+                                         P(p.A), P(p.B), p.r, p.s, P(p.dX), P(p.dA), P(p.dB), 0, P(ws), ws.numel(),
+                                         st)
+    calls = [swap.get(id(cl), cl) for cl in wl.api]
+    for cl in calls:
         cl()
-    # the same building-block calls with the expansions, as a region of its own
-    return region_ms(lora, steps), region_ms(full, steps)
+    out = (region_ms(calls, steps), region_ms(wl.api, steps))
+    del hold, copies, ws
+    return out
 
 
 def merge_rows(wl: Workload, q, reps: int = 20):

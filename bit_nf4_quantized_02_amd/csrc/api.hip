@@ -58,7 +58,7 @@ int path_of_f16(int64_t M, int64_t n, int64_t k, int r, bool bwd) {
 }
 
 int path_of(int64_t M, int64_t n, int64_t k, int r, bool bwd) {
-  if (!bwd && small_m(M)) return QLORA_PATH_GEMV;
+  if (small_m(M)) return QLORA_PATH_GEMV;  // forward GEMV; backward: dX GEMV
   const int xc = lora_extra_cols(r);
   const bool fits = bwd ? gemm_bf16_offsets_fit(M, n, xc, k) : gemm_bf16_offsets_fit(M, k, xc, n);
   if (M >= QLORA_EXPAND_MIN_M && fits && (!bwd || n % 8 == 0)) return QLORA_PATH_EXPANDED;
@@ -123,14 +123,15 @@ struct BwdWs {
   void* proj = nullptr;
   void* grad = nullptr;
   uint16_t* F = nullptr;  // expanded transposed operand (large M)
-  float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles)
+  float* part = nullptr;  // split-K partial sums of its GEMM (few output tiles), or of the dX GEMV (M <= 16)
 };
 
 size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o, bool f16 = false) {
+  const bool gemv = !f16 && path_of(M, n, k, r, true) == QLORA_PATH_GEMV;
   if (r > 0) {
     if (!have_tsaved) o.T = cv.take<float>((size_t)M * r * 4);
     o.U = cv.take<float>((size_t)M * r * 4);
-    o.US = cv.take<uint16_t>((size_t)M * lora_extra_cols(r) * 2);
+    if (!gemv) o.US = cv.take<uint16_t>((size_t)M * lora_extra_cols(r) * 2);
     const size_t p1 = project_ws(M, n, r), p2 = project_ws(M, k, r);
     o.proj = cv.take<char>(p1 > p2 ? p1 : p2);
     const size_t g1 = grad_ws(M, k, r), g2 = grad_ws(M, n, r);
@@ -141,6 +142,7 @@ size_t bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& 
     const size_t pb = gemm_bf16_ws_bytes(M, n, lora_extra_cols(r), k);
     if (pb > 0) o.part = cv.take<float>(pb);
   }
+  if (gemv) o.part = cv.take<float>(gemv_dx_ws_bytes(n, k));
   return cv.used;
 }
 
@@ -342,6 +344,25 @@ qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight* w, const void* X, int64_
                                 r, scale, static_cast<uint16_t*>(Y), ws, static_cast<hipStream_t>(stream)));
 }
 
+size_t qlora_nf4_gemv_dx_workspace_bytes(int64_t n, int64_t k) {
+  if (n < 1 || k < 1 || k % QLORA_BLOCK) return 0;
+  return gemv_dx_ws_bytes(n, k);
+}
+
+qlora_status qlora_nf4_gemv_dx(const qlora_nf4_weight* w, const void* dY, int64_t M, const float* U, const void* A,
+                               int r, float scale, void* dX, void* ws, size_t ws_bytes, void* stream) {
+  const qlora_status s = check_weight(w);
+  if (s != QLORA_OK) return s;
+  if (M < 0 || M > 16 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if (!dY || !dX || !aligned16(dY) || !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!U || !A || !aligned16(U) || !aligned16(A))) return QLORA_ERR_INVALID_ARG;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < gemv_dx_ws_bytes(w->n, w->k)) return QLORA_ERR_WORKSPACE;
+  return hip_status(launch_gemv_dx(view_of(w), static_cast<const uint16_t*>(dY), M, U,
+                                   static_cast<const uint16_t*>(A), r, scale, static_cast<uint16_t*>(dX), ws,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 int qlora_linear_path(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
   if (M < 0 || n < 1 || k < 1 || (k % QLORA_BLOCK) != 0 || r < 0 || r > QLORA_MAX_RANK) return -1;
   if (is_bwd != 0 && is_bwd != 1) return -1;
@@ -504,9 +525,12 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
   const uint16_t* b = static_cast<const uint16_t*>(B);
   hipError_t e = hipSuccess;
   const uint8_t* dmask = drop ? mask : nullptr;  // dX: dropout on its low-rank term
+  const bool gemv = !f16 && path_of(M, w->n, w->k, r, true) == QLORA_PATH_GEMV;
   if (r > 0 && (dX || dA))
-    e = do_project(dy, M, w->n, b, 1, r, scale, o.U, dX ? o.US : nullptr, o.proj, st, nullptr, f16);
-  if (e == hipSuccess && dX) {
+    e = do_project(dy, M, w->n, b, 1, r, scale, o.U, (dX && !gemv) ? o.US : nullptr, o.proj, st, nullptr, f16);
+  if (e == hipSuccess && dX && gemv) {
+    e = launch_gemv_dx(v, dy, M, o.U, a, r, scale, static_cast<uint16_t*>(dX), o.part, st, dmask, keep_scale);
+  } else if (e == hipSuccess && dX) {
     if (f16 || path_of(M, w->n, w->k, r, true) == QLORA_PATH_EXPANDED) {
       e = launch_expand(v, a, r, true, o.F, st, f16);
       if (e == hipSuccess)
@@ -599,3 +623,166 @@ qlora_status qlora_silu_mul_bwd(const void* G, const void* Up, const void* dH, v
 
 }  // extern "C"
 
+// ---- the same layer over a bf16 base weight (LoRA without quantization, the
+// pages' comparison point). Same low-rank kernels; the forward multiplies W as
+// stored (the plain GEMM with the low-rank operand as a separate matrix), and
+// so does dX (the same GEMM reading W's tiles contraction-major).
+namespace {
+
+bool lora_shape_ok(int64_t n, int64_t k, int r) {
+  return n >= 1 && k >= QLORA_BLOCK && k % QLORA_BLOCK == 0 && r >= 0 && r <= QLORA_MAX_RANK;
+}
+
+struct LoraFwdWs {
+  uint16_t* TS = nullptr;
+  void* proj = nullptr;
+  uint16_t* Bx = nullptr;  // [n, xc] low-rank operand rows
+  float* part = nullptr;
+};
+
+size_t lora_fwd_ws(int64_t M, int64_t n, int64_t k, int r, Carver& cv, LoraFwdWs& o) {
+  const int xc = lora_extra_cols(r);
+  if (r > 0) {
+    o.TS = cv.take<uint16_t>((size_t)M * xc * 2);
+    o.proj = cv.take<char>(project_ws(M, k, r));
+    o.Bx = cv.take<uint16_t>((size_t)n * xc * 2);
+  }
+  const size_t pb = gemm_bf16_ws_bytes(M, k, xc, n);
+  if (pb > 0) o.part = cv.take<float>(pb);
+  return cv.used;
+}
+
+// dX over the bf16 base: the plain GEMM reading W's tiles as stored
+// (contraction-major) when dY's rows allow direct copies (n % 8 == 0) and the
+// operands fit its 32-bit offsets; the fused kernel otherwise.
+bool lora_dx_nn(int64_t M, int64_t n, int64_t k, int r) {
+  return n % 8 == 0 && gemm_bf16_offsets_fit(M, n, lora_extra_cols(r), k);
+}
+
+size_t lora_bwd_ws(int64_t M, int64_t n, int64_t k, int r, bool have_tsaved, Carver& cv, BwdWs& o) {
+  if (lora_dx_nn(M, n, k, r)) {
+    if (r > 0) o.F = cv.take<uint16_t>((size_t)lora_extra_cols(r) * k * 2);  // [A ; A ; 0]
+    const size_t pb = gemm_bf16_ws_bytes(M, n, lora_extra_cols(r), k);
+    if (pb > 0) o.part = cv.take<float>(pb);
+  }
+  if (r > 0) {
+    if (!have_tsaved) o.T = cv.take<float>((size_t)M * r * 4);
+    o.U = cv.take<float>((size_t)M * r * 4);
+    o.US = cv.take<uint16_t>((size_t)M * lora_extra_cols(r) * 2);
+    const size_t p1 = project_ws(M, n, r), p2 = project_ws(M, k, r);
+    o.proj = cv.take<char>(p1 > p2 ? p1 : p2);
+    const size_t g1 = grad_ws(M, k, r), g2 = grad_ws(M, n, r);
+    o.grad = cv.take<char>(g1 > g2 ? g1 : g2);
+  }
+  return cv.used;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qlora_lora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
+  if (M < 1 || !lora_shape_ok(n, k, r) || (is_bwd != 0 && is_bwd != 1)) return 0;
+  Carver cv(nullptr);
+  if (!is_bwd) {
+    LoraFwdWs o;
+    return lora_fwd_ws(M, n, k, r, cv, o);
+  }
+  BwdWs o;
+  return lora_bwd_ws(M, n, k, r, false, cv, o);
+}
+
+qlora_status qlora_lora_linear_fwd(const void* W, int64_t n, int64_t k, const void* X, int64_t M, const void* A,
+                                   const void* B, int r, float scale, void* Y, float* T_save, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (M < 0 || !lora_shape_ok(n, k, r)) return QLORA_ERR_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if (!W || !X || !Y || !aligned16(W) || !aligned16(X) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
+  if (T_save && !aligned16(T_save)) return QLORA_ERR_INVALID_ARG;
+  const int xc = lora_extra_cols(r);
+  if (!gemm_bf16_offsets_fit(M, k, xc, n)) return QLORA_ERR_SHAPE;
+  {
+    Carver probe(nullptr);
+    LoraFwdWs tmp;
+    const size_t need = lora_fwd_ws(M, n, k, r, probe, tmp);
+    if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  LoraFwdWs o;
+  lora_fwd_ws(M, n, k, r, cv, o);
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  const uint16_t* w = static_cast<const uint16_t*>(W);
+  hipError_t e = hipSuccess;
+  if (r > 0) {
+    e = do_project(x, M, k, static_cast<const uint16_t*>(A), 0, r, scale, T_save, o.TS, o.proj, st);
+    if (e == hipSuccess) e = launch_lowrank_rows(static_cast<const uint16_t*>(B), n, r, o.Bx, st);
+  }
+  if (e == hipSuccess)
+    e = launch_gemm_bf16_ext(x, M, k, o.TS, xc, w, k, o.Bx, xc, n, static_cast<uint16_t*>(Y), o.part, st);
+  return hip_status(e);
+}
+
+qlora_status qlora_lora_linear_bwd(const void* W, int64_t n, int64_t k, const void* X, const float* T_saved,
+                                   const void* dY, int64_t M, const void* A, const void* B, int r, float scale,
+                                   void* dX, float* dA, float* dB, int accumulate, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (M < 0 || !lora_shape_ok(n, k, r)) return QLORA_ERR_SHAPE;
+  if (accumulate != 0 && accumulate != 1) return QLORA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    if (accumulate || r == 0) return QLORA_OK;
+    if ((dA && !aligned16(dA)) || (dB && !aligned16(dB))) return QLORA_ERR_INVALID_ARG;
+    hipError_t e = dA ? zero_f32(dA, (int64_t)r * k, st) : hipSuccess;
+    if (e == hipSuccess && dB) e = zero_f32(dB, n * (int64_t)r, st);
+    return hip_status(e);
+  }
+  if (!W || !aligned16(W) || !dY || !aligned16(dY)) return QLORA_ERR_INVALID_ARG;
+  if (dX && !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
+  if (r == 0) { dA = nullptr; dB = nullptr; }
+  const bool need_x = (dA != nullptr) || (dB != nullptr && T_saved == nullptr);
+  if (need_x && (!X || !aligned16(X))) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;
+  if ((dA && !aligned16(dA)) || (dB && !aligned16(dB)) || (T_saved && !aligned16(T_saved)))
+    return QLORA_ERR_INVALID_ARG;
+  {
+    Carver probe(nullptr);
+    BwdWs tmp;
+    const size_t need = lora_bwd_ws(M, n, k, r, T_saved != nullptr, probe, tmp);
+    if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  }
+  Carver cv(ws);
+  BwdWs o;
+  lora_bwd_ws(M, n, k, r, T_saved != nullptr, cv, o);
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  const uint16_t* dy = static_cast<const uint16_t*>(dY);
+  const uint16_t* a = static_cast<const uint16_t*>(A);
+  const uint16_t* b = static_cast<const uint16_t*>(B);
+  hipError_t e = hipSuccess;
+  if (r > 0 && (dX || dA)) e = do_project(dy, M, n, b, 1, r, scale, o.U, dX ? o.US : nullptr, o.proj, st);
+  if (e == hipSuccess && dX) {
+    if (lora_dx_nn(M, n, k, r)) {
+      const int xc = lora_extra_cols(r);
+      if (r > 0) e = launch_lowrank_cols(a, r, k, o.F, st);
+      if (e == hipSuccess)
+        e = launch_gemm_bf16_ext(dy, M, n, r > 0 ? o.US : nullptr, xc, static_cast<const uint16_t*>(W), k, o.F, k, k,
+                                 static_cast<uint16_t*>(dX), o.part, st, nullptr, 1.0f, false, /*nn=*/true);
+    } else {
+      e = launch_gemm_w16_dx(static_cast<const uint16_t*>(W), n, k, dy, M, r > 0 ? o.US : nullptr, a, r,
+                             static_cast<uint16_t*>(dX), st);
+    }
+  }
+  if (e == hipSuccess && dA) e = do_grad(x, M, k, o.U, r, scale, dA, 0, accumulate, o.grad, st);
+  if (e == hipSuccess && dB) {
+    const float* T = T_saved;
+    if (T == nullptr) {
+      e = do_project(x, M, k, a, 0, r, scale, o.T, nullptr, o.proj, st);
+      T = o.T;
+    }
+    if (e == hipSuccess) e = do_grad(dy, M, n, T, r, scale, dB, 1, accumulate, o.grad, st);
+  }
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -169,7 +169,62 @@ __global__ __launch_bounds__(256) void expand_cols_kernel(const uint8_t* __restr
     }
 }
 
+// Low-rank operand rows alone, [n, xc]: row i = [B[i, :] | B[i, :] | 0 ...]
+// (the columns the row expansion appends to W'), for a GEMM whose weight
+// operand is a separate matrix. One thread per 8 output columns.
+__global__ __launch_bounds__(256) void lowrank_rows_kernel(const uint16_t* __restrict__ B, int64_t n, int r, int xc,
+                                                           u32x4* __restrict__ out) {
+  const int cpr = xc / 8;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= n * cpr) return;
+  const int64_t i = q / cpr;
+  const int j0 = (int)(q % cpr) * 8;
+  u32x4 v;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t h[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = j0 + 2 * p + e;
+      h[e] = j < 2 * r ? (uint32_t)B[i * r + (j % r)] : 0u;
+    }
+    v[p] = h[0] | (h[1] << 16);
+  }
+  out[q] = v;
+}
+
+// [xc, k] rows [A ; A ; 0]: row x is A's row x % r for x < 2r, zeros after.
+__global__ __launch_bounds__(256) void lowrank_cols_kernel(const uint16_t* __restrict__ A, int r, int xc, int64_t k,
+                                                           u32x4* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = k / 8;
+  if (q >= (int64_t)xc * cpr) return;
+  const int x = (int)(q / cpr);
+  const int64_t c = (q % cpr) * 8;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (x < 2 * r) v = *reinterpret_cast<const u32x4*>(A + (int64_t)(x % r) * k + c);
+  out[q] = v;
+}
+
 }  // namespace
+
+hipError_t launch_lowrank_cols(const uint16_t* A, int r, int64_t k, uint16_t* out, hipStream_t stream) {
+  const int xc = lora_extra_cols(r);
+  if (xc == 0 || k == 0) return hipSuccess;
+  const int64_t total = (int64_t)xc * (k / 8);
+  lowrank_cols_kernel<<<(unsigned)cdiv(total, (int64_t)256), 256, 0, stream>>>(A, r, xc, k,
+                                                                               reinterpret_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_lowrank_rows(const uint16_t* B, int64_t n, int r, uint16_t* out, hipStream_t stream) {
+  const int xc = lora_extra_cols(r);
+  if (xc == 0 || n == 0) return hipSuccess;
+  const int64_t total = n * (xc / 8);
+  lowrank_rows_kernel<<<(unsigned)cdiv(total, (int64_t)256), 256, 0, stream>>>(B, n, r, xc,
+                                                                               reinterpret_cast<u32x4*>(out));
+  return hipGetLastError();
+}
 
 int64_t expand_pad_rows(int64_t n) { return cdiv(n, (int64_t)kBlock) * kBlock; }
 

@@ -41,8 +41,10 @@ struct BfArgs {
   int64_t M, kc;
   const uint16_t* act_x; // [M, kx] low-rank split columns
   int kx;
-  const uint16_t* f;     // [nout, ldf] expanded operand, ldf = 64 * nk_main + kx
+  const uint16_t* f;     // [nout, ldf] weight operand (rows = outputs), ldf >= 64 * nk_main
   int64_t ldf, nout;
+  const uint16_t* fx;    // [nout, ldx] low-rank operand rows [B | B | 0] or [A ; A ; 0]^T (kx columns)
+  int64_t ldx;
   uint16_t* out;         // [M, nout]
   // Workgroups [0, full) compute whole tiles (tiles 0 .. full-1 in tile_of
   // order); the `tail` tiles after them are each split over `splits`
@@ -71,9 +73,18 @@ struct CopyPlan {
   u32x4 a;      // activation, base steps
   u32x4 alast;  // activation, last base step (clamped columns)
   u32x4 x;      // low-rank split columns
-  u32x4 f;      // expanded operand
+  u32x4 f;      // weight operand, base steps
+  u32x4 fx;     // low-rank operand
 };
 
+// kNN: the weight operand is stored [contraction][output] (a bf16 base W
+// [n, k] for dX): its tile is 64 contraction rows x 256 output columns, 512 B
+// per row, and an instruction copies two rows; 16-byte chunk c of row r sits
+// at c ^ (4 (r & 3)), so the four rows one transposing fragment read touches
+// fall on distinct banks.
+__device__ __forceinline__ int nn_key(int row) { return 4 * (row & 3); }
+
+template <bool kNN>
 __device__ __forceinline__ void make_plan(const BfArgs& a, int64_t m0, int64_t n0, int nk_main, int wave, CopyPlan& p) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -81,14 +92,49 @@ __device__ __forceinline__ void make_plan(const BfArgs& a, int64_t m0, int64_t n
     const int row = (wave * kCopies + i) * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ swz_key(row);
     const int64_t m = m0 + row < a.M ? m0 + row : a.M - 1;
-    const int64_t n = n0 + row < a.nout ? n0 + row : a.nout - 1;
     p.a[i] = (uint32_t)((m * a.kc + 8 * lc) * 2);
     const int64_t cl = (int64_t)(nk_main - 1) * kBK + 8 * lc;
     const int64_t cc = cl < a.kc ? cl : a.kc - 8;
     p.alast[i] = (uint32_t)((m * a.kc + cc - (int64_t)(nk_main - 1) * kBK) * 2);
     p.x[i] = (uint32_t)((m * a.kx + 8 * lc) * 2);
-    p.f[i] = (uint32_t)((n * a.ldf + 8 * lc) * 2);
+    if constexpr (!kNN) {
+      const int64_t n = n0 + row < a.nout ? n0 + row : a.nout - 1;
+      p.f[i] = (uint32_t)((n * a.ldf + 8 * lc) * 2);
+      p.fx[i] = (uint32_t)((n * a.ldx + 8 * lc) * 2);
+    } else {
+      // rows 2 blk, 2 blk + 1 of the step's 64; output columns past nout read
+      // other data (those outputs are never stored), rows past the end of the
+      // operand read zeros (buffer range check)
+      const int blk = wave * kCopies + i;
+      const int r = 2 * blk + (lane >> 5);
+      const int c = (lane & 31) ^ nn_key(r);
+      p.f[i] = (uint32_t)((r * a.ldf + n0 + 8 * c) * 2);
+      p.fx[i] = (uint32_t)((r * a.ldx + n0 + 8 * c) * 2);
+    }
   }
+}
+
+// B-operand fragment of v_mfma_f32_32x32x16_bf16 from a kNN tile: output
+// column cb + lane % 32, contraction rows 16 kk + 8 (lane / 32) .. +7. Two
+// transposing reads of 4 rows each: in every 16-lane group lane i addresses
+// row base + i / 4, columns 4 (i % 4) .. +3 of its 16 columns.
+__device__ __forceinline__ bf16x8 nn_frag(const char* T, int cb, int kk, int lane) {
+  const int i = lane & 15;
+  const int col = cb + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+  const int row = 16 * kk + 8 * (lane >> 5) + (i >> 2);
+  const char* p = T + row * 512 + (((col >> 3) ^ nn_key(row)) << 4) + (col & 7) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 4 * 512));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool kNN>
+__device__ __forceinline__ bf16x8 b_frag(const char* Bc, int cb, int kk, int lane) {
+  if constexpr (kNN)
+    return nn_frag(Bc, cb, kk, lane);
+  else
+    return tile_frag(Bc, cb, kk, lane);
 }
 
 // Direct buffer load into LDS (16 bytes per lane, LDS address from the wave-
@@ -111,7 +157,7 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* p, int64_t bytes) {
 }
 
 struct Rsrc {
-  i32x4 act, x, f;
+  i32x4 act, x, f, fx;
 };
 
 __device__ __forceinline__ void copy16(const i32x4& r, uint32_t voff, int soff, char* dst) {
@@ -120,20 +166,28 @@ __device__ __forceinline__ void copy16(const i32x4& r, uint32_t voff, int soff, 
 
 // Copies of step `step` into (As, Bs). The operand choice is wave-uniform
 // (it depends on the step only), so descriptors and step offsets stay scalar.
+template <bool kNN>
 __device__ __forceinline__ void issue_step(const Rsrc& rs, const CopyPlan& p, int step, int nk_main, int wave,
-                                           char* As, char* Bs) {
+                                           char* As, char* Bs, int64_t ldf, int64_t ldx) {
+  // the weight operand advances 64 columns (NT) or 64 rows (NN) per step
+  // (32-bit scalar offsets: unsigned arithmetic, operands under 4 GiB)
+  const uint32_t fstep = kNN ? (uint32_t)(kBK * ldf * 2) : (uint32_t)(kBK * 2);
+  const uint32_t xstep = kNN ? (uint32_t)(kBK * ldx * 2) : (uint32_t)(kBK * 2);
   char* const as = As + wave * kCopies * 1024;
   char* const bs = Bs + wave * kCopies * 1024;
   if (step < nk_main) {
     const u32x4 off = step == nk_main - 1 ? p.alast : p.a;
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) copy16(rs.act, off[i], step * (kBK * 2), as + i * 1024);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy16(rs.f, p.f[i], (int)((uint32_t)step * fstep), bs + i * 1024);
   } else {
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) copy16(rs.x, p.x[i], (step - nk_main) * (kBK * 2), as + i * 1024);
-  }
 #pragma unroll
-  for (int i = 0; i < kCopies; ++i) copy16(rs.f, p.f[i], step * (kBK * 2), bs + i * 1024);
+    for (int i = 0; i < kCopies; ++i)
+      copy16(rs.fx, p.fx[i], (int)((uint32_t)(step - nk_main) * xstep), bs + i * 1024);
+  }
 }
 
 // One step: MFMAs on (Ac, Bc) while the copies of step + 1 fill (An, Bn).
@@ -143,8 +197,9 @@ __device__ __forceinline__ void issue_step(const Rsrc& rs, const CopyPlan& p, in
 // GEMM: 4-6% faster where the operands (360 MB of expanded weight and more)
 // exceed the 256 MB last-level cache and stream from HBM, 3-10% slower where
 // they fit in it; the launch picks it by operand size.
-template <bool kF16, bool kPrio>
-__device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int step, int nk, int nk_main, int wave,
+template <bool kF16, bool kPrio, bool kNN>
+__device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
+                                          int nk_main, int wave,
                                           const char* __restrict__ Ac, const char* __restrict__ Bc,
                                           char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN]) {
   const int lane = threadIdx.x & 63;
@@ -158,11 +213,11 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
 #pragma unroll
     for (int i = 0; i < kTM; ++i) af[buf][i] = tile_frag(Ac, wm0 + i * 32, kk, lane);
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) bfr[buf][j] = tile_frag(Bc, wn0 + j * 32, kk, lane);
+    for (int j = 0; j < kTN; ++j) bfr[buf][j] = b_frag<kNN>(Bc, wn0 + j * 32, kk, lane);
   };
   read_frags(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  issue_step(rs, p, s1, nk_main, wave, An, Bn);
+  issue_step<kNN>(rs, p, s1, nk_main, wave, An, Bn, a.ldf, a.ldx);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (kPrio) {
     __builtin_amdgcn_s_setprio(1);
@@ -180,7 +235,7 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
   }
   // schedule: for substeps 0..2 one fragment read (of the next substep) per
   // MFMA, then the last substep's MFMAs
-  constexpr int kReads = kTM + kTN, kMfma = kTM * kTN;
+  constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk)
 #pragma unroll
@@ -198,7 +253,7 @@ __device__ __forceinline__ void bf16_step(const Rsrc& rs, const CopyPlan& p, int
 }
 
 // One step without copies in flight: fragments of (Ac, Bc) and their MFMAs.
-template <bool kF16>
+template <bool kF16, bool kNN>
 __device__ __forceinline__ void plain_step(const char* Ac, const char* Bc, int wave, f32x16 (&acc)[kTM][kTN]) {
   const int lane = threadIdx.x & 63;
   const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
@@ -208,7 +263,7 @@ __device__ __forceinline__ void plain_step(const char* Ac, const char* Bc, int w
 #pragma unroll
     for (int i = 0; i < kTM; ++i) af[i] = tile_frag(Ac, wm0 + i * 32, kk, lane);
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) bfr[j] = tile_frag(Bc, wn0 + j * 32, kk, lane);
+    for (int j = 0; j < kTN; ++j) bfr[j] = b_frag<kNN>(Bc, wn0 + j * 32, kk, lane);
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -262,7 +317,7 @@ __device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char
 // the tile's mask bytes land in buffers 1, masks and scales the accumulators
 // from there, then runs its main steps as usual.
 // kF16: fp16 operands and output (the compute-type ablation), else bf16.
-template <bool kMask, bool kF16, bool kPrio = false>
+template <bool kMask, bool kF16, bool kPrio = false, bool kNN = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
   // direct copies from the one being read
@@ -296,11 +351,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   const int nk = sbeg + chunk < nk_all ? sbeg + chunk : nk_all;  // exclusive end
 
   CopyPlan plan;
-  make_plan(a, m0, n0, nk_main, wave, plan);
+  make_plan<kNN>(a, m0, n0, nk_main, wave, plan);
   Rsrc rs;
   rs.act = make_rsrc(a.act, a.M * a.kc * 2);
   rs.x = make_rsrc(a.act_x, a.M * (int64_t)a.kx * 2);
-  rs.f = make_rsrc(a.f, a.nout * a.ldf * 2);
+  rs.f = make_rsrc(a.f, (kNN ? a.kc : a.nout) * a.ldf * 2);
+  rs.fx = make_rsrc(a.fx, (kNN ? (int64_t)a.kx : a.nout) * a.ldx * 2);
 
   f32x16 acc[kTM][kTN];
 #pragma unroll
@@ -315,9 +371,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
     if (nk > nk_main) {
       issue_mask_lds(a, m0, n0, wave, As1, Bs1);
       for (int step = sbeg > nk_main ? sbeg : nk_main; step < nk; ++step) {
-        issue_step(rs, plan, step, nk_main, wave, As0, Bs0);
+        issue_step<kNN>(rs, plan, step, nk_main, wave, As0, Bs0, a.ldf, a.ldx);
         step_barrier<0>();  // (the first one also waits for the mask bytes)
-        plain_step<kF16>(As0, Bs0, wave, acc);
+        plain_step<kF16, kNN>(As0, Bs0, wave, acc);
         __syncthreads();  // every wave's reads done before the next copies land
       }
       mask_acc_lds(acc, As1, Bs1, a.keep_scale, a.M, a.nout, m0, n0, wm0, wn0, lane);
@@ -326,12 +382,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
     }
   }
   if (sbeg < nk_end) {  // (every split range is non-empty for the split counts split_plan picks)
-    issue_step(rs, plan, sbeg, nk_main, wave, As0, Bs0);
+    issue_step<kNN>(rs, plan, sbeg, nk_main, wave, As0, Bs0, a.ldf, a.ldx);
     step_barrier<0>();
     for (int step = sbeg; step < nk_end; step += 2) {
-      bf16_step<kF16, kPrio>(rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc);
+      bf16_step<kF16, kPrio, kNN>(a, rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc);
       if (step + 1 < nk_end)
-        bf16_step<kF16, kPrio>(rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc);
+        bf16_step<kF16, kPrio, kNN>(a, rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc);
     }
   }
 
@@ -478,22 +534,28 @@ bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
 // GEMM raises its MFMA priority: the last-level cache (256 MB)
 constexpr int64_t kPrioOperandBytes = 256LL << 20;
 
-hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
-                            const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
-                            const uint8_t* mask, float keep_scale, bool f16) {
+hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
+                                const uint16_t* f, int64_t ldf, const uint16_t* fx, int64_t ldx, int64_t nout,
+                                uint16_t* out, float* part, hipStream_t stream, const uint8_t* mask, float keep_scale,
+                                bool f16, bool nn) {
   BfArgs a{};
   a.mask = mask;
   a.keep_scale = keep_scale;
   a.act = act; a.M = M; a.kc = kc;
   a.act_x = split; a.kx = kx;
-  a.f = f; a.ldf = cdiv(kc, (int64_t)kBK) * kBK + kx; a.nout = nout;
+  a.f = f; a.ldf = ldf; a.nout = nout;
+  a.fx = kx > 0 ? fx : f; a.ldx = kx > 0 ? ldx : ldf;
   a.out = out;
   const SplitPlan sp = split_plan(M, kc, kx, nout);
   a.full = sp.full; a.tail = sp.tail; a.splits = sp.splits;
   a.part = part;
   if (a.splits > 1 && part == nullptr) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.full + a.tail * a.splits));
-  if (f16) {
+  if (nn) {
+    // the weight operand stored [contraction][output] (bf16 base, dX)
+    if (mask != nullptr || f16) return hipErrorInvalidValue;
+    gemm_bf16_kernel<false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
+  } else if (f16) {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
     else
@@ -516,6 +578,17 @@ hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const ui
           part, a.full, a.tail, a.splits, M, nout, out);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
+                            const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
+                            const uint8_t* mask, float keep_scale, bool f16) {
+  // the expanded operand holds the low-rank rows right after the padded base
+  // columns of each row: [W' (kcp) | low-rank (kx)]
+  const int64_t kcp = cdiv(kc, (int64_t)kBK) * kBK;
+  const int64_t ldf = kcp + kx;
+  return launch_gemm_bf16_ext(act, M, kc, split, kx, f, ldf, f + kcp, ldf, nout, out, part, stream, mask, keep_scale,
+                              f16, false);
 }
 
 }  // namespace qlora

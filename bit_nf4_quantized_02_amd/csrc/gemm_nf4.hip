@@ -71,6 +71,10 @@ struct GemmArgs {
   const float* mean;
   const float* codebook;
   bool s2_bf16;           // per-block bf16 scales (no double quantization)
+  // a bf16 base weight [wn, wk] instead (kW16 kernels): its tile is copied as
+  // it is, nothing to expand (the 16-bit-base LoRA layer the pages compare
+  // QLoRA with)
+  const uint16_t* w16;
   int64_t wn, wk;
   // low-rank second factor: B [wn, r] (forward) or A [r, wk] (dX)
   const uint16_t* lr;
@@ -167,11 +171,12 @@ struct WStage {
   uint32_t q[4];  // 4 code words (32 weights)
   uint32_t c8;    // raw code8 byte of the block
   float s2v;      // raw second-level scale of the block
+  u32x4 w[4];     // kW16: the 32 bf16 weights themselves
 };
 
 // Rows outside the weight get code 7 (the zero level) so they contribute
 // exactly zero wherever they enter a contraction.
-template <bool kDX>
+template <bool kDX, bool kW16 = false>
 __device__ __forceinline__ void load_w(const GemmArgs& a, int64_t n0, int step, WStage& st) {
   const int t = threadIdx.x;
   const int64_t kblocks = a.wk / kBlock;
@@ -186,6 +191,16 @@ __device__ __forceinline__ void load_w(const GemmArgs& a, int64_t n0, int step, 
   const bool ok = n < a.wn && k < a.wk;
   const int64_t nc = n < a.wn ? n : a.wn - 1;
   const int64_t kc = k < a.wk ? k : a.wk - 32;
+  if constexpr (kW16) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.w16 + nc * a.wk + kc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 v = src[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.w[j][e] = ok ? v[e] : 0u;
+    }
+    return;
+  }
   const u32x4 q = *reinterpret_cast<const u32x4*>(a.codes + nc * (a.wk / 2) + kc / 2);
   const int64_t blk = nc * kblocks + kc / kBlock;
   scale_fields(a.code8, a.s2, a.s2_bf16, blk, st.c8, st.s2v);
@@ -218,9 +233,26 @@ __device__ __forceinline__ float decode_scale(const WStage& st, float mean) {
   return decode_block_scale(st.c8, st.s2v, mean);
 }
 
-// Whole tile at once (prologue).
+// kW16: quarter `part` of the copied bf16 weights into LDS, where
+// finish_part would put the expanded ones.
 template <bool kDX>
+__device__ __forceinline__ void store_part16(char* Bs, const WStage& st, int part) {
+  const int t = threadIdx.x;
+  if constexpr (!kDX) {
+    *reinterpret_cast<u32x4*>(Bs + swz(t >> 1, (t & 1) * 4 + part)) = st.w[part];
+  } else {
+    *reinterpret_cast<u32x4*>(Bs + (t >> 3) * kDxPitch + ((t & 7) * 32 + part * 8) * 2) = st.w[part];
+  }
+}
+
+// Whole tile at once (prologue).
+template <bool kDX, bool kW16 = false>
 __device__ __forceinline__ void store_w_all(char* Bs, const float* lut, const WStage& st, float mean) {
+  if constexpr (kW16) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) store_part16<kDX>(Bs, st, p);
+    return;
+  }
   const float cp = decode_scale(st, mean);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -294,7 +326,7 @@ __device__ __forceinline__ bf16x8 dx_b_frag(const char* Bc, int cb, int r0, int 
 // direct copies into An cannot alias the fragment reads of Ac, and does not
 // wait for those copies before reading.
 
-template <bool kDX, bool kVec>
+template <bool kDX, bool kVec, bool kW16>
 __device__ __forceinline__ void pipelined_step(const GemmArgs& a, int step, int nk_main, int64_t m0, int64_t n0,
                                                const char* __restrict__ Ac, const char* __restrict__ Bc,
                                                char* __restrict__ An, char* __restrict__ Bn, const float* lut,
@@ -319,14 +351,14 @@ __device__ __forceinline__ void pipelined_step(const GemmArgs& a, int step, int 
     }
   };
   // first consume what the previous step loaded, before issuing new loads
-  const float cp = decode_scale(wnxt, mean);
+  const float cp = kW16 ? 0.0f : decode_scale(wnxt, mean);
   float lv[2][8];
-  lookup_part(lut, wnxt, 0, lv[0]);
+  if constexpr (!kW16) lookup_part(lut, wnxt, 0, lv[0]);
   read_frags(0, 0);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (kVec) issue_act_lds(a, m0, s1, nk_main, An);
   __builtin_amdgcn_sched_barrier(0);  // the copies stay ahead of the weight loads
-  load_w<kDX>(a, n0, s2, wcur);
+  load_w<kDX, kW16>(a, n0, s2, wcur);
   __builtin_amdgcn_sched_barrier(0);  // issue the weight loads now, a full step ahead of their use
 #pragma unroll
   for (int kk = 0; kk < kBK / 16; ++kk) {
@@ -335,14 +367,17 @@ __device__ __forceinline__ void pipelined_step(const GemmArgs& a, int step, int 
     // quarter's MFMAs, so their LDS latency is covered by the MFMAs
     if (kk < 3) {
       read_frags(kk + 1, cb ^ 1);
-      lookup_part(lut, wnxt, kk + 1, lv[cb ^ 1]);
+      if constexpr (!kW16) lookup_part(lut, wnxt, kk + 1, lv[cb ^ 1]);
     }
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][i], bfr[cb][j], acc[i][j], 0, 0, 0);
-    finish_part<kDX>(Bn, lv[cb], cp, kk);
+    if constexpr (kW16)
+      store_part16<kDX>(Bn, wnxt, kk);
+    else
+      finish_part<kDX>(Bn, lv[cb], cp, kk);
   }
   if constexpr (!kVec) {
     store_act(An, ast);
@@ -356,7 +391,7 @@ __device__ __forceinline__ void pipelined_step(const GemmArgs& a, int step, int 
 }
 
 // ------------------------------------------------------------ kernel
-template <bool kDX, bool kVec>
+template <bool kDX, bool kVec, bool kW16 = false>
 __global__ __launch_bounds__(kThreads) void gemm_nf4_kernel(GemmArgs a) {
   constexpr int TM = kTM, TN = kTN;
   // four separate arrays (not one [2][...] array) so the compiler can tell the
@@ -375,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nf4_kernel(GemmArgs a) {
   int64_t tm, tn;
   tile_of(tm, tn, cdiv(a.M, kBM), cdiv(a.nout, kBN));
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
-  if (t < 16) lut[t] = a.codebook[t];
+  if (!kW16 && t < 16) lut[t] = a.codebook[t];
 
   const int nk_main = (int)cdiv(a.kc, kBK);
   const int nk = nk_main + a.kx / kBK;
@@ -439,14 +474,14 @@ __global__ __launch_bounds__(kThreads) void gemm_nf4_kernel(GemmArgs a) {
   } else {
     load_act<kVec>(a, m0, 0, nk_main, ast);
   }
-  load_w<kDX>(a, n0, 0, wst[0]);
-  load_w<kDX>(a, n0, nk_main > 1 ? 1 : 0, wst[1]);
+  load_w<kDX, kW16>(a, n0, 0, wst[0]);
+  load_w<kDX, kW16>(a, n0, nk_main > 1 ? 1 : 0, wst[1]);
   __syncthreads();  // lut
   if constexpr (!kVec) {
     store_act(As[0], ast);
     load_act<kVec>(a, m0, nk_main > 1 ? 1 : 0, nk_main, ast);
   }
-  store_w_all<kDX>(Bs[0], lut, wst[0], mean);
+  store_w_all<kDX, kW16>(Bs[0], lut, wst[0], mean);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -456,10 +491,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nf4_kernel(GemmArgs a) {
   // writes they feed land in a buffer no later step reads, keeping the body
   // free of branches.
   for (int step = 0; step < nk_main; step += 2) {
-    pipelined_step<kDX, kVec>(a, step, nk_main, m0, n0, As0, Bs0, As1, Bs1, lut, mean, wst[0], wst[1], ast, acc);
+    pipelined_step<kDX, kVec, kW16>(a, step, nk_main, m0, n0, As0, Bs0, As1, Bs1, lut, mean, wst[0], wst[1], ast,
+                                    acc);
     if (step + 1 < nk_main)
-      pipelined_step<kDX, kVec>(a, step + 1, nk_main, m0, n0, As1, Bs1, As0, Bs0, lut, mean, wst[1], wst[0], ast,
-                                acc);
+      pipelined_step<kDX, kVec, kW16>(a, step + 1, nk_main, m0, n0, As1, Bs1, As0, Bs0, lut, mean, wst[1], wst[0],
+                                      ast, acc);
   }
   if (!masked) lowrank_steps();
 
@@ -512,6 +548,23 @@ hipError_t launch_gemm_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const
     gemm_nf4_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
   else
     gemm_nf4_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w16_dx(const uint16_t* W, int64_t n, int64_t k, const uint16_t* dY, int64_t M,
+                              const uint16_t* US, const uint16_t* A, int r, uint16_t* dX, hipStream_t stream) {
+  GemmArgs a{};
+  a.act = dY; a.lda = n; a.M = M; a.kc = n;
+  a.act_x = US; a.kx = lora_extra_cols(r);
+  a.w16 = W;
+  a.wn = n; a.wk = k;
+  a.lr = A; a.r = r;
+  a.out = dX; a.nout = k;
+  const dim3 grid((unsigned)(cdiv(k, kBN) * cdiv(M, kBM)));
+  if (n % 8 == 0)
+    gemm_nf4_kernel<true, true, true><<<grid, kThreads, 0, stream>>>(a);
+  else
+    gemm_nf4_kernel<true, false, true><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

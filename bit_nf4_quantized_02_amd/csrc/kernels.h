@@ -74,12 +74,22 @@ hipError_t launch_gemm_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const
                           const uint16_t* A, int r, uint16_t* dX, hipStream_t stream,
                           const uint8_t* mask = nullptr, float keep_scale = 1.0f);
 
+// dX = RN_bf16(dY W + [sU_hi | sU_lo] [A ; A]) for a bf16 base weight W [n, k]
+// (k % 64 == 0): the fused kernel's dX with the weight tile copied instead of
+// expanded.
+hipError_t launch_gemm_w16_dx(const uint16_t* W, int64_t n, int64_t k, const uint16_t* dY, int64_t M,
+                              const uint16_t* US, const uint16_t* A, int r, uint16_t* dX, hipStream_t stream);
+
 // Expanded bf16 operand of the plain GEMM (forward [n, k + xc], or dX
 // [k, np + xc] with np = n rounded up to 64), LoRA factor appended.
 int64_t expand_pad_rows(int64_t n);
 size_t expand_ws_bytes(int64_t n, int64_t k, int r, bool transposed);
 hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool transposed, uint16_t* out,
                          hipStream_t stream, bool f16 = false);
+
+// [n, lora_extra_cols(r)] rows [B | B | 0] (bf16), the low-rank operand of
+// the forward GEMM when the weight operand is a separate matrix.
+hipError_t launch_lowrank_rows(const uint16_t* B, int64_t n, int r, uint16_t* out, hipStream_t stream);
 
 // out = RN_bf16([act | split] F^T) over an expanded operand F [nout, kcp + kx].
 // The kernel addresses each operand with 32-bit byte offsets: every operand
@@ -97,6 +107,23 @@ size_t gemm_bf16_ws_bytes(int64_t M, int64_t kc, int kx, int64_t nout);
 hipError_t launch_gemm_bf16(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                             const uint16_t* f, int64_t nout, uint16_t* out, float* part, hipStream_t stream,
                             const uint8_t* mask = nullptr, float keep_scale = 1.0f, bool f16 = false);
+
+// The same GEMM with the weight operand and the low-rank operand as separate
+// row-major matrices: f [nout, ldf] (the base contraction in its first kc
+// columns; kc % 64 == 0 or the columns up to the next multiple of 64 zero)
+// and fx [nout, ldx] (kx low-rank columns). A bf16 base weight W [n, k] is
+// such an f for the forward as it is stored.
+// nn: f is stored [contraction][output] instead ([kc rows, ldf], kc % 64 == 0,
+// and fx [kx rows, ldx]): dX over a bf16 base weight W [n, k] as stored, the
+// fragments read through the transposing LDS read (bf16, no mask).
+hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
+                                const uint16_t* f, int64_t ldf, const uint16_t* fx, int64_t ldx, int64_t nout,
+                                uint16_t* out, float* part, hipStream_t stream, const uint8_t* mask = nullptr,
+                                float keep_scale = 1.0f, bool f16 = false, bool nn = false);
+
+// [lora_extra_cols(r), k] rows [A ; A ; 0] (bf16), the low-rank operand of the
+// nn GEMM (dX over a bf16 base).
+hipError_t launch_lowrank_cols(const uint16_t* A, int r, int64_t k, uint16_t* out, hipStream_t stream);
 
 // Adapter merge: out = round(W' + scale * B A) (w != NULL; bf16, or fp32 if
 // out_f32) or unmerge: out = RN_bf16(Wm - scale * B A) (w == NULL, Wm bf16).
@@ -118,6 +145,14 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const void* X, int64_t M
                              int r, float scale, const uint8_t* mask, float keep_scale, void* Y, float* T_save,
                              void* ws, size_t ws_bytes, void* stream, bool f16 = false);
 size_t linear_fwd_ws_bytes(int64_t M, int64_t n, int64_t k, int r, bool have_tsave);
+
+// Small-M dX through the frozen base (M <= 16): dX = RN_bf16(dY W' + scale
+// (U A) [. mask * keep]) with U = dY B fp32 [M, r] (nullable when r == 0)
+// and A bf16 [r, k]; ws: gemv_dx_ws_bytes(n, k) bytes of fp32 partials.
+size_t gemv_dx_ws_bytes(int64_t n, int64_t k);
+hipError_t launch_gemv_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const float* U, const uint16_t* A, int r,
+                          float scale, uint16_t* dX, void* ws, hipStream_t stream, const uint8_t* mask = nullptr,
+                          float keep = 1.0f);
 
 hipError_t launch_silu_fwd(const uint16_t* G, const uint16_t* U, uint16_t* H, int64_t count,
                            hipStream_t stream);

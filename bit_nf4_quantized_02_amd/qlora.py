@@ -60,6 +60,10 @@ _SIGS = {
     "qlora_linear_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
     "qlora_linear_bwd": (_int, [_W, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
     "qlora_linear_fwd_scratch": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp]),
+    "qlora_lora_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
+    "qlora_lora_linear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
+    "qlora_lora_linear_bwd": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _int,
+                                      _vp, _sz, _vp]),
     "qlora_dequant_f16": (_int, [_W, _vp, _vp]),
     "qlora_linear_f16_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int]),
     "qlora_linear_fwd_f16": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -75,6 +79,8 @@ _SIGS = {
     "qlora_nf4_gemm_dx": (_int, [_W, _vp, _i64, _vp, _vp, _int, _vp, _vp]),
     "qlora_nf4_gemv_fwd": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _sz, _vp]),
     "qlora_nf4_gemv_workspace_bytes": (_sz, [_i64]),
+    "qlora_nf4_gemv_dx_workspace_bytes": (_sz, [_i64, _i64]),
+    "qlora_nf4_gemv_dx": (_int, [_W, _vp, _i64, _vp, _vp, _int, _f, _vp, _vp, _sz, _vp]),
     "qlora_linear_path": (_int, [_i64, _i64, _i64, _int, _int]),
     "qlora_nf4_expand_bytes": (_sz, [_i64, _i64, _int, _int]),
     "qlora_nf4_expand": (_int, [_W, _vp, _int, _int, _vp, _sz, _vp]),
@@ -402,6 +408,68 @@ def linear_bwd(w: NF4Weight, X: torch.Tensor | None, T: torch.Tensor | None, dY:
     return dX, dA, dB
 
 
+# --------------------------------------------------------------------------- bf16-base LoRA layer
+
+def lora_linear_workspace_bytes(M: int, n: int, k: int, r: int, is_bwd: bool) -> int:
+    return int(_lib.qlora_lora_linear_workspace_bytes(M, n, k, r, int(bool(is_bwd))))
+
+
+def lora_linear_fwd(W: torch.Tensor, X: torch.Tensor, A: torch.Tensor | None, B: torch.Tensor | None, scale: float,
+                    Y: torch.Tensor | None = None, T: torch.Tensor | None = None, save_T: bool = True,
+                    ws: torch.Tensor | None = None, stream=None):
+    """Y = X W^T + scale (X A^T) B^T over a bf16 base W [n, k]
+    (qlora_lora_linear_fwd).  Returns (Y, T)."""
+    n, k = W.shape
+    M = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _need(W, torch.bfloat16, (n, k), "W")
+    _need(X, torch.bfloat16, (M, k), "X")
+    if r:
+        _need(A, torch.bfloat16, (r, k), "A")
+        _need(B, torch.bfloat16, (n, r), "B")
+    if Y is None:
+        Y = torch.empty((M, n), dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, (M, n), "Y")
+    if T is None and save_T and r:
+        T = torch.empty((M, r), dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = _bytes(lora_linear_workspace_bytes(M, n, k, r, False), X.device)
+    _check(_lib.qlora_lora_linear_fwd(_ptr(W), n, k, _ptr(X), M, _ptr(A), _ptr(B), r, float(scale), _ptr(Y), _ptr(T),
+                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "qlora_lora_linear_fwd")
+    return Y, T
+
+
+def lora_linear_bwd(W: torch.Tensor, X: torch.Tensor | None, T: torch.Tensor | None, dY: torch.Tensor,
+                    A: torch.Tensor | None, B: torch.Tensor | None, scale: float, need_dX: bool = True,
+                    need_dA: bool = True, need_dB: bool = True, accumulate: bool = False,
+                    ws: torch.Tensor | None = None, stream=None):
+    """The gradients of lora_linear_fwd (qlora_lora_linear_bwd).  Returns (dX, dA, dB)."""
+    n, k = W.shape
+    M = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dev = dY.device
+    _need(W, torch.bfloat16, (n, k), "W")
+    _need(dY, torch.bfloat16, (M, n), "dY")
+    if X is not None:
+        _need(X, torch.bfloat16, (M, k), "X")
+    if r:
+        _need(A, torch.bfloat16, (r, k), "A")
+        _need(B, torch.bfloat16, (n, r), "B")
+    if T is not None:
+        _need(T, torch.float32, (M, r), "T")
+    dX = torch.empty((M, k), dtype=torch.bfloat16, device=dev) if need_dX else None
+    mk = torch.zeros if accumulate else torch.empty
+    dA = mk((r, k), dtype=torch.float32, device=dev) if (r and need_dA) else None
+    dB = mk((n, r), dtype=torch.float32, device=dev) if (r and need_dB) else None
+    if ws is None:
+        ws = _bytes(lora_linear_workspace_bytes(M, n, k, r, True), dev)
+    _check(_lib.qlora_lora_linear_bwd(_ptr(W), n, k, _ptr(X), _ptr(T), _ptr(dY), M, _ptr(A), _ptr(B), r, float(scale),
+                                      _ptr(dX), _ptr(dA), _ptr(dB), int(bool(accumulate)), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream)), "qlora_lora_linear_bwd")
+    return dX, dA, dB
+
+
 # --------------------------------------------------------------------------- building blocks
 
 def lowrank_split_cols(r: int) -> int:
@@ -517,6 +585,25 @@ def nf4_gemv_fwd(w: NF4Weight, X: torch.Tensor, T: torch.Tensor | None, B: torch
     _check(_lib.qlora_nf4_gemv_fwd(ctypes.byref(st), _ptr(X), M, _ptr(T), _ptr(B), r, float(scale), _ptr(Y),
                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "qlora_nf4_gemv_fwd")
     return Y
+
+
+def nf4_gemv_dx_workspace_bytes(n: int, k: int) -> int:
+    return int(_lib.qlora_nf4_gemv_dx_workspace_bytes(n, k))
+
+
+def nf4_gemv_dx(w: NF4Weight, dY: torch.Tensor, U: torch.Tensor | None, A: torch.Tensor | None, scale: float,
+                dX: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """dX = dY W' + scale U A for M <= 16 (qlora_nf4_gemv_dx); U = dY B fp32."""
+    M = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if dX is None:
+        dX = torch.empty((M, w.k), dtype=torch.bfloat16, device=dY.device)
+    if ws is None:
+        ws = _bytes(nf4_gemv_dx_workspace_bytes(w.n, w.k), dY.device)
+    st = w.struct()
+    _check(_lib.qlora_nf4_gemv_dx(ctypes.byref(st), _ptr(dY), M, _ptr(U), _ptr(A), r, float(scale), _ptr(dX),
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "qlora_nf4_gemv_dx")
+    return dX
 
 
 def lowrank_grad(P: torch.Tensor, Q: torch.Tensor, scale: float, g_layout: int, G: torch.Tensor | None = None,

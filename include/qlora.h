@@ -373,11 +373,30 @@ qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight *w, const void *X, int64_
                                 const void *B, int r, float scale, void *Y, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* Workspace bytes of qlora_nf4_gemv_dx for an [n, k] weight (0 on bad
+ * arguments): fp32 partial sums of the contraction's row ranges. */
+size_t qlora_nf4_gemv_dx_workspace_bytes(int64_t n, int64_t k);
+
+/*
+ * Bandwidth-oriented dX for M <= 16 tokens [WQ "Key Characteristics";
+ * QQ "Batched 4-bit matmuls"]:
+ *   dX = RN_bf16( dY W' + scale U A ),   U (device, [M, r] fp32) = dY B.
+ * dY (device) [M, n] bf16, A (device) [r, k] bf16, dX (device) [M, k] bf16.
+ * One pass over the packed codes: row ranges of the contraction each write
+ * fp32 partials (ws, qlora_nf4_gemv_dx_workspace_bytes(n, k) bytes), added in
+ * range order with the low-rank term (fp32) and rounded once.
+ * Errors: INVALID_ARG, SHAPE (M > 16), WORKSPACE, HIP.
+ */
+qlora_status qlora_nf4_gemv_dx(const qlora_nf4_weight *w, const void *dY, int64_t M, const float *U,
+                               const void *A, int r, float scale, void *dX, void *ws, size_t ws_bytes,
+                               void *stream);
+
 /*
  * Which kernels a pass uses at this size; qlora_linear_fwd (is_bwd = 0) and
  * qlora_linear_bwd (is_bwd = 1, the dX product) make exactly this choice:
- *   QLORA_PATH_GEMV      M <= 16, forward: qlora_nf4_gemv_fwd (one pass over
- *                        the packed codes, bandwidth-bound);
+ *   QLORA_PATH_GEMV      M <= 16: qlora_nf4_gemv_fwd, or for dX
+ *                        qlora_nf4_gemv_dx (one pass over the packed codes,
+ *                        bandwidth-bound);
  *   QLORA_PATH_FUSED     qlora_nf4_gemm_fwd / qlora_nf4_gemm_dx (each 64-block
  *                        expanded in on-chip memory, once per 256-row tile);
  *   QLORA_PATH_EXPANDED  M >= QLORA_EXPAND_MIN_M (and n % 8 == 0 for dX, and
@@ -451,6 +470,32 @@ size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r);
  */
 qlora_status qlora_lowrank_grad(const void *P, int64_t M, int64_t C, const float *Q, int r, float scale, float *G,
                                 int g_layout, int accumulate, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The same layer over a bf16 base weight (LoRA without quantization): the
+ * comparison the pages draw for QLoRA's speed ("QLoRA Explained ..."
+ * (gamut.so), "QLoRA vs LoRA: Memory, Speed, and Quality Tradeoffs": a 16-bit
+ * base trains faster, no dequantization overhead; QQ "Two prices to know",
+ * price 1: every QLoRA matmul pays for unpacking).
+ *   forward:  T = X A^T,  Y = RN_bf16( X W^T + scale * T B^T )
+ *   backward: U = dY B,  dX = RN_bf16( dY W + scale * U A ),
+ *             dA = scale * U^T X,  dB = scale * dY^T T
+ * W (device) [n, k] bf16 row-major, k % 64 == 0; every other argument, the
+ * nullable outputs, accumulate and the workspace rules as in
+ * qlora_linear_fwd / qlora_linear_bwd, workspace sizes from
+ * qlora_lora_linear_workspace_bytes (0 on bad arguments). The low-rank
+ * kernels are the QLoRA layer's; the forward multiplies W as stored, dX
+ * copies W's tiles where the QLoRA layer expands 4-bit ones.
+ * Errors: INVALID_ARG, SHAPE (also when k % 64 != 0), WORKSPACE, HIP.
+ */
+size_t qlora_lora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r, int is_bwd);
+qlora_status qlora_lora_linear_fwd(const void *W, int64_t n, int64_t k, const void *X, int64_t M,
+                                   const void *A, const void *B, int r, float scale, void *Y,
+                                   float *T_save, void *ws, size_t ws_bytes, void *stream);
+qlora_status qlora_lora_linear_bwd(const void *W, int64_t n, int64_t k, const void *X,
+                                   const float *T_saved, const void *dY, int64_t M, const void *A,
+                                   const void *B, int r, float scale, void *dX, float *dA, float *dB,
+                                   int accumulate, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * The gated-MLP join used between the gate/up and down linears of the MLP

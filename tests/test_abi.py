@@ -170,7 +170,8 @@ def test_path_choice_and_expanded_sizes(q):
     assert q.linear_path(17, 4096, 4096, 16, False) == q.PATH_FUSED
     assert q.linear_path(127, 4096, 4096, 16, False) == q.PATH_FUSED
     assert q.linear_path(128, 4096, 4096, 16, False) == q.PATH_EXPANDED
-    assert q.linear_path(16, 4096, 4096, 16, True) == q.PATH_FUSED
+    assert q.linear_path(16, 4096, 4096, 16, True) == q.PATH_GEMV   # dX through the GEMV for M <= 16
+    assert q.linear_path(17, 4096, 4096, 16, True) == q.PATH_FUSED
     big = 4096
     assert q.linear_path(big, 4096, 4096, 16, False) == q.PATH_EXPANDED
     assert q.linear_path(big, 4096, 4096, 16, True) == q.PATH_EXPANDED
@@ -327,3 +328,19 @@ def test_scratch_forward_refuses_oversize_before_any_call(q):
     assert lib.qlora_linear_fwd_scratch(None, p, 4, p, p, 8, 1.0, p, None, None) == -1
     assert lib.qlora_linear_fwd_scratch(ctypes.byref(w), p, 4, p, p, 200, 1.0, p, None, None) == -2
 
+
+def test_bf16_base_layer_argument_errors(q):
+    """The bf16-base LoRA layer rejects k % 64 != 0 and bad ranks as SHAPE
+    and NULL or misaligned pointers as INVALID_ARG, before any launch; M = 0
+    with accumulate launches nothing."""
+    lib = q.raw()
+    p = ctypes.c_void_p(1 << 24)
+    bad = ctypes.c_void_p((1 << 24) + 8)
+    assert lib.qlora_lora_linear_fwd(p, 64, 100, p, 4, p, p, 8, 1.0, p, None, p, 1 << 20, None) == -2
+    assert lib.qlora_lora_linear_fwd(p, 64, 128, p, 4, p, p, 200, 1.0, p, None, p, 1 << 20, None) == -2
+    assert lib.qlora_lora_linear_fwd(None, 64, 128, p, 4, p, p, 8, 1.0, p, None, p, 1 << 20, None) == -1
+    assert lib.qlora_lora_linear_fwd(bad, 64, 128, p, 4, p, p, 8, 1.0, p, None, p, 1 << 20, None) == -1
+    assert lib.qlora_lora_linear_fwd(p, 64, 128, p, 4, p, p, 8, 1.0, p, None, p, 0, None) == -4
+    assert lib.qlora_lora_linear_bwd(p, 64, 128, p, None, p, 0, p, p, 8, 1.0, p, p, p, 1, None, 0, None) == 0
+    assert lib.qlora_lora_linear_workspace_bytes(4, 64, 100, 8, 0) == 0
+    assert lib.qlora_lora_linear_workspace_bytes(4, 64, 128, 8, 1) > 0

@@ -163,3 +163,28 @@ def test_65b_last_layer_device_drawn(q, li):
     W_host = dev.W.cpu()
     assert_encode_equal(gw, oracle_encode(W_host))
     _check_linear(lin.name, W_host, X, dY, dev.A, dev.B, c.scale, Y, T, dX, dA, dB, _rows(M, 32, 53 + li))
+
+
+@pytest.mark.parametrize("li", [0, 1])
+def test_decode_weights_dx_through_the_gemv(q, li):
+    """dX through the 70B-class weights at M = 1 and 16 (the small-M dX
+    kernel, contraction split into row ranges): every output, with the
+    low-rank term."""
+    c = synth.CONFIGS[4]
+    lin = c.linears[li]
+    W = synth.weight_bf16(lin.n, lin.k, c.sigma, 4, li, synth.T_W)
+    gw = q.quantize_nf4(W.cuda())
+    Wd = oracle_encode(W).dequant().astype(np.float64)
+    for M in (1, 16):
+        say(f"case: decode dX {lin.name} {lin.n}x{lin.k} M={M} path={q.linear_path(M, lin.n, lin.k, c.r, True)}")
+        inp = synth.linear_inputs(4, 1, li, 1, lin.k, M, c.r, c.scale)  # X, A of this shape (W unused)
+        X, A = inp.X.cuda(), inp.A.cuda()
+        dY = synth.normal_bf16((M, lin.n), 1.0, 4, 16 + li, synth.T_DY).cuda()
+        B = synth.lora_B(lin.n, c.r, 4, li, synth.T_B).cuda()
+        dX, dA, dB = q.linear_bwd(gw, X, None, dY, A, B, c.scale)
+        torch.cuda.synchronize()
+        Xo, dYo, Ao, Bo = _host(X), _host(dY), _host(A), _host(B)
+        dXr, dAr, dBr, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, c.scale, dYo)
+        assert_dx(f"{lin.name} M={M} dX", dX, dYo, Wd, Ao, Bo, c.scale, dXr)
+        assert_grad(f"{lin.name} M={M} dA", dA, dAr)
+        assert_grad(f"{lin.name} M={M} dB", dB, dBr)
