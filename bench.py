@@ -52,6 +52,7 @@ error is above 2e-3. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -82,6 +83,12 @@ def parse():
     p.add_argument("--path", choices=["auto", "fused", "expanded"], default="auto",
                    help="large-M kernels: the library's choice (auto) or one forced, for comparison")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-side", action="store_true",
+                   help="only the step regions (for counter and trace runs): no step distribution, attainable-peak "
+                        "probes, merge, AdamW, encode, format, dropout, fp16 or bf16-base regions")
+    p.add_argument("--layers", type=int, default=None,
+                   help="layers of the 65B-class stack (default 80, the whole stack; fewer only for per-dispatch "
+                        "counter runs, which measure one launch of each shape; the line then names the count)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     p.add_argument("--json", default=None, help="also write the JSON line to this file")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -267,9 +274,14 @@ class LinearPlan:
 # ----------------------------------------------------------------------------- workloads
 
 class Workload:
-    def __init__(self, cid: int, q, force_path=None):
+    def __init__(self, cid: int, q, force_path=None, layers=None):
         self.cid = cid
         self.c = synth.CONFIGS[cid]
+        if layers is not None and layers != self.c.layers:
+            if cid != 5 or not 1 <= layers <= self.c.layers:
+                raise SystemExit(f"--layers applies to config 5 only, 1..{self.c.layers}")
+            self.c = dataclasses.replace(self.c, layers=layers,
+                                         title=self.c.title.replace(f"{self.c.layers} layers", f"{layers} layers"))
         self.tag = {1: "proj_1024_m16", 2: "attn_proj_4096_m4096", 3: "mlp_7b_m2048", 4: "decode_70b",
                     5: "stack_65b_m4096"}[cid]
         c = self.c
@@ -393,7 +405,7 @@ class Workload:
         self.passes_bytes = 2 * sum(p.packed_bytes for p in self.plans)
         self.desc = dict(workload=c.title, M=M, layers=c.layers, r=c.r, alpha=c.alpha,
                          packed_GB=round(sum(p.packed_bytes for p in self.plans) / 1e9, 2),
-                         passes="fwd through all 80 layers, then bwd in reverse; MLP chained through SiLU "
+                         passes=f"fwd through all {c.layers} layers, then bwd in reverse; MLP chained through SiLU "
                                 "within a layer; one synthetic X and dY shared by the layers")
 
     def dominant_kernels(self):
@@ -883,23 +895,28 @@ def main():
     from bit_nf4_quantized_02_amd import qlora as q
     log(f"bench: building workload config {args.config}")
     force = {"auto": None, "fused": q.PATH_FUSED, "expanded": q.PATH_EXPANDED}[args.path]
-    wl = Workload(args.config, q, force_path=force)
+    wl = Workload(args.config, q, force_path=force, layers=args.layers)
     names_of = {q.PATH_GEMV: "gemv", q.PATH_FUSED: "fused", q.PATH_EXPANDED: "expanded"}
     wl.desc["kernels"] = sorted({f"fwd:{names_of[p.path_fwd]}" for p in wl.plans}
                                 | {f"bwd:{names_of[p.path_bwd]}" for p in wl.plans if p.bwd})
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps after {args.warmup} warmup")
     ms_wall, ms_ev, per_ms, ms_pieces, snap, aux = time_steps(wl, args.steps, args.warmup)
-    log(f"bench: side regions with {aux} steps each")
-    p10, p50, p90, fwd_us, bwd_us = step_distribution(wl, aux)
-    att = attainable(q)
-    merges = merge_rows(wl, q) if args.config in (1, 2, 3, 5) else {}
-    lora_ms = lora_bf16_base(wl, q, aux)
-    adamw = adamw_rows(wl, q)
-    encode = encode_rows(wl, q)
-    variants = variant_rows(wl, q)
-    drop = dropout_step(wl, q, aux)
-    f16 = f16_step(wl, q, aux)
+    if args.no_side:
+        p10 = p50 = p90 = fwd_us = bwd_us = float("nan")
+        att = {"mfma_bf16_tflops": float("nan"), "hbm_read_gbps": float("nan")}
+        merges, lora_ms, adamw, encode, variants, drop, f16 = {}, None, {}, {}, {}, None, None
+    else:
+        log(f"bench: side regions with {aux} steps each")
+        p10, p50, p90, fwd_us, bwd_us = step_distribution(wl, aux)
+        att = attainable(q)
+        merges = merge_rows(wl, q) if args.config in (1, 2, 3, 5) else {}
+        lora_ms = lora_bf16_base(wl, q, aux)
+        adamw = adamw_rows(wl, q)
+        encode = encode_rows(wl, q)
+        variants = variant_rows(wl, q)
+        drop = dropout_step(wl, q, aux)
+        f16 = f16_step(wl, q, aux)
     for row in merges.values():
         row["frac"] = round(row["GBps"] / PEAK_HBM_GBPS, 4)
         row["frac_of_attainable"] = round(row["GBps"] / att["hbm_read_gbps"], 4)
