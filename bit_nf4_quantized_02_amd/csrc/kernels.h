@@ -59,7 +59,6 @@ hipError_t launch_rowdot(const uint16_t* P, int64_t M, int64_t C, const uint16_t
 // Column reduction over M in fixed order, for the adapter gradients:
 //   G[c, j] (+)= scale * sum_m P[m, c] * Q[m, j]    P bf16 [M, C], Q fp32 [M, r]
 // written at G[c * g_sc + j * g_sj]. partial (fp32, [splits, C, r]) is workspace.
-int coldot_splits(int64_t M);
 size_t coldot_ws_bytes(int64_t M, int64_t C, int r);
 hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale,
                          float* G, int64_t g_sc, int64_t g_sj, int accumulate, float* partial,

@@ -25,23 +25,23 @@ namespace qlora {
 
 namespace {
 
-constexpr int kMaxRank = 128;
-
 // G partial on the matrix cores: Gp[s][j][c] = sum_{m in split s} Q[m, j] P[m, c].
 // The contraction runs over the tokens m, which are the slow index of both
 // operands, so each 32-token step is staged in LDS in its stored orientation
-// -- P as [32][256 columns] bf16 (coalesced 16-byte loads), Q as [32][r] bf16
-// hi and lo halves of the fp32 value -- and both MFMA operands are gathered
-// with the transposing read ds_read_b64_tr_b16 (8 consecutive tokens of one
-// column per lane). v_mfma_f32_16x16x32_bf16: rows = j, columns = c; the hi
-// and lo halves of Q are multiplied separately, so the products carry ~16
-// significant bits of Q. Each wave owns 64 columns; a workgroup 256 columns
-// and one token split. The next step's P is loaded into registers while the
-// current step's MFMAs run.
-constexpr int kPPitch = 512 + 32;  // bytes per staged P row (256 bf16 + pad)
+// -- P as [32][4 kCW columns] bf16 (coalesced 16-byte loads), Q as [32][r]
+// bf16 hi and lo halves of the fp32 value -- and both MFMA operands are
+// gathered with the transposing read ds_read_b64_tr_b16 (8 consecutive tokens
+// of one column per lane). v_mfma_f32_16x16x32_bf16: rows = j, columns = c;
+// the hi and lo halves of Q are multiplied separately, so the products carry
+// ~16 significant bits of Q. Each of the 4 waves owns kCW columns (64 or 32);
+// a workgroup 4 kCW columns and one token split. The next steps' P and Q are
+// loaded into registers (a ring of kDepth stages) while the current step's
+// MFMAs run.
+constexpr int kColdotDepth64 = 1;  // register stages in flight at ranks 33..64 (more stages cost occupancy)
 
-template <int kRP>
+template <int kRP, int kCW>
 struct ColdotSmem {
+  static constexpr int kPPitch = 4 * kCW * 2 + 32;  // bytes per staged P row (+ pad)
   static constexpr int kQPitch = kRP * 2 + (kRP >= 32 ? 32 : 0);
   char p[32 * kPPitch];
   char qh[32 * kQPitch];
@@ -64,106 +64,118 @@ __device__ __forceinline__ bf16x8 tr_operand(const char* tile, int pitch, int c0
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// kCW: columns per wave (64 or 32). kVec: 16-byte P rows (C % 8 == 0); then
+// every load is issued from a clamped, in-range address (rows past the split
+// read its last row, columns past C the last 8) and the step that reaches
+// past either end zeroes those values before staging them.
 // kMask (16-byte P rows only): P's elements whose byte in pmask [M, C] is 0
 // read as zero (dropout on the adapter's input).
 // kF16: fp16 P and fp16 hi/lo halves of Q (the compute-type ablation).
-template <int kRP, bool kVec, bool kMask = false, bool kF16 = false>
-__global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
+template <int kRP, int kCW, bool kVec, bool kMask = false, bool kF16 = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void coldot_mfma_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
                                                           const float* __restrict__ Q, int r, int64_t mchunk,
                                                           float* __restrict__ partial,
                                                           const uint8_t* __restrict__ pmask = nullptr) {
 #pragma clang fp contract(off)
   constexpr int kJT = kRP / 16;
-  using Smem = ColdotSmem<kRP>;
+  constexpr int kCT = kCW / 16;              // 16-column tiles per wave
+  constexpr int kCPR = kCW / 2;              // 16-byte chunks per staged P row (4 kCW columns)
+  constexpr int kRPT = 256 / kCPR;           // P rows covered by one pass of the 256 threads
+  constexpr int kPL = 32 / kRPT;             // P chunks per thread per step
+  using Smem = ColdotSmem<kRP, kCW>;
+  constexpr int kPP = Smem::kPPitch;
   constexpr int kQP = Smem::kQPitch;
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
-  const int64_t cw = (int64_t)blockIdx.x * 256;
+  const int64_t cw = (int64_t)blockIdx.x * (4 * kCW);
   const int64_t s = blockIdx.y;
   const int64_t m0 = s * mchunk;
   const int64_t m1 = (m0 + mchunk < M) ? m0 + mchunk : M;
-  f32x4 acc[kJT][4];
+  f32x4 acc[kJT][kCT];
 #pragma unroll
   for (int a = 0; a < kJT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kCT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // P tile: 32 rows x 32 chunks of 16 B; thread t owns chunk t % 32 of rows
-  // t / 32 + 8 i (i = 0..3). Out-of-range rows / columns load zeros.
-  auto load_p = [&](int64_t mb, u32x4 (&v)[4], uint2 (&mk)[kMask ? 4 : 1]) {
+  // P tile: thread t owns chunk t % kCPR of rows t / kCPR + kRPT i (i < kPL).
+  const int pc = (t % kCPR) * 8;
+  const int pr = t / kCPR;
+  const int64_t cp = cw + pc;
+  const int64_t cpl = cp < C ? cp : C - 8;  // kVec: clamped column
+  constexpr int kQE = 32 * kRP / 256;       // Q elements of one step per thread: t + 256 e
+  struct Stage {
+    u32x4 p[kPL];
+    uint2 mk[kMask ? kPL : 1];
+    float q[kQE];
+  };
+  auto load = [&](int64_t mb, Stage& st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = mb + (t >> 5) + 8 * i;
-      const int64_t c = cw + (t & 31) * 8;
-      v[i] = u32x4{0u, 0u, 0u, 0u};
-      if constexpr (kMask) mk[i] = uint2{0u, 0u};
-      if (m < m1) {
-        if constexpr (kVec) {
-          if (c < C) {
-            v[i] = *reinterpret_cast<const u32x4*>(P + m * C + c);
-            if constexpr (kMask) mk[i] = *reinterpret_cast<const uint2*>(pmask + m * C + c);
-          }
-        } else {
+    for (int i = 0; i < kPL; ++i) {
+      const int64_t m = mb + pr + kRPT * i;
+      if constexpr (kVec) {
+        const int64_t ml = m < m1 ? m : m1 - 1;
+        st.p[i] = *reinterpret_cast<const u32x4*>(P + ml * C + cpl);
+        if constexpr (kMask) st.mk[i] = *reinterpret_cast<const uint2*>(pmask + ml * C + cpl);
+      } else {
+        st.p[i] = u32x4{0u, 0u, 0u, 0u};
+        if (m < m1) {
           uint32_t e[8];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) e[q] = (c + q < C) ? (uint32_t)P[m * C + c + q] : 0u;
+          for (int x = 0; x < 8; ++x) e[x] = (cp + x < C) ? (uint32_t)P[m * C + cp + x] : 0u;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[i][q] = e[2 * q] | (e[2 * q + 1] << 16);
+          for (int x = 0; x < 4; ++x) st.p[i][x] = e[2 * x] | (e[2 * x + 1] << 16);
         }
       }
     }
-  };
-  // Q of one step (32 tokens x kRP, fp32): thread t owns elements t + 256 e
-  constexpr int kQE = 32 * kRP / 256;
-  auto load_q = [&](int64_t mb, float (&qv)[kQE]) {
 #pragma unroll
     for (int e = 0; e < kQE; ++e) {
       const int idx = t + 256 * e;
       const int mm = idx / kRP, j = idx % kRP;
       const int64_t m = mb + mm;
-      qv[e] = (j < r && m < m1) ? Q[m * r + j] : 0.0f;
+      // rows past the split read its last row (zeroed below); columns j >= r
+      // read column r - 1: their products land in rows j >= r of the result,
+      // which are never stored
+      st.q[e] = Q[(m < m1 ? m : m1 - 1) * r + (j < r ? j : r - 1)];
     }
   };
-  // Several steps of P and Q in flight: a ring of register stages with
-  // compile-time indices (the loop is unrolled by the ring length), each
-  // refilled for the step kDepth ahead right after it has been staged into
-  // LDS. Four stages up to r = 32; one for larger ranks (register budget).
-  constexpr int kDepth = kRP <= 32 ? 4 : 1;
-  struct Stage {
-    u32x4 p[4];
-    uint2 mk[kMask ? 4 : 1];
-    float q[kQE];
-  };
-  auto step = [&](int64_t mb, Stage& stg) {
+  constexpr int kDepth = kRP <= 32 ? 4 : kRP <= 64 ? kColdotDepth64 : 1;
+  auto step = [&](int64_t mb, Stage& st) {
+    // the step that reaches past the split's last token or past C: zero those values
+    const bool tail = mb + 32 > m1 || (kVec && cw + 4 * kCW > C);
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < kPL; ++i)
+        if (mb + pr + kRPT * i >= m1 || cp >= C) st.p[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < kQE; ++e)
+        if (mb + (t + 256 * e) / kRP >= m1) st.q[e] = 0.0f;
+    }
     // stage this step: P from registers, Q converted to bf16 hi / lo
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(sm.p + ((t >> 5) + 8 * i) * kPPitch + (t & 31) * 16) =
-          kMask ? apply_mask8(stg.p[i], stg.mk[i]) : stg.p[i];
+    for (int i = 0; i < kPL; ++i)
+      *reinterpret_cast<u32x4*>(sm.p + (pr + kRPT * i) * kPP + pc * 2) =
+          kMask ? apply_mask8(st.p[i], st.mk[i]) : st.p[i];
 #pragma unroll
     for (int e = 0; e < kQE; ++e) {
       const int idx = t + 256 * e;
       const int mm = idx / kRP, j = idx % kRP;
-      const uint16_t qh = to16<kF16>(stg.q[e]);
-      const uint16_t ql = to16<kF16>(stg.q[e] - from16<kF16>(qh));
+      const uint16_t qh = to16<kF16>(st.q[e]);
+      const uint16_t ql = to16<kF16>(st.q[e] - from16<kF16>(qh));
       *reinterpret_cast<uint16_t*>(sm.qh + mm * kQP + j * 2) = qh;
       *reinterpret_cast<uint16_t*>(sm.ql + mm * kQP + j * 2) = ql;
     }
     __syncthreads();
-    if (mb + kDepth * 32 < m1) {
-      load_p(mb + kDepth * 32, stg.p, stg.mk);
-      load_q(mb + kDepth * 32, stg.q);
-    }
-    bf16x8 pb[4];
+    if (mb + kDepth * 32 < m1) load(mb + kDepth * 32, st);
+    bf16x8 pb[kCT];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) pb[ct] = tr_operand(sm.p, kPPitch, wave * 64 + ct * 16, lane);
+    for (int ct = 0; ct < kCT; ++ct) pb[ct] = tr_operand(sm.p, kPP, wave * kCW + ct * 16, lane);
 #pragma unroll
     for (int a = 0; a < kJT; ++a) {
       const bf16x8 ah = tr_operand(sm.qh, kQP, a * 16, lane);
       const bf16x8 al = tr_operand(sm.ql, kQP, a * 16, lane);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < kCT; ++ct) {
         acc[a][ct] = mfma16<kF16>(ah, pb[ct], acc[a][ct]);
         acc[a][ct] = mfma16<kF16>(al, pb[ct], acc[a][ct]);
       }
@@ -172,10 +184,10 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
   };
   if constexpr (kDepth == 4) {
     Stage s0, s1, s2, s3;
-    load_p(m0, s0.p, s0.mk); load_q(m0, s0.q);
-    load_p(m0 + 32, s1.p, s1.mk); load_q(m0 + 32, s1.q);
-    load_p(m0 + 64, s2.p, s2.mk); load_q(m0 + 64, s2.q);
-    load_p(m0 + 96, s3.p, s3.mk); load_q(m0 + 96, s3.q);
+    load(m0, s0);
+    if (m0 + 32 < m1) load(m0 + 32, s1);
+    if (m0 + 64 < m1) load(m0 + 64, s2);
+    if (m0 + 96 < m1) load(m0 + 96, s3);
     for (int64_t mb = m0; mb < m1; mb += 4 * 32) {
       step(mb, s0);
       if (mb + 32 >= m1) break;
@@ -185,17 +197,26 @@ __global__ __launch_bounds__(256) void coldot_mfma_kernel(const uint16_t* __rest
       if (mb + 96 >= m1) break;
       step(mb + 96, s3);
     }
+  } else if constexpr (kDepth == 2) {
+    Stage s0, s1;
+    load(m0, s0);
+    if (m0 + 32 < m1) load(m0 + 32, s1);
+    for (int64_t mb = m0; mb < m1; mb += 2 * 32) {
+      step(mb, s0);
+      if (mb + 32 >= m1) break;
+      step(mb + 32, s1);
+    }
   } else {
     Stage s0;
-    load_p(m0, s0.p, s0.mk); load_q(m0, s0.q);
+    load(m0, s0);
     for (int64_t mb = m0; mb < m1; mb += 32) step(mb, s0);
   }
   // D[j][c]: lane -> c = lane % 16, j = 4 (lane / 16) + v
 #pragma unroll
   for (int a = 0; a < kJT; ++a)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int64_t c = cw + wave * 64 + ct * 16 + (lane & 15);
+    for (int ct = 0; ct < kCT; ++ct) {
+      const int64_t c = cw + wave * kCW + ct * 16 + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = a * 16 + 4 * (lane >> 4) + v;
@@ -229,40 +250,51 @@ __global__ __launch_bounds__(256) void coldot_reduce_kernel(const float* __restr
 
 }  // namespace
 
-int coldot_splits(int64_t M) {
-  int64_t s = M / 256;
-  if (s > 32) s = 32;
-  if (s < 1) s = 1;
-  return (int)s;
+// Token splits: the fewest that give about 512 workgroups of 256 columns
+// (each split >= 128 tokens, at most 32 splits). Measured: half as many,
+// longer-running workgroups (or 128-column ones) were slower -- the kernel is
+// bound by the latency of its per-step barriers -- although they write fewer
+// partial sums.
+constexpr int kColdotCW = 64;  // columns per wave
+constexpr int64_t kColdotTargetWG = 512;
+
+int coldot_splits(int64_t M, int64_t C) {
+  int64_t s = cdiv(kColdotTargetWG, cdiv(C, (int64_t)(4 * kColdotCW)));
+  int64_t cap = M / 128;
+  if (cap > 32) cap = 32;
+  if (s > cap) s = cap;
+  return (int)(s < 1 ? 1 : s);
 }
 
 size_t coldot_ws_bytes(int64_t M, int64_t C, int r) {
-  return align256((size_t)coldot_splits(M) * (size_t)C * (size_t)r * 4);
+  return align256((size_t)coldot_splits(M, C) * (size_t)C * (size_t)r * 4);
 }
 
 hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale, float* G,
                          int64_t g_sc, int64_t g_sj, int accumulate, float* partial, hipStream_t stream,
                          const uint8_t* pmask, bool f16) {
-  const int ns = coldot_splits(M);
+  const int ns = coldot_splits(M, C);
   const int64_t mchunk = cdiv(cdiv(M, ns), 32) * 32;
-  const dim3 grid((unsigned)cdiv(C, 256), (unsigned)ns);
+  const dim3 grid((unsigned)cdiv(C, 4 * kColdotCW), (unsigned)ns);
   const bool vec = C % 8 == 0;
   if (pmask != nullptr && !vec) return hipErrorInvalidValue;
   if (pmask != nullptr && f16) return hipErrorInvalidValue;
-#define QLORA_COLDOT(RP)                                                                                    \
-  if (f16 && vec)                                                                                          \
-    coldot_mfma_kernel<RP, true, false, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);   \
-  else if (f16)                                                                                            \
-    coldot_mfma_kernel<RP, false, false, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);  \
-  else if (pmask != nullptr)                                                                               \
-    coldot_mfma_kernel<RP, true, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial, pmask);   \
-  else if (vec) coldot_mfma_kernel<RP, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);    \
-  else coldot_mfma_kernel<RP, false><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
+#define QLORA_COLDOT2(RP, CW)                                                                                   \
+  if (f16 && vec)                                                                                              \
+    coldot_mfma_kernel<RP, CW, true, false, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);   \
+  else if (f16)                                                                                                \
+    coldot_mfma_kernel<RP, CW, false, false, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);  \
+  else if (pmask != nullptr)                                                                                   \
+    coldot_mfma_kernel<RP, CW, true, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial, pmask);   \
+  else if (vec) coldot_mfma_kernel<RP, CW, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);    \
+  else coldot_mfma_kernel<RP, CW, false><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
+#define QLORA_COLDOT(RP) { QLORA_COLDOT2(RP, kColdotCW) }
   if (r <= 16) { QLORA_COLDOT(16) }
   else if (r <= 32) { QLORA_COLDOT(32) }
   else if (r <= 64) { QLORA_COLDOT(64) }
   else { QLORA_COLDOT(128) }
 #undef QLORA_COLDOT
+#undef QLORA_COLDOT2
   coldot_reduce_kernel<<<(unsigned)cdiv(C * r, 256), 256, 0, stream>>>(partial, C, r, ns, scale, G, g_sc, g_sj,
                                                                       accumulate);
   return hipGetLastError();

@@ -11,10 +11,13 @@
 // the 2r extra contraction columns through which the main GEMMs add the
 // low-rank term to their fp32 accumulator, so Y and dX are rounded once.
 //
-// Workgroup: one 16-row tile of P and a range of columns, NW waves splitting
-// the range into contiguous parts. Lanes read P in the MFMA operand layout
-// (8 consecutive bf16 per lane, 16-byte loads, kU column steps in flight).
-// Q as [r, C] is read the same way. Q as [C, r] (j contiguous) is staged per
+// Workgroup: kMR 16-row tiles of P and a range of columns, NW waves splitting
+// the range into contiguous parts; every wave multiplies all kMR row tiles,
+// so each Q fragment it loads serves kMR tiles (kMR = 4 at large M: Q, the
+// whole low-rank factor, is then read once per 64 rows instead of once per
+// 16, which at r = 64 was four times the bytes of P itself). Lanes read P in
+// the MFMA operand layout (8 consecutive bf16 per lane, 16-byte loads, kU
+// column steps in flight). Q as [r, C] is read the same way. Q as [C, r] (j contiguous) is staged per
 // wave in LDS as a [32 c][r] tile and read back with the transposing read
 // ds_read_b64_tr_b16, which hands each lane 4 consecutive c of its column j.
 // The waves' partial sums are added in a fixed order in LDS. With the whole
@@ -48,17 +51,29 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* __restrict__ row, int64_t
   return v;
 }
 
-template <int kRP>
-constexpr int rowdot_threads() { return (kRP <= 64 ? 8 : 4) * 64; }
+// Tall form (kMR > 1): waves per workgroup, workgroups aimed for, and the
+// fewest contraction columns per split.
+constexpr int kTallWaves = 8;
+constexpr int kTallMR = 4;
+constexpr int64_t kTallTargetWG = 256;
+constexpr int64_t kTallMinCols = 1024;
+constexpr int kTallDepth = 2;
+constexpr bool kTallInterleave = true;
 
-template <int kRP, int kQL>
+template <int kRP, int kMR>
+constexpr int rowdot_threads() { return (kMR > 1 ? kTallWaves : kRP <= 64 ? 8 : 4) * 64; }
+
+template <int kRP, int kQL, int kMR>
 struct RowdotCfg {
   static constexpr int kTiles = kRP / 16;
-  static constexpr int kU = kTiles >= 8 ? 1 : 8 / kTiles;           // column steps per load batch
-  static constexpr int kNW = rowdot_threads<kRP>() / 64;              // waves per workgroup
+  static constexpr int kRows = 16 * kMR;                             // rows of P per workgroup
+  static constexpr int kU = kMR > 1 ? (kTiles >= 2 ? 1 : 2)          // column steps per load batch
+                                    : (kTiles >= 8 ? 1 : 8 / kTiles);
+  static constexpr int kNW = rowdot_threads<kRP, kMR>() / 64;        // waves per workgroup
+  static constexpr int kDepth = kMR > 1 ? kTallDepth : 2;             // batches in the load ring
   static constexpr int kQPitch = kRP * 2 + (kRP >= 32 ? 32 : 0);     // bytes per staged Q row
   static constexpr int kStage = kU * 32 * kQPitch;                   // staged Q bytes per wave
-  static constexpr int kRed = kNW * 16 * kRP * 4;                    // partial sums of the waves
+  static constexpr int kRed = kNW * kRows * kRP * 4;                 // partial sums of the waves
   static constexpr int kSmem = (kQL == 1 && kNW * kStage > kRed) ? kNW * kStage : kRed;
 };
 
@@ -67,66 +82,106 @@ struct RowdotCfg {
 // kMask (Q = A only): P's elements whose byte in pmask [M, C] is 0 read as zero
 // (dropout on the adapter's input).
 // kF16: fp16 operands and split (the compute-type ablation), else bf16.
-template <int kRP, int kQL, bool kVecP, bool kVecQ, bool kDirect, bool kMask = false, bool kF16 = false>
-__global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
+// kMR: 16-row tiles per workgroup, all multiplied by every wave.
+template <int kRP, int kQL, bool kVecP, bool kVecQ, bool kDirect, bool kMask = false, bool kF16 = false, int kMR = 1>
+__global__ __launch_bounds__((rowdot_threads<kRP, kMR>())) __attribute__((amdgpu_waves_per_eu(kMR > 1 ? 2 : 1))) void rowdot_kernel(
     const uint16_t* __restrict__ P, int64_t M, int64_t C, const uint16_t* __restrict__ Q, int r, int64_t cchunk,
     float* __restrict__ out, uint16_t* __restrict__ split, int xc, float scale, float* __restrict__ part,
     const uint8_t* __restrict__ pmask = nullptr) {
 #pragma clang fp contract(off)
-  using Cfg = RowdotCfg<kRP, kQL>;
-  constexpr int kTiles = Cfg::kTiles, kU = Cfg::kU, kNW = Cfg::kNW;
+  using Cfg = RowdotCfg<kRP, kQL, kMR>;
+  constexpr int kTiles = Cfg::kTiles, kU = Cfg::kU, kNW = Cfg::kNW, kRows = Cfg::kRows;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::kSmem];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  // wave-uniform (scalar) so that the column range and loop tests are too
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t m0 = (int64_t)blockIdx.x * kRows;
   const int64_t cs = blockIdx.y;
   const int64_t cbeg = cs * cchunk;
   const int64_t cend = (cbeg + cchunk < C) ? cbeg + cchunk : C;
+  // Columns of this wave: a contiguous part of the range, or (kIL) every
+  // kNW-th column step, so that the waves of a workgroup read adjacent
+  // pieces of the same rows at the same time.
+  constexpr bool kIL = kMR > 1 && kTallInterleave;
+  constexpr int64_t kStep = 32 * kU;
   const int64_t qlen = cdiv(cend - cbeg, (int64_t)kNW * 32) * 32;  // per-wave length, multiple of 32
-  const int64_t w0 = cbeg + wave * qlen;
-  const int64_t w1 = (w0 + qlen < cend) ? w0 + qlen : cend;
+  const int64_t w0 = kIL ? cbeg + wave * kStep : cbeg + wave * qlen;
+  const int64_t w1 = kIL ? cend : (w0 + qlen < cend) ? w0 + qlen : cend;
+  const int64_t cstride = kIL ? kNW * kStep : kStep;
 
   const int row = lane & 15;
   const int ko = (lane >> 4) * 8;
-  const int64_t m = m0 + row;
-  const uint16_t* prow = P + (m < M ? m : M - 1) * C;
-  const uint8_t* mrow = kMask ? pmask + (m < M ? m : M - 1) * C : nullptr;
+  const uint16_t* prow[kMR];
+  const uint8_t* mrow[kMR];
+  bool mok[kMR];
+#pragma unroll
+  for (int i = 0; i < kMR; ++i) {
+    const int64_t m = m0 + 16 * i + row;
+    mok[i] = m < M;
+    prow[i] = P + (m < M ? m : M - 1) * C;
+    mrow[i] = kMask ? pmask + (m < M ? m : M - 1) * C : nullptr;
+  }
   char* const stage = smem + wave * Cfg::kStage;
 
-  f32x4 acc[kTiles];
+  f32x4 acc[kMR][kTiles];
 #pragma unroll
-  for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kMR; ++i)
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One batch = kU column steps of 32: the P operand and the raw Q values.
+  // One batch = kU column steps of 32: the P operands and the raw Q values.
   // Two batches rotate (the loop is unrolled by two), so the next batch's
   // loads are in flight while the current one is multiplied.
   constexpr int kChunks = 32 * kRP / 8;  // 16-byte chunks of one staged [32][kRP] Q tile
   constexpr int kQL1 = kQL == 1 ? kU * (kChunks / 64) : 1;
   struct Batch {
-    u32x4 a[kU];
-    uint2 mk[kMask ? kU : 1];
+    u32x4 a[kU][kMR];
+    uint2 mk[kMask ? kU : 1][kMask ? kMR : 1];
     u32x4 q0[kQL == 0 ? kU * kTiles : 1];  // Q = [r, C]: operand layout
     u32x4 q1[kQL1];                        // Q = [C, r]: raw chunks for the LDS tile
+    int64_t c0;                            // first column of the batch
   };
+  // 16-byte rows (kFast): every load is issued unconditionally from a
+  // clamped, in-range address -- rows past M read row M - 1 and Q rows past r
+  // read row r - 1 (their results are never stored), columns past w1 read the
+  // last in-range group and are zeroed before the multiply, in the tail batch
+  // only -- so no load sits behind a branch that waits for it, and the next
+  // batch stays in flight while this one is multiplied.
+  constexpr bool kFast = kVecP && kVecQ && kMR > 1;
   auto load = [&](int64_t c, Batch& bt) {
+    bt.c0 = c;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      bt.a[u] = load8<kVecP>(prow, c + 32 * u + ko, w1);
-      if (m >= M) bt.a[u] = u32x4{0u, 0u, 0u, 0u};
-      if constexpr (kMask) {
-        const int64_t e0 = c + 32 * u + ko;
-        bt.mk[u] = e0 < w1 ? *reinterpret_cast<const uint2*>(mrow + e0) : uint2{0u, 0u};
+      const int64_t e0 = c + 32 * u + ko;
+      const int64_t ec = e0 < w1 ? e0 : w1 - 8;
+#pragma unroll
+      for (int i = 0; i < kMR; ++i) {
+        if constexpr (kFast) {
+          bt.a[u][i] = *reinterpret_cast<const u32x4*>(prow[i] + ec);
+          if constexpr (kMask) bt.mk[u][i] = *reinterpret_cast<const uint2*>(mrow[i] + ec);
+        } else {
+          bt.a[u][i] = load8<kVecP>(prow[i], e0, w1);
+          if (!mok[i]) bt.a[u][i] = u32x4{0u, 0u, 0u, 0u};
+          if constexpr (kMask) bt.mk[u][i] = e0 < w1 ? *reinterpret_cast<const uint2*>(mrow[i] + e0) : uint2{0u, 0u};
+        }
       }
     }
     if constexpr (kQL == 0) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
+      for (int u = 0; u < kU; ++u) {
+        const int64_t e0 = c + 32 * u + ko;
+        const int64_t ec = e0 < w1 ? e0 : w1 - 8;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
           const int j = t * 16 + row;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (j < r) v = load8<kVecQ>(Q + (int64_t)j * C, c + 32 * u + ko, w1);
-          bt.q0[u * kTiles + t] = v;
+          if constexpr (kFast) {
+            bt.q0[u * kTiles + t] = *reinterpret_cast<const u32x4*>(Q + (int64_t)(j < r ? j : r - 1) * C + ec);
+          } else {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (j < r) v = load8<kVecQ>(Q + (int64_t)j * C, e0, w1);
+            bt.q0[u * kTiles + t] = v;
+          }
         }
+      }
     } else {
       // Q[c + 32 u + cc][jc .. jc + 7] for chunk q = lane + 64 i (zeros past w1 / r)
 #pragma unroll
@@ -137,7 +192,9 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
           const int cc = q / (kRP / 8), jc = (q % (kRP / 8)) * 8;
           const int64_t cq = c + 32 * u + cc;
           u32x4 v = {0u, 0u, 0u, 0u};
-          if (cq < w1) {
+          if constexpr (kFast) {
+            v = *reinterpret_cast<const u32x4*>(Q + (cq < w1 ? cq : w1 - 1) * r + (jc < r ? jc : r - 8));
+          } else if (cq < w1) {
             if constexpr (kVecQ) {
               if (jc < r) v = *reinterpret_cast<const u32x4*>(Q + cq * r + jc);
             } else {
@@ -152,7 +209,32 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
         }
     }
   };
-  auto compute = [&](const Batch& bt) {
+  // the tail batch of the fast path: zero what lies past w1 (wave-uniform test)
+  auto clip = [&](Batch& bt) {
+    if (bt.c0 + kStep <= w1) return;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool ok = bt.c0 + 32 * u + ko < w1;
+#pragma unroll
+      for (int i = 0; i < kMR; ++i) {
+        if (!ok) bt.a[u][i] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (kMask) if (!ok) bt.mk[u][i] = uint2{0u, 0u};
+      }
+      if constexpr (kQL == 0) {
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t)
+          if (!ok) bt.q0[u * kTiles + t] = u32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int i = 0; i < kChunks / 64; ++i) {
+          const int cc = (lane + 64 * i) / (kRP / 8);
+          if (bt.c0 + 32 * u + cc >= w1) bt.q1[u * (kChunks / 64) + i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+  auto compute = [&](Batch& bt) {
+    if constexpr (kFast) clip(bt);
     bf16x8 b[kU][kTiles];
     if constexpr (kQL == 0) {
 #pragma unroll
@@ -183,42 +265,50 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t)
-        acc[t] = mfma16<kF16>(__builtin_bit_cast(bf16x8, kMask ? apply_mask8(bt.a[u], bt.mk[u]) : bt.a[u]), b[u][t],
-                              acc[t]);
+      for (int i = 0; i < kMR; ++i) {
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, kMask ? apply_mask8(bt.a[u][i], bt.mk[u][i]) : bt.a[u][i]);
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) acc[i][t] = mfma16<kF16>(pa, b[u][t], acc[i][t]);
+      }
   };
-  constexpr int64_t kStep = 32 * kU;
   if constexpr (!kVecP || !kVecQ) {
     // element-wise loads hold several registers per value: no second batch
-    for (int64_t c = w0; c < w1; c += kStep) {
+    for (int64_t c = w0; c < w1; c += cstride) {
       Batch b0;
       load(c, b0);
       compute(b0);
     }
   } else if (w0 < w1) {
-    Batch b0, b1;
-    load(w0, b0);
-    for (int64_t c = w0; c < w1; c += 2 * kStep) {
-      load(c + kStep, b1);  // past w1 the loads read nothing (zeros)
-      __builtin_amdgcn_sched_barrier(0);
-      compute(b0);
-      if (c + kStep >= w1) break;
-      load(c + 2 * kStep, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(b1);
+    // a ring of kD batches: the loads of batch j + kD - 1 are issued before
+    // batch j is multiplied (past w1 the loads read nothing: zeros)
+    constexpr int kD = Cfg::kDepth;
+    Batch bt[kD];
+#pragma unroll
+    for (int i = 0; i < kD - 1; ++i) load(w0 + i * cstride, bt[i]);
+    for (int64_t c = w0; c < w1; c += kD * cstride) {
+#pragma unroll
+      for (int j = 0; j < kD; ++j) {
+        load(c + (j + kD - 1) * cstride, bt[(j + kD - 1) % kD]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(bt[j]);
+        if (c + (j + 1) * cstride >= w1) break;
+      }
     }
   }
   __syncthreads();  // all staged-Q reads done before the region is reused
-  // D layout: lane -> column (lane & 15), rows 4 (lane >> 4) + v
+  // D layout: lane -> column (lane & 15), rows 4 (lane >> 4) + v of tile i
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int t = 0; t < kTiles; ++t)
+  for (int i = 0; i < kMR; ++i)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * (lane >> 4) + v) * kRP + t * 16 + (lane & 15)] = acc[t][v];
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[(wave * kRows + 16 * i + 4 * (lane >> 4) + v) * kRP + t * 16 + (lane & 15)] = acc[i][t][v];
   __syncthreads();
   if constexpr (kDirect) {
     // one thread per (row, split column): columns [0, r) hi, [r, 2r) lo, rest 0
-    if (split != nullptr) for (int i = threadIdx.x; i < 16 * xc; i += kNW * 64) {
+    if (split != nullptr) for (int i = threadIdx.x; i < kRows * xc; i += kNW * 64) {
       const int rr = i / xc, col = i - rr * xc;
       const int64_t mm = m0 + rr;
       if (mm >= M) continue;
@@ -226,7 +316,7 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
         const int j = col < r ? col : col - r;
         float s = red[rr * kRP + j];
 #pragma unroll
-        for (int w = 1; w < kNW; ++w) s += red[(w * 16 + rr) * kRP + j];  // parts in order
+        for (int w = 1; w < kNW; ++w) s += red[(w * kRows + rr) * kRP + j];  // parts in order
         if (col < r && out != nullptr) out[mm * r + j] = s;
         const float ss = scale * s;
         const uint16_t hi = to16<kF16>(ss);
@@ -236,24 +326,24 @@ __global__ __launch_bounds__(rowdot_threads<kRP>()) void rowdot_kernel(
       }
     }
     else {
-      for (int i = threadIdx.x; i < 16 * r; i += kNW * 64) {
+      for (int i = threadIdx.x; i < kRows * r; i += kNW * 64) {
         const int rr = i / r, j = i - rr * r;
         const int64_t mm = m0 + rr;
         if (mm >= M) continue;
         float s = red[rr * kRP + j];
 #pragma unroll
-        for (int w = 1; w < kNW; ++w) s += red[(w * 16 + rr) * kRP + j];
+        for (int w = 1; w < kNW; ++w) s += red[(w * kRows + rr) * kRP + j];
         out[mm * r + j] = s;
       }
     }
   } else {
-    for (int i = threadIdx.x; i < 16 * r; i += kNW * 64) {
+    for (int i = threadIdx.x; i < kRows * r; i += kNW * 64) {
       const int rr = i / r, j = i - rr * r;
       const int64_t mm = m0 + rr;
       if (mm >= M) continue;
       float s = red[rr * kRP + j];
 #pragma unroll
-      for (int w = 1; w < kNW; ++w) s += red[(w * 16 + rr) * kRP + j];
+      for (int w = 1; w < kNW; ++w) s += red[(w * kRows + rr) * kRP + j];
       part[(cs * M + mm) * r + j] = s;
     }
   }
@@ -317,24 +407,49 @@ int rowdot_splits(int64_t M, int64_t C) {
   return (int)(s < 1 ? 1 : s);
 }
 
-template <int kRP, int kQL>
+// Row tiles per workgroup and contraction splits. From 2048 rows (ranks up
+// to 64) a workgroup takes 64 rows, and the contraction is split until there
+// are about 256 workgroups, keeping >= 1024 columns per split; below that,
+// one 16-row tile per workgroup as before.
+constexpr int64_t kTallMinRows = 2048;
+constexpr int kTallMinRank = 17;
+
+struct RowdotPlan {
+  int mr;  // 16-row tiles per workgroup
+  int ns;  // contraction splits (partials + finalize when > 1)
+};
+
+RowdotPlan rowdot_plan(int64_t M, int64_t C, int r) {
+  if (M >= kTallMinRows && r >= kTallMinRank && r <= 64) {
+    const int64_t tiles = cdiv(M, (int64_t)(16 * kTallMR));
+    int64_t s = cdiv(kTallTargetWG, tiles);
+    const int64_t maxs = C / kTallMinCols;
+    if (s > maxs) s = maxs;
+    return {kTallMR, (int)(s < 1 ? 1 : s)};
+  }
+  return {1, rowdot_splits(M, C)};
+}
+
+template <int kRP, int kQL, int kMR>
 hipError_t launch_rp(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
-                     uint16_t* split, float scale, float* part, hipStream_t stream, const uint8_t* pmask, bool f16) {
-  constexpr int kNW = RowdotCfg<kRP, kQL>::kNW;
-  const int ns = rowdot_splits(M, C);
+                     uint16_t* split, float scale, float* part, hipStream_t stream, const uint8_t* pmask, bool f16,
+                     int ns) {
+  constexpr int kNW = RowdotCfg<kRP, kQL, kMR>::kNW;
+  constexpr int kRows = RowdotCfg<kRP, kQL, kMR>::kRows;
   const int64_t cchunk = cdiv(cdiv(C, (int64_t)ns), (int64_t)32) * 32;
-  const dim3 grid((unsigned)cdiv(M, (int64_t)16), (unsigned)ns);
+  const dim3 grid((unsigned)cdiv(M, (int64_t)kRows), (unsigned)ns);
   const int xc = lora_extra_cols(r);
   const bool vp = C % 8 == 0;
   const bool vq = kQL == 0 ? (C % 8 == 0) : (r % 8 == 0);
-#define QLORA_RD(VP, VQ, D) \
-  rowdot_kernel<kRP, kQL, VP, VQ, D><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, split, xc, scale, part)
+#define QLORA_RD(VP, VQ, D)                                                                                \
+  rowdot_kernel<kRP, kQL, VP, VQ, D, false, false, kMR><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, \
+                                                                                      out, split, xc, scale, part)
 #define QLORA_RDM(VQ, D)                                                                                   \
-  rowdot_kernel<kRP, 0, true, VQ, D, true><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, split, xc, \
-                                                                          scale, part, pmask)
+  rowdot_kernel<kRP, 0, true, VQ, D, true, false, kMR><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, \
+                                                                                     split, xc, scale, part, pmask)
 #define QLORA_RDF(VP, VQ, D)                                                                               \
-  rowdot_kernel<kRP, kQL, VP, VQ, D, false, true><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, \
-                                                                               split, xc, scale, part)
+  rowdot_kernel<kRP, kQL, VP, VQ, D, false, true, kMR><<<grid, kNW * 64, 0, stream>>>(P, M, C, Q, r, cchunk, out, \
+                                                                                     split, xc, scale, part)
 #define QLORA_RD2(D)                                           \
   if (f16) {                                                   \
     if (pmask != nullptr) return hipErrorInvalidValue;         \
@@ -375,10 +490,21 @@ hipError_t launch_rp(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q,
   return hipGetLastError();
 }
 
+template <int kRP, int kQL>
+hipError_t launch_rq(const uint16_t* P, int64_t M, int64_t C, const uint16_t* Q, int r, float* out,
+                     uint16_t* split, float scale, float* part, hipStream_t stream, const uint8_t* pmask, bool f16) {
+  const RowdotPlan pl = rowdot_plan(M, C, r);
+  if constexpr (kRP <= 64) {
+    if (pl.mr > 1)
+      return launch_rp<kRP, kQL, kTallMR>(P, M, C, Q, r, out, split, scale, part, stream, pmask, f16, pl.ns);
+  }
+  return launch_rp<kRP, kQL, 1>(P, M, C, Q, r, out, split, scale, part, stream, pmask, f16, pl.ns);
+}
+
 }  // namespace
 
 size_t rowdot_ws_bytes(int64_t M, int64_t C, int r) {
-  const int ns = rowdot_splits(M, C);
+  const int ns = rowdot_plan(M, C, r).ns;
   return ns > 1 ? align256((size_t)ns * (size_t)M * (size_t)r * 4) : 0;
 }
 
@@ -386,8 +512,8 @@ hipError_t launch_rowdot(const uint16_t* P, int64_t M, int64_t C, const uint16_t
                          float* out, uint16_t* split, float scale, float* part, hipStream_t stream,
                          const uint8_t* pmask, bool f16) {
 #define QLORA_RP(RP)                                                                                  \
-  return q_layout == 0 ? launch_rp<RP, 0>(P, M, C, Q, r, out, split, scale, part, stream, pmask, f16) \
-                       : launch_rp<RP, 1>(P, M, C, Q, r, out, split, scale, part, stream, pmask, f16);
+  return q_layout == 0 ? launch_rq<RP, 0>(P, M, C, Q, r, out, split, scale, part, stream, pmask, f16) \
+                       : launch_rq<RP, 1>(P, M, C, Q, r, out, split, scale, part, stream, pmask, f16);
   if (r <= 16) { QLORA_RP(16) }
   if (r <= 32) { QLORA_RP(32) }
   if (r <= 64) { QLORA_RP(64) }
