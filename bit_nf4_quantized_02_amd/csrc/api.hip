@@ -543,6 +543,17 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
   // the branch's input mask and scale for the adapter gradients
   const uint8_t* pm = drop ? mask : nullptr;
   const float sb = drop ? scale * keep_scale : scale;
+  if (e == hipSuccess && dA && dB && pm == nullptr && coldot_pairable(M, w->k, w->n)) {
+    // few tokens: dA and dB in one launch
+    const float* T = T_saved;
+    if (T == nullptr) {
+      e = do_project(x, M, w->k, a, 0, r, scale, o.T, nullptr, o.proj, st, nullptr, f16);
+      T = o.T;
+    }
+    if (e == hipSuccess)
+      e = launch_coldot_pair(x, w->k, o.U, dA, 1, w->k, dy, w->n, T, dB, r, 1, M, r, sb, accumulate, st, f16);
+    return hip_status(e);
+  }
   if (e == hipSuccess && dA) e = do_grad(x, M, w->k, o.U, r, sb, dA, 0, accumulate, o.grad, st, pm, f16);
   if (e == hipSuccess && dB) {
     const float* T = T_saved;

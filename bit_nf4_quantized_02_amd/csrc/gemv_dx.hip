@@ -37,14 +37,20 @@ struct DxStage {
 };
 
 // kVec: dY rows are 16-byte aligned (n % 8 == 0) and read 16 bytes at a time.
-template <bool kVec>
+// kDirect (one row range covers all n): the workgroup finishes its outputs
+// itself -- the low-rank term and the rounding, with the finalize kernel's
+// arithmetic -- instead of writing a partial for a second launch.
+template <bool kVec, bool kDirect = false>
 __global__ __launch_bounds__(256) void gemv_dx_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ code8,
                                                       const float* __restrict__ s2, bool s2_bf16,
                                                       const float* __restrict__ mean_p,
                                                       const float* __restrict__ codebook, int64_t n, int64_t k,
                                                       const uint16_t* __restrict__ dY, int64_t M, int64_t rows_per,
-                                                      float* __restrict__ part) {
+                                                      float* __restrict__ part, const float* __restrict__ U,
+                                                      const uint16_t* __restrict__ A, int r, float scale,
+                                                      const uint8_t* __restrict__ mask, float keep,
+                                                      uint16_t* __restrict__ dX) {
   __shared__ float lut[16];
   __shared__ __attribute__((aligned(16))) char tile0[kStepRows * kPitch];
   __shared__ __attribute__((aligned(16))) char tile1[kStepRows * kPitch];
@@ -126,15 +132,33 @@ __global__ __launch_bounds__(256) void gemv_dx_kernel(const uint8_t* __restrict_
     if (step + 1 < nsteps) step_body(step + 1, tile1, tile0, s0, s1);
   }
   // D layout of v_mfma_f32_16x16x32: lane -> column lane % 16, rows 4 (lane / 16) + v
-  float* p = part + (int64_t)blockIdx.y * 16 * k;
+  if constexpr (kDirect) {
+#pragma clang fp contract(off)
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int64_t j = j0 + 64 * wave + 16 * c + (lane & 15);
-    if (j >= k) continue;
+    for (int c = 0; c < 4; ++c) {
+      const int64_t j = j0 + 64 * wave + 16 * c + (lane & 15);
+      if (j >= k) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * (lane >> 4) + v;
-      if (m < M) p[(int64_t)m * k + j] = acc[c][v];
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * (lane >> 4) + v;
+        if (m >= M) continue;
+        float l = 0.0f;
+        for (int t = 0; t < r; ++t) l = fmaf(U[m * r + t], bf16_bits_to_f32(A[(int64_t)t * k + j]), l);
+        const float f = mask != nullptr ? (mask[m * k + j] ? scale * keep : 0.0f) : scale;
+        dX[m * k + j] = to_bf16_bits(acc[c][v] + f * l);
+      }
+    }
+  } else {
+    float* p = part + (int64_t)blockIdx.y * 16 * k;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t j = j0 + 64 * wave + 16 * c + (lane & 15);
+      if (j >= k) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * (lane >> 4) + v;
+        if (m < M) p[(int64_t)m * k + j] = acc[c][v];
+      }
     }
   }
 }
@@ -188,7 +212,10 @@ struct DxSplit {
   int splits;
 };
 
-// Row ranges: about 512 workgroups in all, at least 128 rows per range.
+// Row ranges: about 512 workgroups in all, at least 128 rows per range (a
+// single range, n <= 128, finishes its outputs without the finalize launch;
+// making a 1024 x 1024 weight one range to save that launch took 42 instead
+// of 15 us: four workgroups walking 1024 rows each).
 DxSplit dx_split(int64_t n, int64_t k) {
   const int64_t cg = cdiv(k, (int64_t)kCols);
   int64_t s = cdiv((int64_t)512, cg);
@@ -211,12 +238,16 @@ hipError_t launch_gemv_dx(const Nf4View& w, const uint16_t* dY, int64_t M, const
   const DxSplit d = dx_split(w.n, w.k);
   float* part = static_cast<float*>(ws);
   const dim3 grid((unsigned)cdiv(w.k, (int64_t)kCols), (unsigned)d.splits);
-  if (w.n % 8 == 0)
-    gemv_dx_kernel<true><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.s2_bf16, w.mean, w.codebook, w.n, w.k,
-                                                   dY, M, d.rows_per, part);
-  else
-    gemv_dx_kernel<false><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.s2_bf16, w.mean, w.codebook, w.n, w.k,
-                                                    dY, M, d.rows_per, part);
+  const float* u = r > 0 ? U : nullptr;
+#define QLORA_GDX(V, D)                                                                                          \
+  gemv_dx_kernel<V, D><<<grid, 256, 0, stream>>>(w.codes, w.code8, w.s2, w.s2_bf16, w.mean, w.codebook, w.n, w.k, \
+                                                 dY, M, d.rows_per, part, u, A, u ? r : 0, scale, mask, keep, dX)
+  if (d.splits == 1) {
+    if (w.n % 8 == 0) QLORA_GDX(true, true); else QLORA_GDX(false, true);
+    return hipGetLastError();
+  }
+  if (w.n % 8 == 0) QLORA_GDX(true, false); else QLORA_GDX(false, false);
+#undef QLORA_GDX
   const int64_t groups = M * (w.k / 4);
   gemv_dx_finalize_kernel<<<(unsigned)cdiv(groups, (int64_t)256), 256, 0, stream>>>(
       part, d.splits, M, w.k, r > 0 ? U : nullptr, A, r, scale, mask, keep, dX);

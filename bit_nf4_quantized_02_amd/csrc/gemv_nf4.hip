@@ -224,13 +224,16 @@ size_t gemv_ws_bytes(int64_t k) { return align256((size_t)cdiv(k, 256) * 512 * 1
 
 // Token counts from which the activations are first rewritten in operand
 // order: below it the few distinct rows an activation load touches cost less
-// than the extra pass (measured on the 70B-class shapes).
+// than the extra pass (measured on the 70B-class shapes). Weights with fewer
+// than kXpMinN rows never take it: their workgroups re-read X only a few
+// times, and the extra launch costs more (a 1024 x 1024 layer at M = 16).
 constexpr int64_t kXpMinM = QLORA_GEMV_XP_MIN_M;
+constexpr int64_t kXpMinN = 4096;
 
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T, const uint16_t* B, int r,
                        float scale, uint16_t* Y, void* ws, hipStream_t stream, bool f16) {
   u32x4* Xp = static_cast<u32x4*>(ws);
-  const bool xp = M >= kXpMinM;
+  const bool xp = M >= kXpMinM && w.n >= kXpMinN;
   if (xp) {
     const int64_t entries = cdiv(w.k, (int64_t)256) * 512;
     gemv_xperm_kernel<<<(unsigned)cdiv(entries, (int64_t)256), 256, 0, stream>>>(X, M, w.k, Xp, entries);

@@ -63,6 +63,15 @@ size_t coldot_ws_bytes(int64_t M, int64_t C, int r);
 hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q, int r, float scale,
                          float* G, int64_t g_sc, int64_t g_sj, int accumulate, float* partial,
                          hipStream_t stream, const uint8_t* pmask = nullptr, bool f16 = false);
+// dA and dB of one layer in one launch (both with a single token split, no
+// mask): products (P0, C0, Q0 -> G0 with strides g_sc0, g_sj0) and (P1, ...),
+// the same arithmetic as two launch_coldot calls. coldot_pairable tells when
+// it applies.
+bool coldot_pairable(int64_t M, int64_t C0, int64_t C1);
+hipError_t launch_coldot_pair(const uint16_t* P0, int64_t C0, const float* Q0, float* G0, int64_t g_sc0,
+                              int64_t g_sj0, const uint16_t* P1, int64_t C1, const float* Q1, float* G1,
+                              int64_t g_sc1, int64_t g_sj1, int64_t M, int r, float scale, int accumulate,
+                              hipStream_t stream, bool f16);
 
 // Y = RN_bf16(X W'^T + [sT_hi | sT_lo] [B | B]^T): fused dequant + MFMA GEMM.
 hipError_t launch_gemm_fwd(const Nf4View& w, const uint16_t* X, int64_t M, const uint16_t* TS,

@@ -64,6 +64,10 @@ __device__ __forceinline__ bf16x8 tr_operand(const char* tile, int pitch, int c0
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// kDirect (a single token split): the workgroup writes scale * its sums to G
+// itself, (c, j) at G[c * g_sc + j * g_sj], added to G when accumulating --
+// the value the reduce kernel would compute from one partial -- instead of a
+// partial for a second launch.
 // kCW: columns per wave (64 or 32). kVec: 16-byte P rows (C % 8 == 0); then
 // every load is issued from a clamped, in-range address (rows past the split
 // read its last row, columns past C the last 8) and the step that reaches
@@ -71,12 +75,29 @@ __device__ __forceinline__ bf16x8 tr_operand(const char* tile, int pitch, int c0
 // kMask (16-byte P rows only): P's elements whose byte in pmask [M, C] is 0
 // read as zero (dropout on the adapter's input).
 // kF16: fp16 P and fp16 hi/lo halves of Q (the compute-type ablation).
-template <int kRP, int kCW, bool kVec, bool kMask = false, bool kF16 = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void coldot_mfma_kernel(const uint16_t* __restrict__ P, int64_t M, int64_t C,
-                                                          const float* __restrict__ Q, int r, int64_t mchunk,
-                                                          float* __restrict__ partial,
-                                                          const uint8_t* __restrict__ pmask = nullptr) {
+// The second product of a paired launch (kPair: dA and dB of one layer in a
+// single direct launch, blockIdx.y picking the product).
+struct ColdotSecond {
+  const uint16_t* P;
+  int64_t C;
+  const float* Q;
+  float* G;
+  int64_t g_sc, g_sj;
+};
+
+template <int kRP, int kCW, bool kVec, bool kMask = false, bool kF16 = false, bool kDirect = false, bool kPair = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void coldot_mfma_kernel(
+    const uint16_t* __restrict__ P, int64_t M, int64_t C, const float* __restrict__ Q, int r, int64_t mchunk,
+    float* __restrict__ partial, const uint8_t* __restrict__ pmask, float scale, float* __restrict__ G, int64_t g_sc,
+    int64_t g_sj, int accumulate, ColdotSecond second = {}) {
 #pragma clang fp contract(off)
+  static_assert(!kPair || (kDirect && !kMask), "a paired launch writes G directly and takes no mask");
+  if constexpr (kPair) {
+    if (blockIdx.y == 1) {
+      P = second.P; C = second.C; Q = second.Q; G = second.G; g_sc = second.g_sc; g_sj = second.g_sj;
+    }
+    if ((int64_t)blockIdx.x * (4 * kCW) >= C) return;  // (the grid covers the wider product)
+  }
   constexpr int kJT = kRP / 16;
   constexpr int kCT = kCW / 16;              // 16-column tiles per wave
   constexpr int kCPR = kCW / 2;              // 16-byte chunks per staged P row (4 kCW columns)
@@ -89,7 +110,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int64_t cw = (int64_t)blockIdx.x * (4 * kCW);
-  const int64_t s = blockIdx.y;
+  const int64_t s = kPair ? 0 : blockIdx.y;
   const int64_t m0 = s * mchunk;
   const int64_t m1 = (m0 + mchunk < M) ? m0 + mchunk : M;
   f32x4 acc[kJT][kCT];
@@ -220,7 +241,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = a * 16 + 4 * (lane >> 4) + v;
-        if (c < C && j < r) partial[(s * r + j) * C + c] = acc[a][ct][v];
+        if (c < C && j < r) {
+          if constexpr (kDirect) {
+            float* g = G + c * g_sc + j * g_sj;
+            const float val = scale * acc[a][ct][v];
+            *g = accumulate ? (*g + val) : val;
+          } else {
+            partial[(s * r + j) * C + c] = acc[a][ct][v];
+          }
+        }
       }
     }
 }
@@ -279,24 +308,62 @@ hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q
   const bool vec = C % 8 == 0;
   if (pmask != nullptr && !vec) return hipErrorInvalidValue;
   if (pmask != nullptr && f16) return hipErrorInvalidValue;
-#define QLORA_COLDOT2(RP, CW)                                                                                   \
-  if (f16 && vec)                                                                                              \
-    coldot_mfma_kernel<RP, CW, true, false, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);   \
-  else if (f16)                                                                                                \
-    coldot_mfma_kernel<RP, CW, false, false, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);  \
-  else if (pmask != nullptr)                                                                                   \
-    coldot_mfma_kernel<RP, CW, true, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial, pmask);   \
-  else if (vec) coldot_mfma_kernel<RP, CW, true><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);    \
-  else coldot_mfma_kernel<RP, CW, false><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial);
-#define QLORA_COLDOT(RP) { QLORA_COLDOT2(RP, kColdotCW) }
-  if (r <= 16) { QLORA_COLDOT(16) }
-  else if (r <= 32) { QLORA_COLDOT(32) }
-  else if (r <= 64) { QLORA_COLDOT(64) }
-  else { QLORA_COLDOT(128) }
+  const bool direct = ns == 1;
+#define QLORA_COLDOT3(RP, CW, VEC, MASK, F16, D)                                                                \
+  coldot_mfma_kernel<RP, CW, VEC, MASK, F16, D><<<grid, 256, 0, stream>>>(P, M, C, Q, r, mchunk, partial, pmask, \
+                                                                           scale, G, g_sc, g_sj, accumulate)
+#define QLORA_COLDOT2(RP, CW, D)                                  \
+  if (f16 && vec) QLORA_COLDOT3(RP, CW, true, false, true, D);    \
+  else if (f16) QLORA_COLDOT3(RP, CW, false, false, true, D);     \
+  else if (pmask != nullptr) QLORA_COLDOT3(RP, CW, true, true, false, D); \
+  else if (vec) QLORA_COLDOT3(RP, CW, true, false, false, D);     \
+  else QLORA_COLDOT3(RP, CW, false, false, false, D);
+#define QLORA_COLDOT(RP)                                  \
+  {                                                       \
+    if (direct) { QLORA_COLDOT2(RP, kColdotCW, true) }    \
+    else { QLORA_COLDOT2(RP, kColdotCW, false) }          \
+  }
+  if (r <= 16) QLORA_COLDOT(16)
+  else if (r <= 32) QLORA_COLDOT(32)
+  else if (r <= 64) QLORA_COLDOT(64)
+  else QLORA_COLDOT(128)
 #undef QLORA_COLDOT
 #undef QLORA_COLDOT2
-  coldot_reduce_kernel<<<(unsigned)cdiv(C * r, 256), 256, 0, stream>>>(partial, C, r, ns, scale, G, g_sc, g_sj,
-                                                                      accumulate);
+#undef QLORA_COLDOT3
+  if (!direct)
+    coldot_reduce_kernel<<<(unsigned)cdiv(C * r, 256), 256, 0, stream>>>(partial, C, r, ns, scale, G, g_sc, g_sj,
+                                                                        accumulate);
+  return hipGetLastError();
+}
+
+bool coldot_pairable(int64_t M, int64_t C0, int64_t C1) {
+  return coldot_splits(M, C0) == 1 && coldot_splits(M, C1) == 1;
+}
+
+hipError_t launch_coldot_pair(const uint16_t* P0, int64_t C0, const float* Q0, float* G0, int64_t g_sc0,
+                              int64_t g_sj0, const uint16_t* P1, int64_t C1, const float* Q1, float* G1,
+                              int64_t g_sc1, int64_t g_sj1, int64_t M, int r, float scale, int accumulate,
+                              hipStream_t stream, bool f16) {
+  if (!coldot_pairable(M, C0, C1)) return hipErrorInvalidValue;
+  const int64_t mchunk = cdiv(M, (int64_t)32) * 32;
+  const int64_t cmax = C0 > C1 ? C0 : C1;
+  const dim3 grid((unsigned)cdiv(cmax, 4 * kColdotCW), 2u);
+  const ColdotSecond sec{P1, C1, Q1, G1, g_sc1, g_sj1};
+  const bool vec = C0 % 8 == 0 && C1 % 8 == 0;
+#define QLORA_PAIR3(RP, VEC, F16)                                                                              \
+  coldot_mfma_kernel<RP, kColdotCW, VEC, false, F16, true, true><<<grid, 256, 0, stream>>>(                      \
+      P0, M, C0, Q0, r, mchunk, nullptr, nullptr, scale, G0, g_sc0, g_sj0, accumulate, sec)
+#define QLORA_PAIR(RP)                                   \
+  {                                                      \
+    if (f16) { if (vec) QLORA_PAIR3(RP, true, true); else QLORA_PAIR3(RP, false, true); }    \
+    else { if (vec) QLORA_PAIR3(RP, true, false); else QLORA_PAIR3(RP, false, false); }      \
+  }
+  if (r <= 16) QLORA_PAIR(16)
+  else if (r <= 32) QLORA_PAIR(32)
+  else if (r <= 64) QLORA_PAIR(64)
+  else QLORA_PAIR(128)
+#undef QLORA_PAIR
+#undef QLORA_PAIR3
   return hipGetLastError();
 }
 

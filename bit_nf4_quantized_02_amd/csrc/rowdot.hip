@@ -398,9 +398,15 @@ __global__ __launch_bounds__(256) void rowdot_finalize_kernel(const float* __res
   }
 }
 
+// Contractions up to this length are not split over workgroups: each wave
+// then walks at most 256 columns, and the finalize launch would cost more
+// than the split saves (a 1024-wide layer at M = 16).
+constexpr int64_t kShortContraction = 2048;
+
 int rowdot_splits(int64_t M, int64_t C) {
   const int64_t tiles = cdiv(M, (int64_t)16);
   if (tiles >= 128) return 1;                // enough row tiles: whole contraction per workgroup
+  if (C <= kShortContraction) return 1;      // short rows: one pass per tile beats a second launch
   int64_t s = cdiv((int64_t)256, tiles);
   const int64_t maxs = cdiv(C, (int64_t)256);  // keep >= 256 columns per split
   if (s > maxs) s = maxs;
