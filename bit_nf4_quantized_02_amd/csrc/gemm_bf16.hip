@@ -190,52 +190,76 @@ __device__ __forceinline__ void issue_step(const Rsrc& rs, const CopyPlan& p, in
   }
 }
 
+// Fragments of one substep: 4 activation row blocks and 2 weight column
+// blocks of the wave's 128 x 64 sub-tile.
+struct StepFrags {
+  bf16x8 af[2][kTM], bfr[2][kTN];  // double-buffered by substep parity
+};
+
+template <bool kNN>
+__device__ __forceinline__ void read_substep(StepFrags& f, const char* Ac, const char* Bc, int wm0, int wn0, int kk,
+                                             int buf, int lane) {
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) f.af[buf][i] = tile_frag(Ac, wm0 + i * 32, kk, lane);
+#pragma unroll
+  for (int j = 0; j < kTN; ++j) f.bfr[buf][j] = b_frag<kNN>(Bc, wn0 + j * 32, kk, lane);
+}
+
 // One step: MFMAs on (Ac, Bc) while the copies of step + 1 fill (An, Bn).
+// Each substep's MFMAs run while the next substep's fragments are read.
 // Restrict pointers tell the compiler the copies cannot alias the fragment
-// reads, so it does not wait for them before reading. kPrio raises the
-// wave's issue priority over its MFMA stream. Measured on the plain bf16
-// GEMM: 4-6% faster where the operands (360 MB of expanded weight and more)
-// exceed the 256 MB last-level cache and stream from HBM, 3-10% slower where
-// they fit in it; the launch picks it by operand size.
+// reads, so it does not wait for them before reading.
+//
+// Two schedules, chosen with kPrio by operand size:
+//  - operands that fit in the 256 MB last-level cache: substeps 0-2
+//    multiply, then this wave's copies have landed and all waves meet, then
+//    substep 3 multiplies while substep 0 of step + 1 is read from (An, Bn),
+//    so the LDS latency after the barrier hides behind MFMAs. On entry f
+//    holds substep 0 (buffer 0); after the last step that read finds the
+//    repeated copy (valid data, not used). Measured in the 65B-class layer
+//    step: the 8192 x 8192 projections 2-4% faster than with the barrier
+//    after all four substeps.
+//  - larger operands (360 MB of expanded weight and more, streamed from
+//    HBM): all four substeps before the barrier, with the wave's issue
+//    priority raised over its MFMA stream: 4-6% faster there than without
+//    the priority (3-10% slower where the operands fit in the cache), and
+//    4% slower with the cross-barrier schedule.
 template <bool kF16, bool kPrio, bool kNN>
 __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
                                           int nk_main, int wave,
                                           const char* __restrict__ Ac, const char* __restrict__ Bc,
-                                          char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN]) {
+                                          char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN],
+                                          StepFrags& f) {
   const int lane = threadIdx.x & 63;
   const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
   // past the last step (nk: end of this workgroup's range) the copy repeats
   // the last step into a buffer no later step reads: keeps the body free of
   // branches
   const int s1 = step + 1 < nk ? step + 1 : nk - 1;
-  bf16x8 af[2][kTM], bfr[2][kTN];
-  auto read_frags = [&](int kk, int buf) {
-#pragma unroll
-    for (int i = 0; i < kTM; ++i) af[buf][i] = tile_frag(Ac, wm0 + i * 32, kk, lane);
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) bfr[buf][j] = b_frag<kNN>(Bc, wn0 + j * 32, kk, lane);
-  };
-  read_frags(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
+  constexpr bool kCross = !kPrio;
+  if constexpr (!kCross) {
+    read_substep<kNN>(f, Ac, Bc, wm0, wn0, 0, 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   issue_step<kNN>(rs, p, s1, nk_main, wave, An, Bn, a.ldf, a.ldx);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (kPrio) {
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
   }
+  constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
+  constexpr int kBefore = kCross ? 3 : kBK / 16;  // substeps before the barrier
 #pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
+  for (int kk = 0; kk < kBefore; ++kk) {
     const int cb = kk & 1;
-    if (kk < 3) read_frags(kk + 1, cb ^ 1);
+    if (kk < 3) read_substep<kNN>(f, Ac, Bc, wm0, wn0, kk + 1, cb ^ 1, lane);
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        acc[i][j] = mfma32<kF16>(af[cb][i], bfr[cb][j], acc[i][j]);
+      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[cb][i], f.bfr[cb][j], acc[i][j]);
   }
   // schedule: for substeps 0..2 one fragment read (of the next substep) per
-  // MFMA, then the last substep's MFMAs
-  constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
+  // MFMA, then (without the cross-barrier read) the last substep's MFMAs
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk)
 #pragma unroll
@@ -243,13 +267,27 @@ __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const
       if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
     }
-  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+  if constexpr (!kCross) __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
   if constexpr (kPrio) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  step_barrier<0>();
+  if constexpr (kCross) {
+    __builtin_amdgcn_sched_barrier(0);
+    read_substep<kNN>(f, An, Bn, wm0, wn0, 0, 0, lane);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[1][i], f.bfr[1][j], acc[i][j]);
+#pragma unroll
+    for (int g = 0; g < kMfma; ++g) {
+      if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
-  step_barrier<0>();
 }
 
 // One step without copies in flight: fragments of (Ac, Bc) and their MFMAs.
@@ -384,11 +422,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   if (sbeg < nk_end) {  // (every split range is non-empty for the split counts split_plan picks)
     issue_step<kNN>(rs, plan, sbeg, nk_main, wave, As0, Bs0, a.ldf, a.ldx);
     step_barrier<0>();
+    StepFrags f;
+    if constexpr (!kPrio) read_substep<kNN>(f, As0, Bs0, wm0, wn0, 0, 0, lane);  // the cross-barrier schedule's
     for (int step = sbeg; step < nk_end; step += 2) {
-      bf16_step<kF16, kPrio, kNN>(a, rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc);
+      bf16_step<kF16, kPrio, kNN>(a, rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc, f);
       if (step + 1 < nk_end)
-        bf16_step<kF16, kPrio, kNN>(a, rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc);
+        bf16_step<kF16, kPrio, kNN>(a, rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc, f);
     }
+    // the cross-barrier schedule's last read (of the repeated copy) is done
+    // before the epilogue reuses the buffers
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+    __syncthreads();
   }
 
   if (!whole) {
@@ -412,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
 
   // Epilogue: each wave writes its 128 x 64 bf16 block (16 KB) into its own
   // LDS region (all copies have landed and all fragment reads are done: the
-  // last step ended with a barrier after waiting for both), then stores
+  // step loop ends with a barrier after waiting for both), then stores
   // 16-byte row segments.
   {
     char* const bufs0 = wave < 4 ? (wave < 2 ? As0 : As1) : (wave < 6 ? Bs0 : Bs1);
