@@ -218,4 +218,48 @@ __device__ __forceinline__ bf16x8 tr_rows8(const char* tile, int pitch, int c0, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Direct buffer load into LDS (16 bytes per lane, LDS address from the wave-
+// uniform destination), declared through its LLVM intrinsic so the compiler
+// keeps track of the LDS region written and does not wait for these copies
+// before reading the other buffer.
+__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds, int size, int voffset,
+                                    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer descriptor for a whole operand: base address, size in bytes (the
+// offsets of every copy stay below it), raw 32-bit dword format.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r[2] = (int)(uint32_t)(bytes < (int64_t)0xFFFFFFFF ? bytes : (int64_t)0xFFFFFFFF);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from a buffer straight into LDS at dst (wave-uniform;
+// lane i lands at dst + 16 i). Offsets at or past the descriptor's size
+// read as zero.
+__device__ __forceinline__ void copy16(const i32x4& r, uint32_t voff, int soff, char* dst) {
+  raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t*)dst, 16, (int)voff, soff, 0, 0);
+}
+
+// 16 bytes per lane from a buffer into registers; offsets at or past the
+// descriptor's size read as zero.
+__device__ u32x4 raw_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.v4i32");
+
+// Buffer loads of one byte / half-word / word (zero past the descriptor's
+// size). Unlike plain loads the compiler keeps them where they are issued:
+// a plain load whose value is used only after the loop's exit test gets
+// sunk past it, right before its use, which drains the prefetch.
+__device__ uint8_t raw_buffer_load_u8(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.i8");
+__device__ uint16_t raw_buffer_load_u16(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.i16");
+__device__ uint32_t raw_buffer_load_u32(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
+    "llvm.amdgcn.raw.buffer.load.i32");
+
 }  // namespace qlora

@@ -60,8 +60,6 @@ struct BfArgs {
 
 constexpr int kCopies = 32 / kWaves;  // 1 KB copies per wave per operand tile
 
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
 // Byte offsets of this lane's copies, relative to the operands' base pointer
 // advanced to the step's first column. For the last base step of a ragged
 // contraction (kc % 64 != 0) the column is clamped to the last in-range chunk
@@ -137,32 +135,9 @@ __device__ __forceinline__ bf16x8 b_frag(const char* Bc, int cb, int kk, int lan
     return tile_frag(Bc, cb, kk, lane);
 }
 
-// Direct buffer load into LDS (16 bytes per lane, LDS address from the wave-
-// uniform destination), declared through its LLVM intrinsic so the compiler
-// keeps track of the LDS region written and does not wait for these copies
-// before reading the other buffer.
-__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds, int size, int voffset,
-                                    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-
-// Buffer descriptor for a whole operand: base address, size in bytes (the
-// offsets of every copy stay below it), raw 32-bit dword format.
-__device__ __forceinline__ i32x4 make_rsrc(const void* p, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  r[2] = (int)(uint32_t)(bytes < (int64_t)0xFFFFFFFF ? bytes : (int64_t)0xFFFFFFFF);
-  r[3] = 0x00020000;
-  return r;
-}
-
 struct Rsrc {
   i32x4 act, x, f, fx;
 };
-
-__device__ __forceinline__ void copy16(const i32x4& r, uint32_t voff, int soff, char* dst) {
-  raw_buffer_load_lds(r, (__attribute__((address_space(3))) uint32_t*)dst, 16, (int)voff, soff, 0, 0);
-}
 
 // Copies of step `step` into (As, Bs). The operand choice is wave-uniform
 // (it depends on the step only), so descriptors and step offsets stay scalar.

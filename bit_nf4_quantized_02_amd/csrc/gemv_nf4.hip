@@ -8,22 +8,23 @@
 //
 //   Y = RN_bf16( X W'^T + s T B^T ),   T = X A^T precomputed (fp32)
 //
-// Each workgroup owns NT output rows (n) and the whole contraction; its kW
-// waves split the contraction into kW parts. A wave walks its quarter in
-// 256-wide chunks, keeping the loads of the next chunk in flight while it
-// works on one: every lane loads 32 contiguous bytes of codes (one whole
-// 64-block of one row, one scale), expands them to bf16 in registers
-// through an LDS table indexed by whole code bytes (one read yields the
-// levels of two weights; the products are those of the 16-entry codebook)
-// and feeds them straight to
-// v_mfma_f32_16x16x32_bf16 as the B operand; X (padded to 16 rows with zeros)
-// is the A operand. The contraction order inside a chunk is permuted the same
-// way on both operands (lane group g takes columns 64 g .. 64 g + 63), which
-// leaves the sum unchanged and makes each lane's code load contiguous. A
-// first small kernel writes X in exactly that operand order (per 256-column
-// chunk, per MFMA, per lane: 16 bytes), so each activation load instruction
-// reads 1 KB in one run; read in place, the 16 token rows and 4 column groups
-// of one instruction fall in 64 different cache lines.
+// Each workgroup owns 16 kT output rows (n) and the whole contraction; its
+// kW waves take its 256-wide chunks in turn (wave w: chunks w, w + kW, ...). The codes of a chunk (kT tiles x 16 rows x 128 bytes) go from HBM
+// straight into LDS (buffer loads into LDS, no registers held), into a ring
+// of three per wave: one chunk is worked on while the next two are in
+// flight, which keeps about 64 KB of codes per CU on the way. A lane takes
+// one whole 64-block of one row (32 bytes, one scale) from the ring, expands
+// it to bf16 in registers through an LDS table indexed by whole code bytes
+// (one read yields the levels of two weights; the products are those of the
+// 16-entry codebook) and feeds it straight to v_mfma_f32_16x16x32_bf16 as the
+// B operand; X (padded to 16 rows with zeros) is the A operand. The
+// contraction order inside a chunk is permuted the same way on both operands
+// (lane group g takes columns 64 g .. 64 g + 63), which leaves the sum
+// unchanged and makes each lane's codes contiguous. From 5 tokens a first
+// small kernel writes X in exactly that operand order (per 256-column chunk,
+// per MFMA, per lane: 16 bytes), so each activation load instruction reads
+// 1 KB in one run; read in place, the 16 token rows and 4 column groups of
+// one instruction fall in 64 different cache lines.
 // Partial sums of the waves are added in a fixed order through LDS; the
 // low-rank term T B^T is formed with fp32 MFMAs (one 16-row tile per wave,
 // T and B exact in fp32) and added in fp32, and Y is rounded to bf16 once.
@@ -52,9 +53,74 @@ __global__ __launch_bounds__(256) void gemv_xperm_kernel(const uint16_t* __restr
   Xp[e] = v;
 }
 
-// kXp: activations from the operand-ordered copy Xp (else read in place from X).
-// kF16: fp16 activations, weights, B and output (the compute-type ablation).
-template <int NT, int kW, bool kLora, bool kXp, bool kF16>
+// Level table: entry b (a code byte) holds the level pair (L[b & 15],
+// L[b >> 4]) of its two codes, kLutCopies times side by side, so that lane l
+// reads copy l % kLutCopies: the 16 lanes that share the LDS banks in one
+// cycle of an 8-byte read then hit 16 different bank pairs whatever codes
+// they look up (with one shared copy, random codes collide).
+constexpr int kLutCopies = 16;
+constexpr int kLutBytes = 256 * kLutCopies * 8;
+constexpr int kRingDepth = 3;  // chunks of codes per wave: one worked on, two in flight
+
+// s_waitcnt immediate that waits for LDS / scalar-memory operations only
+// (lgkmcnt <= n; vmcnt and expcnt left at their maxima)
+constexpr int lgkm_wait(int n) { return 0xC07F | (n << 8); }
+
+// Eight codes of one word -> four bf16 pairs through the replicated table
+// (lane_off = 8 * (lane % kLutCopies)); products and rounding are those of
+// dequant8.
+template <bool kF16>
+__device__ __forceinline__ u32x4 dequant8_rep(uint32_t word, const char* lut, uint32_t lane_off, float cp) {
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t b = (word >> (8 * p)) & 0xFFu;
+    const float2 l = *reinterpret_cast<const float2*>(lut + ((b * (kLutCopies * 8)) | lane_off));
+    out[p] = pack2<kF16>(nf4_scaled(l.x, cp), nf4_scaled(l.y, cp));
+  }
+  return out;
+}
+
+// Swizzle of a 128-byte code line in LDS: row r of a 16-row tile keeps its
+// 16-byte segment g at position g ^ sw(r). The 8 (or 16) lanes that read one
+// segment of 8 (16) consecutive rows in one LDS cycle then hit distinct banks
+// whether the LDS serves 128 or 256 bytes per cycle.
+__device__ __forceinline__ int code_swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Scale fields of block blk in one of the three stored forms, without
+// branches (kForm 0: double-quantized, E4M3 code + fp32 second-level scale
+// per 256 blocks; 1: fp32 per block; 2: bf16 per block), as scale_fields.
+// c8r / s2r: descriptors of the code and scale arrays.
+template <int kForm>
+__device__ __forceinline__ void scale_fields_of(const i32x4& c8r, const i32x4& s2r, uint32_t blk, uint32_t& c8,
+                                                float& s2v) {
+  if constexpr (kForm == 0) {
+    c8 = raw_buffer_load_u8(c8r, (int)blk, 0, 0);
+    s2v = __builtin_bit_cast(float, raw_buffer_load_u32(s2r, (int)((blk / kDqBlock) * 4), 0, 0));
+  } else if constexpr (kForm == 1) {
+    c8 = kE4m3One;
+    s2v = __builtin_bit_cast(float, raw_buffer_load_u32(s2r, (int)(blk * 4), 0, 0));
+  } else {
+    c8 = kE4m3One;
+    s2v = bf16_bits_to_f32(raw_buffer_load_u16(s2r, (int)(blk * 2), 0, 0));
+  }
+}
+
+// Scale fields of one 256-column chunk for the lane's rows, and its
+// activation operand.
+template <int kT>
+struct GvStage {
+  uint32_t c8[kT];
+  float s2v[kT];
+  u32x4 xa[8];
+};
+
+// kT: 16-row tiles per workgroup (each wave covers all of them over its
+// share of the contraction); kW: waves. kXp: activations from the
+// operand-ordered copy Xp (else read in place from X). kF16: fp16
+// activations, weights, B and output (the compute-type ablation). kForm: the
+// block-scale form (scale_fields_of).
+template <int kT, int kW, bool kXp, bool kF16, int kForm>
 __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ code8,
                                                        const float* __restrict__ s2,
@@ -65,132 +131,211 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
                                                        const float* __restrict__ T,
                                                        const uint16_t* __restrict__ B, int r, float scale,
                                                        uint16_t* __restrict__ Y) {
-  constexpr int kTiles = NT / 16;
-  __shared__ float2 lut2[256];
-  __shared__ float red[kW][kTiles][16][16];
-  __shared__ float lred[kLora ? kTiles : 1][16][16];
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
-  for (int i = t; i < 256; i += 64 * kW)
-    lut2[i] = float2{codebook[i & 15], codebook[i >> 4]};  // levels of the two codes in byte i
+  constexpr int NT = 16 * kT;
+  constexpr int kSlot = kT * 2048;  // one wave's codes of one chunk: kT tiles x 16 rows x 128 bytes
+  // three separate ring arrays, so the compiler can tell the one being read
+  // from the ones being filled by direct copies (and waits only for the copy
+  // of the chunk it reads)
+  __shared__ __attribute__((aligned(16))) char lut[kLutBytes];
+  __shared__ __attribute__((aligned(16))) char ring0[kW * kSlot];
+  __shared__ __attribute__((aligned(16))) char ring1[kW * kSlot];
+  __shared__ __attribute__((aligned(16))) char ring2[kW * kSlot];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // the 16 levels pass through the first ring (not yet in use) so that the
+  // table fill below reads LDS, not 16 rounds of global loads per thread
+  float* const levels = reinterpret_cast<float*>(ring0);
+  if (t < 16) levels[t] = codebook[t];
   __syncthreads();
+  for (int i = t; i < 256 * kLutCopies; i += 64 * kW) {
+    const int e = i / kLutCopies;
+    reinterpret_cast<float2*>(lut)[i] = float2{levels[e & 15], levels[e >> 4]};
+  }
   const float mean = weight_mean(code8, mean_p);
   const int64_t n0 = (int64_t)blockIdx.x * NT;
-  constexpr int kChunk = 256;                            // columns per wave iteration
-  const int64_t kq = cdiv(cdiv(K, kW), kChunk) * kChunk;  // per-wave share
-  const int64_t kb = wave * kq;
-  const int64_t ke = (kb + kq < K) ? kb + kq : K;        // multiple of 64
-  const int grp = lane >> 4;   // 0..3: which 64-block of a 256-column chunk
-  const int col = lane & 15;   // A: token row m; B: weight row within a tile
+  // this wave's contiguous range of 256-column chunks (a multiple-of-64 tail
+  // in the last one)
+  const int nq = (int)cdiv(K, (int64_t)256);
+  // chunks wave, wave + kW, wave + 2 kW, ...: the waves of a workgroup read
+  // neighbouring chunks of the same rows at about the same time (kW x 128
+  // contiguous bytes per row) rather than far-apart pieces of each row
+  const int cnt = wave < nq ? (nq - 1 - wave) / kW + 1 : 0;
+  const int grp = lane >> 4;  // 0..3: which 64-block of a chunk
+  const int col = lane & 15;  // A: token row m; B: weight row within a tile
   const int64_t kblocks = K / kBlock;
-  const int64_t nq = cdiv(K, (int64_t)kChunk);  // chunks of the operand-ordered activations
-  const bool xtok = col < M;                     // lanes of token rows past M load nothing
-  const uint16_t* xrow = X + (int64_t)(col < M ? col : M - 1) * K;
 
-  f32x4 acc[kTiles];
+  // Copies: lane l of copy h of tile i fills row 8 h + l / 8 of the tile at
+  // swizzled position l % 8, i.e. logical segment (l % 8) ^ sw(row). Rows past
+  // N lie past the end of the codes and read as zero (their outputs are not
+  // stored); columns past K in the last chunk read the next row's codes and
+  // meet zero activations.
+  const i32x4 crs = make_rsrc(codes, N * (K / 2));
+  uint32_t cvoff[kT][2];
 #pragma unroll
-  for (int i = 0; i < kTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Per-lane row bases, computed once. Every load below reads a clamped,
-  // in-range address; out-of-range rows / blocks / tokens are then replaced
-  // by code 7 (level 0) or zero activations with selects, so the loop body is
-  // one basic block and the next chunk's loads stay in flight while a chunk
-  // is expanded and multiplied. Lane group g takes the whole 64-block g of
-  // the chunk (32 code bytes, one scale): a row's 128-byte code line is read
-  // by one wave in one iteration. The 64 columns are fed to 8 MFMAs, 8 per
-  // MFMA; the activations follow the same column permutation, which leaves
-  // the sum unchanged.
-  const uint8_t* crow[kTiles];
-  int64_t bbase[kTiles];
-  bool rowok[kTiles];
+  for (int i = 0; i < kT; ++i)
 #pragma unroll
-  for (int i = 0; i < kTiles; ++i) {
-    const int64_t n = n0 + i * 16 + col;
-    const int64_t nc = n < N ? n : N - 1;
-    rowok[i] = n < N;
-    crow[i] = codes + nc * (K / 2);
-    bbase[i] = nc * kblocks;
+    for (int h = 0; h < 2; ++h) {
+      const int rr = 8 * h + (lane >> 3);
+      const int g = (lane & 7) ^ code_swz(rr);
+      cvoff[i][h] = (uint32_t)((n0 + 16 * i + rr) * (K / 2) + 16 * g);
+    }
+  // reads: row col, logical segments 2 grp and 2 grp + 1 (64 codes)
+  const uint32_t rd0 = (uint32_t)(col * 128 + 16 * ((2 * grp) ^ code_swz(col)));
+  const uint32_t lane_off = (uint32_t)(lane % kLutCopies) * 8;
+  // scale rows (clamped: rows past N are computed and dropped)
+  uint32_t bbase[kT];  // (blocks < 2^27: the codes stay under 4 GiB)
+#pragma unroll
+  for (int i = 0; i < kT; ++i) {
+    const int64_t n = n0 + 16 * i + col;
+    bbase[i] = (uint32_t)((n < N ? n : N - 1) * kblocks);
   }
+  // activations: Xp[q][s][lane] (operand order), or X[col][256 q + 64 grp +
+  // 8 s ..] in place, token rows past M and columns past K reading as zero
+  const i32x4 xrs = kXp ? make_rsrc(Xp, (int64_t)nq * 512 * 16) : make_rsrc(X, M * K * 2);
+  const uint32_t xvoff = kXp ? (uint32_t)lane * 16 : (uint32_t)(col * K * 2 + 128 * grp);
 
-  struct Stage {
-    u32x4 cw[kTiles][2];
-    uint32_t c8[kTiles];
-    float s2v[kTiles];
-    u32x4 xa[8];
-    bool kin;
-  };
-  auto load = [&](int64_t k0, Stage& st) {
-    const int64_t k = k0 + 64 * grp;
-    st.kin = k < ke;
-    const int64_t kc = st.kin ? k : ke - 64;  // a valid block of this wave's range
-    // this chunk's operands, in order (a prefetch past the last chunk reads
-    // the last one again: every group then has kin false and code 7)
+  // scale arrays (blocks < 2^30: 32-bit byte offsets)
+  const int64_t nblk = N * kblocks;
+  const i32x4 c8rs = make_rsrc(code8, kForm == 0 ? nblk : 0);
+  const i32x4 s2rs = make_rsrc(s2, kForm == 0 ? cdiv(nblk, (int64_t)kDqBlock) * 4 : nblk * (kForm == 1 ? 4 : 2));
+
+  auto issue = [&](int j, char* R, GvStage<kT>& st) {
+    const int q = wave + kW * (j < cnt ? j : cnt - 1);  // past the range: the last chunk again
+    char* const dst = R + wave * kSlot;
+#pragma unroll
+    for (int i = 0; i < kT; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) copy16(crs, cvoff[i][h], q * 128, dst + i * 2048 + h * 1024);
+    const int kc = q * 256 + 64 * grp;
+    const uint32_t bq = (uint32_t)(kc < K ? kc / kBlock : kblocks - 1);
+#pragma unroll
+    for (int i = 0; i < kT; ++i) scale_fields_of<kForm>(c8rs, s2rs, bbase[i] + bq, st.c8[i], st.s2v[i]);
     if constexpr (kXp) {
-      const int64_t q = k0 / kChunk < nq ? k0 / kChunk : nq - 1;
-      const u32x4* xq = Xp + q * 512 + lane;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) st.xa[s] = xtok ? xq[64 * s] : u32x4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < 8; ++s) st.xa[s] = raw_buffer_load_b128(xrs, (int)xvoff, q * 8192 + s * 1024, 0);
     } else {
+      const uint32_t v = kc < K ? xvoff : 0x80000000u;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) st.xa[s] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * s);
-    }
-#pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      st.cw[i][0] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2);
-      st.cw[i][1] = *reinterpret_cast<const u32x4*>(crow[i] + kc / 2 + 16);
-      const int64_t blk = bbase[i] + kc / kBlock;
-      scale_fields(code8, s2, s2_bf16, blk, st.c8[i], st.s2v[i]);
+      for (int s = 0; s < 8; ++s) st.xa[s] = raw_buffer_load_b128(xrs, (int)(v + 16 * s), q * 512, 0);
     }
   };
-  auto compute = [&](const Stage& st) {
-    const bool xuse = st.kin && xtok;
+
+  f32x4 acc[kT];
+#pragma unroll
+  for (int i = 0; i < kT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Work on one chunk, in groups of kGw code words (8 kGw weights of one
+  // row per lane): the level-table reads of group g + 1 are issued before
+  // the products of group g, so about 4 kGw + 4 reads per wave are in
+  // flight instead of the 4 that one word's expansion waits for.
+  constexpr int kGw = 2;
+  constexpr int kGroups = kT * 8 / kGw;
+  auto compute = [&](const char* R, const GvStage<kT>& st) {
+    const char* const src = R + wave * kSlot;
     bf16x8 xa[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 v = st.xa[s];
+    for (int s = 0; s < 8; ++s) xa[s] = __builtin_bit_cast(bf16x8, st.xa[s]);
+    uint32_t cw[kT][8];
+    float cp[kT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = xuse ? v[e] : 0u;
-      xa[s] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int i = 0; i < kT; ++i) {
+      const u32x4 c0 = *reinterpret_cast<const u32x4*>(src + i * 2048 + rd0);
+      const u32x4 c1 = *reinterpret_cast<const u32x4*>(src + i * 2048 + (rd0 ^ 16u));
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      const bool use = st.kin && rowok[i];
-      const float cp = decode_block_scale(st.c8[i], st.s2v[i], mean);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint32_t word = use ? st.cw[i][s >> 2][s & 3] : 0x77777777u;  // code 7: level 0
-        const u32x4 bw = dequant8_pairs<kF16>(word, lut2, cp);
-        acc[i] = mfma16<kF16>(xa[s], __builtin_bit_cast(bf16x8, bw), acc[i]);
+      for (int e = 0; e < 4; ++e) {
+        cw[i][e] = c0[e];
+        cw[i][4 + e] = c1[e];
       }
+      cp[i] = decode_block_scale(st.c8[i], st.s2v[i], mean);
+    }
+    float2 lv[2][4 * kGw];
+    auto gather = [&](int g, float2 (&out)[4 * kGw]) {
+      const int i = g / (8 / kGw), s0 = (g % (8 / kGw)) * kGw;
+#pragma unroll
+      for (int w = 0; w < kGw; ++w)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t b = (cw[i][s0 + w] >> (8 * p)) & 0xFFu;
+          out[4 * w + p] = *reinterpret_cast<const float2*>(lut + ((b * (kLutCopies * 8)) | lane_off));
+        }
+    };
+    gather(0, lv[0]);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      if (g + 1 < kGroups) {
+        gather(g + 1, lv[(g + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(lgkm_wait(4 * kGw));  // group g's reads (one wait for all of them)
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(lgkm_wait(0));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = g / (8 / kGw), s0 = (g % (8 / kGw)) * kGw;
+#pragma unroll
+      for (int w = 0; w < kGw; ++w) {
+        u32x4 bw;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float2 l = lv[g & 1][4 * w + p];
+          bw[p] = pack2<kF16>(nf4_scaled(l.x, cp[i]), nf4_scaled(l.y, cp[i]));
+        }
+        acc[i] = mfma16<kF16>(xa[s0 + w], __builtin_bit_cast(bf16x8, bw), acc[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  if (kb < ke) {  // (a wave may have no columns when K is tiny)
-    Stage st0, st1;
-    load(kb, st0);
-    for (int64_t k0 = kb; k0 < ke; k0 += 2 * kChunk) {
-      // the scheduling barriers keep each chunk's loads issued ahead of the
-      // work on the previous chunk (the compiler would otherwise sink them to
-      // their first use)
-      load(k0 + kChunk, st1);
+
+  __syncthreads();  // the level table (and the levels read before the copies reuse the first ring)
+  if (cnt > 0) {
+    GvStage<kT> st0, st1, st2;
+    issue(0, ring0, st0);
+    issue(1, ring1, st1);
+    // whole groups of three chunks, with no exit inside a group: an exit
+    // between the chunks leaves a path on which a chunk's loads are still
+    // pending at the loop head, and the compiler then waits for every load
+    // in flight there
+    int j = 0;
+    for (; j + kRingDepth <= cnt; j += kRingDepth) {
+      // the scheduling barriers keep each chunk's copies and loads issued
+      // ahead of the work on the chunk before them
+      issue(j + 2, ring2, st2);
       __builtin_amdgcn_sched_barrier(0);
-      compute(st0);
-      if (k0 + kChunk >= ke) break;
-      load(k0 + 2 * kChunk, st0);
+      compute(ring0, st0);
       __builtin_amdgcn_sched_barrier(0);
-      compute(st1);
+      issue(j + 3, ring0, st0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ring1, st1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(j + 4, ring1, st1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ring2, st2);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the last one or two chunks, already in rings 0 and 1
+    if (j < cnt) compute(ring0, st0);
+    if (j + 1 < cnt) compute(ring1, st1);
   }
+  // copies past the range may still be landing: all done before the rings
+  // are reused below
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // partial sums and the low-rank tiles reuse the rings
+  float(*red)[kT][16][16] = reinterpret_cast<float(*)[kT][16][16]>(ring0);  // [kW]
+  float(*lred)[16][16] = reinterpret_cast<float(*)[16][16]>(ring1);          // [kT]
+  static_assert(sizeof(float) * kW * kT * 256 <= kW * kSlot, "partials fit the ring");
   // D[m][n]: lane -> n = lane & 15, m = 4 (lane >> 4) + v
 #pragma unroll
-  for (int i = 0; i < kTiles; ++i)
+  for (int i = 0; i < kT; ++i)
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[wave][i][4 * (lane >> 4) + v][lane & 15] = acc[i][v];
-  if constexpr (kLora) {
+  if (r > 0) {
     // L[m][n] = sum_j T[m][j] B[n][j] for tile i on wave i (mod kW), 4 ranks
     // per v_mfma_f32_16x16x4_f32: A = T (lane: token lane % 16, rank lane / 16),
     // B = B^T (lane: weight row lane % 16, same rank); rows past M or N and
     // ranks past r read as zero
-    for (int i = wave; i < kTiles; i += kW) {
+    for (int i = wave; i < kT; i += kW) {
       f32x4 l = f32x4{0.f, 0.f, 0.f, 0.f};
       const int m = lane & 15;
       const int64_t n = n0 + i * 16 + (lane & 15);
@@ -213,7 +358,7 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
     float y = red[0][i][m][nc];
 #pragma unroll
     for (int w2 = 1; w2 < kW; ++w2) y += red[w2][i][m][nc];  // in wave order
-    if constexpr (kLora) y = fmaf(scale, lred[i][m][nc], y);
+    if (r > 0) y = fmaf(scale, lred[i][m][nc], y);
     Y[m * N + n] = to16<kF16>(y);
   }
 }
@@ -232,33 +377,46 @@ constexpr int64_t kXpMinN = 4096;
 
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T, const uint16_t* B, int r,
                        float scale, uint16_t* Y, void* ws, hipStream_t stream, bool f16) {
+  // 32-bit buffer offsets: codes (with the last workgroup's rows past n)
+  // under 4 GiB
+  if ((w.n + 256) * (w.k / 2) >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
   u32x4* Xp = static_cast<u32x4*>(ws);
   const bool xp = M >= kXpMinM && w.n >= kXpMinN;
   if (xp) {
     const int64_t entries = cdiv(w.k, (int64_t)256) * 512;
     gemv_xperm_kernel<<<(unsigned)cdiv(entries, (int64_t)256), 256, 0, stream>>>(X, M, w.k, Xp, entries);
   }
-  // Rows and waves per workgroup, measured on the 70B-class shapes: 64 rows
-  // and 4 waves for 28672 rows (448 workgroups), 32 rows and 8 waves for
-  // 8192 rows (256 workgroups, each wave an eighth of the 28672-long
-  // contraction), 16 rows and 4 waves below.
-  const bool lora = r > 0;
-#define QLORA_GEMV3(NT, W, L, XP, H)                                                                           \
-  gemv_nf4_kernel<NT, W, L, XP, H><<<dim3((unsigned)cdiv(w.n, NT)), 64 * W, 0, stream>>>(                      \
+  // Tiles and waves per workgroup: two 16-row tiles where that still gives
+  // every CU a workgroup, else one; four waves (two workgroups per CU) where
+  // there are at least two workgroups per CU, else eight (one per CU, the
+  // contraction split eight ways).
+  const int64_t t2 = cdiv(w.n, (int64_t)32);
+  const int kt = t2 >= 256 ? 2 : 1;
+  const int64_t wgs = kt == 2 ? t2 : cdiv(w.n, (int64_t)16);
+  const int kw = kt == 2 && wgs >= 512 ? 4 : 8;
+#define QLORA_GEMV4(KT, W, XP, H, F)                                                                           \
+  gemv_nf4_kernel<KT, W, XP, H, F><<<dim3((unsigned)wgs), 64 * W, 0, stream>>>(                                \
       w.codes, w.code8, w.s2, w.mean, w.codebook, w.s2_bf16, w.n, w.k, X, Xp, M, T, B, r, scale, Y)
-#define QLORA_GEMV2(NT, W, L, XP) \
-  if (f16) QLORA_GEMV3(NT, W, L, XP, true); else QLORA_GEMV3(NT, W, L, XP, false);
-#define QLORA_GEMV(NT, W)                                                   \
-  {                                                                         \
-    if (lora) { if (xp) { QLORA_GEMV2(NT, W, true, true) } else { QLORA_GEMV2(NT, W, true, false) } } \
-    else { if (xp) { QLORA_GEMV2(NT, W, false, true) } else { QLORA_GEMV2(NT, W, false, false) } }    \
+#define QLORA_GEMV3(KT, W, XP, H)          \
+  {                                        \
+    if (form == 0) QLORA_GEMV4(KT, W, XP, H, 0); \
+    else if (form == 1) QLORA_GEMV4(KT, W, XP, H, 1); \
+    else QLORA_GEMV4(KT, W, XP, H, 2);     \
   }
-  if (w.n / 64 >= 448) QLORA_GEMV(64, 4)
-  else if (w.n / 32 >= 256) QLORA_GEMV(32, 8)
-  else QLORA_GEMV(16, 4)
+#define QLORA_GEMV2(KT, W, XP) \
+  if (f16) QLORA_GEMV3(KT, W, XP, true) else QLORA_GEMV3(KT, W, XP, false)
+#define QLORA_GEMV(KT, W)                                                   \
+  {                                                                         \
+    if (xp) { QLORA_GEMV2(KT, W, true) } else { QLORA_GEMV2(KT, W, false) } \
+  }
+  const int form = w.code8 ? 0 : (w.s2_bf16 ? 2 : 1);
+  if (kt == 2) {
+    if (kw == 4) QLORA_GEMV(2, 4) else QLORA_GEMV(2, 8)
+  } else QLORA_GEMV(1, 8)
 #undef QLORA_GEMV
 #undef QLORA_GEMV2
 #undef QLORA_GEMV3
+#undef QLORA_GEMV4
   return hipGetLastError();
 }
 
