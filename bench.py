@@ -192,7 +192,10 @@ class LinearPlan:
         if self.path_fwd == q.PATH_EXPANDED:
             self.Fw = buf("Fw", (q.nf4_expand_bytes(N, K, r, False) // 2,), torch.bfloat16)
         if backward and self.path_bwd == q.PATH_EXPANDED:
-            self.Fx = buf("Fx", (q.nf4_expand_bytes(N, K, r, True) // 2,), torch.bfloat16)
+            # dX operand: contraction-major (as the layer call builds it) when
+            # N % 64 == 0, else transposed
+            self.dx_mode = 2 if N % 64 == 0 else 1
+            self.Fx = buf("Fx", (q.nf4_expand_bytes(N, K, r, self.dx_mode) // 2,), torch.bfloat16)
         if self.path_fwd == q.PATH_GEMV:
             self.fwd.append(("lowrank_project_T", 2 * M * K * r,
                              q.Call("qlora_lowrank_project", P(self.X), M, K, P(self.A), 0, r, self.s, P(self.T), None,
@@ -230,11 +233,11 @@ class LinearPlan:
                                         P(self.dX), st, keep=(self.wst,))))
             else:
                 self.bwd.append(("nf4_expand_dx", 0,
-                                 q.Call("qlora_nf4_expand", wref, P(self.A), r, 1, P(self.Fx), self.Fx.numel() * 2, st,
-                                        keep=(self.wst,))))
+                                 q.Call("qlora_nf4_expand", wref, P(self.A), r, self.dx_mode, P(self.Fx),
+                                        self.Fx.numel() * 2, st, keep=(self.wst,))))
                 self.bwd.append(("bf16_gemm_dx", 2 * M * N * K + 2 * M * K * r,
-                                 q.Call("qlora_bf16_gemm", P(self.dY), M, N, P(self.US), r, P(self.Fx), K, P(self.dX),
-                                        ws, wsn, st)))
+                                 q.Call("qlora_bf16_gemm_nn" if self.dx_mode == 2 else "qlora_bf16_gemm", P(self.dY),
+                                        M, N, P(self.US), r, P(self.Fx), K, P(self.dX), ws, wsn, st)))
             self.bwd.append(("lowrank_grad_dA", 2 * M * K * r,
                              q.Call("qlora_lowrank_grad", P(self.X), M, K, P(self.U), r, self.s, P(self.dA), 0, 0, ws,
                                     wsn, st)))

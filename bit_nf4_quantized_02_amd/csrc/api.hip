@@ -371,6 +371,7 @@ int qlora_linear_path(int64_t M, int64_t n, int64_t k, int r, int is_bwd) {
 
 size_t qlora_nf4_expand_bytes(int64_t n, int64_t k, int r, int transposed) {
   if (n < 1 || k < 1 || (k % QLORA_BLOCK) != 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (transposed == 2) return n % 64 == 0 ? expand_nn_bytes(n, k, r) : 0;
   if (transposed != 0 && transposed != 1) return 0;
   return expand_ws_bytes(n, k, r, transposed == 1);
 }
@@ -380,10 +381,14 @@ qlora_status qlora_nf4_expand(const qlora_nf4_weight* w, const void* lr, int r, 
   const qlora_status s = check_weight(w);
   if (s != QLORA_OK) return s;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
-  if (transposed != 0 && transposed != 1) return QLORA_ERR_INVALID_ARG;
+  if (transposed != 0 && transposed != 1 && transposed != 2) return QLORA_ERR_INVALID_ARG;
+  if (transposed == 2 && w->n % 64 != 0) return QLORA_ERR_SHAPE;
   if (!out || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
   if (r > 0 && (!lr || !aligned16(lr))) return QLORA_ERR_INVALID_ARG;
-  if (out_bytes < expand_ws_bytes(w->n, w->k, r, transposed == 1)) return QLORA_ERR_WORKSPACE;
+  if (out_bytes < qlora_nf4_expand_bytes(w->n, w->k, r, transposed)) return QLORA_ERR_WORKSPACE;
+  if (transposed == 2)
+    return hip_status(launch_expand_nn(view_of(w), static_cast<const uint16_t*>(lr), r, static_cast<uint16_t*>(out),
+                                       static_cast<hipStream_t>(stream)));
   return hip_status(launch_expand(view_of(w), static_cast<const uint16_t*>(lr), r, transposed == 1,
                                   static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
@@ -406,6 +411,24 @@ qlora_status qlora_bf16_gemm(const void* act, int64_t M, int64_t kc, const void*
                                      lora_extra_cols(r), static_cast<const uint16_t*>(F), nout,
                                      static_cast<uint16_t*>(out), need > 0 ? static_cast<float*>(ws) : nullptr,
                                      static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_bf16_gemm_nn(const void* act, int64_t M, int64_t kc, const void* split, int r, const void* F,
+                                int64_t nout, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || kc < 64 || (kc % 64) != 0 || nout < 8 || (nout % 8) != 0 || r < 0 || r > QLORA_MAX_RANK)
+    return QLORA_ERR_SHAPE;
+  if (M == 0) return QLORA_OK;
+  if (!act || !F || !out || !aligned16(act) || !aligned16(F) || !aligned16(out)) return QLORA_ERR_INVALID_ARG;
+  if (r > 0 && (!split || !aligned16(split))) return QLORA_ERR_INVALID_ARG;
+  const int xc = lora_extra_cols(r);
+  if (!gemm_bf16_offsets_fit(M, kc, xc, nout) || (kc + xc) * nout * 2 >= ((int64_t)1 << 32)) return QLORA_ERR_SHAPE;
+  const size_t need = gemm_bf16_ws_bytes(M, kc, xc, nout);
+  if (need > 0 && (!ws || !aligned16(ws) || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  const uint16_t* f = static_cast<const uint16_t*>(F);
+  return hip_status(launch_gemm_bf16_ext(static_cast<const uint16_t*>(act), M, kc, static_cast<const uint16_t*>(split),
+                                         xc, f, nout, f + kc * nout, nout, nout, static_cast<uint16_t*>(out),
+                                         need > 0 ? static_cast<float*>(ws) : nullptr,
+                                         static_cast<hipStream_t>(stream), nullptr, 1.0f, false, /*nn=*/true));
 }
 
 size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r) {
@@ -531,7 +554,20 @@ static qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const void* X, co
   if (e == hipSuccess && dX && gemv) {
     e = launch_gemv_dx(v, dy, M, o.U, a, r, scale, static_cast<uint16_t*>(dX), o.part, st, dmask, keep_scale);
   } else if (e == hipSuccess && dX) {
-    if (f16 || path_of(M, w->n, w->k, r, true) == QLORA_PATH_EXPANDED) {
+    if (!f16 && dmask == nullptr && path_of(M, w->n, w->k, r, true) == QLORA_PATH_EXPANDED &&
+        w->n % 64 == 0) {
+      // W' expanded as the forward does ([n, k], contraction-major for dX)
+      // and read by the GEMM's NN form through transposing LDS reads, the
+      // low-rank rows [A ; A ; 0] after it (qlora_nf4_expand with
+      // transposed = 2, then qlora_bf16_gemm_nn). This takes the transposed
+      // expansion's workspace: (n + xc) k = k (np + xc) for n % 64 == 0.
+      const int xc = lora_extra_cols(r);
+      uint16_t* const fl = o.F + (size_t)w->n * w->k;
+      e = launch_expand_nn(v, a, r, o.F, st);
+      if (e == hipSuccess)
+        e = launch_gemm_bf16_ext(dy, M, w->n, r > 0 ? o.US : nullptr, xc, o.F, w->k, fl, w->k, w->k,
+                                 static_cast<uint16_t*>(dX), o.part, st, nullptr, 1.0f, false, /*nn=*/true);
+    } else if (f16 || path_of(M, w->n, w->k, r, true) == QLORA_PATH_EXPANDED) {
       e = launch_expand(v, a, r, true, o.F, st, f16);
       if (e == hipSuccess)
         e = launch_gemm_bf16(dy, M, w->n, r > 0 ? o.US : nullptr, lora_extra_cols(r), o.F, w->k,

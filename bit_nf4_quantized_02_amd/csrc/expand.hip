@@ -263,4 +263,14 @@ hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool trans
   return hipGetLastError();
 }
 
+size_t expand_nn_bytes(int64_t n, int64_t k, int r) {
+  return align256((size_t)(n + lora_extra_cols(r)) * (size_t)k * 2);
+}
+
+hipError_t launch_expand_nn(const Nf4View& w, const uint16_t* A, int r, uint16_t* out, hipStream_t stream) {
+  hipError_t e = launch_expand(w, nullptr, 0, false, out, stream);
+  if (e == hipSuccess && r > 0) e = launch_lowrank_cols(A, r, w.k, out + w.n * w.k, stream);
+  return e;
+}
+
 }  // namespace qlora

@@ -573,7 +573,10 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
   if (nn) {
     // the weight operand stored [contraction][output] (bf16 base, dX)
     if (mask != nullptr || f16) return hipErrorInvalidValue;
-    gemm_bf16_kernel<false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
+    if ((M * kc + kc * a.ldf) * 2 > kPrioOperandBytes)
+      gemm_bf16_kernel<false, false, true, true><<<grid, kThreads, 0, stream>>>(a);
+    else
+      gemm_bf16_kernel<false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
   } else if (f16) {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);

@@ -94,6 +94,11 @@ int64_t expand_pad_rows(int64_t n);
 size_t expand_ws_bytes(int64_t n, int64_t k, int r, bool transposed);
 hipError_t launch_expand(const Nf4View& w, const uint16_t* lr, int r, bool transposed, uint16_t* out,
                          hipStream_t stream, bool f16 = false);
+// The dX operand in contraction-major form for the GEMM's NN form (n % 64
+// == 0): out [n + xc, k], rows 0 .. n-1 W' as the forward expansion writes
+// them, then the low-rank rows [A ; A ; 0].
+size_t expand_nn_bytes(int64_t n, int64_t k, int r);
+hipError_t launch_expand_nn(const Nf4View& w, const uint16_t* A, int r, uint16_t* out, hipStream_t stream);
 
 // [n, lora_extra_cols(r)] rows [B | B | 0] (bf16), the low-rank operand of
 // the forward GEMM when the weight operand is a separate matrix.

@@ -86,6 +86,7 @@ _SIGS = {
     "qlora_nf4_expand": (_int, [_W, _vp, _int, _int, _vp, _sz, _vp]),
     "qlora_bf16_gemm_workspace_bytes": (_sz, [_i64, _i64, _int, _i64]),
     "qlora_bf16_gemm": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "qlora_bf16_gemm_nn": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _i64, _vp, _vp, _sz, _vp]),
     "qlora_lowrank_grad_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "qlora_lowrank_grad": (_int, [_vp, _i64, _i64, _vp, _int, _f, _vp, _int, _int, _vp, _sz, _vp]),
     "qlora_silu_mul_fwd": (_int, [_vp, _vp, _vp, _i64, _vp]),
@@ -530,17 +531,21 @@ def linear_path(M: int, n: int, k: int, r: int, is_bwd: bool) -> int:
     return p
 
 
-def nf4_expand_bytes(n: int, k: int, r: int, transposed: bool) -> int:
+def nf4_expand_bytes(n: int, k: int, r: int, transposed: int) -> int:
     return int(_lib.qlora_nf4_expand_bytes(n, k, r, int(transposed)))
 
 
-def nf4_expand(w: NF4Weight, lr: torch.Tensor | None, r: int, transposed: bool, out: torch.Tensor | None = None,
+def nf4_expand(w: NF4Weight, lr: torch.Tensor | None, r: int, transposed: int, out: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
-    """Expanded bf16 operand: [n, k + xc] (forward, lr = B) or [k, np + xc]
-    (transposed, for dX, lr = A); returned as a 2-D bf16 tensor."""
+    """Expanded bf16 operand: [n, k + xc] (transposed = 0, forward, lr = B),
+    [k, np + xc] (1, for dX, lr = A) or [n + xc, k] (2, contraction-major for
+    dX, n % 64 == 0, lr = A); returned as a 2-D bf16 tensor."""
     xc = lowrank_split_cols(r)
-    if transposed:
+    transposed = int(transposed)
+    if transposed == 1:
         rows, cols = w.k, ((w.n + 63) // 64) * 64 + xc
+    elif transposed == 2:
+        rows, cols = w.n + xc, w.k
     else:
         rows, cols = w.n, w.k + xc
     nbytes = nf4_expand_bytes(w.n, w.k, r, transposed)
@@ -550,6 +555,21 @@ def nf4_expand(w: NF4Weight, lr: torch.Tensor | None, r: int, transposed: bool, 
     _check(_lib.qlora_nf4_expand(ctypes.byref(st), _ptr(lr), r, int(transposed), _ptr(out), out.numel() * 2,
                                  _stream(stream)), "qlora_nf4_expand")
     return out.view(-1)[: rows * cols].view(rows, cols)
+
+
+def bf16_gemm_nn(act: torch.Tensor, split: torch.Tensor | None, r: int, F: torch.Tensor, nout: int,
+                 out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """out = RN_bf16(act F[:kc] + split F[kc:]) over the contraction-major
+    operand of nf4_expand(..., transposed=2)."""
+    M, kc = act.shape
+    if out is None:
+        out = torch.empty((M, nout), dtype=torch.bfloat16, device=act.device)
+    if ws is None:
+        ws = _bytes(bf16_gemm_workspace_bytes(M, kc, r, nout), act.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.qlora_bf16_gemm_nn(_ptr(act), M, kc, _ptr(split), r, _ptr(F), nout, _ptr(out), _ptr(ws), nbytes,
+                                   _stream(stream)), "qlora_bf16_gemm_nn")
+    return out
 
 
 def bf16_gemm_workspace_bytes(M: int, kc: int, r: int, nout: int) -> int:

@@ -403,7 +403,9 @@ qlora_status qlora_nf4_gemv_dx(const qlora_nf4_weight *w, const void *dY, int64_
  *                        every operand of the bf16 GEMM under 4 GiB):
  *                        qlora_nf4_expand once into workspace, then
  *                        qlora_bf16_gemm (each weight expanded once per pass
- *                        instead of M / 256 times).
+ *                        instead of M / 256 times); for dX with n % 64 == 0
+ *                        (bf16, no dropout) qlora_nf4_expand with
+ *                        transposed = 2, then qlora_bf16_gemm_nn.
  * r is the LoRA rank. Returns -1 on bad arguments.
  */
 #define QLORA_PATH_GEMV 0
@@ -425,6 +427,11 @@ size_t qlora_nf4_expand_bytes(int64_t n, int64_t k, int r, int transposed);
  *   transposed = 1 (dX): np = n rounded up to 64, out [k, np + xc],
  *       out[c, i] = W'[i, c] (0 for n <= i < np),
  *       out[c, np + j] = A[j mod r, c] for j < 2r, else 0;  lr = A [r, k].
+ *   transposed = 2 (dX, contraction-major operand of qlora_bf16_gemm_nn;
+ *       n % 64 == 0, else SHAPE): out [n + xc, k], out[i, c] = W'[i, c],
+ *       out[n + j, c] = A[j mod r, c] for j < 2r, else 0;  lr = A [r, k].
+ *       The W' rows are the forward's layout, which expands with 16-byte
+ *       stores along rows instead of a transpose through on-chip memory.
  * W' values are bit-identical to qlora_dequant's. out (device) must hold
  * qlora_nf4_expand_bytes(n, k, r, transposed) bytes (out_bytes).
  * Errors: INVALID_ARG, SHAPE, WORKSPACE (out_bytes too small), HIP.
@@ -454,6 +461,24 @@ size_t qlora_bf16_gemm_workspace_bytes(int64_t M, int64_t kc, int r, int64_t nou
  */
 qlora_status qlora_bf16_gemm(const void *act, int64_t M, int64_t kc, const void *split, int r, const void *F,
                              int64_t nout, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The same product over a contraction-major operand F from qlora_nf4_expand
+ * with transposed = 2 [QQ three-piece summary, piece 2; the dX product of the
+ * backward pass]:
+ *   out[m, j] = RN_bf16( sum_{c < kc} act[m, c] F[c, j] + sum_x split[m, x] F[kc + x, j] )
+ * act (device) [M, kc] bf16 (dY, kc = n, kc % 64 == 0); split (device)
+ * [M, xc] bf16 from qlora_lowrank_project (ignored for r = 0); F (device)
+ * [kc + xc, nout] (nout = k, nout % 8 == 0); out (device) [M, nout] bf16.
+ * Workspace and splitting as qlora_bf16_gemm
+ * (qlora_bf16_gemm_workspace_bytes(M, kc, r, nout)). Each operand must be
+ * smaller than 4 GiB. Deterministic; may differ in the last bits from
+ * qlora_bf16_gemm over the transposed operand (a different summation order
+ * inside each 64-wide step).
+ * Errors: INVALID_ARG, SHAPE, WORKSPACE, HIP.
+ */
+qlora_status qlora_bf16_gemm_nn(const void *act, int64_t M, int64_t kc, const void *split, int r, const void *F,
+                                int64_t nout, void *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes of qlora_lowrank_grad (0 on bad arguments). */
 size_t qlora_lowrank_grad_workspace_bytes(int64_t M, int64_t C, int r);

@@ -187,6 +187,11 @@ def test_path_choice_and_expanded_sizes(q):
     assert q.nf4_expand_bytes(100, 256, 16, True) == r256(256 * (128 + 64) * 2)
     assert q.nf4_expand_bytes(100, 256, 0, True) == r256(256 * 128 * 2)
     assert q.nf4_expand_bytes(100, 255, 0, True) == 0
+    # contraction-major dX operand: [n + xc, k], n % 64 == 0 only
+    assert q.nf4_expand_bytes(4096, 4096, 16, 2) == r256((4096 + 64) * 4096 * 2)
+    assert q.nf4_expand_bytes(4096, 4096, 0, 2) == r256(4096 * 4096 * 2)
+    assert q.nf4_expand_bytes(100, 256, 16, 2) == 0
+    assert q.nf4_expand_bytes(64, 256, 16, 3) == 0
     # the layer workspace grows by the expanded operand exactly when that path is taken
     fw_small = q.linear_workspace_bytes(64, 4096, 4096, 16, False)
     fw_big = q.linear_workspace_bytes(big, 4096, 4096, 16, False)
@@ -199,7 +204,9 @@ def test_expand_and_bf16_gemm_errors(q):
     p = ctypes.c_void_p(1 << 24)
     need = q.nf4_expand_bytes(64, 128, 8, False)
     assert lib.qlora_nf4_expand(ctypes.byref(W), p, 8, 0, p, need - 1, None) == -4
-    assert lib.qlora_nf4_expand(ctypes.byref(W), p, 8, 2, p, need, None) == -1
+    assert lib.qlora_nf4_expand(ctypes.byref(W), p, 8, 3, p, need, None) == -1
+    need2 = q.nf4_expand_bytes(64, 128, 8, 2)
+    assert lib.qlora_nf4_expand(ctypes.byref(W), p, 8, 2, p, need2 - 1, None) == -4
     assert lib.qlora_nf4_expand(ctypes.byref(W), None, 8, 0, p, need, None) == -1
     assert lib.qlora_nf4_expand(ctypes.byref(W), p, q.MAX_RANK + 1, 0, p, 1 << 30, None) == -2
     assert lib.qlora_bf16_gemm(p, 64, 100, p, 8, p, 64, p, None, 0, None) == -2      # kc % 8 != 0
@@ -211,6 +218,12 @@ def test_expand_and_bf16_gemm_errors(q):
     assert lib.qlora_bf16_gemm(p, 256, 4096, p, 8, p, 256, p, None, 0, None) == -4
     assert lib.qlora_bf16_gemm(p, 256, 4096, p, 8, p, 256, p, p, need - 1, None) == -4
     assert q.bf16_gemm_workspace_bytes(4096, 4096, 16, 4096) == 0   # 256 tiles: whole contraction per tile
+    # the contraction-major form: kc % 64 == 0 and nout % 8 == 0
+    assert lib.qlora_bf16_gemm_nn(p, 64, 96, p, 8, p, 64, p, None, 0, None) == -2     # kc % 64 != 0
+    assert lib.qlora_bf16_gemm_nn(p, 64, 128, p, 8, p, 100, p, None, 0, None) == -2   # nout % 8 != 0
+    assert lib.qlora_bf16_gemm_nn(p, 64, 128, None, 8, p, 64, p, None, 0, None) == -1  # r > 0 needs split
+    assert lib.qlora_bf16_gemm_nn(p, 0, 128, None, 8, p, 64, p, None, 0, None) == 0    # M = 0: no-op
+    assert lib.qlora_bf16_gemm_nn(p, 256, 4096, p, 8, p, 256, p, None, 0, None) == -4  # split needs workspace
 
 
 def test_expanded_path_needs_operands_under_4gib(q):

@@ -2,9 +2,11 @@
 
 * The expanded operands are compared bit for bit with the oracle's bf16
   expansion of its own encoding (forward [n, k + xc]; dX transposed
-  [k, np + xc]), including the appended LoRA columns, the zero padding and
-  weights whose row count is not a multiple of 64 or 256.
-* qlora_bf16_gemm over those operands, and qlora_linear_fwd / _bwd at token
+  [k, np + xc]; dX contraction-major [n + xc, k]), including the appended
+  LoRA columns / rows, the zero padding and weights whose row count is not a
+  multiple of 64 or 256.
+* qlora_bf16_gemm and qlora_bf16_gemm_nn over those operands, and
+  qlora_linear_fwd / _bwd at token
   counts that select the expanded path, are compared with the fp64 oracle
   (relative Frobenius error <= 2e-3 and the element-wise bound for Y and
   dX, 1e-5 for the fp32 adapter gradients), on shapes with ragged M, N and K
@@ -61,6 +63,30 @@ def test_expanded_operands_bitwise(q, n, k, r):
         assert np.array_equal(fx[:, np_ + j], want_x), j
 
 
+@pytest.mark.parametrize("n,k,r", [(256, 192, 8), (640, 320, 64), (64, 64, 0), (128, 128, 128), (192, 64, 3)])
+def test_contraction_major_operand_bitwise(q, n, k, r):
+    """qlora_nf4_expand with transposed = 2: W' rows as the forward's, then
+    [A ; A ; 0]; n % 64 != 0 is refused."""
+    say(f"case: expand nn n={n} k={k} r={r}")
+    W = synth.weight_bf16(n, k, 0.02, 56, n, k)
+    A = synth.lora_A(max(r, 1), k, 56, n, 1)[:r].contiguous()
+    gw = q.quantize_nf4(W.cuda())
+    Fn = q.nf4_expand(gw, A.cuda() if r else None, r, transposed=2)
+    torch.cuda.synchronize()
+    wb = oracle_encode(W).dequant_bits()
+    xc = q.lowrank_split_cols(r)
+    fn = _bits(Fn)
+    assert fn.shape == (n + xc, k)
+    assert np.array_equal(fn[:n], wb)
+    ab = _bits(A)
+    for j in range(xc):
+        want = ab[j % r, :] if j < 2 * r else np.zeros(k, np.uint16)
+        assert np.array_equal(fn[n + j], want), j
+    odd = q.quantize_nf4(synth.weight_bf16(100, 64, 0.02, 57, 100, 64).cuda())
+    with pytest.raises(q.QLoraError):
+        q.nf4_expand(odd, None, 0, transposed=2)
+
+
 @pytest.mark.parametrize("m,n,k,r", [(300, 200, 192, 8), (520, 264, 640, 16), (17, 72, 64, 1), (256, 512, 256, 0),
                                      (700, 96, 512, 64),
                                      # few output tiles, long contraction: split-K forward (S = 4) / dX (S = 4,
@@ -68,7 +94,9 @@ def test_expanded_operands_bitwise(q, n, k, r):
                                      (300, 520, 2048, 16), (300, 2056, 576, 16),
                                      # a last wave of few tiles split along the contraction: forward 272 tiles
                                      # (16 split in 2), ragged 264 tiles (8 split in 4, n % 256 = 8, M % 256 = 208)
-                                     (4352, 4096, 2048, 16), (2000, 8200, 4160, 8)])
+                                     (4352, 4096, 2048, 16), (2000, 8200, 4160, 8),
+                                     # dX in the contraction-major form: split-K (6 output tiles), rank 64
+                                     (300, 2048, 576, 16), (520, 640, 320, 64)])
 def test_bf16_gemm_building_blocks(q, m, n, k, r):
     """T/U split + expansion + bf16 GEMM, forward and dX, against the oracle."""
     say(f"case: bf16 gemm M={m} N={n} K={k} r={r}")
@@ -94,9 +122,16 @@ def test_bf16_gemm_building_blocks(q, m, n, k, r):
     dXr, _, _, _ = olin.linear_bwd(Xo, Wd, Ao, Bo, s, dYo)
     assert_fwd("Y", Y, Xo, Wd, Ao, Bo, s, Yr)
     assert_dx("dX", dX, dYo, Wd, Ao, Bo, s, dXr)
+    if n % 64 == 0:
+        Fn = q.nf4_expand(gw, A, r, transposed=2)
+        dXn = q.bf16_gemm_nn(dY, US, r, Fn, k)
+        torch.cuda.synchronize()
+        assert_dx("dX nn", dXn, dYo, Wd, Ao, Bo, s, dXr)
 
 
-@pytest.mark.parametrize("m,n,k,r", [(1030, 520, 384, 16), (1024, 100, 256, 8), (1300, 264, 192, 64), (128, 72, 64, 1)])
+@pytest.mark.parametrize("m,n,k,r", [(1030, 520, 384, 16), (1024, 100, 256, 8), (1300, 264, 192, 64), (128, 72, 64, 1),
+                                     # n % 64 == 0: dX through the contraction-major expansion
+                                     (1030, 512, 384, 16), (1300, 256, 192, 64), (4100, 1024, 320, 8)])
 def test_linear_at_expanded_sizes(q, m, n, k, r):
     """qlora_linear_fwd/bwd where the path is the expanded one (n % 8 != 0
     keeps dX on the fused kernel)."""
