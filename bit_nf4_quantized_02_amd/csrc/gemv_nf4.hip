@@ -66,21 +66,6 @@ constexpr int kRingDepth = 3;  // chunks of codes per wave: one worked on, two i
 // (lgkmcnt <= n; vmcnt and expcnt left at their maxima)
 constexpr int lgkm_wait(int n) { return 0xC07F | (n << 8); }
 
-// Eight codes of one word -> four bf16 pairs through the replicated table
-// (lane_off = 8 * (lane % kLutCopies)); products and rounding are those of
-// dequant8.
-template <bool kF16>
-__device__ __forceinline__ u32x4 dequant8_rep(uint32_t word, const char* lut, uint32_t lane_off, float cp) {
-  u32x4 out;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t b = (word >> (8 * p)) & 0xFFu;
-    const float2 l = *reinterpret_cast<const float2*>(lut + ((b * (kLutCopies * 8)) | lane_off));
-    out[p] = pack2<kF16>(nf4_scaled(l.x, cp), nf4_scaled(l.y, cp));
-  }
-  return out;
-}
-
 // Swizzle of a 128-byte code line in LDS: row r of a 16-row tile keeps its
 // 16-byte segment g at position g ^ sw(r). The 8 (or 16) lanes that read one
 // segment of 8 (16) consecutive rows in one LDS cycle then hit distinct banks
