@@ -177,19 +177,40 @@ __global__ __launch_bounds__(256) void gemv_dx_finalize_kernel(const float* __re
   const int64_t groups = k / 4;
   if (g >= M * groups) return;
   const int64_t m = g / groups, j = (g % groups) * 4;
+  // loads issued eight at a time (clamped to the last valid index, the
+  // extra values unused), sums still taken in range / rank order
   float4 s = *reinterpret_cast<const float4*>(part + m * k + j);
-  for (int p = 1; p < splits; ++p) {
-    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)p * 16 + m) * k + j);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  for (int p0 = 1; p0 < splits; p0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int p = p0 + e < splits ? p0 + e : splits - 1;
+      v[e] = *reinterpret_cast<const float4*>(part + ((int64_t)p * 16 + m) * k + j);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (p0 + e < splits) {
+        s.x += v[e].x; s.y += v[e].y; s.z += v[e].z; s.w += v[e].w;
+      }
   }
   float l[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < r; ++t) {
-    const float u = U[m * r + t];
-    const uint2 a = *reinterpret_cast<const uint2*>(A + (int64_t)t * k + j);
-    l[0] = fmaf(u, bf16_bits_to_f32(a.x & 0xFFFFu), l[0]);
-    l[1] = fmaf(u, bf16_bits_to_f32(a.x >> 16), l[1]);
-    l[2] = fmaf(u, bf16_bits_to_f32(a.y & 0xFFFFu), l[2]);
-    l[3] = fmaf(u, bf16_bits_to_f32(a.y >> 16), l[3]);
+  for (int t0 = 0; t0 < r; t0 += 8) {
+    float u[8];
+    uint2 a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = t0 + e < r ? t0 + e : r - 1;
+      u[e] = U[m * r + t];
+      a[e] = *reinterpret_cast<const uint2*>(A + (int64_t)t * k + j);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (t0 + e < r) {
+        l[0] = fmaf(u[e], bf16_bits_to_f32(a[e].x & 0xFFFFu), l[0]);
+        l[1] = fmaf(u[e], bf16_bits_to_f32(a[e].x >> 16), l[1]);
+        l[2] = fmaf(u[e], bf16_bits_to_f32(a[e].y & 0xFFFFu), l[2]);
+        l[3] = fmaf(u[e], bf16_bits_to_f32(a[e].y >> 16), l[3]);
+      }
   }
   float f[4];
   if (mask != nullptr) {
