@@ -51,14 +51,15 @@ bool small_m(int64_t M) { return M <= 16; }
 // fp16 compute (the ablation) runs the GEMV for M <= 16 in the forward and the
 // expanded path otherwise; -1 where that path cannot take the shape.
 int path_of_f16(int64_t M, int64_t n, int64_t k, int r, bool bwd) {
-  if (!bwd && small_m(M)) return QLORA_PATH_GEMV;
+  if (!bwd && small_m(M)) return gemv_fits(n, k) ? QLORA_PATH_GEMV : -1;
   const int xc = lora_extra_cols(r);
   const bool fits = bwd ? gemm_bf16_offsets_fit(M, n, xc, k) : gemm_bf16_offsets_fit(M, k, xc, n);
   return fits && (!bwd || n % 8 == 0) ? QLORA_PATH_EXPANDED : -1;
 }
 
 int path_of(int64_t M, int64_t n, int64_t k, int r, bool bwd) {
-  if (small_m(M)) return QLORA_PATH_GEMV;  // forward GEMV; backward: dX GEMV
+  // forward GEMV (codes under 4 GiB, else the fused kernel); backward: dX GEMV
+  if (small_m(M) && (bwd || gemv_fits(n, k))) return QLORA_PATH_GEMV;
   const int xc = lora_extra_cols(r);
   const bool fits = bwd ? gemm_bf16_offsets_fit(M, n, xc, k) : gemm_bf16_offsets_fit(M, k, xc, n);
   if (M >= QLORA_EXPAND_MIN_M && fits && (!bwd || n % 8 == 0)) return QLORA_PATH_EXPANDED;
@@ -335,7 +336,7 @@ qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight* w, const void* X, int64_
                                 int r, float scale, void* Y, void* ws, size_t ws_bytes, void* stream) {
   const qlora_status s = check_weight(w);
   if (s != QLORA_OK) return s;
-  if (M < 0 || M > 16 || r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_SHAPE;
+  if (M < 0 || M > 16 || r < 0 || r > QLORA_MAX_RANK || !gemv_fits(w->n, w->k)) return QLORA_ERR_SHAPE;
   if (M == 0) return QLORA_OK;
   if (!X || !Y || !aligned16(X) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
   if (r > 0 && (!T || !B || !aligned16(T) || !aligned16(B))) return QLORA_ERR_INVALID_ARG;

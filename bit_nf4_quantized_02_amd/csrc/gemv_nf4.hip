@@ -350,6 +350,8 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
 
 }  // namespace
 
+bool gemv_fits(int64_t n, int64_t k) { return (n + 256) * (k / 2) < ((int64_t)1 << 32); }
+
 size_t gemv_ws_bytes(int64_t k) { return align256((size_t)cdiv(k, 256) * 512 * 16); }
 
 // Token counts from which the activations are first rewritten in operand
@@ -362,9 +364,7 @@ constexpr int64_t kXpMinN = 4096;
 
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T, const uint16_t* B, int r,
                        float scale, uint16_t* Y, void* ws, hipStream_t stream, bool f16) {
-  // 32-bit buffer offsets: codes (with the last workgroup's rows past n)
-  // under 4 GiB
-  if ((w.n + 256) * (w.k / 2) >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  if (!gemv_fits(w.n, w.k)) return hipErrorInvalidValue;
   u32x4* Xp = static_cast<u32x4*>(ws);
   const bool xp = M >= kXpMinM && w.n >= kXpMinN;
   if (xp) {

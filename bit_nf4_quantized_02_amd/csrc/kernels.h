@@ -147,6 +147,9 @@ hipError_t launch_merge(const Nf4View* w, const uint16_t* Wm, int64_t n, int64_t
 // Small-M dequant-GEMV: Y = RN_bf16(X W'^T + scale * T B^T), M <= 16. ws:
 // gemv_ws_bytes(k) bytes for the activations in operand order.
 size_t gemv_ws_bytes(int64_t k);
+// The GEMV addresses the codes with 32-bit buffer offsets: n k / 2 bytes
+// (plus one workgroup's rows past n) under 4 GiB.
+bool gemv_fits(int64_t n, int64_t k);
 hipError_t launch_gemv(const Nf4View& w, const uint16_t* X, int64_t M, const float* T,
                        const uint16_t* B, int r, float scale, uint16_t* Y, void* ws, hipStream_t stream,
                        bool f16 = false);

@@ -365,9 +365,10 @@ size_t qlora_nf4_gemv_workspace_bytes(int64_t k);
 /*
  * Bandwidth-oriented forward for M <= 16 tokens:
  *   Y = RN_bf16( X W'^T + scale T B^T ),   T (device, [M, r] fp32) = X A^T.
- * One pass over the packed codes. ws (device, 16-byte aligned) holds
- * qlora_nf4_gemv_workspace_bytes(k) bytes. Errors: INVALID_ARG, SHAPE
- * (M > 16), WORKSPACE, HIP.
+ * One pass over the packed codes, addressed with 32-bit offsets: the codes
+ * plus 256 rows' worth ((n + 256) k / 2 bytes) must stay under 4 GiB. ws
+ * (device, 16-byte aligned) holds qlora_nf4_gemv_workspace_bytes(k) bytes.
+ * Errors: INVALID_ARG, SHAPE (M > 16, or the codes too large), WORKSPACE, HIP.
  */
 qlora_status qlora_nf4_gemv_fwd(const qlora_nf4_weight *w, const void *X, int64_t M, const float *T,
                                 const void *B, int r, float scale, void *Y, void *ws, size_t ws_bytes,
@@ -394,7 +395,8 @@ qlora_status qlora_nf4_gemv_dx(const qlora_nf4_weight *w, const void *dY, int64_
 /*
  * Which kernels a pass uses at this size; qlora_linear_fwd (is_bwd = 0) and
  * qlora_linear_bwd (is_bwd = 1, the dX product) make exactly this choice:
- *   QLORA_PATH_GEMV      M <= 16: qlora_nf4_gemv_fwd, or for dX
+ *   QLORA_PATH_GEMV      M <= 16: qlora_nf4_gemv_fwd (codes within its
+ *                        4 GiB limit; else the forward is FUSED), or for dX
  *                        qlora_nf4_gemv_dx (one pass over the packed codes,
  *                        bandwidth-bound);
  *   QLORA_PATH_FUSED     qlora_nf4_gemm_fwd / qlora_nf4_gemm_dx (each 64-block

@@ -177,6 +177,10 @@ def test_path_choice_and_expanded_sizes(q):
     assert q.linear_path(big, 4096, 4096, 16, True) == q.PATH_EXPANDED
     # dX over unaligned dY rows (n % 8 != 0) stays on the fused kernel
     assert q.linear_path(big, 100, 4096, 16, True) == q.PATH_FUSED
+    # the GEMV's 32-bit code offsets: a forward whose codes reach 4 GiB runs fused
+    assert q.linear_path(16, 8192, 8192, 16, False) == q.PATH_GEMV
+    assert q.linear_path(16, 1 << 20, 8192, 16, False) == q.PATH_FUSED
+    assert q.linear_path(16, 1 << 20, 8192, 16, True) == q.PATH_GEMV
     assert q.linear_path(big, 100, 4096, 16, False) == q.PATH_EXPANDED
     with pytest.raises(q.QLoraError):
         q.linear_path(big, 64, 100, 16, False)
