@@ -233,8 +233,8 @@ __global__ __launch_bounds__((rowdot_threads<kRP, kMR>())) __attribute__((amdgpu
       }
     }
   };
+  // the batch's MFMAs (a batch that reaches past w1 is clipped first)
   auto compute = [&](Batch& bt) {
-    if constexpr (kFast) clip(bt);
     bf16x8 b[kU][kTiles];
     if constexpr (kQL == 0) {
 #pragma unroll
@@ -279,21 +279,34 @@ __global__ __launch_bounds__((rowdot_threads<kRP, kMR>())) __attribute__((amdgpu
       compute(b0);
     }
   } else if (w0 < w1) {
-    // a ring of kD batches: the loads of batch j + kD - 1 are issued before
-    // batch j is multiplied (past w1 the loads read nothing: zeros)
+    // A ring of kD batches: the loads of batch j + kD - 1 are issued before
+    // batch j is multiplied. Only the wave's last batch can reach past w1, so
+    // the loop takes whole groups of kD batches that end before it, with no
+    // exit and no clip inside (an exit inside the unrolled group made the
+    // compiler wait for every load in flight at the back edge, which emptied
+    // the ring every kD batches); the last 1..kD batches follow the loop.
+    // Loads past w1 read clamped in-range addresses (kFast) or zeros.
     constexpr int kD = Cfg::kDepth;
+    const int64_t nb = cdiv(w1 - w0, cstride);  // >= 1, wave-uniform
     Batch bt[kD];
 #pragma unroll
     for (int i = 0; i < kD - 1; ++i) load(w0 + i * cstride, bt[i]);
-    for (int64_t c = w0; c < w1; c += kD * cstride) {
+    int64_t j = 0;
+    for (; j + kD < nb; j += kD) {
 #pragma unroll
-      for (int j = 0; j < kD; ++j) {
-        load(c + (j + kD - 1) * cstride, bt[(j + kD - 1) % kD]);
+      for (int i = 0; i < kD; ++i) {
+        load(w0 + (j + i + kD - 1) * cstride, bt[(i + kD - 1) % kD]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(bt[j]);
-        if (c + (j + 1) * cstride >= w1) break;
+        compute(bt[i]);
       }
     }
+    load(w0 + (j + kD - 1) * cstride, bt[kD - 1]);
+#pragma unroll
+    for (int i = 0; i < kD; ++i)
+      if (j + i < nb) {
+        if constexpr (kFast) clip(bt[i]);
+        compute(bt[i]);
+      }
   }
   __syncthreads();  // all staged-Q reads done before the region is reused
   // D layout: lane -> column (lane & 15), rows 4 (lane >> 4) + v of tile i
