@@ -278,14 +278,33 @@ __global__ __launch_bounds__((rowdot_threads<kRP, kMR>())) __attribute__((amdgpu
       load(c, b0);
       compute(b0);
     }
+  } else if constexpr (kMR == 1) {
+    // 16-row workgroups: a ring of two batches, the loads of batch j + 1
+    // issued before batch j is multiplied (past w1 the loads read zeros). The
+    // grouped loop below raised these forms' register count past the step
+    // that halves their workgroups per CU.
+    if (w0 < w1) {
+      constexpr int kD = 2;
+      Batch bt[kD];
+      load(w0, bt[0]);
+      for (int64_t c = w0; c < w1; c += kD * cstride) {
+#pragma unroll
+        for (int j = 0; j < kD; ++j) {
+          load(c + (j + kD - 1) * cstride, bt[(j + kD - 1) % kD]);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(bt[j]);
+          if (c + (j + 1) * cstride >= w1) break;
+        }
+      }
+    }
   } else if (w0 < w1) {
-    // A ring of kD batches: the loads of batch j + kD - 1 are issued before
-    // batch j is multiplied. Only the wave's last batch can reach past w1, so
-    // the loop takes whole groups of kD batches that end before it, with no
-    // exit and no clip inside (an exit inside the unrolled group made the
-    // compiler wait for every load in flight at the back edge, which emptied
-    // the ring every kD batches); the last 1..kD batches follow the loop.
-    // Loads past w1 read clamped in-range addresses (kFast) or zeros.
+    // 64-row workgroups: a ring of kD batches, the loads of batch j + kD - 1
+    // issued before batch j is multiplied. Only the wave's last batch can
+    // reach past w1, so the loop takes whole groups of kD batches that end
+    // before it, with no exit and no clip inside (an exit inside the unrolled
+    // group made the compiler wait for every load in flight at the back edge,
+    // which emptied the ring every kD batches); the last 1..kD batches follow
+    // the loop. Loads past w1 read clamped in-range addresses.
     constexpr int kD = Cfg::kDepth;
     const int64_t nb = cdiv(w1 - w0, cstride);  // >= 1, wave-uniform
     Batch bt[kD];
