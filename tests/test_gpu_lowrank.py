@@ -11,7 +11,8 @@ checked bit for bit against RN_bf16 of the kernel's own scaled fp32 result
 Shapes reach every launch form: 64-row workgroups with contraction splits
 (from 2048 rows, ranks 17..64), 16-row workgroups (smaller M or r <= 16),
 ragged row and column tails, rows whose length is not a multiple of 8
-(element-wise loads), and the token-split gradient path.
+(element-wise loads), and the token-split gradient path; in the 64-row form
+also waves with 1, 2, 4 and 5 column batches and waves with none.
 """
 
 import numpy as np
@@ -44,6 +45,8 @@ SHAPES = [
     (2048, 4096, 16),    # r <= 16: 16-row workgroups at large M
     (300, 1000, 24),     # small M: 16-row workgroups, contraction split over workgroups
     (16, 1024, 8),       # decode-sized
+    (2048, 304, 40),     # 64-row form, short contraction: waves with one and two column batches
+    (2112, 40, 64),      # 64-row form, 40 columns: most waves get no batch at all
 ]
 
 
