@@ -130,7 +130,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     uint2 mk[kMask ? kPL : 1];
     float q[kQE];
   };
+  // kBuf (16-byte rows, no mask): buffer loads through descriptors that
+  // start at the split's first token and end after its last, each lane's
+  // offsets fixed for the whole split and a scalar offset per step. Tokens
+  // past the split then read as zero, and no address is recomputed or
+  // clamped per step (64-bit address arithmetic and clamps were most of the
+  // step's vector instructions). Columns past C read the next token's row
+  // (or zero) and are zeroed in the tail step; Q columns j >= r read other
+  // entries of Q, whose products land in rows j >= r of the result, which
+  // are never stored. The launch keeps each split's P bytes under 4 GiB.
+  constexpr bool kBuf = kVec && !kMask;
+  i32x4 prs = {}, qrs = {};
+  uint32_t poff[kBuf ? kPL : 1], qoff[kBuf ? kQE : 1];
+  if constexpr (kBuf) {
+    // (a split that starts past M has no tokens: empty descriptors, whose
+    // loads read zero without touching memory)
+    const int64_t mt = m1 > m0 ? m1 - m0 : 0;
+    prs = make_rsrc(mt > 0 ? P + m0 * C : P, mt * C * 2);
+    qrs = make_rsrc(mt > 0 ? Q + m0 * r : Q, mt * (int64_t)r * 4);
+#pragma unroll
+    for (int i = 0; i < kPL; ++i) poff[i] = (uint32_t)(((pr + kRPT * i) * C + cp) * 2);
+#pragma unroll
+    for (int e = 0; e < kQE; ++e) {
+      const int idx = t + 256 * e;
+      qoff[e] = (uint32_t)(((idx / kRP) * r + idx % kRP) * 4);
+    }
+  }
   auto load = [&](int64_t mb, Stage& st) {
+    if constexpr (kBuf) {
+      const int sp = (int)(uint32_t)((mb - m0) * C * 2), sq = (int)(uint32_t)((mb - m0) * r * 4);
+#pragma unroll
+      for (int i = 0; i < kPL; ++i) st.p[i] = raw_buffer_load_b128(prs, (int)poff[i], sp, 0);
+#pragma unroll
+      for (int e = 0; e < kQE; ++e) st.q[e] = __builtin_bit_cast(float, raw_buffer_load_u32(qrs, (int)qoff[e], sq, 0));
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kPL; ++i) {
       const int64_t m = mb + pr + kRPT * i;
@@ -161,10 +195,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
   };
   constexpr int kDepth = kRP <= 32 ? 4 : kRP <= 64 ? kColdotDepth64 : 1;
+  // (kBuf: tokens past the split already read as zero; the workgroup whose
+  // columns reach past C zeroes those, a fixed set of lanes)
+  const bool ctail = cw + 4 * kCW > C;
   auto step = [&](int64_t mb, Stage& st) {
-    // the step that reaches past the split's last token or past C: zero those values
-    const bool tail = mb + 32 > m1 || (kVec && cw + 4 * kCW > C);
-    if (tail) {
+    if constexpr (kBuf) {
+      if (ctail) {
+        if (cp >= C) {
+#pragma unroll
+          for (int i = 0; i < kPL; ++i) st.p[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    } else if (mb + 32 > m1 || (kVec && ctail)) {
+      // the step that reaches past the split's last token or past C: zero those values
 #pragma unroll
       for (int i = 0; i < kPL; ++i)
         if (mb + pr + kRPT * i >= m1 || cp >= C) st.p[i] = u32x4{0u, 0u, 0u, 0u};
@@ -287,6 +330,9 @@ __global__ __launch_bounds__(256) void coldot_reduce_kernel(const float* __restr
 constexpr int kColdotCW = 64;  // columns per wave
 constexpr int64_t kColdotTargetWG = 512;
 
+// The buffer-load form addresses one split's P rows with 32-bit offsets.
+bool coldot_buf_fits(int64_t mchunk, int64_t C) { return mchunk * C * 2 < ((int64_t)1 << 32) - 256; }
+
 int coldot_splits(int64_t M, int64_t C) {
   int64_t s = cdiv(kColdotTargetWG, cdiv(C, (int64_t)(4 * kColdotCW)));
   int64_t cap = M / 128;
@@ -305,7 +351,9 @@ hipError_t launch_coldot(const uint16_t* P, int64_t M, int64_t C, const float* Q
   const int ns = coldot_splits(M, C);
   const int64_t mchunk = cdiv(cdiv(M, ns), 32) * 32;
   const dim3 grid((unsigned)cdiv(C, 4 * kColdotCW), (unsigned)ns);
-  const bool vec = C % 8 == 0;
+  // 16-byte rows; without a mask they are read through per-split buffer
+  // descriptors (32-bit offsets), so a split's P bytes stay under 4 GiB
+  const bool vec = C % 8 == 0 && (pmask != nullptr || coldot_buf_fits(mchunk, C));
   if (pmask != nullptr && !vec) return hipErrorInvalidValue;
   if (pmask != nullptr && f16) return hipErrorInvalidValue;
   const bool direct = ns == 1;
@@ -349,7 +397,7 @@ hipError_t launch_coldot_pair(const uint16_t* P0, int64_t C0, const float* Q0, f
   const int64_t cmax = C0 > C1 ? C0 : C1;
   const dim3 grid((unsigned)cdiv(cmax, 4 * kColdotCW), 2u);
   const ColdotSecond sec{P1, C1, Q1, G1, g_sc1, g_sj1};
-  const bool vec = C0 % 8 == 0 && C1 % 8 == 0;
+  const bool vec = C0 % 8 == 0 && C1 % 8 == 0 && coldot_buf_fits(mchunk, cmax);
 #define QLORA_PAIR3(RP, VEC, F16)                                                                              \
   coldot_mfma_kernel<RP, kColdotCW, VEC, false, F16, true, true><<<grid, 256, 0, stream>>>(                      \
       P0, M, C0, Q0, r, mchunk, nullptr, nullptr, scale, G0, g_sc0, g_sj0, accumulate, sec)
