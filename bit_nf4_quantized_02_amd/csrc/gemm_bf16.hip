@@ -165,6 +165,38 @@ __device__ __forceinline__ void issue_step(const Rsrc& rs, const CopyPlan& p, in
   }
 }
 
+// The two operands' copies of step `step` issued separately (the weight
+// side of the three-buffer form runs one step further ahead).
+template <bool kNN>
+__device__ __forceinline__ void issue_act(const Rsrc& rs, const CopyPlan& p, int step, int nk_main, int wave,
+                                          char* As) {
+  char* const as = As + wave * kCopies * 1024;
+  if (step < nk_main) {
+    const u32x4 off = step == nk_main - 1 ? p.alast : p.a;
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy16(rs.act, off[i], step * (kBK * 2), as + i * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy16(rs.x, p.x[i], (step - nk_main) * (kBK * 2), as + i * 1024);
+  }
+}
+
+template <bool kNN>
+__device__ __forceinline__ void issue_wt(const Rsrc& rs, const CopyPlan& p, int step, int nk_main, int wave,
+                                         char* Bs, int64_t ldf, int64_t ldx) {
+  const uint32_t fstep = kNN ? (uint32_t)(kBK * ldf * 2) : (uint32_t)(kBK * 2);
+  const uint32_t xstep = kNN ? (uint32_t)(kBK * ldx * 2) : (uint32_t)(kBK * 2);
+  char* const bs = Bs + wave * kCopies * 1024;
+  if (step < nk_main) {
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy16(rs.f, p.f[i], (int)((uint32_t)step * fstep), bs + i * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i)
+      copy16(rs.fx, p.fx[i], (int)((uint32_t)(step - nk_main) * xstep), bs + i * 1024);
+  }
+}
+
 // Fragments of one substep: 4 activation row blocks and 2 weight column
 // blocks of the wave's 128 x 64 sub-tile.
 struct StepFrags {
@@ -185,21 +217,16 @@ __device__ __forceinline__ void read_substep(StepFrags& f, const char* Ac, const
 // Restrict pointers tell the compiler the copies cannot alias the fragment
 // reads, so it does not wait for them before reading.
 //
-// Two schedules, chosen with kPrio by operand size:
-//  - operands that fit in the 256 MB last-level cache: substeps 0-2
-//    multiply, then this wave's copies have landed and all waves meet, then
-//    substep 3 multiplies while substep 0 of step + 1 is read from (An, Bn),
-//    so the LDS latency after the barrier hides behind MFMAs. On entry f
-//    holds substep 0 (buffer 0); after the last step that read finds the
-//    repeated copy (valid data, not used). Measured in the 65B-class layer
-//    step: the 8192 x 8192 projections 2-4% faster than with the barrier
-//    after all four substeps.
-//  - larger operands (360 MB of expanded weight and more, streamed from
-//    HBM): all four substeps before the barrier, with the wave's issue
-//    priority raised over its MFMA stream: 4-6% faster there than without
-//    the priority (3-10% slower where the operands fit in the cache), and
-//    4% slower with the cross-barrier schedule.
-template <bool kF16, bool kPrio, bool kNN>
+// This is the schedule for operands that fit in the 256 MB last-level cache
+// (and for the fp16 and dropout forms): substeps 0-2 multiply, then this
+// wave's copies have landed and all waves meet, then substep 3 multiplies
+// while substep 0 of step + 1 is read from (An, Bn), so the LDS latency after
+// the barrier hides behind MFMAs. On entry f holds substep 0 (buffer 0);
+// after the last step that read finds the repeated copy (valid data, not
+// used). Measured in the 65B-class layer step: the 8192 x 8192 projections
+// 2-4% faster than with the barrier after all four substeps. Larger operands
+// take bf16_step3 (three weight buffers, raised issue priority).
+template <bool kF16, bool kNN>
 __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
                                           int nk_main, int wave,
                                           const char* __restrict__ Ac, const char* __restrict__ Bc,
@@ -211,30 +238,20 @@ __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const
   // the last step into a buffer no later step reads: keeps the body free of
   // branches
   const int s1 = step + 1 < nk ? step + 1 : nk - 1;
-  constexpr bool kCross = !kPrio;
-  if constexpr (!kCross) {
-    read_substep<kNN>(f, Ac, Bc, wm0, wn0, 0, 0, lane);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   issue_step<kNN>(rs, p, s1, nk_main, wave, An, Bn, a.ldf, a.ldx);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kPrio) {
-    __builtin_amdgcn_s_setprio(1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
-  constexpr int kBefore = kCross ? 3 : kBK / 16;  // substeps before the barrier
 #pragma unroll
-  for (int kk = 0; kk < kBefore; ++kk) {
+  for (int kk = 0; kk < 3; ++kk) {  // substeps before the barrier
     const int cb = kk & 1;
-    if (kk < 3) read_substep<kNN>(f, Ac, Bc, wm0, wn0, kk + 1, cb ^ 1, lane);
+    read_substep<kNN>(f, Ac, Bc, wm0, wn0, kk + 1, cb ^ 1, lane);
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[cb][i], f.bfr[cb][j], acc[i][j]);
   }
   // schedule: for substeps 0..2 one fragment read (of the next substep) per
-  // MFMA, then (without the cross-barrier read) the last substep's MFMAs
+  // MFMA
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk)
 #pragma unroll
@@ -242,27 +259,84 @@ __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const
       if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
     }
-  if constexpr (!kCross) __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
-  if constexpr (kPrio) {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
-  }
   __builtin_amdgcn_sched_barrier(0);
   step_barrier<0>();
-  if constexpr (kCross) {
-    __builtin_amdgcn_sched_barrier(0);
-    read_substep<kNN>(f, An, Bn, wm0, wn0, 0, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  read_substep<kNN>(f, An, Bn, wm0, wn0, 0, 0, lane);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[1][i], f.bfr[1][j], acc[i][j]);
+#pragma unroll
+  for (int g = 0; g < kMfma; ++g) {
+    if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Three-buffer step (operands larger than the last-level cache, the weight
+// streamed from HBM): MFMAs on (Ac, Bc) while the activation copies of
+// step + 1 fill An and the weight copies of step + 2 fill Bn2; at the end the
+// copies of step + 1 (both operands) have landed and the weight copies of
+// step + 2 may still be in flight, so a weight copy has two steps to land
+// (A in two 32 KB buffers, B in three: 160 KB of LDS). All four substeps run
+// before the barrier, with the wave's issue priority raised over its MFMA
+// stream (4-6% faster than without it on these shapes, 3-10% slower where
+// the operands fit in the cache). Measured in the 65B-class layer step
+// against the same schedule with two weight buffers: the six 22016-wide
+// GEMMs 1181 -> 1158 us per launch, the step 997 -> 981 ms.
+template <bool kF16, bool kNN>
+__device__ __forceinline__ void bf16_step3(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
+                                           int nk_main, int wave, const char* __restrict__ Ac,
+                                           const char* __restrict__ Bc, char* __restrict__ An,
+                                           char* __restrict__ Bn2, f32x16 (&acc)[kTM][kTN], StepFrags& f) {
+  const int lane = threadIdx.x & 63;
+  const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
+  const int s1 = step + 1 < nk ? step + 1 : nk - 1;
+  const int s2 = step + 2 < nk ? step + 2 : nk - 1;
+  read_substep<kNN>(f, Ac, Bc, wm0, wn0, 0, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_act<kNN>(rs, p, s1, nk_main, wave, An);
+  issue_wt<kNN>(rs, p, s2, nk_main, wave, Bn2, a.ldf, a.ldx);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
+#pragma unroll
+  for (int kk = 0; kk < kBK / 16; ++kk) {
+    const int cb = kk & 1;
+    if (kk < 3) read_substep<kNN>(f, Ac, Bc, wm0, wn0, kk + 1, cb ^ 1, lane);
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[1][i], f.bfr[1][j], acc[i][j]);
+      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[cb][i], f.bfr[cb][j], acc[i][j]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk)
 #pragma unroll
     for (int g = 0; g < kMfma; ++g) {
       if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+  step_barrier<kCopies>();
+}
+
+// First copies of the three-buffer form: step sbeg of both operands and the
+// weight of step sbeg + 1 (restrict pointers, as in the steps, so the
+// compiler can tell these copies from the fragment reads of the loop).
+template <bool kNN>
+__device__ __forceinline__ void prologue3(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int sbeg, int nk,
+                                          int nk_main, int wave, char* __restrict__ A0, char* __restrict__ B0,
+                                          char* __restrict__ B1) {
+  issue_act<kNN>(rs, p, sbeg, nk_main, wave, A0);
+  issue_wt<kNN>(rs, p, sbeg, nk_main, wave, B0, a.ldf, a.ldx);
+  issue_wt<kNN>(rs, p, sbeg + 1 < nk ? sbeg + 1 : nk - 1, nk_main, wave, B1, a.ldf, a.ldx);
+  step_barrier<kCopies>();
 }
 
 // One step without copies in flight: fragments of (Ac, Bc) and their MFMAs.
@@ -330,6 +404,8 @@ __device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char
 // the tile's mask bytes land in buffers 1, masks and scales the accumulators
 // from there, then runs its main steps as usual.
 // kF16: fp16 operands and output (the compute-type ablation), else bf16.
+// kPrio: operands larger than the last-level cache (bf16, no mask): the
+// three-buffer form (bf16_step3).
 template <bool kMask, bool kF16, bool kPrio = false, bool kNN = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
@@ -338,6 +414,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   __shared__ __attribute__((aligned(16))) char As1[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char Bs2[kPrio ? kTileBytes : 16];  // third weight buffer (kPrio)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -394,15 +471,44 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
       nk_end = nk_main;
     }
   }
-  if (sbeg < nk_end) {  // (every split range is non-empty for the split counts split_plan picks)
+  if constexpr (kPrio) {
+    static_assert(!kMask && !kF16, "the three-buffer form is bf16 without dropout");
+    // weight copies two steps ahead: A in 2 buffers, B in 3; whole groups of
+    // six steps (the rotation's period) inside the loop, the last 0..5 after
+    // it, so no exit sits between the unrolled steps
+    if (sbeg < nk_end) {
+      prologue3<kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, Bs1);
+      StepFrags f;
+      // (the first step runs before the loop, whose groups then start at
+      // rotation position 1)
+      bf16_step3<kF16, kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, As1, Bs2, acc, f);
+      int s = sbeg + 1;
+      for (; s + 6 <= nk_end; s += 6) {
+        bf16_step3<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc, f);
+        bf16_step3<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs1, acc, f);
+        bf16_step3<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs2, acc, f);
+        bf16_step3<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs0, acc, f);
+        bf16_step3<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs1, acc, f);
+        bf16_step3<kF16, kNN>(a, rs, plan, s + 5, nk_end, nk_main, wave, As0, Bs0, As1, Bs2, acc, f);
+      }
+      const int rem = nk_end - s;
+      if (rem > 0) bf16_step3<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc, f);
+      if (rem > 1) bf16_step3<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs1, acc, f);
+      if (rem > 2) bf16_step3<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs2, acc, f);
+      if (rem > 3) bf16_step3<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs0, acc, f);
+      if (rem > 4) bf16_step3<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs1, acc, f);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+      __syncthreads();
+    }
+  } else if (sbeg < nk_end) {  // (every split range is non-empty for the split counts split_plan picks)
     issue_step<kNN>(rs, plan, sbeg, nk_main, wave, As0, Bs0, a.ldf, a.ldx);
     step_barrier<0>();
     StepFrags f;
-    if constexpr (!kPrio) read_substep<kNN>(f, As0, Bs0, wm0, wn0, 0, 0, lane);  // the cross-barrier schedule's
+    read_substep<kNN>(f, As0, Bs0, wm0, wn0, 0, 0, lane);  // the cross-barrier schedule's
     for (int step = sbeg; step < nk_end; step += 2) {
-      bf16_step<kF16, kPrio, kNN>(a, rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc, f);
+      bf16_step<kF16, kNN>(a, rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc, f);
       if (step + 1 < nk_end)
-        bf16_step<kF16, kPrio, kNN>(a, rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc, f);
+        bf16_step<kF16, kNN>(a, rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc, f);
     }
     // the cross-barrier schedule's last read (of the repeated copy) is done
     // before the epilogue reuses the buffers
@@ -550,7 +656,7 @@ bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
 }
 
 // operand bytes (activation + expanded weight) above which the plain bf16
-// GEMM raises its MFMA priority: the last-level cache (256 MB)
+// GEMM takes the three-buffer form: the last-level cache (256 MB)
 constexpr int64_t kPrioOperandBytes = 256LL << 20;
 
 hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
