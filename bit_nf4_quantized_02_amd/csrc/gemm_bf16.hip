@@ -217,15 +217,17 @@ __device__ __forceinline__ void read_substep(StepFrags& f, const char* Ac, const
 // Restrict pointers tell the compiler the copies cannot alias the fragment
 // reads, so it does not wait for them before reading.
 //
-// This is the schedule for operands that fit in the 256 MB last-level cache
-// (and for the fp16 and dropout forms): substeps 0-2 multiply, then this
+// This two-buffer step serves the fp16 and dropout forms: substeps 0-2
+// multiply, then this
 // wave's copies have landed and all waves meet, then substep 3 multiplies
 // while substep 0 of step + 1 is read from (An, Bn), so the LDS latency after
 // the barrier hides behind MFMAs. On entry f holds substep 0 (buffer 0);
 // after the last step that read finds the repeated copy (valid data, not
 // used). Measured in the 65B-class layer step: the 8192 x 8192 projections
-// 2-4% faster than with the barrier after all four substeps. Larger operands
-// take bf16_step3 (three weight buffers, raised issue priority).
+// 2-4% faster than with the barrier after all four substeps. The plain bf16
+// forms run the same schedules with three weight buffers: bf16_step3x for
+// operands that fit in the last-level cache, bf16_step3 (raised issue
+// priority) for larger ones.
 template <bool kF16, bool kNN>
 __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
                                           int nk_main, int wave,
@@ -326,6 +328,60 @@ __device__ __forceinline__ void bf16_step3(const BfArgs& a, const Rsrc& rs, cons
   step_barrier<kCopies>();
 }
 
+// Three-buffer step with the cross-barrier schedule (operands that fit in
+// the last-level cache): the copies as in bf16_step3 (activation of
+// step + 1 into An, weight of step + 2 into Bn2); substeps 0-2 multiply,
+// the copies of step + 1 have landed and all waves meet, then substep 3
+// multiplies while substep 0 of step + 1 is read from (An, Bn1). Measured in
+// the 65B-class layer step against the two-buffer step: the 8192 x 8192
+// GEMMs 404-417 -> 400-402 us per launch, the step 972.9 -> 967 ms; the
+// 4096 x 4096 projection unchanged (111.1 -> 110.6 us).
+template <bool kF16, bool kNN>
+__device__ __forceinline__ void bf16_step3x(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
+                                            int nk_main, int wave, const char* __restrict__ Ac,
+                                            const char* __restrict__ Bc, char* __restrict__ An,
+                                            const char* __restrict__ Bn1, char* __restrict__ Bn2,
+                                            f32x16 (&acc)[kTM][kTN], StepFrags& f) {
+  const int lane = threadIdx.x & 63;
+  const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
+  const int s1 = step + 1 < nk ? step + 1 : nk - 1;
+  const int s2 = step + 2 < nk ? step + 2 : nk - 1;
+  issue_act<kNN>(rs, p, s1, nk_main, wave, An);
+  issue_wt<kNN>(rs, p, s2, nk_main, wave, Bn2, a.ldf, a.ldx);
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    const int cb = kk & 1;
+    read_substep<kNN>(f, Ac, Bc, wm0, wn0, kk + 1, cb ^ 1, lane);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[cb][i], f.bfr[cb][j], acc[i][j]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+    for (int g = 0; g < kMfma; ++g) {
+      if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  step_barrier<kCopies>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_substep<kNN>(f, An, Bn1, wm0, wn0, 0, 0, lane);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[1][i], f.bfr[1][j], acc[i][j]);
+#pragma unroll
+  for (int g = 0; g < kMfma; ++g) {
+    if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // First copies of the three-buffer form: step sbeg of both operands and the
 // weight of step sbeg + 1 (restrict pointers, as in the steps, so the
 // compiler can tell these copies from the fragment reads of the loop).
@@ -405,8 +461,10 @@ __device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char
 // from there, then runs its main steps as usual.
 // kF16: fp16 operands and output (the compute-type ablation), else bf16.
 // kPrio: operands larger than the last-level cache (bf16, no mask): the
-// three-buffer form (bf16_step3).
-template <bool kMask, bool kF16, bool kPrio = false, bool kNN = false>
+// three-buffer form with raised priority (bf16_step3). kB3x: the plain bf16
+// form of operands that fit in the cache: three weight buffers with the
+// cross-barrier schedule (bf16_step3x).
+template <bool kMask, bool kF16, bool kPrio = false, bool kNN = false, bool kB3x = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
   // direct copies from the one being read
@@ -414,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   __shared__ __attribute__((aligned(16))) char As1[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char Bs2[kPrio ? kTileBytes : 16];  // third weight buffer (kPrio)
+  __shared__ __attribute__((aligned(16))) char Bs2[kPrio || kB3x ? kTileBytes : 16];  // third weight buffer
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -497,6 +555,30 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
       if (rem > 2) bf16_step3<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs2, acc, f);
       if (rem > 3) bf16_step3<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs0, acc, f);
       if (rem > 4) bf16_step3<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs1, acc, f);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+      __syncthreads();
+    }
+  } else if constexpr (kB3x) {
+    if (sbeg < nk_end) {
+      prologue3<kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, Bs1);
+      StepFrags f;
+      read_substep<kNN>(f, As0, Bs0, wm0, wn0, 0, 0, lane);
+      bf16_step3x<kF16, kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, Bs2, acc, f);
+      int s = sbeg + 1;
+      for (; s + 6 <= nk_end; s += 6) {
+        bf16_step3x<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs2, Bs0, acc, f);
+        bf16_step3x<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs0, Bs1, acc, f);
+        bf16_step3x<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs1, Bs2, acc, f);
+        bf16_step3x<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs2, Bs0, acc, f);
+        bf16_step3x<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs0, Bs1, acc, f);
+        bf16_step3x<kF16, kNN>(a, rs, plan, s + 5, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, Bs2, acc, f);
+      }
+      const int rem = nk_end - s;
+      if (rem > 0) bf16_step3x<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs2, Bs0, acc, f);
+      if (rem > 1) bf16_step3x<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs0, Bs1, acc, f);
+      if (rem > 2) bf16_step3x<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs1, Bs2, acc, f);
+      if (rem > 3) bf16_step3x<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs2, Bs0, acc, f);
+      if (rem > 4) bf16_step3x<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs0, Bs1, acc, f);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
       __syncthreads();
     }
@@ -682,7 +764,7 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
     if ((M * kc + kc * a.ldf) * 2 > kPrioOperandBytes)
       gemm_bf16_kernel<false, false, true, true><<<grid, kThreads, 0, stream>>>(a);
     else
-      gemm_bf16_kernel<false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
+      gemm_bf16_kernel<false, false, false, true, true><<<grid, kThreads, 0, stream>>>(a);
   } else if (f16) {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
@@ -694,7 +776,7 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
     else if ((M * kc + nout * a.ldf) * 2 > kPrioOperandBytes)
       gemm_bf16_kernel<false, false, true><<<grid, kThreads, 0, stream>>>(a);
     else
-      gemm_bf16_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
+      gemm_bf16_kernel<false, false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
   }
   if (a.splits > 1) {
     const int64_t groups = a.tail * (kBM * kBN / 4);
