@@ -96,7 +96,11 @@ def test_contraction_major_operand_bitwise(q, n, k, r):
                                      # (16 split in 2), ragged 264 tiles (8 split in 4, n % 256 = 8, M % 256 = 208)
                                      (4352, 4096, 2048, 16), (2000, 8200, 4160, 8),
                                      # dX in the contraction-major form: split-K (6 output tiles), rank 64
-                                     (300, 2048, 576, 16), (520, 640, 320, 64)])
+                                     (300, 2048, 576, 16), (520, 640, 320, 64),
+                                     # the weight buffers rotate with period six after a first step run
+                                     # alone: forward with 1 step (nothing after it), 7 (one group) and 13
+                                     # steps (two groups, nothing left)
+                                     (300, 128, 64, 0), (300, 200, 384, 8), (257, 448, 768, 8)])
 def test_bf16_gemm_building_blocks(q, m, n, k, r):
     """T/U split + expansion + bf16 GEMM, forward and dX, against the oracle."""
     say(f"case: bf16 gemm M={m} N={n} K={k} r={r}")

@@ -12,7 +12,9 @@ so the same kernel choices) the bench times.
   r = 64): Y and dX on sampled rows, dA and dB whole; layer 79 (q, down) with
   W, A, B drawn on the device as the bench draws every layer past the first,
   copied back for the oracle: the whole encoding bit for bit, then the same
-  checks.
+  checks;
+* GEMMs whose operands exceed the 256 MB last-level cache at step counts the
+  workloads do not reach (the remainders of the weight-buffer rotation).
 The oracle encodes each weight itself (whole tensor) and multiplies in fp64.
 Bars: relative Frobenius error <= 2e-3 for Y and dX (sampled rows: over the
 sampled rows) with every element of them inside the oracle's element-wise
@@ -144,6 +146,23 @@ def test_65b_layer0_linears(q, li):
     inp = synth.linear_inputs(5, 0, li, lin.n, lin.k, M, c.r, c.scale, sigma=c.sigma)
     X, dY, A, B, Y, T, dX, dA, dB = _run_linear(q, inp)
     _check_linear(lin.name, inp.W, X, dY, A, B, c.scale, Y, T, dX, dA, dB, _rows(M, 32, 37 + li))
+
+
+# Operands above the 256 MB last-level cache take the GEMM form that copies
+# the weight tile two steps ahead, whose buffers rotate with period six: the
+# first step runs alone, then whole groups of six, then the last 0..5. The
+# 65B shapes leave 3 or 4 after the first step; these shapes (r = 16: one
+# low-rank step) leave the others, in the forward (K / 64 steps after the
+# first) and in dX (N / 64), and the dX outputs of the first have a last wave
+# split over the contraction (ranges of 55 and 53 steps).
+@pytest.mark.parametrize("n,k", [(27968, 4224), (27776, 4288), (27712, 4352), (28032, 4160)])
+def test_streamed_gemm_step_remainders(q, n, k):
+    M, r, s = 4096, 16, 2.0
+    assert (M * k + n * (k + 64)) * 2 > (256 << 20) and (M * n + n * k) * 2 > (256 << 20)
+    say(f"case: streamed GEMM {n}x{k} M={M} r={r}: forward {(k // 64) % 6}, dX {(n // 64) % 6} steps after the groups")
+    inp = synth.linear_inputs(91, 0, 0, n, k, M, r, s, sigma=0.02)
+    X, dY, A, B, Y, T, dX, dA, dB = _run_linear(q, inp)
+    _check_linear(f"{n}x{k}", inp.W, X, dY, A, B, s, Y, T, dX, dA, dB, _rows(M, 24, 41))
 
 
 @pytest.mark.parametrize("li", [0, 6])
