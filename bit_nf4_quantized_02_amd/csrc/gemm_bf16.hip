@@ -225,9 +225,7 @@ __device__ __forceinline__ void read_substep(StepFrags& f, const char* Ac, const
 // after the last step that read finds the repeated copy (valid data, not
 // used). Measured in the 65B-class layer step: the 8192 x 8192 projections
 // 2-4% faster than with the barrier after all four substeps. The plain bf16
-// forms run the same schedules with three weight buffers: bf16_step3x for
-// operands that fit in the last-level cache, bf16_step3 (raised issue
-// priority) for larger ones.
+// forms run the same schedule with three weight buffers (bf16_step3x).
 template <bool kF16, bool kNN>
 __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
                                           int nk_main, int wave,
@@ -277,65 +275,21 @@ __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Three-buffer step (operands larger than the last-level cache, the weight
-// streamed from HBM): MFMAs on (Ac, Bc) while the activation copies of
-// step + 1 fill An and the weight copies of step + 2 fill Bn2; at the end the
-// copies of step + 1 (both operands) have landed and the weight copies of
-// step + 2 may still be in flight, so a weight copy has two steps to land
-// (A in two 32 KB buffers, B in three: 160 KB of LDS). All four substeps run
-// before the barrier, with the wave's issue priority raised over its MFMA
-// stream (4-6% faster than without it on these shapes, 3-10% slower where
-// the operands fit in the cache). Measured in the 65B-class layer step
-// against the same schedule with two weight buffers: the six 22016-wide
-// GEMMs 1181 -> 1158 us per launch, the step 997 -> 981 ms.
-template <bool kF16, bool kNN>
-__device__ __forceinline__ void bf16_step3(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
-                                           int nk_main, int wave, const char* __restrict__ Ac,
-                                           const char* __restrict__ Bc, char* __restrict__ An,
-                                           char* __restrict__ Bn2, f32x16 (&acc)[kTM][kTN], StepFrags& f) {
-  const int lane = threadIdx.x & 63;
-  const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
-  const int s1 = step + 1 < nk ? step + 1 : nk - 1;
-  const int s2 = step + 2 < nk ? step + 2 : nk - 1;
-  read_substep<kNN>(f, Ac, Bc, wm0, wn0, 0, 0, lane);
-  __builtin_amdgcn_sched_barrier(0);
-  issue_act<kNN>(rs, p, s1, nk_main, wave, An);
-  issue_wt<kNN>(rs, p, s2, nk_main, wave, Bn2, a.ldf, a.ldx);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(1);
-  __builtin_amdgcn_sched_barrier(0);
-  constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
-#pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
-    const int cb = kk & 1;
-    if (kk < 3) read_substep<kNN>(f, Ac, Bc, wm0, wn0, kk + 1, cb ^ 1, lane);
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[cb][i], f.bfr[cb][j], acc[i][j]);
-  }
-#pragma unroll
-  for (int kk = 0; kk < 3; ++kk)
-#pragma unroll
-    for (int g = 0; g < kMfma; ++g) {
-      if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-    }
-  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(0);
-  __builtin_amdgcn_sched_barrier(0);
-  step_barrier<kCopies>();
-}
-
-// Three-buffer step with the cross-barrier schedule (operands that fit in
-// the last-level cache): the copies as in bf16_step3 (activation of
-// step + 1 into An, weight of step + 2 into Bn2); substeps 0-2 multiply,
-// the copies of step + 1 have landed and all waves meet, then substep 3
-// multiplies while substep 0 of step + 1 is read from (An, Bn1). Measured in
-// the 65B-class layer step against the two-buffer step: the 8192 x 8192
-// GEMMs 404-417 -> 400-402 us per launch, the step 972.9 -> 967 ms; the
-// 4096 x 4096 projection unchanged (111.1 -> 110.6 us).
+// Three-buffer step (the plain bf16 forms): MFMAs on (Ac, Bc) while the
+// activation copies of step + 1 fill An and the weight copies of step + 2
+// fill Bn2 (A in two 32 KB buffers, B in three: 160 KB of LDS), so a weight
+// copy has two steps to land. Substeps 0-2 multiply, the copies of step + 1
+// (both operands) have landed and all waves meet, the weight copies of
+// step + 2 may still be in flight; then substep 3 multiplies while substep 0
+// of step + 1 is read from (An, Bn1). Measured in the 65B-class layer step
+// (same box, each against the form before it): the weight side copied two
+// steps ahead with all four substeps before the barrier and raised issue
+// priority for operands above the last-level cache, 997 -> 981 ms (the six
+// 22016-wide GEMMs 1181 -> 1158 us); the same three buffers with this
+// schedule for the cache-resident operands, 972.9 -> 967 ms (8192 x 8192
+// GEMMs 404-417 -> 400-402 us); this schedule for the larger operands too,
+// 969.0 -> 951.2 ms (22016-wide GEMMs 1150 -> 1108 us; with the raised
+// priority kept, 952.2 ms).
 template <bool kF16, bool kNN>
 __device__ __forceinline__ void bf16_step3x(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
                                             int nk_main, int wave, const char* __restrict__ Ac,
@@ -460,11 +414,8 @@ __device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char
 // the tile's mask bytes land in buffers 1, masks and scales the accumulators
 // from there, then runs its main steps as usual.
 // kF16: fp16 operands and output (the compute-type ablation), else bf16.
-// kPrio: operands larger than the last-level cache (bf16, no mask): the
-// three-buffer form with raised priority (bf16_step3). kB3x: the plain bf16
-// form of operands that fit in the cache: three weight buffers with the
-// cross-barrier schedule (bf16_step3x).
-template <bool kMask, bool kF16, bool kPrio = false, bool kNN = false, bool kB3x = false>
+// kB3: the plain bf16 form (no mask): three weight buffers (bf16_step3x).
+template <bool kMask, bool kF16, bool kNN = false, bool kB3 = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
   // direct copies from the one being read
@@ -472,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   __shared__ __attribute__((aligned(16))) char As1[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char Bs2[kPrio || kB3x ? kTileBytes : 16];  // third weight buffer
+  __shared__ __attribute__((aligned(16))) char Bs2[kB3 ? kTileBytes : 16];  // third weight buffer (kB3)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -529,36 +480,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
       nk_end = nk_main;
     }
   }
-  if constexpr (kPrio) {
+  if constexpr (kB3) {
     static_assert(!kMask && !kF16, "the three-buffer form is bf16 without dropout");
-    // weight copies two steps ahead: A in 2 buffers, B in 3; whole groups of
-    // six steps (the rotation's period) inside the loop, the last 0..5 after
-    // it, so no exit sits between the unrolled steps
-    if (sbeg < nk_end) {
-      prologue3<kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, Bs1);
-      StepFrags f;
-      // (the first step runs before the loop, whose groups then start at
-      // rotation position 1)
-      bf16_step3<kF16, kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, As1, Bs2, acc, f);
-      int s = sbeg + 1;
-      for (; s + 6 <= nk_end; s += 6) {
-        bf16_step3<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc, f);
-        bf16_step3<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs1, acc, f);
-        bf16_step3<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs2, acc, f);
-        bf16_step3<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs0, acc, f);
-        bf16_step3<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs1, acc, f);
-        bf16_step3<kF16, kNN>(a, rs, plan, s + 5, nk_end, nk_main, wave, As0, Bs0, As1, Bs2, acc, f);
-      }
-      const int rem = nk_end - s;
-      if (rem > 0) bf16_step3<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc, f);
-      if (rem > 1) bf16_step3<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs1, acc, f);
-      if (rem > 2) bf16_step3<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs2, acc, f);
-      if (rem > 3) bf16_step3<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs0, acc, f);
-      if (rem > 4) bf16_step3<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs1, acc, f);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
-      __syncthreads();
-    }
-  } else if constexpr (kB3x) {
     if (sbeg < nk_end) {
       prologue3<kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, Bs1);
       StepFrags f;
@@ -737,10 +660,6 @@ bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
   return M * kc * 2 < lim && M * (int64_t)kx * 2 < lim && nout * ldf * 2 < lim;
 }
 
-// operand bytes (activation + expanded weight) above which the plain bf16
-// GEMM takes the three-buffer form: the last-level cache (256 MB)
-constexpr int64_t kPrioOperandBytes = 256LL << 20;
-
 hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                                 const uint16_t* f, int64_t ldf, const uint16_t* fx, int64_t ldx, int64_t nout,
                                 uint16_t* out, float* part, hipStream_t stream, const uint8_t* mask, float keep_scale,
@@ -761,10 +680,7 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
   if (nn) {
     // the weight operand stored [contraction][output] (bf16 base, dX)
     if (mask != nullptr || f16) return hipErrorInvalidValue;
-    if ((M * kc + kc * a.ldf) * 2 > kPrioOperandBytes)
-      gemm_bf16_kernel<false, false, true, true><<<grid, kThreads, 0, stream>>>(a);
-    else
-      gemm_bf16_kernel<false, false, false, true, true><<<grid, kThreads, 0, stream>>>(a);
+    gemm_bf16_kernel<false, false, true, true><<<grid, kThreads, 0, stream>>>(a);
   } else if (f16) {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
@@ -773,10 +689,8 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
   } else {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
-    else if ((M * kc + nout * a.ldf) * 2 > kPrioOperandBytes)
-      gemm_bf16_kernel<false, false, true><<<grid, kThreads, 0, stream>>>(a);
     else
-      gemm_bf16_kernel<false, false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
+      gemm_bf16_kernel<false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
   }
   if (a.splits > 1) {
     const int64_t groups = a.tail * (kBM * kBN / 4);

@@ -148,13 +148,14 @@ def test_65b_layer0_linears(q, li):
     _check_linear(lin.name, inp.W, X, dY, A, B, c.scale, Y, T, dX, dA, dB, _rows(M, 32, 37 + li))
 
 
-# Operands above the 256 MB last-level cache take the GEMM form that copies
-# the weight tile two steps ahead, whose buffers rotate with period six: the
-# first step runs alone, then whole groups of six, then the last 0..5. The
-# 65B shapes leave 3 or 4 after the first step; these shapes (r = 16: one
-# low-rank step) leave the others, in the forward (K / 64 steps after the
-# first) and in dX (N / 64), and the dX outputs of the first have a last wave
-# split over the contraction (ranges of 55 and 53 steps).
+# The bf16 GEMM copies the weight tile two steps ahead into buffers that
+# rotate with period six: the first step runs alone, then whole groups of
+# six, then the last 0..5. These shapes have operands above the 256 MB
+# last-level cache, so the weight streams from HBM as in the 65B stack's
+# 22016-wide GEMMs. The 65B shapes leave 3 or 4 after the first step; these
+# (r = 16: one low-rank step) leave the others, in the forward (K / 64 steps
+# after the first) and in dX (N / 64), and the dX outputs of the first have a
+# last wave split over the contraction (ranges of 55 and 53 steps).
 @pytest.mark.parametrize("n,k", [(27968, 4224), (27776, 4288), (27712, 4352), (28032, 4160)])
 def test_streamed_gemm_step_remainders(q, n, k):
     M, r, s = 4096, 16, 2.0
