@@ -11,10 +11,13 @@
 //
 // Same tile shape as the fused kernel (gemm_tile.h): 256 x 256 outputs per
 // workgroup, 8 waves each computing 128 x 64 with v_mfma_f32_32x32x16_bf16,
-// 64-deep steps. Both operand tiles go global -> LDS with
-// global_load_lds_dwordx4 (no registers, no VALU), double-buffered: the copies
-// for step s + 1 are issued at the start of step s and waited for at its end,
-// so one barrier per step separates filling a buffer from reading it.
+// 64-deep steps. Both operand tiles go global -> LDS with direct buffer loads
+// into LDS (no registers, no VALU): the activation tile in two buffers, the
+// weight tile in three (160 KB of LDS). Step s issues the activation copies of
+// step s + 1 and the weight copies of step s + 2, so a weight copy has two
+// steps to land, and one barrier per step (after its third substep)
+// separates filling a buffer from reading it; the buffers rotate with period
+// six.
 //
 // Per-step cost is kept off the vector ALU: every lane's byte offset inside
 // each operand (row, swizzled chunk) is computed once, and a step only moves
@@ -166,7 +169,7 @@ __device__ __forceinline__ void issue_step(const Rsrc& rs, const CopyPlan& p, in
 }
 
 // The two operands' copies of step `step` issued separately (the weight
-// side of the three-buffer form runs one step further ahead).
+// side runs one step further ahead).
 template <bool kNN>
 __device__ __forceinline__ void issue_act(const Rsrc& rs, const CopyPlan& p, int step, int nk_main, int wave,
                                           char* As) {
@@ -212,86 +215,27 @@ __device__ __forceinline__ void read_substep(StepFrags& f, const char* Ac, const
   for (int j = 0; j < kTN; ++j) f.bfr[buf][j] = b_frag<kNN>(Bc, wn0 + j * 32, kk, lane);
 }
 
-// One step: MFMAs on (Ac, Bc) while the copies of step + 1 fill (An, Bn).
-// Each substep's MFMAs run while the next substep's fragments are read.
-// Restrict pointers tell the compiler the copies cannot alias the fragment
-// reads, so it does not wait for them before reading.
-//
-// This two-buffer step serves the fp16 and dropout forms: substeps 0-2
-// multiply, then this
-// wave's copies have landed and all waves meet, then substep 3 multiplies
-// while substep 0 of step + 1 is read from (An, Bn), so the LDS latency after
-// the barrier hides behind MFMAs. On entry f holds substep 0 (buffer 0);
-// after the last step that read finds the repeated copy (valid data, not
-// used). Measured in the 65B-class layer step: the 8192 x 8192 projections
-// 2-4% faster than with the barrier after all four substeps. The plain bf16
-// forms run the same schedule with three weight buffers (bf16_step3x).
+// One step: MFMAs on (Ac, Bc) while the activation copies of step + 1 fill
+// An and the weight copies of step + 2 fill Bn2. Substeps 0-2 multiply, each
+// with the next substep's fragment reads interleaved one-to-one with its
+// MFMAs; then the copies of step + 1 (both operands) have landed, the weight
+// copies of step + 2 may still be in flight, and all waves meet; then
+// substep 3 multiplies while substep 0 of step + 1 is read from (An, Bn1),
+// so the LDS latency after the barrier hides behind MFMAs. Restrict pointers
+// tell the compiler the copies cannot alias the fragment reads, so it does
+// not wait for them before reading. On entry f holds substep 0 (buffer 0);
+// after the last step that read finds a repeated copy (valid data, not used).
+// Measured in the 65B-class layer step (same box, each against the form
+// before it): the weight copied two steps ahead with all four substeps
+// before the barrier and raised issue priority, for operands above the
+// last-level cache, 997 -> 981 ms (the six 22016-wide GEMMs 1181 -> 1158 us;
+// the raised priority had made the two-buffer form 4-6% faster there); the
+// same three buffers with this schedule for the cache-resident operands,
+// 972.9 -> 967 ms (8192 x 8192 GEMMs 404-417 -> 400-402 us); this schedule
+// for the larger operands too, 969.0 -> 951.2 ms (22016-wide GEMMs 1150 ->
+// 1108 us; with the raised priority kept, 952.2 ms).
 template <bool kF16, bool kNN>
 __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
-                                          int nk_main, int wave,
-                                          const char* __restrict__ Ac, const char* __restrict__ Bc,
-                                          char* __restrict__ An, char* __restrict__ Bn, f32x16 (&acc)[kTM][kTN],
-                                          StepFrags& f) {
-  const int lane = threadIdx.x & 63;
-  const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
-  // past the last step (nk: end of this workgroup's range) the copy repeats
-  // the last step into a buffer no later step reads: keeps the body free of
-  // branches
-  const int s1 = step + 1 < nk ? step + 1 : nk - 1;
-  issue_step<kNN>(rs, p, s1, nk_main, wave, An, Bn, a.ldf, a.ldx);
-  __builtin_amdgcn_sched_barrier(0);
-  constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
-#pragma unroll
-  for (int kk = 0; kk < 3; ++kk) {  // substeps before the barrier
-    const int cb = kk & 1;
-    read_substep<kNN>(f, Ac, Bc, wm0, wn0, kk + 1, cb ^ 1, lane);
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[cb][i], f.bfr[cb][j], acc[i][j]);
-  }
-  // schedule: for substeps 0..2 one fragment read (of the next substep) per
-  // MFMA
-#pragma unroll
-  for (int kk = 0; kk < 3; ++kk)
-#pragma unroll
-    for (int g = 0; g < kMfma; ++g) {
-      if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-    }
-  __builtin_amdgcn_sched_barrier(0);
-  step_barrier<0>();
-  __builtin_amdgcn_sched_barrier(0);
-  read_substep<kNN>(f, An, Bn, wm0, wn0, 0, 0, lane);
-#pragma unroll
-  for (int i = 0; i < kTM; ++i)
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[1][i], f.bfr[1][j], acc[i][j]);
-#pragma unroll
-  for (int g = 0; g < kMfma; ++g) {
-    if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Three-buffer step (the plain bf16 forms): MFMAs on (Ac, Bc) while the
-// activation copies of step + 1 fill An and the weight copies of step + 2
-// fill Bn2 (A in two 32 KB buffers, B in three: 160 KB of LDS), so a weight
-// copy has two steps to land. Substeps 0-2 multiply, the copies of step + 1
-// (both operands) have landed and all waves meet, the weight copies of
-// step + 2 may still be in flight; then substep 3 multiplies while substep 0
-// of step + 1 is read from (An, Bn1). Measured in the 65B-class layer step
-// (same box, each against the form before it): the weight side copied two
-// steps ahead with all four substeps before the barrier and raised issue
-// priority for operands above the last-level cache, 997 -> 981 ms (the six
-// 22016-wide GEMMs 1181 -> 1158 us); the same three buffers with this
-// schedule for the cache-resident operands, 972.9 -> 967 ms (8192 x 8192
-// GEMMs 404-417 -> 400-402 us); this schedule for the larger operands too,
-// 969.0 -> 951.2 ms (22016-wide GEMMs 1150 -> 1108 us; with the raised
-// priority kept, 952.2 ms).
-template <bool kF16, bool kNN>
-__device__ __forceinline__ void bf16_step3x(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
                                             int nk_main, int wave, const char* __restrict__ Ac,
                                             const char* __restrict__ Bc, char* __restrict__ An,
                                             const char* __restrict__ Bn1, char* __restrict__ Bn2,
@@ -336,11 +280,11 @@ __device__ __forceinline__ void bf16_step3x(const BfArgs& a, const Rsrc& rs, con
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// First copies of the three-buffer form: step sbeg of both operands and the
+// First copies: step sbeg of both operands and the
 // weight of step sbeg + 1 (restrict pointers, as in the steps, so the
 // compiler can tell these copies from the fragment reads of the loop).
 template <bool kNN>
-__device__ __forceinline__ void prologue3(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int sbeg, int nk,
+__device__ __forceinline__ void prologue(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int sbeg, int nk,
                                           int nk_main, int wave, char* __restrict__ A0, char* __restrict__ B0,
                                           char* __restrict__ B1) {
   issue_act<kNN>(rs, p, sbeg, nk_main, wave, A0);
@@ -414,8 +358,7 @@ __device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char
 // the tile's mask bytes land in buffers 1, masks and scales the accumulators
 // from there, then runs its main steps as usual.
 // kF16: fp16 operands and output (the compute-type ablation), else bf16.
-// kB3: the plain bf16 form (no mask): three weight buffers (bf16_step3x).
-template <bool kMask, bool kF16, bool kNN = false, bool kB3 = false>
+template <bool kMask, bool kF16, bool kNN = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
   // direct copies from the one being read
@@ -423,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   __shared__ __attribute__((aligned(16))) char As1[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs0[kTileBytes];
   __shared__ __attribute__((aligned(16))) char Bs1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char Bs2[kB3 ? kTileBytes : 16];  // third weight buffer (kB3)
+  __shared__ __attribute__((aligned(16))) char Bs2[kTileBytes];  // third weight buffer
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -480,45 +423,30 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
       nk_end = nk_main;
     }
   }
-  if constexpr (kB3) {
-    static_assert(!kMask && !kF16, "the three-buffer form is bf16 without dropout");
-    if (sbeg < nk_end) {
-      prologue3<kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, Bs1);
+  {
+    if (sbeg < nk_end) {  // (every split range is non-empty for the split counts split_plan picks)
+      prologue<kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, Bs1);
       StepFrags f;
       read_substep<kNN>(f, As0, Bs0, wm0, wn0, 0, 0, lane);
-      bf16_step3x<kF16, kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, Bs2, acc, f);
+      bf16_step<kF16, kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, Bs2, acc, f);
       int s = sbeg + 1;
       for (; s + 6 <= nk_end; s += 6) {
-        bf16_step3x<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs2, Bs0, acc, f);
-        bf16_step3x<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs0, Bs1, acc, f);
-        bf16_step3x<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs1, Bs2, acc, f);
-        bf16_step3x<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs2, Bs0, acc, f);
-        bf16_step3x<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs0, Bs1, acc, f);
-        bf16_step3x<kF16, kNN>(a, rs, plan, s + 5, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, Bs2, acc, f);
+        bf16_step<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs2, Bs0, acc, f);
+        bf16_step<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs0, Bs1, acc, f);
+        bf16_step<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs1, Bs2, acc, f);
+        bf16_step<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs2, Bs0, acc, f);
+        bf16_step<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs0, Bs1, acc, f);
+        bf16_step<kF16, kNN>(a, rs, plan, s + 5, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, Bs2, acc, f);
       }
       const int rem = nk_end - s;
-      if (rem > 0) bf16_step3x<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs2, Bs0, acc, f);
-      if (rem > 1) bf16_step3x<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs0, Bs1, acc, f);
-      if (rem > 2) bf16_step3x<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs1, Bs2, acc, f);
-      if (rem > 3) bf16_step3x<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs2, Bs0, acc, f);
-      if (rem > 4) bf16_step3x<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs0, Bs1, acc, f);
+      if (rem > 0) bf16_step<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, As0, Bs2, Bs0, acc, f);
+      if (rem > 1) bf16_step<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, As0, Bs2, As1, Bs0, Bs1, acc, f);
+      if (rem > 2) bf16_step<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As1, Bs0, As0, Bs1, Bs2, acc, f);
+      if (rem > 3) bf16_step<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As0, Bs1, As1, Bs2, Bs0, acc, f);
+      if (rem > 4) bf16_step<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, As1, Bs2, As0, Bs0, Bs1, acc, f);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
       __syncthreads();
     }
-  } else if (sbeg < nk_end) {  // (every split range is non-empty for the split counts split_plan picks)
-    issue_step<kNN>(rs, plan, sbeg, nk_main, wave, As0, Bs0, a.ldf, a.ldx);
-    step_barrier<0>();
-    StepFrags f;
-    read_substep<kNN>(f, As0, Bs0, wm0, wn0, 0, 0, lane);  // the cross-barrier schedule's
-    for (int step = sbeg; step < nk_end; step += 2) {
-      bf16_step<kF16, kNN>(a, rs, plan, step, nk_end, nk_main, wave, As0, Bs0, As1, Bs1, acc, f);
-      if (step + 1 < nk_end)
-        bf16_step<kF16, kNN>(a, rs, plan, step + 1, nk_end, nk_main, wave, As1, Bs1, As0, Bs0, acc, f);
-    }
-    // the cross-barrier schedule's last read (of the repeated copy) is done
-    // before the epilogue reuses the buffers
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
-    __syncthreads();
   }
 
   if (!whole) {
@@ -680,7 +608,7 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
   if (nn) {
     // the weight operand stored [contraction][output] (bf16 base, dX)
     if (mask != nullptr || f16) return hipErrorInvalidValue;
-    gemm_bf16_kernel<false, false, true, true><<<grid, kThreads, 0, stream>>>(a);
+    gemm_bf16_kernel<false, false, true><<<grid, kThreads, 0, stream>>>(a);
   } else if (f16) {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
@@ -690,7 +618,7 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
     else
-      gemm_bf16_kernel<false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
+      gemm_bf16_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
   }
   if (a.splits > 1) {
     const int64_t groups = a.tail * (kBM * kBN / 4);
