@@ -17,7 +17,8 @@
 // step s + 1 and the weight copies of step s + 2, so a weight copy has two
 // steps to land, and one barrier per step (after its third substep)
 // separates filling a buffer from reading it; the buffers rotate with period
-// six.
+// six. Activations above 128 MB take the mirrored ring (activation in three
+// buffers, weight in two).
 //
 // Per-step cost is kept off the vector ALU: every lane's byte offset inside
 // each operand (row, swizzled chunk) is computed once, and a step only moves
@@ -280,6 +281,70 @@ __device__ __forceinline__ void bf16_step(const BfArgs& a, const Rsrc& rs, const
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The same step with the roles of the operands swapped (activation tile in
+// three buffers, copied two steps ahead; weight tile in two), for
+// activations larger than the last-level cache holds beside the weight: the
+// weight copies of step + 1 fill Bn, the activation copies of step + 2 fill
+// An2, and after the barrier substep 0 of step + 1 is read from (An1, Bn).
+// Measured in the 65B-class layer step: down's forward (activation H, 180 MB)
+// 1101.6 -> 1084.8 us, the dX of gate / up (activation dG / dU) 1091-1094 ->
+// 1058-1061 us, the step 946.9 -> 939.7 ms.
+template <bool kF16, bool kNN>
+__device__ __forceinline__ void bf16_step_a3(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int step, int nk,
+                                             int nk_main, int wave, const char* __restrict__ Ac,
+                                             const char* __restrict__ Bc, char* __restrict__ Bn,
+                                             const char* __restrict__ An1, char* __restrict__ An2,
+                                             f32x16 (&acc)[kTM][kTN], StepFrags& f) {
+  const int lane = threadIdx.x & 63;
+  const int wm0 = (wave >> 2) * 128, wn0 = (wave & 3) * 64;
+  const int s1 = step + 1 < nk ? step + 1 : nk - 1;
+  const int s2 = step + 2 < nk ? step + 2 : nk - 1;
+  issue_wt<kNN>(rs, p, s1, nk_main, wave, Bn, a.ldf, a.ldx);
+  issue_act<kNN>(rs, p, s2, nk_main, wave, An2);
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kReads = kTM + (kNN ? 2 : 1) * kTN, kMfma = kTM * kTN;
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    const int cb = kk & 1;
+    read_substep<kNN>(f, Ac, Bc, wm0, wn0, kk + 1, cb ^ 1, lane);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[cb][i], f.bfr[cb][j], acc[i][j]);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk)
+#pragma unroll
+    for (int g = 0; g < kMfma; ++g) {
+      if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  step_barrier<kCopies>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_substep<kNN>(f, An1, Bn, wm0, wn0, 0, 0, lane);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32<kF16>(f.af[1][i], f.bfr[1][j], acc[i][j]);
+#pragma unroll
+  for (int g = 0; g < kMfma; ++g) {
+    if (g < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool kNN>
+__device__ __forceinline__ void prologue_a3(const BfArgs& a, const Rsrc& rs, const CopyPlan& p, int sbeg, int nk,
+                                            int nk_main, int wave, char* __restrict__ A0, char* __restrict__ B0,
+                                            char* __restrict__ A1) {
+  issue_act<kNN>(rs, p, sbeg, nk_main, wave, A0);
+  issue_wt<kNN>(rs, p, sbeg, nk_main, wave, B0, a.ldf, a.ldx);
+  issue_act<kNN>(rs, p, sbeg + 1 < nk ? sbeg + 1 : nk - 1, nk_main, wave, A1);
+  step_barrier<kCopies>();
+}
+
 // First copies: step sbeg of both operands and the
 // weight of step sbeg + 1 (restrict pointers, as in the steps, so the
 // compiler can tell these copies from the fragment reads of the loop).
@@ -358,7 +423,8 @@ __device__ __forceinline__ void mask_acc_lds(f32x16 (&acc)[kTM][kTN], const char
 // the tile's mask bytes land in buffers 1, masks and scales the accumulators
 // from there, then runs its main steps as usual.
 // kF16: fp16 operands and output (the compute-type ablation), else bf16.
-template <bool kMask, bool kF16, bool kNN = false>
+// kA3: the mirrored ring (bf16_step_a3; plain bf16 only).
+template <bool kMask, bool kF16, bool kNN = false, bool kA3 = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
   // four separate arrays so the compiler can tell the buffer being filled by
   // direct copies from the one being read
@@ -423,7 +489,33 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(BfArgs a) {
       nk_end = nk_main;
     }
   }
-  {
+  if constexpr (kA3) {
+    // activation ring of three (As0, As1, Bs2), weight ring of two (Bs0, Bs1)
+    char* const A2 = Bs2;
+    if (sbeg < nk_end) {
+      prologue_a3<kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, As1);
+      StepFrags f;
+      read_substep<kNN>(f, As0, Bs0, wm0, wn0, 0, 0, lane);
+      bf16_step_a3<kF16, kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, Bs1, As1, A2, acc, f);
+      int s = sbeg + 1;
+      for (; s + 6 <= nk_end; s += 6) {
+        bf16_step_a3<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, Bs0, A2, As0, acc, f);
+        bf16_step_a3<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, A2, Bs0, Bs1, As0, As1, acc, f);
+        bf16_step_a3<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As0, Bs1, Bs0, As1, A2, acc, f);
+        bf16_step_a3<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As1, Bs0, Bs1, A2, As0, acc, f);
+        bf16_step_a3<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, A2, Bs1, Bs0, As0, As1, acc, f);
+        bf16_step_a3<kF16, kNN>(a, rs, plan, s + 5, nk_end, nk_main, wave, As0, Bs0, Bs1, As1, A2, acc, f);
+      }
+      const int rem = nk_end - s;
+      if (rem > 0) bf16_step_a3<kF16, kNN>(a, rs, plan, s, nk_end, nk_main, wave, As1, Bs1, Bs0, A2, As0, acc, f);
+      if (rem > 1) bf16_step_a3<kF16, kNN>(a, rs, plan, s + 1, nk_end, nk_main, wave, A2, Bs0, Bs1, As0, As1, acc, f);
+      if (rem > 2) bf16_step_a3<kF16, kNN>(a, rs, plan, s + 2, nk_end, nk_main, wave, As0, Bs1, Bs0, As1, A2, acc, f);
+      if (rem > 3) bf16_step_a3<kF16, kNN>(a, rs, plan, s + 3, nk_end, nk_main, wave, As1, Bs0, Bs1, A2, As0, acc, f);
+      if (rem > 4) bf16_step_a3<kF16, kNN>(a, rs, plan, s + 4, nk_end, nk_main, wave, A2, Bs1, Bs0, As0, As1, acc, f);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+      __syncthreads();
+    }
+  } else {
     if (sbeg < nk_end) {  // (every split range is non-empty for the split counts split_plan picks)
       prologue<kNN>(a, rs, plan, sbeg, nk_end, nk_main, wave, As0, Bs0, Bs1);
       StepFrags f;
@@ -588,6 +680,11 @@ bool gemm_bf16_offsets_fit(int64_t M, int64_t kc, int kx, int64_t nout) {
   return M * kc * 2 < lim && M * (int64_t)kx * 2 < lim && nout * ldf * 2 < lim;
 }
 
+// activation bytes above which the activation takes the three-buffer ring
+// (bf16_step_a3): more than half the 256 MB last-level cache, so it streams
+// from HBM beside the weight instead of staying resident for its re-reads
+constexpr int64_t kActStreamBytes = 128LL << 20;
+
 hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, const uint16_t* split, int kx,
                                 const uint16_t* f, int64_t ldf, const uint16_t* fx, int64_t ldx, int64_t nout,
                                 uint16_t* out, float* part, hipStream_t stream, const uint8_t* mask, float keep_scale,
@@ -608,7 +705,10 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
   if (nn) {
     // the weight operand stored [contraction][output] (bf16 base, dX)
     if (mask != nullptr || f16) return hipErrorInvalidValue;
-    gemm_bf16_kernel<false, false, true><<<grid, kThreads, 0, stream>>>(a);
+    if (M * kc * 2 > kActStreamBytes)
+      gemm_bf16_kernel<false, false, true, true><<<grid, kThreads, 0, stream>>>(a);
+    else
+      gemm_bf16_kernel<false, false, true><<<grid, kThreads, 0, stream>>>(a);
   } else if (f16) {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, true><<<grid, kThreads, 0, stream>>>(a);
@@ -617,6 +717,8 @@ hipError_t launch_gemm_bf16_ext(const uint16_t* act, int64_t M, int64_t kc, cons
   } else {
     if (mask != nullptr && kx > 0)
       gemm_bf16_kernel<true, false><<<grid, kThreads, 0, stream>>>(a);
+    else if (M * kc * 2 > kActStreamBytes)
+      gemm_bf16_kernel<false, false, false, true><<<grid, kThreads, 0, stream>>>(a);
     else
       gemm_bf16_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
   }

@@ -13,8 +13,9 @@ so the same kernel choices) the bench times.
   W, A, B drawn on the device as the bench draws every layer past the first,
   copied back for the oracle: the whole encoding bit for bit, then the same
   checks;
-* GEMMs whose operands exceed the 256 MB last-level cache at step counts the
-  workloads do not reach (the remainders of the weight-buffer rotation).
+* GEMMs whose operands exceed the 256 MB last-level cache, or whose activation
+  exceeds 128 MB, at step counts the workloads do not reach (the remainders
+  of the buffer rotations).
 The oracle encodes each weight itself (whole tensor) and multiplies in fp64.
 Bars: relative Frobenius error <= 2e-3 for Y and dX (sampled rows: over the
 sampled rows) with every element of them inside the oracle's element-wise
@@ -164,6 +165,20 @@ def test_streamed_gemm_step_remainders(q, n, k):
     inp = synth.linear_inputs(91, 0, 0, n, k, M, r, s, sigma=0.02)
     X, dY, A, B, Y, T, dX, dA, dB = _run_linear(q, inp)
     _check_linear(f"{n}x{k}", inp.W, X, dY, A, B, s, Y, T, dX, dA, dB, _rows(M, 24, 41))
+
+
+# Activations above 128 MB take the mirrored ring (activation tile in three
+# buffers, weight tile in two): in the 65B stack down's forward (3 steps left
+# after the groups) and the dX of gate / up; these forwards (M = 4096,
+# K / 64 steps after the first, r = 16) leave 0, 1, 2 and 5.
+@pytest.mark.parametrize("k", [16512, 16576, 16640, 16448])
+def test_streamed_activation_step_remainders(q, k):
+    M, n, r, s = 4096, 1024, 16, 2.0
+    assert M * k * 2 > (128 << 20)
+    say(f"case: streamed activation {n}x{k} M={M} r={r}: forward {(k // 64) % 6} steps after the groups")
+    inp = synth.linear_inputs(92, 0, 0, n, k, M, r, s, sigma=0.02)
+    X, dY, A, B, Y, T, dX, dA, dB = _run_linear(q, inp)
+    _check_linear(f"{n}x{k}", inp.W, X, dY, A, B, s, Y, T, dX, dA, dB, _rows(M, 24, 43))
 
 
 @pytest.mark.parametrize("li", [0, 6])
