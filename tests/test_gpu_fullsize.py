@@ -181,6 +181,18 @@ def test_streamed_activation_step_remainders(q, k):
     _check_linear(f"{n}x{k}", inp.W, X, dY, A, B, s, Y, T, dX, dA, dB, _rows(M, 24, 43))
 
 
+def test_streamed_activation_ragged_contraction(q):
+    """dX over the transposed operand with n = 2056 (not a multiple of 64: the
+    last activation step reads clamped columns) and an activation above 128 MB
+    (dY, M = 32768): the mirrored ring with the ragged step."""
+    M, n, k, r, s = 32768, 2056, 576, 16, 2.0
+    assert M * n * 2 > (128 << 20) and n % 64 != 0
+    say(f"case: streamed ragged dX {n}x{k} M={M} r={r}")
+    inp = synth.linear_inputs(93, 0, 0, n, k, M, r, s, sigma=0.02)
+    X, dY, A, B, Y, T, dX, dA, dB = _run_linear(q, inp)
+    _check_linear(f"{n}x{k}", inp.W, X, dY, A, B, s, Y, T, dX, dA, dB, _rows(M, 24, 47))
+
+
 @pytest.mark.parametrize("li", [0, 6])
 def test_65b_last_layer_device_drawn(q, li):
     c = synth.CONFIGS[5]
