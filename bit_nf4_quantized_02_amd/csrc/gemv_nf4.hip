@@ -58,8 +58,12 @@ __global__ __launch_bounds__(256) void gemv_xperm_kernel(const uint16_t* __restr
 // reads copy l % kLutCopies: the 16 lanes that share the LDS banks in one
 // cycle of an 8-byte read then hit 16 different bank pairs whatever codes
 // they look up (with one shared copy, random codes collide).
-constexpr int kLutCopies = 16;
-constexpr int kLutBytes = 256 * kLutCopies * 8;
+// With eight waves per workgroup (one workgroup per CU) the table holds 32
+// copies, 256 bytes per entry: a lane's address is then its code byte in bits
+// 8..15 and its copy offset in bits 0..7, formed by one byte permute instead
+// of an extract and a shift-or; 32 copies also leave no bank conflict at all.
+template <int kW>
+constexpr int lut_copies() { return kW == 8 ? 32 : 16; }
 constexpr int kRingDepth = 3;  // chunks of codes per wave: one worked on, two in flight
 
 // s_waitcnt immediate that waits for LDS / scalar-memory operations only
@@ -121,7 +125,8 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
   // three separate ring arrays, so the compiler can tell the one being read
   // from the ones being filled by direct copies (and waits only for the copy
   // of the chunk it reads)
-  __shared__ __attribute__((aligned(16))) char lut[kLutBytes];
+  constexpr int kLutCopies = lut_copies<kW>();
+  __shared__ __attribute__((aligned(16))) char lut[256 * kLutCopies * 8];
   __shared__ __attribute__((aligned(16))) char ring0[kW * kSlot];
   __shared__ __attribute__((aligned(16))) char ring1[kW * kSlot];
   __shared__ __attribute__((aligned(16))) char ring2[kW * kSlot];
@@ -240,8 +245,15 @@ __global__ __launch_bounds__(64 * kW) void gemv_nf4_kernel(const uint8_t* __rest
       for (int w = 0; w < kGw; ++w)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t b = (cw[i][s0 + w] >> (8 * p)) & 0xFFu;
-          out[4 * w + p] = *reinterpret_cast<const float2*>(lut + ((b * (kLutCopies * 8)) | lane_off));
+          uint32_t addr;
+          if constexpr (kLutCopies == 32) {
+            // bytes of the result: lane_off (byte 0 of the second operand),
+            // code byte p (byte p of the first), zero, zero
+            addr = __builtin_amdgcn_perm(cw[i][s0 + w], lane_off, 0x0C0C0400u + ((uint32_t)p << 8));
+          } else {
+            addr = (((cw[i][s0 + w] >> (8 * p)) & 0xFFu) * (kLutCopies * 8)) | lane_off;
+          }
+          out[4 * w + p] = *reinterpret_cast<const float2*>(lut + addr);
         }
     };
     gather(0, lv[0]);
