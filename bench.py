@@ -642,8 +642,8 @@ def variant_rows(wl: Workload, q, reps: int = 10):
     P = q._ptr
     Y, T, dX = torch.empty_like(p.Y), torch.empty_like(p.T), torch.empty_like(p.dX)
     dA, dB = torch.empty_like(p.dA), torch.empty_like(p.dB)
-    out = {}
     forms = (("dq", True, torch.float32), ("no_dq", False, torch.float32), ("no_dq_bf16_scale", False, torch.bfloat16))
+    rows = []
     for grid in ("nf4", "uniform"):
         cb = torch.tensor(q.build_nf4_codebook() if grid == "nf4" else q.build_uniform4_codebook(),
                           dtype=torch.float32, device="cuda")
@@ -658,11 +658,19 @@ def variant_rows(wl: Workload, q, reps: int = 10):
             if p.api_bwd is not None:
                 calls.append(q.Call("qlora_linear_bwd", wref, P(p.X), P(T), P(p.dY), p.m, P(p.A), P(p.B), p.r,
                                     p.s, P(dX), P(dA), P(dB), 0, lw, lwn, st, keep=(wst,)))
-            us = _region_us(lambda: [cl() for cl in calls], reps)
-            out[f"{grid}_{tag}"] = dict(
-                bits_per_weight=round(8.0 * w.nbytes() / (w.n * w.k), 4), weight_relerr=round(err, 5),
-                step_us=round(us, 2))
-            del w
+            rows.append((f"{grid}_{tag}", w, err, calls))
+    # the forms timed round-robin, three rounds, each form's best round: the
+    # first form timed alone once read ~10% slow (clock and cache state after
+    # the encodes), which is the order, not the format
+    best = {name: float("inf") for name, *_ in rows}
+    for _ in range(3):
+        for name, w, err, calls in rows:
+            best[name] = min(best[name], _region_us(lambda: [cl() for cl in calls], reps))
+    out = {}
+    for name, w, err, calls in rows:
+        out[name] = dict(bits_per_weight=round(8.0 * w.nbytes() / (w.n * w.k), 4), weight_relerr=round(err, 5),
+                         step_us=round(best[name], 2))
+    del rows
     return out
 
 
